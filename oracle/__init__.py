@@ -1,0 +1,186 @@
+"""The CPU oracle for causal linear attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the benchmark's
+``cpu_baseline`` leg may import this package.  The product path (the HIP
+library and its Python binding) never imports, links or runs anything here,
+and this package imports nothing from the product.
+
+Two oracles, both in float64 on the host:
+
+* :func:`recurrence` -- the token-by-token recurrence of the slide deck
+  "Chunking, causality, and parallel prefill", section "Naive recurrence":
+  ``S_t = S_{t-1} + k_t v_t^T`` then ``o_t = S_t^T q_t``.  It runs in plain C
+  (``lla_oracle.c``, built with ``-O2 -ffp-contract=off``) so the large
+  configurations finish in seconds; this is the oracle every GPU result is
+  compared against.
+* :func:`chunked` -- the same deck's chunk form ("Split into chunks",
+  "Incoming and outgoing state", "Worked case - full trace"): per chunk of C
+  tokens ``M = tril(Q_c K_c^T)`` (diagonal kept), ``O_c = M V_c + Q_c S_in``,
+  ``S_out = S_in + K_c^T V_c``.  Written step by step in numpy for small
+  inputs; it exists to reproduce the deck's chunked trace, its C = 2 transfer
+  exercise and its two bugs, and it is pinned against :func:`recurrence`.
+
+Reading of the deck taken here (each also listed in the design notes):
+the inter-chunk term is ``Q_c S_in`` (the deck's map prints ``K S_in``, but
+its trace uses ``q_t^T S_4`` and has ``q_t = k_t``); the mask keeps the
+diagonal; no feature map, normaliser, scale or decay; S is d_k x d_v with the
+key dimension as rows; a last chunk shorter than C is the same arithmetic on
+fewer rows; decode applies the rank-1 update, then reads the state.
+
+Parity of both functions is pinned in ``tests/test_oracle.py`` against values
+the deck prints, closed forms and brute force.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "lla_oracle.c")
+_SO = os.path.join(_HERE, "liblla_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+__all__ = ["build", "recurrence", "decode_step", "chunked", "causal_mask",
+           "incoming_term"]
+
+
+def build(force: bool = True) -> str:
+    """Compile ``lla_oracle.c`` into ``liblla_oracle.so`` with gcc."""
+    if force or not os.path.exists(_SO):
+        tmp = _SO + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", "-O2", "-ffp-contract=off", "-fPIC", "-shared",
+                        "-pthread", "-o", tmp, _SRC], check=True)
+        os.replace(tmp, _SO)
+    return _SO
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_SO):
+                build(force=True)
+            lib = ctypes.CDLL(_SO)
+            dp = ctypes.POINTER(ctypes.c_double)
+            i64 = ctypes.c_int64
+            lib.lla_oracle_recurrence.argtypes = [dp, dp, dp, dp, dp, i64, i64, i64,
+                                                  i64, i64, dp, ctypes.c_int]
+            lib.lla_oracle_recurrence.restype = ctypes.c_int
+            lib.lla_oracle_decode_step.argtypes = [dp, dp, dp, dp, dp, i64, i64, i64]
+            lib.lla_oracle_decode_step.restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def _f64(a) -> np.ndarray:
+    """Exact upcast to a C-contiguous float64 array (accepts numpy or torch)."""
+    if hasattr(a, "detach"):  # torch tensor: upcast exactly on the host
+        a = a.detach().cpu().double().numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def recurrence(q, k, v, S0=None, ckpt_every: int = 0, nthreads: int = 1):
+    """Token-by-token recurrence in float64.
+
+    q, k: [..., T, dk]; v: [..., T, dv]; S0: [..., dk, dv] or None (zeros).
+    Returns ``(O, S_T)`` -- or ``(O, S_T, ckpt)`` when ``ckpt_every > 0``,
+    where ``ckpt[..., c, :, :]`` is the state after ``(c+1)*ckpt_every``
+    tokens.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    lead = q.shape[:-2]
+    T, dk = q.shape[-2], q.shape[-1]
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:-1] != q.shape[:-1]:
+        raise ValueError("shape mismatch: q %s k %s v %s" % (q.shape, k.shape, v.shape))
+    BH = int(np.prod(lead)) if lead else 1
+    S = np.zeros(lead + (dk, dv)) if S0 is None else _f64(S0).copy()
+    if S.shape != lead + (dk, dv):
+        raise ValueError("S0 shape %s, expected %s" % (S.shape, lead + (dk, dv)))
+    O = np.zeros(lead + (T, dv))
+    n_ck = T // ckpt_every if ckpt_every > 0 else 0
+    ck = np.zeros(lead + (n_ck, dk, dv)) if ckpt_every > 0 else None
+    rc = _load().lla_oracle_recurrence(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(S), _ptr(O), BH, T, dk, dv,
+        int(ckpt_every), _ptr(ck) if ck is not None and ck.size else None,
+        int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle recurrence rejected its arguments")
+    return (O, S, ck) if ckpt_every > 0 else (O, S)
+
+
+def decode_step(q, k, v, S):
+    """One decode step in float64: ``S += k v^T``, then ``o = S^T q``.
+
+    q, k: [..., dk]; v: [..., dv]; S: [..., dk, dv].  Returns ``(o, S_new)``
+    without modifying the caller's S.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    S = _f64(S).copy()
+    lead = q.shape[:-1]
+    dk, dv = q.shape[-1], v.shape[-1]
+    BH = int(np.prod(lead)) if lead else 1
+    o = np.zeros(lead + (dv,))
+    rc = _load().lla_oracle_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(S), _ptr(o),
+                                        BH, dk, dv)
+    if rc != 0:
+        raise RuntimeError("oracle decode step rejected its arguments")
+    return o, S
+
+
+# --- the deck's chunk form, step by step (numpy, float64, small inputs) -----
+
+def causal_mask(A: np.ndarray) -> np.ndarray:
+    """Lower triangle of a chunk's score matrix, diagonal kept.
+
+    Deck section "Causal triangle": row i (reading token) may read column j
+    only when j <= i; cells above the diagonal are forbidden, cells below it
+    keep their computed value (zero or not).
+    """
+    return np.tril(A)
+
+
+def incoming_term(Qc: np.ndarray, S_in: np.ndarray) -> np.ndarray:
+    """What a chunk reads from the past through the state: row t is q_t^T S_in.
+
+    Deck section "Incoming and outgoing state" (o_5 = q_5^T S_4 + local term).
+    """
+    return Qc @ S_in
+
+
+def chunked(q, k, v, C: int, S0=None):
+    """The chunk form for one stream: q, k [T, dk], v [T, dv], S0 [dk, dv].
+
+    Walks the chunks in order; for each chunk of C tokens (the last one may be
+    shorter): the masked score triangle, the output ``M V + Q S_in``, then the
+    outgoing state ``S_in + K^T V``.  Returns ``(O, S_T, handoffs, masks)``
+    where ``handoffs`` lists the state emitted by every chunk but the last
+    (the states handed from one chunk to the next) and ``masks`` the masked
+    triangles.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    T, dk = q.shape
+    dv = v.shape[1]
+    if C < 1:
+        raise ValueError("chunk size must be >= 1")
+    S = np.zeros((dk, dv)) if S0 is None else _f64(S0).copy()
+    O = np.zeros((T, dv))
+    handoffs, masks = [], []
+    for start in range(0, T, C):
+        Qc, Kc, Vc = q[start:start + C], k[start:start + C], v[start:start + C]
+        M = causal_mask(Qc @ Kc.T)
+        O[start:start + C] = M @ Vc + incoming_term(Qc, S)
+        S = S + Kc.T @ Vc
+        masks.append(M)
+        if start + C < T:
+            handoffs.append(S.copy())
+    return O, S, handoffs, masks

@@ -1,0 +1,136 @@
+"""Seeded synthetic inputs for causal linear attention.
+
+This module only draws and shapes inputs; it holds none of the method's
+arithmetic.  Both sides use it: the GPU path (tests, benchmark, smoke check)
+and the oracle (which receives the very same tensors upcast to float64).
+
+The workloads follow the shapes of the slide deck "Chunking, causality, and
+parallel prefill": its worked case (8 tokens, d = 2, chunk C = 4, q_t = k_t,
+"Worked case - full trace"), and larger prefill/decode shapes in the same
+notation (B sequences, H heads, T tokens, head dims d_k = d_v, chunk C).
+
+Recipe (also stated in the design notes):
+* toy variant 0 is the deck's trace; variants 1..100 draw Q, K, V uniformly
+  from {0, 1} (fp32) with ``torch.manual_seed(variant)``;
+* gaussian inputs draw Q, K, V ~ N(0, 1) * scale in fp32 with one CPU or
+  device generator per tensor (seed = 10 * config + {0: q, 1: k, 2: v}),
+  optionally L2-normalise every key row in fp32, then round to the storage
+  dtype (round-to-nearest-even for bf16);
+* integer inputs draw uniformly from {lo..hi}; they are exact in bf16, so
+  every product and partial sum of the method is an exact integer.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+# The deck's worked case ("Worked case - full trace"): 8 tokens, d = 2,
+# q_t = k_t, keys alternate [1,0],[0,1]; values as printed for chunks 1 and 2.
+TRACE_K = [[1, 0], [0, 1], [1, 0], [0, 1], [1, 0], [0, 1], [1, 0], [0, 1]]
+TRACE_V = [[2, 3], [5, 1], [1, 1], [0, 4], [0, 1], [2, 2], [1, 0], [0, 0]]
+
+
+@dataclass(frozen=True)
+class Config:
+    name: str
+    B: int
+    H: int
+    T: int
+    C: int
+    dk: int
+    dv: int
+    dtype: torch.dtype
+    scale: float = 1.0
+    l2norm_k: bool = False
+    seed_base: int = 0
+    decode_steps: int = 0
+    note: str = field(default="", compare=False)
+
+
+# c1: the deck's toy; c2..c4: prefill shapes; c5: decode after a T=4096 prefill.
+CONFIGS = {
+    "c1": Config("toy", 1, 1, 8, 4, 2, 2, torch.float32, seed_base=10,
+                 note="variant 0 = the deck's trace, variants 1..100 uniform {0,1}"),
+    "c2": Config("prefill_B4_H8_T1024_C64_d64", 4, 8, 1024, 64, 64, 64, torch.bfloat16,
+                 scale=64 ** -0.5, seed_base=20),
+    "c3": Config("prefill_B1_H16_T8192_C64_d128", 1, 16, 8192, 64, 128, 128,
+                 torch.bfloat16, scale=128 ** -0.5, l2norm_k=True, seed_base=30),
+    "c4": Config("prefill_B1_H32_T131072_C128_d128", 1, 32, 131072, 128, 128, 128,
+                 torch.bfloat16, scale=128 ** -0.5, seed_base=40),
+    "c5": Config("decode_B256_H32_d128_after_T4096", 256, 32, 4096, 64, 128, 128,
+                 torch.bfloat16, scale=128 ** -0.5, seed_base=50, decode_steps=512),
+}
+
+
+def toy(variant: int):
+    """Toy inputs [1, 1, 8, 2] fp32: variant 0 = the deck's trace."""
+    if variant == 0:
+        k = torch.tensor(TRACE_K, dtype=torch.float32).view(1, 1, 8, 2)
+        v = torch.tensor(TRACE_V, dtype=torch.float32).view(1, 1, 8, 2)
+        return k.clone(), k.clone(), v
+    g = torch.Generator().manual_seed(int(variant))
+    q = torch.randint(0, 2, (1, 1, 8, 2), generator=g).float()
+    k = torch.randint(0, 2, (1, 1, 8, 2), generator=g).float()
+    v = torch.randint(0, 2, (1, 1, 8, 2), generator=g).float()
+    return q, k, v
+
+
+def _gen(device, seed):
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+def gaussian(B, H, T, dk, dv, seed_base, scale, dtype=torch.bfloat16,
+             l2norm_k=False, device="cpu"):
+    """Q, K [B,H,T,dk] and V [B,H,T,dv]: N(0,1)*scale in fp32, then cast.
+
+    Generated in slices along B so that large device workloads never hold
+    more than one slice of fp32 temporaries.
+    """
+    out = []
+    for which, d in ((0, dk), (1, dk), (2, dv)):
+        g = _gen(device, seed_base + which)
+        t = torch.empty((B, H, T, d), dtype=dtype, device=device)
+        for b in range(B):
+            x = torch.randn((H, T, d), generator=g, dtype=torch.float32, device=device)
+            x.mul_(scale)
+            if which == 1 and l2norm_k:
+                x = x / x.norm(dim=-1, keepdim=True).clamp_min(1e-30)
+            t[b].copy_(x)
+            del x
+        out.append(t)
+    return tuple(out)
+
+
+def integers(B, H, T, dk, dv, seed, lo=-1, hi=1, dtype=torch.bfloat16, device="cpu"):
+    """Q, K, V with integer values uniform in [lo, hi], stored in ``dtype``."""
+    g = _gen("cpu", seed)
+    q = torch.randint(lo, hi + 1, (B, H, T, dk), generator=g).to(dtype)
+    k = torch.randint(lo, hi + 1, (B, H, T, dk), generator=g).to(dtype)
+    v = torch.randint(lo, hi + 1, (B, H, T, dv), generator=g).to(dtype)
+    return q.to(device), k.to(device), v.to(device)
+
+
+def config_inputs(cfg: Config, device="cpu", T=None, B=None):
+    """The prefill inputs of a config (optionally truncated in T or B)."""
+    return gaussian(B or cfg.B, cfg.H, T or cfg.T, cfg.dk, cfg.dv, cfg.seed_base,
+                    cfg.scale, cfg.dtype, cfg.l2norm_k, device)
+
+
+def decode_inputs(cfg: Config, steps: int, device="cpu", B=None):
+    """Per-step decode inputs q, k [steps,B,H,dk], v [steps,B,H,dv] (bf16).
+
+    Drawn like :func:`gaussian` with seeds 10*config + {3, 4, 5}.
+    """
+    B = B or cfg.B
+    out = []
+    for which, d in ((3, cfg.dk), (4, cfg.dk), (5, cfg.dv)):
+        g = _gen(device, cfg.seed_base + which)
+        t = torch.empty((steps, B, cfg.H, d), dtype=cfg.dtype, device=device)
+        for s in range(steps):
+            x = torch.randn((B, cfg.H, d), generator=g, dtype=torch.float32, device=device)
+            t[s].copy_(x.mul_(cfg.scale))
+        out.append(t)
+    return tuple(out)
