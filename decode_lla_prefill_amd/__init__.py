@@ -1,0 +1,248 @@
+"""decode_lla_prefill_amd -- causal linear attention on AMD Instinct MI355X.
+
+Chunkwise-parallel prefill and the matching decode step of the recurrence
+``S_t = S_{t-1} + k_t v_t^T``, ``o_t = S_t^T q_t`` (slide deck "Chunking,
+causality, and parallel prefill"), computed by the HIP kernels of
+``liblla.so`` (gfx950).  This module only marshals arguments: it checks
+tensor shapes/dtypes/devices, allocates outputs and the workspace with
+PyTorch, and passes raw device pointers plus the current HIP stream to the
+C ABI declared in ``include/lla.h``.  There is no fallback: without the built
+library every call raises.
+
+Layouts (all contiguous): q, k [B, H, T, dk]; v [B, H, T, dv] (bf16 or fp32);
+o [B, H, T, dv] fp32; state [B, H, dk, dv] fp32 (rows = key dimension).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "LlaError", "library", "library_path", "state_init", "prefill", "decode_step",
+    "prefill_workspace_size", "prefill_segment_chunks", "prefill_segment_states",
+    "prefill_state_scan", "prefill_chunks", "EXPORTS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "liblla.so")
+
+# Every symbol include/lla.h declares.
+EXPORTS = ("lla_status_string", "lla_last_device_error", "lla_state_init",
+           "lla_prefill_segment_chunks", "lla_prefill_workspace_size", "lla_prefill",
+           "lla_prefill_segment_states", "lla_prefill_state_scan", "lla_prefill_chunks",
+           "lla_decode_step")
+
+_BF16, _F32 = 0, 1
+_lib = None
+
+
+class LlaError(RuntimeError):
+    """A non-OK lla_status from the library."""
+
+    def __init__(self, status: int, what: str):
+        self.status = status
+        msg = _lib.lla_status_string(status).decode() if _lib is not None else str(status)
+        if status == 8 and _lib is not None:
+            msg += " (hipError %d)" % _lib.lla_last_device_error()
+        super().__init__("%s: %s (status %d)" % (what, msg, status))
+
+
+def library():
+    """Load liblla.so (built by ``python -m decode_lla_prefill_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise ImportError("liblla.so not built: run `python -m decode_lla_prefill_amd.build` "
+                              "(looked for %s)" % library_path)
+        lib = ctypes.CDLL(library_path)
+        vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+        st, ci = ctypes.c_int, ctypes.c_int
+        lib.lla_status_string.argtypes = [st]
+        lib.lla_status_string.restype = ctypes.c_char_p
+        lib.lla_last_device_error.argtypes = []
+        lib.lla_last_device_error.restype = ci
+        lib.lla_state_init.argtypes = [vp, i64, i64, i64, i64, vp]
+        lib.lla_state_init.restype = st
+        lib.lla_prefill_segment_chunks.argtypes = [i64] * 6
+        lib.lla_prefill_segment_chunks.restype = i64
+        lib.lla_prefill_workspace_size.argtypes = [i64] * 6
+        lib.lla_prefill_workspace_size.restype = sz
+        lib.lla_prefill.argtypes = [vp, vp, vp, ci, i64, i64, i64, i64, i64, i64, vp, vp, vp, sz, vp]
+        lib.lla_prefill.restype = st
+        lib.lla_prefill_chunks.argtypes = lib.lla_prefill.argtypes
+        lib.lla_prefill_chunks.restype = st
+        lib.lla_prefill_segment_states.argtypes = [vp, vp, ci, i64, i64, i64, i64, i64, i64, vp, sz, vp]
+        lib.lla_prefill_segment_states.restype = st
+        lib.lla_prefill_state_scan.argtypes = [vp, i64, i64, i64, i64, i64, i64, vp, sz, vp]
+        lib.lla_prefill_state_scan.restype = st
+        lib.lla_decode_step.argtypes = [vp, vp, vp, ci, i64, i64, i64, i64, vp, vp, vp]
+        lib.lla_decode_step.restype = st
+        _lib = lib
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise LlaError(status, what)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return _BF16
+    if t.dtype == torch.float32:
+        return _F32
+    raise TypeError("inputs must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _ptr(t):
+    return None if t is None or t.numel() == 0 else t.data_ptr()
+
+
+def _stream(t: torch.Tensor):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on the GPU (got %s)" % (name, t.device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s (got %s)" % (name, dtype, t.dtype))
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError("%s must have %d dims (got shape %s)" % (name, ndim, tuple(t.shape)))
+
+
+def _qkv_shape(q, k, v):
+    _need(q, "q", ndim=4)
+    _need(k, "k", dtype=q.dtype, ndim=4)
+    _need(v, "v", dtype=q.dtype, ndim=4)
+    B, H, T, dk = q.shape
+    if tuple(k.shape) != (B, H, T, dk) or tuple(v.shape[:3]) != (B, H, T):
+        raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
+    return B, H, T, dk, v.shape[3]
+
+
+def state_init(B: int, H: int, dk: int, dv: int, device=None, out: torch.Tensor = None):
+    """A zero state [B, H, dk, dv] fp32 (S_0 of a fresh prompt), via lla_state_init."""
+    lib = library()
+    if out is None:
+        out = torch.empty((B, H, dk, dv), dtype=torch.float32,
+                          device=device if device is not None else "cuda")
+    _need(out, "state", dtype=torch.float32, ndim=4)
+    if tuple(out.shape) != (B, H, dk, dv):
+        raise ValueError("state shape %s, expected %s" % (tuple(out.shape), (B, H, dk, dv)))
+    _check(lib.lla_state_init(_ptr(out), B, H, dk, dv, _stream(out)), "lla_state_init")
+    return out
+
+
+def prefill_segment_chunks(B, H, T, dk, dv, chunk) -> int:
+    """Chunks one workgroup walks (G); segment s covers tokens [s*G*C, (s+1)*G*C)."""
+    return int(library().lla_prefill_segment_chunks(B, H, T, dk, dv, chunk))
+
+
+def prefill_workspace_size(B, H, T, dk, dv, chunk) -> int:
+    return int(library().lla_prefill_workspace_size(B, H, T, dk, dv, chunk))
+
+
+def _workspace(B, H, T, dk, dv, chunk, device, workspace):
+    need = prefill_workspace_size(B, H, T, dk, dv, chunk)
+    if workspace is None:
+        if need == 0:
+            return None, 0
+        workspace = torch.empty(need // 4, dtype=torch.float32, device=device)
+    _need(workspace, "workspace")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def _state_check(state, B, H, dk, dv):
+    _need(state, "state", dtype=torch.float32, ndim=4)
+    if tuple(state.shape) != (B, H, dk, dv):
+        raise ValueError("state shape %s, expected %s" % (tuple(state.shape), (B, H, dk, dv)))
+
+
+def _out(out, shape, device):
+    if out is None:
+        return torch.empty(shape, dtype=torch.float32, device=device)
+    _need(out, "out", dtype=torch.float32)
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError("out shape %s, expected %s" % (tuple(out.shape), tuple(shape)))
+    return out
+
+
+def prefill(q, k, v, state, chunk: int, out=None, workspace=None):
+    """Chunkwise prefill: returns o [B,H,T,dv] fp32; ``state`` goes S_0 -> S_T in place."""
+    lib = library()
+    B, H, T, dk, dv = _qkv_shape(q, k, v)
+    _state_check(state, B, H, dk, dv)
+    out = _out(out, (B, H, T, dv), q.device)
+    ws, ws_bytes = _workspace(B, H, T, dk, dv, chunk, q.device, workspace)
+    _check(lib.lla_prefill(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H, T, dk, dv, chunk,
+                           _ptr(state), _ptr(out), _ptr(ws), ws_bytes, _stream(q)), "lla_prefill")
+    return out
+
+
+def prefill_segment_states(k, v, chunk: int, workspace):
+    """Phase 1: K^T V of every segment but the last into workspace slots 1.."""
+    lib = library()
+    _need(k, "k", ndim=4)
+    _need(v, "v", dtype=k.dtype, ndim=4)
+    B, H, T, dk = k.shape
+    dv = v.shape[3]
+    ws, ws_bytes = _workspace(B, H, T, dk, dv, chunk, k.device, workspace)
+    _check(lib.lla_prefill_segment_states(_ptr(k), _ptr(v), _dtype_code(k), B, H, T, dk, dv, chunk,
+                                          _ptr(ws), ws_bytes, _stream(k)),
+           "lla_prefill_segment_states")
+    return ws
+
+
+def prefill_state_scan(state, T: int, chunk: int, workspace):
+    """Phase 2: segment starting states from S_0 (``state``, read only)."""
+    lib = library()
+    B, H, dk, dv = state.shape
+    _state_check(state, B, H, dk, dv)
+    ws, ws_bytes = _workspace(B, H, T, dk, dv, chunk, state.device, workspace)
+    _check(lib.lla_prefill_state_scan(_ptr(state), B, H, T, dk, dv, chunk, _ptr(ws), ws_bytes,
+                                      _stream(state)), "lla_prefill_state_scan")
+    return ws
+
+
+def prefill_chunks(q, k, v, state, chunk: int, workspace=None, out=None):
+    """Phase 3: the chunk walk from the segment states; writes o and S_T."""
+    lib = library()
+    B, H, T, dk, dv = _qkv_shape(q, k, v)
+    _state_check(state, B, H, dk, dv)
+    out = _out(out, (B, H, T, dv), q.device)
+    need = prefill_workspace_size(B, H, T, dk, dv, chunk)
+    if workspace is not None:
+        _need(workspace, "workspace")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if need and workspace is None:
+        raise ValueError("this shape needs a %d-byte workspace filled by phases 1 and 2" % need)
+    _check(lib.lla_prefill_chunks(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H, T, dk, dv, chunk,
+                                  _ptr(state), _ptr(out), _ptr(workspace), ws_bytes, _stream(q)),
+           "lla_prefill_chunks")
+    return out
+
+
+def decode_step(q, k, v, state, out=None):
+    """One decode step: ``state += k v^T`` in place; returns o = state^T q [B,H,dv] fp32."""
+    lib = library()
+    _need(q, "q", ndim=3)
+    _need(k, "k", dtype=q.dtype, ndim=3)
+    _need(v, "v", dtype=q.dtype, ndim=3)
+    B, H, dk = q.shape
+    dv = v.shape[2]
+    if tuple(k.shape) != (B, H, dk) or tuple(v.shape[:2]) != (B, H):
+        raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
+    _state_check(state, B, H, dk, dv)
+    out = _out(out, (B, H, dv), q.device)
+    _check(lib.lla_decode_step(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H, dk, dv,
+                               _ptr(state), _ptr(out), _stream(q)), "lla_decode_step")
+    return out

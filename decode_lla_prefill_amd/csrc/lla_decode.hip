@@ -1,0 +1,136 @@
+// lla_decode.hip -- the decode step and the state fill for gfx950 (MI355X).
+//
+// Decode (slide deck "Chunking, causality, and parallel prefill", "Mechanism
+// map", decode line, and the instructor note answering the prefill/decode
+// check): one token gives a 1x1 triangle, so all that is left is the rank-1
+// state update and the state read,
+//     S <- S + k v^T,      o = S^T q      (o[j] = sum_i q[i] S[i][j]).
+//
+// The step is bound by HBM: each (b,h) state of dk x dv fp32 is read once and
+// written once, while q, k, v and o are a few hundred bytes.  One workgroup
+// owns one (b,h).  A thread owns VW consecutive value columns and a strided
+// set of key rows; all of its state rows are loaded before any is used (deep
+// memory-level parallelism), each 16-byte row piece is updated in registers,
+// written back with a streaming store, and folded into the thread's partial
+// o; the partials of the row groups are summed through LDS in a fixed order.
+#include "lla_device.h"
+#include "lla_internal.h"
+
+namespace lla {
+
+template <typename Tin, int VW, int RPT>
+__global__ __launch_bounds__(kThreads) void k_decode_step(const Tin* __restrict__ q,
+                                                          const Tin* __restrict__ k,
+                                                          const Tin* __restrict__ v,
+                                                          float* __restrict__ S,
+                                                          float* __restrict__ o, int dk, int dv) {
+    typedef float vecf __attribute__((ext_vector_type(VW)));
+    __shared__ float qs[128], ks[128], vs[128];
+    __shared__ float red[kThreads * VW];
+
+    const int tid = threadIdx.x;
+    const int64_t bh = blockIdx.x;
+    for (int i = tid; i < dk; i += kThreads) {
+        qs[i] = to_f32(q[bh * dk + i]);
+        ks[i] = to_f32(k[bh * dk + i]);
+    }
+    for (int j = tid; j < dv; j += kThreads) vs[j] = to_f32(v[bh * dv + j]);
+    __syncthreads();
+
+    const int ncg = (dv + VW - 1) / VW;  // column groups
+    const int rg_n = kThreads / ncg;     // row groups
+    const int cg = tid % ncg, rg = tid / ncg;
+    const bool active = rg < rg_n;
+    const int j0 = cg * VW;
+    float* Sb = S + bh * (int64_t)dk * dv;
+
+    vecf vj;
+#pragma unroll
+    for (int u = 0; u < VW; ++u) vj[u] = (j0 + u < dv) ? vs[j0 + u] : 0.0f;
+    vecf acc = {};
+
+    if (active) {
+        for (int i0 = rg; i0 < dk; i0 += rg_n * RPT) {
+            vecf s[RPT];
+#pragma unroll
+            for (int m = 0; m < RPT; ++m) {
+                const int i = i0 + m * rg_n;
+                if (i < dk) {
+                    if constexpr (VW == 4)
+                        s[m] = __builtin_nontemporal_load(reinterpret_cast<const vecf*>(Sb + (int64_t)i * dv + j0));
+                    else
+                        s[m] = Sb[(int64_t)i * dv + j0];
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < RPT; ++m) {
+                const int i = i0 + m * rg_n;
+                if (i < dk) {
+                    const float ki = ks[i], qi = qs[i];
+#pragma unroll
+                    for (int u = 0; u < VW; ++u) {
+                        s[m][u] = fmaf(ki, vj[u], s[m][u]);  // rank-1 update
+                        acc[u] = fmaf(qi, s[m][u], acc[u]);  // state read
+                    }
+                    if constexpr (VW == 4)
+                        __builtin_nontemporal_store(s[m], reinterpret_cast<vecf*>(Sb + (int64_t)i * dv + j0));
+                    else
+                        Sb[(int64_t)i * dv + j0] = s[m][0];
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < VW; ++u) red[tid * VW + u] = active ? acc[u] : 0.0f;
+    __syncthreads();
+    // o[j] = sum over row groups, in row-group order
+    for (int j = tid; j < dv; j += kThreads) {
+        const int c = j / VW, u = j % VW;
+        float sum = 0.0f;
+        for (int r = 0; r < rg_n; ++r) sum += red[(r * ncg + c) * VW + u];
+        o[bh * dv + j] = sum;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_fill_zero(float* __restrict__ p, int64_t n) {
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if ((n & 3) == 0) {
+        f32x4* p4 = reinterpret_cast<f32x4*>(p);
+        for (; i < n / 4; i += stride) p4[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    } else {
+        for (; i < n; i += stride) p[i] = 0.0f;
+    }
+}
+
+template <typename Tin>
+static hipError_t decode_t(const void* q, const void* k, const void* v, int64_t BH, int dk,
+                           int dv, float* S, float* o, hipStream_t st) {
+    if ((dv & 3) == 0) {
+        // 256 threads = (dv/4) column groups x rg row groups; RPT rows each
+        // cover dk <= 128 in one batch when dv = 128 (8 row groups x 16).
+        hipLaunchKernelGGL((k_decode_step<Tin, 4, 16>), dim3((unsigned)BH), dim3(kThreads), 0, st,
+                           (const Tin*)q, (const Tin*)k, (const Tin*)v, S, o, dk, dv);
+    } else {
+        hipLaunchKernelGGL((k_decode_step<Tin, 1, 4>), dim3((unsigned)BH), dim3(kThreads), 0, st,
+                           (const Tin*)q, (const Tin*)k, (const Tin*)v, S, o, dk, dv);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_step(lla_dtype dtype, const void* q, const void* k, const void* v,
+                              int64_t BH, int dk, int dv, float* S, float* o, hipStream_t st) {
+    if (dtype == LLA_BF16) return decode_t<bf16>(q, k, v, BH, dk, dv, S, o, st);
+    return decode_t<float>(q, k, v, BH, dk, dv, S, o, st);
+}
+
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    int64_t work = (n & 3) == 0 ? n / 4 : n;
+    int64_t blocks = (work + kThreads - 1) / kThreads;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)blocks), dim3(kThreads), 0, st, p, n);
+    return hipGetLastError();
+}
+
+}  // namespace lla

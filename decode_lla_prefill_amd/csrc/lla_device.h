@@ -1,0 +1,110 @@
+// lla_device.h -- device-side building blocks shared by the HIP kernels of
+// liblla (gfx950 only): vector types, the 16x16 matrix-core step, bf16
+// rounding, and global->LDS tile staging.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lla {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kThreads = 256;  // four waves per workgroup
+constexpr int kWaves = kThreads / kWave;
+
+// One 32-deep slice of a 16x16 matrix-core product, held 8 elements per lane.
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { typedef bf16x8 type; };
+template <> struct Frag<float> { typedef f32x8 type; };
+
+// c += a * b for a 16x32 by 32x16 slice.  Lane l supplies row (of a) or
+// column (of b) l % 16 and eight depth slots; slot i of lane l pairs with
+// slot i of the lanes of the same group l / 16.  Any assignment of depth
+// indices to (group, slot) works as long as a and b use the same one.
+// Result layout: lane l holds rows 4*(l/16) + {0,1,2,3} of column l % 16.
+__device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(f32x8 a, f32x8 b, f32x4 c) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], c, 0, 0, 0);
+    return c;
+}
+
+__device__ __forceinline__ bf16 to_bf16(float x) { return (bf16)x; }  // round to nearest even
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+
+// Elements per 16-byte vector.
+template <typename T> struct Vec { static constexpr int n = 16 / sizeof(T); };
+
+// A ROWS x COLS tile of T staged in LDS with row stride LD (elements).
+//
+// Staging is split in two halves so that the global loads of the next tile
+// can be in flight while the current one is being used: gather() issues the
+// 16-byte loads into registers, scatter() writes them to LDS.  Rows at or past
+// `nrows`, and columns at or past `ncols`, are stored as zero.
+template <typename T, int ROWS, int COLS, int LD>
+struct Tile {
+    static constexpr int VE = Vec<T>::n;            // elements per vector
+    static constexpr int VPR = COLS / VE;           // vectors per row
+    static constexpr int NV = ROWS * VPR;           // vectors per tile
+    static constexpr int NPT = (NV + kThreads - 1) / kThreads;  // per thread
+    static_assert(COLS % VE == 0, "tile width must be a whole number of vectors");
+    static_assert(LD % (8 / sizeof(T)) == 0, "LDS rows must be 8-byte aligned");
+
+    u32x4 r[NPT];
+
+    // Vector path: global row stride `ld` is a multiple of VE and ncols % VE == 0.
+    __device__ __forceinline__ void gather(const T* __restrict__ g, int64_t ld, int nrows,
+                                           int ncols, int tid) {
+#pragma unroll
+        for (int n = 0; n < NPT; ++n) {
+            const int e = tid + n * kThreads;
+            const int row = e / VPR, cv = e % VPR;
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if (e < NV && row < nrows && cv * VE < ncols)
+                x = *reinterpret_cast<const u32x4*>(g + (int64_t)row * ld + cv * VE);
+            r[n] = x;
+        }
+    }
+    __device__ __forceinline__ void scatter(T* lds, int tid) const {
+#pragma unroll
+        for (int n = 0; n < NPT; ++n) {
+            const int e = tid + n * kThreads;
+            if (e < NV) {
+                const int row = e / VPR, cv = e % VPR;
+                T* p = lds + row * LD + cv * VE;
+                if constexpr ((LD * sizeof(T)) % 16 == 0) {
+                    *reinterpret_cast<u32x4*>(p) = r[n];
+                } else {
+                    reinterpret_cast<u32x2*>(p)[0] = u32x2{r[n][0], r[n][1]};
+                    reinterpret_cast<u32x2*>(p)[1] = u32x2{r[n][2], r[n][3]};
+                }
+            }
+        }
+    }
+    // Element path for shapes the vector path cannot take: straight to LDS.
+    __device__ __forceinline__ static void load_scalar(const T* __restrict__ g, int64_t ld,
+                                                       int nrows, int ncols, T* lds, int tid) {
+        for (int e = tid; e < ROWS * COLS; e += kThreads) {
+            const int row = e / COLS, col = e % COLS;
+            T x = from_f32<T>(0.0f);
+            if (row < nrows && col < ncols) x = g[(int64_t)row * ld + col];
+            lds[row * LD + col] = x;
+        }
+    }
+};
+
+}  // namespace lla

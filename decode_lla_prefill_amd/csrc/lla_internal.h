@@ -1,0 +1,45 @@
+// lla_internal.h -- host-side contract between the C ABI (lla_abi.cpp) and
+// the kernel launchers (lla_prefill.hip, lla_decode.hip).  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/lla.h"
+
+namespace lla {
+
+// Workgroups the chunk walk aims to launch: two per compute unit of a
+// 256-CU MI355X.  A constant (not a device query) so that the segmentation,
+// and therefore the rounding order, depends on the shape alone.
+constexpr int64_t kTargetWalkers = 512;
+
+// Everything the launchers need about a prefill shape, derived once on the
+// host from the user's sizes.
+struct PrefillPlan {
+    int64_t B, H, BH, T;
+    int dk, dv, C;
+    int D;        // padded head dim (32, 64 or 128) used for both dk and dv
+    int CT;       // padded chunk tile (32, 64 or 128 rows)
+    int64_t n_c;  // chunks per sequence = ceil(T / C)
+    int64_t G;    // chunks per segment (walked by one workgroup)
+    int64_t n_seg;  // segments per sequence = ceil(n_c / G)
+    bool vec;     // 16-byte vector loads possible (dk, dv multiples of one vector)
+    lla_dtype dtype;
+};
+
+// Fills the derived fields from B, H, T, dk, dv, C, dtype (already validated).
+void plan_prefill(PrefillPlan& p);
+
+hipError_t launch_segment_states(const PrefillPlan& p, const void* K, const void* V,
+                                 float* ws, hipStream_t st);
+hipError_t launch_state_scan(const PrefillPlan& p, const float* S, float* ws, hipStream_t st);
+hipError_t launch_chunk_walk(const PrefillPlan& p, const void* Q, const void* K, const void* V,
+                             float* S, float* O, float* ws, hipStream_t st);
+
+hipError_t launch_decode_step(lla_dtype dtype, const void* q, const void* k, const void* v,
+                              int64_t BH, int dk, int dv, float* S, float* o, hipStream_t st);
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
+
+}  // namespace lla

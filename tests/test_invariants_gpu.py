@@ -1,0 +1,136 @@
+"""GPU invariants the deck states, and the prefill phases, through the C ABI.
+
+* chunking is exact: every C gives the same result (deck, "Common errors");
+* the state is the one object handed between blocks: prefill(T1) then
+  prefill(T2) from its state equals prefill(T1 + T2); prefill then decode
+  steps equals a longer prefill (deck, "Prefill and decode": two code paths,
+  the same numbers);
+* the three phases called one by one equal lla_prefill, and the workspace
+  holds the state at every segment start;
+* repeat runs are bitwise identical; every output element is written.
+"""
+import numpy as np
+import pytest
+import torch
+
+import decode_lla_prefill_amd as lla
+import oracle
+import workloads
+from gpu_util import TOL, gpu_prefill, need_gpu, np64, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return need_gpu()
+
+
+def test_chunk_size_invariance_integers(dev):
+    q, k, v = workloads.integers(2, 3, 1500, 128, 128, seed=9)
+    ref = None
+    for C in (1, 5, 16, 32, 48, 64, 100, 128):
+        o, S = gpu_prefill(q, k, v, C=C)
+        if ref is None:
+            ref = (np64(o), np64(S))
+            O_ref, S_ref = oracle.recurrence(q, k, v, nthreads=6)
+            assert np.array_equal(ref[0], O_ref) and np.array_equal(ref[1], S_ref)
+        else:
+            assert np.array_equal(np64(o), ref[0]), C
+            assert np.array_equal(np64(S), ref[1]), C
+
+
+def test_chunk_size_invariance_long_prompt_all_heads(dev):
+    """The T=131072 shape at C = 64 and C = 128: every head agrees within the
+    tolerance (the oracle checks sampled heads in the parity suite)."""
+    cfg = workloads.CONFIGS["c4"]
+    q, k, v = workloads.config_inputs(cfg, device=dev)
+    o1, S1 = gpu_prefill(q, k, v, C=128)
+    o2, S2 = gpu_prefill(q, k, v, C=64)
+    e_o = (o1 - o2).abs().max().item() / o1.abs().max().item()
+    e_s = (S1 - S2).abs().max().item() / S1.abs().max().item()
+    assert e_o <= TOL and e_s <= TOL
+
+
+def test_continuation_prefill_then_prefill(dev):
+    q, k, v = workloads.integers(1, 4, 2500, 64, 64, seed=12)
+    o_all, S_all = gpu_prefill(q, k, v, C=64)
+    o1, S1 = gpu_prefill(q[:, :, :1111], k[:, :, :1111], v[:, :, :1111], C=64)
+    o2, S2 = gpu_prefill(q[:, :, 1111:], k[:, :, 1111:], v[:, :, 1111:], C=64, S0=S1)
+    assert torch.equal(torch.cat([o1, o2], 2), o_all) and torch.equal(S2, S_all)
+
+
+def test_prefill_then_decode_equals_longer_prefill(dev):
+    q, k, v = workloads.integers(2, 4, 520, 128, 128, seed=13)
+    o_all, S_all = gpu_prefill(q, k, v, C=64)
+    o_pre, S = gpu_prefill(q[:, :, :500], k[:, :, :500], v[:, :, :500], C=64)
+    for t in range(500, 520):
+        o = lla.decode_step(q[:, :, t].contiguous().to(dev), k[:, :, t].contiguous().to(dev),
+                            v[:, :, t].contiguous().to(dev), S)
+        assert torch.equal(o, o_all[:, :, t]), t
+    assert torch.equal(S, S_all)
+
+
+def test_phases_equal_prefill_and_workspace_holds_segment_states(dev):
+    B, H, T, d, C = 1, 2, 64 * 600, 64, 64
+    q, k, v = (x.to(dev) for x in workloads.integers(B, H, T, d, d, seed=14))
+    G = lla.prefill_segment_chunks(B, H, T, d, d, C)
+    n_c = -(-T // C)
+    n_seg = -(-n_c // G)
+    assert G > 1 and n_seg > 1
+    S_a = lla.state_init(B, H, d, d, device=dev)
+    o_a = lla.prefill(q, k, v, S_a, chunk=C)
+    S_b = lla.state_init(B, H, d, d, device=dev)
+    ws = lla.prefill_segment_states(k, v, C, None)
+    lla.prefill_state_scan(S_b, T, C, ws)
+    o_b = lla.prefill_chunks(q, k, v, S_b, C, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, o_b) and torch.equal(S_a, S_b)
+    slots = np64(ws.view(B, H, n_seg, d, d))
+    _, _, ck = oracle.recurrence(q.cpu(), k.cpu(), v.cpu(), ckpt_every=G * C, nthreads=2)
+    assert np.array_equal(slots[:, :, 0], np.zeros((B, H, d, d)))
+    assert np.array_equal(slots[:, :, 1:], ck[:, :, :n_seg - 1])
+
+
+def test_repeat_runs_are_bitwise_identical_and_outputs_fully_written(dev):
+    cfg = workloads.CONFIGS["c3"]
+    q, k, v = (x.to(dev) for x in workloads.config_inputs(cfg))
+    outs = []
+    for _ in range(2):
+        S = lla.state_init(cfg.B, cfg.H, cfg.dk, cfg.dv, device=dev)
+        o = torch.full((cfg.B, cfg.H, cfg.T, cfg.dv), float("nan"), device=dev)
+        lla.prefill(q, k, v, S, chunk=cfg.C, out=o)
+        torch.cuda.synchronize()
+        assert not torch.isnan(o).any()
+        outs.append((o, S))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def test_empty_prompt_is_a_no_op(dev):
+    S = torch.arange(2 * 3 * 8 * 8, dtype=torch.float32, device=dev).view(2, 3, 8, 8)
+    S0 = S.clone()
+    e = torch.empty((2, 3, 0, 8), dtype=torch.bfloat16, device=dev)
+    o = lla.prefill(e, e, e, S, chunk=4)
+    torch.cuda.synchronize()
+    assert o.shape == (2, 3, 0, 8) and torch.equal(S, S0)
+
+
+def test_state_init_zeroes(dev):
+    S = torch.full((3, 5, 7, 9), 7.0, device=dev)
+    lla.state_init(3, 5, 7, 9, out=S)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(S).item() == 0
+
+
+def test_bad_arguments_raise_before_launch(dev):
+    q = torch.zeros((1, 1, 64, 64), dtype=torch.bfloat16, device=dev)
+    S = lla.state_init(1, 1, 64, 64, device=dev)
+    with pytest.raises(lla.LlaError):
+        lla.prefill(q, q, q, S, chunk=0)
+    with pytest.raises(lla.LlaError):
+        lla.prefill(q, q, q, S, chunk=129)
+    qf = q.float()
+    with pytest.raises(lla.LlaError):
+        lla.prefill(qf, qf, qf, S, chunk=128)  # fp32 needs C <= 64
+    with pytest.raises(TypeError):
+        lla.prefill(q.half(), q.half(), q.half(), S, chunk=64)
