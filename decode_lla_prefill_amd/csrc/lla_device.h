@@ -49,20 +49,28 @@ template <> __device__ __forceinline__ float from_f32<float>(float x) { return x
 // Elements per 16-byte vector.
 template <typename T> struct Vec { static constexpr int n = 16 / sizeof(T); };
 
-// A ROWS x COLS tile of T staged in LDS with row stride LD (elements).
+// ---- LDS tile layouts: (row, col) -> element offset ---------------------------
+
+// Plain row-major tile with LD elements per row (LD a multiple of 4).
+template <int LD>
+struct PadLayout {
+    static constexpr int kRowElems = LD;
+    __device__ __forceinline__ static int off(int row, int col) { return row * LD + col; }
+};
+
+// A ROWS x COLS tile of T staged in LDS with layout L.
 //
 // Staging is split in two halves so that the global loads of the next tile
 // can be in flight while the current one is being used: gather() issues the
 // 16-byte loads into registers, scatter() writes them to LDS.  Rows at or past
 // `nrows`, and columns at or past `ncols`, are stored as zero.
-template <typename T, int ROWS, int COLS, int LD>
+template <typename T, int ROWS, int COLS, typename L>
 struct Tile {
     static constexpr int VE = Vec<T>::n;            // elements per vector
     static constexpr int VPR = COLS / VE;           // vectors per row
     static constexpr int NV = ROWS * VPR;           // vectors per tile
     static constexpr int NPT = (NV + kThreads - 1) / kThreads;  // per thread
     static_assert(COLS % VE == 0, "tile width must be a whole number of vectors");
-    static_assert(LD % (8 / sizeof(T)) == 0, "LDS rows must be 8-byte aligned");
 
     u32x4 r[NPT];
 
@@ -85,13 +93,7 @@ struct Tile {
             const int e = tid + n * kThreads;
             if (e < NV) {
                 const int row = e / VPR, cv = e % VPR;
-                T* p = lds + row * LD + cv * VE;
-                if constexpr ((LD * sizeof(T)) % 16 == 0) {
-                    *reinterpret_cast<u32x4*>(p) = r[n];
-                } else {
-                    reinterpret_cast<u32x2*>(p)[0] = u32x2{r[n][0], r[n][1]};
-                    reinterpret_cast<u32x2*>(p)[1] = u32x2{r[n][2], r[n][3]};
-                }
+                *reinterpret_cast<u32x4*>(lds + L::off(row, cv * VE)) = r[n];
             }
         }
     }
@@ -102,7 +104,7 @@ struct Tile {
             const int row = e / COLS, col = e % COLS;
             T x = from_f32<T>(0.0f);
             if (row < nrows && col < ncols) x = g[(int64_t)row * ld + col];
-            lds[row * LD + col] = x;
+            lds[L::off(row, col)] = x;
         }
     }
 };

@@ -13,7 +13,10 @@ namespace lla {
 // Workgroups the chunk walk aims to launch: two per compute unit of a
 // 256-CU MI355X.  A constant (not a device query) so that the segmentation,
 // and therefore the rounding order, depends on the shape alone.
-constexpr int64_t kTargetWalkers = 512;
+#ifndef LLA_TARGET_WALKERS
+#define LLA_TARGET_WALKERS 512
+#endif
+constexpr int64_t kTargetWalkers = LLA_TARGET_WALKERS;
 
 // Everything the launchers need about a prefill shape, derived once on the
 // host from the user's sizes.
@@ -22,6 +25,8 @@ struct PrefillPlan {
     int dk, dv, C;
     int D;        // padded head dim (32, 64 or 128) used for both dk and dv
     int CT;       // padded chunk tile (32, 64 or 128 rows)
+    int BV;       // value columns per workgroup (D, or 64 when D = 128)
+    int n_vb;     // value-column blocks = D / BV
     int64_t n_c;  // chunks per sequence = ceil(T / C)
     int64_t G;    // chunks per segment (walked by one workgroup)
     int64_t n_seg;  // segments per sequence = ceil(n_c / G)

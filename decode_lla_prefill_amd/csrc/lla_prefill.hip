@@ -7,23 +7,25 @@
 // only the chunk-to-chunk state hop is serial.
 //
 // Three kernels:
-//   k_segment_states : per (b,h) and segment of G chunks, the increment
-//                      K_seg^T V_seg (fp32, matrix cores).
+//   k_segment_states : per (b,h), segment of G chunks and block of value
+//                      columns, the increment K_seg^T V_seg (fp32, matrix cores).
 //   k_state_scan     : exclusive prefix over segments -> the state each
 //                      segment starts from (the serial hop, one add per
 //                      segment instead of one per chunk).
-//   k_chunk_walk     : one workgroup per (b,h,segment) walks its G chunks with
-//                      the fp32 state in registers: scores on matrix cores,
-//                      causal mask in registers, masked scores times V plus
-//                      Q times the state (state split into bf16 high + low
-//                      parts), then the state hop K_c^T V_c.
+//   k_chunk_walk     : one workgroup per (b,h), segment and block of value
+//                      columns walks its G chunks with the fp32 state slice
+//                      in registers: scores on matrix cores, causal mask in
+//                      registers, masked scores times V plus Q times the state
+//                      (state split into bf16 high + low parts), then the
+//                      state hop K_c^T V_c.
 //
-// Matrix-core layout used throughout (16x16 tiles, 32-deep steps): see
-// lla::mma.  The score tile is computed transposed (keys as rows), so that a
-// lane ends up holding four consecutive key columns of one query row: those
-// are stored to LDS as one 8-byte write, and the output tile is computed
-// transposed as well (values as rows), so a lane holds four consecutive
-// output columns: one 16-byte global store.
+// Matrix-core layout (16x16 tiles, 32-deep steps): see lla::mma.  The score
+// tile is computed transposed (keys as rows) so that a lane holds four
+// consecutive key columns of one query row -- one 8-byte LDS write -- and the
+// output tile is computed transposed (values as rows) so that a lane holds
+// four consecutive output columns -- one 16-byte global store.  Operands that
+// contract over time (K^T in the state hop, V everywhere) are read from the
+// row-major LDS tiles with the gfx950 LDS transpose read (lla::lds_col).
 #include "lla_device.h"
 #include "lla_internal.h"
 
@@ -31,50 +33,96 @@
 
 namespace lla {
 
-template <typename T, int CT_, int D_>
+template <typename T, int CT_, int D_, int BV_>
 struct WalkCfg {
-    static constexpr int CT = CT_, D = D_;
+    static constexpr int CT = CT_, D = D_, BV = BV_;
     static constexpr bool BF = std::is_same<T, bf16>::value;
-    static constexpr int LQ = D + (BF ? 8 : 4);   // Q/K LDS row stride: 16-byte rows
-    static constexpr int LV = D + (BF ? 4 : 2);   // V LDS row stride: 8-byte rows, bank skew
-    static constexpr int LP = CT + (BF ? 8 : 4);  // score LDS row stride
-    static constexpr int NT = CT / 16;            // 16-row tiles per chunk
-    static constexpr int NTS = CT / 32;           // 32-deep time steps per chunk
-    static constexpr int NDT = D / 16;            // 16-wide tiles over the head dim
-    static constexpr int NDS = D / 32;            // 32-deep steps over the head dim
-    static constexpr int NVW = (NDT + kWaves - 1) / kWaves;  // value tiles per wave
+    // LDS row strides (elements), chosen for the 64 four-byte LDS banks:
+    //  Q: 4 (mod 8) dwords -- 16-byte reads of 16 rows and 8-byte reads of
+    //     16 rows x 2 halves hit distinct banks;
+    //  K, V: 8 (mod 16) dwords -- a transpose read by two 16-lane groups
+    //     covers 8 consecutive rows x 32 bytes, on distinct banks;
+    //  P: 4 (mod 8) dwords -- its 8-byte writes and reads are conflict-free.
+    static constexpr int LQ = D + (BF ? 8 : 4);
+    static constexpr int LK = D + (BF ? 16 : 4);
+    static constexpr int LV = BV + (BF ? 16 : 4);
+    static constexpr int LP = CT + (BF ? 8 : 4);
+    using LQL = PadLayout<LQ>;
+    using LKL = PadLayout<LK>;
+    using LVL = PadLayout<LV>;
+    // One LDS buffer per workgroup: the Q, K, V and score tiles during the
+    // walk; the fp32 state slice (D x BV, row stride SLD) before and after it.
+    static constexpr int K_OFF = CT * LQ, V_OFF = K_OFF + CT * LK, P_OFF = V_OFF + CT * LV;
+    static constexpr int SLD = BV + 4;
+    static constexpr int STATE_BYTES = D * SLD * 4;
+    static constexpr int WALK_BYTES = (P_OFF + CT * LP) * (int)sizeof(T) > STATE_BYTES
+                                          ? (P_OFF + CT * LP) * (int)sizeof(T) : STATE_BYTES;
+    static constexpr int SEG_TILES = (CT * LK + CT * LV) * (int)sizeof(T);
+    static constexpr int SEG_BYTES = SEG_TILES > STATE_BYTES ? SEG_TILES : STATE_BYTES;
+    static constexpr int NT = CT / 16;              // 16-row tiles per chunk
+    static constexpr int NTS = CT / 32;             // 32-deep time steps per chunk
+    static constexpr int NDT = D / 16;              // 16-wide tiles over the key dim
+    static constexpr int NDS = D / 32;              // 32-deep steps over the key dim
+    static constexpr int NVT = BV / 16;             // value tiles in the block
+    static constexpr int NVW = (NVT + kWaves - 1) / kWaves;  // value tiles per wave
+    static constexpr bool ALL_WAVES = NVT % kWaves == 0;     // every wave owns tiles
     static constexpr int NTRI = NT * (NT + 1) / 2;           // lower-triangle tiles
     using Fr = typename Frag<T>::type;
 };
 
-// 8 consecutive elements from LDS (16-byte aligned) as one operand slice.
-__device__ __forceinline__ bf16x8 lds_frag(const bf16* p) {
+// ---- LDS operand reads -------------------------------------------------------
+
+// 8 consecutive elements of one row (the depth index runs along the row).
+__device__ __forceinline__ bf16x8 lds_row(const bf16* p) {
     return *reinterpret_cast<const bf16x8*>(p);
 }
-__device__ __forceinline__ f32x8 lds_frag(const float* p) {
+__device__ __forceinline__ f32x8 lds_row(const float* p) {
     const f32x4 a = reinterpret_cast<const f32x4*>(p)[0];
     const f32x4 b = reinterpret_cast<const f32x4*>(p)[1];
     return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
-// 4 + 4 elements from two 8-byte aligned LDS addresses.
-__device__ __forceinline__ bf16x8 lds_frag2(const bf16* p0, const bf16* p1) {
+// 4 + 4 elements of one row from two 8-byte aligned addresses.
+__device__ __forceinline__ bf16x8 lds_row2(const bf16* p0, const bf16* p1) {
     const bf16x4 a = *reinterpret_cast<const bf16x4*>(p0);
     const bf16x4 b = *reinterpret_cast<const bf16x4*>(p1);
     return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
-__device__ __forceinline__ f32x8 lds_frag2(const float* p0, const float* p1) {
+__device__ __forceinline__ f32x8 lds_row2(const float* p0, const float* p1) {
     const f32x4 a = *reinterpret_cast<const f32x4*>(p0);
     const f32x4 b = *reinterpret_cast<const f32x4*>(p1);
     return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
-// 8 elements down a column (stride `ld` elements).
-template <typename T>
-__device__ __forceinline__ typename Frag<T>::type lds_col(const T* p, int ld) {
-    typename Frag<T>::type f;
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Operand slice down one column of a row-major tile (row stride ld): lane
+// (group g, column c16) gets, in slots s = 0..3 and 4..7, the elements
+// M[row0 + 4g + s][col0 + c16] and M[row0 + 16 + 4g + (s - 4)][col0 + c16]
+// -- the interleaved depth order used by every product that contracts over
+// time.  bf16 uses the LDS transpose read: within a 16-lane group, lanes
+// 4r..4r+3 address row r of a 4x16 block and lane i receives column i; the
+// two groups that share an LDS pass then read 8 consecutive rows.
+__device__ __forceinline__ bf16x8 lds_col(const bf16* base, int ld, int row0, int col0, int lane) {
+    const int r = (lane >> 2) & 3, j = lane & 3, g = lane >> 4;
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const bf16* p0 = base + (row0 + 4 * g + r) * ld + col0 + 4 * j;
+    const bf16* p1 = p0 + 16 * ld;
+    const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(const_cast<bf16*>(p0)));
+    const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(const_cast<bf16*>(p1)));
+    const bf16x4 ab = __builtin_bit_cast(bf16x4, a), bb = __builtin_bit_cast(bf16x4, b);
+    return bf16x8{ab[0], ab[1], ab[2], ab[3], bb[0], bb[1], bb[2], bb[3]};
+}
+__device__ __forceinline__ f32x8 lds_col(const float* base, int ld, int row0, int col0, int lane) {
+    const float* p = base + (row0 + 4 * (lane >> 4)) * ld + col0 + (lane & 15);
+    f32x8 f;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) f[s] = p[s * ld];
+    for (int s = 0; s < 4; ++s) {
+        f[s] = p[s * ld];
+        f[4 + s] = p[(16 + s) * ld];
+    }
     return f;
 }
+
 __device__ __forceinline__ void lds_store4(bf16* p, f32x4 x) {
     *reinterpret_cast<bf16x4*>(p) = bf16x4{to_bf16(x[0]), to_bf16(x[1]), to_bf16(x[2]), to_bf16(x[3])};
 }
@@ -82,56 +130,150 @@ __device__ __forceinline__ void lds_store4(float* p, f32x4 x) {
     *reinterpret_cast<f32x4*>(p) = x;
 }
 
-// State hop for the tiles a wave owns: S[:, value tile w + 4*vw] += K^T V,
-// contracting over the CT rows (time) of the staged tiles.
-template <typename Cf, typename T>
-__device__ __forceinline__ void state_hop(f32x4 (&Sacc)[Cf::NVW][Cf::NDT],
-                                          const typename Cf::Fr (&Vf)[Cf::NVW][Cf::NTS],
-                                          const T* Ks, int w, int g, int c16) {
-#pragma unroll
-    for (int dt = 0; dt < Cf::NDT; ++dt) {
-#pragma unroll
-        for (int ts = 0; ts < Cf::NTS; ++ts) {
-            const typename Cf::Fr kt = lds_col(Ks + (32 * ts + 8 * g) * Cf::LQ + 16 * dt + c16, Cf::LQ);
-#pragma unroll
-            for (int vw = 0; vw < Cf::NVW; ++vw)
-                if (w + kWaves * vw < Cf::NDT) Sacc[vw][dt] = mma(kt, Vf[vw][ts], Sacc[vw][dt]);
-        }
-    }
+// ---- work mapping ---------------------------------------------------------------
+
+// Workgroup id -> (line, value block), where a "line" is one (b,h,segment).
+// Consecutive ids go round-robin over the 8 XCDs, so the value blocks of one
+// line get ids congruent mod 8: they share an XCD and its L2, where the
+// second block's Q and K reads hit.
+__device__ __forceinline__ void split_id(int64_t id, int64_t n_lines, int n_vb, int64_t& line,
+                                         int& vb) {
+    const int64_t per = 8 * (int64_t)n_vb;
+    const int64_t grp = id / per, off = id - grp * per;
+    const int64_t r = min((int64_t)8, n_lines - 8 * grp);
+    vb = (int)(off / r);
+    line = 8 * grp + off % r;
 }
 
-// The value-column operand slices of a wave: V[32*ts + 8g + s][16*vt + c16].
+// The value-column operand slices of a wave: V[32 ts + (time slot)][16 vt + c16].
 template <typename Cf, typename T>
 __device__ __forceinline__ void load_vfrags(typename Cf::Fr (&Vf)[Cf::NVW][Cf::NTS], const T* Vs,
-                                            int w, int g, int c16) {
+                                            int w, int g, int lane) {
 #pragma unroll
     for (int vw = 0; vw < Cf::NVW; ++vw) {
         const int vt = w + kWaves * vw;
 #pragma unroll
         for (int ts = 0; ts < Cf::NTS; ++ts)
-            if (vt < Cf::NDT) Vf[vw][ts] = lds_col(Vs + (32 * ts + 8 * g) * Cf::LV + 16 * vt + c16, Cf::LV);
+            if (Cf::ALL_WAVES || vt < Cf::NVT)
+                Vf[vw][ts] = lds_col(Vs, Cf::LV, 32 * ts, 16 * vt, lane);
+    }
+}
+
+// The fp32 state slice moves between global memory and registers through
+// LDS: coalesced 16-byte global accesses on one side, the matrix-core
+// accumulator layout (lane (g, c16) holds S[16 dt + 4g + r][16 vt + c16]) on
+// the other.  Rows d >= dk and columns >= nv read as zero and are not written.
+template <typename Cf>
+__device__ __forceinline__ void state_gmem_to_lds(float* lds, const float* g, int dk, int dv,
+                                                  int nv, int tid) {
+    constexpr int VPR = Cf::BV / 4;
+    if ((dv & 3) == 0) {
+        for (int e = tid; e < Cf::D * VPR; e += kThreads) {
+            const int d = e / VPR, c = 4 * (e % VPR);
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+            if (d < dk && c < nv) x = *reinterpret_cast<const f32x4*>(g + (int64_t)d * dv + c);
+            *reinterpret_cast<f32x4*>(lds + d * Cf::SLD + c) = x;
+        }
+    } else {
+        for (int e = tid; e < Cf::D * Cf::BV; e += kThreads) {
+            const int d = e / Cf::BV, c = e % Cf::BV;
+            lds[d * Cf::SLD + c] = (d < dk && c < nv) ? g[(int64_t)d * dv + c] : 0.0f;
+        }
+    }
+}
+template <typename Cf>
+__device__ __forceinline__ void state_lds_to_gmem(float* g, const float* lds, int dk, int dv,
+                                                  int nv, int tid) {
+    constexpr int VPR = Cf::BV / 4;
+    if ((dv & 3) == 0) {
+        for (int e = tid; e < Cf::D * VPR; e += kThreads) {
+            const int d = e / VPR, c = 4 * (e % VPR);
+            if (d < dk && c < nv)
+                *reinterpret_cast<f32x4*>(g + (int64_t)d * dv + c) =
+                    *reinterpret_cast<const f32x4*>(lds + d * Cf::SLD + c);
+        }
+    } else {
+        for (int e = tid; e < Cf::D * Cf::BV; e += kThreads) {
+            const int d = e / Cf::BV, c = e % Cf::BV;
+            if (d < dk && c < nv) g[(int64_t)d * dv + c] = lds[d * Cf::SLD + c];
+        }
+    }
+}
+template <typename Cf>
+__device__ __forceinline__ void state_lds_to_regs(f32x4 (&Sacc)[Cf::NVW][Cf::NDT], const float* lds,
+                                                  int w, int g, int c16) {
+#pragma unroll
+    for (int vw = 0; vw < Cf::NVW; ++vw) {
+        const int vt = (Cf::ALL_WAVES || w + kWaves * vw < Cf::NVT) ? w + kWaves * vw : 0;
+#pragma unroll
+        for (int dt = 0; dt < Cf::NDT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                Sacc[vw][dt][r] = lds[(16 * dt + 4 * g + r) * Cf::SLD + 16 * vt + c16];
+    }
+}
+template <typename Cf>
+__device__ __forceinline__ void state_regs_to_lds(float* lds, const f32x4 (&Sacc)[Cf::NVW][Cf::NDT],
+                                                  int w, int g, int c16) {
+#pragma unroll
+    for (int vw = 0; vw < Cf::NVW; ++vw) {
+        if (!(Cf::ALL_WAVES || w + kWaves * vw < Cf::NVT)) continue;
+        const int vt = w + kWaves * vw;
+#pragma unroll
+        for (int dt = 0; dt < Cf::NDT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                lds[(16 * dt + 4 * g + r) * Cf::SLD + 16 * vt + c16] = Sacc[vw][dt][r];
+    }
+}
+
+// State hop for the tiles a wave owns: S[:, value tile w + 4 vw] += K^T V,
+// contracting over the CT rows (time) of the staged tiles.
+template <typename Cf, typename T>
+__device__ __forceinline__ void state_hop(f32x4 (&Sacc)[Cf::NVW][Cf::NDT],
+                                          const typename Cf::Fr (&Vf)[Cf::NVW][Cf::NTS],
+                                          const T* Ks, int w, int g, int lane) {
+#pragma unroll
+    for (int dt = 0; dt < Cf::NDT; ++dt) {
+#pragma unroll
+        for (int ts = 0; ts < Cf::NTS; ++ts) {
+            const typename Cf::Fr kt = lds_col(Ks, Cf::LK, 32 * ts, 16 * dt, lane);
+#pragma unroll
+            for (int vw = 0; vw < Cf::NVW; ++vw)
+                if (Cf::ALL_WAVES || w + kWaves * vw < Cf::NVT)
+                    Sacc[vw][dt] = mma(kt, Vf[vw][ts], Sacc[vw][dt]);
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
-// Phase 1: per-segment state increments K_seg^T V_seg -> ws slot seg + 1.
+// Phase 1: per-segment state increments K_seg^T V_seg -> ws slot seg + 1,
+// one workgroup per (b,h), segment (all but the last) and value block.
 // ---------------------------------------------------------------------------
-template <typename T, int CT, int D>
+template <typename T, int CT, int D, int BV, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_segment_states(
     const T* __restrict__ K, const T* __restrict__ V, float* __restrict__ ws, int64_t T_len,
-    int dk, int dv, int C, int64_t G, int64_t n_seg, int vec) {
-    using Cf = WalkCfg<T, CT, D>;
+    int dk, int dv, int C, int64_t G, int64_t n_seg, int n_vb) {
+    using Cf = WalkCfg<T, CT, D, BV>;
     using Fr = typename Cf::Fr;
-    __shared__ __attribute__((aligned(16))) T Ks[CT * Cf::LQ];
-    __shared__ __attribute__((aligned(16))) T Vs[CT * Cf::LV];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Cf::SEG_BYTES];
+    T* Ks = reinterpret_cast<T*>(smem);
+    T* Vs = Ks + CT * Cf::LK;
+    float* Sst = reinterpret_cast<float*>(smem);
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c16 = lane & 15;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t nsm1 = n_seg - 1;
-    const int64_t bh = blockIdx.x / nsm1, seg = blockIdx.x % nsm1;
+    int64_t line;
+    int vb;
+    split_id(blockIdx.x, (int64_t)(gridDim.x / n_vb), n_vb, line, vb);
+    const int64_t bh = line / nsm1, seg = line - bh * nsm1;
+    const int v0 = vb * BV;
+    const int nv = min(BV, dv - v0);
     const int64_t n_c = (T_len + C - 1) / C;
     const int64_t c0 = seg * G, c1 = min(n_c, c0 + G);
     const T* Kb = K + bh * T_len * dk;
-    const T* Vb = V + bh * T_len * dv;
+    const T* Vb = V + bh * T_len * dv + v0;
 
     f32x4 Sacc[Cf::NVW][Cf::NDT];
 #pragma unroll
@@ -139,44 +281,38 @@ __global__ __launch_bounds__(kThreads) void k_segment_states(
 #pragma unroll
         for (int dt = 0; dt < Cf::NDT; ++dt) Sacc[vw][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    Tile<T, CT, D, Cf::LQ> tk;
-    Tile<T, CT, D, Cf::LV> tv;
+    Tile<T, CT, D, typename Cf::LKL> tk;
+    Tile<T, CT, BV, typename Cf::LVL> tv;
     auto rows_of = [&](int64_t c) { return (int)min((int64_t)C, T_len - c * C); };
-    if (vec) {
+    if constexpr (VEC) {
         tk.gather(Kb + c0 * C * dk, dk, rows_of(c0), dk, tid);
-        tv.gather(Vb + c0 * C * dv, dv, rows_of(c0), dv, tid);
+        tv.gather(Vb + c0 * C * dv, dv, rows_of(c0), nv, tid);
     }
     for (int64_t c = c0; c < c1; ++c) {
-        if (vec) {
+        if constexpr (VEC) {
             tk.scatter(Ks, tid);
             tv.scatter(Vs, tid);
         } else {
-            Tile<T, CT, D, Cf::LQ>::load_scalar(Kb + c * C * dk, dk, rows_of(c), dk, Ks, tid);
-            Tile<T, CT, D, Cf::LV>::load_scalar(Vb + c * C * dv, dv, rows_of(c), dv, Vs, tid);
+            Tile<T, CT, D, typename Cf::LKL>::load_scalar(Kb + c * C * dk, dk, rows_of(c), dk, Ks, tid);
+            Tile<T, CT, BV, typename Cf::LVL>::load_scalar(Vb + c * C * dv, dv, rows_of(c), nv, Vs, tid);
         }
         __syncthreads();
-        if (vec && c + 1 < c1) {
-            tk.gather(Kb + (c + 1) * C * dk, dk, rows_of(c + 1), dk, tid);
-            tv.gather(Vb + (c + 1) * C * dv, dv, rows_of(c + 1), dv, tid);
+        if constexpr (VEC) {
+            if (c + 1 < c1) {
+                tk.gather(Kb + (c + 1) * C * dk, dk, rows_of(c + 1), dk, tid);
+                tv.gather(Vb + (c + 1) * C * dv, dv, rows_of(c + 1), nv, tid);
+            }
         }
         Fr Vf[Cf::NVW][Cf::NTS];
-        load_vfrags<Cf>(Vf, Vs, w, g, c16);
-        state_hop<Cf>(Sacc, Vf, Ks, w, g, c16);
+        load_vfrags<Cf>(Vf, Vs, w, g, lane);
+        state_hop<Cf>(Sacc, Vf, Ks, w, g, lane);
         __syncthreads();
     }
 
-    float* out = ws + (bh * n_seg + seg + 1) * (int64_t)dk * dv;
-#pragma unroll
-    for (int vw = 0; vw < Cf::NVW; ++vw) {
-        const int v = 16 * (w + kWaves * vw) + c16;
-#pragma unroll
-        for (int dt = 0; dt < Cf::NDT; ++dt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int d = 16 * dt + 4 * g + r;
-                if (d < dk && v < dv) out[(int64_t)d * dv + v] = Sacc[vw][dt][r];
-            }
-    }
+    // (the loop ended with a barrier: the tiles are free)
+    state_regs_to_lds<Cf>(Sst, Sacc, w, g, c16);
+    __syncthreads();
+    state_lds_to_gmem<Cf>(ws + (bh * n_seg + seg + 1) * (int64_t)dk * dv + v0, Sst, dk, dv, nv, tid);
 }
 
 // ---------------------------------------------------------------------------
@@ -221,75 +357,112 @@ __global__ __launch_bounds__(kThreads) void k_state_scan(const float* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// Phase 3: the chunk walk.  One workgroup per (b,h,segment); four waves; the
-// fp32 state of the whole head lives in registers, split over the waves by
-// value columns (wave w owns value tiles w, w+4, ...).
+// Phase 3: the chunk walk.  One workgroup per (b,h), segment and block of BV
+// value columns; four waves; the fp32 state slice S[:, block] lives in
+// registers, split over the waves by value tiles (wave w owns tiles w, w+4..).
 // ---------------------------------------------------------------------------
-template <typename T, int CT, int D>
+// Writes a chunk's output tiles held by a wave: Oacc[it][vw] holds
+// O[t0 + 16 it + c16][v0 + 16 vt + 4g + r], r = 0..3 (vt = w + 4 vw).
+template <typename Cf, bool VEC>
+__device__ __forceinline__ void store_out(float* Ob, const f32x4 (&Oacc)[Cf::NT][Cf::NVW], int64_t t0,
+                                          int nrows, int nv, int dv, int w, int g, int c16) {
+#pragma unroll
+    for (int it = 0; it < Cf::NT; ++it) {
+        const int i = 16 * it + c16;
+        if (i >= nrows) continue;
+        float* orow = Ob + (t0 + i) * dv;
+#pragma unroll
+        for (int vw = 0; vw < Cf::NVW; ++vw) {
+            const int v = 16 * (w + kWaves * vw) + 4 * g;
+            if (!(Cf::ALL_WAVES || w + kWaves * vw < Cf::NVT) || v >= nv) continue;
+            if constexpr (VEC) {
+                *reinterpret_cast<f32x4*>(orow + v) = Oacc[it][vw];
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (v + r < nv) orow[v + r] = Oacc[it][vw][r];
+            }
+        }
+    }
+}
+
+template <typename T, int CT, int D, int BV, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_chunk_walk(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     float* __restrict__ S, float* __restrict__ O, const float* __restrict__ ws, int64_t T_len,
-    int dk, int dv, int C, int64_t G, int64_t n_seg, int vec) {
-    using Cf = WalkCfg<T, CT, D>;
+    int dk, int dv, int C, int64_t G, int64_t n_seg, int n_vb) {
+    using Cf = WalkCfg<T, CT, D, BV>;
     using Fr = typename Cf::Fr;
-    __shared__ __attribute__((aligned(16))) T Qs[CT * Cf::LQ];
-    __shared__ __attribute__((aligned(16))) T Ks[CT * Cf::LQ];
-    __shared__ __attribute__((aligned(16))) T Vs[CT * Cf::LV];
-    __shared__ __attribute__((aligned(16))) T Ps[CT * Cf::LP];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Cf::WALK_BYTES];
+    T* Qs = reinterpret_cast<T*>(smem);
+    T* Ks = Qs + Cf::K_OFF;
+    T* Vs = Qs + Cf::V_OFF;
+    T* Ps = Qs + Cf::P_OFF;
+    float* Sst = reinterpret_cast<float*>(smem);
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c16 = lane & 15;
-    const int64_t bh = blockIdx.x / n_seg, seg = blockIdx.x % n_seg;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int64_t line;
+    int vb;
+    split_id(blockIdx.x, (int64_t)(gridDim.x / n_vb), n_vb, line, vb);
+    const int64_t bh = line / n_seg, seg = line - bh * n_seg;
+    const int v0 = vb * BV;
+    const int nv = min(BV, dv - v0);  // valid columns of this block
     const int64_t n_c = (T_len + C - 1) / C;
     const int64_t c0 = seg * G, c1 = min(n_c, c0 + G);
     const bool last_seg = seg == n_seg - 1;
     const int64_t dkdv = (int64_t)dk * dv;
     const T* Qb = Q + bh * T_len * dk;
     const T* Kb = K + bh * T_len * dk;
-    const T* Vb = V + bh * T_len * dv;
-    float* Ob = O + bh * T_len * dv;
+    const T* Vb = V + bh * T_len * dv + v0;
+    float* Ob = O + bh * T_len * dv + v0;
 
-    // Incoming state of this segment.
-    const float* Sin = n_seg == 1 ? S + bh * dkdv : ws + (bh * n_seg + seg) * dkdv;
+    // Incoming state of this segment, columns [v0, v0 + nv).
+    const float* Sin = (n_seg == 1 ? S + bh * dkdv : ws + (bh * n_seg + seg) * dkdv) + v0;
     f32x4 Sacc[Cf::NVW][Cf::NDT];
-#pragma unroll
-    for (int vw = 0; vw < Cf::NVW; ++vw) {
-        const int v = 16 * (w + kWaves * vw) + c16;
-#pragma unroll
-        for (int dt = 0; dt < Cf::NDT; ++dt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int d = 16 * dt + 4 * g + r;
-                Sacc[vw][dt][r] = (d < dk && v < dv) ? Sin[(int64_t)d * dv + v] : 0.0f;
-            }
-    }
+    state_gmem_to_lds<Cf>(Sst, Sin, dk, dv, nv, tid);
+    __syncthreads();
+    state_lds_to_regs<Cf>(Sacc, Sst, w, g, c16);
+    __syncthreads();  // the state area is reused by the tiles
 
-    Tile<T, CT, D, Cf::LQ> tq, tk;
-    Tile<T, CT, D, Cf::LV> tv;
+    Tile<T, CT, D, typename Cf::LQL> tq;
+    Tile<T, CT, D, typename Cf::LKL> tk;
+    Tile<T, CT, BV, typename Cf::LVL> tv;
     auto rows_of = [&](int64_t c) { return (int)min((int64_t)C, T_len - c * C); };
-    if (vec) {
+    if constexpr (VEC) {
         tq.gather(Qb + c0 * C * dk, dk, rows_of(c0), dk, tid);
         tk.gather(Kb + c0 * C * dk, dk, rows_of(c0), dk, tid);
-        tv.gather(Vb + c0 * C * dv, dv, rows_of(c0), dv, tid);
+        tv.gather(Vb + c0 * C * dv, dv, rows_of(c0), nv, tid);
     }
+
+    // A chunk's outputs stay in registers until the next chunk has started:
+    // the wait for the next tiles' loads then never includes stores issued
+    // late in the previous chunk (loads and stores share one counter).
+    f32x4 Oacc[Cf::NT][Cf::NVW];
+    int64_t t_prev = 0;
+    int n_prev = 0;
 
     for (int64_t c = c0; c < c1; ++c) {
         const int nrows = rows_of(c);
         const int64_t t0 = c * C;
-        if (vec) {
+        if constexpr (VEC) {
             tq.scatter(Qs, tid);
             tk.scatter(Ks, tid);
             tv.scatter(Vs, tid);
         } else {
-            Tile<T, CT, D, Cf::LQ>::load_scalar(Qb + t0 * dk, dk, nrows, dk, Qs, tid);
-            Tile<T, CT, D, Cf::LQ>::load_scalar(Kb + t0 * dk, dk, nrows, dk, Ks, tid);
-            Tile<T, CT, D, Cf::LV>::load_scalar(Vb + t0 * dv, dv, nrows, dv, Vs, tid);
+            Tile<T, CT, D, typename Cf::LQL>::load_scalar(Qb + t0 * dk, dk, nrows, dk, Qs, tid);
+            Tile<T, CT, D, typename Cf::LKL>::load_scalar(Kb + t0 * dk, dk, nrows, dk, Ks, tid);
+            Tile<T, CT, BV, typename Cf::LVL>::load_scalar(Vb + t0 * dv, dv, nrows, nv, Vs, tid);
         }
         __syncthreads();
-        if (vec && c + 1 < c1) {  // next chunk's loads fly during this chunk's math
-            const int nr = rows_of(c + 1);
-            tq.gather(Qb + (t0 + C) * dk, dk, nr, dk, tid);
-            tk.gather(Kb + (t0 + C) * dk, dk, nr, dk, tid);
-            tv.gather(Vb + (t0 + C) * dv, dv, nr, dv, tid);
+        if (c > c0) store_out<Cf, VEC>(Ob, Oacc, t_prev, n_prev, nv, dv, w, g, c16);
+        if constexpr (VEC) {
+            if (c + 1 < c1) {  // next chunk's loads fly during this chunk's math
+                const int nr = rows_of(c + 1);
+                tq.gather(Qb + (t0 + C) * dk, dk, nr, dk, tid);
+                tk.gather(Kb + (t0 + C) * dk, dk, nr, dk, tid);
+                tv.gather(Vb + (t0 + C) * dv, dv, nr, nv, tid);
+            }
         }
 
         // (1) Scores of the kept triangle, computed transposed: tile (jt, it)
@@ -303,8 +476,8 @@ __global__ __launch_bounds__(kThreads) void k_chunk_walk(
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ds = 0; ds < Cf::NDS; ++ds)
-                acc = mma(lds_frag(Ks + (16 * jt + c16) * Cf::LQ + 32 * ds + 8 * g),
-                          lds_frag(Qs + (16 * it + c16) * Cf::LQ + 32 * ds + 8 * g), acc);
+                acc = mma(lds_row(Ks + (16 * jt + c16) * Cf::LK + 32 * ds + 8 * g),
+                          lds_row(Qs + (16 * it + c16) * Cf::LQ + 32 * ds + 8 * g), acc);
             const int i = 16 * it + c16;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
@@ -318,7 +491,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_walk(
 
         // (2) Output, transposed: O^T tile (vt, it) = V^T P^T + S^T Q^T.
         Fr Vf[Cf::NVW][Cf::NTS];
-        load_vfrags<Cf>(Vf, Vs, w, g, c16);
+        load_vfrags<Cf>(Vf, Vs, w, g, lane);
 
         // The state as the first operand: value row c16, depth slots
         // {4g + r} from tile 2ds and {16 + 4g + r} from tile 2ds + 1 -- exactly
@@ -342,68 +515,46 @@ __global__ __launch_bounds__(kThreads) void k_chunk_walk(
 
 #pragma unroll
         for (int it = 0; it < Cf::NT; ++it) {
-            f32x4 acc[Cf::NVW];
 #pragma unroll
-            for (int vw = 0; vw < Cf::NVW; ++vw) acc[vw] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int vw = 0; vw < Cf::NVW; ++vw) Oacc[it][vw] = f32x4{0.f, 0.f, 0.f, 0.f};
             const int i = 16 * it + c16;
             // masked scores times values: only time steps at or left of the diagonal
 #pragma unroll
             for (int ts = 0; ts <= it / 2; ++ts) {
-                const Fr pb = lds_frag(Ps + i * Cf::LP + 32 * ts + 8 * g);
+                const Fr pb = lds_row2(Ps + i * Cf::LP + 32 * ts + 4 * g,
+                                       Ps + i * Cf::LP + 32 * ts + 16 + 4 * g);
 #pragma unroll
                 for (int vw = 0; vw < Cf::NVW; ++vw)
-                    if (w + kWaves * vw < Cf::NDT) acc[vw] = mma(Vf[vw][ts], pb, acc[vw]);
+                    if (Cf::ALL_WAVES || w + kWaves * vw < Cf::NVT)
+                        Oacc[it][vw] = mma(Vf[vw][ts], pb, Oacc[it][vw]);
             }
             // incoming state read: Q_c S_c
 #pragma unroll
             for (int ds = 0; ds < Cf::NDS; ++ds) {
-                const Fr qb = lds_frag2(Qs + i * Cf::LQ + 32 * ds + 4 * g,
-                                        Qs + i * Cf::LQ + 32 * ds + 16 + 4 * g);
+                const Fr qb = lds_row2(Qs + i * Cf::LQ + 32 * ds + 4 * g,
+                                       Qs + i * Cf::LQ + 32 * ds + 16 + 4 * g);
 #pragma unroll
                 for (int vw = 0; vw < Cf::NVW; ++vw)
-                    if (w + kWaves * vw < Cf::NDT) {
-                        acc[vw] = mma(Shi[vw][ds], qb, acc[vw]);
-                        if constexpr (Cf::BF) acc[vw] = mma(Slo[vw][ds], qb, acc[vw]);
+                    if (Cf::ALL_WAVES || w + kWaves * vw < Cf::NVT) {
+                        Oacc[it][vw] = mma(Shi[vw][ds], qb, Oacc[it][vw]);
+                        if constexpr (Cf::BF) Oacc[it][vw] = mma(Slo[vw][ds], qb, Oacc[it][vw]);
                     }
-            }
-            // lane holds O[t0 + i][16 vt + 4g + r], r = 0..3
-            if (i < nrows) {
-                float* orow = Ob + (t0 + i) * dv;
-#pragma unroll
-                for (int vw = 0; vw < Cf::NVW; ++vw) {
-                    const int v = 16 * (w + kWaves * vw) + 4 * g;
-                    if (w + kWaves * vw < Cf::NDT && v < dv) {
-                        if ((dv & 3) == 0) {
-                            __builtin_nontemporal_store(acc[vw], reinterpret_cast<f32x4*>(orow + v));
-                        } else {
-#pragma unroll
-                            for (int r = 0; r < 4; ++r)
-                                if (v + r < dv) orow[v + r] = acc[vw][r];
-                        }
-                    }
-                }
             }
         }
+        t_prev = t0;
+        n_prev = nrows;
 
         // (3) State hop S_{c+1} = S_c + K_c^T V_c (not needed after the last
         // chunk of a segment whose successor starts from the scanned state).
-        if (c + 1 < c1 || last_seg) state_hop<Cf>(Sacc, Vf, Ks, w, g, c16);
+        if (c + 1 < c1 || last_seg) state_hop<Cf>(Sacc, Vf, Ks, w, g, lane);
         __syncthreads();
     }
+    if (c1 > c0) store_out<Cf, VEC>(Ob, Oacc, t_prev, n_prev, nv, dv, w, g, c16);
 
-    if (last_seg) {
-        float* Sout = S + bh * dkdv;
-#pragma unroll
-        for (int vw = 0; vw < Cf::NVW; ++vw) {
-            const int v = 16 * (w + kWaves * vw) + c16;
-#pragma unroll
-            for (int dt = 0; dt < Cf::NDT; ++dt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int d = 16 * dt + 4 * g + r;
-                    if (d < dk && v < dv) Sout[(int64_t)d * dv + v] = Sacc[vw][dt][r];
-                }
-        }
+    if (last_seg) {  // (the loop ended with a barrier: the tiles are free)
+        state_regs_to_lds<Cf>(Sst, Sacc, w, g, c16);
+        __syncthreads();
+        state_lds_to_gmem<Cf>(S + bh * dkdv + v0, Sst, dk, dv, nv, tid);
     }
 }
 
@@ -416,8 +567,10 @@ void plan_prefill(PrefillPlan& p) {
     p.BH = p.B * p.H;
     p.D = pad_dim(p.dk > p.dv ? p.dk : p.dv);
     p.CT = pad_dim(p.C);
+    p.BV = p.D > 64 ? 64 : p.D;
+    p.n_vb = p.D / p.BV;
     p.n_c = p.T > 0 ? (p.T + p.C - 1) / p.C : 0;
-    const int64_t want = p.n_c * p.BH;
+    const int64_t want = p.n_c * p.BH * p.n_vb;
     p.G = want > kTargetWalkers ? (want + kTargetWalkers - 1) / kTargetWalkers : 1;
     if (p.G > p.n_c) p.G = p.n_c > 0 ? p.n_c : 1;
     p.n_seg = p.n_c > 0 ? (p.n_c + p.G - 1) / p.G : 0;
@@ -428,24 +581,36 @@ void plan_prefill(PrefillPlan& p) {
 template <typename T, int CT, int D>
 static hipError_t launch_walk_t(const PrefillPlan& p, const void* Q, const void* K, const void* V,
                                 float* S, float* O, float* ws, hipStream_t st) {
-    const int64_t grid = p.BH * p.n_seg;
-    hipLaunchKernelGGL((k_chunk_walk<T, CT, D>), dim3((unsigned)grid), dim3(kThreads), 0, st,
-                       (const T*)Q, (const T*)K, (const T*)V, S, O, (const float*)ws, p.T, p.dk,
-                       p.dv, p.C, p.G, p.n_seg, (int)p.vec);
+    constexpr int BV = D > 64 ? 64 : D;
+    const int64_t grid = p.BH * p.n_seg * p.n_vb;
+    if (p.vec)
+        hipLaunchKernelGGL((k_chunk_walk<T, CT, D, BV, true>), dim3((unsigned)grid), dim3(kThreads), 0,
+                           st, (const T*)Q, (const T*)K, (const T*)V, S, O, (const float*)ws, p.T,
+                           p.dk, p.dv, p.C, p.G, p.n_seg, p.n_vb);
+    else
+        hipLaunchKernelGGL((k_chunk_walk<T, CT, D, BV, false>), dim3((unsigned)grid), dim3(kThreads), 0,
+                           st, (const T*)Q, (const T*)K, (const T*)V, S, O, (const float*)ws, p.T,
+                           p.dk, p.dv, p.C, p.G, p.n_seg, p.n_vb);
     return hipGetLastError();
 }
 
 template <typename T, int CT, int D>
 static hipError_t launch_seg_t(const PrefillPlan& p, const void* K, const void* V, float* ws,
                                hipStream_t st) {
-    const int64_t grid = p.BH * (p.n_seg - 1);
-    hipLaunchKernelGGL((k_segment_states<T, CT, D>), dim3((unsigned)grid), dim3(kThreads), 0, st,
-                       (const T*)K, (const T*)V, ws, p.T, p.dk, p.dv, p.C, p.G, p.n_seg,
-                       (int)p.vec);
+    constexpr int BV = D > 64 ? 64 : D;
+    const int64_t grid = p.BH * (p.n_seg - 1) * p.n_vb;
+    if (p.vec)
+        hipLaunchKernelGGL((k_segment_states<T, CT, D, BV, true>), dim3((unsigned)grid), dim3(kThreads),
+                           0, st, (const T*)K, (const T*)V, ws, p.T, p.dk, p.dv, p.C, p.G, p.n_seg,
+                           p.n_vb);
+    else
+        hipLaunchKernelGGL((k_segment_states<T, CT, D, BV, false>), dim3((unsigned)grid), dim3(kThreads),
+                           0, st, (const T*)K, (const T*)V, ws, p.T, p.dk, p.dv, p.C, p.G, p.n_seg,
+                           p.n_vb);
     return hipGetLastError();
 }
 
-// Calls F<T, CT, D>::run(args...) for the plan's padded sizes.
+// Calls FN<T, CT, D>(args...) for the plan's padded sizes.
 #define LLA_DISPATCH(FN, ...)                                                              \
     do {                                                                                   \
         if (p.dtype == LLA_BF16) {                                                         \
