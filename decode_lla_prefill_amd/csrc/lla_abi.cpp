@@ -6,7 +6,7 @@
 #include <stdint.h>
 #include <string.h>
 
-#include "../../include/lla.h"
+#include "lla.h"
 #include "lla_internal.h"
 
 namespace {

@@ -58,6 +58,24 @@ struct PadLayout {
     __device__ __forceinline__ static int off(int row, int col) { return row * LD + col; }
 };
 
+// ---- buffer (descriptor-based) global access ----------------------------------
+//
+// A buffer descriptor covers [base, base + bytes); a load whose offset falls
+// outside returns zero and a store outside is dropped.  Tiles therefore need
+// no per-lane branches: padding rows and columns get an offset past the end.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOutside = 0x80000000u;  // an offset beyond every descriptor here
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    // dword 3 = 0x00020000: raw (untyped) 32-bit data, the gfx9-family setting
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ void buf_store16(rsrc_t r, uint32_t off, f32x4 x) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, off, 0, 0);
+}
+
 // A ROWS x COLS tile of T staged in LDS with layout L.
 //
 // Staging is split in two halves so that the global loads of the next tile
@@ -70,28 +88,34 @@ struct Tile {
     static constexpr int VPR = COLS / VE;           // vectors per row
     static constexpr int NV = ROWS * VPR;           // vectors per tile
     static constexpr int NPT = (NV + kThreads - 1) / kThreads;  // per thread
+    static constexpr bool FULL = NV % kThreads == 0;
     static_assert(COLS % VE == 0, "tile width must be a whole number of vectors");
 
     u32x4 r[NPT];
+    uint32_t off[NPT];  // this thread's byte offsets within a tile (kOutside: padding)
 
-    // Vector path: global row stride `ld` is a multiple of VE and ncols % VE == 0.
-    __device__ __forceinline__ void gather(const T* __restrict__ g, int64_t ld, int nrows,
-                                           int ncols, int tid) {
+    // Vector path set-up: global row stride `ld` elements (a multiple of VE),
+    // valid columns `ncols` (a multiple of VE).  Offsets are the same for
+    // every tile of a sequence.
+    __device__ __forceinline__ void init(int64_t ld, int ncols, int tid) {
 #pragma unroll
         for (int n = 0; n < NPT; ++n) {
             const int e = tid + n * kThreads;
             const int row = e / VPR, cv = e % VPR;
-            u32x4 x = {0u, 0u, 0u, 0u};
-            if (e < NV && row < nrows && cv * VE < ncols)
-                x = *reinterpret_cast<const u32x4*>(g + (int64_t)row * ld + cv * VE);
-            r[n] = x;
+            off[n] = (e < NV && cv * VE < ncols) ? (uint32_t)((row * ld + cv * VE) * sizeof(T)) : kOutside;
         }
+    }
+    // Loads the tile whose first row is at g; rows >= nrows read as zero.
+    __device__ __forceinline__ void gather(const T* __restrict__ g, int64_t ld, int nrows) {
+        const rsrc_t rs = make_rsrc(g, (uint32_t)(nrows * ld * sizeof(T)));
+#pragma unroll
+        for (int n = 0; n < NPT; ++n) r[n] = buf_load16(rs, off[n]);
     }
     __device__ __forceinline__ void scatter(T* lds, int tid) const {
 #pragma unroll
         for (int n = 0; n < NPT; ++n) {
             const int e = tid + n * kThreads;
-            if (e < NV) {
+            if (FULL || e < NV) {
                 const int row = e / VPR, cv = e % VPR;
                 *reinterpret_cast<u32x4*>(lds + L::off(row, cv * VE)) = r[n];
             }

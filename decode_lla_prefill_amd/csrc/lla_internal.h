@@ -6,7 +6,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/lla.h"
+#include "lla.h"
 
 namespace lla {
 

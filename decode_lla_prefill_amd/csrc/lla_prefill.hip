@@ -281,32 +281,51 @@ __global__ __launch_bounds__(kThreads) void k_segment_states(
 #pragma unroll
         for (int dt = 0; dt < Cf::NDT; ++dt) Sacc[vw][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    Tile<T, CT, D, typename Cf::LKL> tk;
-    Tile<T, CT, BV, typename Cf::LVL> tv;
     auto rows_of = [&](int64_t c) { return (int)min((int64_t)C, T_len - c * C); };
     if constexpr (VEC) {
-        tk.gather(Kb + c0 * C * dk, dk, rows_of(c0), dk, tid);
-        tv.gather(Vb + c0 * C * dv, dv, rows_of(c0), nv, tid);
-    }
-    for (int64_t c = c0; c < c1; ++c) {
-        if constexpr (VEC) {
-            tk.scatter(Ks, tid);
-            tv.scatter(Vs, tid);
-        } else {
-            Tile<T, CT, D, typename Cf::LKL>::load_scalar(Kb + c * C * dk, dk, rows_of(c), dk, Ks, tid);
-            Tile<T, CT, BV, typename Cf::LVL>::load_scalar(Vb + c * C * dv, dv, rows_of(c), nv, Vs, tid);
-        }
-        __syncthreads();
-        if constexpr (VEC) {
-            if (c + 1 < c1) {
-                tk.gather(Kb + (c + 1) * C * dk, dk, rows_of(c + 1), dk, tid);
-                tv.gather(Vb + (c + 1) * C * dv, dv, rows_of(c + 1), nv, tid);
+        // The loop is bound by memory latency, not by its math: keep PF
+        // chunks of loads in flight (one register set per chunk, used round
+        // robin; the loop is unrolled by PF so the sets are static).
+        constexpr int PF = 2;
+        Tile<T, CT, D, typename Cf::LKL> tk[PF];
+        Tile<T, CT, BV, typename Cf::LVL> tv[PF];
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+            tk[u].init(dk, dk, tid);
+            tv[u].init(dv, nv, tid);
+            if (c0 + u < c1) {
+                tk[u].gather(Kb + (c0 + u) * C * dk, dk, rows_of(c0 + u));
+                tv[u].gather(Vb + (c0 + u) * C * dv, dv, rows_of(c0 + u));
             }
         }
-        Fr Vf[Cf::NVW][Cf::NTS];
-        load_vfrags<Cf>(Vf, Vs, w, g, lane);
-        state_hop<Cf>(Sacc, Vf, Ks, w, g, lane);
-        __syncthreads();
+        for (int64_t c = c0; c < c1; c += PF) {
+#pragma unroll
+            for (int u = 0; u < PF; ++u) {
+                const int64_t cc = c + u;
+                if (cc >= c1) break;
+                tk[u].scatter(Ks, tid);
+                tv[u].scatter(Vs, tid);
+                __syncthreads();
+                if (cc + PF < c1) {
+                    tk[u].gather(Kb + (cc + PF) * C * dk, dk, rows_of(cc + PF));
+                    tv[u].gather(Vb + (cc + PF) * C * dv, dv, rows_of(cc + PF));
+                }
+                Fr Vf[Cf::NVW][Cf::NTS];
+                load_vfrags<Cf>(Vf, Vs, w, g, lane);
+                state_hop<Cf>(Sacc, Vf, Ks, w, g, lane);
+                __syncthreads();
+            }
+        }
+    } else {
+        for (int64_t c = c0; c < c1; ++c) {
+            Tile<T, CT, D, typename Cf::LKL>::load_scalar(Kb + c * C * dk, dk, rows_of(c), dk, Ks, tid);
+            Tile<T, CT, BV, typename Cf::LVL>::load_scalar(Vb + c * C * dv, dv, rows_of(c), nv, Vs, tid);
+            __syncthreads();
+            Fr Vf[Cf::NVW][Cf::NTS];
+            load_vfrags<Cf>(Vf, Vs, w, g, lane);
+            state_hop<Cf>(Sacc, Vf, Ks, w, g, lane);
+            __syncthreads();
+        }
     }
 
     // (the loop ended with a barrier: the tiles are free)
@@ -330,7 +349,7 @@ __global__ __launch_bounds__(kThreads) void k_state_scan(const float* __restrict
     if (e + 4 <= dkdv && (dkdv & 3) == 0) {
         f32x4 acc = *reinterpret_cast<const f32x4*>(s0);
         *reinterpret_cast<f32x4*>(slot) = acc;
-        constexpr int U = 8;
+        constexpr int U = 16;  // loads in flight per thread (segments per batch)
         for (int64_t s = 1; s < n_seg; s += U) {
             f32x4 x[U];
 #pragma unroll
@@ -362,22 +381,35 @@ __global__ __launch_bounds__(kThreads) void k_state_scan(const float* __restrict
 // registers, split over the waves by value tiles (wave w owns tiles w, w+4..).
 // ---------------------------------------------------------------------------
 // Writes a chunk's output tiles held by a wave: Oacc[it][vw] holds
-// O[t0 + 16 it + c16][v0 + 16 vt + 4g + r], r = 0..3 (vt = w + 4 vw).
+// O[t0 + 16 it + c16][v0 + 16 vt + 4g + r], r = 0..3 (vt = w + 4 vw).  The
+// vector path stores through a buffer descriptor that ends at the chunk's
+// last valid row, so rows past it are dropped without a branch.
 template <typename Cf, bool VEC>
 __device__ __forceinline__ void store_out(float* Ob, const f32x4 (&Oacc)[Cf::NT][Cf::NVW], int64_t t0,
                                           int nrows, int nv, int dv, int w, int g, int c16) {
+    if constexpr (VEC) {
+        const rsrc_t rs = make_rsrc(Ob + t0 * dv, (uint32_t)(nrows * dv * 4));
 #pragma unroll
-    for (int it = 0; it < Cf::NT; ++it) {
-        const int i = 16 * it + c16;
-        if (i >= nrows) continue;
-        float* orow = Ob + (t0 + i) * dv;
+        for (int it = 0; it < Cf::NT; ++it) {
+            const int i = 16 * it + c16;
 #pragma unroll
-        for (int vw = 0; vw < Cf::NVW; ++vw) {
-            const int v = 16 * (w + kWaves * vw) + 4 * g;
-            if (!(Cf::ALL_WAVES || w + kWaves * vw < Cf::NVT) || v >= nv) continue;
-            if constexpr (VEC) {
-                *reinterpret_cast<f32x4*>(orow + v) = Oacc[it][vw];
-            } else {
+            for (int vw = 0; vw < Cf::NVW; ++vw) {
+                const int v = 16 * (w + kWaves * vw) + 4 * g;
+                if (!(Cf::ALL_WAVES || w + kWaves * vw < Cf::NVT)) continue;
+                const uint32_t off = v < nv ? (uint32_t)((i * dv + v) * 4) : kOutside;
+                buf_store16(rs, off, Oacc[it][vw]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int it = 0; it < Cf::NT; ++it) {
+            const int i = 16 * it + c16;
+            if (i >= nrows) continue;
+            float* orow = Ob + (t0 + i) * dv;
+#pragma unroll
+            for (int vw = 0; vw < Cf::NVW; ++vw) {
+                const int v = 16 * (w + kWaves * vw) + 4 * g;
+                if (!(Cf::ALL_WAVES || w + kWaves * vw < Cf::NVT) || v >= nv) continue;
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     if (v + r < nv) orow[v + r] = Oacc[it][vw][r];
@@ -430,9 +462,12 @@ __global__ __launch_bounds__(kThreads) void k_chunk_walk(
     Tile<T, CT, BV, typename Cf::LVL> tv;
     auto rows_of = [&](int64_t c) { return (int)min((int64_t)C, T_len - c * C); };
     if constexpr (VEC) {
-        tq.gather(Qb + c0 * C * dk, dk, rows_of(c0), dk, tid);
-        tk.gather(Kb + c0 * C * dk, dk, rows_of(c0), dk, tid);
-        tv.gather(Vb + c0 * C * dv, dv, rows_of(c0), nv, tid);
+        tq.init(dk, dk, tid);
+        tk.init(dk, dk, tid);
+        tv.init(dv, nv, tid);
+        tq.gather(Qb + c0 * C * dk, dk, rows_of(c0));
+        tk.gather(Kb + c0 * C * dk, dk, rows_of(c0));
+        tv.gather(Vb + c0 * C * dv, dv, rows_of(c0));
     }
 
     // A chunk's outputs stay in registers until the next chunk has started:
@@ -459,9 +494,9 @@ __global__ __launch_bounds__(kThreads) void k_chunk_walk(
         if constexpr (VEC) {
             if (c + 1 < c1) {  // next chunk's loads fly during this chunk's math
                 const int nr = rows_of(c + 1);
-                tq.gather(Qb + (t0 + C) * dk, dk, nr, dk, tid);
-                tk.gather(Kb + (t0 + C) * dk, dk, nr, dk, tid);
-                tv.gather(Vb + (t0 + C) * dv, dv, nr, nv, tid);
+                tq.gather(Qb + (t0 + C) * dk, dk, nr);
+                tk.gather(Kb + (t0 + C) * dk, dk, nr);
+                tv.gather(Vb + (t0 + C) * dv, dv, nr);
             }
         }
 
@@ -469,20 +504,38 @@ __global__ __launch_bounds__(kThreads) void k_chunk_walk(
         // holds A^T = K_c Q_c^T, i.e. lane (g, c16) has A[i][j] for query
         // i = 16 it + c16 and keys j = 16 jt + 4g + r.  Entries with j > i are
         // masked in registers; the rest is rounded to the input type (P).
-        for (int e = w; e < Cf::NTRI; e += kWaves) {
-            int it = 0;
-            while ((it + 1) * (it + 2) / 2 <= e) ++it;
-            const int jt = e - it * (it + 1) / 2;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        // Wave w owns tiles w, w + 4, ... of the triangle and runs them as
+        // independent accumulators (a wave short of tiles recomputes the last
+        // one and does not store it), so the matrix-core latency overlaps.
+        {
+            constexpr int PW = (Cf::NTRI + kWaves - 1) / kWaves;
+            int tit[PW], tjt[PW];
+            f32x4 sacc[PW];
+#pragma unroll
+            for (int m = 0; m < PW; ++m) {
+                int e = w + kWaves * m;
+                e = e < Cf::NTRI ? e : Cf::NTRI - 1;
+                int it = 0;
+                while ((it + 1) * (it + 2) / 2 <= e) ++it;
+                tit[m] = it;
+                tjt[m] = e - it * (it + 1) / 2;
+                sacc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
 #pragma unroll
             for (int ds = 0; ds < Cf::NDS; ++ds)
-                acc = mma(lds_row(Ks + (16 * jt + c16) * Cf::LK + 32 * ds + 8 * g),
-                          lds_row(Qs + (16 * it + c16) * Cf::LQ + 32 * ds + 8 * g), acc);
-            const int i = 16 * it + c16;
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (16 * jt + 4 * g + r > i) acc[r] = 0.0f;
-            lds_store4(Ps + i * Cf::LP + 16 * jt + 4 * g, acc);
+                for (int m = 0; m < PW; ++m)
+                    sacc[m] = mma(lds_row(Ks + (16 * tjt[m] + c16) * Cf::LK + 32 * ds + 8 * g),
+                                  lds_row(Qs + (16 * tit[m] + c16) * Cf::LQ + 32 * ds + 8 * g), sacc[m]);
+#pragma unroll
+            for (int m = 0; m < PW; ++m) {
+                if (w + kWaves * m >= Cf::NTRI) continue;
+                const int i = 16 * tit[m] + c16;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (16 * tjt[m] + 4 * g + r > i) sacc[m][r] = 0.0f;
+                lds_store4(Ps + i * Cf::LP + 16 * tjt[m] + 4 * g, sacc[m]);
+            }
         }
         // Tiles right of the diagonal that a 32-deep step still reads: zero.
         for (int it = 2 * w; it + 1 < Cf::NT; it += 2 * kWaves)
@@ -513,14 +566,19 @@ __global__ __launch_bounds__(kThreads) void k_chunk_walk(
                     }
                 }
 
+        // All query tiles of the chunk are accumulated side by side (depth
+        // outer, tile inner), so consecutive matrix-core ops are independent.
 #pragma unroll
-        for (int it = 0; it < Cf::NT; ++it) {
+        for (int it = 0; it < Cf::NT; ++it)
 #pragma unroll
             for (int vw = 0; vw < Cf::NVW; ++vw) Oacc[it][vw] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const int i = 16 * it + c16;
-            // masked scores times values: only time steps at or left of the diagonal
+        // masked scores times values: a 32-deep time step ts reaches query
+        // tiles it >= 2 ts (steps right of the diagonal are all zero)
 #pragma unroll
-            for (int ts = 0; ts <= it / 2; ++ts) {
+        for (int ts = 0; ts < Cf::NTS; ++ts) {
+#pragma unroll
+            for (int it = 2 * ts; it < Cf::NT; ++it) {
+                const int i = 16 * it + c16;
                 const Fr pb = lds_row2(Ps + i * Cf::LP + 32 * ts + 4 * g,
                                        Ps + i * Cf::LP + 32 * ts + 16 + 4 * g);
 #pragma unroll
@@ -528,23 +586,31 @@ __global__ __launch_bounds__(kThreads) void k_chunk_walk(
                     if (Cf::ALL_WAVES || w + kWaves * vw < Cf::NVT)
                         Oacc[it][vw] = mma(Vf[vw][ts], pb, Oacc[it][vw]);
             }
-            // incoming state read: Q_c S_c
+        }
+        // incoming state read: Q_c S_c
 #pragma unroll
-            for (int ds = 0; ds < Cf::NDS; ++ds) {
-                const Fr qb = lds_row2(Qs + i * Cf::LQ + 32 * ds + 4 * g,
-                                       Qs + i * Cf::LQ + 32 * ds + 16 + 4 * g);
+        for (int ds = 0; ds < Cf::NDS; ++ds) {
+            Fr qb[Cf::NT];
 #pragma unroll
-                for (int vw = 0; vw < Cf::NVW; ++vw)
-                    if (Cf::ALL_WAVES || w + kWaves * vw < Cf::NVT) {
-                        Oacc[it][vw] = mma(Shi[vw][ds], qb, Oacc[it][vw]);
-                        if constexpr (Cf::BF) Oacc[it][vw] = mma(Slo[vw][ds], qb, Oacc[it][vw]);
-                    }
+            for (int it = 0; it < Cf::NT; ++it) {
+                const int i = 16 * it + c16;
+                qb[it] = lds_row2(Qs + i * Cf::LQ + 32 * ds + 4 * g, Qs + i * Cf::LQ + 32 * ds + 16 + 4 * g);
+            }
+#pragma unroll
+            for (int vw = 0; vw < Cf::NVW; ++vw) {
+                if (!(Cf::ALL_WAVES || w + kWaves * vw < Cf::NVT)) continue;
+#pragma unroll
+                for (int it = 0; it < Cf::NT; ++it) Oacc[it][vw] = mma(Shi[vw][ds], qb[it], Oacc[it][vw]);
+                if constexpr (Cf::BF) {
+#pragma unroll
+                    for (int it = 0; it < Cf::NT; ++it) Oacc[it][vw] = mma(Slo[vw][ds], qb[it], Oacc[it][vw]);
+                }
             }
         }
         t_prev = t0;
         n_prev = nrows;
 
-        // (3) State hop S_{c+1} = S_c + K_c^T V_c (not needed after the last
+        // State hop S_{c+1} = S_c + K_c^T V_c (not needed after the last
         // chunk of a segment whose successor starts from the scanned state).
         if (c + 1 < c1 || last_seg) state_hop<Cf>(Sacc, Vf, Ks, w, g, lane);
         __syncthreads();
