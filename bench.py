@@ -10,11 +10,17 @@ steps/s.
 
 Prefill is timed cold: the timed steps rotate over several input/output
 sets whose total exceeds the 256 MB Infinity Cache, so each step's inputs
-come from HBM; a warm figure (one set repeated) is given for context.  Each
-step calls the three prefill phases in order (exactly what lla_prefill
-does) with HIP events between them on the launch stream, which gives the
-per-kernel duration of the dominant kernel (the chunk walk) for the
-roofline.  Decode steps are timed the same way, one event pair per step.
+come from HBM; a warm figure (one set repeated) is given for context.  A
+second pass calls the three prefill phases one by one with HIP events
+between them on the launch stream (per-phase times, launch gaps included),
+and a third times back-to-back launches of the dominant kernel, the chunk
+walk, for the roofline.  The decode step is one kernel: HIP events around
+the timed steps give its launch duration.
+
+``roofline.traffic`` is the HBM traffic per launch that the hardware
+counters measured (FETCH_SIZE + WRITE_SIZE, calibrated against a plain
+copy), read from the committed counter summary under profiles/ when that
+was taken on the current kernel source, else null.
 
 The CPU baseline is the float64 oracle (the token-by-token recurrence) on
 the host cores, timed on a bounded sample of the same workloads.
@@ -22,7 +28,6 @@ the host cores, timed on a bounded sample of the same workloads.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -34,11 +39,6 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 matrix cores, TFLOP/s
 METRIC = "prefill tokens/s + % bf16 MFMA peak; decode steps/s + % HBM BW (1 GPU)"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_walk_T8192_traffic.txt")
-KERNEL_SOURCES = [os.path.join(ROOT, "decode_lla_prefill_amd", "csrc", f)
-                  for f in ("lla_prefill.hip", "lla_device.h")]
-
-
 def prefill_work(B, H, T, C, d):
     """Algorithmic flops and bytes of one prefill (kept triangle only).
 
@@ -58,128 +58,133 @@ def decode_bytes(B, H, d):
     return B * H * (8 * d * d + 10 * d)
 
 
-def kernel_source_sha():
-    h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+def repeat_for(fn, min_seconds):
+    """Runs fn() until at least min_seconds have passed; returns (calls, seconds)."""
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        secs = time.perf_counter() - t0
+        if secs >= min_seconds:
+            return reps, secs
 
 
-def stored_traffic():
-    """HBM bytes per chunk-walk launch from the committed counter summary,
-    or None if it is missing or was taken on a different kernel source."""
-    try:
-        kv = {}
-        with open(TRAFFIC_FILE) as f:
-            for line in f:
-                if "=" in line and not line.startswith("#"):
-                    key, val = line.split("=", 1)
-                    kv[key.strip()] = val.strip()
-        if kv.get("kernel_source_sha") != kernel_source_sha():
-            return None
-        return float(kv["hbm_bytes_per_launch"])
-    except (OSError, KeyError, ValueError):
-        return None
-
-
-def time_oracle_prefill(q, k, v, threads):
-    import oracle
+def _timed(torch, fn, n_steps):
+    """Wall clock and GPU-event time of n_steps calls of fn(i), synchronised on both sides."""
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    oracle.recurrence(q, k, v, nthreads=threads)
-    return time.perf_counter() - t0
+    e0.record(stream)
+    for i in range(n_steps):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, e0.elapsed_time(e1) * 1e-3
 
 
-def bench_prefill(args, torch, lla, workloads):
+def bench_prefill(args, torch, lla, workloads, profiling):
     cfg = workloads.CONFIGS[args.prefill_config]
     dev = torch.device("cuda:0")
     B, H, T, C, d = cfg.B, cfg.H, cfg.T, cfg.C, cfg.dk
     q0, k0, v0 = workloads.config_inputs(cfg, device=dev)
-    sets = []
+    sets, ins = [], []
     for r in range(args.rotate):
         q, k, v = (x.clone() for x in (q0, k0, v0)) if r else (q0, k0, v0)
         S = lla.state_init(B, H, d, d, device=dev)
-        o = torch.empty((B, H, T, d), dtype=torch.float32, device=dev)
-        ws = torch.empty(max(1, lla.prefill_workspace_size(B, H, T, d, d, C) // 4),
-                         dtype=torch.float32, device=dev)
-        sets.append((q, k, v, S, o, ws))
-    stream = torch.cuda.current_stream(dev)
+        sets.append(lla.PreparedPrefill(q, k, v, S, C))
+        ins.append((q, k, v))
+    n_sets = len(sets)
 
-    def step(i, ev=None):
-        q, k, v, S, o, ws = sets[i % len(sets)]
-        lla.state_init(B, H, d, d, out=S)
-        if ev is not None:
-            ev[0].record(stream)
-        lla.prefill_segment_states(k, v, C, ws)
-        if ev is not None:
-            ev[1].record(stream)
-        lla.prefill_state_scan(S, T, C, ws)
-        if ev is not None:
-            ev[2].record(stream)
-        lla.prefill_chunks(q, k, v, S, C, workspace=ws, out=o)
-        if ev is not None:
-            ev[3].record(stream)
-
-    def run(n_steps, n_sets_used):
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_steps)]
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(n_steps):
-            step(i % n_sets_used, evs[i])
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        phase = [[e[j].elapsed_time(e[j + 1]) for e in evs] for j in range(3)]
-        per_step = [e[0].elapsed_time(e[3]) for e in evs]
-        return wall, phase, per_step
+    # One step = the fresh-prompt state init (S = 0) + one lla_prefill call.
+    def step(i):
+        sets[i % n_sets](zero_state=True)
 
     for i in range(args.warmup):
         step(i)
-    wall, phase, per_step = run(args.steps, len(sets))
-    _, phase_w, per_step_w = run(args.steps, 1)
+    wall, gpu = _timed(torch, step, args.steps)
+    wall_w, gpu_w = _timed(torch, lambda i: sets[0](zero_state=True), args.steps)
+
+    # Per-phase durations: the same steps with HIP events between the three
+    # phases (what lla_prefill enqueues), on the launch stream.  An interval
+    # between two events also holds the launch gap in front of the kernel.
+    stream = torch.cuda.current_stream(dev)
+    evs = []
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        st = sets[i % n_sets]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        st.zero_state()
+        ev[0].record(stream)
+        st.segment_states()
+        ev[1].record(stream)
+        st.state_scan()
+        ev[2].record(stream)
+        st.chunks()
+        ev[3].record(stream)
+        evs.append(ev)
+    torch.cuda.synchronize()
+    phase = [[ev[j].elapsed_time(ev[j + 1]) for ev in evs] for j in range(3)]
+
+    # The chunk walk's launch duration: back-to-back walks over the rotating
+    # sets between two events.  Every set's workspace holds its segment
+    # states from the pass above, and a walk reads only those, q, k and v, so
+    # the repeated walks are the same work as the one inside a step.
+    n_walk = max(args.steps, 4 * n_sets)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(n_walk):
+        sets[i % n_sets].chunks()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    walk_launch_ms = e0.elapsed_time(e1) / n_walk
     flops, nbytes = prefill_work(B, H, T, C, d)
     ms_step = wall * 1e3 / args.steps
-    gpu_ms = sum(per_step) / len(per_step)
     walk_ms = sum(phase[2]) / len(phase[2])
-    achieved = nbytes / (walk_ms * 1e-3) / 1e9
-    traffic = stored_traffic()
+    achieved = nbytes / (walk_launch_ms * 1e-3) / 1e9
     res = {
         "config": {"workload": cfg.name, "B": B, "H": H, "T": T, "C": C, "dk": d, "dv": d,
                    "inputs": "bf16 N(0,1)/sqrt(128), K rows L2-normalised; fp32 state and output",
-                   "cache": "cold: %d rotating input/output sets (%.0f MB each)" % (
-                       len(sets), (nbytes + 0) / 1e6)},
+                   "cache": "cold: %d rotating input/output sets of %.0f MB" % (n_sets, nbytes / 1e6),
+                   "step": "state init (S=0) + lla_prefill (per-segment K^T V, segment scan, chunk walk)"},
         "value": B * T / (ms_step * 1e-3),
         "ms_per_step": ms_step,
-        "gpu_ms_per_step": gpu_ms,
+        "gpu_ms_per_step": gpu * 1e3 / args.steps,
         "phase_ms": {"segment_states": sum(phase[0]) / len(phase[0]),
                      "state_scan": sum(phase[1]) / len(phase[1]),
                      "chunk_walk": walk_ms},
         "mfma_frac": flops / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
         "hbm_gbs": nbytes / (ms_step * 1e-3) / 1e9,
-        "roofline": {"kernel": "k_chunk_walk<bf16,64,128>", "bound": "hbm",
+        "roofline": {"kernel": "k_chunk_walk<bf16,64,128,64>", "bound": "hbm",
                      "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS,
-                     "traffic": traffic,
+                     "traffic": profiling.stored_traffic("chunk_walk"),
                      "algorithmic_bytes": nbytes,
-                     "algorithmic_flops": flops},
-        "warm": {"gpu_ms_per_step": sum(per_step_w) / len(per_step_w),
-                 "tokens_per_s": B * T / (sum(per_step_w) / len(per_step_w) * 1e-3),
-                 "chunk_walk_ms": sum(phase_w[2]) / len(phase_w[2]),
-                 "mfma_frac": flops / (sum(per_step_w) / len(per_step_w) * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)},
+                     "algorithmic_flops": flops,
+                     "kernel_ms": walk_launch_ms,
+                     "timing": "HIP events around %d back-to-back walk launches" % n_walk},
+        "warm": {"ms_per_step": wall_w * 1e3 / args.steps,
+                 "tokens_per_s": B * T / (wall_w / args.steps),
+                 "mfma_frac": flops / (wall_w / args.steps) / (PEAK_BF16_TFLOPS * 1e12)},
     }
     if not args.no_cpu_baseline:
+        import oracle
         threads = args.cpu_threads
         qc, kc, vc = (x.cpu() for x in (q0, k0, v0))
-        secs = time_oracle_prefill(qc, kc, vc, threads)
-        res["cpu_baseline"] = {"value": B * T / secs, "unit": "tokens/s", "cores": threads,
+        reps, secs = repeat_for(lambda: oracle.recurrence(qc, kc, vc, nthreads=threads),
+                                args.cpu_seconds)
+        res["cpu_baseline"] = {"value": reps * B * T / secs, "unit": "tokens/s", "cores": threads,
                                "kind": "oracle", "seconds": secs,
-                               "sample": "the whole workload (%d heads x %d tokens), float64 "
-                                         "token-by-token recurrence, one head per thread" % (B * H, T)}
+                               "sample": "the whole workload (%d heads x %d tokens) %d times over, "
+                                         "float64 token-by-token recurrence, one head per thread"
+                                         % (B * H, T, reps)}
     del sets
     torch.cuda.empty_cache()
     return res
 
 
-def bench_decode(args, torch, lla, workloads):
+def bench_decode(args, torch, lla, workloads, profiling):
     cfg = workloads.CONFIGS["c5"]
     dev = torch.device("cuda:0")
     B, H, T, C, d = cfg.B, cfg.H, cfg.T, cfg.C, cfg.dk
@@ -198,31 +203,26 @@ def bench_decode(args, torch, lla, workloads):
     n = args.decode_steps
     qd, kd, vd = workloads.decode_inputs(cfg, n + args.warmup, device=dev)
     o = torch.empty((B, H, d), dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream(dev)
+    calls = [lla.PreparedDecode(qd[i], kd[i], vd[i], S, out=o) for i in range(n + args.warmup)]
     for i in range(args.warmup):
-        lla.decode_step(qd[n + i], kd[n + i], vd[n + i], S, out=o)
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    evs[0].record(stream)
-    for i in range(n):
-        lla.decode_step(qd[i], kd[i], vd[i], S, out=o)
-        evs[i + 1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(n)]
+        calls[n + i]()
+    # The step is one kernel, so the events around the timed steps give its
+    # per-launch duration directly.
+    wall, gpu = _timed(torch, lambda i: calls[i](), n)
+    kern_ms = gpu * 1e3 / n
     ms_step = wall * 1e3 / n
-    kern_ms = sum(per) / n
     nbytes = decode_bytes(B, H, d)
     res = {
         "workload": cfg.name, "B": B, "H": H, "dk": d, "dv": d, "steps": n,
         "value": n / wall, "unit": "steps/s", "ms_per_step": ms_step,
+        "gpu_ms_per_step": gpu * 1e3 / n,
         "tokens_per_s": B * n / wall,
         "hbm_frac": nbytes / (ms_step * 1e-3) / (PEAK_HBM_GBS * 1e9),
-        "roofline": {"kernel": "k_decode_step<bf16,4,16>", "bound": "hbm",
+        "roofline": {"kernel": "k_decode_step_sq<bf16,128,512>", "bound": "hbm",
                      "achieved": nbytes / (kern_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": nbytes / (kern_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                     "traffic": None, "algorithmic_bytes": nbytes},
+                     "traffic": profiling.stored_traffic("decode_step"), "algorithmic_bytes": nbytes,
+                     "kernel_ms": kern_ms, "timing": "HIP events around the timed steps"},
     }
     if not args.no_cpu_baseline:
         # n decode steps of one (b,h) are n iterations of the recurrence from
@@ -231,14 +231,14 @@ def bench_decode(args, torch, lla, workloads):
         nb, ns = 8, min(128, n)
         qs, ks, vs = (x[:ns, :nb].permute(1, 2, 0, 3).contiguous().cpu() for x in (qd, kd, vd))
         threads = args.cpu_threads
-        t0 = time.perf_counter()
-        oracle.recurrence(qs, ks, vs, S_start[:nb], nthreads=threads)
-        secs = time.perf_counter() - t0
-        head_steps_per_s = nb * H * ns / secs
+        reps, secs = repeat_for(lambda: oracle.recurrence(qs, ks, vs, S_start[:nb], nthreads=threads),
+                                args.cpu_seconds)
+        head_steps_per_s = reps * nb * H * ns / secs
         res["cpu_baseline"] = {"value": head_steps_per_s / (B * H), "unit": "steps/s",
                                "cores": threads, "kind": "oracle", "seconds": secs,
                                "sample": "%d sequences x %d heads x %d decode steps (float64), "
-                                         "scaled to the %d states of one step" % (nb, H, ns, B * H)}
+                                         "%d times over, scaled to the %d states of one step"
+                                         % (nb, H, ns, reps, B * H)}
     return res
 
 
@@ -252,6 +252,8 @@ def main():
     ap.add_argument("--prefill-config", default="c3")
     ap.add_argument("--cpu-threads", type=int, default=min(16, os.cpu_count() or 1))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum oracle time of each CPU baseline (the sample is repeated)")
     ap.add_argument("--skip-decode", action="store_true")
     args = ap.parse_args()
 
@@ -264,6 +266,7 @@ def main():
 
     import torch
     import decode_lla_prefill_amd as lla
+    from decode_lla_prefill_amd import profiling
     import workloads
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -271,7 +274,7 @@ def main():
     lla.library()
     torch.cuda.set_device(0)
 
-    pre = bench_prefill(args, torch, lla, workloads)
+    pre = bench_prefill(args, torch, lla, workloads, profiling)
     line = {
         "metric": METRIC, "value": pre["value"], "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": pre["ms_per_step"],
@@ -279,11 +282,15 @@ def main():
         "data": "synthetic", "config": pre["config"], "mfma_frac": pre["mfma_frac"],
         "hbm_gbs": pre["hbm_gbs"], "gpu_ms_per_step": pre["gpu_ms_per_step"],
         "phase_ms": pre["phase_ms"], "roofline": pre["roofline"], "warm": pre["warm"],
+        "timing": "value and ms_per_step: wall clock over the timed steps (synchronised on both "
+                  "sides); gpu_ms_per_step: HIP events around them; phase_ms: HIP events "
+                  "between the phases in a second pass of the same steps (launch gaps "
+                  "included); roofline kernel_ms: HIP events around back-to-back launches",
     }
     if "cpu_baseline" in pre:
         line["cpu_baseline"] = pre["cpu_baseline"]
     if not args.skip_decode:
-        line["decode"] = bench_decode(args, torch, lla, workloads)
+        line["decode"] = bench_decode(args, torch, lla, workloads, profiling)
     print(json.dumps(line))
 
 

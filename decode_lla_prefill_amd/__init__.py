@@ -22,7 +22,7 @@ import torch
 __all__ = [
     "LlaError", "library", "library_path", "state_init", "prefill", "decode_step",
     "prefill_workspace_size", "prefill_segment_chunks", "prefill_segment_states",
-    "prefill_state_scan", "prefill_chunks", "EXPORTS",
+    "prefill_state_scan", "prefill_chunks", "PreparedPrefill", "PreparedDecode", "EXPORTS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -246,3 +246,80 @@ def decode_step(q, k, v, state, out=None):
     _check(lib.lla_decode_step(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H, dk, dv,
                                _ptr(state), _ptr(out), _stream(q)), "lla_decode_step")
     return out
+
+
+class PreparedPrefill:
+    """A prefill whose arguments were checked and marshalled once.
+
+    For loops that call the same prefill on the same buffers many times (the
+    benchmark, a serving loop): calling the object only re-zeroes the state
+    (optional) and calls lla_prefill with the stored pointers on the current
+    stream.  The tensors must stay alive and keep their shapes.
+    """
+
+    def __init__(self, q, k, v, state, chunk, out=None, workspace=None):
+        lib = library()
+        B, H, T, dk, dv = _qkv_shape(q, k, v)
+        _state_check(state, B, H, dk, dv)
+        self.out = _out(out, (B, H, T, dv), q.device)
+        self.workspace, ws_bytes = _workspace(B, H, T, dk, dv, chunk, q.device, workspace)
+        self.state = state
+        self._lib = lib
+        self._fn = lib.lla_prefill
+        self._init = lib.lla_state_init
+        dt, ws = _dtype_code(q), _ptr(self.workspace)
+        self._args = (_ptr(q), _ptr(k), _ptr(v), dt, B, H, T, dk, dv, chunk,
+                      _ptr(state), _ptr(self.out), ws, ws_bytes)
+        self._init_args = (_ptr(state), B, H, dk, dv)
+        self._seg_args = (_ptr(k), _ptr(v), dt, B, H, T, dk, dv, chunk, ws, ws_bytes)
+        self._scan_args = (_ptr(state), B, H, T, dk, dv, chunk, ws, ws_bytes)
+        self._device = q.device
+
+    def _stream(self):
+        return torch.cuda.current_stream(self._device).cuda_stream
+
+    def __call__(self, zero_state: bool = False):
+        st = self._stream()
+        if zero_state:
+            _check(self._init(*self._init_args, st), "lla_state_init")
+        _check(self._fn(*self._args, st), "lla_prefill")
+        return self.out
+
+    # The three phases of the call, one by one (for per-kernel timing).
+    def zero_state(self):
+        _check(self._init(*self._init_args, self._stream()), "lla_state_init")
+
+    def segment_states(self):
+        _check(self._lib.lla_prefill_segment_states(*self._seg_args, self._stream()),
+               "lla_prefill_segment_states")
+
+    def state_scan(self):
+        _check(self._lib.lla_prefill_state_scan(*self._scan_args, self._stream()),
+               "lla_prefill_state_scan")
+
+    def chunks(self):
+        _check(self._lib.lla_prefill_chunks(*self._args, self._stream()), "lla_prefill_chunks")
+        return self.out
+
+
+class PreparedDecode:
+    """A decode step over fixed buffers, marshalled once (see PreparedPrefill)."""
+
+    def __init__(self, q, k, v, state, out=None):
+        lib = library()
+        _need(q, "q", ndim=3)
+        _need(k, "k", dtype=q.dtype, ndim=3)
+        _need(v, "v", dtype=q.dtype, ndim=3)
+        B, H, dk = q.shape
+        dv = v.shape[2]
+        _state_check(state, B, H, dk, dv)
+        self.out = _out(out, (B, H, dv), q.device)
+        self._fn = lib.lla_decode_step
+        self._args = (_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H, dk, dv, _ptr(state),
+                      _ptr(self.out))
+        self._device = q.device
+
+    def __call__(self):
+        _check(self._fn(*self._args, torch.cuda.current_stream(self._device).cuda_stream),
+               "lla_decode_step")
+        return self.out

@@ -26,6 +26,8 @@ def _decode(q, k, v, S, dev):
 @pytest.mark.parametrize("B,H,dk,dv,dtype", [
     (4, 8, 128, 128, torch.bfloat16), (2, 3, 64, 64, torch.bfloat16), (3, 2, 5, 7, torch.bfloat16),
     (1, 4, 128, 12, torch.bfloat16), (2, 2, 128, 128, torch.float32), (1, 1, 1, 1, torch.float32),
+    (3, 1, 64, 64, torch.float32), (2, 2, 64, 128, torch.bfloat16), (2, 2, 128, 64, torch.bfloat16),
+    (1, 2, 32, 32, torch.bfloat16),
 ])
 def test_decode_integers_exact(dev, B, H, dk, dv, dtype):
     g = torch.Generator().manual_seed(B * 100 + dk + dv)
