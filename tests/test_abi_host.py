@@ -1,0 +1,190 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+function include/lla.h declares, and rejects bad arguments with the
+documented status before it enqueues anything.
+
+Every call here fails validation (or is a no-op such as T = 0), so no HIP
+call is made and no device memory is touched: pointers are plain integers.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import decode_lla_prefill_amd as lla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lla.h")
+
+OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_ALIGN, E_ALIAS, E_WS, E_DEV = range(9)
+BF16, F32 = 0, 1
+i64, vp, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lla_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    L = ctypes.CDLL(lla.library_path)
+    L.lla_status_string.restype = ctypes.c_char_p
+    L.lla_status_string.argtypes = [ctypes.c_int]
+    L.lla_prefill_segment_chunks.restype = i64
+    L.lla_prefill_segment_chunks.argtypes = [i64] * 6
+    L.lla_prefill_workspace_size.restype = sz
+    L.lla_prefill_workspace_size.argtypes = [i64] * 6
+    L.lla_prefill.restype = ctypes.c_int
+    L.lla_prefill.argtypes = [vp, vp, vp, ctypes.c_int] + [i64] * 6 + [vp, vp, vp, sz, vp]
+    L.lla_prefill_chunks.restype = ctypes.c_int
+    L.lla_prefill_chunks.argtypes = L.lla_prefill.argtypes
+    L.lla_prefill_segment_states.restype = ctypes.c_int
+    L.lla_prefill_segment_states.argtypes = [vp, vp, ctypes.c_int] + [i64] * 6 + [vp, sz, vp]
+    L.lla_prefill_state_scan.restype = ctypes.c_int
+    L.lla_prefill_state_scan.argtypes = [vp] + [i64] * 6 + [vp, sz, vp]
+    L.lla_decode_step.restype = ctypes.c_int
+    L.lla_decode_step.argtypes = [vp, vp, vp, ctypes.c_int] + [i64] * 4 + [vp, vp, vp]
+    L.lla_state_init.restype = ctypes.c_int
+    L.lla_state_init.argtypes = [vp] + [i64] * 4 + [vp]
+    L.lla_last_device_error.restype = ctypes.c_int
+    return L
+
+
+def test_header_declares_the_documented_entry_points():
+    names = declared_functions()
+    for n in ("lla_prefill", "lla_decode_step", "lla_state_init", "lla_prefill_workspace_size",
+              "lla_status_string", "lla_last_device_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_function(lib):
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_binding_exports_match_header():
+    assert set(lla.EXPORTS) == set(declared_functions())
+
+
+def test_status_strings(lib):
+    seen = set()
+    for code in range(9):
+        s = lib.lla_status_string(code)
+        assert s and s not in seen
+        seen.add(s)
+    assert lib.lla_status_string(99)  # unknown codes still get a string
+    assert lib.lla_last_device_error() == 0
+
+
+# ---- prefill argument checks ------------------------------------------------------
+
+A = 1 << 32  # a 16-byte aligned fake address; buffers are placed far apart
+
+
+class Bufs:
+    def __init__(self, B=1, H=2, T=100, dk=64, dv=64, C=64, dtype=BF16):
+        self.B, self.H, self.T, self.dk, self.dv, self.C, self.dtype = B, H, T, dk, dv, C, dtype
+        self.q, self.k, self.v = A, 2 * A, 3 * A
+        self.S, self.O, self.ws = 4 * A, 5 * A, 6 * A
+        self.ws_bytes = 1 << 30
+
+    def args(self):
+        return (self.q, self.k, self.v, self.dtype, self.B, self.H, self.T, self.dk, self.dv,
+                self.C, self.S, self.O, self.ws, self.ws_bytes, None)
+
+
+@pytest.mark.parametrize("fn", ["lla_prefill", "lla_prefill_chunks"])
+@pytest.mark.parametrize("change,expect", [
+    (dict(q=None), E_NULL), (dict(k=None), E_NULL), (dict(v=None), E_NULL),
+    (dict(O=None), E_NULL), (dict(S=None), E_NULL),
+    (dict(B=0), E_SHAPE), (dict(H=0), E_SHAPE), (dict(T=-1), E_SHAPE),
+    (dict(dk=0), E_SHAPE), (dict(dk=129), E_SHAPE), (dict(dv=129), E_SHAPE),
+    (dict(C=0), E_SHAPE), (dict(C=129), E_SHAPE),
+    (dict(dtype=7), E_DTYPE), (dict(dtype=F32, C=128), E_UNSUP),
+    (dict(q=A + 8), E_ALIGN), (dict(O=5 * A + 4), E_ALIGN), (dict(S=4 * A + 2), E_ALIGN),
+    (dict(O=A + 64), E_ALIAS), (dict(S=3 * A), E_ALIAS), (dict(O=4 * A + 16), E_ALIAS),
+    (dict(T=8192, ws_bytes=16), E_WS), (dict(T=8192, ws=None), E_WS),
+])
+def test_prefill_rejects(lib, fn, change, expect):
+    b = Bufs()
+    for key, val in change.items():
+        setattr(b, key, val)
+    assert getattr(lib, fn)(*b.args()) == expect
+
+
+def test_prefill_empty_prompt_is_a_noop(lib):
+    b = Bufs(T=0)
+    b.q = b.k = b.v = b.O = None  # not needed for T = 0
+    assert lib.lla_prefill(*b.args()) == OK
+
+
+def test_prefill_phase_checks(lib):
+    b = Bufs(T=8192)
+    assert lib.lla_prefill_segment_states(None, b.v, BF16, 1, 2, 8192, 64, 64, 64, b.ws,
+                                          b.ws_bytes, None) == E_NULL
+    assert lib.lla_prefill_segment_states(b.k, b.v, BF16, 1, 2, 8192, 64, 64, 64, b.ws, 8,
+                                          None) == E_WS
+    assert lib.lla_prefill_state_scan(None, 1, 2, 8192, 64, 64, 64, b.ws, b.ws_bytes,
+                                      None) == E_NULL
+    assert lib.lla_prefill_state_scan(b.S, 1, 2, 8192, 64, 200, 64, b.ws, b.ws_bytes,
+                                      None) == E_SHAPE
+
+
+@pytest.mark.parametrize("change,expect", [
+    (dict(q=None), E_NULL), (dict(S=None), E_NULL), (dict(o=None), E_NULL),
+    (dict(B=0), E_SHAPE), (dict(dk=0), E_SHAPE), (dict(dv=200), E_SHAPE),
+    (dict(dtype=5), E_DTYPE), (dict(k=2 * A + 2), E_ALIGN), (dict(S=4 * A + 8), E_ALIGN),
+    (dict(o=4 * A + 64), E_ALIAS), (dict(S=A), E_ALIAS), (dict(o=3 * A), E_ALIAS),
+])
+def test_decode_rejects(lib, change, expect):
+    d = dict(q=A, k=2 * A, v=3 * A, dtype=BF16, B=2, H=4, dk=128, dv=128, S=4 * A, o=5 * A)
+    d.update(change)
+    assert lib.lla_decode_step(d["q"], d["k"], d["v"], d["dtype"], d["B"], d["H"], d["dk"],
+                               d["dv"], d["S"], d["o"], None) == expect
+
+
+def test_state_init_rejects(lib):
+    assert lib.lla_state_init(None, 1, 1, 4, 4, None) == E_NULL
+    assert lib.lla_state_init(A + 4, 1, 1, 4, 4, None) == E_ALIGN
+    assert lib.lla_state_init(A, 0, 1, 4, 4, None) == E_SHAPE
+    assert lib.lla_state_init(A, 1, 1, 4, 300, None) == E_SHAPE
+
+
+# ---- planning: segments and workspace ------------------------------------------------
+
+@pytest.mark.parametrize("B,H,T,d,C", [
+    (1, 1, 8, 2, 4), (1, 1, 7, 2, 4), (4, 8, 1024, 64, 64), (1, 16, 8192, 128, 64),
+    (1, 32, 131072, 128, 128), (256, 32, 4096, 128, 64), (3, 5, 1000, 33, 17), (1, 1, 1, 1, 1),
+])
+def test_segments_cover_the_sequence(lib, B, H, T, d, C):
+    G = lib.lla_prefill_segment_chunks(B, H, T, d, d, C)
+    ws = lib.lla_prefill_workspace_size(B, H, T, d, d, C)
+    n_c = math.ceil(T / C)
+    assert 1 <= G <= n_c
+    n_seg = math.ceil(n_c / G)
+    # one fp32 d x d state per segment per (b,h), or nothing for one segment
+    assert ws == (B * H * n_seg * d * d * 4 if n_seg > 1 else 0)
+    # enough workgroups to fill the chip without one per chunk
+    assert n_seg * B * H * (2 if d > 64 else 1) >= min(n_c * B * H, 256)
+
+
+def test_segment_plan_for_the_t8192_workload(lib):
+    # 128 chunks x 16 heads x 2 value blocks = 4096 chunk-walks, 512 workgroups of 8
+    assert lib.lla_prefill_segment_chunks(1, 16, 8192, 128, 128, 64) == 8
+    assert lib.lla_prefill_workspace_size(1, 16, 8192, 128, 128, 64) == 16 * 16 * 128 * 128 * 4
+
+
+def test_plan_rejects_bad_sizes(lib):
+    assert lib.lla_prefill_segment_chunks(1, 1, 8, 2, 2, 0) == 0
+    assert lib.lla_prefill_workspace_size(0, 1, 8, 2, 2, 4) == 0
+
+
+def test_python_binding_raises_without_touching_the_gpu():
+    import torch
+    q = torch.zeros((1, 1, 8, 2), dtype=torch.bfloat16)
+    S = torch.zeros((1, 1, 2, 2), dtype=torch.float32)
+    with pytest.raises((lla.LlaError, ValueError, RuntimeError)):
+        lla.prefill(q, q, q, S, chunk=4)  # CPU tensors are refused
