@@ -177,8 +177,8 @@ def test_toy_variants_exact(variant):
 # --- invariants -------------------------------------------------------------------
 
 def test_chunking_is_exact_for_every_chunk_size():
-    """Deck, 'Common errors': chunking is an exact reordering; C changes cost,
-    never the result (integer inputs: exact equality for every C)."""
+    """Deck, 'Common errors': chunking reorders the sums exactly, so the chunk
+    size changes only the cost (integer inputs: exact equality for every C)."""
     q, k, v = workloads.integers(1, 1, 37, 6, 5, seed=11)
     qn, kn, vn = (x.double().numpy()[0, 0] for x in (q, k, v))
     O_rec, S_rec = oracle.recurrence(qn, kn, vn)

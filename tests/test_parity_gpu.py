@@ -51,6 +51,8 @@ INT_CASES = [
     (1, 2, 2000, 64, 32, 32, torch.float32),
     (2, 1, 333, 128, 128, 64, torch.float32),
     (1, 1, 50, 3, 2, 7, torch.float32),
+    (1, 2, 37, 16, 16, 1, torch.bfloat16),      # C = 1: the recurrence itself
+    (2, 1, 300, 24, 40, 128, torch.bfloat16),   # C = 128 with odd head dims
 ]
 
 
