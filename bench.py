@@ -156,7 +156,7 @@ def bench_prefill(args, torch, lla, workloads, profiling):
                      "chunk_walk": walk_ms},
         "mfma_frac": flops / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
         "hbm_gbs": nbytes / (ms_step * 1e-3) / 1e9,
-        "roofline": {"kernel": "k_chunk_walk<bf16,64,128,64>", "bound": "hbm",
+        "roofline": {"kernel": "k_chunk_walk_wide<64> (bf16, d=128)", "bound": "hbm",
                      "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS,
                      "traffic": profiling.stored_traffic("chunk_walk"),

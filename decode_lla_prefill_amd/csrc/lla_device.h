@@ -82,13 +82,13 @@ __device__ __forceinline__ void buf_store16(rsrc_t r, uint32_t off, f32x4 x) {
 // can be in flight while the current one is being used: gather() issues the
 // 16-byte loads into registers, scatter() writes them to LDS.  Rows at or past
 // `nrows`, and columns at or past `ncols`, are stored as zero.
-template <typename T, int ROWS, int COLS, typename L>
+template <typename T, int ROWS, int COLS, typename L, int NTH = kThreads>
 struct Tile {
     static constexpr int VE = Vec<T>::n;            // elements per vector
     static constexpr int VPR = COLS / VE;           // vectors per row
     static constexpr int NV = ROWS * VPR;           // vectors per tile
-    static constexpr int NPT = (NV + kThreads - 1) / kThreads;  // per thread
-    static constexpr bool FULL = NV % kThreads == 0;
+    static constexpr int NPT = (NV + NTH - 1) / NTH;  // per thread (NTH threads)
+    static constexpr bool FULL = NV % NTH == 0;
     static_assert(COLS % VE == 0, "tile width must be a whole number of vectors");
 
     u32x4 r[NPT];
@@ -100,21 +100,26 @@ struct Tile {
     __device__ __forceinline__ void init(int64_t ld, int ncols, int tid) {
 #pragma unroll
         for (int n = 0; n < NPT; ++n) {
-            const int e = tid + n * kThreads;
+            const int e = tid + n * NTH;
             const int row = e / VPR, cv = e % VPR;
             off[n] = (e < NV && cv * VE < ncols) ? (uint32_t)((row * ld + cv * VE) * sizeof(T)) : kOutside;
         }
     }
     // Loads the tile whose first row is at g; rows >= nrows read as zero.
     __device__ __forceinline__ void gather(const T* __restrict__ g, int64_t ld, int nrows) {
-        const rsrc_t rs = make_rsrc(g, (uint32_t)(nrows * ld * sizeof(T)));
+        const rsrc_t rs = source(g, ld, nrows);
 #pragma unroll
-        for (int n = 0; n < NPT; ++n) r[n] = buf_load16(rs, off[n]);
+        for (int n = 0; n < NPT; ++n) load(rs, n);
     }
+    // The same in parts: the descriptor of a tile, then its n-th load.
+    __device__ __forceinline__ static rsrc_t source(const T* __restrict__ g, int64_t ld, int nrows) {
+        return make_rsrc(g, (uint32_t)(nrows * ld * sizeof(T)));
+    }
+    __device__ __forceinline__ void load(rsrc_t rs, int n) { r[n] = buf_load16(rs, off[n]); }
     __device__ __forceinline__ void scatter(T* lds, int tid) const {
 #pragma unroll
         for (int n = 0; n < NPT; ++n) {
-            const int e = tid + n * kThreads;
+            const int e = tid + n * NTH;
             if (FULL || e < NV) {
                 const int row = e / VPR, cv = e % VPR;
                 *reinterpret_cast<u32x4*>(lds + L::off(row, cv * VE)) = r[n];
@@ -124,7 +129,7 @@ struct Tile {
     // Element path for shapes the vector path cannot take: straight to LDS.
     __device__ __forceinline__ static void load_scalar(const T* __restrict__ g, int64_t ld,
                                                        int nrows, int ncols, T* lds, int tid) {
-        for (int e = tid; e < ROWS * COLS; e += kThreads) {
+        for (int e = tid; e < ROWS * COLS; e += NTH) {
             const int row = e / COLS, col = e % COLS;
             T x = from_f32<T>(0.0f);
             if (row < nrows && col < ncols) x = g[(int64_t)row * ld + col];

@@ -33,9 +33,10 @@
 
 namespace lla {
 
-template <typename T, int CT_, int D_, int BV_>
+template <typename T, int CT_, int D_, int BV_, int NW_ = kWaves>
 struct WalkCfg {
     static constexpr int CT = CT_, D = D_, BV = BV_;
+    static constexpr int NW = NW_, NTH = NW * kWave;  // waves, threads per workgroup
     static constexpr bool BF = std::is_same<T, bf16>::value;
     // LDS row strides (elements), chosen for the 64 four-byte LDS banks:
     //  Q: 4 (mod 8) dwords -- 16-byte reads of 16 rows and 8-byte reads of
@@ -64,8 +65,8 @@ struct WalkCfg {
     static constexpr int NDT = D / 16;              // 16-wide tiles over the key dim
     static constexpr int NDS = D / 32;              // 32-deep steps over the key dim
     static constexpr int NVT = BV / 16;             // value tiles in the block
-    static constexpr int NVW = (NVT + kWaves - 1) / kWaves;  // value tiles per wave
-    static constexpr bool ALL_WAVES = NVT % kWaves == 0;     // every wave owns tiles
+    static constexpr int NVW = (NVT + NW - 1) / NW;  // value tiles per wave
+    static constexpr bool ALL_WAVES = NVT % NW == 0;  // every wave owns tiles
     static constexpr int NTRI = NT * (NT + 1) / 2;           // lower-triangle tiles
     using Fr = typename Frag<T>::type;
 };
@@ -151,7 +152,7 @@ __device__ __forceinline__ void load_vfrags(typename Cf::Fr (&Vf)[Cf::NVW][Cf::N
                                             int w, int g, int lane) {
 #pragma unroll
     for (int vw = 0; vw < Cf::NVW; ++vw) {
-        const int vt = w + kWaves * vw;
+        const int vt = w + Cf::NW * vw;
 #pragma unroll
         for (int ts = 0; ts < Cf::NTS; ++ts)
             if (Cf::ALL_WAVES || vt < Cf::NVT)
@@ -168,32 +169,58 @@ __device__ __forceinline__ void state_gmem_to_lds(float* lds, const float* g, in
                                                   int nv, int tid) {
     constexpr int VPR = Cf::BV / 4;
     if ((dv & 3) == 0) {
-        for (int e = tid; e < Cf::D * VPR; e += kThreads) {
+        for (int e = tid; e < Cf::D * VPR; e += Cf::NTH) {
             const int d = e / VPR, c = 4 * (e % VPR);
             f32x4 x = {0.f, 0.f, 0.f, 0.f};
             if (d < dk && c < nv) x = *reinterpret_cast<const f32x4*>(g + (int64_t)d * dv + c);
             *reinterpret_cast<f32x4*>(lds + d * Cf::SLD + c) = x;
         }
     } else {
-        for (int e = tid; e < Cf::D * Cf::BV; e += kThreads) {
+        for (int e = tid; e < Cf::D * Cf::BV; e += Cf::NTH) {
             const int d = e / Cf::BV, c = e % Cf::BV;
             lds[d * Cf::SLD + c] = (d < dk && c < nv) ? g[(int64_t)d * dv + c] : 0.0f;
         }
     }
 }
+// The same transfer split in two halves -- loads into registers, then LDS
+// writes -- so that other loads can be issued in between.  Needs dv % 4 == 0
+// and a 16-byte aligned source.
+template <typename Cf>
+struct StateStage {
+    static constexpr int VPR = Cf::BV / 4;
+    static constexpr int NPT = (Cf::D * VPR + Cf::NTH - 1) / Cf::NTH;
+    f32x4 x[NPT];
+    __device__ __forceinline__ void load(const float* g, int dk, int dv, int nv, int tid) {
+        const rsrc_t rs = make_rsrc(g, (uint32_t)(((int64_t)(dk - 1) * dv + nv) * 4));
+#pragma unroll
+        for (int n = 0; n < NPT; ++n) {
+            const int e = tid + n * Cf::NTH, d = e / VPR, c = 4 * (e % VPR);
+            const uint32_t off = (d < dk && c < nv) ? (uint32_t)((d * dv + c) * 4) : kOutside;
+            x[n] = __builtin_bit_cast(f32x4, buf_load16(rs, off));
+        }
+    }
+    __device__ __forceinline__ void store(float* lds, int tid) const {
+#pragma unroll
+        for (int n = 0; n < NPT; ++n) {
+            const int e = tid + n * Cf::NTH, d = e / VPR, c = 4 * (e % VPR);
+            if (e < Cf::D * VPR) *reinterpret_cast<f32x4*>(lds + d * Cf::SLD + c) = x[n];
+        }
+    }
+};
+
 template <typename Cf>
 __device__ __forceinline__ void state_lds_to_gmem(float* g, const float* lds, int dk, int dv,
                                                   int nv, int tid) {
     constexpr int VPR = Cf::BV / 4;
     if ((dv & 3) == 0) {
-        for (int e = tid; e < Cf::D * VPR; e += kThreads) {
+        for (int e = tid; e < Cf::D * VPR; e += Cf::NTH) {
             const int d = e / VPR, c = 4 * (e % VPR);
             if (d < dk && c < nv)
                 *reinterpret_cast<f32x4*>(g + (int64_t)d * dv + c) =
                     *reinterpret_cast<const f32x4*>(lds + d * Cf::SLD + c);
         }
     } else {
-        for (int e = tid; e < Cf::D * Cf::BV; e += kThreads) {
+        for (int e = tid; e < Cf::D * Cf::BV; e += Cf::NTH) {
             const int d = e / Cf::BV, c = e % Cf::BV;
             if (d < dk && c < nv) g[(int64_t)d * dv + c] = lds[d * Cf::SLD + c];
         }
@@ -204,7 +231,7 @@ __device__ __forceinline__ void state_lds_to_regs(f32x4 (&Sacc)[Cf::NVW][Cf::NDT
                                                   int w, int g, int c16) {
 #pragma unroll
     for (int vw = 0; vw < Cf::NVW; ++vw) {
-        const int vt = (Cf::ALL_WAVES || w + kWaves * vw < Cf::NVT) ? w + kWaves * vw : 0;
+        const int vt = (Cf::ALL_WAVES || w + Cf::NW * vw < Cf::NVT) ? w + Cf::NW * vw : 0;
 #pragma unroll
         for (int dt = 0; dt < Cf::NDT; ++dt)
 #pragma unroll
@@ -217,8 +244,8 @@ __device__ __forceinline__ void state_regs_to_lds(float* lds, const f32x4 (&Sacc
                                                   int w, int g, int c16) {
 #pragma unroll
     for (int vw = 0; vw < Cf::NVW; ++vw) {
-        if (!(Cf::ALL_WAVES || w + kWaves * vw < Cf::NVT)) continue;
-        const int vt = w + kWaves * vw;
+        if (!(Cf::ALL_WAVES || w + Cf::NW * vw < Cf::NVT)) continue;
+        const int vt = w + Cf::NW * vw;
 #pragma unroll
         for (int dt = 0; dt < Cf::NDT; ++dt)
 #pragma unroll
@@ -240,9 +267,175 @@ __device__ __forceinline__ void state_hop(f32x4 (&Sacc)[Cf::NVW][Cf::NDT],
             const typename Cf::Fr kt = lds_col(Ks, Cf::LK, 32 * ts, 16 * dt, lane);
 #pragma unroll
             for (int vw = 0; vw < Cf::NVW; ++vw)
-                if (Cf::ALL_WAVES || w + kWaves * vw < Cf::NVT)
+                if (Cf::ALL_WAVES || w + Cf::NW * vw < Cf::NVT)
                     Sacc[vw][dt] = mma(kt, Vf[vw][ts], Sacc[vw][dt]);
         }
+    }
+}
+
+// ---- the math of one chunk, shared by the walk kernels ---------------------------
+
+// Masked scores of the chunk staged in Qs, Ks -> P (Ps), for the tiles wave w
+// owns.  Every wave of the workgroup must call it; Ps is complete after the
+// next barrier.
+struct NoHook {
+    __device__ __forceinline__ void operator()(int) const {}
+};
+
+// The score tiles wave w owns: triangle tiles e = w, w + NW, ... as (query
+// tile it, key tile jt) pairs.  A wave short of tiles repeats the last one
+// (computed, not stored).  Depends on the wave alone: built once per kernel.
+template <typename Cf>
+struct ScoreTiles {
+    static constexpr int PW = (Cf::NTRI + Cf::NW - 1) / Cf::NW;
+    int it[PW], jt[PW];
+    bool own[PW];
+    __device__ __forceinline__ explicit ScoreTiles(int w) {
+#pragma unroll
+        for (int m = 0; m < PW; ++m) {
+            const int e0 = w + Cf::NW * m;
+            const int e = e0 < Cf::NTRI ? e0 : Cf::NTRI - 1;
+            int row = 0;
+#pragma unroll
+            for (int k = 1; k < Cf::NT; ++k) row += k * (k + 1) / 2 <= e;
+            it[m] = row;
+            jt[m] = e - row * (row + 1) / 2;
+            own[m] = e0 < Cf::NTRI;
+        }
+    }
+};
+
+// `hook(ds)` runs after the matrix-core ops of depth step ds: a caller can
+// place other work (global stores, loads) between the steps.
+template <typename Cf, typename T, typename Hook = NoHook>
+__device__ __forceinline__ void chunk_scores(const ScoreTiles<Cf>& st, const T* Qs, const T* Ks, T* Ps,
+                                             int w, int g, int c16, const Hook& hook = Hook()) {
+    // Scores of the kept triangle, computed transposed: tile (jt, it) holds
+    // A^T = K_c Q_c^T, i.e. lane (g, c16) has A[i][j] for query
+    // i = 16 it + c16 and keys j = 16 jt + 4g + r.  Entries with j > i are
+    // masked in registers; the rest is rounded to the input type (P).
+    // Wave w owns tiles w, w + NW, ... of the triangle and runs them as
+    // independent accumulators (a wave short of tiles recomputes the last
+    // one and does not store it), so the matrix-core latency overlaps.
+    {
+        constexpr int PW = ScoreTiles<Cf>::PW;
+        const int* tit = st.it;
+        const int* tjt = st.jt;
+        f32x4 sacc[PW];
+#pragma unroll
+        for (int m = 0; m < PW; ++m) sacc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ds = 0; ds < Cf::NDS; ++ds) {
+#pragma unroll
+            for (int m = 0; m < PW; ++m)
+                sacc[m] = mma(lds_row(Ks + (16 * tjt[m] + c16) * Cf::LK + 32 * ds + 8 * g),
+                              lds_row(Qs + (16 * tit[m] + c16) * Cf::LQ + 32 * ds + 8 * g), sacc[m]);
+            hook(ds);
+        }
+#pragma unroll
+        for (int m = 0; m < PW; ++m) {
+            if (!st.own[m]) continue;
+            const int i = 16 * tit[m] + c16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (16 * tjt[m] + 4 * g + r > i) sacc[m][r] = 0.0f;
+            lds_store4(Ps + i * Cf::LP + 16 * tjt[m] + 4 * g, sacc[m]);
+        }
+    }
+    // Tiles right of the diagonal that a 32-deep step still reads: zero.
+    for (int it = 2 * w; it + 1 < Cf::NT; it += 2 * Cf::NW)
+        lds_store4(Ps + (16 * it + c16) * Cf::LP + 16 * (it + 1) + 4 * g, f32x4{0.f, 0.f, 0.f, 0.f});
+}
+
+// O_c for the value tiles wave w owns: Oacc[it][vw] = (P V_c + Q_c S_c)^T,
+// from P (Ps), the wave's V operand slices Vf, Q (Qs) and the state slice
+// Sacc.  Oacc is overwritten.
+// One depth step of the state operand: value row c16, depth slots {4g + r}
+// from tile 2ds and {16 + 4g + r} from tile 2ds + 1 -- exactly the elements
+// the lane already holds.  bf16 inputs: S = hi + lo (lo is zero for fp32).
+template <typename Cf>
+__device__ __forceinline__ void state_operand(typename Cf::Fr& hi, typename Cf::Fr& lo,
+                                              const f32x4 (&Sv)[Cf::NDT], int ds) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        const float x = Sv[2 * ds + (s >> 2)][s & 3];
+        if constexpr (Cf::BF) {
+            const bf16 h = to_bf16(x);
+            hi[s] = h;
+            lo[s] = to_bf16(x - to_f32(h));
+        } else {
+            hi[s] = x;
+        }
+    }
+}
+
+// O_c for the value tiles wave w owns: Oacc[it][vw] = (P V_c + Q_c S_c)^T,
+// from P (Ps), the wave's V operand slices Vf, Q (Qs) and the state slice
+// Sacc.  Oacc is overwritten.  The Q S part is software pipelined: the Q
+// slices and the state operand of depth step ds + 1 are read and formed
+// while the matrix-core ops of step ds run; `hook(ds)` runs after step ds.
+template <typename Cf, typename T, typename Hook = NoHook>
+__device__ __forceinline__ void chunk_output(f32x4 (&Oacc)[Cf::NT][Cf::NVW],
+                                             const f32x4 (&Sacc)[Cf::NVW][Cf::NDT],
+                                             const typename Cf::Fr (&Vf)[Cf::NVW][Cf::NTS],
+                                             const T* Qs, const T* Ps, int w, int g, int c16,
+                                             const Hook& hook = Hook()) {
+    using Fr = typename Cf::Fr;
+    auto q_slices = [&](Fr (&qb)[Cf::NT], int ds) {
+#pragma unroll
+        for (int it = 0; it < Cf::NT; ++it) {
+            const int i = 16 * it + c16;
+            qb[it] = lds_row2(Qs + i * Cf::LQ + 32 * ds + 4 * g, Qs + i * Cf::LQ + 32 * ds + 16 + 4 * g);
+        }
+    };
+    auto owns = [&](int vw) { return Cf::ALL_WAVES || w + Cf::NW * vw < Cf::NVT; };
+
+    Fr qb[2][Cf::NT], Shi[2][Cf::NVW], Slo[2][Cf::NVW];
+    q_slices(qb[0], 0);
+#pragma unroll
+    for (int vw = 0; vw < Cf::NVW; ++vw) state_operand<Cf>(Shi[0][vw], Slo[0][vw], Sacc[vw], 0);
+
+    // All query tiles of the chunk are accumulated side by side (depth
+    // outer, tile inner), so consecutive matrix-core ops are independent.
+#pragma unroll
+    for (int it = 0; it < Cf::NT; ++it)
+#pragma unroll
+        for (int vw = 0; vw < Cf::NVW; ++vw) Oacc[it][vw] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // masked scores times values: a 32-deep time step ts reaches query
+    // tiles it >= 2 ts (steps right of the diagonal are all zero)
+#pragma unroll
+    for (int ts = 0; ts < Cf::NTS; ++ts) {
+#pragma unroll
+        for (int it = 2 * ts; it < Cf::NT; ++it) {
+            const int i = 16 * it + c16;
+            const Fr pb = lds_row2(Ps + i * Cf::LP + 32 * ts + 4 * g,
+                                   Ps + i * Cf::LP + 32 * ts + 16 + 4 * g);
+#pragma unroll
+            for (int vw = 0; vw < Cf::NVW; ++vw)
+                if (owns(vw)) Oacc[it][vw] = mma(Vf[vw][ts], pb, Oacc[it][vw]);
+        }
+    }
+    // incoming state read: Q_c S_c
+#pragma unroll
+    for (int ds = 0; ds < Cf::NDS; ++ds) {
+        const int cur = ds & 1, nxt = cur ^ 1;
+        if (ds + 1 < Cf::NDS) {
+            q_slices(qb[nxt], ds + 1);
+#pragma unroll
+            for (int vw = 0; vw < Cf::NVW; ++vw)
+                state_operand<Cf>(Shi[nxt][vw], Slo[nxt][vw], Sacc[vw], ds + 1);
+        }
+#pragma unroll
+        for (int vw = 0; vw < Cf::NVW; ++vw) {
+            if (!owns(vw)) continue;
+#pragma unroll
+            for (int it = 0; it < Cf::NT; ++it) Oacc[it][vw] = mma(Shi[cur][vw], qb[cur][it], Oacc[it][vw]);
+            if constexpr (Cf::BF) {
+#pragma unroll
+                for (int it = 0; it < Cf::NT; ++it) Oacc[it][vw] = mma(Slo[cur][vw], qb[cur][it], Oacc[it][vw]);
+            }
+        }
+        hook(ds);
     }
 }
 
@@ -394,8 +587,8 @@ __device__ __forceinline__ void store_out(float* Ob, const f32x4 (&Oacc)[Cf::NT]
             const int i = 16 * it + c16;
 #pragma unroll
             for (int vw = 0; vw < Cf::NVW; ++vw) {
-                const int v = 16 * (w + kWaves * vw) + 4 * g;
-                if (!(Cf::ALL_WAVES || w + kWaves * vw < Cf::NVT)) continue;
+                const int v = 16 * (w + Cf::NW * vw) + 4 * g;
+                if (!(Cf::ALL_WAVES || w + Cf::NW * vw < Cf::NVT)) continue;
                 const uint32_t off = v < nv ? (uint32_t)((i * dv + v) * 4) : kOutside;
                 buf_store16(rs, off, Oacc[it][vw]);
             }
@@ -408,8 +601,8 @@ __device__ __forceinline__ void store_out(float* Ob, const f32x4 (&Oacc)[Cf::NT]
             float* orow = Ob + (t0 + i) * dv;
 #pragma unroll
             for (int vw = 0; vw < Cf::NVW; ++vw) {
-                const int v = 16 * (w + kWaves * vw) + 4 * g;
-                if (!(Cf::ALL_WAVES || w + kWaves * vw < Cf::NVT) || v >= nv) continue;
+                const int v = 16 * (w + Cf::NW * vw) + 4 * g;
+                if (!(Cf::ALL_WAVES || w + Cf::NW * vw < Cf::NVT) || v >= nv) continue;
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     if (v + r < nv) orow[v + r] = Oacc[it][vw][r];
@@ -438,6 +631,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_walk(
     int vb;
     split_id(blockIdx.x, (int64_t)(gridDim.x / n_vb), n_vb, line, vb);
     const int64_t bh = line / n_seg, seg = line - bh * n_seg;
+    const ScoreTiles<Cf> stiles(w);
     const int v0 = vb * BV;
     const int nv = min(BV, dv - v0);  // valid columns of this block
     const int64_t n_c = (T_len + C - 1) / C;
@@ -500,113 +694,14 @@ __global__ __launch_bounds__(kThreads) void k_chunk_walk(
             }
         }
 
-        // (1) Scores of the kept triangle, computed transposed: tile (jt, it)
-        // holds A^T = K_c Q_c^T, i.e. lane (g, c16) has A[i][j] for query
-        // i = 16 it + c16 and keys j = 16 jt + 4g + r.  Entries with j > i are
-        // masked in registers; the rest is rounded to the input type (P).
-        // Wave w owns tiles w, w + 4, ... of the triangle and runs them as
-        // independent accumulators (a wave short of tiles recomputes the last
-        // one and does not store it), so the matrix-core latency overlaps.
-        {
-            constexpr int PW = (Cf::NTRI + kWaves - 1) / kWaves;
-            int tit[PW], tjt[PW];
-            f32x4 sacc[PW];
-#pragma unroll
-            for (int m = 0; m < PW; ++m) {
-                int e = w + kWaves * m;
-                e = e < Cf::NTRI ? e : Cf::NTRI - 1;
-                int it = 0;
-                while ((it + 1) * (it + 2) / 2 <= e) ++it;
-                tit[m] = it;
-                tjt[m] = e - it * (it + 1) / 2;
-                sacc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-#pragma unroll
-            for (int ds = 0; ds < Cf::NDS; ++ds)
-#pragma unroll
-                for (int m = 0; m < PW; ++m)
-                    sacc[m] = mma(lds_row(Ks + (16 * tjt[m] + c16) * Cf::LK + 32 * ds + 8 * g),
-                                  lds_row(Qs + (16 * tit[m] + c16) * Cf::LQ + 32 * ds + 8 * g), sacc[m]);
-#pragma unroll
-            for (int m = 0; m < PW; ++m) {
-                if (w + kWaves * m >= Cf::NTRI) continue;
-                const int i = 16 * tit[m] + c16;
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (16 * tjt[m] + 4 * g + r > i) sacc[m][r] = 0.0f;
-                lds_store4(Ps + i * Cf::LP + 16 * tjt[m] + 4 * g, sacc[m]);
-            }
-        }
-        // Tiles right of the diagonal that a 32-deep step still reads: zero.
-        for (int it = 2 * w; it + 1 < Cf::NT; it += 2 * kWaves)
-            lds_store4(Ps + (16 * it + c16) * Cf::LP + 16 * (it + 1) + 4 * g, f32x4{0.f, 0.f, 0.f, 0.f});
+        chunk_scores<Cf>(stiles, Qs, Ks, Ps, w, g, c16);
         __syncthreads();
 
         // (2) Output, transposed: O^T tile (vt, it) = V^T P^T + S^T Q^T.
         Fr Vf[Cf::NVW][Cf::NTS];
         load_vfrags<Cf>(Vf, Vs, w, g, lane);
 
-        // The state as the first operand: value row c16, depth slots
-        // {4g + r} from tile 2ds and {16 + 4g + r} from tile 2ds + 1 -- exactly
-        // the elements the lane already holds.  bf16 inputs: S = hi + lo.
-        Fr Shi[Cf::NVW][Cf::NDS], Slo[Cf::NVW][Cf::NDS];
-#pragma unroll
-        for (int vw = 0; vw < Cf::NVW; ++vw)
-#pragma unroll
-            for (int ds = 0; ds < Cf::NDS; ++ds)
-#pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    const float x = Sacc[vw][2 * ds + (s >> 2)][s & 3];
-                    if constexpr (Cf::BF) {
-                        const bf16 h = to_bf16(x);
-                        Shi[vw][ds][s] = h;
-                        Slo[vw][ds][s] = to_bf16(x - to_f32(h));
-                    } else {
-                        Shi[vw][ds][s] = x;
-                    }
-                }
-
-        // All query tiles of the chunk are accumulated side by side (depth
-        // outer, tile inner), so consecutive matrix-core ops are independent.
-#pragma unroll
-        for (int it = 0; it < Cf::NT; ++it)
-#pragma unroll
-            for (int vw = 0; vw < Cf::NVW; ++vw) Oacc[it][vw] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // masked scores times values: a 32-deep time step ts reaches query
-        // tiles it >= 2 ts (steps right of the diagonal are all zero)
-#pragma unroll
-        for (int ts = 0; ts < Cf::NTS; ++ts) {
-#pragma unroll
-            for (int it = 2 * ts; it < Cf::NT; ++it) {
-                const int i = 16 * it + c16;
-                const Fr pb = lds_row2(Ps + i * Cf::LP + 32 * ts + 4 * g,
-                                       Ps + i * Cf::LP + 32 * ts + 16 + 4 * g);
-#pragma unroll
-                for (int vw = 0; vw < Cf::NVW; ++vw)
-                    if (Cf::ALL_WAVES || w + kWaves * vw < Cf::NVT)
-                        Oacc[it][vw] = mma(Vf[vw][ts], pb, Oacc[it][vw]);
-            }
-        }
-        // incoming state read: Q_c S_c
-#pragma unroll
-        for (int ds = 0; ds < Cf::NDS; ++ds) {
-            Fr qb[Cf::NT];
-#pragma unroll
-            for (int it = 0; it < Cf::NT; ++it) {
-                const int i = 16 * it + c16;
-                qb[it] = lds_row2(Qs + i * Cf::LQ + 32 * ds + 4 * g, Qs + i * Cf::LQ + 32 * ds + 16 + 4 * g);
-            }
-#pragma unroll
-            for (int vw = 0; vw < Cf::NVW; ++vw) {
-                if (!(Cf::ALL_WAVES || w + kWaves * vw < Cf::NVT)) continue;
-#pragma unroll
-                for (int it = 0; it < Cf::NT; ++it) Oacc[it][vw] = mma(Shi[vw][ds], qb[it], Oacc[it][vw]);
-                if constexpr (Cf::BF) {
-#pragma unroll
-                    for (int it = 0; it < Cf::NT; ++it) Oacc[it][vw] = mma(Slo[vw][ds], qb[it], Oacc[it][vw]);
-                }
-            }
-        }
+        chunk_output<Cf>(Oacc, Sacc, Vf, Qs, Ps, w, g, c16);
         t_prev = t0;
         n_prev = nrows;
 
@@ -621,6 +716,141 @@ __global__ __launch_bounds__(kThreads) void k_chunk_walk(
         state_regs_to_lds<Cf>(Sst, Sacc, w, g, c16);
         __syncthreads();
         state_lds_to_gmem<Cf>(S + bh * dkdv + v0, Sst, dk, dv, nv, tid);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Phase 3, wide form for d = 128 bf16 inputs and chunks of up to 64 tokens:
+// one workgroup of eight waves per (b,h) and segment covers all 128 value
+// columns (wave w owns value tile w), so the score triangle is computed and
+// the Q, K tiles are loaded once per chunk.  Q, K, V are double buffered in
+// LDS: while chunk c is computed from one buffer, chunk c+1 is written into
+// the other from registers loaded one chunk earlier and the loads of chunk
+// c+2 are issued -- two barriers per chunk, none of them behind a load.
+// ---------------------------------------------------------------------------
+template <int CT>
+struct WideCfg : WalkCfg<bf16, CT, 128, 128, 8> {
+    using Base = WalkCfg<bf16, CT, 128, 128, 8>;
+    static constexpr int BUF = Base::P_OFF;  // elements of one Q, K, V buffer
+    static constexpr int TILE_BYTES = (2 * BUF + CT * Base::LP) * 2;
+    static constexpr int BYTES = TILE_BYTES > Base::STATE_BYTES ? TILE_BYTES : Base::STATE_BYTES;
+};
+
+template <int CT>
+__global__ __launch_bounds__(512) void k_chunk_walk_wide(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    float* __restrict__ S, float* __restrict__ O, const float* __restrict__ ws, int64_t T_len,
+    int dk, int dv, int C, int64_t G, int64_t n_seg) {
+    using Cf = WideCfg<CT>;
+    using Fr = typename Cf::Fr;
+    constexpr int NTH = Cf::NTH;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Cf::BYTES];
+    bf16* const buf = reinterpret_cast<bf16*>(smem);
+    bf16* const Ps = buf + 2 * Cf::BUF;
+    float* const Sst = reinterpret_cast<float*>(smem);
+
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t line = blockIdx.x;
+    const ScoreTiles<Cf> stiles(w);
+    const int64_t bh = line / n_seg, seg = line - bh * n_seg;
+    const int64_t n_c = (T_len + C - 1) / C;
+    const int64_t c0 = seg * G, c1 = min(n_c, c0 + G);
+    const bool last_seg = seg == n_seg - 1;
+    const int64_t dkdv = (int64_t)dk * dv;
+    const bf16* Qb = Q + bh * T_len * dk;
+    const bf16* Kb = K + bh * T_len * dk;
+    const bf16* Vb = V + bh * T_len * dv;
+    float* Ob = O + bh * T_len * dv;
+    auto rows_of = [&](int64_t c) { return c < c1 ? (int)min((int64_t)C, T_len - c * C) : 0; };
+
+    // Incoming state (loads first), then the first chunk's tile loads.
+    const float* Sin = n_seg == 1 ? S + bh * dkdv : ws + (bh * n_seg + seg) * dkdv;
+    StateStage<Cf> ss;
+    ss.load(Sin, dk, dv, dv, tid);
+    Tile<bf16, CT, 128, typename Cf::LQL, NTH> tq;
+    Tile<bf16, CT, 128, typename Cf::LKL, NTH> tk;
+    Tile<bf16, CT, 128, typename Cf::LVL, NTH> tv;
+    tq.init(dk, dk, tid);
+    tk.init(dk, dk, tid);
+    tv.init(dv, dv, tid);
+    tq.gather(Qb + c0 * C * dk, dk, rows_of(c0));
+    tk.gather(Kb + c0 * C * dk, dk, rows_of(c0));
+    tv.gather(Vb + c0 * C * dv, dv, rows_of(c0));
+    ss.store(Sst, tid);
+    __syncthreads();
+    f32x4 Sacc[Cf::NVW][Cf::NDT];
+    state_lds_to_regs<Cf>(Sacc, Sst, w, g, c16);
+    __syncthreads();  // the state area is reused by the tiles
+    tq.scatter(buf, tid);
+    tk.scatter(buf + Cf::K_OFF, tid);
+    tv.scatter(buf + Cf::V_OFF, tid);
+    tq.gather(Qb + (c0 + 1) * C * dk, dk, rows_of(c0 + 1));
+    tk.gather(Kb + (c0 + 1) * C * dk, dk, rows_of(c0 + 1));
+    tv.gather(Vb + (c0 + 1) * C * dv, dv, rows_of(c0 + 1));
+    __syncthreads();
+
+    // A chunk's outputs are stored during the next chunk (see k_chunk_walk).
+    f32x4 Oacc[Cf::NT][Cf::NVW];
+#pragma unroll
+    for (int it = 0; it < Cf::NT; ++it) Oacc[it][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    int64_t t_prev = 0;
+    int n_prev = 0;
+
+    for (int64_t c = c0; c < c1; ++c) {
+        const int b = (int)((c - c0) & 1);
+        const bf16* Qs = buf + b * Cf::BUF;
+        const bf16* Ks = Qs + Cf::K_OFF;
+        const bf16* Vs = Qs + Cf::V_OFF;
+        bf16* nxt = buf + (1 - b) * Cf::BUF;
+
+        // The global traffic of a chunk is spread over its math, so that
+        // the eight waves do not queue their memory instructions at once:
+        // the previous chunk's output tiles are stored one per depth step of
+        // the scores, the loads of chunk c + 2 go between the depth steps of
+        // the output.
+        const rsrc_t rso = make_rsrc(Ob + t_prev * dv, (uint32_t)(n_prev * dv * 4));
+        const int vcol = 16 * w + 4 * g;
+        chunk_scores<Cf>(stiles, Qs, Ks, Ps, w, g, c16, [&](int ds) {
+            if (ds < Cf::NT) {
+                const uint32_t off = vcol < dv ? (uint32_t)(((16 * ds + c16) * dv + vcol) * 4) : kOutside;
+                buf_store16(rso, off, Oacc[ds][0]);
+            }
+        });
+        // The next chunk into the free buffer (its last readers finished
+        // before the previous barrier).
+        if (c + 1 < c1) {
+            tq.scatter(nxt, tid);
+            tk.scatter(nxt + Cf::K_OFF, tid);
+            tv.scatter(nxt + Cf::V_OFF, tid);
+        }
+        __syncthreads();  // P complete
+
+        const int64_t t2 = (c + 2) * C;
+        const int n2 = rows_of(c + 2);
+        const rsrc_t rq = tq.source(Qb + t2 * dk, dk, n2), rk = tk.source(Kb + t2 * dk, dk, n2),
+                     rv = tv.source(Vb + t2 * dv, dv, n2);
+        Fr Vf[Cf::NVW][Cf::NTS];
+        load_vfrags<Cf>(Vf, Vs, w, g, lane);
+        chunk_output<Cf>(Oacc, Sacc, Vf, Qs, Ps, w, g, c16, [&](int ds) {
+#pragma unroll
+            for (int n = 0; n < decltype(tq)::NPT; ++n) {
+                if (ds == 0) tq.load(rq, n);
+                if (ds == 1) tk.load(rk, n);
+                if (ds == 2) tv.load(rv, n);
+            }
+        });
+        t_prev = c * C;
+        n_prev = rows_of(c);
+        if (c + 1 < c1 || last_seg) state_hop<Cf>(Sacc, Vf, Ks, w, g, lane);
+        __syncthreads();  // this buffer and P free; the next buffer visible
+    }
+    store_out<Cf, true>(Ob, Oacc, t_prev, n_prev, dv, dv, w, g, c16);
+
+    if (last_seg) {  // (the loop ended with a barrier: the tiles are free)
+        state_regs_to_lds<Cf>(Sst, Sacc, w, g, c16);
+        __syncthreads();
+        state_lds_to_gmem<Cf>(S + bh * dkdv, Sst, dk, dv, dv, tid);
     }
 }
 
@@ -647,6 +877,14 @@ void plan_prefill(PrefillPlan& p) {
 template <typename T, int CT, int D>
 static hipError_t launch_walk_t(const PrefillPlan& p, const void* Q, const void* K, const void* V,
                                 float* S, float* O, float* ws, hipStream_t st) {
+    if constexpr (std::is_same<T, bf16>::value && D == 128 && CT <= 64) {
+        if (p.vec) {  // one eight-wave workgroup per (b,h) and segment
+            hipLaunchKernelGGL((k_chunk_walk_wide<CT>), dim3((unsigned)(p.BH * p.n_seg)), dim3(512), 0, st,
+                               (const bf16*)Q, (const bf16*)K, (const bf16*)V, S, O, (const float*)ws,
+                               p.T, p.dk, p.dv, p.C, p.G, p.n_seg);
+            return hipGetLastError();
+        }
+    }
     constexpr int BV = D > 64 ? 64 : D;
     const int64_t grid = p.BH * p.n_seg * p.n_vb;
     if (p.vec)

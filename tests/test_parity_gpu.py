@@ -53,6 +53,8 @@ INT_CASES = [
     (1, 1, 50, 3, 2, 7, torch.float32),
     (1, 2, 37, 16, 16, 1, torch.bfloat16),      # C = 1: the recurrence itself
     (2, 1, 300, 24, 40, 128, torch.bfloat16),   # C = 128 with odd head dims
+    (1, 3, 500, 128, 128, 32, torch.bfloat16),  # C = 32 at d = 128
+    (2, 2, 260, 104, 120, 20, torch.bfloat16),  # ragged chunks, partial columns
 ]
 
 
