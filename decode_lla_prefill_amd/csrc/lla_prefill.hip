@@ -855,6 +855,110 @@ __global__ __launch_bounds__(512) void k_chunk_walk_wide(
 }
 
 // ---------------------------------------------------------------------------
+// Phase 1, wide form for d = 128 bf16 inputs and chunks of up to 64 tokens:
+// one workgroup of eight waves per (b,h) and segment (all but the last)
+// covers all 128 value columns, so K is loaded once.  The K, V tiles are
+// double buffered: chunk c + 1 is written into the free buffer while chunk
+// c is reduced, and the loads of chunk c + 2 go between the matrix-core
+// steps -- one barrier per chunk.
+// ---------------------------------------------------------------------------
+template <int CT>
+struct SegWideCfg : WalkCfg<bf16, CT, 128, 128, 8> {
+    using Base = WalkCfg<bf16, CT, 128, 128, 8>;
+    static constexpr int V_AT = CT * Base::LK;             // V tile inside a buffer
+    static constexpr int BUF = V_AT + CT * Base::LV;       // elements of one K, V buffer
+    static constexpr int TILE_BYTES = 2 * BUF * 2;
+    static constexpr int BYTES = TILE_BYTES > Base::STATE_BYTES ? TILE_BYTES : Base::STATE_BYTES;
+};
+
+template <int CT>
+__global__ __launch_bounds__(512) void k_segment_states_wide(const bf16* __restrict__ K,
+                                                             const bf16* __restrict__ V,
+                                                             float* __restrict__ ws, int64_t T_len,
+                                                             int dk, int dv, int C, int64_t G,
+                                                             int64_t n_seg) {
+    using Cf = SegWideCfg<CT>;
+    using Fr = typename Cf::Fr;
+    constexpr int NTH = Cf::NTH;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Cf::BYTES];
+    bf16* const buf = reinterpret_cast<bf16*>(smem);
+    float* const Sst = reinterpret_cast<float*>(smem);
+
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t nsm1 = n_seg - 1;
+    const int64_t bh = blockIdx.x / nsm1, seg = blockIdx.x - bh * nsm1;
+    const int64_t n_c = (T_len + C - 1) / C;
+    const int64_t c0 = seg * G, c1 = min(n_c, c0 + G);
+    const bf16* Kb = K + bh * T_len * dk;
+    const bf16* Vb = V + bh * T_len * dv;
+    auto rows_of = [&](int64_t c) { return c < c1 ? (int)min((int64_t)C, T_len - c * C) : 0; };
+
+    f32x4 Sacc[Cf::NVW][Cf::NDT];
+#pragma unroll
+    for (int dt = 0; dt < Cf::NDT; ++dt) Sacc[0][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // PF register sets, used round robin (the loop is unrolled by PF so the
+    // sets are static): the loads of chunk c + PF are issued while chunk c
+    // is reduced, PF - 1 chunks ahead of their use.  Deeper rings measured
+    // slower (more registers, two workgroups per CU either way).
+    constexpr int PF = 2;
+    Tile<bf16, CT, 128, typename Cf::LKL, NTH> tk[PF];
+    Tile<bf16, CT, 128, typename Cf::LVL, NTH> tv[PF];
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+        tk[u].init(dk, dk, tid);
+        tv[u].init(dv, dv, tid);
+        tk[u].gather(Kb + (c0 + u) * C * dk, dk, rows_of(c0 + u));
+        tv[u].gather(Vb + (c0 + u) * C * dv, dv, rows_of(c0 + u));
+    }
+    tk[0].scatter(buf, tid);
+    tv[0].scatter(buf + Cf::V_AT, tid);
+    __syncthreads();
+
+    for (int64_t cb = c0; cb < c1; cb += PF) {
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+            const int64_t c = cb + u;
+            if (c >= c1) break;
+            const int b = (int)((c - c0) & 1);
+            const bf16* Ks = buf + b * Cf::BUF;
+            const bf16* Vs = Ks + Cf::V_AT;
+            bf16* nxt = buf + (1 - b) * Cf::BUF;
+            const int un = (u + 1) % PF;  // the set holding chunk c + 1 (static after unrolling)
+            if (c + 1 < c1) {  // the free buffer's last readers passed the previous barrier
+                tk[un].scatter(nxt, tid);
+                tv[un].scatter(nxt + Cf::V_AT, tid);
+            }
+            // set u held chunk c, written to LDS one chunk ago: reload it
+            const int64_t tn = (c + PF) * C;
+            const int nn = rows_of(c + PF);
+            const rsrc_t rk = tk[u].source(Kb + tn * dk, dk, nn), rv = tv[u].source(Vb + tn * dv, dv, nn);
+
+            Fr Vf[Cf::NVW][Cf::NTS];
+            load_vfrags<Cf>(Vf, Vs, w, g, lane);
+#pragma unroll
+            for (int dt = 0; dt < Cf::NDT; ++dt) {
+#pragma unroll
+                for (int ts = 0; ts < Cf::NTS; ++ts)
+                    Sacc[0][dt] = mma(lds_col(Ks, Cf::LK, 32 * ts, 16 * dt, lane), Vf[0][ts], Sacc[0][dt]);
+#pragma unroll
+                for (int n = 0; n < Tile<bf16, CT, 128, typename Cf::LKL, NTH>::NPT; ++n) {
+                    if (dt == 1) tk[u].load(rk, n);
+                    if (dt == 3) tv[u].load(rv, n);
+                }
+            }
+            __syncthreads();  // this buffer free; the next one visible
+        }
+    }
+
+    // (the loop ended with a barrier: the tiles are free)
+    state_regs_to_lds<Cf>(Sst, Sacc, w, g, c16);
+    __syncthreads();
+    state_lds_to_gmem<Cf>(ws + (bh * n_seg + seg + 1) * (int64_t)dk * dv, Sst, dk, dv, dv, tid);
+}
+
+// ---------------------------------------------------------------------------
 // Host side: planning and dispatch over (input type, chunk tile, head dim).
 // ---------------------------------------------------------------------------
 static int pad_dim(int x) { return x <= 32 ? 32 : (x <= 64 ? 64 : 128); }
@@ -901,6 +1005,14 @@ static hipError_t launch_walk_t(const PrefillPlan& p, const void* Q, const void*
 template <typename T, int CT, int D>
 static hipError_t launch_seg_t(const PrefillPlan& p, const void* K, const void* V, float* ws,
                                hipStream_t st) {
+    if constexpr (std::is_same<T, bf16>::value && D == 128 && CT <= 64) {
+        if (p.vec) {  // one eight-wave workgroup per (b,h) and segment
+            hipLaunchKernelGGL((k_segment_states_wide<CT>), dim3((unsigned)(p.BH * (p.n_seg - 1))),
+                               dim3(512), 0, st, (const bf16*)K, (const bf16*)V, ws, p.T, p.dk, p.dv,
+                               p.C, p.G, p.n_seg);
+            return hipGetLastError();
+        }
+    }
     constexpr int BV = D > 64 ? 64 : D;
     const int64_t grid = p.BH * (p.n_seg - 1) * p.n_vb;
     if (p.vec)
