@@ -224,6 +224,29 @@ def bench_decode(args, torch, lla, workloads, profiling):
                      "traffic": profiling.stored_traffic("decode_step"), "algorithmic_bytes": nbytes,
                      "kernel_ms": kern_ms, "timing": "HIP events around the timed steps"},
     }
+    # Short continuations from the same states: T tokens per call through
+    # lla_prefill (the fused path for T <= 16).
+    res["continuation"] = []
+    for tc in (4, 16):
+        qc, kc, vc = (x.permute(1, 2, 0, 3).contiguous()
+                      for x in workloads.decode_inputs(cfg, tc, device=dev))
+        call = lla.PreparedPrefill(qc, kc, vc, S, C)
+        for _ in range(3):
+            call()
+        nc = 50
+        wall_c, gpu_c = _timed(torch, lambda i: call(), nc)
+        ms_c = gpu_c * 1e3 / nc
+        cbytes = B * H * (8 * d * d + tc * 10 * d)
+        res["continuation"].append({
+            "tokens_per_call": tc, "value": B * tc * nc / wall_c, "unit": "tokens/s",
+            "ms_per_call": wall_c * 1e3 / nc, "gpu_ms_per_call": ms_c,
+            "roofline": {"kernel": "k_decode_tokens<bf16,128,512>", "bound": "hbm",
+                         "achieved": cbytes / (ms_c * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": cbytes / (ms_c * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                         "algorithmic_bytes": cbytes, "kernel_ms": ms_c,
+                         "timing": "HIP events around back-to-back calls"}})
+        del call, qc, kc, vc
+
     if not args.no_cpu_baseline:
         # n decode steps of one (b,h) are n iterations of the recurrence from
         # its state: time the oracle on 8 sequences x all heads x 128 steps.

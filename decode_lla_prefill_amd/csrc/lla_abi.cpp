@@ -208,6 +208,8 @@ lla_status lla_prefill(const void* Q, const void* K, const void* V, lla_dtype dt
     lla_status st = check_prefill(b, true, true, true, true, true, dtype, B, H, T, dk, dv, C, p);
     if (st != LLA_OK || T == 0) return st;
     hipStream_t s = (hipStream_t)stream;
+    if (lla::decode_tokens_fit(T, (int)dk, (int)dv))  // a short prompt: fused decode steps
+        return device_status(lla::launch_decode_tokens(dtype, Q, K, V, p.BH, (int)T, (int)dk, S, O, s));
     float* ws = (float*)workspace;
     st = device_status(lla::launch_segment_states(p, K, V, ws, s));
     if (st != LLA_OK) return st;

@@ -146,6 +146,66 @@ __global__ __launch_bounds__(NT) void k_decode_step_sq(const Tin* __restrict__ q
     }
 }
 
+
+// Several tokens per call (a short continuation from an existing state:
+// deck "Mechanism map", decode line, applied T times).  The state slice stays
+// in registers across the T steps -- one state read and one write for all T
+// tokens.  Each step is the decode step above with the same per-element
+// arithmetic and the same reduction order, so T = 1 gives identical bits.
+// q, k, v: [BH][T][D] (Tin), o: [BH][T][D] fp32, T <= TMAX.
+template <typename Tin, int D, int NT, int TMAX>
+__global__ __launch_bounds__(NT) void k_decode_tokens(const Tin* __restrict__ q,
+                                                      const Tin* __restrict__ k,
+                                                      const Tin* __restrict__ v,
+                                                      float* __restrict__ S,
+                                                      float* __restrict__ o, int T) {
+    constexpr int CG = D / 4, RG = NT / CG, RPT = D / RG;
+    static_assert(NT % CG == 0 && D % RG == 0, "thread layout must tile the state");
+    __shared__ float qs[TMAX][D], ks[TMAX][D], vs[TMAX][D];
+    __shared__ f32x4 red[RG][CG];
+    const int tid = threadIdx.x, cg = tid % CG, rg = tid / CG;
+    const int64_t bh = blockIdx.x;
+    float* Sb = S + bh * (int64_t)D * D;
+    const int64_t tok0 = bh * T;  // first token row of this (b,h)
+    for (int e = tid; e < T * D; e += NT) {
+        const int t = e / D, i = e % D;
+        qs[t][i] = to_f32(q[tok0 * D + e]);
+        ks[t][i] = to_f32(k[tok0 * D + e]);
+        vs[t][i] = to_f32(v[tok0 * D + e]);
+    }
+    __syncthreads();
+    f32x4 x[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m)
+        x[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sb + (rg + m * RG) * D + 4 * cg));
+    for (int t = 0; t < T; ++t) {
+        const f32x4 vj = {vs[t][4 * cg], vs[t][4 * cg + 1], vs[t][4 * cg + 2], vs[t][4 * cg + 3]};
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) {
+            const int i = rg + m * RG;
+            const float ki = ks[t][i], qi = qs[t][i];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                x[m][u] = fmaf(ki, vj[u], x[m][u]);  // rank-1 update
+                acc[u] = fmaf(qi, x[m][u], acc[u]);  // state read
+            }
+        }
+        red[rg][cg] = acc;
+        __syncthreads();
+        for (int j = tid; j < D; j += NT) {  // o_t[j] = sum over row groups, in order
+            float sum = 0.0f;
+#pragma unroll
+            for (int r = 0; r < RG; ++r) sum += red[r][j / 4][j % 4];
+            o[(tok0 + t) * D + j] = sum;
+        }
+        __syncthreads();  // red is rewritten by the next token
+    }
+#pragma unroll
+    for (int m = 0; m < RPT; ++m)
+        __builtin_nontemporal_store(x[m], reinterpret_cast<f32x4*>(Sb + (rg + m * RG) * D + 4 * cg));
+}
+
 __global__ __launch_bounds__(kThreads) void k_fill_zero(float* __restrict__ p, int64_t n) {
     const int64_t stride = (int64_t)gridDim.x * kThreads;
     int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -182,6 +242,28 @@ hipError_t launch_decode_step(lla_dtype dtype, const void* q, const void* k, con
                               int64_t BH, int dk, int dv, float* S, float* o, hipStream_t st) {
     if (dtype == LLA_BF16) return decode_t<bf16>(q, k, v, BH, dk, dv, S, o, st);
     return decode_t<float>(q, k, v, BH, dk, dv, S, o, st);
+}
+
+bool decode_tokens_fit(int64_t T, int dk, int dv) {
+    return T >= 1 && T <= kDecodeTokensMax && dk == dv && (dk == 64 || dk == 128);
+}
+
+template <typename Tin>
+static hipError_t tokens_t(const void* q, const void* k, const void* v, int64_t BH, int T, int d,
+                           float* S, float* o, hipStream_t st) {
+    if (d == 128)
+        hipLaunchKernelGGL((k_decode_tokens<Tin, 128, 512, kDecodeTokensMax>), dim3((unsigned)BH), dim3(512),
+                           0, st, (const Tin*)q, (const Tin*)k, (const Tin*)v, S, o, T);
+    else
+        hipLaunchKernelGGL((k_decode_tokens<Tin, 64, 256, kDecodeTokensMax>), dim3((unsigned)BH), dim3(256),
+                           0, st, (const Tin*)q, (const Tin*)k, (const Tin*)v, S, o, T);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_tokens(lla_dtype dtype, const void* q, const void* k, const void* v,
+                                int64_t BH, int T, int d, float* S, float* o, hipStream_t st) {
+    if (dtype == LLA_BF16) return tokens_t<bf16>(q, k, v, BH, T, d, S, o, st);
+    return tokens_t<float>(q, k, v, BH, T, d, S, o, st);
 }
 
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st) {

@@ -123,6 +123,14 @@ size_t lla_prefill_workspace_size(int64_t B, int64_t H, int64_t T, int64_t dk,
  * masked score triangle, O_c, and the state hop).  Equivalent to calling
  * lla_prefill_segment_states, lla_prefill_state_scan and lla_prefill_chunks
  * in that order.
+ *
+ * Short prompts -- a few tokens continuing an existing state, where prefill
+ * behaves like decode (deck: "Prefill and decode") -- take another route:
+ * for 1 <= T <= 16 with dk = dv in {64, 128} the call runs T fused decode
+ * steps in one kernel (the state read and written once, held in registers
+ * between the steps) with the arithmetic of lla_decode_step, so its results
+ * equal T successive lla_decode_step calls bit for bit.  The workspace is not
+ * touched on this route (it is still validated).
  */
 lla_status lla_prefill(const void *Q, const void *K, const void *V, lla_dtype dtype,
                        int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int64_t C,
