@@ -6,7 +6,8 @@ Prints ONE JSON line.  ``value`` is prefill throughput in tokens/s (B*T per
 second) on the T=8192 workload (B=1, H=16, C=64, d_k=d_v=128, bf16 Q/K/V,
 fp32 state and output); the decode workload (256 sequences x 32 heads,
 d=128, state from a seeded T=4096 prefill) is reported under ``decode`` in
-steps/s.
+steps/s.  The same two workloads with query heads grouped four to a
+key/value head (shared states) are reported under ``grouped_heads``.
 
 Prefill is timed cold: the timed steps rotate over several input/output
 sets whose total exceeds the 256 MB Infinity Cache, so each step's inputs
@@ -39,23 +40,28 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 matrix cores, TFLOP/s
 METRIC = "prefill tokens/s + % bf16 MFMA peak; decode steps/s + % HBM BW (1 GPU)"
-def prefill_work(B, H, T, C, d):
-    """Algorithmic flops and bytes of one prefill (kept triangle only).
+def prefill_work(B, H, T, C, d, Hkv=None):
+    """Algorithmic flops and bytes of one prefill (kept triangle only), with
+    H query heads on Hkv key/value heads (default: one each).
 
-    flops per head-token: 2d(C+1) (scores + masked scores x V over the kept
-    triangle) + 4d^2 (Q S and K^T V) + d^2/C (the state add per chunk);
-    bytes per head-token: 6d (bf16 Q, K, V) + 4d (fp32 O); plus 8d^2 per
-    (b,h) for reading S_0 and writing S_T.
+    flops per query-head token: 2d(C+1) (scores + masked scores x V over the
+    kept triangle) + 2d^2 (Q S); per key/value-head token: 2d^2 (K^T V) +
+    d^2/C (the state add per chunk).  bytes per query-head token: 2d (bf16 Q)
+    + 4d (fp32 O); per key/value-head token: 4d (bf16 K, V); plus 8d^2 per
+    key/value head for reading S_0 and writing S_T.
     """
-    ht = B * H * T
-    flops = ht * (2 * d * (C + 1) + 4 * d * d + d * d / C)
-    nbytes = ht * 10 * d + B * H * 8 * d * d
+    Hkv = Hkv or H
+    tq, tkv = B * H * T, B * Hkv * T
+    flops = tq * (2 * d * (C + 1) + 2 * d * d) + tkv * (2 * d * d + d * d / C)
+    nbytes = tq * 6 * d + tkv * 4 * d + B * Hkv * 8 * d * d
     return flops, nbytes
 
 
-def decode_bytes(B, H, d):
-    """Per step: fp32 state read + write (8d^2), bf16 q,k,v (6d), fp32 o (4d)."""
-    return B * H * (8 * d * d + 10 * d)
+def decode_bytes(B, H, d, Hkv=None):
+    """Per step: per key/value head the fp32 state read + write (8d^2) and
+    bf16 k, v (4d); per query head bf16 q (2d) and fp32 o (4d)."""
+    Hkv = Hkv or H
+    return B * Hkv * (8 * d * d + 4 * d) + B * H * 6 * d
 
 
 def repeat_for(fn, min_seconds):
@@ -265,6 +271,62 @@ def bench_decode(args, torch, lla, workloads, profiling):
     return res
 
 
+def bench_grouped(args, torch, lla, workloads):
+    """Shared-state heads: the T=8192 prefill with 16 query heads on 4
+    key/value heads, and the decode batch with 32 query heads on 8."""
+    dev = torch.device("cuda:0")
+    cfg = workloads.CONFIGS["g3"]
+    B, H, Hkv, T, C, d = cfg.B, cfg.H, cfg.kv_heads, cfg.T, cfg.C, cfg.dk
+    q0, k0, v0 = workloads.config_inputs(cfg, device=dev)
+    sets = []
+    for r in range(args.rotate):
+        q, k, v = (x.clone() for x in (q0, k0, v0)) if r else (q0, k0, v0)
+        sets.append(lla.PreparedPrefill(q, k, v, lla.state_init(B, Hkv, d, d, device=dev), C))
+    for i in range(args.warmup):
+        sets[i % len(sets)](zero_state=True)
+    wall, gpu = _timed(torch, lambda i: sets[i % len(sets)](zero_state=True), args.steps)
+    flops, nbytes = prefill_work(B, H, T, C, d, Hkv)
+    step_s = gpu / args.steps
+    pre = {"workload": cfg.name, "B": B, "Hq": H, "Hkv": Hkv, "T": T, "C": C, "dk": d, "dv": d,
+           "value": B * T / (wall / args.steps), "unit": "tokens/s",
+           "ms_per_step": wall * 1e3 / args.steps, "gpu_ms_per_step": step_s * 1e3,
+           "mfma_frac": flops / step_s / (PEAK_BF16_TFLOPS * 1e12),
+           "hbm_frac": nbytes / step_s / (PEAK_HBM_GBS * 1e9),
+           "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+           "timing": "HIP events around the timed steps (state init + lla_prefill_gqa), "
+                     "%d rotating input sets" % len(sets)}
+    del sets, q0, k0, v0
+    torch.cuda.empty_cache()
+
+    cfg = workloads.CONFIGS["g5"]
+    B, H, Hkv, d = cfg.B, cfg.H, cfg.kv_heads, cfg.dk
+    # The grouped states (134 MB) would fit in the 256 MB Infinity Cache:
+    # the steps cycle over three state sets so that every step reads its
+    # states from HBM, as the layers of a model would.
+    S0 = workloads.random_state(cfg, device=dev)
+    S = [S0] + [S0.clone() for _ in range(2)]
+    n = args.decode_steps
+    qd, kd, vd = workloads.decode_inputs(cfg, n + args.warmup, device=dev)
+    o = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    calls = [lla.PreparedDecode(qd[i], kd[i], vd[i], S[i % 3], out=o) for i in range(n + args.warmup)]
+    for i in range(args.warmup):
+        calls[n + i]()
+    wall, gpu = _timed(torch, lambda i: calls[i](), n)
+    kern_ms = gpu * 1e3 / n
+    nbytes = decode_bytes(B, H, d, Hkv)
+    dec = {"workload": cfg.name, "B": B, "Hq": H, "Hkv": Hkv, "dk": d, "dv": d, "steps": n,
+           "value": n / wall, "unit": "steps/s", "ms_per_step": wall * 1e3 / n,
+           "gpu_ms_per_step": kern_ms, "tokens_per_s": B * n / wall,
+           "roofline": {"kernel": "k_decode_group<bf16,128,512>", "bound": "hbm",
+                        "achieved": nbytes / (kern_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": nbytes / (kern_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                        "algorithmic_bytes": nbytes, "kernel_ms": kern_ms,
+                        "timing": "HIP events around the timed steps, cycling over 3 state sets"}}
+    del calls, qd, kd, vd, S, S0
+    torch.cuda.empty_cache()
+    return {"prefill": pre, "decode": dec}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -278,6 +340,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum oracle time of each CPU baseline (the sample is repeated)")
     ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--skip-grouped", action="store_true")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -314,6 +377,8 @@ def main():
         line["cpu_baseline"] = pre["cpu_baseline"]
     if not args.skip_decode:
         line["decode"] = bench_decode(args, torch, lla, workloads, profiling)
+    if not args.skip_grouped:
+        line["grouped_heads"] = bench_grouped(args, torch, lla, workloads)
     print(json.dumps(line))
 
 

@@ -21,7 +21,8 @@ import torch
 
 __all__ = [
     "LlaError", "library", "library_path", "state_init", "prefill", "decode_step",
-    "prefill_workspace_size", "prefill_segment_chunks", "prefill_segment_states",
+    "prefill_workspace_size", "prefill_gqa_workspace_size", "prefill_segment_chunks",
+    "prefill_segment_states",
     "prefill_state_scan", "prefill_chunks", "PreparedPrefill", "PreparedDecode", "EXPORTS",
 ]
 
@@ -32,7 +33,8 @@ library_path = os.path.join(_HERE, "liblla.so")
 EXPORTS = ("lla_status_string", "lla_last_device_error", "lla_state_init",
            "lla_prefill_segment_chunks", "lla_prefill_workspace_size", "lla_prefill",
            "lla_prefill_segment_states", "lla_prefill_state_scan", "lla_prefill_chunks",
-           "lla_decode_step")
+           "lla_decode_step", "lla_prefill_gqa_workspace_size", "lla_prefill_gqa",
+           "lla_decode_step_gqa")
 
 _BF16, _F32 = 0, 1
 _lib = None
@@ -79,6 +81,13 @@ def library():
         lib.lla_prefill_state_scan.restype = st
         lib.lla_decode_step.argtypes = [vp, vp, vp, ci, i64, i64, i64, i64, vp, vp, vp]
         lib.lla_decode_step.restype = st
+        lib.lla_prefill_gqa_workspace_size.argtypes = [i64] * 7
+        lib.lla_prefill_gqa_workspace_size.restype = sz
+        lib.lla_prefill_gqa.argtypes = [vp, vp, vp, ci, i64, i64, i64, i64, i64, i64, i64, vp, vp, vp,
+                                        sz, vp]
+        lib.lla_prefill_gqa.restype = st
+        lib.lla_decode_step_gqa.argtypes = [vp, vp, vp, ci, i64, i64, i64, i64, i64, vp, vp, vp]
+        lib.lla_decode_step_gqa.restype = st
         _lib = lib
     return _lib
 
@@ -118,15 +127,24 @@ def _need(t: torch.Tensor, name: str, dtype=None, ndim=None):
 
 
 def _qkv_shape(q, k, v):
+    """(B, Hq, Hkv, T, dk, dv) of q [B,Hq,T,dk], k [B,Hkv,T,dk], v [B,Hkv,T,dv]."""
     _need(q, "q", ndim=4)
     _need(k, "k", dtype=q.dtype, ndim=4)
     _need(v, "v", dtype=q.dtype, ndim=4)
-    B, H, T, dk = q.shape
-    if tuple(k.shape) != (B, H, T, dk) or tuple(v.shape[:3]) != (B, H, T):
+    B, Hq, T, dk = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, T, dk) or tuple(v.shape[:3]) != (B, Hkv, T) or Hq % Hkv:
         raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
     if not (q.device == k.device == v.device):
         raise ValueError("q, k, v must be on one device")
-    return B, H, T, dk, v.shape[3]
+    return B, Hq, Hkv, T, dk, v.shape[3]
+
+
+def _mha_shape(q, k, v):
+    B, Hq, Hkv, T, dk, dv = _qkv_shape(q, k, v)
+    if Hq != Hkv:
+        raise ValueError("the prefill phases take one key/value head per query head")
+    return B, Hq, T, dk, dv
 
 
 def state_init(B: int, H: int, dk: int, dv: int, device=None, out: torch.Tensor = None):
@@ -151,8 +169,12 @@ def prefill_workspace_size(B, H, T, dk, dv, chunk) -> int:
     return int(library().lla_prefill_workspace_size(B, H, T, dk, dv, chunk))
 
 
-def _workspace(B, H, T, dk, dv, chunk, device, workspace):
-    need = prefill_workspace_size(B, H, T, dk, dv, chunk)
+def prefill_gqa_workspace_size(B, Hq, Hkv, T, dk, dv, chunk) -> int:
+    return int(library().lla_prefill_gqa_workspace_size(B, Hq, Hkv, T, dk, dv, chunk))
+
+
+def _workspace(B, H, T, dk, dv, chunk, device, workspace, Hkv=None):
+    need = prefill_gqa_workspace_size(B, H, H if Hkv is None else Hkv, T, dk, dv, chunk)
     if workspace is None:
         if need == 0:
             return None, 0
@@ -177,14 +199,21 @@ def _out(out, shape, device):
 
 
 def prefill(q, k, v, state, chunk: int, out=None, workspace=None):
-    """Chunkwise prefill: returns o [B,H,T,dv] fp32; ``state`` goes S_0 -> S_T in place."""
+    """Chunkwise prefill: returns o [B,Hq,T,dv] fp32; ``state`` [B,Hkv,dk,dv] goes
+    S_0 -> S_T in place.  k, v with fewer heads than q (Hq a multiple of Hkv)
+    select shared-state heads (lla_prefill_gqa)."""
     lib = library()
-    B, H, T, dk, dv = _qkv_shape(q, k, v)
-    _state_check(state, B, H, dk, dv)
-    out = _out(out, (B, H, T, dv), q.device)
-    ws, ws_bytes = _workspace(B, H, T, dk, dv, chunk, q.device, workspace)
-    _check(lib.lla_prefill(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H, T, dk, dv, chunk,
-                           _ptr(state), _ptr(out), _ptr(ws), ws_bytes, _stream(q)), "lla_prefill")
+    B, Hq, Hkv, T, dk, dv = _qkv_shape(q, k, v)
+    _state_check(state, B, Hkv, dk, dv)
+    out = _out(out, (B, Hq, T, dv), q.device)
+    ws, ws_bytes = _workspace(B, Hq, T, dk, dv, chunk, q.device, workspace, Hkv)
+    if Hq == Hkv:
+        _check(lib.lla_prefill(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, Hq, T, dk, dv, chunk,
+                               _ptr(state), _ptr(out), _ptr(ws), ws_bytes, _stream(q)), "lla_prefill")
+    else:
+        _check(lib.lla_prefill_gqa(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, Hq, Hkv, T, dk, dv,
+                                   chunk, _ptr(state), _ptr(out), _ptr(ws), ws_bytes, _stream(q)),
+               "lla_prefill_gqa")
     return out
 
 
@@ -216,7 +245,7 @@ def prefill_state_scan(state, T: int, chunk: int, workspace):
 def prefill_chunks(q, k, v, state, chunk: int, workspace=None, out=None):
     """Phase 3: the chunk walk from the segment states; writes o and S_T."""
     lib = library()
-    B, H, T, dk, dv = _qkv_shape(q, k, v)
+    B, H, T, dk, dv = _mha_shape(q, k, v)
     _state_check(state, B, H, dk, dv)
     out = _out(out, (B, H, T, dv), q.device)
     need = prefill_workspace_size(B, H, T, dk, dv, chunk)
@@ -231,20 +260,36 @@ def prefill_chunks(q, k, v, state, chunk: int, workspace=None, out=None):
     return out
 
 
-def decode_step(q, k, v, state, out=None):
-    """One decode step: ``state += k v^T`` in place; returns o = state^T q [B,H,dv] fp32."""
-    lib = library()
+def _step_shape(q, k, v):
+    """(B, Hq, Hkv, dk, dv) of q [B,Hq,dk], k [B,Hkv,dk], v [B,Hkv,dv]."""
     _need(q, "q", ndim=3)
     _need(k, "k", dtype=q.dtype, ndim=3)
     _need(v, "v", dtype=q.dtype, ndim=3)
-    B, H, dk = q.shape
-    dv = v.shape[2]
-    if tuple(k.shape) != (B, H, dk) or tuple(v.shape[:2]) != (B, H):
+    B, Hq, dk = q.shape
+    Hkv, dv = k.shape[1], v.shape[2]
+    if tuple(k.shape) != (B, Hkv, dk) or tuple(v.shape[:2]) != (B, Hkv) or Hq % Hkv:
         raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
-    _state_check(state, B, H, dk, dv)
-    out = _out(out, (B, H, dv), q.device)
-    _check(lib.lla_decode_step(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H, dk, dv,
-                               _ptr(state), _ptr(out), _stream(q)), "lla_decode_step")
+    return B, Hq, Hkv, dk, dv
+
+
+def _step_call(lib, q, k, v, state, out, B, Hq, Hkv, dk, dv):
+    """(function, argument tuple) of the decode step for these buffers."""
+    if Hq == Hkv:
+        return lib.lla_decode_step, (_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, Hq, dk, dv,
+                                     _ptr(state), _ptr(out))
+    return lib.lla_decode_step_gqa, (_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, Hq, Hkv, dk, dv,
+                                     _ptr(state), _ptr(out))
+
+
+def decode_step(q, k, v, state, out=None):
+    """One decode step: ``state += k v^T`` in place; returns o = state^T q [B,Hq,dv]
+    fp32.  k, v with fewer heads than q select shared-state heads."""
+    lib = library()
+    B, Hq, Hkv, dk, dv = _step_shape(q, k, v)
+    _state_check(state, B, Hkv, dk, dv)
+    out = _out(out, (B, Hq, dv), q.device)
+    fn, args = _step_call(lib, q, k, v, state, out, B, Hq, Hkv, dk, dv)
+    _check(fn(*args, _stream(q)), fn.__name__)
     return out
 
 
@@ -259,18 +304,24 @@ class PreparedPrefill:
 
     def __init__(self, q, k, v, state, chunk, out=None, workspace=None):
         lib = library()
-        B, H, T, dk, dv = _qkv_shape(q, k, v)
-        _state_check(state, B, H, dk, dv)
+        B, H, Hkv, T, dk, dv = _qkv_shape(q, k, v)
+        _state_check(state, B, Hkv, dk, dv)
         self.out = _out(out, (B, H, T, dv), q.device)
-        self.workspace, ws_bytes = _workspace(B, H, T, dk, dv, chunk, q.device, workspace)
+        self.workspace, ws_bytes = _workspace(B, H, T, dk, dv, chunk, q.device, workspace, Hkv)
         self.state = state
         self._lib = lib
-        self._fn = lib.lla_prefill
         self._init = lib.lla_state_init
+        self._grouped = H != Hkv
         dt, ws = _dtype_code(q), _ptr(self.workspace)
-        self._args = (_ptr(q), _ptr(k), _ptr(v), dt, B, H, T, dk, dv, chunk,
-                      _ptr(state), _ptr(self.out), ws, ws_bytes)
-        self._init_args = (_ptr(state), B, H, dk, dv)
+        if self._grouped:
+            self._fn = lib.lla_prefill_gqa
+            self._args = (_ptr(q), _ptr(k), _ptr(v), dt, B, H, Hkv, T, dk, dv, chunk,
+                          _ptr(state), _ptr(self.out), ws, ws_bytes)
+        else:
+            self._fn = lib.lla_prefill
+            self._args = (_ptr(q), _ptr(k), _ptr(v), dt, B, H, T, dk, dv, chunk,
+                          _ptr(state), _ptr(self.out), ws, ws_bytes)
+        self._init_args = (_ptr(state), B, Hkv, dk, dv)
         self._seg_args = (_ptr(k), _ptr(v), dt, B, H, T, dk, dv, chunk, ws, ws_bytes)
         self._scan_args = (_ptr(state), B, H, T, dk, dv, chunk, ws, ws_bytes)
         self._device = q.device
@@ -282,22 +333,30 @@ class PreparedPrefill:
         st = self._stream()
         if zero_state:
             _check(self._init(*self._init_args, st), "lla_state_init")
-        _check(self._fn(*self._args, st), "lla_prefill")
+        _check(self._fn(*self._args, st), self._fn.__name__)
         return self.out
 
-    # The three phases of the call, one by one (for per-kernel timing).
+    # The three phases of the call, one by one (for per-kernel timing; one
+    # key/value head per query head only).
     def zero_state(self):
         _check(self._init(*self._init_args, self._stream()), "lla_state_init")
 
     def segment_states(self):
+        self._mha_only()
         _check(self._lib.lla_prefill_segment_states(*self._seg_args, self._stream()),
                "lla_prefill_segment_states")
 
     def state_scan(self):
+        self._mha_only()
         _check(self._lib.lla_prefill_state_scan(*self._scan_args, self._stream()),
                "lla_prefill_state_scan")
 
+    def _mha_only(self):
+        if self._grouped:
+            raise ValueError("the prefill phases take one key/value head per query head")
+
     def chunks(self):
+        self._mha_only()
         _check(self._lib.lla_prefill_chunks(*self._args, self._stream()), "lla_prefill_chunks")
         return self.out
 
@@ -307,19 +366,13 @@ class PreparedDecode:
 
     def __init__(self, q, k, v, state, out=None):
         lib = library()
-        _need(q, "q", ndim=3)
-        _need(k, "k", dtype=q.dtype, ndim=3)
-        _need(v, "v", dtype=q.dtype, ndim=3)
-        B, H, dk = q.shape
-        dv = v.shape[2]
-        _state_check(state, B, H, dk, dv)
-        self.out = _out(out, (B, H, dv), q.device)
-        self._fn = lib.lla_decode_step
-        self._args = (_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H, dk, dv, _ptr(state),
-                      _ptr(self.out))
+        B, Hq, Hkv, dk, dv = _step_shape(q, k, v)
+        _state_check(state, B, Hkv, dk, dv)
+        self.out = _out(out, (B, Hq, dv), q.device)
+        self._fn, self._args = _step_call(lib, q, k, v, state, self.out, B, Hq, Hkv, dk, dv)
         self._device = q.device
 
     def __call__(self):
         _check(self._fn(*self._args, torch.cuda.current_stream(self._device).cuda_stream),
-               "lla_decode_step")
+               self._fn.__name__)
         return self.out

@@ -56,11 +56,23 @@ lla_status device_status(hipError_t e) {
     return LLA_ERR_DEVICE;
 }
 
-lla::PrefillPlan make_plan(lla_dtype dt, int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
+// Query heads Hq and key/value heads Hkv (Hq = Hkv without grouping).
+struct Heads {
+    int64_t q, kv;
+};
+
+// Head counts: 1 <= Hkv <= Hq, Hq a multiple of Hkv.
+lla_status check_heads(Heads h) {
+    if (h.q < 1 || h.kv < 1 || h.kv > h.q || h.q % h.kv != 0) return LLA_ERR_SHAPE;
+    return LLA_OK;
+}
+
+lla::PrefillPlan make_plan(lla_dtype dt, int64_t B, Heads h, int64_t T, int64_t dk, int64_t dv,
                            int64_t C) {
     lla::PrefillPlan p{};
     p.B = B;
-    p.H = H;
+    p.H = h.q;
+    p.Hkv = h.kv;
     p.T = T;
     p.dk = (int)dk;
     p.dv = (int)dv;
@@ -71,7 +83,7 @@ lla::PrefillPlan make_plan(lla_dtype dt, int64_t B, int64_t H, int64_t T, int64_
 }
 
 size_t ws_bytes_for(const lla::PrefillPlan& p) {
-    if (p.n_seg <= 1) return 0;
+    if (!p.use_ws) return 0;
     return (size_t)(p.BH * p.n_seg * (int64_t)p.dk * p.dv) * sizeof(float);
 }
 
@@ -86,13 +98,15 @@ struct PrefillBufs {
 };
 
 lla_status check_prefill(const PrefillBufs& b, bool needs_q, bool needs_kv, bool needs_s,
-                         bool needs_o, bool needs_ws, lla_dtype dt, int64_t B, int64_t H,
+                         bool needs_o, bool needs_ws, lla_dtype dt, int64_t B, Heads h,
                          int64_t T, int64_t dk, int64_t dv, int64_t C, lla::PrefillPlan& plan) {
-    lla_status st = check_sizes(B, H, T, dk, dv, C);
+    lla_status st = check_heads(h);
+    if (st != LLA_OK) return st;
+    st = check_sizes(B, h.q, T, dk, dv, C);
     if (st != LLA_OK) return st;
     st = check_dtype((int)dt, C);
     if (st != LLA_OK) return st;
-    plan = make_plan(dt, B, H, T, dk, dv, C);
+    plan = make_plan(dt, B, h, T, dk, dv, C);
     const bool empty = T == 0;
     // Pointers: Q/K/V/O may be NULL only for an empty prompt; S never.
     if (needs_q && !empty && !b.Q) return LLA_ERR_NULL;
@@ -109,13 +123,13 @@ lla_status check_prefill(const PrefillBufs& b, bool needs_q, bool needs_kv, bool
         if (p && !aligned16(p)) return LLA_ERR_ALIGN;
     if (empty) return LLA_OK;
     const int64_t es = elem_size(dt);
-    const int64_t BH = B * H;
-    const Span q = span(needs_q ? b.Q : nullptr, needs_q ? BH * T * dk * es : 0);
-    const Span k = span(needs_kv ? b.K : nullptr, needs_kv ? BH * T * dk * es : 0);
-    const Span v = span(needs_kv ? b.V : nullptr, needs_kv ? BH * T * dv * es : 0);
-    const Span o = span(needs_o ? b.O : nullptr, needs_o ? BH * T * dv * 4 : 0);
+    const int64_t BHq = B * h.q, BHkv = B * h.kv;
+    const Span q = span(needs_q ? b.Q : nullptr, needs_q ? BHq * T * dk * es : 0);
+    const Span k = span(needs_kv ? b.K : nullptr, needs_kv ? BHkv * T * dk * es : 0);
+    const Span v = span(needs_kv ? b.V : nullptr, needs_kv ? BHkv * T * dv * es : 0);
+    const Span o = span(needs_o ? b.O : nullptr, needs_o ? BHq * T * dv * 4 : 0);
     const void* s_ptr = b.S_out ? (const void*)b.S_out : (const void*)b.S_in;
-    const Span s = span(needs_s ? s_ptr : nullptr, needs_s ? BH * dk * dv * 4 : 0);
+    const Span s = span(needs_s ? s_ptr : nullptr, needs_s ? BHkv * dk * dv * 4 : 0);
     const Span w = span((needs_ws && need_ws > 0) ? b.ws : nullptr, (int64_t)need_ws);
     // Outputs (O, S when written, the workspace) must not overlap anything else.
     const Span all[] = {q, k, v, o, s, w};
@@ -160,13 +174,18 @@ lla_status lla_state_init(float* S, int64_t B, int64_t H, int64_t dk, int64_t dv
 int64_t lla_prefill_segment_chunks(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
                                    int64_t C) {
     if (check_sizes(B, H, T, dk, dv, C) != LLA_OK) return 0;
-    return make_plan(LLA_BF16, B, H, T, dk, dv, C).G;
+    return make_plan(LLA_BF16, B, Heads{H, H}, T, dk, dv, C).G;
 }
 
 size_t lla_prefill_workspace_size(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
                                   int64_t C) {
-    if (check_sizes(B, H, T, dk, dv, C) != LLA_OK) return 0;
-    return ws_bytes_for(make_plan(LLA_BF16, B, H, T, dk, dv, C));
+    return lla_prefill_gqa_workspace_size(B, H, H, T, dk, dv, C);
+}
+
+size_t lla_prefill_gqa_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t dk,
+                                      int64_t dv, int64_t C) {
+    if (check_heads(Heads{Hq, Hkv}) != LLA_OK || check_sizes(B, Hq, T, dk, dv, C) != LLA_OK) return 0;
+    return ws_bytes_for(make_plan(LLA_BF16, B, Heads{Hq, Hkv}, T, dk, dv, C));
 }
 
 lla_status lla_prefill_segment_states(const void* K, const void* V, lla_dtype dtype, int64_t B,
@@ -174,7 +193,7 @@ lla_status lla_prefill_segment_states(const void* K, const void* V, lla_dtype dt
                                       void* workspace, size_t workspace_bytes, void* stream) {
     lla::PrefillPlan p;
     PrefillBufs b{nullptr, K, V, nullptr, nullptr, nullptr, workspace, workspace_bytes};
-    lla_status st = check_prefill(b, false, true, false, false, true, dtype, B, H, T, dk, dv, C, p);
+    lla_status st = check_prefill(b, false, true, false, false, true, dtype, B, Heads{H, H}, T, dk, dv, C, p);
     if (st != LLA_OK || T == 0) return st;
     return device_status(lla::launch_segment_states(p, K, V, (float*)workspace, (hipStream_t)stream));
 }
@@ -184,7 +203,8 @@ lla_status lla_prefill_state_scan(const float* S, int64_t B, int64_t H, int64_t 
                                   void* stream) {
     lla::PrefillPlan p;
     PrefillBufs b{nullptr, nullptr, nullptr, S, nullptr, nullptr, workspace, workspace_bytes};
-    lla_status st = check_prefill(b, false, false, true, false, true, LLA_BF16, B, H, T, dk, dv, C, p);
+    lla_status st = check_prefill(b, false, false, true, false, true, LLA_BF16, B, Heads{H, H}, T, dk,
+                                  dv, C, p);
     if (st != LLA_OK || T == 0) return st;
     return device_status(lla::launch_state_scan(p, S, (float*)workspace, (hipStream_t)stream));
 }
@@ -195,20 +215,24 @@ lla_status lla_prefill_chunks(const void* Q, const void* K, const void* V, lla_d
                               void* stream) {
     lla::PrefillPlan p;
     PrefillBufs b{Q, K, V, nullptr, S, O, workspace, workspace_bytes};
-    lla_status st = check_prefill(b, true, true, true, true, true, dtype, B, H, T, dk, dv, C, p);
+    lla_status st = check_prefill(b, true, true, true, true, true, dtype, B, Heads{H, H}, T, dk, dv, C, p);
     if (st != LLA_OK || T == 0) return st;
     return device_status(lla::launch_chunk_walk(p, Q, K, V, S, O, (float*)workspace, (hipStream_t)stream));
 }
 
-lla_status lla_prefill(const void* Q, const void* K, const void* V, lla_dtype dtype, int64_t B,
-                       int64_t H, int64_t T, int64_t dk, int64_t dv, int64_t C, float* S, float* O,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+lla_status prefill_impl(const void* Q, const void* K, const void* V, lla_dtype dtype, int64_t B,
+                        Heads h, int64_t T, int64_t dk, int64_t dv, int64_t C, float* S, float* O,
+                        void* workspace, size_t workspace_bytes, void* stream) {
     lla::PrefillPlan p;
     PrefillBufs b{Q, K, V, nullptr, S, O, workspace, workspace_bytes};
-    lla_status st = check_prefill(b, true, true, true, true, true, dtype, B, H, T, dk, dv, C, p);
+    lla_status st = check_prefill(b, true, true, true, true, true, dtype, B, h, T, dk, dv, C, p);
     if (st != LLA_OK || T == 0) return st;
     hipStream_t s = (hipStream_t)stream;
-    if (lla::decode_tokens_fit(T, (int)dk, (int)dv))  // a short prompt: fused decode steps
+    if (p.group == 1 && lla::decode_tokens_fit(T, (int)dk, (int)dv))  // a short prompt: fused decode steps
         return device_status(lla::launch_decode_tokens(dtype, Q, K, V, p.BH, (int)T, (int)dk, S, O, s));
     float* ws = (float*)workspace;
     st = device_status(lla::launch_segment_states(p, K, V, ws, s));
@@ -218,23 +242,58 @@ lla_status lla_prefill(const void* Q, const void* K, const void* V, lla_dtype dt
     return device_status(lla::launch_chunk_walk(p, Q, K, V, S, O, ws, s));
 }
 
-lla_status lla_decode_step(const void* q, const void* k, const void* v, lla_dtype dtype,
-                           int64_t B, int64_t H, int64_t dk, int64_t dv, float* S, float* o,
-                           void* stream) {
-    lla_status st = check_sizes(B, H, 1, dk, dv, -1);
+lla_status decode_impl(const void* q, const void* k, const void* v, lla_dtype dtype, int64_t B,
+                       Heads h, int64_t dk, int64_t dv, float* S, float* o, void* stream) {
+    lla_status st = check_heads(h);
+    if (st != LLA_OK) return st;
+    st = check_sizes(B, h.q, 1, dk, dv, -1);
     if (st != LLA_OK) return st;
     if (dtype != LLA_BF16 && dtype != LLA_F32) return LLA_ERR_DTYPE;
+    const int64_t group = h.q / h.kv;
+    if (group > 1 && !lla::decode_group_fit(group, (int)dk, (int)dv)) return LLA_ERR_UNSUPPORTED;
     if (!q || !k || !v || !S || !o) return LLA_ERR_NULL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(S) || !aligned16(o))
         return LLA_ERR_ALIGN;
-    const int64_t BH = B * H, es = elem_size(dtype);
-    const Span sq = span(q, BH * dk * es), sk = span(k, BH * dk * es), sv = span(v, BH * dv * es);
-    const Span ss = span(S, BH * dk * dv * 4), so = span(o, BH * dv * 4);
+    const int64_t BHq = B * h.q, BHkv = B * h.kv, es = elem_size(dtype);
+    const Span sq = span(q, BHq * dk * es), sk = span(k, BHkv * dk * es), sv = span(v, BHkv * dv * es);
+    const Span ss = span(S, BHkv * dk * dv * 4), so = span(o, BHq * dv * 4);
     if (overlap(ss, sq) || overlap(ss, sk) || overlap(ss, sv) || overlap(ss, so) || overlap(so, sq) ||
         overlap(so, sk) || overlap(so, sv))
         return LLA_ERR_ALIAS;
-    return device_status(
-        lla::launch_decode_step(dtype, q, k, v, BH, (int)dk, (int)dv, S, o, (hipStream_t)stream));
+    hipStream_t s = (hipStream_t)stream;
+    if (group > 1)
+        return device_status(lla::launch_decode_group(dtype, q, k, v, BHkv, (int)group, (int)dk, S, o, s));
+    return device_status(lla::launch_decode_step(dtype, q, k, v, BHkv, (int)dk, (int)dv, S, o, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+lla_status lla_prefill(const void* Q, const void* K, const void* V, lla_dtype dtype, int64_t B,
+                       int64_t H, int64_t T, int64_t dk, int64_t dv, int64_t C, float* S, float* O,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    return prefill_impl(Q, K, V, dtype, B, Heads{H, H}, T, dk, dv, C, S, O, workspace,
+                        workspace_bytes, stream);
+}
+
+lla_status lla_prefill_gqa(const void* Q, const void* K, const void* V, lla_dtype dtype, int64_t B,
+                           int64_t Hq, int64_t Hkv, int64_t T, int64_t dk, int64_t dv, int64_t C,
+                           float* S, float* O, void* workspace, size_t workspace_bytes, void* stream) {
+    return prefill_impl(Q, K, V, dtype, B, Heads{Hq, Hkv}, T, dk, dv, C, S, O, workspace,
+                        workspace_bytes, stream);
+}
+
+lla_status lla_decode_step(const void* q, const void* k, const void* v, lla_dtype dtype,
+                           int64_t B, int64_t H, int64_t dk, int64_t dv, float* S, float* o,
+                           void* stream) {
+    return decode_impl(q, k, v, dtype, B, Heads{H, H}, dk, dv, S, o, stream);
+}
+
+lla_status lla_decode_step_gqa(const void* q, const void* k, const void* v, lla_dtype dtype,
+                               int64_t B, int64_t Hq, int64_t Hkv, int64_t dk, int64_t dv, float* S,
+                               float* o, void* stream) {
+    return decode_impl(q, k, v, dtype, B, Heads{Hq, Hkv}, dk, dv, S, o, stream);
 }
 
 }  // extern "C"

@@ -206,6 +206,65 @@ __global__ __launch_bounds__(NT) void k_decode_tokens(const Tin* __restrict__ q,
         __builtin_nontemporal_store(x[m], reinterpret_cast<f32x4*>(Sb + (rg + m * RG) * D + 4 * cg));
 }
 
+
+// Shared-state heads (query heads grouped on one key/value head, as in
+// grouped-query attention): the state is updated once and then read by each
+// of the group's G query heads.  Query head g of state bh is row bh * G + g
+// of q and o.  For every query head the arithmetic (update, then the state
+// read in row order, then the row-group reduction) is that of
+// k_decode_step_sq, so a group of one gives identical bits.
+template <typename Tin, int D, int NT, int GMAX>
+__global__ __launch_bounds__(NT) void k_decode_group(const Tin* __restrict__ q,
+                                                     const Tin* __restrict__ k,
+                                                     const Tin* __restrict__ v,
+                                                     float* __restrict__ S,
+                                                     float* __restrict__ o, int G) {
+    constexpr int CG = D / 4, RG = NT / CG, RPT = D / RG;
+    static_assert(NT % CG == 0 && D % RG == 0, "thread layout must tile the state");
+    __shared__ float qs[GMAX][D], ks[D], vs[D];
+    __shared__ f32x4 red[RG][CG];
+    const int tid = threadIdx.x, cg = tid % CG, rg = tid / CG;
+    const int64_t bh = blockIdx.x;
+    float* Sb = S + bh * (int64_t)D * D;
+    for (int e = tid; e < G * D; e += NT) qs[e / D][e % D] = to_f32(q[bh * G * D + e]);
+    for (int i = tid; i < D; i += NT) {
+        ks[i] = to_f32(k[bh * D + i]);
+        vs[i] = to_f32(v[bh * D + i]);
+    }
+    __syncthreads();
+    f32x4 x[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m)
+        x[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sb + (rg + m * RG) * D + 4 * cg));
+    const f32x4 vj = {vs[4 * cg], vs[4 * cg + 1], vs[4 * cg + 2], vs[4 * cg + 3]};
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const int i = rg + m * RG;
+        const float ki = ks[i];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) x[m][u] = fmaf(ki, vj[u], x[m][u]);  // rank-1 update
+        __builtin_nontemporal_store(x[m], reinterpret_cast<f32x4*>(Sb + i * D + 4 * cg));
+    }
+    for (int g = 0; g < G; ++g) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) {
+            const float qi = qs[g][rg + m * RG];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) acc[u] = fmaf(qi, x[m][u], acc[u]);  // state read
+        }
+        red[rg][cg] = acc;
+        __syncthreads();
+        for (int j = tid; j < D; j += NT) {  // o[j] = sum over row groups, in order
+            float sum = 0.0f;
+#pragma unroll
+            for (int r = 0; r < RG; ++r) sum += red[r][j / 4][j % 4];
+            o[(bh * G + g) * D + j] = sum;
+        }
+        __syncthreads();  // red is rewritten by the next query head
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void k_fill_zero(float* __restrict__ p, int64_t n) {
     const int64_t stride = (int64_t)gridDim.x * kThreads;
     int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -264,6 +323,28 @@ hipError_t launch_decode_tokens(lla_dtype dtype, const void* q, const void* k, c
                                 int64_t BH, int T, int d, float* S, float* o, hipStream_t st) {
     if (dtype == LLA_BF16) return tokens_t<bf16>(q, k, v, BH, T, d, S, o, st);
     return tokens_t<float>(q, k, v, BH, T, d, S, o, st);
+}
+
+bool decode_group_fit(int64_t group, int dk, int dv) {
+    return group >= 1 && group <= kDecodeGroupMax && dk == dv && (dk == 64 || dk == 128);
+}
+
+template <typename Tin>
+static hipError_t group_t(const void* q, const void* k, const void* v, int64_t BHkv, int G, int d,
+                          float* S, float* o, hipStream_t st) {
+    if (d == 128)
+        hipLaunchKernelGGL((k_decode_group<Tin, 128, 512, kDecodeGroupMax>), dim3((unsigned)BHkv), dim3(512),
+                           0, st, (const Tin*)q, (const Tin*)k, (const Tin*)v, S, o, G);
+    else
+        hipLaunchKernelGGL((k_decode_group<Tin, 64, 256, kDecodeGroupMax>), dim3((unsigned)BHkv), dim3(256),
+                           0, st, (const Tin*)q, (const Tin*)k, (const Tin*)v, S, o, G);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_group(lla_dtype dtype, const void* q, const void* k, const void* v,
+                               int64_t BHkv, int group, int d, float* S, float* o, hipStream_t st) {
+    if (dtype == LLA_BF16) return group_t<bf16>(q, k, v, BHkv, group, d, S, o, st);
+    return group_t<float>(q, k, v, BHkv, group, d, S, o, st);
 }
 
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st) {

@@ -21,7 +21,11 @@ constexpr int64_t kTargetWalkers = LLA_TARGET_WALKERS;
 // Everything the launchers need about a prefill shape, derived once on the
 // host from the user's sizes.
 struct PrefillPlan {
-    int64_t B, H, BH, T;
+    int64_t B, H, BH, T;  // H: query heads; BH = B * Hkv (key/value heads, states)
+    int64_t Hkv;          // key/value heads (0 on input: H)
+    int group;            // query heads per key/value head = H / Hkv
+    int64_t BHq;          // B * H
+    bool use_ws;          // the walk starts every segment from the workspace
     int dk, dv, C;
     int D;        // padded head dim (32, 64 or 128) used for both dk and dv
     int CT;       // padded chunk tile (32, 64 or 128 rows)
@@ -54,5 +58,12 @@ bool decode_tokens_fit(int64_t T, int dk, int dv);
 hipError_t launch_decode_tokens(lla_dtype dtype, const void* q, const void* k, const void* v,
                                 int64_t BH, int T, int d, float* S, float* o, hipStream_t st);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
+
+// Shared-state heads: `group` query heads read each key/value state (dk = dv
+// in {64, 128}, group <= kDecodeGroupMax).  q, o: [BHkv * group][d].
+constexpr int kDecodeGroupMax = 16;
+bool decode_group_fit(int64_t group, int dk, int dv);
+hipError_t launch_decode_group(lla_dtype dtype, const void* q, const void* k, const void* v,
+                               int64_t BHkv, int group, int d, float* S, float* o, hipStream_t st);
 
 }  // namespace lla

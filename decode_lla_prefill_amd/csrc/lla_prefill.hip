@@ -615,7 +615,7 @@ template <typename T, int CT, int D, int BV, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_chunk_walk(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     float* __restrict__ S, float* __restrict__ O, const float* __restrict__ ws, int64_t T_len,
-    int dk, int dv, int C, int64_t G, int64_t n_seg, int n_vb) {
+    int dk, int dv, int C, int64_t G, int64_t n_seg, int n_vb, int group) {
     using Cf = WalkCfg<T, CT, D, BV>;
     using Fr = typename Cf::Fr;
     __shared__ __attribute__((aligned(16))) unsigned char smem[Cf::WALK_BYTES];
@@ -630,7 +630,9 @@ __global__ __launch_bounds__(kThreads) void k_chunk_walk(
     int64_t line;
     int vb;
     split_id(blockIdx.x, (int64_t)(gridDim.x / n_vb), n_vb, line, vb);
-    const int64_t bh = line / n_seg, seg = line - bh * n_seg;
+    // line = (query head, segment); the query heads of a group share the
+    // key/value head bh = bq / group: its K, V and states
+    const int64_t bq = line / n_seg, seg = line - bq * n_seg, bh = bq / group;
     const ScoreTiles<Cf> stiles(w);
     const int v0 = vb * BV;
     const int nv = min(BV, dv - v0);  // valid columns of this block
@@ -638,13 +640,13 @@ __global__ __launch_bounds__(kThreads) void k_chunk_walk(
     const int64_t c0 = seg * G, c1 = min(n_c, c0 + G);
     const bool last_seg = seg == n_seg - 1;
     const int64_t dkdv = (int64_t)dk * dv;
-    const T* Qb = Q + bh * T_len * dk;
+    const T* Qb = Q + bq * T_len * dk;
     const T* Kb = K + bh * T_len * dk;
     const T* Vb = V + bh * T_len * dv + v0;
-    float* Ob = O + bh * T_len * dv + v0;
+    float* Ob = O + bq * T_len * dv + v0;
 
     // Incoming state of this segment, columns [v0, v0 + nv).
-    const float* Sin = (n_seg == 1 ? S + bh * dkdv : ws + (bh * n_seg + seg) * dkdv) + v0;
+    const float* Sin = (ws == nullptr ? S + bh * dkdv : ws + (bh * n_seg + seg) * dkdv) + v0;
     f32x4 Sacc[Cf::NVW][Cf::NDT];
     state_gmem_to_lds<Cf>(Sst, Sin, dk, dv, nv, tid);
     __syncthreads();
@@ -712,7 +714,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_walk(
     }
     if (c1 > c0) store_out<Cf, VEC>(Ob, Oacc, t_prev, n_prev, nv, dv, w, g, c16);
 
-    if (last_seg) {  // (the loop ended with a barrier: the tiles are free)
+    if (last_seg && bq % group == 0) {  // one writer per group (the loop ended with a barrier)
         state_regs_to_lds<Cf>(Sst, Sacc, w, g, c16);
         __syncthreads();
         state_lds_to_gmem<Cf>(S + bh * dkdv + v0, Sst, dk, dv, nv, tid);
@@ -740,7 +742,7 @@ template <int CT>
 __global__ __launch_bounds__(512) void k_chunk_walk_wide(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     float* __restrict__ S, float* __restrict__ O, const float* __restrict__ ws, int64_t T_len,
-    int dk, int dv, int C, int64_t G, int64_t n_seg) {
+    int dk, int dv, int C, int64_t G, int64_t n_seg, int group) {
     using Cf = WideCfg<CT>;
     using Fr = typename Cf::Fr;
     constexpr int NTH = Cf::NTH;
@@ -753,19 +755,20 @@ __global__ __launch_bounds__(512) void k_chunk_walk_wide(
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t line = blockIdx.x;
     const ScoreTiles<Cf> stiles(w);
-    const int64_t bh = line / n_seg, seg = line - bh * n_seg;
+    // line = (query head, segment); the group's key/value head is bq / group
+    const int64_t bq = line / n_seg, seg = line - bq * n_seg, bh = bq / group;
     const int64_t n_c = (T_len + C - 1) / C;
     const int64_t c0 = seg * G, c1 = min(n_c, c0 + G);
     const bool last_seg = seg == n_seg - 1;
     const int64_t dkdv = (int64_t)dk * dv;
-    const bf16* Qb = Q + bh * T_len * dk;
+    const bf16* Qb = Q + bq * T_len * dk;
     const bf16* Kb = K + bh * T_len * dk;
     const bf16* Vb = V + bh * T_len * dv;
-    float* Ob = O + bh * T_len * dv;
+    float* Ob = O + bq * T_len * dv;
     auto rows_of = [&](int64_t c) { return c < c1 ? (int)min((int64_t)C, T_len - c * C) : 0; };
 
     // Incoming state (loads first), then the first chunk's tile loads.
-    const float* Sin = n_seg == 1 ? S + bh * dkdv : ws + (bh * n_seg + seg) * dkdv;
+    const float* Sin = ws == nullptr ? S + bh * dkdv : ws + (bh * n_seg + seg) * dkdv;
     StateStage<Cf> ss;
     ss.load(Sin, dk, dv, dv, tid);
     Tile<bf16, CT, 128, typename Cf::LQL, NTH> tq;
@@ -847,7 +850,7 @@ __global__ __launch_bounds__(512) void k_chunk_walk_wide(
     }
     store_out<Cf, true>(Ob, Oacc, t_prev, n_prev, dv, dv, w, g, c16);
 
-    if (last_seg) {  // (the loop ended with a barrier: the tiles are free)
+    if (last_seg && bq % group == 0) {  // one writer per group (the loop ended with a barrier)
         state_regs_to_lds<Cf>(Sst, Sacc, w, g, c16);
         __syncthreads();
         state_lds_to_gmem<Cf>(S + bh * dkdv, Sst, dk, dv, dv, tid);
@@ -964,16 +967,23 @@ __global__ __launch_bounds__(512) void k_segment_states_wide(const bf16* __restr
 static int pad_dim(int x) { return x <= 32 ? 32 : (x <= 64 ? 64 : 128); }
 
 void plan_prefill(PrefillPlan& p) {
-    p.BH = p.B * p.H;
+    if (p.Hkv == 0) p.Hkv = p.H;
+    p.group = (int)(p.H / p.Hkv);
+    p.BH = p.B * p.Hkv;   // key/value heads: states, segment pass, scan
+    p.BHq = p.B * p.H;    // query heads: the walk
     p.D = pad_dim(p.dk > p.dv ? p.dk : p.dv);
     p.CT = pad_dim(p.C);
     p.BV = p.D > 64 ? 64 : p.D;
     p.n_vb = p.D / p.BV;
     p.n_c = p.T > 0 ? (p.T + p.C - 1) / p.C : 0;
-    const int64_t want = p.n_c * p.BH * p.n_vb;
+    const int64_t want = p.n_c * p.BHq * p.n_vb;
     p.G = want > kTargetWalkers ? (want + kTargetWalkers - 1) / kTargetWalkers : 1;
     if (p.G > p.n_c) p.G = p.n_c > 0 ? p.n_c : 1;
     p.n_seg = p.n_c > 0 ? (p.n_c + p.G - 1) / p.G : 0;
+    // a walk reads its starting state from the workspace when there are
+    // several segments, or several query heads per state (the group's walks
+    // must not read S while one of them writes S_T)
+    p.use_ws = p.n_seg > 1 || p.group > 1;
     const int ve = p.dtype == LLA_BF16 ? 8 : 4;
     p.vec = (p.dk % ve == 0) && (p.dv % ve == 0);
 }
@@ -983,22 +993,24 @@ static hipError_t launch_walk_t(const PrefillPlan& p, const void* Q, const void*
                                 float* S, float* O, float* ws, hipStream_t st) {
     if constexpr (std::is_same<T, bf16>::value && D == 128 && CT <= 64) {
         if (p.vec) {  // one eight-wave workgroup per (b,h) and segment
-            hipLaunchKernelGGL((k_chunk_walk_wide<CT>), dim3((unsigned)(p.BH * p.n_seg)), dim3(512), 0, st,
-                               (const bf16*)Q, (const bf16*)K, (const bf16*)V, S, O, (const float*)ws,
-                               p.T, p.dk, p.dv, p.C, p.G, p.n_seg);
+            hipLaunchKernelGGL((k_chunk_walk_wide<CT>), dim3((unsigned)(p.BHq * p.n_seg)), dim3(512), 0, st,
+                               (const bf16*)Q, (const bf16*)K, (const bf16*)V, S, O,
+                               (const float*)(p.use_ws ? ws : nullptr), p.T, p.dk, p.dv, p.C, p.G,
+                               p.n_seg, p.group);
             return hipGetLastError();
         }
     }
     constexpr int BV = D > 64 ? 64 : D;
-    const int64_t grid = p.BH * p.n_seg * p.n_vb;
+    const int64_t grid = p.BHq * p.n_seg * p.n_vb;
+    const float* wsr = p.use_ws ? ws : nullptr;
     if (p.vec)
         hipLaunchKernelGGL((k_chunk_walk<T, CT, D, BV, true>), dim3((unsigned)grid), dim3(kThreads), 0,
-                           st, (const T*)Q, (const T*)K, (const T*)V, S, O, (const float*)ws, p.T,
-                           p.dk, p.dv, p.C, p.G, p.n_seg, p.n_vb);
+                           st, (const T*)Q, (const T*)K, (const T*)V, S, O, wsr, p.T,
+                           p.dk, p.dv, p.C, p.G, p.n_seg, p.n_vb, p.group);
     else
         hipLaunchKernelGGL((k_chunk_walk<T, CT, D, BV, false>), dim3((unsigned)grid), dim3(kThreads), 0,
-                           st, (const T*)Q, (const T*)K, (const T*)V, S, O, (const float*)ws, p.T,
-                           p.dk, p.dv, p.C, p.G, p.n_seg, p.n_vb);
+                           st, (const T*)Q, (const T*)K, (const T*)V, S, O, wsr, p.T,
+                           p.dk, p.dv, p.C, p.G, p.n_seg, p.n_vb, p.group);
     return hipGetLastError();
 }
 
@@ -1069,7 +1081,7 @@ hipError_t launch_segment_states(const PrefillPlan& p, const void* K, const void
 }
 
 hipError_t launch_state_scan(const PrefillPlan& p, const float* S, float* ws, hipStream_t st) {
-    if (p.n_seg <= 1) return hipSuccess;
+    if (!p.use_ws) return hipSuccess;
     const int64_t dkdv = (int64_t)p.dk * p.dv;
     const int64_t per_block = (int64_t)kThreads * 4;
     const int64_t blocks_per_bh = (dkdv + per_block - 1) / per_block;

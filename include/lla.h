@@ -179,6 +179,43 @@ lla_status lla_decode_step(const void *q, const void *k, const void *v, lla_dtyp
                            int64_t B, int64_t H, int64_t dk, int64_t dv, float *S, float *o,
                            void *stream);
 
+/*
+ * Shared-state heads.  Hq query heads are grouped on Hkv key/value heads
+ * (group size G = Hq / Hkv; query head h reads key/value head h / G), as in
+ * grouped-query attention (blog "A 128 000 tokens, l'attention avale 85 % du
+ * calcul", section on sharing heads to lighten memory).  Every key/value head
+ * carries one state, updated once per token; each query head of its group
+ * reads it:  S_t = S_{t-1} + k_t v_t^T,  o_t^(h) = S_t^T q_t^(h).
+ *
+ * Layouts: Q, O as lla_prefill with Hq heads; K, V and S as lla_prefill with
+ * Hkv heads.  Conditions: 1 <= Hkv <= Hq, Hq a multiple of Hkv (else
+ * LLA_ERR_SHAPE); the rest as lla_prefill.  With Hq = Hkv these are
+ * lla_prefill and lla_prefill_workspace_size.  The per-segment K^T V and the
+ * segment scan run once per key/value head; each query head's walk reads
+ * them.  When G > 1 the walks always start from the workspace (which then
+ * holds at least one state per key/value head), and the fused short-prompt
+ * route is not taken.
+ */
+size_t lla_prefill_gqa_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t T,
+                                      int64_t dk, int64_t dv, int64_t C);
+
+lla_status lla_prefill_gqa(const void *Q, const void *K, const void *V, lla_dtype dtype,
+                           int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t dk,
+                           int64_t dv, int64_t C, float *S, float *O, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+/*
+ * One decode step with shared-state heads: q: [B][Hq][dk], k: [B][Hkv][dk],
+ * v: [B][Hkv][dv] (dtype); S: [B][Hkv][dk][dv] fp32 updated once in place;
+ * o: [B][Hq][dv] fp32.  Each state is read from memory once for the G query
+ * heads of its group.  For G > 1 this build needs dk = dv in {64, 128} and
+ * G <= 16 (else LLA_ERR_UNSUPPORTED); G = 1 is lla_decode_step.  Per query
+ * head the arithmetic is that of lla_decode_step (identical bits).
+ */
+lla_status lla_decode_step_gqa(const void *q, const void *k, const void *v, lla_dtype dtype,
+                               int64_t B, int64_t Hq, int64_t Hkv, int64_t dk, int64_t dv,
+                               float *S, float *o, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

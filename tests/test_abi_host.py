@@ -50,6 +50,12 @@ def lib():
     L.lla_state_init.restype = ctypes.c_int
     L.lla_state_init.argtypes = [vp] + [i64] * 4 + [vp]
     L.lla_last_device_error.restype = ctypes.c_int
+    L.lla_prefill_gqa_workspace_size.restype = sz
+    L.lla_prefill_gqa_workspace_size.argtypes = [i64] * 7
+    L.lla_prefill_gqa.restype = ctypes.c_int
+    L.lla_prefill_gqa.argtypes = [vp, vp, vp, ctypes.c_int] + [i64] * 7 + [vp, vp, vp, sz, vp]
+    L.lla_decode_step_gqa.restype = ctypes.c_int
+    L.lla_decode_step_gqa.argtypes = [vp, vp, vp, ctypes.c_int] + [i64] * 5 + [vp, vp, vp]
     return L
 
 
@@ -188,3 +194,75 @@ def test_python_binding_raises_without_touching_the_gpu():
     S = torch.zeros((1, 1, 2, 2), dtype=torch.float32)
     with pytest.raises((lla.LlaError, ValueError, RuntimeError)):
         lla.prefill(q, q, q, S, chunk=4)  # CPU tensors are refused
+
+
+# ---- shared-state heads (Hq query heads on Hkv key/value heads) --------------------
+
+def _gqa_args(b, Hq, Hkv):
+    return (b.q, b.k, b.v, b.dtype, b.B, Hq, Hkv, b.T, b.dk, b.dv, b.C, b.S, b.O, b.ws,
+            b.ws_bytes, None)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 0), (4, 3), (2, 4), (0, 0), (6, -2)])
+def test_prefill_gqa_rejects_head_counts(lib, Hq, Hkv):
+    assert lib.lla_prefill_gqa(*_gqa_args(Bufs(), Hq, Hkv)) == E_SHAPE
+    assert lib.lla_prefill_gqa_workspace_size(1, Hq, Hkv, 100, 64, 64, 64) == 0
+
+
+@pytest.mark.parametrize("change,expect", [
+    (dict(q=None), E_NULL), (dict(S=None), E_NULL), (dict(dtype=7), E_DTYPE),
+    (dict(k=2 * A + 4), E_ALIGN), (dict(T=8192, ws=None), E_WS),
+])
+def test_prefill_gqa_checks_like_prefill(lib, change, expect):
+    b = Bufs()
+    for key, val in change.items():
+        setattr(b, key, val)
+    assert lib.lla_prefill_gqa(*_gqa_args(b, 8, 2)) == expect
+
+
+def test_prefill_gqa_spans_use_their_own_head_counts(lib):
+    # Q and O span Hq heads, K, V and S span Hkv: with 8 query heads on 2
+    # key/value heads (T = 100, dk = dv = 64, bf16), K ends at 2*A + 2*100*64*2.
+    b = Bufs()
+    kv_bytes = 2 * 100 * 64 * 2
+    b.O = 2 * A + kv_bytes - 64  # inside K
+    assert lib.lla_prefill_gqa(*_gqa_args(b, 8, 2)) == E_ALIAS
+    b = Bufs()
+    b.S = 3 * A + 2 * 100 * 64 * 2 - 16  # S starts inside V
+    assert lib.lla_prefill_gqa(*_gqa_args(b, 8, 2)) == E_ALIAS
+
+
+def test_prefill_gqa_workspace(lib):
+    # a group of one is the plain call
+    for args in [(1, 16, 8192, 128, 128, 64), (3, 5, 1000, 33, 33, 17), (2, 4, 10, 64, 64, 64)]:
+        B, H = args[0], args[1]
+        assert lib.lla_prefill_gqa_workspace_size(B, H, H, *args[2:]) == \
+            lib.lla_prefill_workspace_size(*args)
+    # groups always stage the start states in the workspace: one state per
+    # key/value head per segment, even for a single segment
+    assert lib.lla_prefill_gqa_workspace_size(2, 8, 2, 10, 64, 64, 64) == 2 * 2 * 64 * 64 * 4
+    ws = lib.lla_prefill_gqa_workspace_size(1, 16, 4, 8192, 128, 128, 64)
+    assert ws == 4 * 16 * 128 * 128 * 4  # the T=8192 plan: 16 segments of 8 chunks
+
+
+@pytest.mark.parametrize("change,expect", [
+    (dict(Hkv=0), E_SHAPE), (dict(Hq=6, Hkv=4), E_SHAPE), (dict(Hq=2, Hkv=4), E_SHAPE),
+    (dict(Hq=17, Hkv=1), E_UNSUP), (dict(dk=96, dv=96), E_UNSUP), (dict(dk=64, dv=128), E_UNSUP),
+    (dict(q=None), E_NULL), (dict(dtype=5), E_DTYPE), (dict(o=2 * A + 256), E_ALIAS),
+])
+def test_decode_gqa_rejects(lib, change, expect):
+    d = dict(q=A, k=2 * A, v=3 * A, dtype=BF16, B=2, Hq=8, Hkv=2, dk=128, dv=128, S=4 * A, o=5 * A)
+    d.update(change)
+    assert lib.lla_decode_step_gqa(d["q"], d["k"], d["v"], d["dtype"], d["B"], d["Hq"], d["Hkv"],
+                                   d["dk"], d["dv"], d["S"], d["o"], None) == expect
+
+
+def test_python_binding_checks_grouped_shapes():
+    import torch
+    q = torch.zeros((1, 6, 8, 4), dtype=torch.bfloat16)
+    k = torch.zeros((1, 4, 8, 4), dtype=torch.bfloat16)
+    S = torch.zeros((1, 4, 4, 4), dtype=torch.float32)
+    with pytest.raises(ValueError):
+        lla.prefill(q, k, k, S, chunk=4)  # 6 query heads cannot share 4 key/value heads
+    with pytest.raises(ValueError):
+        lla.decode_step(q[:, :, 0], k[:, :, 0], k[:, :, 0], S)

@@ -1,0 +1,175 @@
+"""Shared-state heads: Hq query heads grouped on Hkv key/value heads (blog "A
+128 000 tokens, l'attention avale 85 % du calcul", section on sharing heads).
+Query head h reads key/value head h // G, G = Hq / Hkv.  The prefill and the
+decode step are checked against the oracle (exact on integer inputs, within
+the bf16 tolerance on gaussian ones), against the plain call on key/value
+heads repeated over their group (the same arithmetic: identical bits), and at
+the full benchmark sizes on sampled heads."""
+import numpy as np
+import pytest
+import torch
+
+import decode_lla_prefill_amd as lla
+import oracle
+import workloads
+from gpu_util import TOL, need_gpu, np64, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return need_gpu()
+
+
+def _run_prefill(q, k, v, S0, C, dev):
+    S = S0.to(dev, torch.float32).contiguous().clone()
+    o = lla.prefill(q.to(dev).contiguous(), k.to(dev).contiguous(), v.to(dev).contiguous(), S, chunk=C)
+    torch.cuda.synchronize()
+    return o, S
+
+
+# B, Hq, Hkv, T, dk, dv, C, dtype: the eight-wave bf16 d=128 walk (one and
+# several segments, ragged tail), d=64, a short prompt (chunked for groups),
+# the fp32 and ragged-dimension paths, the largest group the decode takes
+GQA_INT = [
+    (2, 8, 2, 300, 128, 128, 64, torch.bfloat16),
+    (1, 4, 1, 2100, 128, 128, 64, torch.bfloat16),
+    (1, 6, 3, 130, 64, 64, 32, torch.bfloat16),
+    (2, 4, 2, 9, 128, 128, 64, torch.bfloat16),
+    (2, 6, 3, 77, 40, 72, 16, torch.float32),
+    (1, 16, 1, 200, 64, 64, 64, torch.bfloat16),
+    (3, 2, 1, 260, 104, 120, 20, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,dk,dv,C,dtype", GQA_INT)
+def test_gqa_prefill_integers_exact(dev, B, Hq, Hkv, T, dk, dv, C, dtype):
+    print("gqa prefill int", B, Hq, Hkv, T, dk, dv, C, dtype, flush=True)
+    q, k, v = workloads.integers(B, Hq, T, dk, dv, seed=T + Hq, dtype=dtype, Hkv=Hkv)
+    S0 = torch.randint(-300, 301, (B, Hkv, dk, dv), generator=torch.Generator().manual_seed(T)).float()
+    o, S = _run_prefill(q, k, v, S0, C, dev)
+    O_ref, S_ref = oracle.grouped_recurrence(q, k, v, S0, nthreads=8)
+    assert np.array_equal(np64(o), O_ref)
+    assert np.array_equal(np64(S), S_ref)
+
+
+@pytest.mark.parametrize("T,C", [(1000, 64), (517, 32)])
+def test_gqa_prefill_gaussian(dev, T, C):
+    B, Hq, Hkv, d = 1, 16, 4, 128
+    q, k, v = workloads.gaussian(B, Hq, T, d, d, seed_base=T, scale=d ** -0.5, l2norm_k=True, Hkv=Hkv)
+    S0 = torch.randn((B, Hkv, d, d), generator=torch.Generator().manual_seed(C))
+    o, S = _run_prefill(q, k, v, S0, C, dev)
+    O_ref, S_ref = oracle.grouped_recurrence(q, k, v, S0, nthreads=8)
+    assert rel_err(np64(o), O_ref) <= TOL
+    assert rel_err(np64(S), S_ref) <= TOL
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,d,C", [(2, 8, 2, 300, 128, 64), (1, 12, 4, 1500, 64, 64),
+                                            (1, 16, 4, 8192, 128, 64)])
+def test_gqa_prefill_equals_repeated_heads(dev, B, Hq, Hkv, T, d, C):
+    """Repeating every key/value head (and its state) over its group and making
+    the plain call gives the same bits: each query head's walk does the same
+    arithmetic on the same data, and the segment plan depends on Hq only."""
+    G = Hq // Hkv
+    q, k, v = workloads.gaussian(B, Hq, T, d, d, seed_base=7, scale=d ** -0.5, device=dev, Hkv=Hkv)
+    S0 = torch.randn((B, Hkv, d, d), generator=torch.Generator(device=dev).manual_seed(3), device=dev)
+    S_g = S0.clone()
+    o_g = lla.prefill(q, k, v, S_g, chunk=C)
+    S_r = S0.repeat_interleave(G, dim=1).contiguous()
+    o_r = lla.prefill(q, k.repeat_interleave(G, dim=1).contiguous(),
+                      v.repeat_interleave(G, dim=1).contiguous(), S_r, chunk=C)
+    torch.cuda.synchronize()
+    assert torch.equal(o_g, o_r)
+    for g in range(G):
+        assert torch.equal(S_g, S_r[:, g::G])
+
+
+def test_gqa_prefill_full_size_sampled(dev):
+    """The grouped T=8192 workload (16 query heads on 4 key/value heads,
+    d=128, C=64) in the launch configuration the benchmark times; three query
+    heads and every key/value state against the oracle."""
+    cfg = workloads.CONFIGS["g3"]
+    q, k, v = workloads.config_inputs(cfg, device=dev)
+    S = lla.state_init(cfg.B, cfg.kv_heads, cfg.dk, cfg.dv, device=dev)
+    call = lla.PreparedPrefill(q, k, v, S, cfg.C)
+    call(zero_state=True)
+    torch.cuda.synchronize()
+    G = cfg.H // cfg.kv_heads
+    for h in (0, 6, 15):
+        O_ref, _ = oracle.recurrence(q[:, h:h + 1].cpu(), k[:, h // G:h // G + 1].cpu(),
+                                     v[:, h // G:h // G + 1].cpu(), nthreads=8)
+        assert rel_err(np64(call.out[:, h:h + 1]), O_ref) <= TOL, h
+    kc, vc = k.cpu(), v.cpu()
+    _, S_ref = oracle.recurrence(kc, kc, vc, nthreads=8)  # the state ignores the queries
+    assert rel_err(np64(S), S_ref) <= TOL
+
+
+# ---- decode ---------------------------------------------------------------------
+
+@pytest.mark.parametrize("B,Hq,Hkv,d,dtype", [(3, 8, 2, 128, torch.bfloat16), (2, 16, 1, 64, torch.float32),
+                                              (4, 6, 3, 64, torch.bfloat16), (1, 2, 1, 128, torch.float32)])
+def test_gqa_decode_integers_exact(dev, B, Hq, Hkv, d, dtype):
+    print("gqa decode int", B, Hq, Hkv, d, dtype, flush=True)
+    gen = torch.Generator().manual_seed(Hq * 10 + d)
+    q = torch.randint(-2, 3, (B, Hq, d), generator=gen).to(dtype)
+    k = torch.randint(-2, 3, (B, Hkv, d), generator=gen).to(dtype)
+    v = torch.randint(-2, 3, (B, Hkv, d), generator=gen).to(dtype)
+    S0 = torch.randint(-300, 301, (B, Hkv, d, d), generator=gen).float()
+    S = S0.to(dev).contiguous()
+    o = lla.decode_step(q.to(dev).contiguous(), k.to(dev).contiguous(), v.to(dev).contiguous(), S)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.grouped_decode_step(q, k, v, S0)
+    assert np.array_equal(np64(o), o_ref)
+    assert np.array_equal(np64(S), S_ref)
+
+
+@pytest.mark.parametrize("Hq,Hkv,d", [(32, 8, 128), (16, 1, 128), (8, 8, 64), (12, 3, 64)])
+def test_gqa_decode_equals_repeated_heads(dev, Hq, Hkv, d):
+    B, G = 5, Hq // Hkv
+    gen = torch.Generator(device=dev).manual_seed(Hq + d)
+    q = torch.randn((B, Hq, d), generator=gen, device=dev).to(torch.bfloat16)
+    k = torch.randn((B, Hkv, d), generator=gen, device=dev).to(torch.bfloat16)
+    v = torch.randn((B, Hkv, d), generator=gen, device=dev).to(torch.bfloat16)
+    S0 = torch.randn((B, Hkv, d, d), generator=gen, device=dev)
+    S_g = S0.clone()
+    o_g = lla.decode_step(q, k, v, S_g)
+    S_r = S0.repeat_interleave(G, dim=1).contiguous()
+    o_r = lla.decode_step(q, k.repeat_interleave(G, dim=1).contiguous(),
+                          v.repeat_interleave(G, dim=1).contiguous(), S_r)
+    torch.cuda.synchronize()
+    assert torch.equal(o_g, o_r)
+    assert torch.equal(S_g, S_r[:, ::G])
+
+
+def test_gqa_decode_steps_continue_a_grouped_prefill(dev):
+    B, Hq, Hkv, T, d = 2, 8, 2, 150, 128
+    q, k, v = workloads.gaussian(B, Hq, T, d, d, seed_base=11, scale=d ** -0.5, Hkv=Hkv)
+    S = lla.state_init(B, Hkv, d, d, device=dev)
+    o = lla.prefill(q[:, :, :140].to(dev).contiguous(), k[:, :, :140].to(dev).contiguous(),
+                    v[:, :, :140].to(dev).contiguous(), S, chunk=64)
+    outs = [lla.decode_step(q[:, :, t].to(dev).contiguous(), k[:, :, t].to(dev).contiguous(),
+                            v[:, :, t].to(dev).contiguous(), S) for t in range(140, T)]
+    torch.cuda.synchronize()
+    O_ref, S_ref = oracle.grouped_recurrence(q, k, v, nthreads=8)
+    assert rel_err(np64(o), O_ref[:, :, :140]) <= TOL
+    assert rel_err(np.stack([np64(x) for x in outs], axis=2), O_ref[:, :, 140:]) <= TOL
+    assert rel_err(np64(S), S_ref) <= TOL
+
+
+def test_gqa_decode_full_size_sampled(dev):
+    """One step of the grouped decode batch (256 sequences, 32 query heads on
+    8 key/value heads, d=128) as the benchmark launches it; sampled sequences
+    against the oracle."""
+    cfg = workloads.CONFIGS["g5"]
+    S0 = workloads.random_state(cfg, device=dev)
+    qd, kd, vd = workloads.decode_inputs(cfg, 1, device=dev)
+    S = S0.clone()
+    o = torch.empty((cfg.B, cfg.H, cfg.dv), dtype=torch.float32, device=dev)
+    lla.PreparedDecode(qd[0], kd[0], vd[0], S, out=o)()
+    torch.cuda.synchronize()
+    for b in (0, 97, 255):
+        o_ref, S_ref = oracle.grouped_decode_step(qd[0, b:b + 1].cpu(), kd[0, b:b + 1].cpu(),
+                                                  vd[0, b:b + 1].cpu(), S0[b:b + 1].cpu())
+        assert rel_err(np64(o[b:b + 1]), o_ref) <= 1e-5, b
+        assert rel_err(np64(S[b:b + 1]), S_ref) <= 1e-6, b

@@ -247,3 +247,105 @@ def test_bf16_inputs_are_upcast_exactly():
     v = torch.ones(1, 1, 1, dtype=torch.bfloat16)
     O, _ = oracle.recurrence(q, k, v)
     assert O[0, 0, 0] == (1.0 + 2 ** -7) - 3.0 + 2 ** -20
+
+
+# --- shared-state heads (grouped query heads) -----------------------------------
+# Blog "A 128 000 tokens, l'attention avale 85 % du calcul", section on sharing
+# heads: G query heads read one key/value head.  Query head h uses key/value
+# head h // G.
+
+def _grouped_brute_force(q, k, v, S0):
+    """o[b,h,t,j] = sum_{s<=t} (q_t . k_s) v_s[j] + sum_i q_t[i] S0[i][j] over the
+    key/value head h // G, as explicit loops; S_T[b,g] = S0 + sum_s k_s v_s^T."""
+    B, Hq, T, dk = q.shape
+    Hkv, dv = k.shape[1], v.shape[3]
+    G = Hq // Hkv
+    O = np.zeros((B, Hq, T, dv))
+    for b, h, t, j in itertools.product(range(B), range(Hq), range(T), range(dv)):
+        g = h // G
+        acc = 0.0
+        for s in range(t + 1):
+            acc += sum(q[b, h, t, i] * k[b, g, s, i] for i in range(dk)) * v[b, g, s, j]
+        acc += sum(q[b, h, t, i] * S0[b, g, i, j] for i in range(dk))
+        O[b, h, t, j] = acc
+    S = np.zeros((B, Hkv, dk, dv))
+    for b, g, i, j in itertools.product(range(B), range(Hkv), range(dk), range(dv)):
+        S[b, g, i, j] = S0[b, g, i, j] + sum(k[b, g, s, i] * v[b, g, s, j] for s in range(T))
+    return O, S
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(6, 2), (4, 1), (3, 3), (4, 2)])
+def test_grouped_recurrence_vs_brute_force(Hq, Hkv):
+    rng = np.random.default_rng(50 + 10 * Hq + Hkv)
+    B, T, dk, dv = 2, 5, 3, 2
+    q, k, v = _rand((B, Hq, T, dk), rng), _rand((B, Hkv, T, dk), rng), _rand((B, Hkv, T, dv), rng)
+    S0 = _rand((B, Hkv, dk, dv), rng)
+    O, S = oracle.grouped_recurrence(q, k, v, S0)
+    O_ref, S_ref = _grouped_brute_force(q, k, v, S0)
+    assert O.shape == (B, Hq, T, dv) and S.shape == (B, Hkv, dk, dv)
+    assert np.abs(O - O_ref).max() <= 1e-12 * (1 + np.abs(O_ref).max())
+    assert np.abs(S - S_ref).max() <= 1e-12 * (1 + np.abs(S_ref).max())
+
+
+def test_grouped_recurrence_closed_form_integers():
+    """Per query head h: O = tril(Q_h K_g^T) V_g + Q_h S0_g with g = h // G, exact
+    on integer inputs (dense products, a different formula from the loop)."""
+    B, Hq, Hkv, T, dk, dv = 2, 8, 2, 70, 6, 5
+    G = Hq // Hkv
+    q, _, _ = workloads.integers(B, Hq, T, dk, dv, seed=61)
+    _, k, v = workloads.integers(B, Hkv, T, dk, dv, seed=62)
+    S0 = np.random.default_rng(63).integers(-50, 51, (B, Hkv, dk, dv)).astype(np.float64)
+    O, S = oracle.grouped_recurrence(q, k, v, S0)
+    qn, kn, vn = (x.double().numpy() for x in (q, k, v))
+    for b, h in itertools.product(range(B), range(Hq)):
+        g = h // G
+        assert np.array_equal(O[b, h], np.tril(qn[b, h] @ kn[b, g].T) @ vn[b, g] + qn[b, h] @ S0[b, g])
+    assert np.array_equal(S, S0 + np.swapaxes(kn, -1, -2) @ vn)
+
+
+def test_grouped_mapping_mistake_is_caught(monkeypatch):
+    """Planted in the oracle: pairing query head h with key/value head h % Hkv
+    (tiling the heads instead of repeating each one) must fail the closed form."""
+    B, Hq, Hkv, T, d = 1, 4, 2, 6, 3
+    q, _, _ = workloads.integers(B, Hq, T, d, d, seed=71)
+    _, k, v = workloads.integers(B, Hkv, T, d, d, seed=72)
+    qn, kn, vn = (x.double().numpy() for x in (q, k, v))
+    ref = np.stack([np.tril(qn[0, h] @ kn[0, h // 2].T) @ vn[0, h // 2] for h in range(Hq)])
+    O, _ = oracle.grouped_recurrence(q, k, v)
+    assert np.array_equal(O[0], ref)
+    monkeypatch.setattr(oracle.np, "repeat", lambda a, G, axis: np.concatenate([a] * G, axis=axis))
+    O_bad, _ = oracle.grouped_recurrence(q, k, v)
+    assert not np.array_equal(O_bad[0], ref)
+
+
+def test_group_of_one_is_the_recurrence_and_state_ignores_queries():
+    q, k, v = workloads.integers(2, 3, 40, 7, 5, seed=81)
+    S0 = np.random.default_rng(82).integers(-9, 10, (2, 3, 7, 5)).astype(np.float64)
+    O1, S1 = oracle.grouped_recurrence(q, k, v, S0)
+    O_ref, S_ref = oracle.recurrence(q, k, v, S0)
+    assert np.array_equal(O1, O_ref) and np.array_equal(S1, S_ref)
+    # with groups of 3 the state is the key/value heads' own recurrence state
+    q3, _, _ = workloads.integers(2, 9, 40, 7, 5, seed=83)
+    _, S3 = oracle.grouped_recurrence(q3, k, v, S0)
+    assert np.array_equal(S3, S_ref)
+
+
+def test_grouped_decode_continues_grouped_prefill():
+    B, Hq, Hkv, T, dk, dv = 2, 6, 2, 24, 8, 4
+    q, _, _ = workloads.integers(B, Hq, T, dk, dv, seed=91)
+    _, k, v = workloads.integers(B, Hkv, T, dk, dv, seed=92)
+    O_all, S_all = oracle.grouped_recurrence(q, k, v)
+    O_pre, S = oracle.grouped_recurrence(q[:, :, :20], k[:, :, :20], v[:, :, :20])
+    assert np.array_equal(O_pre, O_all[:, :, :20])
+    for t in range(20, T):
+        o, S = oracle.grouped_decode_step(q[:, :, t], k[:, :, t], v[:, :, t], S)
+        assert np.array_equal(o, O_all[:, :, t])
+    assert np.array_equal(S, S_all)
+
+
+def test_grouped_rejects_bad_head_counts():
+    z = np.zeros
+    with pytest.raises(ValueError):
+        oracle.grouped_recurrence(z((1, 5, 2, 3)), z((1, 2, 2, 3)), z((1, 2, 2, 3)))
+    with pytest.raises(ValueError):
+        oracle.grouped_decode_step(z((1, 2, 3)), z((1, 4, 3)), z((1, 4, 3)), z((1, 4, 3, 3)))

@@ -45,10 +45,17 @@ class Config:
     l2norm_k: bool = False
     seed_base: int = 0
     decode_steps: int = 0
+    Hkv: int = 0  # key/value heads (0: one per query head)
     note: str = field(default="", compare=False)
 
+    @property
+    def kv_heads(self) -> int:
+        return self.Hkv or self.H
 
-# c1: the deck's toy; c2..c4: prefill shapes; c5: decode after a T=4096 prefill.
+
+# c1: the deck's toy; c2..c4: prefill shapes; c5: decode after a T=4096 prefill;
+# g3, g5: the T=8192 prefill and the decode batch with four query heads per
+# key/value head (shared-state heads, as in grouped-query attention).
 CONFIGS = {
     "c1": Config("toy", 1, 1, 8, 4, 2, 2, torch.float32, seed_base=10,
                  note="variant 0 = the deck's trace, variants 1..100 uniform {0,1}"),
@@ -60,6 +67,11 @@ CONFIGS = {
                  torch.bfloat16, scale=128 ** -0.5, seed_base=40),
     "c5": Config("decode_B256_H32_d128_after_T4096", 256, 32, 4096, 64, 128, 128,
                  torch.bfloat16, scale=128 ** -0.5, seed_base=50, decode_steps=512),
+    "g3": Config("prefill_B1_Hq16_Hkv4_T8192_C64_d128", 1, 16, 8192, 64, 128, 128,
+                 torch.bfloat16, scale=128 ** -0.5, l2norm_k=True, seed_base=60, Hkv=4),
+    "g5": Config("decode_B256_Hq32_Hkv8_d128", 256, 32, 1, 64, 128, 128,
+                 torch.bfloat16, scale=128 ** -0.5, seed_base=70, decode_steps=512, Hkv=8,
+                 note="state drawn N(0,1) (seed 10*config + 6), not from a prefill"),
 }
 
 
@@ -83,18 +95,20 @@ def _gen(device, seed):
 
 
 def gaussian(B, H, T, dk, dv, seed_base, scale, dtype=torch.bfloat16,
-             l2norm_k=False, device="cpu"):
-    """Q, K [B,H,T,dk] and V [B,H,T,dv]: N(0,1)*scale in fp32, then cast.
+             l2norm_k=False, device="cpu", Hkv=None):
+    """Q [B,H,T,dk], K [B,Hkv,T,dk] and V [B,Hkv,T,dv] (Hkv defaults to H):
+    N(0,1)*scale in fp32, then cast.
 
     Generated in slices along B so that large device workloads never hold
     more than one slice of fp32 temporaries.
     """
     out = []
-    for which, d in ((0, dk), (1, dk), (2, dv)):
+    Hkv = Hkv or H
+    for which, d, heads in ((0, dk, H), (1, dk, Hkv), (2, dv, Hkv)):
         g = _gen(device, seed_base + which)
-        t = torch.empty((B, H, T, d), dtype=dtype, device=device)
+        t = torch.empty((B, heads, T, d), dtype=dtype, device=device)
         for b in range(B):
-            x = torch.randn((H, T, d), generator=g, dtype=torch.float32, device=device)
+            x = torch.randn((heads, T, d), generator=g, dtype=torch.float32, device=device)
             x.mul_(scale)
             if which == 1 and l2norm_k:
                 x = x / x.norm(dim=-1, keepdim=True).clamp_min(1e-30)
@@ -104,33 +118,43 @@ def gaussian(B, H, T, dk, dv, seed_base, scale, dtype=torch.bfloat16,
     return tuple(out)
 
 
-def integers(B, H, T, dk, dv, seed, lo=-1, hi=1, dtype=torch.bfloat16, device="cpu"):
-    """Q, K, V with integer values uniform in [lo, hi], stored in ``dtype``."""
+def integers(B, H, T, dk, dv, seed, lo=-1, hi=1, dtype=torch.bfloat16, device="cpu", Hkv=None):
+    """Q [B,H,T,dk], K, V [B,Hkv,T,*] (Hkv defaults to H) with integer values
+    uniform in [lo, hi], stored in ``dtype``."""
     g = _gen("cpu", seed)
+    Hkv = Hkv or H
     q = torch.randint(lo, hi + 1, (B, H, T, dk), generator=g).to(dtype)
-    k = torch.randint(lo, hi + 1, (B, H, T, dk), generator=g).to(dtype)
-    v = torch.randint(lo, hi + 1, (B, H, T, dv), generator=g).to(dtype)
+    k = torch.randint(lo, hi + 1, (B, Hkv, T, dk), generator=g).to(dtype)
+    v = torch.randint(lo, hi + 1, (B, Hkv, T, dv), generator=g).to(dtype)
     return q.to(device), k.to(device), v.to(device)
 
 
 def config_inputs(cfg: Config, device="cpu", T=None, B=None):
     """The prefill inputs of a config (optionally truncated in T or B)."""
     return gaussian(B or cfg.B, cfg.H, T or cfg.T, cfg.dk, cfg.dv, cfg.seed_base,
-                    cfg.scale, cfg.dtype, cfg.l2norm_k, device)
+                    cfg.scale, cfg.dtype, cfg.l2norm_k, device, Hkv=cfg.kv_heads)
 
 
 def decode_inputs(cfg: Config, steps: int, device="cpu", B=None):
-    """Per-step decode inputs q, k [steps,B,H,dk], v [steps,B,H,dv] (bf16).
+    """Per-step decode inputs q [steps,B,H,dk], k [steps,B,Hkv,dk] and
+    v [steps,B,Hkv,dv] (bf16).
 
     Drawn like :func:`gaussian` with seeds 10*config + {3, 4, 5}.
     """
     B = B or cfg.B
     out = []
-    for which, d in ((3, cfg.dk), (4, cfg.dk), (5, cfg.dv)):
+    for which, d, heads in ((3, cfg.dk, cfg.H), (4, cfg.dk, cfg.kv_heads), (5, cfg.dv, cfg.kv_heads)):
         g = _gen(device, cfg.seed_base + which)
-        t = torch.empty((steps, B, cfg.H, d), dtype=cfg.dtype, device=device)
+        t = torch.empty((steps, B, heads, d), dtype=cfg.dtype, device=device)
         for s in range(steps):
-            x = torch.randn((B, cfg.H, d), generator=g, dtype=torch.float32, device=device)
+            x = torch.randn((B, heads, d), generator=g, dtype=torch.float32, device=device)
             t[s].copy_(x.mul_(cfg.scale))
         out.append(t)
     return tuple(out)
+
+
+def random_state(cfg: Config, device="cpu", B=None):
+    """A state S [B,Hkv,dk,dv] fp32 drawn N(0,1) with seed 10*config + 6."""
+    g = _gen(device, cfg.seed_base + 6)
+    return torch.randn((B or cfg.B, cfg.kv_heads, cfg.dk, cfg.dv), generator=g,
+                       dtype=torch.float32, device=device)
