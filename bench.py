@@ -271,7 +271,7 @@ def bench_decode(args, torch, lla, workloads, profiling):
     return res
 
 
-def bench_grouped(args, torch, lla, workloads):
+def bench_grouped(args, torch, lla, workloads, profiling):
     """Shared-state heads: the T=8192 prefill with 16 query heads on 4
     key/value heads, and the decode batch with 32 query heads on 8."""
     dev = torch.device("cuda:0")
@@ -320,6 +320,7 @@ def bench_grouped(args, torch, lla, workloads):
            "roofline": {"kernel": "k_decode_group<bf16,128,512>", "bound": "hbm",
                         "achieved": nbytes / (kern_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                         "unit": "GB/s", "frac": nbytes / (kern_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                        "traffic": profiling.stored_traffic("decode_group"),
                         "algorithmic_bytes": nbytes, "kernel_ms": kern_ms,
                         "timing": "HIP events around the timed steps, cycling over 3 state sets"}}
     del calls, qd, kd, vd, S, S0
@@ -378,7 +379,7 @@ def main():
     if not args.skip_decode:
         line["decode"] = bench_decode(args, torch, lla, workloads, profiling)
     if not args.skip_grouped:
-        line["grouped_heads"] = bench_grouped(args, torch, lla, workloads)
+        line["grouped_heads"] = bench_grouped(args, torch, lla, workloads, profiling)
     print(json.dumps(line))
 
 

@@ -3,9 +3,11 @@
     python -m decode_lla_prefill_amd.profiling run [--launches N]
         On cuda:0: N prefill steps of the T=8192 workload (B=1, H=16, C=64,
         d=128; state init and the three phases, over rotating input sets),
-        N decode steps of the 256 x 32 x 128 x 128 state, and N device-to-
-        device copies of 1 GiB, the reference of known size for the HBM byte
-        counters.  Meant to run under ``rocprofv3 --pmc``.
+        N decode steps of the 256 x 32 x 128 x 128 state, N grouped decode
+        steps (256 sequences, 32 query heads on 8 key/value heads, three
+        rotating state sets), and N device-to-device copies of 1 GiB, the
+        reference of known size for the HBM byte counters.  Meant to run
+        under ``rocprofv3 --pmc``.
 
     python -m decode_lla_prefill_amd.profiling stats OUT_DIR
         Per-kernel launch durations from a ``rocprofv3 --kernel-trace --stats
@@ -13,7 +15,7 @@
         the trace split by grid size (one kernel can run on several shapes).
 
     python -m decode_lla_prefill_amd.profiling traffic KERNEL FETCH_DIR WRITE_DIR
-        HBM bytes per launch of KERNEL (chunk_walk or decode_step) from a
+        HBM bytes per launch of KERNEL (a key of KERNELS) from a
         FETCH_SIZE pass and a WRITE_SIZE pass of ``run``: each counter is
         scaled by what it reads for the 1 GiB copy, whose true traffic is
         1 GiB read and 1 GiB written.  Prints ``key = value`` lines; bench.py
@@ -45,6 +47,8 @@ KERNELS = {
                    ("lla_prefill.hip", "lla_device.h")),
     "decode_step": ("k_decode_step", 256 * 32 * 512, "decode_step_B256_H32_traffic.txt",
                     ("lla_decode.hip", "lla_device.h")),
+    "decode_group": ("k_decode_group", 256 * 8 * 512, "decode_group_B256_Hq32_Hkv8_traffic.txt",
+                     ("lla_decode.hip", "lla_device.h")),
 }
 
 
@@ -118,6 +122,18 @@ def run(launches: int) -> None:
     torch.cuda.synchronize()
     print("decode: %d steps" % launches, flush=True)
     del calls, S
+    torch.cuda.empty_cache()
+
+    gc = workloads.CONFIGS["g5"]
+    S0 = workloads.random_state(gc, device=dev)
+    states = [S0] + [S0.clone() for _ in range(2)]
+    qd, kd, vd = workloads.decode_inputs(gc, launches, device=dev)
+    calls = [PreparedDecode(qd[i], kd[i], vd[i], states[i % 3]) for i in range(launches)]
+    for c in calls:
+        c()
+    torch.cuda.synchronize()
+    print("grouped decode: %d steps" % launches, flush=True)
+    del calls, states, S0
     torch.cuda.empty_cache()
 
     src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
