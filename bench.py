@@ -7,7 +7,8 @@ second) on the T=8192 workload (B=1, H=16, C=64, d_k=d_v=128, bf16 Q/K/V,
 fp32 state and output); the decode workload (256 sequences x 32 heads,
 d=128, state from a seeded T=4096 prefill) is reported under ``decode`` in
 steps/s.  The same two workloads with query heads grouped four to a
-key/value head (shared states) are reported under ``grouped_heads``.
+key/value head (shared states) are reported under ``grouped_heads``, and with
+FP8 (E4M3) inputs under ``fp8_inputs``.
 
 Prefill is timed cold: the timed steps rotate over several input/output
 sets whose total exceeds the 256 MB Infinity Cache, so each step's inputs
@@ -40,28 +41,29 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 matrix cores, TFLOP/s
 METRIC = "prefill tokens/s + % bf16 MFMA peak; decode steps/s + % HBM BW (1 GPU)"
-def prefill_work(B, H, T, C, d, Hkv=None):
+def prefill_work(B, H, T, C, d, Hkv=None, in_bytes=2):
     """Algorithmic flops and bytes of one prefill (kept triangle only), with
-    H query heads on Hkv key/value heads (default: one each).
+    H query heads on Hkv key/value heads (default: one each) and inputs of
+    `in_bytes` bytes per element (2: bf16, 1: FP8).
 
     flops per query-head token: 2d(C+1) (scores + masked scores x V over the
     kept triangle) + 2d^2 (Q S); per key/value-head token: 2d^2 (K^T V) +
-    d^2/C (the state add per chunk).  bytes per query-head token: 2d (bf16 Q)
-    + 4d (fp32 O); per key/value-head token: 4d (bf16 K, V); plus 8d^2 per
-    key/value head for reading S_0 and writing S_T.
+    d^2/C (the state add per chunk).  bytes per query-head token: Q (d
+    elements) + 4d (fp32 O); per key/value-head token: K and V (2d
+    elements); plus 8d^2 per key/value head for reading S_0 and writing S_T.
     """
     Hkv = Hkv or H
     tq, tkv = B * H * T, B * Hkv * T
     flops = tq * (2 * d * (C + 1) + 2 * d * d) + tkv * (2 * d * d + d * d / C)
-    nbytes = tq * 6 * d + tkv * 4 * d + B * Hkv * 8 * d * d
+    nbytes = tq * (in_bytes + 4) * d + tkv * 2 * in_bytes * d + B * Hkv * 8 * d * d
     return flops, nbytes
 
 
-def decode_bytes(B, H, d, Hkv=None):
+def decode_bytes(B, H, d, Hkv=None, in_bytes=2):
     """Per step: per key/value head the fp32 state read + write (8d^2) and
-    bf16 k, v (4d); per query head bf16 q (2d) and fp32 o (4d)."""
+    k, v (2d elements); per query head q (d elements) and fp32 o (4d)."""
     Hkv = Hkv or H
-    return B * Hkv * (8 * d * d + 4 * d) + B * H * 6 * d
+    return B * Hkv * (8 * d * d + 2 * in_bytes * d) + B * H * (in_bytes + 4) * d
 
 
 def repeat_for(fn, min_seconds):
@@ -328,6 +330,66 @@ def bench_grouped(args, torch, lla, workloads, profiling):
     return {"prefill": pre, "decode": dec}
 
 
+def bench_fp8(args, torch, lla, workloads, profiling):
+    """FP8 (E4M3) inputs: the T=8192 prefill and the 256 x 32 decode batch."""
+    dev = torch.device("cuda:0")
+    cfg = workloads.CONFIGS["f3"]
+    B, H, T, C, d = cfg.B, cfg.H, cfg.T, cfg.C, cfg.dk
+    q0, k0, v0 = workloads.config_inputs(cfg, device=dev)
+    sets = []
+    for r in range(args.rotate):
+        q, k, v = (x.clone() for x in (q0, k0, v0)) if r else (q0, k0, v0)
+        sets.append(lla.PreparedPrefill(q, k, v, lla.state_init(B, H, d, d, device=dev), C))
+    for i in range(args.warmup):
+        sets[i % len(sets)](zero_state=True)
+    wall, gpu = _timed(torch, lambda i: sets[i % len(sets)](zero_state=True), args.steps)
+    # the walk alone, back to back (every set's workspace holds its segment states)
+    n_walk = max(args.steps, 4 * len(sets))
+    _, walk_s = _timed(torch, lambda i: sets[i % len(sets)].chunks(), n_walk)
+    walk_ms = walk_s * 1e3 / n_walk
+    flops, nbytes = prefill_work(B, H, T, C, d, in_bytes=1)
+    step_s = gpu / args.steps
+    pre = {"workload": cfg.name, "B": B, "H": H, "T": T, "C": C, "dk": d, "dv": d,
+           "inputs": "FP8 E4M3 N(0,1); fp32 state and output",
+           "value": B * T / (wall / args.steps), "unit": "tokens/s",
+           "ms_per_step": wall * 1e3 / args.steps, "gpu_ms_per_step": step_s * 1e3,
+           "mfma_frac": flops / step_s / (PEAK_BF16_TFLOPS * 1e12),
+           "hbm_frac": nbytes / step_s / (PEAK_HBM_GBS * 1e9),
+           "roofline": {"kernel": "k_chunk_walk_wide<64, fp8e4m3>", "bound": "hbm",
+                        "achieved": nbytes / (walk_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": nbytes / (walk_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                        "traffic": None, "algorithmic_bytes": nbytes, "kernel_ms": walk_ms,
+                        "timing": "HIP events around %d back-to-back walk launches" % n_walk},
+           "timing": "HIP events around the timed steps (state init + lla_prefill), "
+                     "%d rotating input sets" % len(sets)}
+    del sets, q0, k0, v0
+    torch.cuda.empty_cache()
+
+    cfg = workloads.CONFIGS["f5"]
+    B, H, d = cfg.B, cfg.H, cfg.dk
+    S = workloads.random_state(cfg, device=dev)  # 512 MB: larger than the Infinity Cache
+    n = args.decode_steps
+    qd, kd, vd = workloads.decode_inputs(cfg, n + args.warmup, device=dev)
+    o = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    calls = [lla.PreparedDecode(qd[i], kd[i], vd[i], S, out=o) for i in range(n + args.warmup)]
+    for i in range(args.warmup):
+        calls[n + i]()
+    wall, gpu = _timed(torch, lambda i: calls[i](), n)
+    kern_ms = gpu * 1e3 / n
+    nbytes = decode_bytes(B, H, d, in_bytes=1)
+    dec = {"workload": cfg.name, "B": B, "H": H, "dk": d, "dv": d, "steps": n,
+           "value": n / wall, "unit": "steps/s", "ms_per_step": wall * 1e3 / n,
+           "gpu_ms_per_step": kern_ms, "tokens_per_s": B * n / wall,
+           "roofline": {"kernel": "k_decode_step_sq<fp8e4m3,128,512>", "bound": "hbm",
+                        "achieved": nbytes / (kern_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": nbytes / (kern_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                        "traffic": None, "algorithmic_bytes": nbytes, "kernel_ms": kern_ms,
+                        "timing": "HIP events around the timed steps"}}
+    del calls, qd, kd, vd, S
+    torch.cuda.empty_cache()
+    return {"prefill": pre, "decode": dec}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -342,6 +404,7 @@ def main():
                     help="minimum oracle time of each CPU baseline (the sample is repeated)")
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-grouped", action="store_true")
+    ap.add_argument("--skip-fp8", action="store_true")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -380,6 +443,8 @@ def main():
         line["decode"] = bench_decode(args, torch, lla, workloads, profiling)
     if not args.skip_grouped:
         line["grouped_heads"] = bench_grouped(args, torch, lla, workloads, profiling)
+    if not args.skip_fp8:
+        line["fp8_inputs"] = bench_fp8(args, torch, lla, workloads, profiling)
     print(json.dumps(line))
 
 

@@ -36,7 +36,7 @@ EXPORTS = ("lla_status_string", "lla_last_device_error", "lla_state_init",
            "lla_decode_step", "lla_prefill_gqa_workspace_size", "lla_prefill_gqa",
            "lla_decode_step_gqa")
 
-_BF16, _F32 = 0, 1
+_BF16, _F32, _FP8 = 0, 1, 2
 _lib = None
 
 
@@ -102,7 +102,9 @@ def _dtype_code(t: torch.Tensor) -> int:
         return _BF16
     if t.dtype == torch.float32:
         return _F32
-    raise TypeError("inputs must be bfloat16 or float32, got %s" % t.dtype)
+    if t.dtype == torch.float8_e4m3fn:  # OCP FP8 E4M3
+        return _FP8
+    raise TypeError("inputs must be bfloat16, float32 or float8_e4m3fn, got %s" % t.dtype)
 
 
 def _ptr(t):

@@ -30,7 +30,8 @@ Span span(const void* p, int64_t bytes) {
 }
 bool overlap(Span a, Span b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
 
-int64_t elem_size(lla_dtype dt) { return dt == LLA_BF16 ? 2 : 4; }
+int64_t elem_size(lla_dtype dt) { return dt == LLA_FP8_E4M3 ? 1 : (dt == LLA_BF16 ? 2 : 4); }
+bool known_dtype(int dt) { return dt == LLA_BF16 || dt == LLA_F32 || dt == LLA_FP8_E4M3; }
 
 // Sizes shared by every call.  `C` < 0 means "no chunk size" (decode, init).
 lla_status check_sizes(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int64_t C) {
@@ -45,7 +46,7 @@ lla_status check_sizes(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, 
 }
 
 lla_status check_dtype(int dt, int64_t C) {
-    if (dt != LLA_BF16 && dt != LLA_F32) return LLA_ERR_DTYPE;
+    if (!known_dtype(dt)) return LLA_ERR_DTYPE;
     if (dt == LLA_F32 && C > kMaxChunkF32) return LLA_ERR_UNSUPPORTED;
     return LLA_OK;
 }
@@ -248,7 +249,7 @@ lla_status decode_impl(const void* q, const void* k, const void* v, lla_dtype dt
     if (st != LLA_OK) return st;
     st = check_sizes(B, h.q, 1, dk, dv, -1);
     if (st != LLA_OK) return st;
-    if (dtype != LLA_BF16 && dtype != LLA_F32) return LLA_ERR_DTYPE;
+    if (!known_dtype(dtype)) return LLA_ERR_DTYPE;
     const int64_t group = h.q / h.kv;
     if (group > 1 && !lla::decode_group_fit(group, (int)dk, (int)dv)) return LLA_ERR_UNSUPPORTED;
     if (!q || !k || !v || !S || !o) return LLA_ERR_NULL;

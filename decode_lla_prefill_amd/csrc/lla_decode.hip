@@ -15,6 +15,7 @@
 // o; the partials of the row groups are summed through LDS in a fixed order.
 // Square heads of 64 and 128 take a compile-time-shaped kernel (128: 512
 // threads, 8 rows each), the rest a general one bounded by runtime sizes.
+// q, k, v may be bf16, fp32 or FP8 (E4M3); they are decoded to fp32 exactly.
 #include "lla_device.h"
 #include "lla_internal.h"
 
@@ -299,6 +300,7 @@ static hipError_t decode_t(const void* q, const void* k, const void* v, int64_t 
 
 hipError_t launch_decode_step(lla_dtype dtype, const void* q, const void* k, const void* v,
                               int64_t BH, int dk, int dv, float* S, float* o, hipStream_t st) {
+    if (dtype == LLA_FP8_E4M3) return decode_t<fp8e4m3>(q, k, v, BH, dk, dv, S, o, st);
     if (dtype == LLA_BF16) return decode_t<bf16>(q, k, v, BH, dk, dv, S, o, st);
     return decode_t<float>(q, k, v, BH, dk, dv, S, o, st);
 }
@@ -321,6 +323,7 @@ static hipError_t tokens_t(const void* q, const void* k, const void* v, int64_t 
 
 hipError_t launch_decode_tokens(lla_dtype dtype, const void* q, const void* k, const void* v,
                                 int64_t BH, int T, int d, float* S, float* o, hipStream_t st) {
+    if (dtype == LLA_FP8_E4M3) return tokens_t<fp8e4m3>(q, k, v, BH, T, d, S, o, st);
     if (dtype == LLA_BF16) return tokens_t<bf16>(q, k, v, BH, T, d, S, o, st);
     return tokens_t<float>(q, k, v, BH, T, d, S, o, st);
 }
@@ -343,6 +346,7 @@ static hipError_t group_t(const void* q, const void* k, const void* v, int64_t B
 
 hipError_t launch_decode_group(lla_dtype dtype, const void* q, const void* k, const void* v,
                                int64_t BHkv, int group, int d, float* S, float* o, hipStream_t st) {
+    if (dtype == LLA_FP8_E4M3) return group_t<fp8e4m3>(q, k, v, BHkv, group, d, S, o, st);
     if (dtype == LLA_BF16) return group_t<bf16>(q, k, v, BHkv, group, d, S, o, st);
     return group_t<float>(q, k, v, BHkv, group, d, S, o, st);
 }

@@ -1,6 +1,6 @@
 // lla_device.h -- device-side building blocks shared by the HIP kernels of
 // liblla (gfx950 only): vector types, the 16x16 matrix-core step, bf16
-// rounding, and global->LDS tile staging.
+// rounding, FP8 (E4M3) decoding, and global->LDS tile staging.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -39,12 +39,40 @@ __device__ __forceinline__ f32x4 mma(f32x8 a, f32x8 b, f32x4 c) {
     return c;
 }
 
+// FP8 inputs: the OCP 8-bit float with 4 exponent bits (bias 7) and 3
+// mantissa bits, subnormals, no infinities, NaN = S.1111.111 -- the format
+// torch calls float8_e4m3fn.  Every such value is a bf16 value, so decoding
+// is exact; gfx950's conversion instructions decode this format (checked on
+// all 256 codes against the format's definition).
+struct fp8e4m3 {
+    uint8_t bits;
+};
+static_assert(sizeof(fp8e4m3) == 1, "one byte per element");
+
+// Four FP8 values (byte i of w = element i) -> bf16 pairs {e0, e1}, {e2, e3}.
+__device__ __forceinline__ void fp8x4_to_bf16(uint32_t w, uint32_t& lo, uint32_t& hi) {
+    lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+    hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+}
+
+// The type the matrix cores take for a given input type: FP8 inputs are
+// staged as bf16.
+template <typename In> struct Compute { typedef In type; };
+template <> struct Compute<fp8e4m3> { typedef bf16 type; };
+
 __device__ __forceinline__ bf16 to_bf16(float x) { return (bf16)x; }  // round to nearest even
 __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
 __device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(fp8e4m3 x) {
+    const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)x.bits, false);  // element 0 = byte 0
+    return f[0];
+}
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+// Input element -> the staged type (exact for every pair used here).
+template <typename T> __device__ __forceinline__ T stage(T x) { return x; }
+template <typename T> __device__ __forceinline__ T stage(fp8e4m3 x) { return from_f32<T>(to_f32(x)); }
 
 // Elements per 16-byte vector.
 template <typename T> struct Vec { static constexpr int n = 16 / sizeof(T); };
@@ -76,15 +104,17 @@ __device__ __forceinline__ void buf_store16(rsrc_t r, uint32_t off, f32x4 x) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, off, 0, 0);
 }
 
-// A ROWS x COLS tile of T staged in LDS with layout L.
+// A ROWS x COLS tile of T staged in LDS with layout L, read from global
+// memory holding elements of type In (T itself, or FP8 decoded to bf16 on
+// the way into LDS).
 //
 // Staging is split in two halves so that the global loads of the next tile
 // can be in flight while the current one is being used: gather() issues the
 // 16-byte loads into registers, scatter() writes them to LDS.  Rows at or past
 // `nrows`, and columns at or past `ncols`, are stored as zero.
-template <typename T, int ROWS, int COLS, typename L, int NTH = kThreads>
+template <typename T, int ROWS, int COLS, typename L, int NTH = kThreads, typename In = T>
 struct Tile {
-    static constexpr int VE = Vec<T>::n;            // elements per vector
+    static constexpr int VE = Vec<In>::n;           // elements per 16-byte global vector
     static constexpr int VPR = COLS / VE;           // vectors per row
     static constexpr int NV = ROWS * VPR;           // vectors per tile
     static constexpr int NPT = (NV + NTH - 1) / NTH;  // per thread (NTH threads)
@@ -102,18 +132,18 @@ struct Tile {
         for (int n = 0; n < NPT; ++n) {
             const int e = tid + n * NTH;
             const int row = e / VPR, cv = e % VPR;
-            off[n] = (e < NV && cv * VE < ncols) ? (uint32_t)((row * ld + cv * VE) * sizeof(T)) : kOutside;
+            off[n] = (e < NV && cv * VE < ncols) ? (uint32_t)((row * ld + cv * VE) * sizeof(In)) : kOutside;
         }
     }
     // Loads the tile whose first row is at g; rows >= nrows read as zero.
-    __device__ __forceinline__ void gather(const T* __restrict__ g, int64_t ld, int nrows) {
+    __device__ __forceinline__ void gather(const In* __restrict__ g, int64_t ld, int nrows) {
         const rsrc_t rs = source(g, ld, nrows);
 #pragma unroll
         for (int n = 0; n < NPT; ++n) load(rs, n);
     }
     // The same in parts: the descriptor of a tile, then its n-th load.
-    __device__ __forceinline__ static rsrc_t source(const T* __restrict__ g, int64_t ld, int nrows) {
-        return make_rsrc(g, (uint32_t)(nrows * ld * sizeof(T)));
+    __device__ __forceinline__ static rsrc_t source(const In* __restrict__ g, int64_t ld, int nrows) {
+        return make_rsrc(g, (uint32_t)(nrows * ld * sizeof(In)));
     }
     __device__ __forceinline__ void load(rsrc_t rs, int n) { r[n] = buf_load16(rs, off[n]); }
     __device__ __forceinline__ void scatter(T* lds, int tid) const {
@@ -122,17 +152,26 @@ struct Tile {
             const int e = tid + n * NTH;
             if (FULL || e < NV) {
                 const int row = e / VPR, cv = e % VPR;
-                *reinterpret_cast<u32x4*>(lds + L::off(row, cv * VE)) = r[n];
+                if constexpr (sizeof(In) == sizeof(T)) {
+                    *reinterpret_cast<u32x4*>(lds + L::off(row, cv * VE)) = r[n];
+                } else {  // 16 FP8 values -> two 8-element bf16 vectors
+                    static_assert(sizeof(In) == 1 && sizeof(T) == 2, "FP8 stages as bf16");
+                    uint32_t x[8];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) fp8x4_to_bf16(r[n][i], x[2 * i], x[2 * i + 1]);
+                    *reinterpret_cast<u32x4*>(lds + L::off(row, cv * VE)) = u32x4{x[0], x[1], x[2], x[3]};
+                    *reinterpret_cast<u32x4*>(lds + L::off(row, cv * VE + 8)) = u32x4{x[4], x[5], x[6], x[7]};
+                }
             }
         }
     }
     // Element path for shapes the vector path cannot take: straight to LDS.
-    __device__ __forceinline__ static void load_scalar(const T* __restrict__ g, int64_t ld,
+    __device__ __forceinline__ static void load_scalar(const In* __restrict__ g, int64_t ld,
                                                        int nrows, int ncols, T* lds, int tid) {
         for (int e = tid; e < ROWS * COLS; e += NTH) {
             const int row = e / COLS, col = e % COLS;
             T x = from_f32<T>(0.0f);
-            if (row < nrows && col < ncols) x = g[(int64_t)row * ld + col];
+            if (row < nrows && col < ncols) x = stage<T>(g[(int64_t)row * ld + col]);
             lds[L::off(row, col)] = x;
         }
     }

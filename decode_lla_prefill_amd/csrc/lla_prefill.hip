@@ -443,10 +443,11 @@ __device__ __forceinline__ void chunk_output(f32x4 (&Oacc)[Cf::NT][Cf::NVW],
 // Phase 1: per-segment state increments K_seg^T V_seg -> ws slot seg + 1,
 // one workgroup per (b,h), segment (all but the last) and value block.
 // ---------------------------------------------------------------------------
-template <typename T, int CT, int D, int BV, bool VEC>
+template <typename In, int CT, int D, int BV, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_segment_states(
-    const T* __restrict__ K, const T* __restrict__ V, float* __restrict__ ws, int64_t T_len,
+    const In* __restrict__ K, const In* __restrict__ V, float* __restrict__ ws, int64_t T_len,
     int dk, int dv, int C, int64_t G, int64_t n_seg, int n_vb) {
+    using T = typename Compute<In>::type;
     using Cf = WalkCfg<T, CT, D, BV>;
     using Fr = typename Cf::Fr;
     __shared__ __attribute__((aligned(16))) unsigned char smem[Cf::SEG_BYTES];
@@ -465,8 +466,8 @@ __global__ __launch_bounds__(kThreads) void k_segment_states(
     const int nv = min(BV, dv - v0);
     const int64_t n_c = (T_len + C - 1) / C;
     const int64_t c0 = seg * G, c1 = min(n_c, c0 + G);
-    const T* Kb = K + bh * T_len * dk;
-    const T* Vb = V + bh * T_len * dv + v0;
+    const In* Kb = K + bh * T_len * dk;
+    const In* Vb = V + bh * T_len * dv + v0;
 
     f32x4 Sacc[Cf::NVW][Cf::NDT];
 #pragma unroll
@@ -480,8 +481,8 @@ __global__ __launch_bounds__(kThreads) void k_segment_states(
         // chunks of loads in flight (one register set per chunk, used round
         // robin; the loop is unrolled by PF so the sets are static).
         constexpr int PF = 2;
-        Tile<T, CT, D, typename Cf::LKL> tk[PF];
-        Tile<T, CT, BV, typename Cf::LVL> tv[PF];
+        Tile<T, CT, D, typename Cf::LKL, kThreads, In> tk[PF];
+        Tile<T, CT, BV, typename Cf::LVL, kThreads, In> tv[PF];
 #pragma unroll
         for (int u = 0; u < PF; ++u) {
             tk[u].init(dk, dk, tid);
@@ -511,8 +512,8 @@ __global__ __launch_bounds__(kThreads) void k_segment_states(
         }
     } else {
         for (int64_t c = c0; c < c1; ++c) {
-            Tile<T, CT, D, typename Cf::LKL>::load_scalar(Kb + c * C * dk, dk, rows_of(c), dk, Ks, tid);
-            Tile<T, CT, BV, typename Cf::LVL>::load_scalar(Vb + c * C * dv, dv, rows_of(c), nv, Vs, tid);
+            Tile<T, CT, D, typename Cf::LKL, kThreads, In>::load_scalar(Kb + c * C * dk, dk, rows_of(c), dk, Ks, tid);
+            Tile<T, CT, BV, typename Cf::LVL, kThreads, In>::load_scalar(Vb + c * C * dv, dv, rows_of(c), nv, Vs, tid);
             __syncthreads();
             Fr Vf[Cf::NVW][Cf::NTS];
             load_vfrags<Cf>(Vf, Vs, w, g, lane);
@@ -611,11 +612,12 @@ __device__ __forceinline__ void store_out(float* Ob, const f32x4 (&Oacc)[Cf::NT]
     }
 }
 
-template <typename T, int CT, int D, int BV, bool VEC>
+template <typename In, int CT, int D, int BV, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_chunk_walk(
-    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const In* __restrict__ Q, const In* __restrict__ K, const In* __restrict__ V,
     float* __restrict__ S, float* __restrict__ O, const float* __restrict__ ws, int64_t T_len,
     int dk, int dv, int C, int64_t G, int64_t n_seg, int n_vb, int group) {
+    using T = typename Compute<In>::type;
     using Cf = WalkCfg<T, CT, D, BV>;
     using Fr = typename Cf::Fr;
     __shared__ __attribute__((aligned(16))) unsigned char smem[Cf::WALK_BYTES];
@@ -640,9 +642,9 @@ __global__ __launch_bounds__(kThreads) void k_chunk_walk(
     const int64_t c0 = seg * G, c1 = min(n_c, c0 + G);
     const bool last_seg = seg == n_seg - 1;
     const int64_t dkdv = (int64_t)dk * dv;
-    const T* Qb = Q + bq * T_len * dk;
-    const T* Kb = K + bh * T_len * dk;
-    const T* Vb = V + bh * T_len * dv + v0;
+    const In* Qb = Q + bq * T_len * dk;
+    const In* Kb = K + bh * T_len * dk;
+    const In* Vb = V + bh * T_len * dv + v0;
     float* Ob = O + bq * T_len * dv + v0;
 
     // Incoming state of this segment, columns [v0, v0 + nv).
@@ -653,9 +655,12 @@ __global__ __launch_bounds__(kThreads) void k_chunk_walk(
     state_lds_to_regs<Cf>(Sacc, Sst, w, g, c16);
     __syncthreads();  // the state area is reused by the tiles
 
-    Tile<T, CT, D, typename Cf::LQL> tq;
-    Tile<T, CT, D, typename Cf::LKL> tk;
-    Tile<T, CT, BV, typename Cf::LVL> tv;
+    using TQ = Tile<T, CT, D, typename Cf::LQL, kThreads, In>;
+    using TK = Tile<T, CT, D, typename Cf::LKL, kThreads, In>;
+    using TV = Tile<T, CT, BV, typename Cf::LVL, kThreads, In>;
+    TQ tq;
+    TK tk;
+    TV tv;
     auto rows_of = [&](int64_t c) { return (int)min((int64_t)C, T_len - c * C); };
     if constexpr (VEC) {
         tq.init(dk, dk, tid);
@@ -681,9 +686,9 @@ __global__ __launch_bounds__(kThreads) void k_chunk_walk(
             tk.scatter(Ks, tid);
             tv.scatter(Vs, tid);
         } else {
-            Tile<T, CT, D, typename Cf::LQL>::load_scalar(Qb + t0 * dk, dk, nrows, dk, Qs, tid);
-            Tile<T, CT, D, typename Cf::LKL>::load_scalar(Kb + t0 * dk, dk, nrows, dk, Ks, tid);
-            Tile<T, CT, BV, typename Cf::LVL>::load_scalar(Vb + t0 * dv, dv, nrows, nv, Vs, tid);
+            TQ::load_scalar(Qb + t0 * dk, dk, nrows, dk, Qs, tid);
+            TK::load_scalar(Kb + t0 * dk, dk, nrows, dk, Ks, tid);
+            TV::load_scalar(Vb + t0 * dv, dv, nrows, nv, Vs, tid);
         }
         __syncthreads();
         if (c > c0) store_out<Cf, VEC>(Ob, Oacc, t_prev, n_prev, nv, dv, w, g, c16);
@@ -722,7 +727,8 @@ __global__ __launch_bounds__(kThreads) void k_chunk_walk(
 }
 
 // ---------------------------------------------------------------------------
-// Phase 3, wide form for d = 128 bf16 inputs and chunks of up to 64 tokens:
+// Phase 3, wide form for d = 128 bf16 (or FP8, staged as bf16) inputs and
+// chunks of up to 64 tokens:
 // one workgroup of eight waves per (b,h) and segment covers all 128 value
 // columns (wave w owns value tile w), so the score triangle is computed and
 // the Q, K tiles are loaded once per chunk.  Q, K, V are double buffered in
@@ -738,9 +744,9 @@ struct WideCfg : WalkCfg<bf16, CT, 128, 128, 8> {
     static constexpr int BYTES = TILE_BYTES > Base::STATE_BYTES ? TILE_BYTES : Base::STATE_BYTES;
 };
 
-template <int CT>
+template <int CT, typename In>
 __global__ __launch_bounds__(512) void k_chunk_walk_wide(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const In* __restrict__ Q, const In* __restrict__ K, const In* __restrict__ V,
     float* __restrict__ S, float* __restrict__ O, const float* __restrict__ ws, int64_t T_len,
     int dk, int dv, int C, int64_t G, int64_t n_seg, int group) {
     using Cf = WideCfg<CT>;
@@ -761,9 +767,9 @@ __global__ __launch_bounds__(512) void k_chunk_walk_wide(
     const int64_t c0 = seg * G, c1 = min(n_c, c0 + G);
     const bool last_seg = seg == n_seg - 1;
     const int64_t dkdv = (int64_t)dk * dv;
-    const bf16* Qb = Q + bq * T_len * dk;
-    const bf16* Kb = K + bh * T_len * dk;
-    const bf16* Vb = V + bh * T_len * dv;
+    const In* Qb = Q + bq * T_len * dk;
+    const In* Kb = K + bh * T_len * dk;
+    const In* Vb = V + bh * T_len * dv;
     float* Ob = O + bq * T_len * dv;
     auto rows_of = [&](int64_t c) { return c < c1 ? (int)min((int64_t)C, T_len - c * C) : 0; };
 
@@ -771,9 +777,9 @@ __global__ __launch_bounds__(512) void k_chunk_walk_wide(
     const float* Sin = ws == nullptr ? S + bh * dkdv : ws + (bh * n_seg + seg) * dkdv;
     StateStage<Cf> ss;
     ss.load(Sin, dk, dv, dv, tid);
-    Tile<bf16, CT, 128, typename Cf::LQL, NTH> tq;
-    Tile<bf16, CT, 128, typename Cf::LKL, NTH> tk;
-    Tile<bf16, CT, 128, typename Cf::LVL, NTH> tv;
+    Tile<bf16, CT, 128, typename Cf::LQL, NTH, In> tq;
+    Tile<bf16, CT, 128, typename Cf::LKL, NTH, In> tk;
+    Tile<bf16, CT, 128, typename Cf::LVL, NTH, In> tv;
     tq.init(dk, dk, tid);
     tk.init(dk, dk, tid);
     tv.init(dv, dv, tid);
@@ -858,7 +864,7 @@ __global__ __launch_bounds__(512) void k_chunk_walk_wide(
 }
 
 // ---------------------------------------------------------------------------
-// Phase 1, wide form for d = 128 bf16 inputs and chunks of up to 64 tokens:
+// Phase 1, wide form for d = 128 bf16 (or FP8) inputs and chunks of up to 64 tokens:
 // one workgroup of eight waves per (b,h) and segment (all but the last)
 // covers all 128 value columns, so K is loaded once.  The K, V tiles are
 // double buffered: chunk c + 1 is written into the free buffer while chunk
@@ -874,9 +880,9 @@ struct SegWideCfg : WalkCfg<bf16, CT, 128, 128, 8> {
     static constexpr int BYTES = TILE_BYTES > Base::STATE_BYTES ? TILE_BYTES : Base::STATE_BYTES;
 };
 
-template <int CT>
-__global__ __launch_bounds__(512) void k_segment_states_wide(const bf16* __restrict__ K,
-                                                             const bf16* __restrict__ V,
+template <int CT, typename In>
+__global__ __launch_bounds__(512) void k_segment_states_wide(const In* __restrict__ K,
+                                                             const In* __restrict__ V,
                                                              float* __restrict__ ws, int64_t T_len,
                                                              int dk, int dv, int C, int64_t G,
                                                              int64_t n_seg) {
@@ -893,8 +899,8 @@ __global__ __launch_bounds__(512) void k_segment_states_wide(const bf16* __restr
     const int64_t bh = blockIdx.x / nsm1, seg = blockIdx.x - bh * nsm1;
     const int64_t n_c = (T_len + C - 1) / C;
     const int64_t c0 = seg * G, c1 = min(n_c, c0 + G);
-    const bf16* Kb = K + bh * T_len * dk;
-    const bf16* Vb = V + bh * T_len * dv;
+    const In* Kb = K + bh * T_len * dk;
+    const In* Vb = V + bh * T_len * dv;
     auto rows_of = [&](int64_t c) { return c < c1 ? (int)min((int64_t)C, T_len - c * C) : 0; };
 
     f32x4 Sacc[Cf::NVW][Cf::NDT];
@@ -906,8 +912,9 @@ __global__ __launch_bounds__(512) void k_segment_states_wide(const bf16* __restr
     // is reduced, PF - 1 chunks ahead of their use.  Deeper rings measured
     // slower (more registers, two workgroups per CU either way).
     constexpr int PF = 2;
-    Tile<bf16, CT, 128, typename Cf::LKL, NTH> tk[PF];
-    Tile<bf16, CT, 128, typename Cf::LVL, NTH> tv[PF];
+    using TK = Tile<bf16, CT, 128, typename Cf::LKL, NTH, In>;
+    TK tk[PF];
+    Tile<bf16, CT, 128, typename Cf::LVL, NTH, In> tv[PF];
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
         tk[u].init(dk, dk, tid);
@@ -946,7 +953,7 @@ __global__ __launch_bounds__(512) void k_segment_states_wide(const bf16* __restr
                 for (int ts = 0; ts < Cf::NTS; ++ts)
                     Sacc[0][dt] = mma(lds_col(Ks, Cf::LK, 32 * ts, 16 * dt, lane), Vf[0][ts], Sacc[0][dt]);
 #pragma unroll
-                for (int n = 0; n < Tile<bf16, CT, 128, typename Cf::LKL, NTH>::NPT; ++n) {
+                for (int n = 0; n < TK::NPT; ++n) {
                     if (dt == 1) tk[u].load(rk, n);
                     if (dt == 3) tv[u].load(rv, n);
                 }
@@ -984,17 +991,20 @@ void plan_prefill(PrefillPlan& p) {
     // several segments, or several query heads per state (the group's walks
     // must not read S while one of them writes S_T)
     p.use_ws = p.n_seg > 1 || p.group > 1;
-    const int ve = p.dtype == LLA_BF16 ? 8 : 4;
+    const int ve = p.dtype == LLA_FP8_E4M3 ? 16 : (p.dtype == LLA_BF16 ? 8 : 4);  // per 16 bytes
     p.vec = (p.dk % ve == 0) && (p.dv % ve == 0);
 }
 
-template <typename T, int CT, int D>
+// In: the input element type (bf16, FP8 or fp32); the matrix cores run on
+// Compute<In>::type.
+template <typename In, int CT, int D>
 static hipError_t launch_walk_t(const PrefillPlan& p, const void* Q, const void* K, const void* V,
                                 float* S, float* O, float* ws, hipStream_t st) {
+    using T = typename Compute<In>::type;
     if constexpr (std::is_same<T, bf16>::value && D == 128 && CT <= 64) {
         if (p.vec) {  // one eight-wave workgroup per (b,h) and segment
-            hipLaunchKernelGGL((k_chunk_walk_wide<CT>), dim3((unsigned)(p.BHq * p.n_seg)), dim3(512), 0, st,
-                               (const bf16*)Q, (const bf16*)K, (const bf16*)V, S, O,
+            hipLaunchKernelGGL((k_chunk_walk_wide<CT, In>), dim3((unsigned)(p.BHq * p.n_seg)), dim3(512), 0, st,
+                               (const In*)Q, (const In*)K, (const In*)V, S, O,
                                (const float*)(p.use_ws ? ws : nullptr), p.T, p.dk, p.dv, p.C, p.G,
                                p.n_seg, p.group);
             return hipGetLastError();
@@ -1004,23 +1014,24 @@ static hipError_t launch_walk_t(const PrefillPlan& p, const void* Q, const void*
     const int64_t grid = p.BHq * p.n_seg * p.n_vb;
     const float* wsr = p.use_ws ? ws : nullptr;
     if (p.vec)
-        hipLaunchKernelGGL((k_chunk_walk<T, CT, D, BV, true>), dim3((unsigned)grid), dim3(kThreads), 0,
-                           st, (const T*)Q, (const T*)K, (const T*)V, S, O, wsr, p.T,
+        hipLaunchKernelGGL((k_chunk_walk<In, CT, D, BV, true>), dim3((unsigned)grid), dim3(kThreads), 0,
+                           st, (const In*)Q, (const In*)K, (const In*)V, S, O, wsr, p.T,
                            p.dk, p.dv, p.C, p.G, p.n_seg, p.n_vb, p.group);
     else
-        hipLaunchKernelGGL((k_chunk_walk<T, CT, D, BV, false>), dim3((unsigned)grid), dim3(kThreads), 0,
-                           st, (const T*)Q, (const T*)K, (const T*)V, S, O, wsr, p.T,
+        hipLaunchKernelGGL((k_chunk_walk<In, CT, D, BV, false>), dim3((unsigned)grid), dim3(kThreads), 0,
+                           st, (const In*)Q, (const In*)K, (const In*)V, S, O, wsr, p.T,
                            p.dk, p.dv, p.C, p.G, p.n_seg, p.n_vb, p.group);
     return hipGetLastError();
 }
 
-template <typename T, int CT, int D>
+template <typename In, int CT, int D>
 static hipError_t launch_seg_t(const PrefillPlan& p, const void* K, const void* V, float* ws,
                                hipStream_t st) {
+    using T = typename Compute<In>::type;
     if constexpr (std::is_same<T, bf16>::value && D == 128 && CT <= 64) {
         if (p.vec) {  // one eight-wave workgroup per (b,h) and segment
-            hipLaunchKernelGGL((k_segment_states_wide<CT>), dim3((unsigned)(p.BH * (p.n_seg - 1))),
-                               dim3(512), 0, st, (const bf16*)K, (const bf16*)V, ws, p.T, p.dk, p.dv,
+            hipLaunchKernelGGL((k_segment_states_wide<CT, In>), dim3((unsigned)(p.BH * (p.n_seg - 1))),
+                               dim3(512), 0, st, (const In*)K, (const In*)V, ws, p.T, p.dk, p.dv,
                                p.C, p.G, p.n_seg);
             return hipGetLastError();
         }
@@ -1028,20 +1039,34 @@ static hipError_t launch_seg_t(const PrefillPlan& p, const void* K, const void* 
     constexpr int BV = D > 64 ? 64 : D;
     const int64_t grid = p.BH * (p.n_seg - 1) * p.n_vb;
     if (p.vec)
-        hipLaunchKernelGGL((k_segment_states<T, CT, D, BV, true>), dim3((unsigned)grid), dim3(kThreads),
-                           0, st, (const T*)K, (const T*)V, ws, p.T, p.dk, p.dv, p.C, p.G, p.n_seg,
+        hipLaunchKernelGGL((k_segment_states<In, CT, D, BV, true>), dim3((unsigned)grid), dim3(kThreads),
+                           0, st, (const In*)K, (const In*)V, ws, p.T, p.dk, p.dv, p.C, p.G, p.n_seg,
                            p.n_vb);
     else
-        hipLaunchKernelGGL((k_segment_states<T, CT, D, BV, false>), dim3((unsigned)grid), dim3(kThreads),
-                           0, st, (const T*)K, (const T*)V, ws, p.T, p.dk, p.dv, p.C, p.G, p.n_seg,
+        hipLaunchKernelGGL((k_segment_states<In, CT, D, BV, false>), dim3((unsigned)grid), dim3(kThreads),
+                           0, st, (const In*)K, (const In*)V, ws, p.T, p.dk, p.dv, p.C, p.G, p.n_seg,
                            p.n_vb);
     return hipGetLastError();
 }
 
-// Calls FN<T, CT, D>(args...) for the plan's padded sizes.
+// Calls FN<In, CT, D>(args...) for the plan's input type and padded sizes.
 #define LLA_DISPATCH(FN, ...)                                                              \
     do {                                                                                   \
-        if (p.dtype == LLA_BF16) {                                                         \
+        if (p.dtype == LLA_FP8_E4M3) {                                                     \
+            if (p.CT == 32) {                                                              \
+                if (p.D == 32) return FN<fp8e4m3, 32, 32>(__VA_ARGS__);                    \
+                if (p.D == 64) return FN<fp8e4m3, 32, 64>(__VA_ARGS__);                    \
+                return FN<fp8e4m3, 32, 128>(__VA_ARGS__);                                  \
+            } else if (p.CT == 64) {                                                       \
+                if (p.D == 32) return FN<fp8e4m3, 64, 32>(__VA_ARGS__);                    \
+                if (p.D == 64) return FN<fp8e4m3, 64, 64>(__VA_ARGS__);                    \
+                return FN<fp8e4m3, 64, 128>(__VA_ARGS__);                                  \
+            } else {                                                                       \
+                if (p.D == 32) return FN<fp8e4m3, 128, 32>(__VA_ARGS__);                   \
+                if (p.D == 64) return FN<fp8e4m3, 128, 64>(__VA_ARGS__);                   \
+                return FN<fp8e4m3, 128, 128>(__VA_ARGS__);                                 \
+            }                                                                              \
+        } else if (p.dtype == LLA_BF16) {                                                  \
             if (p.CT == 32) {                                                              \
                 if (p.D == 32) return FN<bf16, 32, 32>(__VA_ARGS__);                       \
                 if (p.D == 64) return FN<bf16, 32, 64>(__VA_ARGS__);                       \

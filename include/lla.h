@@ -21,7 +21,7 @@
  * Conventions for every call
  * --------------------------
  * Layouts (dense, row-major, no strides):
- *   Q, K : [B][H][T][dk]      V : [B][H][T][dv]      (dtype: bf16 or fp32)
+ *   Q, K : [B][H][T][dk]      V : [B][H][T][dv]      (dtype: bf16, fp32 or FP8)
  *   O    : [B][H][T][dv]      fp32 output
  *   S    : [B][H][dk][dv]     fp32 recurrent state, row i = key dimension i
  *   decode: q, k : [B][H][dk]   v : [B][H][dv]   o : [B][H][dv] fp32
@@ -33,8 +33,8 @@
  * enqueues work on that stream and returns without synchronising; results
  * are valid once the stream has been synchronised.
  * Limits: B, H >= 1; T >= 0 (T = 0 is a no-op that leaves S untouched);
- * 1 <= dk, dv <= 128; 1 <= C <= 128 for bf16 inputs, 1 <= C <= 64 for fp32
- * inputs; B*H*T*max(dk,dv) < 2^62.  C need not divide T: the last chunk of a
+ * 1 <= dk, dv <= 128; 1 <= C <= 128 for bf16 and FP8 inputs, 1 <= C <= 64 for
+ * fp32 inputs; B*H*T*max(dk,dv) < 2^62.  C need not divide T: the last chunk of a
  * sequence is shorter.
  * Errors: arguments are checked on the host before anything is enqueued; on
  * any error no buffer is touched and a status other than LLA_OK is returned.
@@ -45,7 +45,17 @@
  * accumulation; the fp32 state enters Q_c S_c as a sum of two bf16 parts
  * (high and low), so integer-valued inputs whose partial sums stay below
  * 2^16 in the state and 2^24 elsewhere give exact results.  fp32 inputs use
- * fp32 matrix-core instructions throughout.
+ * fp32 matrix-core instructions throughout.  FP8 inputs (the 8-bit format
+ * that the blog "A 128 000 tokens, l'attention avale 85 % du calcul" says the
+ * attention measurements it reports use, for the arithmetic and the cache
+ * alike) are the OCP E4M3 format: 1 sign, 4 exponent (bias 7) and 3
+ * mantissa bits, subnormals, no infinities, NaN = S.1111.111 (torch's
+ * float8_e4m3fn).  Every E4M3 value is exactly a bf16 value, so they are
+ * decoded to bf16 on their way into LDS and take the bf16 path with the same
+ * results as those values given in bf16.  No scale factor is applied: the
+ * method is linear in each of q, k and v, so per-tensor scales s_q, s_k, s_v
+ * fold into the outputs (O and the state's increment scale by s_q s_k s_v
+ * and s_k s_v) and stay with the caller.  The state and O stay fp32.
  */
 #ifndef LLA_H
 #define LLA_H
@@ -70,8 +80,9 @@ typedef enum {
 } lla_status;
 
 typedef enum {
-    LLA_BF16 = 0, /* bfloat16 Q/K/V (q/k/v) */
-    LLA_F32 = 1   /* float32 Q/K/V (q/k/v) */
+    LLA_BF16 = 0,    /* bfloat16 Q/K/V (q/k/v) */
+    LLA_F32 = 1,     /* float32 Q/K/V (q/k/v) */
+    LLA_FP8_E4M3 = 2 /* OCP FP8 E4M3 Q/K/V (q/k/v), one byte per element */
 } lla_dtype;
 
 /* Short, static, human-readable name of a status code. */

@@ -349,3 +349,46 @@ def test_grouped_rejects_bad_head_counts():
         oracle.grouped_recurrence(z((1, 5, 2, 3)), z((1, 2, 2, 3)), z((1, 2, 2, 3)))
     with pytest.raises(ValueError):
         oracle.grouped_decode_step(z((1, 2, 3)), z((1, 4, 3)), z((1, 4, 3)), z((1, 4, 3, 3)))
+
+
+# --- FP8 (E4M3) inputs: the oracle's decoder ---------------------------------------
+
+def test_e4m3_decoder_special_codes():
+    """Values the OCP E4M3 definition fixes: 1.0, -2.0, the largest finite value
+    448, the smallest normal 2^-6, the smallest subnormal 2^-9, the largest
+    subnormal 7/8 * 2^-6, signed zeros and the two NaN codes."""
+    d = oracle.decode_e4m3(np.arange(256))
+    assert d[0x38] == 1.0 and d[0xC0] == -2.0
+    assert d[0x7E] == 448.0 and d[0xFE] == -448.0
+    assert d[0x08] == 2.0 ** -6 and d[0x01] == 2.0 ** -9 and d[0x07] == 7 / 8 * 2.0 ** -6
+    assert d[0x00] == 0.0 and not np.signbit(d[0x00]) and d[0x80] == 0.0 and np.signbit(d[0x80])
+    assert np.isnan(d[0x7F]) and np.isnan(d[0xFF]) and np.isnan(d).sum() == 2
+    assert np.all(np.diff(d[:0x7F]) > 0)  # positive codes are ordered
+    assert np.array_equal(d[0x80:0xFF], -d[:0x7F])
+
+
+def test_e4m3_decoder_matches_torch_and_fits_bf16():
+    """Every code decodes as torch's float8_e4m3fn does, and every finite value
+    is exactly a bf16 value (so FP8 inputs may be staged as bf16)."""
+    codes = torch.arange(256, dtype=torch.uint8)
+    d = oracle.decode_e4m3(codes.numpy())
+    ref = codes.view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(d, ref, equal_nan=True)
+    fin = d[np.isfinite(d)]
+    assert np.array_equal(torch.tensor(fin).to(torch.bfloat16).double().numpy(), fin)
+    # FP8 tensors enter the oracle through the same decoder
+    t = torch.randn(2, 3, 7).to(torch.float8_e4m3fn)
+    O, _ = oracle.recurrence(t, t, t)
+    tb = t.to(torch.bfloat16)
+    O_b, _ = oracle.recurrence(tb, tb, tb)
+    assert np.array_equal(O, O_b)
+
+
+def test_e4m3_wrong_bias_is_caught():
+    """Planted: an exponent bias of 8 (the other 8-bit E4M3 variant) fails the
+    fixed values above."""
+    b = np.arange(256)
+    e = (b >> 3) & 0xF
+    m = b & 7
+    wrong = np.where(e == 0, m / 8 * 2.0 ** -7, (1 + m / 8) * np.exp2(e - 8.0))
+    assert wrong[0x38] != 1.0 and oracle.decode_e4m3(b)[0x38] == 1.0

@@ -55,7 +55,8 @@ class Config:
 
 # c1: the deck's toy; c2..c4: prefill shapes; c5: decode after a T=4096 prefill;
 # g3, g5: the T=8192 prefill and the decode batch with four query heads per
-# key/value head (shared-state heads, as in grouped-query attention).
+# key/value head (shared-state heads, as in grouped-query attention);
+# f3, f5: the T=8192 prefill and the decode batch with FP8 (E4M3) inputs.
 CONFIGS = {
     "c1": Config("toy", 1, 1, 8, 4, 2, 2, torch.float32, seed_base=10,
                  note="variant 0 = the deck's trace, variants 1..100 uniform {0,1}"),
@@ -71,6 +72,12 @@ CONFIGS = {
                  torch.bfloat16, scale=128 ** -0.5, l2norm_k=True, seed_base=60, Hkv=4),
     "g5": Config("decode_B256_Hq32_Hkv8_d128", 256, 32, 1, 64, 128, 128,
                  torch.bfloat16, scale=128 ** -0.5, seed_base=70, decode_steps=512, Hkv=8,
+                 note="state drawn N(0,1) (seed 10*config + 6), not from a prefill"),
+    "f3": Config("prefill_B1_H16_T8192_C64_d128_fp8", 1, 16, 8192, 64, 128, 128,
+                 torch.float8_e4m3fn, scale=1.0, seed_base=80,
+                 note="N(0,1) rounded to FP8 E4M3 (unit scale uses the format's range)"),
+    "f5": Config("decode_B256_H32_d128_fp8", 256, 32, 1, 64, 128, 128,
+                 torch.float8_e4m3fn, scale=1.0, seed_base=90, decode_steps=512,
                  note="state drawn N(0,1) (seed 10*config + 6), not from a prefill"),
 }
 
