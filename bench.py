@@ -104,7 +104,8 @@ def bench_prefill(args, torch, lla, workloads, profiling):
         ins.append((q, k, v))
     n_sets = len(sets)
 
-    # One step = the fresh-prompt state init (S = 0) + one lla_prefill call.
+    # One step = one fresh-prompt prefill: lla_prefill_ex with the zero-state
+    # option (S_0 = 0 without reading S; S receives S_T).
     def step(i):
         sets[i % n_sets](zero_state=True)
 
@@ -113,9 +114,10 @@ def bench_prefill(args, torch, lla, workloads, profiling):
     wall, gpu = _timed(torch, step, args.steps)
     wall_w, gpu_w = _timed(torch, lambda i: sets[0](zero_state=True), args.steps)
 
-    # Per-phase durations: the same steps with HIP events between the three
-    # phases (what lla_prefill enqueues), on the launch stream.  An interval
-    # between two events also holds the launch gap in front of the kernel.
+    # Per-phase durations: the same work with HIP events between the three
+    # phases (what lla_prefill enqueues; the state is zeroed by lla_state_init
+    # before them), on the launch stream.  An interval between two events
+    # also holds the launch gap in front of the kernel.
     stream = torch.cuda.current_stream(dev)
     evs = []
     torch.cuda.synchronize()
@@ -155,7 +157,8 @@ def bench_prefill(args, torch, lla, workloads, profiling):
         "config": {"workload": cfg.name, "B": B, "H": H, "T": T, "C": C, "dk": d, "dv": d,
                    "inputs": "bf16 N(0,1)/sqrt(128), K rows L2-normalised; fp32 state and output",
                    "cache": "cold: %d rotating input/output sets of %.0f MB" % (n_sets, nbytes / 1e6),
-                   "step": "state init (S=0) + lla_prefill (per-segment K^T V, segment scan, chunk walk)"},
+                   "step": "one fresh-prompt lla_prefill_ex (S_0 = 0): per-segment K^T V, "
+                           "segment scan, chunk walk"},
         "value": B * T / (ms_step * 1e-3),
         "ms_per_step": ms_step,
         "gpu_ms_per_step": gpu * 1e3 / args.steps,
@@ -295,7 +298,7 @@ def bench_grouped(args, torch, lla, workloads, profiling):
            "mfma_frac": flops / step_s / (PEAK_BF16_TFLOPS * 1e12),
            "hbm_frac": nbytes / step_s / (PEAK_HBM_GBS * 1e9),
            "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
-           "timing": "HIP events around the timed steps (state init + lla_prefill_gqa), "
+           "timing": "HIP events around the timed steps (fresh-prompt lla_prefill_ex), "
                      "%d rotating input sets" % len(sets)}
     del sets, q0, k0, v0
     torch.cuda.empty_cache()
@@ -360,7 +363,7 @@ def bench_fp8(args, torch, lla, workloads, profiling):
                         "unit": "GB/s", "frac": nbytes / (walk_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                         "traffic": None, "algorithmic_bytes": nbytes, "kernel_ms": walk_ms,
                         "timing": "HIP events around %d back-to-back walk launches" % n_walk},
-           "timing": "HIP events around the timed steps (state init + lla_prefill), "
+           "timing": "HIP events around the timed steps (fresh-prompt lla_prefill_ex), "
                      "%d rotating input sets" % len(sets)}
     del sets, q0, k0, v0
     torch.cuda.empty_cache()

@@ -34,7 +34,8 @@ EXPORTS = ("lla_status_string", "lla_last_device_error", "lla_state_init",
            "lla_prefill_segment_chunks", "lla_prefill_workspace_size", "lla_prefill",
            "lla_prefill_segment_states", "lla_prefill_state_scan", "lla_prefill_chunks",
            "lla_decode_step", "lla_prefill_gqa_workspace_size", "lla_prefill_gqa",
-           "lla_decode_step_gqa")
+           "lla_decode_step_gqa", "lla_prefill_ex")
+PREFILL_ZERO_STATE = 1  # lla_prefill_ex: start from S_0 = 0 without reading S
 
 _BF16, _F32, _FP8 = 0, 1, 2
 _lib = None
@@ -88,6 +89,9 @@ def library():
         lib.lla_prefill_gqa.restype = st
         lib.lla_decode_step_gqa.argtypes = [vp, vp, vp, ci, i64, i64, i64, i64, i64, vp, vp, vp]
         lib.lla_decode_step_gqa.restype = st
+        lib.lla_prefill_ex.argtypes = [vp, vp, vp, ci, i64, i64, i64, i64, i64, i64, i64,
+                                       ctypes.c_uint, vp, vp, vp, sz, vp]
+        lib.lla_prefill_ex.restype = st
         _lib = lib
     return _lib
 
@@ -200,16 +204,21 @@ def _out(out, shape, device):
     return out
 
 
-def prefill(q, k, v, state, chunk: int, out=None, workspace=None):
+def prefill(q, k, v, state, chunk: int, out=None, workspace=None, zero_state: bool = False):
     """Chunkwise prefill: returns o [B,Hq,T,dv] fp32; ``state`` [B,Hkv,dk,dv] goes
     S_0 -> S_T in place.  k, v with fewer heads than q (Hq a multiple of Hkv)
-    select shared-state heads (lla_prefill_gqa)."""
+    select shared-state heads (lla_prefill_gqa).  ``zero_state``: a fresh
+    prompt -- start from S_0 = 0 without reading ``state`` (lla_prefill_ex)."""
     lib = library()
     B, Hq, Hkv, T, dk, dv = _qkv_shape(q, k, v)
     _state_check(state, B, Hkv, dk, dv)
     out = _out(out, (B, Hq, T, dv), q.device)
     ws, ws_bytes = _workspace(B, Hq, T, dk, dv, chunk, q.device, workspace, Hkv)
-    if Hq == Hkv:
+    if zero_state:
+        _check(lib.lla_prefill_ex(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, Hq, Hkv, T, dk, dv,
+                                  chunk, PREFILL_ZERO_STATE, _ptr(state), _ptr(out), _ptr(ws),
+                                  ws_bytes, _stream(q)), "lla_prefill_ex")
+    elif Hq == Hkv:
         _check(lib.lla_prefill(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, Hq, T, dk, dv, chunk,
                                _ptr(state), _ptr(out), _ptr(ws), ws_bytes, _stream(q)), "lla_prefill")
     else:
@@ -299,9 +308,10 @@ class PreparedPrefill:
     """A prefill whose arguments were checked and marshalled once.
 
     For loops that call the same prefill on the same buffers many times (the
-    benchmark, a serving loop): calling the object only re-zeroes the state
-    (optional) and calls lla_prefill with the stored pointers on the current
-    stream.  The tensors must stay alive and keep their shapes.
+    benchmark, a serving loop): calling the object calls lla_prefill (or, for
+    a fresh prompt, lla_prefill_ex with PREFILL_ZERO_STATE) with the stored
+    pointers on the current stream.  The tensors must stay alive and keep
+    their shapes.
     """
 
     def __init__(self, q, k, v, state, chunk, out=None, workspace=None):
@@ -323,6 +333,8 @@ class PreparedPrefill:
             self._fn = lib.lla_prefill
             self._args = (_ptr(q), _ptr(k), _ptr(v), dt, B, H, T, dk, dv, chunk,
                           _ptr(state), _ptr(self.out), ws, ws_bytes)
+        self._fresh_args = (_ptr(q), _ptr(k), _ptr(v), dt, B, H, Hkv, T, dk, dv, chunk,
+                            PREFILL_ZERO_STATE, _ptr(state), _ptr(self.out), ws, ws_bytes)
         self._init_args = (_ptr(state), B, Hkv, dk, dv)
         self._seg_args = (_ptr(k), _ptr(v), dt, B, H, T, dk, dv, chunk, ws, ws_bytes)
         self._scan_args = (_ptr(state), B, H, T, dk, dv, chunk, ws, ws_bytes)
@@ -332,10 +344,13 @@ class PreparedPrefill:
         return torch.cuda.current_stream(self._device).cuda_stream
 
     def __call__(self, zero_state: bool = False):
+        """One prefill; ``zero_state``: a fresh prompt (S_0 = 0, the state is
+        not read)."""
         st = self._stream()
         if zero_state:
-            _check(self._init(*self._init_args, st), "lla_state_init")
-        _check(self._fn(*self._args, st), self._fn.__name__)
+            _check(self._lib.lla_prefill_ex(*self._fresh_args, st), "lla_prefill_ex")
+        else:
+            _check(self._fn(*self._args, st), self._fn.__name__)
         return self.out
 
     # The three phases of the call, one by one (for per-kernel timing; one

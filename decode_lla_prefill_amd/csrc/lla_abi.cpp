@@ -226,15 +226,20 @@ lla_status lla_prefill_chunks(const void* Q, const void* K, const void* V, lla_d
 namespace {
 
 lla_status prefill_impl(const void* Q, const void* K, const void* V, lla_dtype dtype, int64_t B,
-                        Heads h, int64_t T, int64_t dk, int64_t dv, int64_t C, float* S, float* O,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+                        Heads h, int64_t T, int64_t dk, int64_t dv, int64_t C, unsigned flags,
+                        float* S, float* O, void* workspace, size_t workspace_bytes, void* stream) {
+    if (flags & ~(unsigned)LLA_PREFILL_ZERO_STATE) return LLA_ERR_UNSUPPORTED;
+    const bool zero = (flags & LLA_PREFILL_ZERO_STATE) != 0;
     lla::PrefillPlan p;
     PrefillBufs b{Q, K, V, nullptr, S, O, workspace, workspace_bytes};
     lla_status st = check_prefill(b, true, true, true, true, true, dtype, B, h, T, dk, dv, C, p);
-    if (st != LLA_OK || T == 0) return st;
+    if (st != LLA_OK) return st;
     hipStream_t s = (hipStream_t)stream;
+    if (T == 0)  // S_T = S_0: untouched, or zero for a fresh prompt
+        return zero ? device_status(lla::launch_fill_zero(S, p.BH * dk * dv, s)) : LLA_OK;
+    p.zero_start = zero;
     if (p.group == 1 && lla::decode_tokens_fit(T, (int)dk, (int)dv))  // a short prompt: fused decode steps
-        return device_status(lla::launch_decode_tokens(dtype, Q, K, V, p.BH, (int)T, (int)dk, S, O, s));
+        return device_status(lla::launch_decode_tokens(dtype, Q, K, V, p.BH, (int)T, (int)dk, S, O, zero, s));
     float* ws = (float*)workspace;
     st = device_status(lla::launch_segment_states(p, K, V, ws, s));
     if (st != LLA_OK) return st;
@@ -274,14 +279,22 @@ extern "C" {
 lla_status lla_prefill(const void* Q, const void* K, const void* V, lla_dtype dtype, int64_t B,
                        int64_t H, int64_t T, int64_t dk, int64_t dv, int64_t C, float* S, float* O,
                        void* workspace, size_t workspace_bytes, void* stream) {
-    return prefill_impl(Q, K, V, dtype, B, Heads{H, H}, T, dk, dv, C, S, O, workspace,
+    return prefill_impl(Q, K, V, dtype, B, Heads{H, H}, T, dk, dv, C, 0u, S, O, workspace,
                         workspace_bytes, stream);
 }
 
 lla_status lla_prefill_gqa(const void* Q, const void* K, const void* V, lla_dtype dtype, int64_t B,
                            int64_t Hq, int64_t Hkv, int64_t T, int64_t dk, int64_t dv, int64_t C,
                            float* S, float* O, void* workspace, size_t workspace_bytes, void* stream) {
-    return prefill_impl(Q, K, V, dtype, B, Heads{Hq, Hkv}, T, dk, dv, C, S, O, workspace,
+    return prefill_impl(Q, K, V, dtype, B, Heads{Hq, Hkv}, T, dk, dv, C, 0u, S, O, workspace,
+                        workspace_bytes, stream);
+}
+
+lla_status lla_prefill_ex(const void* Q, const void* K, const void* V, lla_dtype dtype, int64_t B,
+                          int64_t Hq, int64_t Hkv, int64_t T, int64_t dk, int64_t dv, int64_t C,
+                          unsigned flags, float* S, float* O, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    return prefill_impl(Q, K, V, dtype, B, Heads{Hq, Hkv}, T, dk, dv, C, flags, S, O, workspace,
                         workspace_bytes, stream);
 }
 

@@ -159,7 +159,8 @@ __global__ __launch_bounds__(NT) void k_decode_tokens(const Tin* __restrict__ q,
                                                       const Tin* __restrict__ k,
                                                       const Tin* __restrict__ v,
                                                       float* __restrict__ S,
-                                                      float* __restrict__ o, int T) {
+                                                      float* __restrict__ o, int T,
+                                                      int zero_start) {
     constexpr int CG = D / 4, RG = NT / CG, RPT = D / RG;
     static_assert(NT % CG == 0 && D % RG == 0, "thread layout must tile the state");
     __shared__ float qs[TMAX][D], ks[TMAX][D], vs[TMAX][D];
@@ -178,7 +179,8 @@ __global__ __launch_bounds__(NT) void k_decode_tokens(const Tin* __restrict__ q,
     f32x4 x[RPT];
 #pragma unroll
     for (int m = 0; m < RPT; ++m)
-        x[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sb + (rg + m * RG) * D + 4 * cg));
+        x[m] = zero_start ? f32x4{0.f, 0.f, 0.f, 0.f}  // S_0 = 0: S is not read
+                          : __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sb + (rg + m * RG) * D + 4 * cg));
     for (int t = 0; t < T; ++t) {
         const f32x4 vj = {vs[t][4 * cg], vs[t][4 * cg + 1], vs[t][4 * cg + 2], vs[t][4 * cg + 3]};
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -311,21 +313,23 @@ bool decode_tokens_fit(int64_t T, int dk, int dv) {
 
 template <typename Tin>
 static hipError_t tokens_t(const void* q, const void* k, const void* v, int64_t BH, int T, int d,
-                           float* S, float* o, hipStream_t st) {
+                           float* S, float* o, int zero, hipStream_t st) {
     if (d == 128)
         hipLaunchKernelGGL((k_decode_tokens<Tin, 128, 512, kDecodeTokensMax>), dim3((unsigned)BH), dim3(512),
-                           0, st, (const Tin*)q, (const Tin*)k, (const Tin*)v, S, o, T);
+                           0, st, (const Tin*)q, (const Tin*)k, (const Tin*)v, S, o, T, zero);
     else
         hipLaunchKernelGGL((k_decode_tokens<Tin, 64, 256, kDecodeTokensMax>), dim3((unsigned)BH), dim3(256),
-                           0, st, (const Tin*)q, (const Tin*)k, (const Tin*)v, S, o, T);
+                           0, st, (const Tin*)q, (const Tin*)k, (const Tin*)v, S, o, T, zero);
     return hipGetLastError();
 }
 
 hipError_t launch_decode_tokens(lla_dtype dtype, const void* q, const void* k, const void* v,
-                                int64_t BH, int T, int d, float* S, float* o, hipStream_t st) {
-    if (dtype == LLA_FP8_E4M3) return tokens_t<fp8e4m3>(q, k, v, BH, T, d, S, o, st);
-    if (dtype == LLA_BF16) return tokens_t<bf16>(q, k, v, BH, T, d, S, o, st);
-    return tokens_t<float>(q, k, v, BH, T, d, S, o, st);
+                                int64_t BH, int T, int d, float* S, float* o, bool zero_start,
+                                hipStream_t st) {
+    const int z = zero_start ? 1 : 0;
+    if (dtype == LLA_FP8_E4M3) return tokens_t<fp8e4m3>(q, k, v, BH, T, d, S, o, z, st);
+    if (dtype == LLA_BF16) return tokens_t<bf16>(q, k, v, BH, T, d, S, o, z, st);
+    return tokens_t<float>(q, k, v, BH, T, d, S, o, z, st);
 }
 
 bool decode_group_fit(int64_t group, int dk, int dv) {

@@ -35,6 +35,7 @@ struct PrefillPlan {
     int64_t G;    // chunks per segment (walked by one workgroup)
     int64_t n_seg;  // segments per sequence = ceil(n_c / G)
     bool vec;     // 16-byte vector loads possible (dk, dv multiples of one vector)
+    bool zero_start;  // S_0 = 0: S is written (S_T) but not read
     lla_dtype dtype;
 };
 
@@ -56,7 +57,8 @@ hipError_t launch_decode_step(lla_dtype dtype, const void* q, const void* k, con
 constexpr int kDecodeTokensMax = 16;
 bool decode_tokens_fit(int64_t T, int dk, int dv);
 hipError_t launch_decode_tokens(lla_dtype dtype, const void* q, const void* k, const void* v,
-                                int64_t BH, int T, int d, float* S, float* o, hipStream_t st);
+                                int64_t BH, int T, int d, float* S, float* o, bool zero_start,
+                                hipStream_t st);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 
 // Shared-state heads: `group` query heads read each key/value state (dk = dv

@@ -534,21 +534,25 @@ __global__ __launch_bounds__(kThreads) void k_segment_states(
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void k_state_scan(const float* __restrict__ S,
                                                          float* __restrict__ ws, int64_t n_seg,
-                                                         int64_t dkdv, int64_t blocks_per_bh) {
+                                                         int64_t dkdv, int64_t blocks_per_bh,
+                                                         int zero_start) {
     const int64_t bh = blockIdx.x / blocks_per_bh;
     const int64_t e = ((blockIdx.x % blocks_per_bh) * kThreads + threadIdx.x) * 4;
     if (e >= dkdv) return;
     float* slot = ws + bh * n_seg * dkdv + e;
     const float* s0 = S + bh * dkdv + e;
     if (e + 4 <= dkdv && (dkdv & 3) == 0) {
-        f32x4 acc = *reinterpret_cast<const f32x4*>(s0);
-        *reinterpret_cast<f32x4*>(slot) = acc;
+        // S_0 and the first U increments are loaded together (one memory
+        // round trip), then summed in segment order.
         constexpr int U = 16;  // loads in flight per thread (segments per batch)
-        for (int64_t s = 1; s < n_seg; s += U) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (!zero_start) acc = *reinterpret_cast<const f32x4*>(s0);
+        for (int64_t s = 1; s < n_seg || s == 1; s += U) {
             f32x4 x[U];
 #pragma unroll
             for (int u = 0; u < U; ++u)
                 if (s + u < n_seg) x[u] = *reinterpret_cast<const f32x4*>(slot + (s + u) * dkdv);
+            if (s == 1) *reinterpret_cast<f32x4*>(slot) = acc;
 #pragma unroll
             for (int u = 0; u < U; ++u)
                 if (s + u < n_seg) {
@@ -559,7 +563,7 @@ __global__ __launch_bounds__(kThreads) void k_state_scan(const float* __restrict
     } else {
         const int m = (int)min((int64_t)4, dkdv - e);
         for (int j = 0; j < m; ++j) {
-            float acc = s0[j];
+            float acc = zero_start ? 0.0f : s0[j];
             slot[j] = acc;
             for (int64_t s = 1; s < n_seg; ++s) {
                 acc += slot[s * dkdv + j];
@@ -616,7 +620,7 @@ template <typename In, int CT, int D, int BV, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_chunk_walk(
     const In* __restrict__ Q, const In* __restrict__ K, const In* __restrict__ V,
     float* __restrict__ S, float* __restrict__ O, const float* __restrict__ ws, int64_t T_len,
-    int dk, int dv, int C, int64_t G, int64_t n_seg, int n_vb, int group) {
+    int dk, int dv, int C, int64_t G, int64_t n_seg, int n_vb, int group, int zero_start) {
     using T = typename Compute<In>::type;
     using Cf = WalkCfg<T, CT, D, BV>;
     using Fr = typename Cf::Fr;
@@ -648,9 +652,11 @@ __global__ __launch_bounds__(kThreads) void k_chunk_walk(
     float* Ob = O + bq * T_len * dv + v0;
 
     // Incoming state of this segment, columns [v0, v0 + nv).
+    // (zero_start without a workspace: S_0 = 0, S is not read -- columns
+    // past `nv` read as zero)
     const float* Sin = (ws == nullptr ? S + bh * dkdv : ws + (bh * n_seg + seg) * dkdv) + v0;
     f32x4 Sacc[Cf::NVW][Cf::NDT];
-    state_gmem_to_lds<Cf>(Sst, Sin, dk, dv, nv, tid);
+    state_gmem_to_lds<Cf>(Sst, Sin, dk, dv, (ws == nullptr && zero_start) ? 0 : nv, tid);
     __syncthreads();
     state_lds_to_regs<Cf>(Sacc, Sst, w, g, c16);
     __syncthreads();  // the state area is reused by the tiles
@@ -736,19 +742,24 @@ __global__ __launch_bounds__(kThreads) void k_chunk_walk(
 // the other from registers loaded one chunk earlier and the loads of chunk
 // c+2 are issued -- two barriers per chunk, none of them behind a load.
 // ---------------------------------------------------------------------------
+#ifndef LLA_WIDE_WAVES
+#define LLA_WIDE_WAVES 8
+#endif
+constexpr int kWideWaves = LLA_WIDE_WAVES;  // waves of the wide walk (value tiles per wave: 8 / waves)
+
 template <int CT>
-struct WideCfg : WalkCfg<bf16, CT, 128, 128, 8> {
-    using Base = WalkCfg<bf16, CT, 128, 128, 8>;
+struct WideCfg : WalkCfg<bf16, CT, 128, 128, kWideWaves> {
+    using Base = WalkCfg<bf16, CT, 128, 128, kWideWaves>;
     static constexpr int BUF = Base::P_OFF;  // elements of one Q, K, V buffer
     static constexpr int TILE_BYTES = (2 * BUF + CT * Base::LP) * 2;
     static constexpr int BYTES = TILE_BYTES > Base::STATE_BYTES ? TILE_BYTES : Base::STATE_BYTES;
 };
 
 template <int CT, typename In>
-__global__ __launch_bounds__(512) void k_chunk_walk_wide(
+__global__ __launch_bounds__(kWideWaves * kWave) void k_chunk_walk_wide(
     const In* __restrict__ Q, const In* __restrict__ K, const In* __restrict__ V,
     float* __restrict__ S, float* __restrict__ O, const float* __restrict__ ws, int64_t T_len,
-    int dk, int dv, int C, int64_t G, int64_t n_seg, int group) {
+    int dk, int dv, int C, int64_t G, int64_t n_seg, int group, int zero_start) {
     using Cf = WideCfg<CT>;
     using Fr = typename Cf::Fr;
     constexpr int NTH = Cf::NTH;
@@ -774,9 +785,10 @@ __global__ __launch_bounds__(512) void k_chunk_walk_wide(
     auto rows_of = [&](int64_t c) { return c < c1 ? (int)min((int64_t)C, T_len - c * C) : 0; };
 
     // Incoming state (loads first), then the first chunk's tile loads.
+    // (zero_start without a workspace: S_0 = 0 -- no column is read)
     const float* Sin = ws == nullptr ? S + bh * dkdv : ws + (bh * n_seg + seg) * dkdv;
     StateStage<Cf> ss;
-    ss.load(Sin, dk, dv, dv, tid);
+    ss.load(Sin, dk, dv, (ws == nullptr && zero_start) ? 0 : dv, tid);
     Tile<bf16, CT, 128, typename Cf::LQL, NTH, In> tq;
     Tile<bf16, CT, 128, typename Cf::LKL, NTH, In> tk;
     Tile<bf16, CT, 128, typename Cf::LVL, NTH, In> tv;
@@ -802,7 +814,9 @@ __global__ __launch_bounds__(512) void k_chunk_walk_wide(
     // A chunk's outputs are stored during the next chunk (see k_chunk_walk).
     f32x4 Oacc[Cf::NT][Cf::NVW];
 #pragma unroll
-    for (int it = 0; it < Cf::NT; ++it) Oacc[it][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < Cf::NT; ++it)
+#pragma unroll
+        for (int vw = 0; vw < Cf::NVW; ++vw) Oacc[it][vw] = f32x4{0.f, 0.f, 0.f, 0.f};
     int64_t t_prev = 0;
     int n_prev = 0;
 
@@ -819,11 +833,14 @@ __global__ __launch_bounds__(512) void k_chunk_walk_wide(
         // the scores, the loads of chunk c + 2 go between the depth steps of
         // the output.
         const rsrc_t rso = make_rsrc(Ob + t_prev * dv, (uint32_t)(n_prev * dv * 4));
-        const int vcol = 16 * w + 4 * g;
         chunk_scores<Cf>(stiles, Qs, Ks, Ps, w, g, c16, [&](int ds) {
             if (ds < Cf::NT) {
-                const uint32_t off = vcol < dv ? (uint32_t)(((16 * ds + c16) * dv + vcol) * 4) : kOutside;
-                buf_store16(rso, off, Oacc[ds][0]);
+#pragma unroll
+                for (int vw = 0; vw < Cf::NVW; ++vw) {
+                    const int vcol = 16 * (w + Cf::NW * vw) + 4 * g;
+                    const uint32_t off = vcol < dv ? (uint32_t)(((16 * ds + c16) * dv + vcol) * 4) : kOutside;
+                    buf_store16(rso, off, Oacc[ds][vw]);
+                }
             }
         });
         // The next chunk into the free buffer (its last readers finished
@@ -1003,10 +1020,10 @@ static hipError_t launch_walk_t(const PrefillPlan& p, const void* Q, const void*
     using T = typename Compute<In>::type;
     if constexpr (std::is_same<T, bf16>::value && D == 128 && CT <= 64) {
         if (p.vec) {  // one eight-wave workgroup per (b,h) and segment
-            hipLaunchKernelGGL((k_chunk_walk_wide<CT, In>), dim3((unsigned)(p.BHq * p.n_seg)), dim3(512), 0, st,
+            hipLaunchKernelGGL((k_chunk_walk_wide<CT, In>), dim3((unsigned)(p.BHq * p.n_seg)), dim3(kWideWaves * kWave), 0, st,
                                (const In*)Q, (const In*)K, (const In*)V, S, O,
                                (const float*)(p.use_ws ? ws : nullptr), p.T, p.dk, p.dv, p.C, p.G,
-                               p.n_seg, p.group);
+                               p.n_seg, p.group, (int)p.zero_start);
             return hipGetLastError();
         }
     }
@@ -1016,11 +1033,11 @@ static hipError_t launch_walk_t(const PrefillPlan& p, const void* Q, const void*
     if (p.vec)
         hipLaunchKernelGGL((k_chunk_walk<In, CT, D, BV, true>), dim3((unsigned)grid), dim3(kThreads), 0,
                            st, (const In*)Q, (const In*)K, (const In*)V, S, O, wsr, p.T,
-                           p.dk, p.dv, p.C, p.G, p.n_seg, p.n_vb, p.group);
+                           p.dk, p.dv, p.C, p.G, p.n_seg, p.n_vb, p.group, (int)p.zero_start);
     else
         hipLaunchKernelGGL((k_chunk_walk<In, CT, D, BV, false>), dim3((unsigned)grid), dim3(kThreads), 0,
                            st, (const In*)Q, (const In*)K, (const In*)V, S, O, wsr, p.T,
-                           p.dk, p.dv, p.C, p.G, p.n_seg, p.n_vb, p.group);
+                           p.dk, p.dv, p.C, p.G, p.n_seg, p.n_vb, p.group, (int)p.zero_start);
     return hipGetLastError();
 }
 
@@ -1111,7 +1128,7 @@ hipError_t launch_state_scan(const PrefillPlan& p, const float* S, float* ws, hi
     const int64_t per_block = (int64_t)kThreads * 4;
     const int64_t blocks_per_bh = (dkdv + per_block - 1) / per_block;
     hipLaunchKernelGGL(k_state_scan, dim3((unsigned)(p.BH * blocks_per_bh)), dim3(kThreads), 0, st,
-                       S, ws, p.n_seg, dkdv, blocks_per_bh);
+                       S, ws, p.n_seg, dkdv, blocks_per_bh, (int)p.zero_start);
     return hipGetLastError();
 }
 

@@ -216,6 +216,27 @@ lla_status lla_prefill_gqa(const void *Q, const void *K, const void *V, lla_dtyp
                            size_t workspace_bytes, void *stream);
 
 /*
+ * Options of lla_prefill_ex.
+ *   LLA_PREFILL_ZERO_STATE: a fresh prompt.  The prefill starts from S_0 = 0
+ *     (the deck's worked trace starts from zero) without reading S, which is
+ *     output only and receives S_T; for T = 0, S is set to zero.  Saves the
+ *     lla_state_init call and the read of S_0.
+ */
+#define LLA_PREFILL_ZERO_STATE 1u
+
+/*
+ * lla_prefill_gqa with options (a bitwise OR of LLA_PREFILL_* values, 0 for
+ * none); unknown bits give LLA_ERR_UNSUPPORTED.  With flags = 0 and Hq = Hkv
+ * this is lla_prefill; the workspace is that of lla_prefill_gqa_workspace_size.
+ * Results with LLA_PREFILL_ZERO_STATE equal those of lla_state_init followed
+ * by the call without it, bit for bit.
+ */
+lla_status lla_prefill_ex(const void *Q, const void *K, const void *V, lla_dtype dtype,
+                          int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t dk,
+                          int64_t dv, int64_t C, unsigned flags, float *S, float *O,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * One decode step with shared-state heads: q: [B][Hq][dk], k: [B][Hkv][dk],
  * v: [B][Hkv][dv] (dtype); S: [B][Hkv][dk][dv] fp32 updated once in place;
  * o: [B][Hq][dv] fp32.  Each state is read from memory once for the G query

@@ -56,6 +56,9 @@ def lib():
     L.lla_prefill_gqa.argtypes = [vp, vp, vp, ctypes.c_int] + [i64] * 7 + [vp, vp, vp, sz, vp]
     L.lla_decode_step_gqa.restype = ctypes.c_int
     L.lla_decode_step_gqa.argtypes = [vp, vp, vp, ctypes.c_int] + [i64] * 5 + [vp, vp, vp]
+    L.lla_prefill_ex.restype = ctypes.c_int
+    L.lla_prefill_ex.argtypes = ([vp, vp, vp, ctypes.c_int] + [i64] * 7 + [ctypes.c_uint] +
+                                 [vp, vp, vp, sz, vp])
     return L
 
 
@@ -266,3 +269,35 @@ def test_python_binding_checks_grouped_shapes():
         lla.prefill(q, k, k, S, chunk=4)  # 6 query heads cannot share 4 key/value heads
     with pytest.raises(ValueError):
         lla.decode_step(q[:, :, 0], k[:, :, 0], k[:, :, 0], S)
+
+
+# ---- lla_prefill_ex -------------------------------------------------------------
+
+ZERO_STATE = 1
+
+
+def _ex_args(b, Hq, Hkv, flags):
+    return (b.q, b.k, b.v, b.dtype, b.B, Hq, Hkv, b.T, b.dk, b.dv, b.C, flags, b.S, b.O, b.ws,
+            b.ws_bytes, None)
+
+
+@pytest.mark.parametrize("flags", [2, 4, 0x80000000, 3])
+def test_prefill_ex_rejects_unknown_flags(lib, flags):
+    assert lib.lla_prefill_ex(*_ex_args(Bufs(), 2, 2, flags)) == E_UNSUP
+
+
+@pytest.mark.parametrize("change,expect", [
+    (dict(q=None), E_NULL), (dict(S=None), E_NULL), (dict(B=0), E_SHAPE), (dict(dtype=7), E_DTYPE),
+    (dict(O=5 * A + 4), E_ALIGN), (dict(O=A + 64), E_ALIAS), (dict(T=8192, ws=None), E_WS),
+])
+@pytest.mark.parametrize("flags", [0, ZERO_STATE])
+def test_prefill_ex_checks_like_prefill(lib, change, expect, flags):
+    b = Bufs()
+    for key, val in change.items():
+        setattr(b, key, val)
+    assert lib.lla_prefill_ex(*_ex_args(b, 2, 2, flags)) == expect
+    assert lib.lla_prefill(*b.args()) == expect
+
+
+def test_prefill_ex_head_counts(lib):
+    assert lib.lla_prefill_ex(*_ex_args(Bufs(), 4, 3, ZERO_STATE)) == E_SHAPE

@@ -134,3 +134,57 @@ def test_bad_arguments_raise_before_launch(dev):
         lla.prefill(qf, qf, qf, S, chunk=128)  # fp32 needs C <= 64
     with pytest.raises(TypeError):
         lla.prefill(q.half(), q.half(), q.half(), S, chunk=64)
+
+
+# B, Hq, Hkv, T, dk, dv, C, dtype: several segments (eight-wave walk), one
+# segment and no workspace (the walk reads S itself), d = 64 and fp32
+# four-wave walks, a short prompt (fused decode steps), grouped heads, FP8
+ZERO_CASES = [
+    (1, 16, 16, 8192, 128, 128, 64, torch.bfloat16),
+    (64, 8, 8, 128, 128, 128, 64, torch.bfloat16),
+    (4, 8, 8, 1024, 64, 64, 64, torch.bfloat16),
+    (64, 8, 8, 128, 64, 64, 64, torch.bfloat16),
+    (1, 2, 2, 77, 40, 72, 16, torch.float32),
+    (2, 3, 3, 5, 128, 128, 64, torch.bfloat16),
+    (1, 8, 2, 333, 128, 128, 32, torch.bfloat16),
+    (2, 4, 4, 300, 128, 128, 64, torch.float8_e4m3fn),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,dk,dv,C,dtype", ZERO_CASES)
+def test_zero_state_option_equals_init_then_prefill(dev, B, Hq, Hkv, T, dk, dv, C, dtype):
+    """lla_prefill_ex with the zero-state option never reads S (here full of
+    NaN) and gives the bits of lla_state_init followed by lla_prefill."""
+    print("zero-state", B, Hq, Hkv, T, dk, dv, C, dtype, flush=True)
+    q, k, v = workloads.gaussian(B, Hq, T, dk, dv, seed_base=T + B, scale=dk ** -0.5, dtype=dtype,
+                                 device=dev, Hkv=Hkv)
+    S_a = lla.state_init(B, Hkv, dk, dv, device=dev)
+    o_a = lla.prefill(q, k, v, S_a, chunk=C)
+    S_b = torch.full((B, Hkv, dk, dv), float("nan"), device=dev)
+    o_b = lla.prefill(q, k, v, S_b, chunk=C, zero_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, o_b)
+    assert torch.equal(S_a, S_b)
+
+
+def test_zero_state_option_on_an_empty_prompt_zeroes_the_state(dev):
+    q = torch.zeros((2, 3, 0, 64), dtype=torch.bfloat16, device=dev)
+    S = torch.full((2, 3, 64, 64), 7.0, device=dev)
+    lla.prefill(q, q, q, S, chunk=64, zero_state=True)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(S) == 0
+
+
+def test_prepared_fresh_prompt_repeats(dev):
+    """PreparedPrefill(zero_state=True) repeated on the same buffers: the state
+    it leaves behind is never read back, so every call gives the same bits."""
+    q, k, v = workloads.gaussian(1, 4, 700, 128, 128, seed_base=3, scale=128 ** -0.5, device=dev)
+    S = lla.state_init(1, 4, 128, 128, device=dev)
+    call = lla.PreparedPrefill(q, k, v, S, 64)
+    o1 = call(zero_state=True).clone()
+    S1 = S.clone()
+    o2 = call(zero_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S)
+    O_ref, S_ref = oracle.recurrence(q.cpu(), k.cpu(), v.cpu(), nthreads=8)
+    assert rel_err(np64(o2), O_ref) <= TOL and rel_err(np64(S), S_ref) <= TOL
