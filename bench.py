@@ -190,6 +190,13 @@ def bench_prefill(args, torch, lla, workloads, profiling):
                                "sample": "the whole workload (%d heads x %d tokens) %d times over, "
                                          "float64 token-by-token recurrence, one head per thread"
                                          % (B * H, T, reps)}
+        # one core: one head of the workload, scaled to all B*H heads
+        q1, k1, v1 = (x[:1, :1] for x in (qc, kc, vc))
+        reps1, secs1 = repeat_for(lambda: oracle.recurrence(q1, k1, v1, nthreads=1), 2.0)
+        res["cpu_baseline"]["single_thread"] = {
+            "value": reps1 * T / secs1 / (B * H) * B, "unit": "tokens/s", "cores": 1,
+            "seconds": secs1, "sample": "one head (%d tokens) %d times over, scaled to the %d heads"
+                                        % (T, reps1, B * H)}
     del sets
     torch.cuda.empty_cache()
     return res
@@ -274,6 +281,59 @@ def bench_decode(args, torch, lla, workloads, profiling):
                                          "%d times over, scaled to the %d states of one step"
                                          % (nb, H, ns, reps, B * H)}
     return res
+
+
+def bench_other_prefills(args, torch, lla, workloads):
+    """The small (B=4, H=8, T=1024, d=64) and the very long (B=1, H=32,
+    T=131072, C=128) prefill workloads: cold fresh-prompt steps over rotating
+    input sets, back-to-back walks for the walk kernel's roofline, and the
+    oracle on the whole workload."""
+    import oracle
+    dev = torch.device("cuda:0")
+    out = []
+    for name, rotate, steps in (("c2", 16, args.steps), ("c4", 2, 3)):
+        cfg = workloads.CONFIGS[name]
+        B, H, T, C, d = cfg.B, cfg.H, cfg.T, cfg.C, cfg.dk
+        q0, k0, v0 = workloads.config_inputs(cfg, device=dev)
+        sets = []
+        for r in range(rotate):
+            q, k, v = (x.clone() for x in (q0, k0, v0)) if r else (q0, k0, v0)
+            sets.append(lla.PreparedPrefill(q, k, v, lla.state_init(B, H, d, d, device=dev), C))
+        for i in range(max(2, args.warmup if name == "c2" else 1)):
+            sets[i % rotate](zero_state=True)
+        wall, gpu = _timed(torch, lambda i: sets[i % rotate](zero_state=True), steps)
+        n_walk = max(steps, 2 * rotate)
+        _, walk_s = _timed(torch, lambda i: sets[i % rotate].chunks(), n_walk)
+        walk_ms = walk_s * 1e3 / n_walk
+        flops, nbytes = prefill_work(B, H, T, C, d)
+        step_s = gpu / steps
+        line = {"workload": cfg.name, "B": B, "H": H, "T": T, "C": C, "dk": d, "dv": d,
+                "value": B * T / (wall / steps), "unit": "tokens/s", "steps": steps,
+                "ms_per_step": wall * 1e3 / steps, "gpu_ms_per_step": step_s * 1e3,
+                "mfma_frac": flops / step_s / (PEAK_BF16_TFLOPS * 1e12),
+                "hbm_frac": nbytes / step_s / (PEAK_HBM_GBS * 1e9),
+                "cache": "cold: %d rotating input/output sets of %.0f MB" % (rotate, nbytes / 1e6),
+                "roofline": {"kernel": "k_chunk_walk (four-wave, d=%d, C=%d)" % (d, C), "bound": "hbm",
+                             "achieved": nbytes / (walk_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                             "unit": "GB/s", "frac": nbytes / (walk_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                             "algorithmic_bytes": nbytes, "kernel_ms": walk_ms,
+                             "timing": "HIP events around %d back-to-back walk launches" % n_walk}}
+        del sets
+        torch.cuda.empty_cache()
+        if not args.no_cpu_baseline:
+            qc, kc, vc = (x.cpu() for x in (q0, k0, v0))
+            t0 = time.perf_counter()
+            oracle.recurrence(qc, kc, vc, nthreads=args.cpu_threads)
+            secs = time.perf_counter() - t0
+            line["cpu_baseline"] = {"value": B * T / secs, "unit": "tokens/s", "cores": args.cpu_threads,
+                                    "kind": "oracle", "seconds": secs,
+                                    "sample": "the whole workload once (%d heads x %d tokens), float64 "
+                                              "token-by-token recurrence" % (B * H, T)}
+            del qc, kc, vc
+        del q0, k0, v0
+        torch.cuda.empty_cache()
+        out.append(line)
+    return out
 
 
 def bench_grouped(args, torch, lla, workloads, profiling):
@@ -407,6 +467,7 @@ def main():
                     help="minimum oracle time of each CPU baseline (the sample is repeated)")
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-grouped", action="store_true")
+    ap.add_argument("--skip-other", action="store_true", help="skip the B=4 T=1024 and T=131072 prefills")
     ap.add_argument("--skip-fp8", action="store_true")
     args = ap.parse_args()
 
@@ -442,6 +503,8 @@ def main():
     }
     if "cpu_baseline" in pre:
         line["cpu_baseline"] = pre["cpu_baseline"]
+    if not args.skip_other:
+        line["other_prefills"] = bench_other_prefills(args, torch, lla, workloads)
     if not args.skip_decode:
         line["decode"] = bench_decode(args, torch, lla, workloads, profiling)
     if not args.skip_grouped:

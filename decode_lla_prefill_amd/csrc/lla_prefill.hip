@@ -254,6 +254,50 @@ __device__ __forceinline__ void state_regs_to_lds(float* lds, const f32x4 (&Sacc
     }
 }
 
+// The same moves straight between global memory and the accumulator layout,
+// 4 bytes per lane per element: lane (g, c16) of wave w reads or writes
+// S[16 dt + 4g + r][16 vt + c16], so one instruction covers four 64-byte row
+// pieces.  Used where the LDS round trip (a 64 KB stage and two barriers)
+// would sit on the critical path.  Rows >= dk and columns >= nv read as zero
+// (the buffer range drops them) and are not written.
+template <typename Cf>
+__device__ __forceinline__ void state_gmem_to_regs(f32x4 (&Sacc)[Cf::NVW][Cf::NDT], const float* g_state,
+                                                   int dk, int dv, int nv, int w, int g, int c16) {
+    const rsrc_t rs = make_rsrc(g_state, (uint32_t)((int64_t)dk * dv * 4));
+#pragma unroll
+    for (int vw = 0; vw < Cf::NVW; ++vw) {
+        const int col = 16 * (w + Cf::NW * vw) + c16;
+#pragma unroll
+        for (int dt = 0; dt < Cf::NDT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * dt + 4 * g + r;
+                const uint32_t off = (row < dk && col < nv) ? (uint32_t)((row * dv + col) * 4) : kOutside;
+                Sacc[vw][dt][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+            }
+    }
+}
+template <typename Cf>
+__device__ __forceinline__ void state_regs_to_gmem(float* g_state, const f32x4 (&Sacc)[Cf::NVW][Cf::NDT],
+                                                   int dk, int dv, int w, int g, int c16) {
+    const rsrc_t rs = make_rsrc(g_state, (uint32_t)((int64_t)dk * dv * 4));
+#pragma unroll
+    for (int vw = 0; vw < Cf::NVW; ++vw) {
+        const int col = 16 * (w + Cf::NW * vw) + c16;
+#pragma unroll
+        for (int dt = 0; dt < Cf::NDT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * dt + 4 * g + r;
+                const uint32_t off = (row < dk && col < dv) ? (uint32_t)((row * dv + col) * 4) : kOutside;
+                // (the element goes through a scalar: this compiler bit-casts a
+                // subscripted vector element as element 0)
+                const float x = Sacc[vw][dt][r];
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rs, off, 0, 0);
+            }
+    }
+}
+
 // State hop for the tiles a wave owns: S[:, value tile w + 4 vw] += K^T V,
 // contracting over the CT rows (time) of the staged tiles.
 template <typename Cf, typename T>
@@ -443,12 +487,12 @@ __device__ __forceinline__ void chunk_output(f32x4 (&Oacc)[Cf::NT][Cf::NVW],
 // Phase 1: per-segment state increments K_seg^T V_seg -> ws slot seg + 1,
 // one workgroup per (b,h), segment (all but the last) and value block.
 // ---------------------------------------------------------------------------
-template <typename In, int CT, int D, int BV, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_segment_states(
+template <typename In, int CT, int D, int BV, bool VEC, int NW = kWaves>
+__global__ __launch_bounds__(NW * kWave) void k_segment_states(
     const In* __restrict__ K, const In* __restrict__ V, float* __restrict__ ws, int64_t T_len,
     int dk, int dv, int C, int64_t G, int64_t n_seg, int n_vb) {
     using T = typename Compute<In>::type;
-    using Cf = WalkCfg<T, CT, D, BV>;
+    using Cf = WalkCfg<T, CT, D, BV, NW>;
     using Fr = typename Cf::Fr;
     __shared__ __attribute__((aligned(16))) unsigned char smem[Cf::SEG_BYTES];
     T* Ks = reinterpret_cast<T*>(smem);
@@ -481,8 +525,8 @@ __global__ __launch_bounds__(kThreads) void k_segment_states(
         // chunks of loads in flight (one register set per chunk, used round
         // robin; the loop is unrolled by PF so the sets are static).
         constexpr int PF = 2;
-        Tile<T, CT, D, typename Cf::LKL, kThreads, In> tk[PF];
-        Tile<T, CT, BV, typename Cf::LVL, kThreads, In> tv[PF];
+        Tile<T, CT, D, typename Cf::LKL, Cf::NTH, In> tk[PF];
+        Tile<T, CT, BV, typename Cf::LVL, Cf::NTH, In> tv[PF];
 #pragma unroll
         for (int u = 0; u < PF; ++u) {
             tk[u].init(dk, dk, tid);
@@ -512,8 +556,8 @@ __global__ __launch_bounds__(kThreads) void k_segment_states(
         }
     } else {
         for (int64_t c = c0; c < c1; ++c) {
-            Tile<T, CT, D, typename Cf::LKL, kThreads, In>::load_scalar(Kb + c * C * dk, dk, rows_of(c), dk, Ks, tid);
-            Tile<T, CT, BV, typename Cf::LVL, kThreads, In>::load_scalar(Vb + c * C * dv, dv, rows_of(c), nv, Vs, tid);
+            Tile<T, CT, D, typename Cf::LKL, Cf::NTH, In>::load_scalar(Kb + c * C * dk, dk, rows_of(c), dk, Ks, tid);
+            Tile<T, CT, BV, typename Cf::LVL, Cf::NTH, In>::load_scalar(Vb + c * C * dv, dv, rows_of(c), nv, Vs, tid);
             __syncthreads();
             Fr Vf[Cf::NVW][Cf::NTS];
             load_vfrags<Cf>(Vf, Vs, w, g, lane);
@@ -616,13 +660,13 @@ __device__ __forceinline__ void store_out(float* Ob, const f32x4 (&Oacc)[Cf::NT]
     }
 }
 
-template <typename In, int CT, int D, int BV, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_chunk_walk(
+template <typename In, int CT, int D, int BV, bool VEC, int NW = kWaves>
+__global__ __launch_bounds__(NW * kWave) void k_chunk_walk(
     const In* __restrict__ Q, const In* __restrict__ K, const In* __restrict__ V,
     float* __restrict__ S, float* __restrict__ O, const float* __restrict__ ws, int64_t T_len,
     int dk, int dv, int C, int64_t G, int64_t n_seg, int n_vb, int group, int zero_start) {
     using T = typename Compute<In>::type;
-    using Cf = WalkCfg<T, CT, D, BV>;
+    using Cf = WalkCfg<T, CT, D, BV, NW>;
     using Fr = typename Cf::Fr;
     __shared__ __attribute__((aligned(16))) unsigned char smem[Cf::WALK_BYTES];
     T* Qs = reinterpret_cast<T*>(smem);
@@ -661,9 +705,9 @@ __global__ __launch_bounds__(kThreads) void k_chunk_walk(
     state_lds_to_regs<Cf>(Sacc, Sst, w, g, c16);
     __syncthreads();  // the state area is reused by the tiles
 
-    using TQ = Tile<T, CT, D, typename Cf::LQL, kThreads, In>;
-    using TK = Tile<T, CT, D, typename Cf::LKL, kThreads, In>;
-    using TV = Tile<T, CT, BV, typename Cf::LVL, kThreads, In>;
+    using TQ = Tile<T, CT, D, typename Cf::LQL, Cf::NTH, In>;
+    using TK = Tile<T, CT, D, typename Cf::LKL, Cf::NTH, In>;
+    using TV = Tile<T, CT, BV, typename Cf::LVL, Cf::NTH, In>;
     TQ tq;
     TK tk;
     TV tv;
@@ -766,7 +810,6 @@ __global__ __launch_bounds__(kWideWaves * kWave) void k_chunk_walk_wide(
     __shared__ __attribute__((aligned(16))) unsigned char smem[Cf::BYTES];
     bf16* const buf = reinterpret_cast<bf16*>(smem);
     bf16* const Ps = buf + 2 * Cf::BUF;
-    float* const Sst = reinterpret_cast<float*>(smem);
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -784,11 +827,10 @@ __global__ __launch_bounds__(kWideWaves * kWave) void k_chunk_walk_wide(
     float* Ob = O + bq * T_len * dv;
     auto rows_of = [&](int64_t c) { return c < c1 ? (int)min((int64_t)C, T_len - c * C) : 0; };
 
-    // Incoming state (loads first), then the first chunk's tile loads.
+    // The first chunk's tile loads, then the incoming state straight into
+    // the accumulator registers: the first chunk's scores need only the
+    // tiles, so the state arrives while they run (loads complete in order).
     // (zero_start without a workspace: S_0 = 0 -- no column is read)
-    const float* Sin = ws == nullptr ? S + bh * dkdv : ws + (bh * n_seg + seg) * dkdv;
-    StateStage<Cf> ss;
-    ss.load(Sin, dk, dv, (ws == nullptr && zero_start) ? 0 : dv, tid);
     Tile<bf16, CT, 128, typename Cf::LQL, NTH, In> tq;
     Tile<bf16, CT, 128, typename Cf::LKL, NTH, In> tk;
     Tile<bf16, CT, 128, typename Cf::LVL, NTH, In> tv;
@@ -798,11 +840,9 @@ __global__ __launch_bounds__(kWideWaves * kWave) void k_chunk_walk_wide(
     tq.gather(Qb + c0 * C * dk, dk, rows_of(c0));
     tk.gather(Kb + c0 * C * dk, dk, rows_of(c0));
     tv.gather(Vb + c0 * C * dv, dv, rows_of(c0));
-    ss.store(Sst, tid);
-    __syncthreads();
+    const float* Sin = ws == nullptr ? S + bh * dkdv : ws + (bh * n_seg + seg) * dkdv;
     f32x4 Sacc[Cf::NVW][Cf::NDT];
-    state_lds_to_regs<Cf>(Sacc, Sst, w, g, c16);
-    __syncthreads();  // the state area is reused by the tiles
+    state_gmem_to_regs<Cf>(Sacc, Sin, dk, dv, (ws == nullptr && zero_start) ? 0 : dv, w, g, c16);
     tq.scatter(buf, tid);
     tk.scatter(buf + Cf::K_OFF, tid);
     tv.scatter(buf + Cf::V_OFF, tid);
@@ -873,11 +913,8 @@ __global__ __launch_bounds__(kWideWaves * kWave) void k_chunk_walk_wide(
     }
     store_out<Cf, true>(Ob, Oacc, t_prev, n_prev, dv, dv, w, g, c16);
 
-    if (last_seg && bq % group == 0) {  // one writer per group (the loop ended with a barrier)
-        state_regs_to_lds<Cf>(Sst, Sacc, w, g, c16);
-        __syncthreads();
-        state_lds_to_gmem<Cf>(S + bh * dkdv, Sst, dk, dv, dv, tid);
-    }
+    if (last_seg && bq % group == 0)  // one writer per group
+        state_regs_to_gmem<Cf>(S + bh * dkdv, Sacc, dk, dv, w, g, c16);
 }
 
 // ---------------------------------------------------------------------------
@@ -1027,6 +1064,15 @@ static hipError_t launch_walk_t(const PrefillPlan& p, const void* Q, const void*
             return hipGetLastError();
         }
     }
+    if constexpr (std::is_same<T, bf16>::value && D == 128 && CT == 128) {
+        if (p.vec) {  // chunks of 128: one single-buffered eight-wave workgroup per (b,h) and segment
+            hipLaunchKernelGGL((k_chunk_walk<In, 128, 128, 128, true, 8>), dim3((unsigned)(p.BHq * p.n_seg)),
+                               dim3(8 * kWave), 0, st, (const In*)Q, (const In*)K, (const In*)V, S, O,
+                               (const float*)(p.use_ws ? ws : nullptr), p.T, p.dk, p.dv, p.C, p.G,
+                               p.n_seg, 1, p.group, (int)p.zero_start);
+            return hipGetLastError();
+        }
+    }
     constexpr int BV = D > 64 ? 64 : D;
     const int64_t grid = p.BHq * p.n_seg * p.n_vb;
     const float* wsr = p.use_ws ? ws : nullptr;
@@ -1050,6 +1096,14 @@ static hipError_t launch_seg_t(const PrefillPlan& p, const void* K, const void* 
             hipLaunchKernelGGL((k_segment_states_wide<CT, In>), dim3((unsigned)(p.BH * (p.n_seg - 1))),
                                dim3(512), 0, st, (const In*)K, (const In*)V, ws, p.T, p.dk, p.dv,
                                p.C, p.G, p.n_seg);
+            return hipGetLastError();
+        }
+    }
+    if constexpr (std::is_same<T, bf16>::value && D == 128 && CT == 128) {
+        if (p.vec) {  // chunks of 128: one eight-wave workgroup per (b,h) and segment
+            hipLaunchKernelGGL((k_segment_states<In, 128, 128, 128, true, 8>),
+                               dim3((unsigned)(p.BH * (p.n_seg - 1))), dim3(8 * kWave), 0, st,
+                               (const In*)K, (const In*)V, ws, p.T, p.dk, p.dv, p.C, p.G, p.n_seg, 1);
             return hipGetLastError();
         }
     }

@@ -31,7 +31,8 @@ def _run_prefill(q, k, v, S0, C, dev):
 
 # B, Hq, Hkv, T, dk, dv, C, dtype: the eight-wave bf16 d=128 walk (one and
 # several segments, ragged tail), d=64, a short prompt (chunked for groups),
-# the fp32 and ragged-dimension paths, the largest group the decode takes
+# the fp32 and ragged-dimension paths, the largest group the decode takes,
+# chunks of 128
 GQA_INT = [
     (2, 8, 2, 300, 128, 128, 64, torch.bfloat16),
     (1, 4, 1, 2100, 128, 128, 64, torch.bfloat16),
@@ -40,6 +41,7 @@ GQA_INT = [
     (2, 6, 3, 77, 40, 72, 16, torch.float32),
     (1, 16, 1, 200, 64, 64, 64, torch.bfloat16),
     (3, 2, 1, 260, 104, 120, 20, torch.bfloat16),
+    (1, 6, 2, 700, 128, 128, 128, torch.bfloat16),
 ]
 
 

@@ -138,7 +138,8 @@ def test_bad_arguments_raise_before_launch(dev):
 
 # B, Hq, Hkv, T, dk, dv, C, dtype: several segments (eight-wave walk), one
 # segment and no workspace (the walk reads S itself), d = 64 and fp32
-# four-wave walks, a short prompt (fused decode steps), grouped heads, FP8
+# four-wave walks, a short prompt (fused decode steps), grouped heads, FP8,
+# chunks of 128 (single-buffered eight-wave walk; several segments, then one)
 ZERO_CASES = [
     (1, 16, 16, 8192, 128, 128, 64, torch.bfloat16),
     (64, 8, 8, 128, 128, 128, 64, torch.bfloat16),
@@ -148,6 +149,8 @@ ZERO_CASES = [
     (2, 3, 3, 5, 128, 128, 64, torch.bfloat16),
     (1, 8, 2, 333, 128, 128, 32, torch.bfloat16),
     (2, 4, 4, 300, 128, 128, 64, torch.float8_e4m3fn),
+    (1, 4, 4, 600, 128, 128, 128, torch.bfloat16),
+    (64, 4, 4, 256, 128, 128, 128, torch.bfloat16),
 ]
 
 
