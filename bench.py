@@ -167,6 +167,12 @@ def bench_prefill(args, torch, lla, workloads, profiling):
                      "chunk_walk": walk_ms},
         "mfma_frac": flops / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
         "hbm_gbs": nbytes / (ms_step * 1e-3) / 1e9,
+        # the step against its attainable roofline: min(MFMA peak, AI x HBM peak)
+        "attainable": {"ms_at_roof": max(flops / (PEAK_BF16_TFLOPS * 1e12), nbytes / (PEAK_HBM_GBS * 1e9)) * 1e3,
+                       "frac": max(flops / (PEAK_BF16_TFLOPS * 1e12), nbytes / (PEAK_HBM_GBS * 1e9))
+                               / (ms_step * 1e-3),
+                       "bound": "hbm" if nbytes / (PEAK_HBM_GBS * 1e9) > flops / (PEAK_BF16_TFLOPS * 1e12)
+                                else "mfma"},
         "roofline": {"kernel": "k_chunk_walk_wide<64> (bf16, d=128)", "bound": "hbm",
                      "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS,
@@ -494,7 +500,8 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": pre["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic", "config": pre["config"], "mfma_frac": pre["mfma_frac"],
-        "hbm_gbs": pre["hbm_gbs"], "gpu_ms_per_step": pre["gpu_ms_per_step"],
+        "hbm_gbs": pre["hbm_gbs"], "attainable": pre["attainable"],
+        "gpu_ms_per_step": pre["gpu_ms_per_step"],
         "phase_ms": pre["phase_ms"], "roofline": pre["roofline"], "warm": pre["warm"],
         "timing": "value and ms_per_step: wall clock over the timed steps (synchronised on both "
                   "sides); gpu_ms_per_step: HIP events around them; phase_ms: HIP events "
