@@ -182,32 +182,6 @@ __device__ __forceinline__ void state_gmem_to_lds(float* lds, const float* g, in
         }
     }
 }
-// The same transfer split in two halves -- loads into registers, then LDS
-// writes -- so that other loads can be issued in between.  Needs dv % 4 == 0
-// and a 16-byte aligned source.
-template <typename Cf>
-struct StateStage {
-    static constexpr int VPR = Cf::BV / 4;
-    static constexpr int NPT = (Cf::D * VPR + Cf::NTH - 1) / Cf::NTH;
-    f32x4 x[NPT];
-    __device__ __forceinline__ void load(const float* g, int dk, int dv, int nv, int tid) {
-        const rsrc_t rs = make_rsrc(g, (uint32_t)(((int64_t)(dk - 1) * dv + nv) * 4));
-#pragma unroll
-        for (int n = 0; n < NPT; ++n) {
-            const int e = tid + n * Cf::NTH, d = e / VPR, c = 4 * (e % VPR);
-            const uint32_t off = (d < dk && c < nv) ? (uint32_t)((d * dv + c) * 4) : kOutside;
-            x[n] = __builtin_bit_cast(f32x4, buf_load16(rs, off));
-        }
-    }
-    __device__ __forceinline__ void store(float* lds, int tid) const {
-#pragma unroll
-        for (int n = 0; n < NPT; ++n) {
-            const int e = tid + n * Cf::NTH, d = e / VPR, c = 4 * (e % VPR);
-            if (e < Cf::D * VPR) *reinterpret_cast<f32x4*>(lds + d * Cf::SLD + c) = x[n];
-        }
-    }
-};
-
 template <typename Cf>
 __device__ __forceinline__ void state_lds_to_gmem(float* g, const float* lds, int dk, int dv,
                                                   int nv, int tid) {
