@@ -72,7 +72,9 @@ typedef enum {
     LLA_ERR_NULL = 1,        /* a required pointer is NULL */
     LLA_ERR_SHAPE = 2,       /* a size is out of range */
     LLA_ERR_DTYPE = 3,       /* unknown dtype */
-    LLA_ERR_UNSUPPORTED = 4, /* valid request this build does not handle (fp32 with C > 64) */
+    LLA_ERR_UNSUPPORTED = 4, /* valid request this build does not handle: fp32 with C > 64,
+                                a grouped decode shape other than dk = dv in {64, 128} with
+                                at most 16 query heads per group, unknown option bits */
     LLA_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned */
     LLA_ERR_ALIAS = 6,       /* an output overlaps an input, another output or the workspace */
     LLA_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than lla_prefill_workspace_size() */
