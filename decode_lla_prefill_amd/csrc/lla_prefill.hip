@@ -769,8 +769,9 @@ template <int CT>
 struct WideCfg : WalkCfg<bf16, CT, 128, 128, kWideWaves> {
     using Base = WalkCfg<bf16, CT, 128, 128, kWideWaves>;
     static constexpr int BUF = Base::P_OFF;  // elements of one Q, K, V buffer
-    static constexpr int TILE_BYTES = (2 * BUF + CT * Base::LP) * 2;
-    static constexpr int BYTES = TILE_BYTES > Base::STATE_BYTES ? TILE_BYTES : Base::STATE_BYTES;
+    // two Q, K, V buffers and P; the state moves between global memory and
+    // registers directly, so it takes no LDS
+    static constexpr int BYTES = (2 * BUF + CT * Base::LP) * 2;
 };
 
 template <int CT, typename In>
