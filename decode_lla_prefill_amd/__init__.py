@@ -310,8 +310,9 @@ class PreparedPrefill:
     For loops that call the same prefill on the same buffers many times (the
     benchmark, a serving loop): calling the object calls lla_prefill (or, for
     a fresh prompt, lla_prefill_ex with PREFILL_ZERO_STATE) with the stored
-    pointers on the current stream.  The tensors must stay alive and keep
-    their shapes.
+    pointers on the current stream.  The object holds references to every
+    tensor it was given, so their memory stays allocated while it lives; the
+    tensors must keep their shapes.
     """
 
     def __init__(self, q, k, v, state, chunk, out=None, workspace=None):
@@ -336,6 +337,9 @@ class PreparedPrefill:
         self._fresh_args = (_ptr(q), _ptr(k), _ptr(v), dt, B, H, Hkv, T, dk, dv, chunk,
                             PREFILL_ZERO_STATE, _ptr(state), _ptr(self.out), ws, ws_bytes)
         self._init_args = (_ptr(state), B, Hkv, dk, dv)
+        # every tensor whose address is stored above stays alive with this
+        # object (the library reads and writes them on each call)
+        self._keep = (q, k, v, state, self.out, self.workspace)
         self._seg_args = (_ptr(k), _ptr(v), dt, B, H, T, dk, dv, chunk, ws, ws_bytes)
         self._scan_args = (_ptr(state), B, H, T, dk, dv, chunk, ws, ws_bytes)
         self._device = q.device
@@ -387,6 +391,7 @@ class PreparedDecode:
         _state_check(state, B, Hkv, dk, dv)
         self.out = _out(out, (B, Hq, dv), q.device)
         self._fn, self._args = _step_call(lib, q, k, v, state, self.out, B, Hq, Hkv, dk, dv)
+        self._keep = (q, k, v, state, self.out)  # the buffers behind the stored addresses
         self._device = q.device
 
     def __call__(self):

@@ -25,9 +25,9 @@
  *   O    : [B][H][T][dv]      fp32 output
  *   S    : [B][H][dk][dv]     fp32 recurrent state, row i = key dimension i
  *   decode: q, k : [B][H][dk]   v : [B][H][dv]   o : [B][H][dv] fp32
- * HIP graphs: capturing these calls into a HIP graph is not supported by this
- * build (a replay of a captured fresh-prompt lla_prefill_ex faulted in
- * testing, cause not found); call them on a stream directly.
+ * HIP graphs: the calls launch kernels only (no allocation, no memset node),
+ * so they may be captured into a HIP graph on the capture stream; a replay
+ * reuses the captured pointers, which must stay allocated.
  * Pointers are device pointers (HIP device memory of the current device),
  * 16-byte aligned.  The caller owns every buffer, including the workspace;
  * the library allocates nothing, holds no mutable global state and is safe
@@ -98,7 +98,8 @@ int lla_last_device_error(void);
 
 /*
  * S = 0 for B*H states of dk x dv fp32: the fresh-prompt state S_0 = 0 of the
- * deck's worked trace.  Uses a fill kernel, not hipMemsetAsync.
+ * deck's worked trace.  Uses a fill kernel (no memset node), so it may be
+ * captured into a HIP graph.
  */
 lla_status lla_state_init(float *S, int64_t B, int64_t H, int64_t dk, int64_t dv,
                           void *stream);

@@ -1,0 +1,82 @@
+"""Prepared calls and HIP graphs.
+
+* PreparedPrefill and PreparedDecode hold references to every buffer whose
+  address they store, so dropping the caller's references and emptying
+  torch's cache cannot free memory the library still reads.
+* A fresh-prompt prefill and a decode step captured into a HIP graph (their
+  kernels only: no allocation and no memset node is recorded) and replayed
+  several times, with new inputs written eagerly and the stream synchronised
+  between replays, give the bits of the same calls made eagerly.
+"""
+import gc
+
+import pytest
+import torch
+
+import decode_lla_prefill_amd as lla
+import oracle
+import workloads
+from gpu_util import TOL, need_gpu, np64, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def test_prepared_calls_keep_their_buffers_alive():
+    dev = need_gpu()
+
+    def make():
+        q, k, v = workloads.gaussian(1, 4, 700, 128, 128, seed_base=5, scale=128 ** -0.5, device=dev)
+        S = lla.state_init(1, 4, 128, 128, device=dev)
+        return lla.PreparedPrefill(q, k, v, S, 64), tuple(x.cpu() for x in (q, k, v))
+
+    call, (qc, kc, vc) = make()  # the only references to q, k, v, S are inside `call`
+    gc.collect()
+    torch.cuda.empty_cache()
+    junk = torch.full((32 << 20,), float("nan"), device=dev)  # would take freed blocks
+    o = call(zero_state=True)
+    torch.cuda.synchronize()
+    O_ref, S_ref = oracle.recurrence(qc, kc, vc, nthreads=8)
+    assert rel_err(np64(o), O_ref) <= TOL
+    assert rel_err(np64(call.state), S_ref) <= TOL
+    del junk
+
+
+def _fill(tensors, seed):
+    g = torch.Generator(device=tensors[0].device).manual_seed(seed)
+    for t in tensors:
+        t.copy_(torch.randn(t.shape, generator=g, device=t.device).mul_(t.shape[-1] ** -0.5))
+
+
+def test_graph_replays_equal_eager_calls():
+    dev = need_gpu()
+    B, H, T, d, C = 1, 4, 700, 128, 64
+    q, k, v = (torch.empty((B, H, T, d), dtype=torch.bfloat16, device=dev) for _ in range(3))
+    qd, kd, vd = (torch.empty((B, H, d), dtype=torch.bfloat16, device=dev) for _ in range(3))
+    S = lla.state_init(B, H, d, d, device=dev)
+    pre = lla.PreparedPrefill(q, k, v, S, C)
+    dec = lla.PreparedDecode(qd, kd, vd, S)
+    _fill((q, k, v, qd, kd, vd), 0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm up on a side stream, as capture does
+        pre(zero_state=True)
+        dec()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        pre(zero_state=True)
+        dec()
+    torch.cuda.synchronize()
+    for r in range(1, 5):
+        print("graph replay", r, flush=True)
+        _fill((q, k, v, qd, kd, vd), r)
+        S_ref = torch.empty_like(S)
+        o_ref = lla.prefill(q.clone(), k.clone(), v.clone(), S_ref, chunk=C, zero_state=True)
+        od_ref = lla.decode_step(qd.clone(), kd.clone(), vd.clone(), S_ref)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(pre.out, o_ref), r
+        assert torch.equal(dec.out, od_ref), r
+        assert torch.equal(S, S_ref), r
