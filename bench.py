@@ -209,7 +209,7 @@ def bench_prefill(args, torch, lla, workloads, profiling):
 
 
 def bench_decode(args, torch, lla, workloads, profiling):
-    cfg = workloads.CONFIGS["c5"]
+    cfg = workloads.CONFIGS["decode_B256"]
     dev = torch.device("cuda:0")
     B, H, T, C, d = cfg.B, cfg.H, cfg.T, cfg.C, cfg.dk
     S = lla.state_init(B, H, d, d, device=dev)
@@ -297,7 +297,7 @@ def bench_other_prefills(args, torch, lla, workloads):
     import oracle
     dev = torch.device("cuda:0")
     out = []
-    for name, rotate, steps in (("c2", 16, args.steps), ("c4", 2, 3)):
+    for name, rotate, steps in (("prefill_B4_T1024", 16, args.steps), ("prefill_T131072", 2, 3)):
         cfg = workloads.CONFIGS[name]
         B, H, T, C, d = cfg.B, cfg.H, cfg.T, cfg.C, cfg.dk
         q0, k0, v0 = workloads.config_inputs(cfg, device=dev)
@@ -305,7 +305,7 @@ def bench_other_prefills(args, torch, lla, workloads):
         for r in range(rotate):
             q, k, v = (x.clone() for x in (q0, k0, v0)) if r else (q0, k0, v0)
             sets.append(lla.PreparedPrefill(q, k, v, lla.state_init(B, H, d, d, device=dev), C))
-        for i in range(max(2, args.warmup if name == "c2" else 1)):
+        for i in range(max(2, args.warmup if name == "prefill_B4_T1024" else 1)):
             sets[i % rotate](zero_state=True)
         wall, gpu = _timed(torch, lambda i: sets[i % rotate](zero_state=True), steps)
         n_walk = max(steps, 2 * rotate)
@@ -346,7 +346,7 @@ def bench_grouped(args, torch, lla, workloads, profiling):
     """Shared-state heads: the T=8192 prefill with 16 query heads on 4
     key/value heads, and the decode batch with 32 query heads on 8."""
     dev = torch.device("cuda:0")
-    cfg = workloads.CONFIGS["g3"]
+    cfg = workloads.CONFIGS["prefill_T8192_gqa"]
     B, H, Hkv, T, C, d = cfg.B, cfg.H, cfg.kv_heads, cfg.T, cfg.C, cfg.dk
     q0, k0, v0 = workloads.config_inputs(cfg, device=dev)
     sets = []
@@ -369,7 +369,7 @@ def bench_grouped(args, torch, lla, workloads, profiling):
     del sets, q0, k0, v0
     torch.cuda.empty_cache()
 
-    cfg = workloads.CONFIGS["g5"]
+    cfg = workloads.CONFIGS["decode_B256_gqa"]
     B, H, Hkv, d = cfg.B, cfg.H, cfg.kv_heads, cfg.dk
     # The grouped states (134 MB) would fit in the 256 MB Infinity Cache:
     # the steps cycle over three state sets so that every step reads its
@@ -402,7 +402,7 @@ def bench_grouped(args, torch, lla, workloads, profiling):
 def bench_fp8(args, torch, lla, workloads, profiling):
     """FP8 (E4M3) inputs: the T=8192 prefill and the 256 x 32 decode batch."""
     dev = torch.device("cuda:0")
-    cfg = workloads.CONFIGS["f3"]
+    cfg = workloads.CONFIGS["prefill_T8192_fp8"]
     B, H, T, C, d = cfg.B, cfg.H, cfg.T, cfg.C, cfg.dk
     q0, k0, v0 = workloads.config_inputs(cfg, device=dev)
     sets = []
@@ -434,7 +434,7 @@ def bench_fp8(args, torch, lla, workloads, profiling):
     del sets, q0, k0, v0
     torch.cuda.empty_cache()
 
-    cfg = workloads.CONFIGS["f5"]
+    cfg = workloads.CONFIGS["decode_B256_fp8"]
     B, H, d = cfg.B, cfg.H, cfg.dk
     S = workloads.random_state(cfg, device=dev)  # 512 MB: larger than the Infinity Cache
     n = args.decode_steps
@@ -466,7 +466,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-steps", type=int, default=512)
     ap.add_argument("--rotate", type=int, default=4, help="input/output sets cycled (cold cache)")
-    ap.add_argument("--prefill-config", default="c3")
+    ap.add_argument("--prefill-config", default="prefill_T8192")
     ap.add_argument("--cpu-threads", type=int, default=min(16, os.cpu_count() or 1))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,

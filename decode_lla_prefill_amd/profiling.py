@@ -94,7 +94,7 @@ def run(launches: int) -> None:
     library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    cfg = workloads.CONFIGS["c3"]
+    cfg = workloads.CONFIGS["prefill_T8192"]
     q0, k0, v0 = workloads.config_inputs(cfg, device=dev)
     sets, keep = [], []
     for r in range(4):
@@ -113,7 +113,7 @@ def run(launches: int) -> None:
     del sets, keep
     torch.cuda.empty_cache()
 
-    dc = workloads.CONFIGS["c5"]
+    dc = workloads.CONFIGS["decode_B256"]
     S = state_init(dc.B, dc.H, dc.dk, dc.dv, device=dev)
     qd, kd, vd = workloads.decode_inputs(dc, launches, device=dev)
     calls = [PreparedDecode(qd[i], kd[i], vd[i], S) for i in range(launches)]
@@ -124,7 +124,7 @@ def run(launches: int) -> None:
     del calls, S
     torch.cuda.empty_cache()
 
-    gc = workloads.CONFIGS["g5"]
+    gc = workloads.CONFIGS["decode_B256_gqa"]
     S0 = workloads.random_state(gc, device=dev)
     states = [S0] + [S0.clone() for _ in range(2)]
     qd, kd, vd = workloads.decode_inputs(gc, launches, device=dev)

@@ -74,7 +74,7 @@ def test_short_prompt_gaussian_and_chunked_boundary(dev, T):
 def test_continuation_of_the_decode_workload(dev):
     """4-token continuations of the decode workload's states (256 sequences x 32
     heads, d = 128, after the T = 4096 prefill): sampled heads vs the oracle."""
-    cfg = workloads.CONFIGS["c5"]
+    cfg = workloads.CONFIGS["decode_B256"]
     B, H, T, C, d = cfg.B, cfg.H, cfg.T, cfg.C, cfg.dk
     S = lla.state_init(B, H, d, d, device=dev)
     slice_b = 32

@@ -55,7 +55,7 @@ def test_decode_after_prefill_config(dev):
     """The decode workload: a T=4096 prefill of 256 x 32 heads (d=128, C=64),
     then 512 decode steps; sampled heads against the oracle over every step
     and the final state."""
-    cfg = workloads.CONFIGS["c5"]
+    cfg = workloads.CONFIGS["decode_B256"]
     B, H, d = cfg.B, cfg.H, cfg.dk
     steps = cfg.decode_steps
     q, k, v = workloads.config_inputs(cfg, device=dev)

@@ -77,7 +77,7 @@ def test_fp8_prefill_gaussian(dev, T, C):
 def test_fp8_prefill_full_size(dev):
     """The T=8192 workload with FP8 inputs (B=1, H=16, C=64, d=128) in the
     launch configuration the benchmark times, every head against the oracle."""
-    cfg = workloads.CONFIGS["f3"]
+    cfg = workloads.CONFIGS["prefill_T8192_fp8"]
     q, k, v = workloads.config_inputs(cfg, device=dev)
     S = lla.state_init(cfg.B, cfg.H, cfg.dk, cfg.dv, device=dev)
     call = lla.PreparedPrefill(q, k, v, S, cfg.C)
@@ -125,7 +125,7 @@ def test_fp8_decode_integers_exact_and_equal_to_bf16(dev, B, Hq, Hkv, dk, dv):
 def test_fp8_decode_full_size_sampled(dev):
     """One step of the FP8 decode batch (256 sequences x 32 heads, d=128) as the
     benchmark launches it; sampled sequences against the oracle."""
-    cfg = workloads.CONFIGS["f5"]
+    cfg = workloads.CONFIGS["decode_B256_fp8"]
     S0 = workloads.random_state(cfg, device=dev)
     qd, kd, vd = workloads.decode_inputs(cfg, 1, device=dev)
     S = S0.clone()

@@ -91,7 +91,7 @@ def test_gqa_prefill_full_size_sampled(dev):
     """The grouped T=8192 workload (16 query heads on 4 key/value heads,
     d=128, C=64) in the launch configuration the benchmark times; three query
     heads and every key/value state against the oracle."""
-    cfg = workloads.CONFIGS["g3"]
+    cfg = workloads.CONFIGS["prefill_T8192_gqa"]
     q, k, v = workloads.config_inputs(cfg, device=dev)
     S = lla.state_init(cfg.B, cfg.kv_heads, cfg.dk, cfg.dv, device=dev)
     call = lla.PreparedPrefill(q, k, v, S, cfg.C)
@@ -163,7 +163,7 @@ def test_gqa_decode_full_size_sampled(dev):
     """One step of the grouped decode batch (256 sequences, 32 query heads on
     8 key/value heads, d=128) as the benchmark launches it; sampled sequences
     against the oracle."""
-    cfg = workloads.CONFIGS["g5"]
+    cfg = workloads.CONFIGS["decode_B256_gqa"]
     S0 = workloads.random_state(cfg, device=dev)
     qd, kd, vd = workloads.decode_inputs(cfg, 1, device=dev)
     S = S0.clone()

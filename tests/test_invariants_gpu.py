@@ -43,7 +43,7 @@ def test_chunk_size_invariance_integers(dev):
 def test_chunk_size_invariance_long_prompt_all_heads(dev):
     """The T=131072 shape at C = 64 and C = 128: every head agrees within the
     tolerance (the oracle checks sampled heads in the parity suite)."""
-    cfg = workloads.CONFIGS["c4"]
+    cfg = workloads.CONFIGS["prefill_T131072"]
     q, k, v = workloads.config_inputs(cfg, device=dev)
     o1, S1 = gpu_prefill(q, k, v, C=128)
     o2, S2 = gpu_prefill(q, k, v, C=64)
@@ -93,7 +93,7 @@ def test_phases_equal_prefill_and_workspace_holds_segment_states(dev):
 
 
 def test_repeat_runs_are_bitwise_identical_and_outputs_fully_written(dev):
-    cfg = workloads.CONFIGS["c3"]
+    cfg = workloads.CONFIGS["prefill_T8192"]
     q, k, v = (x.to(dev) for x in workloads.config_inputs(cfg))
     outs = []
     for _ in range(2):

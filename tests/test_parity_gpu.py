@@ -93,15 +93,15 @@ def _check_config(name, dev, heads=None, device_inputs=False, nthreads=16):
 
 
 def test_config_T1024_all_heads(dev):
-    _check_config("c2", dev)
+    _check_config("prefill_B4_T1024", dev)
 
 
 def test_config_T8192_all_heads(dev):
-    _check_config("c3", dev)
+    _check_config("prefill_T8192", dev)
 
 
 def test_config_T131072_sampled_heads(dev):
-    _check_config("c4", dev, heads=[0, 13, 31], device_inputs=True)
+    _check_config("prefill_T131072", dev, heads=[0, 13, 31], device_inputs=True)
 
 
 def test_gaussian_with_random_incoming_state(dev):

@@ -13,7 +13,7 @@ Recipe (also stated in the design notes):
 * toy variant 0 is the deck's trace; variants 1..100 draw Q, K, V uniformly
   from {0, 1} (fp32) with ``torch.manual_seed(variant)``;
 * gaussian inputs draw Q, K, V ~ N(0, 1) * scale in fp32 with one CPU or
-  device generator per tensor (seed = 10 * config + {0: q, 1: k, 2: v}),
+  device generator per tensor (seed = seed_base + {0: q, 1: k, 2: v}),
   optionally L2-normalise every key row in fp32, then round to the storage
   dtype (round-to-nearest-even for bf16);
 * integer inputs draw uniformly from {lo..hi}; they are exact in bf16, so
@@ -53,32 +53,33 @@ class Config:
         return self.Hkv or self.H
 
 
-# c1: the deck's toy; c2..c4: prefill shapes; c5: decode after a T=4096 prefill;
-# g3, g5: the T=8192 prefill and the decode batch with four query heads per
-# key/value head (shared-state heads, as in grouped-query attention);
-# f3, f5: the T=8192 prefill and the decode batch with FP8 (E4M3) inputs.
+# The deck's toy; three prefill shapes; decode after a T=4096 prefill; the
+# T=8192 prefill and the decode batch with four query heads per key/value head
+# (shared-state heads, as in grouped-query attention) and with FP8 (E4M3)
+# inputs.  Each workload draws from seeds seed_base + {0, 1, 2} (q, k, v),
+# + {3, 4, 5} (per-step decode q, k, v) and + 6 (a random state).
 CONFIGS = {
-    "c1": Config("toy", 1, 1, 8, 4, 2, 2, torch.float32, seed_base=10,
+    "toy": Config("toy", 1, 1, 8, 4, 2, 2, torch.float32, seed_base=10,
                  note="variant 0 = the deck's trace, variants 1..100 uniform {0,1}"),
-    "c2": Config("prefill_B4_H8_T1024_C64_d64", 4, 8, 1024, 64, 64, 64, torch.bfloat16,
+    "prefill_B4_T1024": Config("prefill_B4_H8_T1024_C64_d64", 4, 8, 1024, 64, 64, 64, torch.bfloat16,
                  scale=64 ** -0.5, seed_base=20),
-    "c3": Config("prefill_B1_H16_T8192_C64_d128", 1, 16, 8192, 64, 128, 128,
+    "prefill_T8192": Config("prefill_B1_H16_T8192_C64_d128", 1, 16, 8192, 64, 128, 128,
                  torch.bfloat16, scale=128 ** -0.5, l2norm_k=True, seed_base=30),
-    "c4": Config("prefill_B1_H32_T131072_C128_d128", 1, 32, 131072, 128, 128, 128,
+    "prefill_T131072": Config("prefill_B1_H32_T131072_C128_d128", 1, 32, 131072, 128, 128, 128,
                  torch.bfloat16, scale=128 ** -0.5, seed_base=40),
-    "c5": Config("decode_B256_H32_d128_after_T4096", 256, 32, 4096, 64, 128, 128,
+    "decode_B256": Config("decode_B256_H32_d128_after_T4096", 256, 32, 4096, 64, 128, 128,
                  torch.bfloat16, scale=128 ** -0.5, seed_base=50, decode_steps=512),
-    "g3": Config("prefill_B1_Hq16_Hkv4_T8192_C64_d128", 1, 16, 8192, 64, 128, 128,
+    "prefill_T8192_gqa": Config("prefill_B1_Hq16_Hkv4_T8192_C64_d128", 1, 16, 8192, 64, 128, 128,
                  torch.bfloat16, scale=128 ** -0.5, l2norm_k=True, seed_base=60, Hkv=4),
-    "g5": Config("decode_B256_Hq32_Hkv8_d128", 256, 32, 1, 64, 128, 128,
+    "decode_B256_gqa": Config("decode_B256_Hq32_Hkv8_d128", 256, 32, 1, 64, 128, 128,
                  torch.bfloat16, scale=128 ** -0.5, seed_base=70, decode_steps=512, Hkv=8,
-                 note="state drawn N(0,1) (seed 10*config + 6), not from a prefill"),
-    "f3": Config("prefill_B1_H16_T8192_C64_d128_fp8", 1, 16, 8192, 64, 128, 128,
+                 note="state drawn N(0,1) (seed seed_base + 6), not from a prefill"),
+    "prefill_T8192_fp8": Config("prefill_B1_H16_T8192_C64_d128_fp8", 1, 16, 8192, 64, 128, 128,
                  torch.float8_e4m3fn, scale=1.0, seed_base=80,
                  note="N(0,1) rounded to FP8 E4M3 (unit scale uses the format's range)"),
-    "f5": Config("decode_B256_H32_d128_fp8", 256, 32, 1, 64, 128, 128,
+    "decode_B256_fp8": Config("decode_B256_H32_d128_fp8", 256, 32, 1, 64, 128, 128,
                  torch.float8_e4m3fn, scale=1.0, seed_base=90, decode_steps=512,
-                 note="state drawn N(0,1) (seed 10*config + 6), not from a prefill"),
+                 note="state drawn N(0,1) (seed seed_base + 6), not from a prefill"),
 }
 
 
@@ -146,7 +147,7 @@ def decode_inputs(cfg: Config, steps: int, device="cpu", B=None):
     """Per-step decode inputs q [steps,B,H,dk], k [steps,B,Hkv,dk] and
     v [steps,B,Hkv,dv] (bf16).
 
-    Drawn like :func:`gaussian` with seeds 10*config + {3, 4, 5}.
+    Drawn like :func:`gaussian` with seeds seed_base + {3, 4, 5}.
     """
     B = B or cfg.B
     out = []
@@ -161,7 +162,7 @@ def decode_inputs(cfg: Config, steps: int, device="cpu", B=None):
 
 
 def random_state(cfg: Config, device="cpu", B=None):
-    """A state S [B,Hkv,dk,dv] fp32 drawn N(0,1) with seed 10*config + 6."""
+    """A state S [B,Hkv,dk,dv] fp32 drawn N(0,1) with seed seed_base + 6."""
     g = _gen(device, cfg.seed_base + 6)
     return torch.randn((B or cfg.B, cfg.kv_heads, cfg.dk, cfg.dv), generator=g,
                        dtype=torch.float32, device=device)
