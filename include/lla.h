@@ -75,7 +75,7 @@ typedef enum {
     LLA_ERR_NULL = 1,        /* a required pointer is NULL */
     LLA_ERR_SHAPE = 2,       /* a size is out of range */
     LLA_ERR_DTYPE = 3,       /* unknown dtype */
-    LLA_ERR_UNSUPPORTED = 4, /* valid request this build does not handle: fp32 with C > 64,
+    LLA_ERR_UNSUPPORTED = 4, /* valid request the library does not handle: fp32 with C > 64,
                                 a grouped decode shape other than dk = dv in {64, 128} with
                                 at most 16 query heads per group, unknown option bits */
     LLA_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned */
@@ -245,7 +245,7 @@ lla_status lla_prefill_ex(const void *Q, const void *K, const void *V, lla_dtype
  * One decode step with shared-state heads: q: [B][Hq][dk], k: [B][Hkv][dk],
  * v: [B][Hkv][dv] (dtype); S: [B][Hkv][dk][dv] fp32 updated once in place;
  * o: [B][Hq][dv] fp32.  Each state is read from memory once for the G query
- * heads of its group.  For G > 1 this build needs dk = dv in {64, 128} and
+ * heads of its group.  For G > 1 the library needs dk = dv in {64, 128} and
  * G <= 16 (else LLA_ERR_UNSUPPORTED); G = 1 is lla_decode_step.  Per query
  * head the arithmetic is that of lla_decode_step (identical bits).
  */

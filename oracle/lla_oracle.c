@@ -1,7 +1,7 @@
 /*
  * lla_oracle.c -- the CPU oracle for causal linear attention (TEST INFRASTRUCTURE).
  *
- * This file is the checker, not the product.  Only the test suite, the smoke
+ * This file is test infrastructure (the oracle), not the product.  Only the test suite, the smoke
  * check and the benchmark's CPU-baseline leg load it.  It shares no source,
  * header or helper with the GPU library.
  *
