@@ -394,6 +394,28 @@ def bench_grouped(args, torch, lla, workloads, profiling):
                         "traffic": profiling.stored_traffic("decode_group"),
                         "algorithmic_bytes": nbytes, "kernel_ms": kern_ms,
                         "timing": "HIP events around the timed steps, cycling over 3 state sets"}}
+    # Short continuations with shared-state heads: T tokens per call through
+    # lla_prefill_gqa (fused grouped decode steps while T * G <= 64), from
+    # the cycled state sets.
+    dec["continuation"] = []
+    for tc in (4, 16):
+        qc, kc, vc = (x.permute(1, 2, 0, 3).contiguous()
+                      for x in workloads.decode_inputs(cfg, tc, device=dev))
+        cont = [lla.PreparedPrefill(qc, kc, vc, S[i], cfg.C) for i in range(3)]
+        for i in range(3):
+            cont[i]()
+        nc = 48
+        wall_c, gpu_c = _timed(torch, lambda i: cont[i % 3](), nc)
+        ms_c = gpu_c * 1e3 / nc
+        cbytes = B * Hkv * (8 * d * d + tc * 4 * d) + B * H * tc * 6 * d
+        dec["continuation"].append({
+            "tokens_per_call": tc, "value": B * tc * nc / wall_c, "unit": "tokens/s",
+            "gpu_ms_per_call": ms_c,
+            "roofline": {"kernel": "k_decode_tokens<bf16,128,512> (grouped)", "bound": "hbm",
+                         "achieved": cbytes / (ms_c * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": cbytes / (ms_c * 1e-3) / 1e9 / PEAK_HBM_GBS, "algorithmic_bytes": cbytes,
+                         "kernel_ms": ms_c, "timing": "HIP events around back-to-back calls"}})
+        del cont, qc, kc, vc
     del calls, qd, kd, vd, S, S0
     torch.cuda.empty_cache()
     return {"prefill": pre, "decode": dec}

@@ -238,8 +238,9 @@ lla_status prefill_impl(const void* Q, const void* K, const void* V, lla_dtype d
     if (T == 0)  // S_T = S_0: untouched, or zero for a fresh prompt
         return zero ? device_status(lla::launch_fill_zero(S, p.BH * dk * dv, s)) : LLA_OK;
     p.zero_start = zero;
-    if (p.group == 1 && lla::decode_tokens_fit(T, (int)dk, (int)dv))  // a short prompt: fused decode steps
-        return device_status(lla::launch_decode_tokens(dtype, Q, K, V, p.BH, (int)T, (int)dk, S, O, zero, s));
+    if (lla::decode_tokens_fit(T, (int)dk, (int)dv, p.group))  // a short prompt: fused decode steps
+        return device_status(lla::launch_decode_tokens(dtype, Q, K, V, p.BH, (int)T, p.group, (int)dk, S, O,
+                                                       zero, s));
     float* ws = (float*)workspace;
     st = device_status(lla::launch_segment_states(p, K, V, ws, s));
     if (st != LLA_OK) return st;

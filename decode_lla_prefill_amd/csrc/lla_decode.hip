@@ -153,27 +153,36 @@ __global__ __launch_bounds__(NT) void k_decode_step_sq(const Tin* __restrict__ q
 // in registers across the T steps -- one state read and one write for all T
 // tokens.  Each step is the decode step above with the same per-element
 // arithmetic and the same reduction order, so T = 1 gives identical bits.
-// q, k, v: [BH][T][D] (Tin), o: [BH][T][D] fp32, T <= TMAX.
-template <typename Tin, int D, int NT, int TMAX>
+// With shared-state heads (G query heads per key/value head, as in
+// k_decode_group below) every step updates the state once and then reads it
+// for each of the G query heads, as k_decode_group does.
+// One workgroup per key/value head bh: k, v rows bh * T + t; q, o rows
+// (bh * G + g) * T + t (the query heads of a group are consecutive);
+// T <= TMAX, T * G <= QMAX.  The query heads of a step are reduced GB at a
+// time (one LDS reduction, two barriers, per batch).
+template <typename Tin, int D, int NT, int TMAX, int QMAX, int GB>
 __global__ __launch_bounds__(NT) void k_decode_tokens(const Tin* __restrict__ q,
                                                       const Tin* __restrict__ k,
                                                       const Tin* __restrict__ v,
                                                       float* __restrict__ S,
-                                                      float* __restrict__ o, int T,
+                                                      float* __restrict__ o, int T, int G,
                                                       int zero_start) {
     constexpr int CG = D / 4, RG = NT / CG, RPT = D / RG;
     static_assert(NT % CG == 0 && D % RG == 0, "thread layout must tile the state");
-    __shared__ float qs[TMAX][D], ks[TMAX][D], vs[TMAX][D];
-    __shared__ f32x4 red[RG][CG];
+    __shared__ float qs[QMAX][D], ks[TMAX][D], vs[TMAX][D];  // qs row t * G + g
+    __shared__ f32x4 red[GB][RG][CG];
     const int tid = threadIdx.x, cg = tid % CG, rg = tid / CG;
     const int64_t bh = blockIdx.x;
     float* Sb = S + bh * (int64_t)D * D;
-    const int64_t tok0 = bh * T;  // first token row of this (b,h)
+    const int64_t tok0 = bh * T;  // first k, v row of this key/value head
     for (int e = tid; e < T * D; e += NT) {
         const int t = e / D, i = e % D;
-        qs[t][i] = to_f32(q[tok0 * D + e]);
         ks[t][i] = to_f32(k[tok0 * D + e]);
         vs[t][i] = to_f32(v[tok0 * D + e]);
+    }
+    for (int e = tid; e < G * T * D; e += NT) {
+        const int g = e / (T * D), r = e % (T * D), t = r / D, i = r % D;
+        qs[t * G + g][i] = to_f32(q[(bh * G + g) * (int64_t)T * D + r]);
     }
     __syncthreads();
     f32x4 x[RPT];
@@ -183,26 +192,36 @@ __global__ __launch_bounds__(NT) void k_decode_tokens(const Tin* __restrict__ q,
                           : __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sb + (rg + m * RG) * D + 4 * cg));
     for (int t = 0; t < T; ++t) {
         const f32x4 vj = {vs[t][4 * cg], vs[t][4 * cg + 1], vs[t][4 * cg + 2], vs[t][4 * cg + 3]};
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < RPT; ++m) {
-            const int i = rg + m * RG;
-            const float ki = ks[t][i], qi = qs[t][i];
+            const float ki = ks[t][rg + m * RG];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                x[m][u] = fmaf(ki, vj[u], x[m][u]);  // rank-1 update
-                acc[u] = fmaf(qi, x[m][u], acc[u]);  // state read
+            for (int u = 0; u < 4; ++u) x[m][u] = fmaf(ki, vj[u], x[m][u]);  // rank-1 update
+        }
+        for (int g0 = 0; g0 < G; g0 += GB) {
+            const int nb = min(GB, G - g0);
+#pragma unroll
+            for (int b = 0; b < GB; ++b) {
+                if (b >= nb) break;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int m = 0; m < RPT; ++m) {
+                    const float qi = qs[t * G + g0 + b][rg + m * RG];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) acc[u] = fmaf(qi, x[m][u], acc[u]);  // state read
+                }
+                red[b][rg][cg] = acc;
             }
-        }
-        red[rg][cg] = acc;
-        __syncthreads();
-        for (int j = tid; j < D; j += NT) {  // o_t[j] = sum over row groups, in order
-            float sum = 0.0f;
+            __syncthreads();
+            for (int e = tid; e < nb * D; e += NT) {  // o_t[j] = sum over row groups, in order
+                const int b = e / D, j = e % D;
+                float sum = 0.0f;
 #pragma unroll
-            for (int r = 0; r < RG; ++r) sum += red[r][j / 4][j % 4];
-            o[(tok0 + t) * D + j] = sum;
+                for (int r = 0; r < RG; ++r) sum += red[b][r][j / 4][j % 4];
+                o[((bh * G + g0 + b) * T + t) * (int64_t)D + j] = sum;
+            }
+            __syncthreads();  // red is rewritten by the next batch or token
         }
-        __syncthreads();  // red is rewritten by the next token
     }
 #pragma unroll
     for (int m = 0; m < RPT; ++m)
@@ -307,29 +326,39 @@ hipError_t launch_decode_step(lla_dtype dtype, const void* q, const void* k, con
     return decode_t<float>(q, k, v, BH, dk, dv, S, o, st);
 }
 
-bool decode_tokens_fit(int64_t T, int dk, int dv) {
-    return T >= 1 && T <= kDecodeTokensMax && dk == dv && (dk == 64 || dk == 128);
+bool decode_tokens_fit(int64_t T, int dk, int dv, int64_t group) {
+    return T >= 1 && T <= kDecodeTokensMax && group >= 1 && group <= kDecodeGroupMax &&
+           T * group <= kDecodeTokensQueries && dk == dv && (dk == 64 || dk == 128);
 }
 
-template <typename Tin>
-static hipError_t tokens_t(const void* q, const void* k, const void* v, int64_t BH, int T, int d,
-                           float* S, float* o, int zero, hipStream_t st) {
+template <typename Tin, int QMAX, int GB>
+static hipError_t tokens_t(const void* q, const void* k, const void* v, int64_t BHkv, int T, int G,
+                           int d, float* S, float* o, int zero, hipStream_t st) {
     if (d == 128)
-        hipLaunchKernelGGL((k_decode_tokens<Tin, 128, 512, kDecodeTokensMax>), dim3((unsigned)BH), dim3(512),
-                           0, st, (const Tin*)q, (const Tin*)k, (const Tin*)v, S, o, T, zero);
+        hipLaunchKernelGGL((k_decode_tokens<Tin, 128, 512, kDecodeTokensMax, QMAX, GB>), dim3((unsigned)BHkv),
+                           dim3(512), 0, st, (const Tin*)q, (const Tin*)k, (const Tin*)v, S, o, T, G, zero);
     else
-        hipLaunchKernelGGL((k_decode_tokens<Tin, 64, 256, kDecodeTokensMax>), dim3((unsigned)BH), dim3(256),
-                           0, st, (const Tin*)q, (const Tin*)k, (const Tin*)v, S, o, T, zero);
+        hipLaunchKernelGGL((k_decode_tokens<Tin, 64, 256, kDecodeTokensMax, QMAX, GB>), dim3((unsigned)BHkv),
+                           dim3(256), 0, st, (const Tin*)q, (const Tin*)k, (const Tin*)v, S, o, T, G, zero);
     return hipGetLastError();
 }
 
+template <typename Tin>
+static hipError_t tokens_g(const void* q, const void* k, const void* v, int64_t BHkv, int T, int G,
+                           int d, float* S, float* o, int zero, hipStream_t st) {
+    // one query head per state: the query stage is no bigger than the k, v
+    // stage and one reduction buffer serves; groups reduce four heads at a time
+    if (G == 1) return tokens_t<Tin, kDecodeTokensMax, 1>(q, k, v, BHkv, T, G, d, S, o, zero, st);
+    return tokens_t<Tin, kDecodeTokensQueries, 4>(q, k, v, BHkv, T, G, d, S, o, zero, st);
+}
+
 hipError_t launch_decode_tokens(lla_dtype dtype, const void* q, const void* k, const void* v,
-                                int64_t BH, int T, int d, float* S, float* o, bool zero_start,
-                                hipStream_t st) {
+                                int64_t BHkv, int T, int group, int d, float* S, float* o,
+                                bool zero_start, hipStream_t st) {
     const int z = zero_start ? 1 : 0;
-    if (dtype == LLA_FP8_E4M3) return tokens_t<fp8e4m3>(q, k, v, BH, T, d, S, o, z, st);
-    if (dtype == LLA_BF16) return tokens_t<bf16>(q, k, v, BH, T, d, S, o, z, st);
-    return tokens_t<float>(q, k, v, BH, T, d, S, o, z, st);
+    if (dtype == LLA_FP8_E4M3) return tokens_g<fp8e4m3>(q, k, v, BHkv, T, group, d, S, o, z, st);
+    if (dtype == LLA_BF16) return tokens_g<bf16>(q, k, v, BHkv, T, group, d, S, o, z, st);
+    return tokens_g<float>(q, k, v, BHkv, T, group, d, S, o, z, st);
 }
 
 bool decode_group_fit(int64_t group, int dk, int dv) {

@@ -51,14 +51,16 @@ hipError_t launch_chunk_walk(const PrefillPlan& p, const void* Q, const void* K,
 hipError_t launch_decode_step(lla_dtype dtype, const void* q, const void* k, const void* v,
                               int64_t BH, int dk, int dv, float* S, float* o, hipStream_t st);
 
-// Short prompts (T <= kDecodeTokensMax tokens, dk = dv in {64, 128}) run as T
-// fused decode steps with the state in registers; lla_prefill takes this
-// route when decode_tokens_fit() holds.
+// Short prompts (T <= kDecodeTokensMax tokens, dk = dv in {64, 128}; with
+// shared-state heads, T * group <= kDecodeTokensQueries) run as T fused decode
+// steps with the state in registers; lla_prefill takes this route when
+// decode_tokens_fit() holds.  One workgroup per key/value head.
 constexpr int kDecodeTokensMax = 16;
-bool decode_tokens_fit(int64_t T, int dk, int dv);
+constexpr int kDecodeTokensQueries = 64;
+bool decode_tokens_fit(int64_t T, int dk, int dv, int64_t group);
 hipError_t launch_decode_tokens(lla_dtype dtype, const void* q, const void* k, const void* v,
-                                int64_t BH, int T, int d, float* S, float* o, bool zero_start,
-                                hipStream_t st);
+                                int64_t BHkv, int T, int group, int d, float* S, float* o,
+                                bool zero_start, hipStream_t st);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 
 // Shared-state heads: `group` query heads read each key/value state (dk = dv

@@ -142,10 +142,11 @@ size_t lla_prefill_workspace_size(int64_t B, int64_t H, int64_t T, int64_t dk,
  *
  * Short prompts -- a few tokens continuing an existing state, where prefill
  * behaves like decode (deck: "Prefill and decode") -- take another route:
- * for 1 <= T <= 16 with dk = dv in {64, 128} the call runs T fused decode
- * steps in one kernel (the state read and written once, held in registers
- * between the steps) with the arithmetic of lla_decode_step, so its results
- * equal T successive lla_decode_step calls bit for bit.  The workspace is not
+ * for 1 <= T <= 16 with dk = dv in {64, 128} (and, with shared-state heads,
+ * T * G <= 64) the call runs T fused decode steps in one kernel (the state
+ * read and written once, held in registers between the steps) with the
+ * arithmetic of lla_decode_step (lla_decode_step_gqa), so its results equal T
+ * successive decode-step calls bit for bit.  The workspace is not
  * touched on this route (it is still validated).
  */
 lla_status lla_prefill(const void *Q, const void *K, const void *V, lla_dtype dtype,
@@ -209,8 +210,8 @@ lla_status lla_decode_step(const void *q, const void *k, const void *v, lla_dtyp
  * lla_prefill and lla_prefill_workspace_size.  The per-segment K^T V and the
  * segment scan run once per key/value head; each query head's walk reads
  * them.  When G > 1 the walks always start from the workspace (which then
- * holds at least one state per key/value head), and the fused short-prompt
- * route is not taken.
+ * holds at least one state per key/value head).  Short prompts with
+ * T * G <= 64 take the fused decode-step route described at lla_prefill.
  */
 size_t lla_prefill_gqa_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t T,
                                       int64_t dk, int64_t dv, int64_t C);

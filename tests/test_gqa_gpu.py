@@ -175,3 +175,46 @@ def test_gqa_decode_full_size_sampled(dev):
                                                   vd[0, b:b + 1].cpu(), S0[b:b + 1].cpu())
         assert rel_err(np64(o[b:b + 1]), o_ref) <= 1e-5, b
         assert rel_err(np64(S[b:b + 1]), S_ref) <= 1e-6, b
+
+
+# ---- short continuations with shared-state heads ---------------------------------
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,d,dtype", [
+    (2, 8, 2, 5, 128, torch.bfloat16), (1, 16, 1, 4, 128, torch.bfloat16),
+    (3, 4, 2, 16, 64, torch.float32), (2, 6, 3, 7, 64, torch.float8_e4m3fn),
+    (1, 8, 1, 8, 128, torch.bfloat16),
+])
+def test_gqa_short_prompt_equals_grouped_decode_steps(dev, B, Hq, Hkv, T, d, dtype):
+    """T <= 16 tokens with T * G <= 64 run as fused grouped decode steps: the
+    same bits as T lla_decode_step_gqa calls."""
+    print("gqa short prompt", B, Hq, Hkv, T, d, dtype, flush=True)
+    q, k, v = workloads.gaussian(B, Hq, T, d, d, seed_base=T * 3 + Hq, scale=d ** -0.5, dtype=dtype,
+                                 device=dev, Hkv=Hkv)
+    S0 = torch.randn((B, Hkv, d, d), generator=torch.Generator(device=dev).manual_seed(T), device=dev)
+    S_a = S0.clone()
+    o_a = lla.prefill(q, k, v, S_a, chunk=64)
+    S_b = S0.clone()
+    o_b = torch.stack([lla.decode_step(q[:, :, t].contiguous(), k[:, :, t].contiguous(),
+                                       v[:, :, t].contiguous(), S_b) for t in range(T)], dim=2)
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, o_b)
+    assert torch.equal(S_a, S_b)
+
+
+@pytest.mark.parametrize("Hq,Hkv,T", [(8, 1, 8), (8, 1, 9), (4, 1, 16), (4, 1, 17), (2, 1, 1)])
+def test_gqa_short_prompt_integers_exact_at_the_route_boundary(dev, Hq, Hkv, T):
+    """T * G = 64 (fused) and 72 (chunked), T = 16 and 17: all exact."""
+    B, d = 2, 128
+    q, k, v = workloads.integers(B, Hq, T, d, d, seed=T + Hq, Hkv=Hkv)
+    S0 = torch.randint(-300, 301, (B, Hkv, d, d), generator=torch.Generator().manual_seed(T)).float()
+    o, S = _run_prefill(q, k, v, S0, 64, dev)
+    O_ref, S_ref = oracle.grouped_recurrence(q, k, v, S0, nthreads=8)
+    assert np.array_equal(np64(o), O_ref)
+    assert np.array_equal(np64(S), S_ref)
+    S_z = torch.full((B, Hkv, d, d), float("nan"), device=dev)  # fresh prompt: S never read
+    o_z = lla.prefill(q.to(dev).contiguous(), k.to(dev).contiguous(), v.to(dev).contiguous(), S_z,
+                      chunk=64, zero_state=True)
+    torch.cuda.synchronize()
+    O_z, S_zr = oracle.grouped_recurrence(q, k, v, nthreads=8)
+    assert np.array_equal(np64(o_z), O_z)
+    assert np.array_equal(np64(S_z), S_zr)
