@@ -139,7 +139,7 @@ def _qkv_shape(q, k, v):
     _need(v, "v", dtype=q.dtype, ndim=4)
     B, Hq, T, dk = q.shape
     Hkv = k.shape[1]
-    if tuple(k.shape) != (B, Hkv, T, dk) or tuple(v.shape[:3]) != (B, Hkv, T) or Hq % Hkv:
+    if Hkv < 1 or tuple(k.shape) != (B, Hkv, T, dk) or tuple(v.shape[:3]) != (B, Hkv, T) or Hq % Hkv:
         raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
     if not (q.device == k.device == v.device):
         raise ValueError("q, k, v must be on one device")
@@ -278,7 +278,7 @@ def _step_shape(q, k, v):
     _need(v, "v", dtype=q.dtype, ndim=3)
     B, Hq, dk = q.shape
     Hkv, dv = k.shape[1], v.shape[2]
-    if tuple(k.shape) != (B, Hkv, dk) or tuple(v.shape[:2]) != (B, Hkv) or Hq % Hkv:
+    if Hkv < 1 or tuple(k.shape) != (B, Hkv, dk) or tuple(v.shape[:2]) != (B, Hkv) or Hq % Hkv:
         raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
     return B, Hq, Hkv, dk, dv
 
