@@ -26,6 +26,11 @@ was taken on the current kernel source, else null.
 
 The CPU baseline is the float64 oracle (the token-by-token recurrence) on
 the host cores, timed on a bounded sample of the same workloads.
+
+``measured_peaks`` holds what this GPU sustains on a plain 1 GiB stream and a
+large bf16 GEMM (both through torch); the headline fractions are given
+against those too (``frac_of_measured_stream``, ``mfma_frac_of_measured_gemm``)
+beside the fractions of the published peaks.
 """
 from __future__ import annotations
 
@@ -89,6 +94,46 @@ def _timed(torch, fn, n_steps):
     e1.record(stream)
     torch.cuda.synchronize()
     return time.perf_counter() - t0, e0.elapsed_time(e1) * 1e-3
+
+
+def measure_peaks(torch):
+    """Achievable peaks of this GPU, measured for context beside the published
+    ones.  HBM: the best of two plain streams over 1 GiB fp32 (torch's
+    out-of-place add, which reads 1 GiB and writes 1 GiB, and torch's
+    device-to-device copy).  Matrix cores: torch.mm in bf16 (fp32
+    accumulate), 16384 x 16384 x 16384 with the second operand transposed,
+    the layout the GEMM library runs fastest."""
+    dev = torch.device("cuda:0")
+    n, reps = 1 << 28, 20
+    src = torch.ones(n, device=dev)
+    dst = torch.empty_like(src)
+    streams = {}
+    for name, fn in (("add", lambda i: torch.add(src, 1.0, out=dst)), ("copy", lambda i: dst.copy_(src))):
+        for i in range(3):
+            fn(i)
+        _, secs = _timed(torch, fn, reps)
+        streams[name] = 2 * n * 4 * reps / secs / 1e9
+    del src, dst
+    m, mreps = 16384, 10
+    g = torch.Generator(device=dev).manual_seed(0)
+    a = torch.randn((m, m), generator=g, device=dev).bfloat16()
+    bt = torch.randn((m, m), generator=g, device=dev).bfloat16()
+    c = torch.empty((m, m), dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        torch.mm(a, bt.t(), out=c)
+    _, secs = _timed(torch, lambda i: torch.mm(a, bt.t(), out=c), mreps)
+    gemm_tflops = 2 * m ** 3 * mreps / secs / 1e12
+    del a, bt, c
+    torch.cuda.empty_cache()
+    stream_gbs = max(streams.values())
+    return {
+        "stream_gbs": stream_gbs, "stream_frac_of_spec": stream_gbs / PEAK_HBM_GBS,
+        "stream_by_kind_gbs": streams,
+        "bf16_gemm_tflops": gemm_tflops, "bf16_gemm_frac_of_spec": gemm_tflops / PEAK_BF16_TFLOPS,
+        "how": "stream: best of torch add (out of place) and copy over 1 GiB fp32, %d calls each, "
+               "bytes read + written; GEMM: torch.mm bf16 %d^3 (A times B transposed), %d calls; "
+               "HIP events around each batch" % (reps, m, mreps),
+    }
 
 
 def bench_prefill(args, torch, lla, workloads, profiling):
@@ -540,6 +585,14 @@ def main():
         line["grouped_heads"] = bench_grouped(args, torch, lla, workloads, profiling)
     if not args.skip_fp8:
         line["fp8_inputs"] = bench_fp8(args, torch, lla, workloads, profiling)
+    peaks = measure_peaks(torch)
+    line["measured_peaks"] = peaks
+    # the same figures against what this GPU measurably sustains
+    line["roofline"]["frac_of_measured_stream"] = line["roofline"]["achieved"] / peaks["stream_gbs"]
+    line["mfma_frac_of_measured_gemm"] = line["mfma_frac"] * PEAK_BF16_TFLOPS / peaks["bf16_gemm_tflops"]
+    if "decode" in line:
+        r = line["decode"]["roofline"]
+        r["frac_of_measured_stream"] = r["achieved"] / peaks["stream_gbs"]
     print(json.dumps(line))
 
 

@@ -37,8 +37,9 @@
  * are valid once the stream has been synchronised.
  * Limits: B, H >= 1; T >= 0 (T = 0 is a no-op that leaves S untouched);
  * 1 <= dk, dv <= 128; 1 <= C <= 128 for bf16 and FP8 inputs, 1 <= C <= 64 for
- * fp32 inputs; B*H*T*max(dk,dv) < 2^62.  C need not divide T: the last chunk of a
- * sequence is shorter.
+ * fp32 inputs; B*H <= 2^20 (H counts query heads in the grouped calls) and
+ * B*H*T*max(dk,dv) <= 2^58, else LLA_ERR_SHAPE.  C need not divide T: the last
+ * chunk of a sequence is shorter.
  * Errors: arguments are checked on the host before anything is enqueued; on
  * any error no buffer is touched and a status other than LLA_OK is returned.
  * LLA_ERR_DEVICE means the HIP launch itself failed (lla_last_device_error()

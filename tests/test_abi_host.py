@@ -186,6 +186,25 @@ def test_segment_plan_for_the_t8192_workload(lib):
     assert lib.lla_prefill_workspace_size(1, 16, 8192, 128, 128, 64) == 16 * 16 * 128 * 128 * 4
 
 
+def test_size_bounds(lib):
+    """B*H <= 2^20 and B*H*T*max(dk,dv) <= 2^58: beyond either, every call
+    reports a shape error (and the planners 0) before touching anything."""
+    b = Bufs(B=1 << 10, H=1 << 10, T=100)
+    assert lib.lla_prefill_segment_chunks(1 << 10, 1 << 10, 100, 64, 64, 64) > 0
+    b.H = (1 << 10) + 1
+    assert lib.lla_prefill(*b.args()) == E_SHAPE
+    assert lib.lla_prefill_segment_chunks(1 << 10, (1 << 10) + 1, 100, 64, 64, 64) == 0
+    assert lib.lla_decode_step(A, 2 * A, 3 * A, BF16, 1 << 10, (1 << 10) + 1, 64, 64, 4 * A, 5 * A,
+                               None) == E_SHAPE
+    assert lib.lla_state_init(A, 1 << 21, 1, 4, 4, None) == E_SHAPE
+    # the element bound: 2^58 / (16 heads x 128) tokens is the largest T
+    T_max = (1 << 58) // (16 * 128)
+    assert lib.lla_prefill_segment_chunks(1, 16, T_max, 128, 128, 64) > 0
+    assert lib.lla_prefill_segment_chunks(1, 16, T_max + 1, 128, 128, 64) == 0
+    b = Bufs(B=1, H=16, T=T_max + 1, dk=128, dv=128)
+    assert lib.lla_prefill(*b.args()) == E_SHAPE
+
+
 def test_plan_rejects_bad_sizes(lib):
     assert lib.lla_prefill_segment_chunks(1, 1, 8, 2, 2, 0) == 0
     assert lib.lla_prefill_workspace_size(0, 1, 8, 2, 2, 4) == 0
