@@ -132,6 +132,13 @@ def _need(t: torch.Tensor, name: str, dtype=None, ndim=None):
         raise ValueError("%s must have %d dims (got shape %s)" % (name, ndim, tuple(t.shape)))
 
 
+def _same_device(device, **tensors):
+    """Every buffer of a call on the inputs' device (the kernels run there)."""
+    for name, t in tensors.items():
+        if t is not None and t.device != device:
+            raise ValueError("%s is on %s, the inputs on %s" % (name, t.device, device))
+
+
 def _qkv_shape(q, k, v):
     """(B, Hq, Hkv, T, dk, dv) of q [B,Hq,T,dk], k [B,Hkv,T,dk], v [B,Hkv,T,dv]."""
     _need(q, "q", ndim=4)
@@ -141,8 +148,7 @@ def _qkv_shape(q, k, v):
     Hkv = k.shape[1]
     if Hkv < 1 or tuple(k.shape) != (B, Hkv, T, dk) or tuple(v.shape[:3]) != (B, Hkv, T) or Hq % Hkv:
         raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
-    if not (q.device == k.device == v.device):
-        raise ValueError("q, k, v must be on one device")
+    _same_device(q.device, k=k, v=v)
     return B, Hq, Hkv, T, dk, v.shape[3]
 
 
@@ -214,6 +220,7 @@ def prefill(q, k, v, state, chunk: int, out=None, workspace=None, zero_state: bo
     _state_check(state, B, Hkv, dk, dv)
     out = _out(out, (B, Hq, T, dv), q.device)
     ws, ws_bytes = _workspace(B, Hq, T, dk, dv, chunk, q.device, workspace, Hkv)
+    _same_device(q.device, state=state, out=out, workspace=ws)
     if zero_state:
         _check(lib.lla_prefill_ex(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, Hq, Hkv, T, dk, dv,
                                   chunk, PREFILL_ZERO_STATE, _ptr(state), _ptr(out), _ptr(ws),
@@ -236,6 +243,7 @@ def prefill_segment_states(k, v, chunk: int, workspace):
     B, H, T, dk = k.shape
     dv = v.shape[3]
     ws, ws_bytes = _workspace(B, H, T, dk, dv, chunk, k.device, workspace)
+    _same_device(k.device, v=v, workspace=ws)
     _check(lib.lla_prefill_segment_states(_ptr(k), _ptr(v), _dtype_code(k), B, H, T, dk, dv, chunk,
                                           _ptr(ws), ws_bytes, _stream(k)),
            "lla_prefill_segment_states")
@@ -248,6 +256,7 @@ def prefill_state_scan(state, T: int, chunk: int, workspace):
     B, H, dk, dv = state.shape
     _state_check(state, B, H, dk, dv)
     ws, ws_bytes = _workspace(B, H, T, dk, dv, chunk, state.device, workspace)
+    _same_device(state.device, workspace=ws)
     _check(lib.lla_prefill_state_scan(_ptr(state), B, H, T, dk, dv, chunk, _ptr(ws), ws_bytes,
                                       _stream(state)), "lla_prefill_state_scan")
     return ws
@@ -265,6 +274,7 @@ def prefill_chunks(q, k, v, state, chunk: int, workspace=None, out=None):
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if need and workspace is None:
         raise ValueError("this shape needs a %d-byte workspace filled by phases 1 and 2" % need)
+    _same_device(q.device, state=state, out=out, workspace=workspace)
     _check(lib.lla_prefill_chunks(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H, T, dk, dv, chunk,
                                   _ptr(state), _ptr(out), _ptr(workspace), ws_bytes, _stream(q)),
            "lla_prefill_chunks")
@@ -280,6 +290,7 @@ def _step_shape(q, k, v):
     Hkv, dv = k.shape[1], v.shape[2]
     if Hkv < 1 or tuple(k.shape) != (B, Hkv, dk) or tuple(v.shape[:2]) != (B, Hkv) or Hq % Hkv:
         raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
+    _same_device(q.device, k=k, v=v)
     return B, Hq, Hkv, dk, dv
 
 
@@ -299,6 +310,7 @@ def decode_step(q, k, v, state, out=None):
     B, Hq, Hkv, dk, dv = _step_shape(q, k, v)
     _state_check(state, B, Hkv, dk, dv)
     out = _out(out, (B, Hq, dv), q.device)
+    _same_device(q.device, state=state, out=out)
     fn, args = _step_call(lib, q, k, v, state, out, B, Hq, Hkv, dk, dv)
     _check(fn(*args, _stream(q)), fn.__name__)
     return out
@@ -321,6 +333,7 @@ class PreparedPrefill:
         _state_check(state, B, Hkv, dk, dv)
         self.out = _out(out, (B, H, T, dv), q.device)
         self.workspace, ws_bytes = _workspace(B, H, T, dk, dv, chunk, q.device, workspace, Hkv)
+        _same_device(q.device, state=state, out=self.out, workspace=self.workspace)
         self.state = state
         self._lib = lib
         self._init = lib.lla_state_init
@@ -390,6 +403,7 @@ class PreparedDecode:
         B, Hq, Hkv, dk, dv = _step_shape(q, k, v)
         _state_check(state, B, Hkv, dk, dv)
         self.out = _out(out, (B, Hq, dv), q.device)
+        _same_device(q.device, state=state, out=self.out)
         self._fn, self._args = _step_call(lib, q, k, v, state, self.out, B, Hq, Hkv, dk, dv)
         self._keep = (q, k, v, state, self.out)  # the buffers behind the stored addresses
         self._device = q.device
