@@ -561,7 +561,9 @@ __global__ __launch_bounds__(kThreads) void k_state_scan(const float* __restrict
     const float* s0 = S + bh * dkdv + e;
     if (e + 4 <= dkdv && (dkdv & 3) == 0) {
         // S_0 and the first U increments are loaded together (one memory
-        // round trip), then summed in segment order.
+        // round trip), then summed in segment order.  The first batch always
+        // runs, so slot 0 receives S_0 even for a single segment (grouped
+        // heads read their start state from there).
         constexpr int U = 16;  // loads in flight per thread (segments per batch)
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         if (!zero_start) acc = *reinterpret_cast<const f32x4*>(s0);
