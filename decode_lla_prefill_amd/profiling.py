@@ -52,12 +52,39 @@ KERNELS = {
 }
 
 
+def code_only(text: str) -> str:
+    """C/C++ source without its comments, one space for each run of
+    whitespace: what the compiler sees, so a reworded comment does not
+    invalidate counters taken on the same code."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":  # string or character literal, copied whole
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_sha(kernel: str) -> str:
-    """Digest of the sources that define `kernel` (a key of KERNELS)."""
+    """Digest of the code (comments and layout aside) of the sources that
+    define `kernel` (a key of KERNELS)."""
     h = hashlib.sha256()
     for name in KERNELS[kernel][3]:
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(CSRC, name)) as f:
+            h.update(code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
