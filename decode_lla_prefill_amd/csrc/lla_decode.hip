@@ -158,9 +158,13 @@ __global__ __launch_bounds__(NT) void k_decode_step_sq(const Tin* __restrict__ q
 // for each of the G query heads, as k_decode_group does.
 // One workgroup per key/value head bh: k, v rows bh * T + t; q, o rows
 // (bh * G + g) * T + t (the query heads of a group are consecutive);
-// T <= TMAX, T * G <= QMAX.  The query heads of a step are reduced GB at a
-// time (one LDS reduction, two barriers, per batch).
-template <typename Tin, int D, int NT, int TMAX, int QMAX, int GB>
+// T <= TMAX.  The query heads of a step are reduced GB at a time (one LDS
+// reduction, two barriers, per batch).  Query rows: with GQ = 0 all T * G
+// (<= QMAX) are staged up front; with GQ > 0 (G <= GQ) only the G rows of the
+// current and of the next token are staged, double-buffered, and the next
+// token's rows are fetched while the current token updates the state -- the
+// smaller LDS footprint lets more workgroups share a CU.
+template <typename Tin, int D, int NT, int TMAX, int QMAX, int GB, int GQ>
 __global__ __launch_bounds__(NT) void k_decode_tokens(const Tin* __restrict__ q,
                                                       const Tin* __restrict__ k,
                                                       const Tin* __restrict__ v,
@@ -169,7 +173,10 @@ __global__ __launch_bounds__(NT) void k_decode_tokens(const Tin* __restrict__ q,
                                                       int zero_start) {
     constexpr int CG = D / 4, RG = NT / CG, RPT = D / RG;
     static_assert(NT % CG == 0 && D % RG == 0, "thread layout must tile the state");
-    __shared__ float qs[QMAX][D], ks[TMAX][D], vs[TMAX][D];  // qs row t * G + g
+    constexpr int QROWS = GQ > 0 ? 2 * GQ : QMAX;             // staged query rows
+    constexpr int QPT = GQ > 0 ? (GQ * D + NT - 1) / NT : 1;  // next-token q elements per thread
+    // qs row t * G + g (GQ = 0), or (t & 1) * GQ + g (GQ > 0)
+    __shared__ float qs[QROWS][D], ks[TMAX][D], vs[TMAX][D];
     __shared__ f32x4 red[GB][RG][CG];
     const int tid = threadIdx.x, cg = tid % CG, rg = tid / CG;
     const int64_t bh = blockIdx.x;
@@ -180,9 +187,14 @@ __global__ __launch_bounds__(NT) void k_decode_tokens(const Tin* __restrict__ q,
         ks[t][i] = to_f32(k[tok0 * D + e]);
         vs[t][i] = to_f32(v[tok0 * D + e]);
     }
-    for (int e = tid; e < G * T * D; e += NT) {
-        const int g = e / (T * D), r = e % (T * D), t = r / D, i = r % D;
-        qs[t * G + g][i] = to_f32(q[(bh * G + g) * (int64_t)T * D + r]);
+    if constexpr (GQ == 0) {
+        for (int e = tid; e < G * T * D; e += NT) {
+            const int g = e / (T * D), r = e % (T * D), t = r / D, i = r % D;
+            qs[t * G + g][i] = to_f32(q[(bh * G + g) * (int64_t)T * D + r]);
+        }
+    } else {  // token 0's rows into buffer 0
+        for (int e = tid; e < G * D; e += NT)
+            qs[e / D][e % D] = to_f32(q[(bh * G + e / D) * (int64_t)T * D + e % D]);
     }
     __syncthreads();
     f32x4 x[RPT];
@@ -191,6 +203,16 @@ __global__ __launch_bounds__(NT) void k_decode_tokens(const Tin* __restrict__ q,
         x[m] = zero_start ? f32x4{0.f, 0.f, 0.f, 0.f}  // S_0 = 0: S is not read
                           : __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sb + (rg + m * RG) * D + 4 * cg));
     for (int t = 0; t < T; ++t) {
+        float qn[QPT];  // the next token's query rows, on their way to LDS
+        if constexpr (GQ > 0) {
+            if (t + 1 < T) {
+#pragma unroll
+                for (int n = 0; n < QPT; ++n) {
+                    const int e = tid + n * NT;
+                    if (e < G * D) qn[n] = to_f32(q[((bh * G + e / D) * (int64_t)T + t + 1) * D + e % D]);
+                }
+            }
+        }
         const f32x4 vj = {vs[t][4 * cg], vs[t][4 * cg + 1], vs[t][4 * cg + 2], vs[t][4 * cg + 3]};
 #pragma unroll
         for (int m = 0; m < RPT; ++m) {
@@ -198,6 +220,18 @@ __global__ __launch_bounds__(NT) void k_decode_tokens(const Tin* __restrict__ q,
 #pragma unroll
             for (int u = 0; u < 4; ++u) x[m][u] = fmaf(ki, vj[u], x[m][u]);  // rank-1 update
         }
+        if constexpr (GQ > 0) {
+            // buffer (t + 1) & 1 was last read by token t - 1, before the
+            // barriers that ended it; the barriers below publish it
+            if (t + 1 < T) {
+#pragma unroll
+                for (int n = 0; n < QPT; ++n) {
+                    const int e = tid + n * NT;
+                    if (e < G * D) qs[((t + 1) & 1) * GQ + e / D][e % D] = qn[n];
+                }
+            }
+        }
+        const int qrow0 = GQ > 0 ? (t & 1) * GQ : t * G;
         for (int g0 = 0; g0 < G; g0 += GB) {
             const int nb = min(GB, G - g0);
 #pragma unroll
@@ -206,7 +240,7 @@ __global__ __launch_bounds__(NT) void k_decode_tokens(const Tin* __restrict__ q,
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int m = 0; m < RPT; ++m) {
-                    const float qi = qs[t * G + g0 + b][rg + m * RG];
+                    const float qi = qs[qrow0 + g0 + b][rg + m * RG];
 #pragma unroll
                     for (int u = 0; u < 4; ++u) acc[u] = fmaf(qi, x[m][u], acc[u]);  // state read
                 }
@@ -331,14 +365,14 @@ bool decode_tokens_fit(int64_t T, int dk, int dv, int64_t group) {
            T * group <= kDecodeTokensQueries && dk == dv && (dk == 64 || dk == 128);
 }
 
-template <typename Tin, int QMAX, int GB>
+template <typename Tin, int QMAX, int GB, int GQ>
 static hipError_t tokens_t(const void* q, const void* k, const void* v, int64_t BHkv, int T, int G,
                            int d, float* S, float* o, int zero, hipStream_t st) {
     if (d == 128)
-        hipLaunchKernelGGL((k_decode_tokens<Tin, 128, 512, kDecodeTokensMax, QMAX, GB>), dim3((unsigned)BHkv),
+        hipLaunchKernelGGL((k_decode_tokens<Tin, 128, 512, kDecodeTokensMax, QMAX, GB, GQ>), dim3((unsigned)BHkv),
                            dim3(512), 0, st, (const Tin*)q, (const Tin*)k, (const Tin*)v, S, o, T, G, zero);
     else
-        hipLaunchKernelGGL((k_decode_tokens<Tin, 64, 256, kDecodeTokensMax, QMAX, GB>), dim3((unsigned)BHkv),
+        hipLaunchKernelGGL((k_decode_tokens<Tin, 64, 256, kDecodeTokensMax, QMAX, GB, GQ>), dim3((unsigned)BHkv),
                            dim3(256), 0, st, (const Tin*)q, (const Tin*)k, (const Tin*)v, S, o, T, G, zero);
     return hipGetLastError();
 }
@@ -346,10 +380,13 @@ static hipError_t tokens_t(const void* q, const void* k, const void* v, int64_t 
 template <typename Tin>
 static hipError_t tokens_g(const void* q, const void* k, const void* v, int64_t BHkv, int T, int G,
                            int d, float* S, float* o, int zero, hipStream_t st) {
-    // one query head per state: the query stage is no bigger than the k, v
-    // stage and one reduction buffer serves; groups reduce four heads at a time
-    if (G == 1) return tokens_t<Tin, kDecodeTokensMax, 1>(q, k, v, BHkv, T, G, d, S, o, zero, st);
-    return tokens_t<Tin, kDecodeTokensQueries, 4>(q, k, v, BHkv, T, G, d, S, o, zero, st);
+    // One query head per state: all query rows are staged up front, no more
+    // than the k, v rows.  Groups stage the query rows of two tokens at a
+    // time; up to four heads per state reduce two heads per LDS pass (37 KB
+    // of LDS at d = 128: four workgroups per CU), larger groups four.
+    if (G == 1) return tokens_t<Tin, kDecodeTokensMax, 1, 0>(q, k, v, BHkv, T, G, d, S, o, zero, st);
+    if (G <= 4) return tokens_t<Tin, kDecodeTokensQueries, 2, 4>(q, k, v, BHkv, T, G, d, S, o, zero, st);
+    return tokens_t<Tin, kDecodeTokensQueries, 4, kDecodeGroupMax>(q, k, v, BHkv, T, G, d, S, o, zero, st);
 }
 
 hipError_t launch_decode_tokens(lla_dtype dtype, const void* q, const void* k, const void* v,
