@@ -85,3 +85,27 @@ def test_decode_after_prefill_config(dev):
     e_s = rel_err(np64(S[bi, hi]), S_ref)
     print("decode after prefill: rel err o %.3e  S %.3e" % (e_o, e_s))
     assert e_o <= TOL and e_s <= TOL
+
+
+def test_decode_continues_prefill_on_a_batch_slice_all_heads(dev):
+    """Eight sequences drawn like the decode workload (32 heads, d=128): the
+    T=4096 prefill followed by the 512 decode steps equals one prefill of all
+    4,608 tokens on every head, outputs and final state (GPU against GPU; the
+    two sum in different orders, so within the bar)."""
+    cfg = workloads.CONFIGS["decode_B256"]
+    nb, steps = 8, cfg.decode_steps
+    q, k, v = workloads.config_inputs(cfg, device=dev, B=nb)
+    qd, kd, vd = workloads.decode_inputs(cfg, steps, device=dev, B=nb)
+    S = torch.empty((nb, cfg.H, cfg.dk, cfg.dv), device=dev)
+    lla.prefill(q, k, v, S, chunk=cfg.C, zero_state=True)
+    o_dec = torch.empty((steps, nb, cfg.H, cfg.dv), device=dev)
+    for t in range(steps):
+        lla.decode_step(qd[t], kd[t], vd[t], S, out=o_dec[t])
+    cat = lambda a, b: torch.cat([a, b.permute(1, 2, 0, 3)], dim=2).contiguous()
+    S_all = torch.empty_like(S)
+    o_all = lla.prefill(cat(q, qd), cat(k, kd), cat(v, vd), S_all, chunk=cfg.C, zero_state=True)
+    torch.cuda.synchronize()
+    e_o = rel_err(np64(o_dec.permute(1, 2, 0, 3)), np64(o_all[:, :, cfg.T:]))
+    e_s = rel_err(np64(S), np64(S_all))
+    print("prefill + 512 decode steps vs one prefill: rel err o %.3e  S %.3e" % (e_o, e_s))
+    assert e_o <= TOL and e_s <= TOL

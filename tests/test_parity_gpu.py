@@ -3,7 +3,7 @@
 Bar: bit-exact on small-integer inputs (the deck's trace, its {0,1} toy
 variants, {-1,0,1} inputs across tile counts, ragged tails and segment
 counts); max|err|/max|ref| <= 2e-3 for bf16 inputs (all heads of the T=1024
-and T=8192 shapes, sampled heads of the T=131072 shape).
+and T=8192 shapes, four sampled heads of the T=131072 shape).
 """
 import numpy as np
 import pytest
@@ -101,7 +101,7 @@ def test_config_T8192_all_heads(dev):
 
 
 def test_config_T131072_sampled_heads(dev):
-    _check_config("prefill_T131072", dev, heads=[0, 13, 31], device_inputs=True)
+    _check_config("prefill_T131072", dev, heads=[0, 13, 22, 31], device_inputs=True)
 
 
 def test_gaussian_with_random_incoming_state(dev):
