@@ -230,6 +230,8 @@ def bench_prefill(args, torch, lla, workloads, profiling):
         "phase_ms": {"segment_states": sum(phase[0]) / len(phase[0]),
                      "state_scan": sum(phase[1]) / len(phase[1]),
                      "chunk_walk": walk_ms},
+        "head_tokens_per_s": B * H * T / (ms_step * 1e-3),
+        "tflops": flops / (ms_step * 1e-3) / 1e12,  # algorithmic (kept triangle)
         "mfma_frac": flops / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
         "hbm_gbs": nbytes / (ms_step * 1e-3) / 1e9,
         # the step against its attainable roofline: min(MFMA peak, AI x HBM peak)
@@ -581,7 +583,8 @@ def main():
         "metric": METRIC, "value": pre["value"], "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": pre["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic", "config": pre["config"], "mfma_frac": pre["mfma_frac"],
+        "data": "synthetic", "config": pre["config"], "head_tokens_per_s": pre["head_tokens_per_s"],
+        "tflops": pre["tflops"], "mfma_frac": pre["mfma_frac"],
         "hbm_gbs": pre["hbm_gbs"], "attainable": pre["attainable"],
         "gpu_ms_per_step": pre["gpu_ms_per_step"],
         "phase_ms": pre["phase_ms"], "roofline": pre["roofline"], "warm": pre["warm"],
