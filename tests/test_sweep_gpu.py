@@ -13,7 +13,7 @@ import torch
 import decode_lla_prefill_amd as lla
 import oracle
 import workloads
-from gpu_util import need_gpu, np64
+from gpu_util import need_gpu, np64, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -98,3 +98,45 @@ def test_sweep_decode_steps_integers_exact(B, Hq, dk, dv, G, dtype):
         o_ref, S_ref = oracle.grouped_decode_step(q, k, v, S_ref)
         assert np.array_equal(np64(o), o_ref), step
     assert np.array_equal(np64(S), S_ref)
+
+
+def _draw_float_cases(n, seed):
+    rng = np.random.RandomState(seed)
+    cases = []
+    while len(cases) < n:
+        dtype = DTYPES[rng.randint(3)]
+        dk = int(rng.choice([128, 128, 64, 32, 40, 96, 8]))
+        dv = dk if rng.rand() < 0.7 else int(rng.choice([128, 64, 24]))
+        C = int(rng.choice([64, 64, 128, 32, 16, 48]))
+        if dtype == torch.float32 and C > 64:
+            C = 64
+        Hkv = int(rng.choice([1, 2, 3]))
+        G = int(rng.choice([1, 1, 2, 4]))
+        B = int(rng.choice([1, 2]))
+        T = int(rng.choice([3, 16, 17, 100, 333, 1000, 2500]))
+        if B * Hkv * G * T * max(dk, dv) > 1_500_000:
+            continue
+        cases.append((B, Hkv * G, Hkv, T, dk, dv, C, dtype))
+    return cases
+
+
+FLOAT_CASES = _draw_float_cases(24, 777)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,dk,dv,C,dtype", FLOAT_CASES)
+def test_sweep_prefill_gaussian_within_the_bar(B, Hq, Hkv, T, dk, dv, C, dtype):
+    """Gaussian inputs (scaled 1/sqrt(dk); unit scale for FP8, whose range
+    allows it) and a gaussian S_0, against the oracle: max|err|/max|ref| within
+    2e-3 for bf16 and FP8 inputs, 1e-5 for fp32."""
+    dev = need_gpu()
+    print("float sweep prefill", B, Hq, Hkv, T, dk, dv, C, dtype, flush=True)
+    scale = 1.0 if dtype == torch.float8_e4m3fn else dk ** -0.5
+    q, k, v = workloads.gaussian(B, Hq, T, dk, dv, seed_base=T * 11 + dk + C, scale=scale, dtype=dtype, Hkv=Hkv)
+    S0 = torch.randn((B, Hkv, dk, dv), generator=torch.Generator().manual_seed(T + dv))
+    S = S0.to(dev).contiguous()
+    o = lla.prefill(q.to(dev).contiguous(), k.to(dev).contiguous(), v.to(dev).contiguous(), S, chunk=C)
+    torch.cuda.synchronize()
+    O_ref, S_ref = oracle.grouped_recurrence(q, k, v, S0, nthreads=8)
+    bar = 1e-5 if dtype == torch.float32 else 2e-3
+    e_o, e_s = rel_err(np64(o), O_ref), rel_err(np64(S), S_ref)
+    assert e_o <= bar and e_s <= bar, (e_o, e_s)
