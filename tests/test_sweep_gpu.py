@@ -5,7 +5,9 @@ integer inputs and compared with the oracle bit for bit.  Every kernel
 variant the plan can pick is reached: the eight-wave double-buffered walk
 (d = 128, C <= 64), the eight-wave single-buffered walk (d = 128, C = 128),
 the four-wave walks (vector and element paths), one or several segments,
-grouped heads, the fused short-prompt route, bf16, fp32 and FP8 inputs."""
+grouped heads, the fused short-prompt route, bf16, fp32 and FP8 inputs.
+A second draw runs gaussian inputs from a gaussian state and holds every
+path to the floating-point bar."""
 import numpy as np
 import pytest
 import torch
