@@ -38,13 +38,18 @@ struct WalkCfg {
     static constexpr int CT = CT_, D = D_, BV = BV_;
     static constexpr int NW = NW_, NTH = NW * kWave;  // waves, threads per workgroup
     static constexpr bool BF = std::is_same<T, bf16>::value;
+    // The state operand of Q S in natural depth order, so that Q is read in
+    // 16-byte rows (see state_operand).  Chunks of 128 keep the interleaved
+    // order: their walks have no registers to spare for the regrouping.
+    static constexpr bool NATQ = BF && CT <= 64;
     // LDS row strides (elements), chosen for the 64 four-byte LDS banks:
-    //  Q: 4 (mod 8) dwords -- 16-byte reads of 16 rows and 8-byte reads of
-    //     16 rows x 2 halves hit distinct banks;
+    //  Q: 8 (mod 16) dwords with NATQ -- its 16-byte row reads, in the
+    //     scores and in Q S, are conflict-free; else 4 (mod 8) dwords, for
+    //     the 8-byte pairs of Q S;
     //  K, V: 8 (mod 16) dwords -- a transpose read by two 16-lane groups
     //     covers 8 consecutive rows x 32 bytes, on distinct banks;
     //  P: 4 (mod 8) dwords -- its 8-byte writes and reads are conflict-free.
-    static constexpr int LQ = D + (BF ? 8 : 4);
+    static constexpr int LQ = D + (NATQ ? 16 : (BF ? 8 : 4));
     static constexpr int LK = D + (BF ? 16 : 4);
     static constexpr int LV = BV + (BF ? 16 : 4);
     static constexpr int LP = CT + (BF ? 8 : 4);
@@ -365,24 +370,48 @@ __device__ __forceinline__ void chunk_scores(const ScoreTiles<Cf>& st, const T* 
         lds_store4(Ps + (16 * it + c16) * Cf::LP + 16 * (it + 1) + 4 * g, f32x4{0.f, 0.f, 0.f, 0.f});
 }
 
-// O_c for the value tiles wave w owns: Oacc[it][vw] = (P V_c + Q_c S_c)^T,
-// from P (Ps), the wave's V operand slices Vf, Q (Qs) and the state slice
-// Sacc.  Oacc is overwritten.
-// One depth step of the state operand: value row c16, depth slots {4g + r}
-// from tile 2ds and {16 + 4g + r} from tile 2ds + 1 -- exactly the elements
-// the lane already holds.  bf16 inputs: S = hi + lo (lo is zero for fp32).
+// One depth step of the state operand: value row c16 and eight depth slots.
+// The lane holds depths {4g + r} of tile 2ds and {16 + 4g + r} of tile
+// 2ds + 1 (the accumulator layout).  Without NATQ the operand uses exactly
+// those slots, and Q is read to match in two 8-byte halves.  With NATQ they
+// are regrouped with two lane swaps into the natural order, depths
+// 8g .. 8g + 7, so that Q's slice is one 16-byte row read: 8-byte LDS reads
+// run at half the rate of 16-byte ones.  The 32-lane swap trades lane groups
+// {2, 3} of tile 2ds with groups {0, 1} of tile 2ds + 1; the 16-lane swap
+// then trades the odd groups of the first with the even groups of the
+// second.  bf16 inputs: S = hi + lo (lo is zero for fp32).
 template <typename Cf>
 __device__ __forceinline__ void state_operand(typename Cf::Fr& hi, typename Cf::Fr& lo,
                                               const f32x4 (&Sv)[Cf::NDT], int ds) {
+    if constexpr (Cf::NATQ) {
+        float x[8];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        const float x = Sv[2 * ds + (s >> 2)][s & 3];
-        if constexpr (Cf::BF) {
-            const bf16 h = to_bf16(x);
+        for (int r = 0; r < 4; ++r) {
+            const float fa = Sv[2 * ds][r], fb = Sv[2 * ds + 1][r];
+            const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(fa), __float_as_uint(fb), false, false);
+            const uint32_t a32 = p32[0], b32 = p32[1];
+            const auto p16 = __builtin_amdgcn_permlane16_swap(a32, b32, false, false);
+            const uint32_t a16 = p16[0], b16 = p16[1];
+            x[r] = __uint_as_float(a16);
+            x[4 + r] = __uint_as_float(b16);
+        }
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const bf16 h = to_bf16(x[s]);
             hi[s] = h;
-            lo[s] = to_bf16(x - to_f32(h));
-        } else {
-            hi[s] = x;
+            lo[s] = to_bf16(x[s] - to_f32(h));
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const float x = Sv[2 * ds + (s >> 2)][s & 3];
+            if constexpr (Cf::BF) {
+                const bf16 h = to_bf16(x);
+                hi[s] = h;
+                lo[s] = to_bf16(x - to_f32(h));
+            } else {
+                hi[s] = x;
+            }
         }
     }
 }
@@ -399,11 +428,14 @@ __device__ __forceinline__ void chunk_output(f32x4 (&Oacc)[Cf::NT][Cf::NVW],
                                              const T* Qs, const T* Ps, int w, int g, int c16,
                                              const Hook& hook = Hook()) {
     using Fr = typename Cf::Fr;
-    auto q_slices = [&](Fr (&qb)[Cf::NT], int ds) {
+    auto q_slices = [&](Fr (&qb)[Cf::NT], int ds) {  // depth slots as in state_operand
 #pragma unroll
         for (int it = 0; it < Cf::NT; ++it) {
             const int i = 16 * it + c16;
-            qb[it] = lds_row2(Qs + i * Cf::LQ + 32 * ds + 4 * g, Qs + i * Cf::LQ + 32 * ds + 16 + 4 * g);
+            if constexpr (Cf::NATQ)
+                qb[it] = lds_row(Qs + i * Cf::LQ + 32 * ds + 8 * g);
+            else
+                qb[it] = lds_row2(Qs + i * Cf::LQ + 32 * ds + 4 * g, Qs + i * Cf::LQ + 32 * ds + 16 + 4 * g);
         }
     };
     auto owns = [&](int vw) { return Cf::ALL_WAVES || w + Cf::NW * vw < Cf::NVT; };
