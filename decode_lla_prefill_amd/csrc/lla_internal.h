@@ -18,6 +18,12 @@ namespace lla {
 #endif
 constexpr int64_t kTargetWalkers = LLA_TARGET_WALKERS;
 
+// Chunks of up to 64 tokens carry the masked scores P into P V as a bf16
+// high + low pair (1), not as one bf16 value (0).
+#ifndef LLA_SPLIT_P
+#define LLA_SPLIT_P 1
+#endif
+
 // Everything the launchers need about a prefill shape, derived once on the
 // host from the user's sizes.
 struct PrefillPlan {

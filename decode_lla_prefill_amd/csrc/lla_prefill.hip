@@ -42,6 +42,12 @@ struct WalkCfg {
     // 16-byte rows (see state_operand).  Chunks of 128 keep the interleaved
     // order: their walks have no registers to spare for the regrouping.
     static constexpr bool NATQ = BF && CT <= 64;
+    // The masked scores P as a bf16 high + low pair (second tile right after
+    // P), so that P V carries P to about 16 bits instead of bf16's 8: an
+    // output dominated by one large score term then keeps fp32-like accuracy.
+    // Chunks of 128 have no LDS to spare for the second tile.
+    static constexpr bool SPLITP = BF && CT <= 64 && LLA_SPLIT_P;
+    static constexpr int NP = SPLITP ? 2 : 1;  // P tiles
     // LDS row strides (elements), chosen for the 64 four-byte LDS banks:
     //  Q: 8 (mod 16) dwords with NATQ -- its 16-byte row reads, in the
     //     scores and in Q S, are conflict-free; else 4 (mod 8) dwords, for
@@ -61,8 +67,8 @@ struct WalkCfg {
     static constexpr int K_OFF = CT * LQ, V_OFF = K_OFF + CT * LK, P_OFF = V_OFF + CT * LV;
     static constexpr int SLD = BV + 4;
     static constexpr int STATE_BYTES = D * SLD * 4;
-    static constexpr int WALK_BYTES = (P_OFF + CT * LP) * (int)sizeof(T) > STATE_BYTES
-                                          ? (P_OFF + CT * LP) * (int)sizeof(T) : STATE_BYTES;
+    static constexpr int WALK_BYTES = (P_OFF + NP * CT * LP) * (int)sizeof(T) > STATE_BYTES
+                                          ? (P_OFF + NP * CT * LP) * (int)sizeof(T) : STATE_BYTES;
     static constexpr int SEG_TILES = (CT * LK + CT * LV) * (int)sizeof(T);
     static constexpr int SEG_BYTES = SEG_TILES > STATE_BYTES ? SEG_TILES : STATE_BYTES;
     static constexpr int NT = CT / 16;              // 16-row tiles per chunk
@@ -134,6 +140,19 @@ __device__ __forceinline__ void lds_store4(bf16* p, f32x4 x) {
 }
 __device__ __forceinline__ void lds_store4(float* p, f32x4 x) {
     *reinterpret_cast<f32x4*>(p) = x;
+}
+// x = hi + lo, both rounded to bf16: hi to p_hi, lo to p_lo.
+__device__ __forceinline__ void lds_store4_split(bf16* p_hi, bf16* p_lo, f32x4 x) {
+    bf16x4 h, l;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float xr = x[r];
+        const bf16 hr = to_bf16(xr);
+        h[r] = hr;
+        l[r] = to_bf16(xr - to_f32(hr));
+    }
+    *reinterpret_cast<bf16x4*>(p_hi) = h;
+    *reinterpret_cast<bf16x4*>(p_lo) = l;
 }
 
 // ---- work mapping ---------------------------------------------------------------
@@ -362,12 +381,19 @@ __device__ __forceinline__ void chunk_scores(const ScoreTiles<Cf>& st, const T* 
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 if (16 * tjt[m] + 4 * g + r > i) sacc[m][r] = 0.0f;
-            lds_store4(Ps + i * Cf::LP + 16 * tjt[m] + 4 * g, sacc[m]);
+            if constexpr (Cf::SPLITP)
+                lds_store4_split(Ps + i * Cf::LP + 16 * tjt[m] + 4 * g,
+                                 Ps + Cf::CT * Cf::LP + i * Cf::LP + 16 * tjt[m] + 4 * g, sacc[m]);
+            else
+                lds_store4(Ps + i * Cf::LP + 16 * tjt[m] + 4 * g, sacc[m]);
         }
     }
     // Tiles right of the diagonal that a 32-deep step still reads: zero.
     for (int it = 2 * w; it + 1 < Cf::NT; it += 2 * Cf::NW)
-        lds_store4(Ps + (16 * it + c16) * Cf::LP + 16 * (it + 1) + 4 * g, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int pt = 0; pt < Cf::NP; ++pt)
+            lds_store4(Ps + pt * Cf::CT * Cf::LP + (16 * it + c16) * Cf::LP + 16 * (it + 1) + 4 * g,
+                       f32x4{0.f, 0.f, 0.f, 0.f});
 }
 
 // One depth step of the state operand: value row c16 and eight depth slots.
@@ -463,6 +489,13 @@ __device__ __forceinline__ void chunk_output(f32x4 (&Oacc)[Cf::NT][Cf::NVW],
 #pragma unroll
             for (int vw = 0; vw < Cf::NVW; ++vw)
                 if (owns(vw)) Oacc[it][vw] = mma(Vf[vw][ts], pb, Oacc[it][vw]);
+            if constexpr (Cf::SPLITP) {  // the low part of P
+                const T* Pl = Ps + Cf::CT * Cf::LP;
+                const Fr pl = lds_row2(Pl + i * Cf::LP + 32 * ts + 4 * g, Pl + i * Cf::LP + 32 * ts + 16 + 4 * g);
+#pragma unroll
+                for (int vw = 0; vw < Cf::NVW; ++vw)
+                    if (owns(vw)) Oacc[it][vw] = mma(Vf[vw][ts], pl, Oacc[it][vw]);
+            }
         }
     }
     // incoming state read: Q_c S_c
@@ -805,7 +838,7 @@ struct WideCfg : WalkCfg<bf16, CT, 128, 128, kWideWaves> {
     static constexpr int BUF = Base::P_OFF;  // elements of one Q, K, V buffer
     // two Q, K, V buffers and P; the state moves between global memory and
     // registers directly, so it takes no LDS
-    static constexpr int BYTES = (2 * BUF + CT * Base::LP) * 2;
+    static constexpr int BYTES = (2 * BUF + Base::NP * CT * Base::LP) * 2;
 };
 
 template <int CT, typename In>

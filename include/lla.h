@@ -47,8 +47,10 @@
  * synchronisation.  The library never aborts, exits or prints.
  * Numerics: bf16 inputs are multiplied on bf16 matrix cores with fp32
  * accumulation; the fp32 state enters Q_c S_c as a sum of two bf16 parts
- * (high and low), so integer-valued inputs whose partial sums stay below
- * 2^16 in the state and 2^24 elsewhere give exact results.  fp32 inputs use
+ * (high and low), and so do the masked scores entering P V for chunks of up
+ * to 64 tokens (chunks of 128 round them to one bf16 value), so
+ * integer-valued inputs whose partial sums stay below 2^16 in the state and
+ * 2^24 elsewhere give exact results.  fp32 inputs use
  * fp32 matrix-core instructions throughout.  FP8 inputs (the 8-bit format
  * that the blog "A 128 000 tokens, l'attention avale 85 % du calcul" says the
  * attention measurements it reports use, for the arithmetic and the cache
