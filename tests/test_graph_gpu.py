@@ -80,3 +80,51 @@ def test_graph_replays_equal_eager_calls():
         assert torch.equal(pre.out, o_ref), r
         assert torch.equal(dec.out, od_ref), r
         assert torch.equal(S, S_ref), r
+
+
+@pytest.mark.parametrize("Hq,Hkv,dtype", [(8, 2, torch.bfloat16), (4, 4, torch.float8_e4m3fn),
+                                           (8, 4, torch.float8_e4m3fn)])
+def test_graph_replays_equal_eager_calls_grouped_and_fp8(Hq, Hkv, dtype):
+    """The same capture with shared-state heads (the walks read their start
+    states from the workspace the scan fills) and with FP8 inputs."""
+    dev = need_gpu()
+    B, T, d, C = 2, 700, 128, 64
+    q = torch.empty((B, Hq, T, d), dtype=dtype, device=dev)
+    k, v = (torch.empty((B, Hkv, T, d), dtype=dtype, device=dev) for _ in range(2))
+    qd = torch.empty((B, Hq, d), dtype=dtype, device=dev)
+    kd, vd = (torch.empty((B, Hkv, d), dtype=dtype, device=dev) for _ in range(2))
+    S = lla.state_init(B, Hkv, d, d, device=dev)
+    pre = lla.PreparedPrefill(q, k, v, S, C)
+    dec = lla.PreparedDecode(qd, kd, vd, S)
+
+    def fill(seed):
+        g = torch.Generator(device=dev).manual_seed(seed)
+        scale = 1.0 if dtype == torch.float8_e4m3fn else d ** -0.5
+        for t in (q, k, v, qd, kd, vd):
+            t.copy_(torch.randn(t.shape, generator=g, device=dev).mul_(scale).to(dtype))
+
+    fill(0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        pre(zero_state=True)
+        dec()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        pre(zero_state=True)
+        dec()
+    torch.cuda.synchronize()
+    for r in range(1, 5):
+        print("graph replay", Hq, Hkv, dtype, r, flush=True)
+        fill(r)
+        S_ref = torch.empty_like(S)
+        o_ref = lla.prefill(q.clone(), k.clone(), v.clone(), S_ref, chunk=C, zero_state=True)
+        od_ref = lla.decode_step(qd.clone(), kd.clone(), vd.clone(), S_ref)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(pre.out, o_ref), r
+        assert torch.equal(dec.out, od_ref), r
+        assert torch.equal(S, S_ref), r
