@@ -27,7 +27,9 @@ __all__ = [
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-library_path = os.path.join(_HERE, "liblla.so")
+# LLA_LIBRARY names another build of the same library (the host-sanitized
+# copy the CPU tests use); by default the in-tree liblla.so.
+library_path = os.environ.get("LLA_LIBRARY") or os.path.join(_HERE, "liblla.so")
 
 # Every symbol include/lla.h declares.
 EXPORTS = ("lla_status_string", "lla_last_device_error", "lla_state_init",

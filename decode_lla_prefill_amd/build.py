@@ -21,7 +21,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "liblla.so")
 BUILD_DIR = os.path.join(ROOT, "_build", "lla")
 
-SOURCES = ["lla_abi.cpp", "lla_prefill.hip", "lla_decode.hip"]
+SOURCES = ["lla_abi.cpp", "lla_plan.cpp", "lla_prefill.hip", "lla_decode.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -55,6 +55,51 @@ def build(extra_flags=(), out: str = OUT, verbose: bool = False) -> str:
     os.replace(tmp, out)
     if verbose:
         print("built", out)
+    return out
+
+
+# Host-side sources: argument checking, status codes and the plan.  They hold
+# no kernels, so a plain host compiler builds them.
+HOST_SOURCES = ["lla_abi.cpp", "lla_plan.cpp"]
+SANITIZE_DIR = os.path.join(ROOT, "_build", "asan")
+CLANGXX = os.environ.get("LLA_CLANGXX", "/opt/rocm/llvm/bin/clang++")
+
+
+def asan_runtime() -> str:
+    """The address-sanitizer runtime of the ROCm clang (to preload into a
+    process that loads a sanitized build)."""
+    import glob
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not hits:
+        raise RuntimeError("no clang address-sanitizer runtime under /opt/rocm/llvm")
+    return hits[-1]
+
+
+def build_sanitized(out_dir: str = SANITIZE_DIR) -> str:
+    """A copy of liblla.so whose host code (HOST_SOURCES) is built with the
+    address and undefined-behaviour sanitizers (clang++, no recovery: the
+    first finding aborts), linked with the kernel objects of the regular
+    build.  For CPU tests of the host-side paths, run with asan_runtime()
+    preloaded; device code is not sanitized."""
+    os.makedirs(out_dir, exist_ok=True)
+    build()  # the kernel objects under BUILD_DIR
+    objs = []
+    for src in HOST_SOURCES:
+        obj = os.path.join(out_dir, src + ".o")
+        cmd = [CLANGXX, "-O1", "-g", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+               "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", "-I" + os.path.join(ROOT, "include"),
+               "-I" + CSRC, "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+               "-fno-omit-frame-pointer", "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("sanitized compile failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
+        objs.append(obj)
+    objs += [os.path.join(BUILD_DIR, s + ".o") for s in SOURCES if s not in HOST_SOURCES]
+    out = os.path.join(out_dir, "liblla.so")
+    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("sanitized link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
     return out
 
 

@@ -20,6 +20,19 @@ constexpr int kWave = 64;
 constexpr int kThreads = 256;  // four waves per workgroup
 constexpr int kWaves = kThreads / kWave;
 
+// x, hidden from the optimiser: arithmetic on the result is redone where it
+// is used instead of being hoisted out of a loop into registers that stay
+// live across it (an empty asm statement that claims to modify x; no
+// instruction is emitted).
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 // One 32-deep slice of a 16x16 matrix-core product, held 8 elements per lane.
 template <typename T> struct Frag;
 template <> struct Frag<bf16> { typedef bf16x8 type; };
@@ -97,6 +110,8 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     // dword 3 = 0x00020000: raw (untyped) 32-bit data, the gfx9-family setting
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
+// The whole offset goes in the lane's offset operand (the scalar offset is
+// left at zero), so the range check covers all of it.
 __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
@@ -120,20 +135,25 @@ struct Tile {
     static constexpr int NPT = (NV + NTH - 1) / NTH;  // per thread (NTH threads)
     static constexpr bool FULL = NV % NTH == 0;
     static_assert(COLS % VE == 0, "tile width must be a whole number of vectors");
+    static_assert(NTH % VPR == 0, "a thread's vectors share one column");
 
     u32x4 r[NPT];
-    uint32_t off[NPT];  // this thread's byte offsets within a tile (kOutside: padding)
+    // Vector n of this thread is (row tid / VPR + n * NTH / VPR, column
+    // vector tid % VPR): byte offset off + n * step within a tile (computed
+    // next to each load, so one register holds all of them).  `off` is
+    // kOutside for a padding column (kOutside + n * step stays outside:
+    // n * step < 2^31); rows at or past the tile's last valid row, vectors
+    // past the tile included, fall outside the descriptor.
+    uint32_t off;
+    uint32_t step;  // the same for every thread
 
     // Vector path set-up: global row stride `ld` elements (a multiple of VE),
     // valid columns `ncols` (a multiple of VE).  Offsets are the same for
     // every tile of a sequence.
     __device__ __forceinline__ void init(int64_t ld, int ncols, int tid) {
-#pragma unroll
-        for (int n = 0; n < NPT; ++n) {
-            const int e = tid + n * NTH;
-            const int row = e / VPR, cv = e % VPR;
-            off[n] = (e < NV && cv * VE < ncols) ? (uint32_t)((row * ld + cv * VE) * sizeof(In)) : kOutside;
-        }
+        const int row = tid / VPR, cv = tid % VPR;
+        off = cv * VE < ncols ? (uint32_t)((row * ld + cv * VE) * sizeof(In)) : kOutside;
+        step = (uint32_t)((NTH / VPR) * ld * sizeof(In));
     }
     // Loads the tile whose first row is at g; rows >= nrows read as zero.
     __device__ __forceinline__ void gather(const In* __restrict__ g, int64_t ld, int nrows) {
@@ -145,7 +165,7 @@ struct Tile {
     __device__ __forceinline__ static rsrc_t source(const In* __restrict__ g, int64_t ld, int nrows) {
         return make_rsrc(g, (uint32_t)(nrows * ld * sizeof(In)));
     }
-    __device__ __forceinline__ void load(rsrc_t rs, int n) { r[n] = buf_load16(rs, off[n]); }
+    __device__ __forceinline__ void load(rsrc_t rs, int n) { r[n] = buf_load16(rs, opaque(off) + n * step); }
     __device__ __forceinline__ void scatter(T* lds, int tid) const {
 #pragma unroll
         for (int n = 0; n < NPT; ++n) {

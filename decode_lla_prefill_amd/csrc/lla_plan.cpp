@@ -1,0 +1,42 @@
+// lla_plan.cpp -- the prefill plan: how a shape is cut into work for the
+// kernels.  Host code only (no kernels): the chunk tile and head-dim tile a
+// shape compiles to, the number of chunks one workgroup walks (a segment) and
+// whether the walks start from the workspace.
+//
+// The chunk form of the slide deck "Chunking, causality, and parallel
+// prefill" ("Split into chunks", "Incoming and outgoing state") serialises
+// only the chunk-to-chunk state hop.  A sequence of n_c chunks is cut into
+// segments of G chunks: each segment's K^T V is summed in parallel, a scan
+// over segments gives every segment its starting state, and one workgroup
+// walks each segment's chunks.  G depends on the shape alone, never on the
+// device, so the rounding order and hence the results are reproducible.
+#include "lla_internal.h"
+
+namespace lla {
+
+// Padded tile size (32, 64 or 128) for a head dim or a chunk size.
+static int pad_dim(int x) { return x <= 32 ? 32 : (x <= 64 ? 64 : 128); }
+
+void plan_prefill(PrefillPlan& p) {
+    if (p.Hkv == 0) p.Hkv = p.H;
+    p.group = (int)(p.H / p.Hkv);
+    p.BH = p.B * p.Hkv;   // key/value heads: states, segment pass, scan
+    p.BHq = p.B * p.H;    // query heads: the walk
+    p.D = pad_dim(p.dk > p.dv ? p.dk : p.dv);
+    p.CT = pad_dim(p.C);
+    p.BV = p.D > 64 ? 64 : p.D;
+    p.n_vb = p.D / p.BV;
+    p.n_c = p.T > 0 ? (p.T + p.C - 1) / p.C : 0;
+    const int64_t want = p.n_c * p.BHq * p.n_vb;
+    p.G = want > kTargetWalkers ? (want + kTargetWalkers - 1) / kTargetWalkers : 1;
+    if (p.G > p.n_c) p.G = p.n_c > 0 ? p.n_c : 1;
+    p.n_seg = p.n_c > 0 ? (p.n_c + p.G - 1) / p.G : 0;
+    // a walk reads its starting state from the workspace when there are
+    // several segments, or several query heads per state (the group's walks
+    // must not read S while one of them writes S_T)
+    p.use_ws = p.n_seg > 1 || p.group > 1;
+    const int ve = p.dtype == LLA_FP8_E4M3 ? 16 : (p.dtype == LLA_BF16 ? 8 : 4);  // per 16 bytes
+    p.vec = (p.dk % ve == 0) && (p.dv % ve == 0);
+}
+
+}  // namespace lla

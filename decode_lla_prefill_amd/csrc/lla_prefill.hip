@@ -45,8 +45,7 @@ struct WalkCfg {
     // The masked scores P as a bf16 high + low pair (second tile right after
     // P), so that P V carries P to about 16 bits instead of bf16's 8: an
     // output dominated by one large score term then keeps fp32-like accuracy.
-    // Chunks of 128 have no LDS to spare for the second tile.
-    static constexpr bool SPLITP = BF && CT <= 64 && LLA_SPLIT_P;
+    static constexpr bool SPLITP = BF && LLA_SPLIT_P;
     static constexpr int NP = SPLITP ? 2 : 1;  // P tiles
     // LDS row strides (elements), chosen for the 64 four-byte LDS banks:
     //  Q: 8 (mod 16) dwords with NATQ -- its 16-byte row reads, in the
@@ -58,7 +57,26 @@ struct WalkCfg {
     static constexpr int LQ = D + (NATQ ? 16 : (BF ? 8 : 4));
     static constexpr int LK = D + (BF ? 16 : 4);
     static constexpr int LV = BV + (BF ? 16 : 4);
-    static constexpr int LP = CT + (BF ? 8 : 4);
+    // P is stored as far as P V reads it: query tile it (rows 16 it ..
+    // 16 it + 15) needs the columns of the 32-deep time steps 0 .. it / 2,
+    // 32 (it / 2 + 1) of them.  Tiles it and NT - 1 - it need 32 (NT / 2 + 1)
+    // columns together, so each such pair shares 16 rows of one stride:
+    // tile it < NT / 2 from column 0, its partner right after it.  At
+    // C = 128 a P tile is 10,752 elements instead of the 17,408 of the
+    // padded square, which makes room for the low part in the
+    // single-buffered walk; one row stride keeps every tile's lane offset
+    // the same.
+    static constexpr int PPAD = BF ? 8 : 4;
+    static constexpr int PLD = 32 * (CT / 32 + 1) + PPAD;  // elements per row
+    __device__ __host__ static constexpr int p_row0(int it) { return 16 * (it < CT / 32 ? it : CT / 16 - 1 - it); }
+    __device__ __host__ static constexpr int p_col0(int it) {
+        return it < CT / 32 ? 0 : 32 * ((CT / 16 - 1 - it) / 2 + 1);
+    }
+    // element (row 16 it + r, column col) of P
+    __device__ __host__ static constexpr int p_at(int it, int r, int col) {
+        return (p_row0(it) + r) * PLD + p_col0(it) + col;
+    }
+    static constexpr int P_ELEMS = CT / 2 * PLD;  // one P tile
     using LQL = PadLayout<LQ>;
     using LKL = PadLayout<LK>;
     using LVL = PadLayout<LV>;
@@ -67,8 +85,8 @@ struct WalkCfg {
     static constexpr int K_OFF = CT * LQ, V_OFF = K_OFF + CT * LK, P_OFF = V_OFF + CT * LV;
     static constexpr int SLD = BV + 4;
     static constexpr int STATE_BYTES = D * SLD * 4;
-    static constexpr int WALK_BYTES = (P_OFF + NP * CT * LP) * (int)sizeof(T) > STATE_BYTES
-                                          ? (P_OFF + NP * CT * LP) * (int)sizeof(T) : STATE_BYTES;
+    static constexpr int WALK_BYTES = (P_OFF + NP * P_ELEMS) * (int)sizeof(T) > STATE_BYTES
+                                          ? (P_OFF + NP * P_ELEMS) * (int)sizeof(T) : STATE_BYTES;
     static constexpr int SEG_TILES = (CT * LK + CT * LV) * (int)sizeof(T);
     static constexpr int SEG_BYTES = SEG_TILES > STATE_BYTES ? SEG_TILES : STATE_BYTES;
     static constexpr int NT = CT / 16;              // 16-row tiles per chunk
@@ -381,18 +399,20 @@ __device__ __forceinline__ void chunk_scores(const ScoreTiles<Cf>& st, const T* 
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 if (16 * tjt[m] + 4 * g + r > i) sacc[m][r] = 0.0f;
+            // the lane's part of the address, recomputed per chunk rather
+            // than one live register per tile
+            const int at = opaque(c16 * Cf::PLD + 4 * g) + Cf::p_at(tit[m], 0, 16 * tjt[m]);
             if constexpr (Cf::SPLITP)
-                lds_store4_split(Ps + i * Cf::LP + 16 * tjt[m] + 4 * g,
-                                 Ps + Cf::CT * Cf::LP + i * Cf::LP + 16 * tjt[m] + 4 * g, sacc[m]);
+                lds_store4_split(Ps + at, Ps + Cf::P_ELEMS + at, sacc[m]);
             else
-                lds_store4(Ps + i * Cf::LP + 16 * tjt[m] + 4 * g, sacc[m]);
+                lds_store4(Ps + at, sacc[m]);
         }
     }
     // Tiles right of the diagonal that a 32-deep step still reads: zero.
     for (int it = 2 * w; it + 1 < Cf::NT; it += 2 * Cf::NW)
 #pragma unroll
         for (int pt = 0; pt < Cf::NP; ++pt)
-            lds_store4(Ps + pt * Cf::CT * Cf::LP + (16 * it + c16) * Cf::LP + 16 * (it + 1) + 4 * g,
+            lds_store4(Ps + pt * Cf::P_ELEMS + opaque(c16 * Cf::PLD + 4 * g) + Cf::p_at(it, 0, 16 * (it + 1)),
                        f32x4{0.f, 0.f, 0.f, 0.f});
 }
 
@@ -466,10 +486,17 @@ __device__ __forceinline__ void chunk_output(f32x4 (&Oacc)[Cf::NT][Cf::NVW],
     };
     auto owns = [&](int vw) { return Cf::ALL_WAVES || w + Cf::NW * vw < Cf::NVT; };
 
+    // The first depth step's Q slices and state operand are read ahead of
+    // P V, except in chunks of 128 tokens, whose walks have no registers to
+    // hold them through it.
+    constexpr bool EARLY_QS = Cf::CT <= 64;
     Fr qb[2][Cf::NT], Shi[2][Cf::NVW], Slo[2][Cf::NVW];
-    q_slices(qb[0], 0);
+    auto qs_prologue = [&]() {
+        q_slices(qb[0], 0);
 #pragma unroll
-    for (int vw = 0; vw < Cf::NVW; ++vw) state_operand<Cf>(Shi[0][vw], Slo[0][vw], Sacc[vw], 0);
+        for (int vw = 0; vw < Cf::NVW; ++vw) state_operand<Cf>(Shi[0][vw], Slo[0][vw], Sacc[vw], 0);
+    };
+    if constexpr (EARLY_QS) qs_prologue();
 
     // All query tiles of the chunk are accumulated side by side (depth
     // outer, tile inner), so consecutive matrix-core ops are independent.
@@ -483,15 +510,14 @@ __device__ __forceinline__ void chunk_output(f32x4 (&Oacc)[Cf::NT][Cf::NVW],
     for (int ts = 0; ts < Cf::NTS; ++ts) {
 #pragma unroll
         for (int it = 2 * ts; it < Cf::NT; ++it) {
-            const int i = 16 * it + c16;
-            const Fr pb = lds_row2(Ps + i * Cf::LP + 32 * ts + 4 * g,
-                                   Ps + i * Cf::LP + 32 * ts + 16 + 4 * g);
+            const int at = Cf::p_at(it, c16, 32 * ts + 4 * g);
+            const Fr pb = lds_row2(Ps + at, Ps + at + 16);
 #pragma unroll
             for (int vw = 0; vw < Cf::NVW; ++vw)
                 if (owns(vw)) Oacc[it][vw] = mma(Vf[vw][ts], pb, Oacc[it][vw]);
             if constexpr (Cf::SPLITP) {  // the low part of P
-                const T* Pl = Ps + Cf::CT * Cf::LP;
-                const Fr pl = lds_row2(Pl + i * Cf::LP + 32 * ts + 4 * g, Pl + i * Cf::LP + 32 * ts + 16 + 4 * g);
+                const T* Pl = Ps + Cf::P_ELEMS;
+                const Fr pl = lds_row2(Pl + at, Pl + at + 16);
 #pragma unroll
                 for (int vw = 0; vw < Cf::NVW; ++vw)
                     if (owns(vw)) Oacc[it][vw] = mma(Vf[vw][ts], pl, Oacc[it][vw]);
@@ -499,6 +525,7 @@ __device__ __forceinline__ void chunk_output(f32x4 (&Oacc)[Cf::NT][Cf::NVW],
         }
     }
     // incoming state read: Q_c S_c
+    if constexpr (!EARLY_QS) qs_prologue();
 #pragma unroll
     for (int ds = 0; ds < Cf::NDS; ++ds) {
         const int cur = ds & 1, nxt = cur ^ 1;
@@ -673,15 +700,15 @@ __device__ __forceinline__ void store_out(float* Ob, const f32x4 (&Oacc)[Cf::NT]
     if constexpr (VEC) {
         const rsrc_t rs = make_rsrc(Ob + t0 * dv, (uint32_t)(nrows * dv * 4));
 #pragma unroll
-        for (int it = 0; it < Cf::NT; ++it) {
-            const int i = 16 * it + c16;
+        for (int vw = 0; vw < Cf::NVW; ++vw) {
+            const int v = 16 * (w + Cf::NW * vw) + 4 * g;
+            if (!(Cf::ALL_WAVES || w + Cf::NW * vw < Cf::NVT)) continue;
+            // row c16 of every query tile: one lane offset, plus the tile's
+            // first row (kOutside plus it stays outside)
+            const uint32_t off = v < nv ? (uint32_t)((c16 * dv + v) * 4) : kOutside;
 #pragma unroll
-            for (int vw = 0; vw < Cf::NVW; ++vw) {
-                const int v = 16 * (w + Cf::NW * vw) + 4 * g;
-                if (!(Cf::ALL_WAVES || w + Cf::NW * vw < Cf::NVT)) continue;
-                const uint32_t off = v < nv ? (uint32_t)((i * dv + v) * 4) : kOutside;
-                buf_store16(rs, off, Oacc[it][vw]);
-            }
+            for (int it = 0; it < Cf::NT; ++it)
+                buf_store16(rs, opaque(off) + (uint32_t)(16 * it * dv * 4), Oacc[it][vw]);
         }
     } else {
 #pragma unroll
@@ -838,7 +865,7 @@ struct WideCfg : WalkCfg<bf16, CT, 128, 128, kWideWaves> {
     static constexpr int BUF = Base::P_OFF;  // elements of one Q, K, V buffer
     // two Q, K, V buffers and P; the state moves between global memory and
     // registers directly, so it takes no LDS
-    static constexpr int BYTES = (2 * BUF + Base::NP * CT * Base::LP) * 2;
+    static constexpr int BYTES = (2 * BUF + Base::NP * Base::P_ELEMS) * 2;
 };
 
 template <int CT, typename In>
@@ -920,8 +947,8 @@ __global__ __launch_bounds__(kWideWaves * kWave) void k_chunk_walk_wide(
 #pragma unroll
                 for (int vw = 0; vw < Cf::NVW; ++vw) {
                     const int vcol = 16 * (w + Cf::NW * vw) + 4 * g;
-                    const uint32_t off = vcol < dv ? (uint32_t)(((16 * ds + c16) * dv + vcol) * 4) : kOutside;
-                    buf_store16(rso, off, Oacc[ds][vw]);
+                    const uint32_t off = vcol < dv ? (uint32_t)((c16 * dv + vcol) * 4) : kOutside;
+                    buf_store16(rso, opaque(off) + (uint32_t)(16 * ds * dv * 4), Oacc[ds][vw]);
                 }
             }
         });
@@ -1065,32 +1092,9 @@ __global__ __launch_bounds__(512) void k_segment_states_wide(const In* __restric
 }
 
 // ---------------------------------------------------------------------------
-// Host side: planning and dispatch over (input type, chunk tile, head dim).
+// Host side: dispatch over (input type, chunk tile, head dim); the plan
+// itself is made in lla_plan.cpp.
 // ---------------------------------------------------------------------------
-static int pad_dim(int x) { return x <= 32 ? 32 : (x <= 64 ? 64 : 128); }
-
-void plan_prefill(PrefillPlan& p) {
-    if (p.Hkv == 0) p.Hkv = p.H;
-    p.group = (int)(p.H / p.Hkv);
-    p.BH = p.B * p.Hkv;   // key/value heads: states, segment pass, scan
-    p.BHq = p.B * p.H;    // query heads: the walk
-    p.D = pad_dim(p.dk > p.dv ? p.dk : p.dv);
-    p.CT = pad_dim(p.C);
-    p.BV = p.D > 64 ? 64 : p.D;
-    p.n_vb = p.D / p.BV;
-    p.n_c = p.T > 0 ? (p.T + p.C - 1) / p.C : 0;
-    const int64_t want = p.n_c * p.BHq * p.n_vb;
-    p.G = want > kTargetWalkers ? (want + kTargetWalkers - 1) / kTargetWalkers : 1;
-    if (p.G > p.n_c) p.G = p.n_c > 0 ? p.n_c : 1;
-    p.n_seg = p.n_c > 0 ? (p.n_c + p.G - 1) / p.G : 0;
-    // a walk reads its starting state from the workspace when there are
-    // several segments, or several query heads per state (the group's walks
-    // must not read S while one of them writes S_T)
-    p.use_ws = p.n_seg > 1 || p.group > 1;
-    const int ve = p.dtype == LLA_FP8_E4M3 ? 16 : (p.dtype == LLA_BF16 ? 8 : 4);  // per 16 bytes
-    p.vec = (p.dk % ve == 0) && (p.dv % ve == 0);
-}
-
 // In: the input element type (bf16, FP8 or fp32); the matrix cores run on
 // Compute<In>::type.
 template <typename In, int CT, int D>

@@ -46,12 +46,16 @@
  * gives the hipError_t); faults inside a kernel surface at the caller's next
  * synchronisation.  The library never aborts, exits or prints.
  * Numerics: bf16 inputs are multiplied on bf16 matrix cores with fp32
- * accumulation; the fp32 state enters Q_c S_c as a sum of two bf16 parts
- * (high and low), and so do the masked scores entering P V for chunks of up
- * to 64 tokens (chunks of 128 round them to one bf16 value), so
- * integer-valued inputs whose partial sums stay below 2^16 in the state and
- * 2^24 elsewhere give exact results.  fp32 inputs use
- * fp32 matrix-core instructions throughout.  FP8 inputs (the 8-bit format
+ * accumulation.  The fp32 state enters Q_c S_c, and the masked scores
+ * P = tril(Q_c K_c^T) enter P V, each as a sum of two bf16 parts (high and
+ * low): about 16 significant bits, a relative error of at most 2^-16.  So
+ * integer-valued inputs give exact results as long as every score
+ * |q_t . k_s| and every state entry is at most 2^16 in magnitude and every
+ * other partial sum (of P V, Q S, K^T V and O) stays below 2^24; one bf16
+ * value alone would hold integers exactly only up to 256.  The decode
+ * kernels (and the short-prompt route) run fp32 FMAs: exact while partial
+ * sums stay below 2^24.  fp32 inputs use fp32 matrix-core instructions
+ * throughout, exact under the same 2^24 condition.  FP8 inputs (the 8-bit format
  * that the blog "A 128 000 tokens, l'attention avale 85 % du calcul" says the
  * attention measurements it reports use, for the arithmetic and the cache
  * alike) are the OCP E4M3 format: 1 sign, 4 exponent (bias 7) and 3

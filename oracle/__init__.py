@@ -52,7 +52,7 @@ _SO = os.path.join(_HERE, "liblla_oracle.so")
 _lock = threading.Lock()
 _lib = None
 
-__all__ = ["build", "recurrence", "decode_step", "chunked", "causal_mask",
+__all__ = ["build", "build_sanitized", "recurrence", "decode_step", "chunked", "causal_mask",
            "incoming_term", "grouped_recurrence", "grouped_decode_step", "decode_e4m3"]
 
 
@@ -66,13 +66,30 @@ def build(force: bool = True) -> str:
     return _SO
 
 
+def build_sanitized(out_dir: str) -> str:
+    """``lla_oracle.c`` built with the address and undefined-behaviour
+    sanitizers (ROCm clang, so that one preloaded runtime serves it and the
+    sanitized library; the first finding aborts) into out_dir."""
+    os.makedirs(out_dir, exist_ok=True)
+    out = os.path.join(out_dir, "liblla_oracle.so")
+    subprocess.run(["/opt/rocm/llvm/bin/clang", "-O1", "-g", "-ffp-contract=off", "-fPIC", "-shared",
+                    "-pthread", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                    "-fno-omit-frame-pointer", "-o", out, _SRC], check=True)
+    return out
+
+
 def _load():
     global _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(_SO):
-                build(force=True)
-            lib = ctypes.CDLL(_SO)
+            # LLA_ORACLE_LIBRARY names another build of lla_oracle.c (the
+            # sanitized copy of build_sanitized); by default the in-tree one
+            path = os.environ.get("LLA_ORACLE_LIBRARY")
+            if not path:
+                path = _SO
+                if not os.path.exists(_SO):
+                    build(force=True)
+            lib = ctypes.CDLL(path)
             dp = ctypes.POINTER(ctypes.c_double)
             i64 = ctypes.c_int64
             lib.lla_oracle_recurrence.argtypes = [dp, dp, dp, dp, dp, i64, i64, i64,

@@ -2,13 +2,15 @@
 
 Bar: bit-exact on small-integer inputs (the deck's trace, its {0,1} toy
 variants, {-1,0,1} inputs across tile counts, ragged tails and segment
-counts); max|err|/max|ref| <= 2e-3 for bf16 inputs (all heads of the T=1024
+counts, and {-8..8} queries and keys whose scores reach 8192);
+max|err|/max|ref| <= 2e-3 for bf16 inputs (all heads of the T=1024
 and T=8192 shapes, four sampled heads of the T=131072 shape).
 """
 import numpy as np
 import pytest
 import torch
 
+import decode_lla_prefill_amd as lla
 import oracle
 import workloads
 from gpu_util import TOL, gpu_prefill, need_gpu, np64, rel_err
@@ -63,6 +65,40 @@ def test_integer_inputs_exact(dev, B, H, T, dk, dv, C, dtype):
     q, k, v = workloads.integers(B, H, T, dk, dv, seed=T + dk + C, dtype=dtype)
     o, S = gpu_prefill(q, k, v, C=C)
     O_ref, S_ref = oracle.recurrence(q, k, v, nthreads=8)
+    assert np.array_equal(np64(S), S_ref)
+    assert np.array_equal(np64(o), O_ref)
+
+
+# Scores beyond what one bf16 value holds exactly: q, k in {-8..8} at d_k up
+# to 128 give |q . k| up to 8192 (one bf16 value is exact only up to 256;
+# the high + low pair to 2^16), with v in {-1, 0, 1} so that every partial sum
+# stays below 2^24 for T < 2048 (|P V| <= 8192 C, |S| <= 8 T, |Q S| <= 8192 T):
+# the results are exact integers, the same at every chunk size.
+LARGE_SCORE_CASES = [
+    # B, Hq, Hkv, T, dk, dv, C, dtype
+    (1, 2, 2, 1000, 128, 128, 128, torch.bfloat16),      # eight-wave walk, chunks of 128
+    (1, 2, 2, 1000, 128, 128, 64, torch.bfloat16),       # double-buffered eight-wave walk
+    (1, 2, 2, 500, 128, 128, 32, torch.bfloat16),
+    (2, 2, 2, 700, 128, 128, 128, torch.float8_e4m3fn),  # E4M3 holds {-8..8} exactly
+    (1, 3, 3, 900, 64, 64, 128, torch.bfloat16),         # four-wave walk
+    (2, 1, 1, 300, 40, 72, 100, torch.bfloat16),         # element path
+    (1, 4, 2, 600, 128, 128, 64, torch.bfloat16),        # shared-state heads
+    (1, 4, 2, 600, 128, 128, 128, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,dk,dv,C,dtype", LARGE_SCORE_CASES)
+def test_integer_inputs_with_large_scores_exact(dev, B, Hq, Hkv, T, dk, dv, C, dtype):
+    q, k, v = workloads.integers(B, Hq, T, dk, dv, seed=3 * T + C, lo=-8, hi=8, dtype=dtype, Hkv=Hkv,
+                                 v_range=(-1, 1))
+    # the case does reach scores that one bf16 value cannot hold
+    G = Hq // Hkv
+    P = torch.tril(q.float() @ k.float().repeat_interleave(G, dim=1).transpose(-1, -2))
+    assert P.abs().max() <= 2 ** 16 and (P != P.bfloat16().float()).any()
+    S = torch.zeros((B, Hkv, dk, dv), device=dev)
+    o = lla.prefill(q.to(dev), k.to(dev), v.to(dev), S, chunk=C)
+    torch.cuda.synchronize()
+    O_ref, S_ref = oracle.grouped_recurrence(q, k, v, np.zeros((B, Hkv, dk, dv)), nthreads=8)
     assert np.array_equal(np64(S), S_ref)
     assert np.array_equal(np64(o), O_ref)
 

@@ -1,16 +1,16 @@
 """Where the prefill rounds.  Inside a chunk the masked scores P = tril(Q K^T)
-enter the matrix-core product P V in bf16: for chunks of up to 64 tokens as a
-high + low pair (P to about 16 bits: an error of at most 2^-16 |P|), for
-chunks of 128 as one bf16 value (round to nearest even: at most 2^-8 |P|).
-Everything else accumulates in fp32, and the state enters Q S as a bf16
-high + low pair.  So for a prompt of one chunk from a zero state, every output
-element is within that factor times (|P| |V|) of the exact result, plus fp32
-slack, whatever the inputs.
+enter the matrix-core product P V in bf16 as a high + low pair (P to about 16
+bits: an error of at most 2^-16 |P|), at every chunk size.  Everything else
+accumulates in fp32, and the state enters Q S as a bf16 high + low pair.  So
+for a prompt of one chunk from a zero state, every output element is within
+that factor times (|P| |V|) of the exact result, plus fp32 slack, whatever the
+inputs.
 
-With one bf16 value, an output dominated by one large score term (few tokens,
-large q . k) can pass max|err|/max|ref| = 2e-3: the first case below measured
-2.09e-3 at C = 128 (unit-scale FP8 inputs, dk = 32, 100 tokens).  The same
-kind of input at C = 64 stays far inside the bar."""
+With one bf16 value (2^-8 |P|) instead of the pair, an output dominated by one
+large score term (few tokens, large q . k) could pass max|err|/max|ref| = 2e-3:
+the first case below measured 2.09e-3 at C = 128 that way (unit-scale FP8
+inputs, dk = 32, 100 tokens).  With the pair every case stays far inside the
+bar."""
 import numpy as np
 import pytest
 import torch
@@ -49,13 +49,13 @@ def test_one_chunk_error_is_bounded_by_the_rounding_of_p(B, Hq, Hkv, T, dk, dv, 
     kt = k64.transpose(0, 1, 3, 2)
     absP = np.abs(np.tril(q64 @ kt))          # |P| of the one chunk
     absQK = np.tril(np.abs(q64) @ np.abs(kt))  # sum_i |q_i k_i| (fp32 slack of the scores)
-    # rounding of P to bf16 (2^-8 |P|), fp32 sums over T terms (P V) and dk
+    # rounding of P to a bf16 pair (2^-16 |P|), fp32 sums over T terms (P V) and dk
     # terms (Q K^T), each n * 2^-24 of its absolute sum
     u = 2.0 ** -24
-    p_round = 2.0 ** -16 if C <= 64 else 2.0 ** -8  # P as hi + lo, or one bf16 value
+    p_round = 2.0 ** -16  # P as a bf16 hi + lo pair
     allowed = ((p_round + (T + 4) * u) * (absP @ v64) * (1 + 2.0 ** -8)
                + 2 * (dk + 4) * u * (absQK @ v64))
     err = np.abs(np.asarray(np64(o)) - O_ref)
     assert (err <= allowed).all(), float((err / np.maximum(allowed, 1e-300)).max())
-    if C <= 64:  # the split keeps even dominated outputs far inside the bar
-        assert err.max() / np.abs(O_ref).max() <= 1e-4
+    # the split keeps even dominated outputs far inside the bar
+    assert err.max() / np.abs(O_ref).max() <= 1e-4

@@ -7,11 +7,7 @@ variant the plan can pick is reached: the eight-wave double-buffered walk
 the four-wave walks (vector and element paths), one or several segments,
 grouped heads, the fused short-prompt route, bf16, fp32 and FP8 inputs.
 A second draw runs gaussian inputs from a gaussian state and holds every
-path to the floating-point bar on these shapes.  For chunks of 128, whose
-masked scores enter P V as one bf16 value, the ratio bar is not guaranteed
-for arbitrary inputs: where one score term dominates an output, that
-rounding can pass it (the elementwise bound that does hold, for every chunk
-size, is checked in test_precision_gpu.py)."""
+path to the floating-point bar on these shapes."""
 import numpy as np
 import pytest
 import torch

@@ -126,14 +126,17 @@ def gaussian(B, H, T, dk, dv, seed_base, scale, dtype=torch.bfloat16,
     return tuple(out)
 
 
-def integers(B, H, T, dk, dv, seed, lo=-1, hi=1, dtype=torch.bfloat16, device="cpu", Hkv=None):
+def integers(B, H, T, dk, dv, seed, lo=-1, hi=1, dtype=torch.bfloat16, device="cpu", Hkv=None,
+             v_range=None):
     """Q [B,H,T,dk], K, V [B,Hkv,T,*] (Hkv defaults to H) with integer values
-    uniform in [lo, hi], stored in ``dtype``."""
+    uniform in [lo, hi] (V in ``v_range`` = (lo, hi) when given), stored in
+    ``dtype``."""
     g = _gen("cpu", seed)
     Hkv = Hkv or H
+    v_lo, v_hi = v_range if v_range is not None else (lo, hi)
     q = torch.randint(lo, hi + 1, (B, H, T, dk), generator=g).to(dtype)
     k = torch.randint(lo, hi + 1, (B, Hkv, T, dk), generator=g).to(dtype)
-    v = torch.randint(lo, hi + 1, (B, Hkv, T, dv), generator=g).to(dtype)
+    v = torch.randint(v_lo, v_hi + 1, (B, Hkv, T, dv), generator=g).to(dtype)
     return q.to(device), k.to(device), v.to(device)
 
 
