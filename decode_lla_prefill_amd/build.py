@@ -65,6 +65,12 @@ SANITIZE_DIR = os.path.join(ROOT, "_build", "asan")
 CLANGXX = os.environ.get("LLA_CLANGXX", "/opt/rocm/llvm/bin/clang++")
 
 
+def _newest_source() -> float:
+    import glob
+    files = glob.glob(os.path.join(CSRC, "*")) + [os.path.join(ROOT, "include", "lla.h")]
+    return max(os.path.getmtime(f) for f in files)
+
+
 def asan_runtime() -> str:
     """The address-sanitizer runtime of the ROCm clang (to preload into a
     process that loads a sanitized build)."""
@@ -82,7 +88,10 @@ def build_sanitized(out_dir: str = SANITIZE_DIR) -> str:
     build.  For CPU tests of the host-side paths, run with asan_runtime()
     preloaded; device code is not sanitized."""
     os.makedirs(out_dir, exist_ok=True)
-    build()  # the kernel objects under BUILD_DIR
+    kernel_objs = [os.path.join(BUILD_DIR, s + ".o") for s in SOURCES if s not in HOST_SOURCES]
+    stale = any(not os.path.exists(o) or os.path.getmtime(o) < _newest_source() for o in kernel_objs)
+    if stale:
+        build()  # the kernel objects under BUILD_DIR
     objs = []
     for src in HOST_SOURCES:
         obj = os.path.join(out_dir, src + ".o")
@@ -94,7 +103,7 @@ def build_sanitized(out_dir: str = SANITIZE_DIR) -> str:
         if r.returncode != 0:
             raise RuntimeError("sanitized compile failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
         objs.append(obj)
-    objs += [os.path.join(BUILD_DIR, s + ".o") for s in SOURCES if s not in HOST_SOURCES]
+    objs += kernel_objs
     out = os.path.join(out_dir, "liblla.so")
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -30,6 +30,18 @@ Span span(const void* p, int64_t bytes) {
 }
 bool overlap(Span a, Span b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
 
+// The int a caller passed for an enum parameter.  C lets any int through an
+// enum; C++ may assume an enum object holds only values in its enumerators'
+// range, so such a parameter is read as raw bytes and checked before it is
+// used as the enum.
+template <typename E>
+int raw_enum(const E& e) {
+    static_assert(sizeof(E) == sizeof(int), "the C enums are int-sized");
+    int v;
+    memcpy(&v, &e, sizeof v);
+    return v;
+}
+
 int64_t elem_size(lla_dtype dt) { return dt == LLA_FP8_E4M3 ? 1 : (dt == LLA_BF16 ? 2 : 4); }
 bool known_dtype(int dt) { return dt == LLA_BF16 || dt == LLA_F32 || dt == LLA_FP8_E4M3; }
 
@@ -99,14 +111,15 @@ struct PrefillBufs {
 };
 
 lla_status check_prefill(const PrefillBufs& b, bool needs_q, bool needs_kv, bool needs_s,
-                         bool needs_o, bool needs_ws, lla_dtype dt, int64_t B, Heads h,
+                         bool needs_o, bool needs_ws, int dt_raw, int64_t B, Heads h,
                          int64_t T, int64_t dk, int64_t dv, int64_t C, lla::PrefillPlan& plan) {
     lla_status st = check_heads(h);
     if (st != LLA_OK) return st;
     st = check_sizes(B, h.q, T, dk, dv, C);
     if (st != LLA_OK) return st;
-    st = check_dtype((int)dt, C);
+    st = check_dtype(dt_raw, C);
     if (st != LLA_OK) return st;
+    const lla_dtype dt = (lla_dtype)dt_raw;
     plan = make_plan(dt, B, h, T, dk, dv, C);
     const bool empty = T == 0;
     // Pointers: Q/K/V/O may be NULL only for an empty prompt; S never.
@@ -148,12 +161,14 @@ lla_status check_prefill(const PrefillBufs& b, bool needs_q, bool needs_kv, bool
 extern "C" {
 
 const char* lla_status_string(lla_status s) {
-    switch (s) {
+    switch (raw_enum(s)) {
         case LLA_OK: return "ok";
         case LLA_ERR_NULL: return "a required pointer is NULL";
         case LLA_ERR_SHAPE: return "a size is out of range";
         case LLA_ERR_DTYPE: return "unknown dtype";
-        case LLA_ERR_UNSUPPORTED: return "unsupported combination (fp32 inputs need C <= 64)";
+        case LLA_ERR_UNSUPPORTED:
+            return "unsupported request (fp32 inputs with C > 64, a grouped decode shape other than "
+                   "dk = dv in {64, 128} with at most 16 query heads per group, or unknown option bits)";
         case LLA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
         case LLA_ERR_ALIAS: return "an output overlaps another buffer";
         case LLA_ERR_WORKSPACE: return "workspace missing or too small";
@@ -194,7 +209,8 @@ lla_status lla_prefill_segment_states(const void* K, const void* V, lla_dtype dt
                                       void* workspace, size_t workspace_bytes, void* stream) {
     lla::PrefillPlan p;
     PrefillBufs b{nullptr, K, V, nullptr, nullptr, nullptr, workspace, workspace_bytes};
-    lla_status st = check_prefill(b, false, true, false, false, true, dtype, B, Heads{H, H}, T, dk, dv, C, p);
+    lla_status st = check_prefill(b, false, true, false, false, true, raw_enum(dtype), B, Heads{H, H}, T, dk,
+                                  dv, C, p);
     if (st != LLA_OK || T == 0) return st;
     return device_status(lla::launch_segment_states(p, K, V, (float*)workspace, (hipStream_t)stream));
 }
@@ -204,7 +220,7 @@ lla_status lla_prefill_state_scan(const float* S, int64_t B, int64_t H, int64_t 
                                   void* stream) {
     lla::PrefillPlan p;
     PrefillBufs b{nullptr, nullptr, nullptr, S, nullptr, nullptr, workspace, workspace_bytes};
-    lla_status st = check_prefill(b, false, false, true, false, true, LLA_BF16, B, Heads{H, H}, T, dk,
+    lla_status st = check_prefill(b, false, false, true, false, true, (int)LLA_BF16, B, Heads{H, H}, T, dk,
                                   dv, C, p);
     if (st != LLA_OK || T == 0) return st;
     return device_status(lla::launch_state_scan(p, S, (float*)workspace, (hipStream_t)stream));
@@ -216,7 +232,8 @@ lla_status lla_prefill_chunks(const void* Q, const void* K, const void* V, lla_d
                               void* stream) {
     lla::PrefillPlan p;
     PrefillBufs b{Q, K, V, nullptr, S, O, workspace, workspace_bytes};
-    lla_status st = check_prefill(b, true, true, true, true, true, dtype, B, Heads{H, H}, T, dk, dv, C, p);
+    lla_status st = check_prefill(b, true, true, true, true, true, raw_enum(dtype), B, Heads{H, H}, T, dk,
+                                  dv, C, p);
     if (st != LLA_OK || T == 0) return st;
     return device_status(lla::launch_chunk_walk(p, Q, K, V, S, O, (float*)workspace, (hipStream_t)stream));
 }
@@ -225,15 +242,16 @@ lla_status lla_prefill_chunks(const void* Q, const void* K, const void* V, lla_d
 
 namespace {
 
-lla_status prefill_impl(const void* Q, const void* K, const void* V, lla_dtype dtype, int64_t B,
+lla_status prefill_impl(const void* Q, const void* K, const void* V, int dt_raw, int64_t B,
                         Heads h, int64_t T, int64_t dk, int64_t dv, int64_t C, unsigned flags,
                         float* S, float* O, void* workspace, size_t workspace_bytes, void* stream) {
     if (flags & ~(unsigned)LLA_PREFILL_ZERO_STATE) return LLA_ERR_UNSUPPORTED;
     const bool zero = (flags & LLA_PREFILL_ZERO_STATE) != 0;
     lla::PrefillPlan p;
     PrefillBufs b{Q, K, V, nullptr, S, O, workspace, workspace_bytes};
-    lla_status st = check_prefill(b, true, true, true, true, true, dtype, B, h, T, dk, dv, C, p);
+    lla_status st = check_prefill(b, true, true, true, true, true, dt_raw, B, h, T, dk, dv, C, p);
     if (st != LLA_OK) return st;
+    const lla_dtype dtype = (lla_dtype)dt_raw;  // checked
     hipStream_t s = (hipStream_t)stream;
     if (T == 0)  // S_T = S_0: untouched, or zero for a fresh prompt
         return zero ? device_status(lla::launch_fill_zero(S, p.BH * dk * dv, s)) : LLA_OK;
@@ -249,13 +267,14 @@ lla_status prefill_impl(const void* Q, const void* K, const void* V, lla_dtype d
     return device_status(lla::launch_chunk_walk(p, Q, K, V, S, O, ws, s));
 }
 
-lla_status decode_impl(const void* q, const void* k, const void* v, lla_dtype dtype, int64_t B,
+lla_status decode_impl(const void* q, const void* k, const void* v, int dt_raw, int64_t B,
                        Heads h, int64_t dk, int64_t dv, float* S, float* o, void* stream) {
     lla_status st = check_heads(h);
     if (st != LLA_OK) return st;
     st = check_sizes(B, h.q, 1, dk, dv, -1);
     if (st != LLA_OK) return st;
-    if (!known_dtype(dtype)) return LLA_ERR_DTYPE;
+    if (!known_dtype(dt_raw)) return LLA_ERR_DTYPE;
+    const lla_dtype dtype = (lla_dtype)dt_raw;
     const int64_t group = h.q / h.kv;
     if (group > 1 && !lla::decode_group_fit(group, (int)dk, (int)dv)) return LLA_ERR_UNSUPPORTED;
     if (!q || !k || !v || !S || !o) return LLA_ERR_NULL;
@@ -280,14 +299,14 @@ extern "C" {
 lla_status lla_prefill(const void* Q, const void* K, const void* V, lla_dtype dtype, int64_t B,
                        int64_t H, int64_t T, int64_t dk, int64_t dv, int64_t C, float* S, float* O,
                        void* workspace, size_t workspace_bytes, void* stream) {
-    return prefill_impl(Q, K, V, dtype, B, Heads{H, H}, T, dk, dv, C, 0u, S, O, workspace,
+    return prefill_impl(Q, K, V, raw_enum(dtype), B, Heads{H, H}, T, dk, dv, C, 0u, S, O, workspace,
                         workspace_bytes, stream);
 }
 
 lla_status lla_prefill_gqa(const void* Q, const void* K, const void* V, lla_dtype dtype, int64_t B,
                            int64_t Hq, int64_t Hkv, int64_t T, int64_t dk, int64_t dv, int64_t C,
                            float* S, float* O, void* workspace, size_t workspace_bytes, void* stream) {
-    return prefill_impl(Q, K, V, dtype, B, Heads{Hq, Hkv}, T, dk, dv, C, 0u, S, O, workspace,
+    return prefill_impl(Q, K, V, raw_enum(dtype), B, Heads{Hq, Hkv}, T, dk, dv, C, 0u, S, O, workspace,
                         workspace_bytes, stream);
 }
 
@@ -295,20 +314,20 @@ lla_status lla_prefill_ex(const void* Q, const void* K, const void* V, lla_dtype
                           int64_t Hq, int64_t Hkv, int64_t T, int64_t dk, int64_t dv, int64_t C,
                           unsigned flags, float* S, float* O, void* workspace,
                           size_t workspace_bytes, void* stream) {
-    return prefill_impl(Q, K, V, dtype, B, Heads{Hq, Hkv}, T, dk, dv, C, flags, S, O, workspace,
+    return prefill_impl(Q, K, V, raw_enum(dtype), B, Heads{Hq, Hkv}, T, dk, dv, C, flags, S, O, workspace,
                         workspace_bytes, stream);
 }
 
 lla_status lla_decode_step(const void* q, const void* k, const void* v, lla_dtype dtype,
                            int64_t B, int64_t H, int64_t dk, int64_t dv, float* S, float* o,
                            void* stream) {
-    return decode_impl(q, k, v, dtype, B, Heads{H, H}, dk, dv, S, o, stream);
+    return decode_impl(q, k, v, raw_enum(dtype), B, Heads{H, H}, dk, dv, S, o, stream);
 }
 
 lla_status lla_decode_step_gqa(const void* q, const void* k, const void* v, lla_dtype dtype,
                                int64_t B, int64_t Hq, int64_t Hkv, int64_t dk, int64_t dv, float* S,
                                float* o, void* stream) {
-    return decode_impl(q, k, v, dtype, B, Heads{Hq, Hkv}, dk, dv, S, o, stream);
+    return decode_impl(q, k, v, raw_enum(dtype), B, Heads{Hq, Hkv}, dk, dv, S, o, stream);
 }
 
 }  // extern "C"
