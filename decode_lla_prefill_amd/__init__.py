@@ -23,7 +23,8 @@ __all__ = [
     "LlaError", "library", "library_path", "state_init", "prefill", "decode_step",
     "prefill_workspace_size", "prefill_gqa_workspace_size", "prefill_segment_chunks",
     "prefill_segment_states",
-    "prefill_state_scan", "prefill_chunks", "PreparedPrefill", "PreparedDecode", "EXPORTS",
+    "prefill_state_scan", "prefill_chunks", "prefill_noalloc", "PreparedPrefill", "PreparedDecode",
+    "EXPORTS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -36,7 +37,7 @@ EXPORTS = ("lla_status_string", "lla_last_device_error", "lla_state_init",
            "lla_prefill_segment_chunks", "lla_prefill_workspace_size", "lla_prefill",
            "lla_prefill_segment_states", "lla_prefill_state_scan", "lla_prefill_chunks",
            "lla_decode_step", "lla_prefill_gqa_workspace_size", "lla_prefill_gqa",
-           "lla_decode_step_gqa", "lla_prefill_ex")
+           "lla_decode_step_gqa", "lla_prefill_ex", "lla_prefill_noalloc")
 PREFILL_ZERO_STATE = 1  # lla_prefill_ex: start from S_0 = 0 without reading S
 
 _BF16, _F32, _FP8 = 0, 1, 2
@@ -49,7 +50,7 @@ class LlaError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
         msg = _lib.lla_status_string(status).decode() if _lib is not None else str(status)
-        if status == 8 and _lib is not None:
+        if status == 8 and _lib is not None:  # LLA_ERR_DEVICE
             msg += " (hipError %d)" % _lib.lla_last_device_error()
         super().__init__("%s: %s (status %d)" % (what, msg, status))
 
@@ -94,6 +95,9 @@ def library():
         lib.lla_prefill_ex.argtypes = [vp, vp, vp, ci, i64, i64, i64, i64, i64, i64, i64,
                                        ctypes.c_uint, vp, vp, vp, sz, vp]
         lib.lla_prefill_ex.restype = st
+        lib.lla_prefill_noalloc.argtypes = [vp, vp, vp, ci, i64, i64, i64, i64, i64, i64, i64,
+                                            ctypes.c_uint, vp, vp, vp]
+        lib.lla_prefill_noalloc.restype = st
         _lib = lib
     return _lib
 
@@ -234,6 +238,22 @@ def prefill(q, k, v, state, chunk: int, out=None, workspace=None, zero_state: bo
         _check(lib.lla_prefill_gqa(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, Hq, Hkv, T, dk, dv,
                                    chunk, _ptr(state), _ptr(out), _ptr(ws), ws_bytes, _stream(q)),
                "lla_prefill_gqa")
+    return out
+
+
+def prefill_noalloc(q, k, v, state, chunk: int, out=None, zero_state: bool = False):
+    """:func:`prefill` through lla_prefill_noalloc: the library takes the
+    workspace from its static per-device array instead of the caller, so the
+    call allocates nothing when ``out`` is given.  Calls that overlap in time
+    on one device race on that array."""
+    lib = library()
+    B, Hq, Hkv, T, dk, dv = _qkv_shape(q, k, v)
+    _state_check(state, B, Hkv, dk, dv)
+    out = _out(out, (B, Hq, T, dv), q.device)
+    _same_device(q.device, state=state, out=out)
+    _check(lib.lla_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, Hq, Hkv, T, dk, dv, chunk,
+                                   PREFILL_ZERO_STATE if zero_state else 0, _ptr(state), _ptr(out),
+                                   _stream(q)), "lla_prefill_noalloc")
     return out
 
 

@@ -21,7 +21,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "liblla.so")
 BUILD_DIR = os.path.join(ROOT, "_build", "lla")
 
-SOURCES = ["lla_abi.cpp", "lla_plan.cpp", "lla_prefill.hip", "lla_decode.hip"]
+SOURCES = ["lla_abi.cpp", "lla_plan.cpp", "lla_prefill.hip", "lla_decode.hip", "lla_noalloc.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

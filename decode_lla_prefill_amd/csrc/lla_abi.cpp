@@ -173,6 +173,7 @@ const char* lla_status_string(lla_status s) {
         case LLA_ERR_ALIAS: return "an output overlaps another buffer";
         case LLA_ERR_WORKSPACE: return "workspace missing or too small";
         case LLA_ERR_DEVICE: return "a HIP call failed";
+        case LLA_ERR_SCRATCH: return "the shape needs more workspace than the static scratch array holds";
     }
     return "unknown status";
 }
@@ -316,6 +317,28 @@ lla_status lla_prefill_ex(const void* Q, const void* K, const void* V, lla_dtype
                           size_t workspace_bytes, void* stream) {
     return prefill_impl(Q, K, V, raw_enum(dtype), B, Heads{Hq, Hkv}, T, dk, dv, C, flags, S, O, workspace,
                         workspace_bytes, stream);
+}
+
+lla_status lla_prefill_noalloc(const void* Q, const void* K, const void* V, lla_dtype dtype, int64_t B,
+                               int64_t Hq, int64_t Hkv, int64_t T, int64_t dk, int64_t dv, int64_t C,
+                               unsigned flags, float* S, float* O, void* stream) {
+    // Everything but the workspace is checked first (no HIP call), then the
+    // workspace the plan needs against the static array's size.
+    if (flags & ~(unsigned)LLA_PREFILL_ZERO_STATE) return LLA_ERR_UNSUPPORTED;
+    lla::PrefillPlan p;
+    PrefillBufs b{Q, K, V, nullptr, S, O, nullptr, 0};
+    lla_status st = check_prefill(b, true, true, true, true, false, raw_enum(dtype), B, Heads{Hq, Hkv}, T, dk,
+                                  dv, C, p);
+    if (st != LLA_OK) return st;
+    const size_t need = ws_bytes_for(p);
+    if (need > lla::kNoAllocScratchBytes) return LLA_ERR_SCRATCH;
+    float* ws = nullptr;
+    if (T > 0 && need > 0) {
+        st = device_status(lla::noalloc_scratch((hipStream_t)stream, &ws));
+        if (st != LLA_OK) return st;
+    }
+    return prefill_impl(Q, K, V, raw_enum(dtype), B, Heads{Hq, Hkv}, T, dk, dv, C, flags, S, O, ws,
+                        ws ? lla::kNoAllocScratchBytes : 0, stream);
 }
 
 lla_status lla_decode_step(const void* q, const void* k, const void* v, lla_dtype dtype,

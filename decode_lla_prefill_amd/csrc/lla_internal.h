@@ -76,4 +76,11 @@ bool decode_group_fit(int64_t group, int dk, int dv);
 hipError_t launch_decode_group(lla_dtype dtype, const void* q, const void* k, const void* v,
                                int64_t BHkv, int group, int d, float* S, float* o, hipStream_t st);
 
+// lla_prefill_noalloc: the prefill workspace in a static device array of
+// this many bytes per device (lla_noalloc.hip); *out = its address on the
+// stream's device (the current device for the NULL stream), looked up on the
+// first call per device.
+constexpr size_t kNoAllocScratchBytes = LLA_NOALLOC_SCRATCH_BYTES;
+hipError_t noalloc_scratch(hipStream_t stream, float** out);
+
 }  // namespace lla

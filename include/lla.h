@@ -88,7 +88,9 @@ typedef enum {
     LLA_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned */
     LLA_ERR_ALIAS = 6,       /* an output overlaps an input, another output or the workspace */
     LLA_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than lla_prefill_workspace_size() */
-    LLA_ERR_DEVICE = 8       /* a HIP call failed (see lla_last_device_error) */
+    LLA_ERR_DEVICE = 8,      /* a HIP call failed (see lla_last_device_error) */
+    LLA_ERR_SCRATCH = 9      /* lla_prefill_noalloc: the shape needs more workspace than
+                                LLA_NOALLOC_SCRATCH_BYTES */
 } lla_status;
 
 typedef enum {
@@ -248,6 +250,36 @@ lla_status lla_prefill_ex(const void *Q, const void *K, const void *V, lla_dtype
                           int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t dk,
                           int64_t dv, int64_t C, unsigned flags, float *S, float *O,
                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * lla_prefill_ex without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The call itself allocates nothing and
+ * calls no allocating routine.  The workspace lla_prefill_ex would take
+ * (lla_prefill_gqa_workspace_size bytes) is a static device array of
+ * LLA_NOALLOC_SCRATCH_BYTES inside the library, one per device, held from the
+ * first call on that device until the process ends; that first call looks up
+ * its address (hipGetSymbolAddress, with the stream's device made current for
+ * the lookup).  The stream's device is the one used (the current device for
+ * the NULL stream).
+ *
+ * Every call on a device shares that device's array, and it keeps the last
+ * call's contents: nothing in it needs to start at zero (each call writes
+ * every state it reads).  Calls that overlap in time on one device -- on two
+ * streams, or from two host threads -- race on the array; serialise them.
+ * A graph that captures this call keeps the array's address.
+ *
+ * Errors as lla_prefill_ex; a shape whose workspace exceeds
+ * LLA_NOALLOC_SCRATCH_BYTES (for example more than 512 key/value heads x
+ * segments at d_k = d_v = 128) returns LLA_ERR_SCRATCH before any HIP call.
+ * Results equal those of lla_prefill_ex on the same arguments bit for bit.
+ */
+#define LLA_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u)
+
+lla_status lla_prefill_noalloc(const void *Q, const void *K, const void *V, lla_dtype dtype,
+                               int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t dk,
+                               int64_t dv, int64_t C, unsigned flags, float *S, float *O,
+                               void *stream);
 
 /*
  * One decode step with shared-state heads: q: [B][Hq][dk], k: [B][Hkv][dk],

@@ -17,7 +17,7 @@ import decode_lla_prefill_amd as lla
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "lla.h")
 
-OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_ALIGN, E_ALIAS, E_WS, E_DEV = range(9)
+OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_ALIGN, E_ALIAS, E_WS, E_DEV, E_SCRATCH = range(10)
 BF16, F32 = 0, 1
 i64, vp, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
 
@@ -56,6 +56,8 @@ def lib():
     L.lla_prefill_gqa.argtypes = [vp, vp, vp, ctypes.c_int] + [i64] * 7 + [vp, vp, vp, sz, vp]
     L.lla_decode_step_gqa.restype = ctypes.c_int
     L.lla_decode_step_gqa.argtypes = [vp, vp, vp, ctypes.c_int] + [i64] * 5 + [vp, vp, vp]
+    L.lla_prefill_noalloc.restype = ctypes.c_int
+    L.lla_prefill_noalloc.argtypes = [vp, vp, vp, ctypes.c_int] + [i64] * 7 + [ctypes.c_uint, vp, vp, vp]
     L.lla_prefill_ex.restype = ctypes.c_int
     L.lla_prefill_ex.argtypes = ([vp, vp, vp, ctypes.c_int] + [i64] * 7 + [ctypes.c_uint] +
                                  [vp, vp, vp, sz, vp])
@@ -80,7 +82,7 @@ def test_binding_exports_match_header():
 
 def test_status_strings(lib):
     seen = set()
-    for code in range(9):
+    for code in range(10):
         s = lib.lla_status_string(code)
         assert s and s not in seen
         seen.add(s)
@@ -320,3 +322,55 @@ def test_prefill_ex_checks_like_prefill(lib, change, expect, flags):
 
 def test_prefill_ex_head_counts(lib):
     assert lib.lla_prefill_ex(*_ex_args(Bufs(), 4, 3, ZERO_STATE)) == E_SHAPE
+
+
+# lla_prefill_noalloc: the checks of lla_prefill_ex (no workspace argument),
+# then the workspace the shape needs against the library's static array.
+def _noalloc_args(b, Hq, Hkv, flags):
+    return (b.q, b.k, b.v, b.dtype, b.B, Hq, Hkv, b.T, b.dk, b.dv, b.C, flags, b.S, b.O, None)
+
+
+def _scratch_bytes():
+    text = open(HEADER).read()
+    m = re.search(r"#define LLA_NOALLOC_SCRATCH_BYTES \((\d+)u \* 1024u \* 1024u\)", text)
+    return int(m.group(1)) << 20
+
+
+@pytest.mark.parametrize("change,expect", [
+    (dict(q=None), E_NULL), (dict(S=None), E_NULL), (dict(B=0), E_SHAPE), (dict(dtype=7), E_DTYPE),
+    (dict(O=5 * A + 4), E_ALIGN), (dict(O=A + 64), E_ALIAS), (dict(dtype=F32, C=128), E_UNSUP),
+])
+@pytest.mark.parametrize("flags", [0, ZERO_STATE])
+def test_prefill_noalloc_checks_like_prefill_ex(lib, change, expect, flags):
+    b = Bufs()
+    for key, val in change.items():
+        setattr(b, key, val)
+    assert lib.lla_prefill_noalloc(*_noalloc_args(b, 2, 2, flags)) == expect
+    assert lib.lla_prefill_ex(*_ex_args(b, 2, 2, flags)) == expect
+
+
+def test_prefill_noalloc_rejects_unknown_flags(lib):
+    assert lib.lla_prefill_noalloc(*_noalloc_args(Bufs(), 2, 2, 2)) == E_UNSUP
+
+
+def test_prefill_noalloc_rejects_a_workspace_beyond_the_static_array(lib):
+    # 5 x 128 key/value heads, one 64 KiB state each (grouped heads start from
+    # the workspace): 40 MiB, beyond the 32 MiB array; refused before any HIP call
+    b = Bufs(B=5, T=64, dk=128, dv=128)
+    need = lib.lla_prefill_gqa_workspace_size(5, 256, 128, 64, 128, 128, 64)
+    assert need > _scratch_bytes() == 32 << 20
+    assert lib.lla_prefill_noalloc(*_noalloc_args(b, 256, 128, 0)) == E_SCRATCH
+    assert lib.lla_prefill_noalloc(*_noalloc_args(b, 256, 128, ZERO_STATE)) == E_SCRATCH
+
+
+def test_every_multi_head_shape_fits_the_static_array(lib):
+    """With one query head per key/value head the plan keeps about 512 / n_vb
+    segment states in all, so the largest workspace stays below the array: a
+    scan over head counts and lengths at d = 128 and d = 64."""
+    worst = 0
+    for BH in (1, 2, 3, 5, 8, 16, 31, 64, 100, 128, 200, 255, 256, 300, 511, 512, 1000):
+        for T in (1, 64, 65, 200, 1000, 4096, 8192, 65536, 131072):
+            for d in (64, 128):
+                for C in (32, 64, 128):
+                    worst = max(worst, lib.lla_prefill_workspace_size(1, BH, T, d, d, C))
+    assert 0 < worst <= _scratch_bytes()
