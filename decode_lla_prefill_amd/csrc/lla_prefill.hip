@@ -53,7 +53,9 @@ struct WalkCfg {
     //     the 8-byte pairs of Q S;
     //  K, V: 8 (mod 16) dwords -- a transpose read by two 16-lane groups
     //     covers 8 consecutive rows x 32 bytes, on distinct banks;
-    //  P: 4 (mod 8) dwords -- its 8-byte writes and reads are conflict-free.
+    //  P: bf16, 8 (mod 16) dwords, like K and V, for its 16-byte reads (its
+    //     columns are stored in the order of those reads, see p_col); fp32,
+    //     4 (mod 8) dwords -- its 8-byte writes and reads are conflict-free.
     static constexpr int LQ = D + (NATQ ? 16 : (BF ? 8 : 4));
     static constexpr int LK = D + (BF ? 16 : 4);
     static constexpr int LV = BV + (BF ? 16 : 4);
@@ -66,16 +68,26 @@ struct WalkCfg {
     // padded square, which makes room for the low part in the
     // single-buffered walk; one row stride keeps every tile's lane offset
     // the same.
-    static constexpr int PPAD = BF ? 8 : 4;
+    static constexpr int PPAD = BF ? 16 : 4;
     static constexpr int PLD = 32 * (CT / 32 + 1) + PPAD;  // elements per row
     __device__ __host__ static constexpr int p_row0(int it) { return 16 * (it < CT / 32 ? it : CT / 16 - 1 - it); }
     __device__ __host__ static constexpr int p_col0(int it) {
         return it < CT / 32 ? 0 : 32 * ((CT / 16 - 1 - it) / 2 + 1);
     }
+    // Where column col of P sits in its row.  bf16: each 32-column block
+    // holds its columns in the depth order of the P V operand, which the
+    // transpose read of V fixes (slots 0..3 of lane group g: columns
+    // 4g .. 4g + 3, slots 4..7: 16 + 4g .. 16 + 4g + 3), so that a lane's
+    // operand is one 16-byte read instead of two 8-byte ones; the scores are
+    // still written 4 columns (8 bytes) at a time.  fp32: natural order.
+    __device__ __host__ static constexpr int p_col(int col) {
+        return BF ? (col & ~31) + 8 * ((col & 15) >> 2) + 4 * ((col >> 4) & 1) + (col & 3) : col;
+    }
     // element (row 16 it + r, column col) of P
     __device__ __host__ static constexpr int p_at(int it, int r, int col) {
-        return (p_row0(it) + r) * PLD + p_col0(it) + col;
+        return (p_row0(it) + r) * PLD + p_col0(it) + p_col(col);
     }
+    static constexpr int PG = BF ? 8 : 4;  // p_col(c + 4g) - p_col(c) for c a multiple of 16, per g
     static constexpr int P_ELEMS = CT / 2 * PLD;  // one P tile
     using LQL = PadLayout<LQ>;
     using LKL = PadLayout<LK>;
@@ -401,7 +413,7 @@ __device__ __forceinline__ void chunk_scores(const ScoreTiles<Cf>& st, const T* 
                 if (16 * tjt[m] + 4 * g + r > i) sacc[m][r] = 0.0f;
             // the lane's part of the address, recomputed per chunk rather
             // than one live register per tile
-            const int at = opaque(c16 * Cf::PLD + 4 * g) + Cf::p_at(tit[m], 0, 16 * tjt[m]);
+            const int at = opaque(c16 * Cf::PLD + Cf::PG * g) + Cf::p_at(tit[m], 0, 16 * tjt[m]);
             if constexpr (Cf::SPLITP)
                 lds_store4_split(Ps + at, Ps + Cf::P_ELEMS + at, sacc[m]);
             else
@@ -412,7 +424,7 @@ __device__ __forceinline__ void chunk_scores(const ScoreTiles<Cf>& st, const T* 
     for (int it = 2 * w; it + 1 < Cf::NT; it += 2 * Cf::NW)
 #pragma unroll
         for (int pt = 0; pt < Cf::NP; ++pt)
-            lds_store4(Ps + pt * Cf::P_ELEMS + opaque(c16 * Cf::PLD + 4 * g) + Cf::p_at(it, 0, 16 * (it + 1)),
+            lds_store4(Ps + pt * Cf::P_ELEMS + opaque(c16 * Cf::PLD + Cf::PG * g) + Cf::p_at(it, 0, 16 * (it + 1)),
                        f32x4{0.f, 0.f, 0.f, 0.f});
 }
 
@@ -491,12 +503,11 @@ __device__ __forceinline__ void chunk_output(f32x4 (&Oacc)[Cf::NT][Cf::NVW],
     // hold them through it.
     constexpr bool EARLY_QS = Cf::CT <= 64;
     Fr qb[2][Cf::NT], Shi[2][Cf::NVW], Slo[2][Cf::NVW];
-    auto qs_prologue = [&]() {
+    if constexpr (EARLY_QS) {
         q_slices(qb[0], 0);
 #pragma unroll
         for (int vw = 0; vw < Cf::NVW; ++vw) state_operand<Cf>(Shi[0][vw], Slo[0][vw], Sacc[vw], 0);
-    };
-    if constexpr (EARLY_QS) qs_prologue();
+    }
 
     // All query tiles of the chunk are accumulated side by side (depth
     // outer, tile inner), so consecutive matrix-core ops are independent.
@@ -511,13 +522,18 @@ __device__ __forceinline__ void chunk_output(f32x4 (&Oacc)[Cf::NT][Cf::NVW],
 #pragma unroll
         for (int it = 2 * ts; it < Cf::NT; ++it) {
             const int at = Cf::p_at(it, c16, 32 * ts + 4 * g);
-            const Fr pb = lds_row2(Ps + at, Ps + at + 16);
+            auto p_operand = [&](const T* base) -> Fr {
+                if constexpr (Cf::BF)
+                    return lds_row(base + at);  // slots in storage order (p_col)
+                else
+                    return lds_row2(base + at, base + at + 16);
+            };
+            const Fr pb = p_operand(Ps);
 #pragma unroll
             for (int vw = 0; vw < Cf::NVW; ++vw)
                 if (owns(vw)) Oacc[it][vw] = mma(Vf[vw][ts], pb, Oacc[it][vw]);
             if constexpr (Cf::SPLITP) {  // the low part of P
-                const T* Pl = Ps + Cf::P_ELEMS;
-                const Fr pl = lds_row2(Pl + at, Pl + at + 16);
+                const Fr pl = p_operand(Ps + Cf::P_ELEMS);
 #pragma unroll
                 for (int vw = 0; vw < Cf::NVW; ++vw)
                     if (owns(vw)) Oacc[it][vw] = mma(Vf[vw][ts], pl, Oacc[it][vw]);
@@ -525,7 +541,11 @@ __device__ __forceinline__ void chunk_output(f32x4 (&Oacc)[Cf::NT][Cf::NVW],
         }
     }
     // incoming state read: Q_c S_c
-    if constexpr (!EARLY_QS) qs_prologue();
+    if constexpr (!EARLY_QS) {
+        q_slices(qb[0], 0);
+#pragma unroll
+        for (int vw = 0; vw < Cf::NVW; ++vw) state_operand<Cf>(Shi[0][vw], Slo[0][vw], Sacc[vw], 0);
+    }
 #pragma unroll
     for (int ds = 0; ds < Cf::NDS; ++ds) {
         const int cur = ds & 1, nxt = cur ^ 1;
