@@ -17,7 +17,10 @@ second pass calls the three prefill phases one by one with HIP events
 between them on the launch stream (per-phase times, launch gaps included),
 and a third times back-to-back launches of the dominant kernel, the chunk
 walk, for the roofline.  The decode step is one kernel: HIP events around
-the timed steps give its launch duration.
+the timed steps give its launch time.  Every back-to-back launch also waits
+out the dispatch gap in front of it; the run measures that gap once
+(near-empty launches replayed from a HIP graph) and each roofline takes it
+off, keeping the raw back-to-back figure beside it.
 
 ``roofline.traffic`` is the HBM traffic per launch that the hardware
 counters measured (FETCH_SIZE + WRITE_SIZE, calibrated against a plain
@@ -37,6 +40,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -116,6 +120,81 @@ def _timed(torch, fn, n_steps):
     return time.perf_counter() - t0, e0.elapsed_time(e1) * 1e-3
 
 
+def _step_events(torch, fn, n_steps):
+    """GPU time of each of n_steps calls of fn(i), in ms: one HIP event on the
+    launch stream between consecutive calls (so each interval also holds the
+    gap before its call).  A pass of its own, after the wall-clock one."""
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for i in range(n_steps):
+        fn(i)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return [evs[i].elapsed_time(evs[i + 1]) for i in range(n_steps)]
+
+
+def spread(ms):
+    """Median and spread of per-step times (ms)."""
+    s = sorted(ms)
+    pick = lambda f: s[min(len(s) - 1, int(round(f * (len(s) - 1))))]
+    return {"median_ms": statistics.median(s), "mean_ms": sum(s) / len(s), "min_ms": s[0],
+            "p10_ms": pick(0.1), "p90_ms": pick(0.9), "max_ms": s[-1], "n": len(s),
+            "timing": "HIP events between consecutive steps on the launch stream"}
+
+
+def host_cores():
+    """Threads for the CPU oracle, and the host's core counts.  All cores this
+    process may run on, except where the environment sets a CPU share per
+    process (OMP_NUM_THREADS, as a GPU machine does for its one GPU): more
+    threads than that share would only oversubscribe it."""
+    affinity = len(os.sched_getaffinity(0))
+    share = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    threads = min(affinity, share) if share > 0 else affinity
+    return threads, {"logical_cpus": os.cpu_count(), "cpus_in_affinity": affinity,
+                     "omp_num_threads": share or None,
+                     "why": "all cores in this process's affinity mask, capped by OMP_NUM_THREADS "
+                            "(the CPU share the environment gives this process) when it is set"}
+
+
+def launch_gap_ms(torch, lla, n=64, reps=10):
+    """GPU time per launch of back-to-back launches of an almost empty kernel
+    (lla_state_init on one 4 x 4 state: one workgroup), replayed from a HIP
+    graph so that host launch overhead stays out: the dispatch gap that timing
+    back-to-back launches adds to each kernel, plus that tiny kernel itself."""
+    dev = torch.device("cuda:0")
+    S = torch.empty((1, 1, 4, 4), device=dev)
+    lla.state_init(1, 1, 4, 4, out=S)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n):
+            lla.state_init(1, 1, 4, 4, out=S)
+    for _ in range(3):
+        g.replay()
+    _, secs = _timed(torch, lambda i: g.replay(), reps)
+    del g
+    return secs * 1e3 / (n * reps)
+
+
+def hbm_roofline(kernel, nbytes, b2b_ms, gap_ms, traffic=None, timing="", **extra):
+    """Roofline of an HBM-bound kernel: algorithmic bytes per launch over its
+    launch duration.  b2b_ms is the per-launch time of back-to-back launches
+    between HIP events on the launch stream; each of those launches also
+    waits out the dispatch gap before it, measured separately (launch_gap_ms),
+    so the launch duration is b2b_ms - gap_ms -- what a kernel trace reports
+    for the kernel.  Both raw figures are kept."""
+    ms = b2b_ms - gap_ms
+    r = {"kernel": kernel, "bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+         "unit": "GB/s", "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "traffic": traffic,
+         "algorithmic_bytes": nbytes, "kernel_ms": ms, "kernel_ms_back_to_back": b2b_ms,
+         "launch_gap_ms": gap_ms, "frac_back_to_back": nbytes / (b2b_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+         "timing": timing + "; kernel_ms = kernel_ms_back_to_back - launch_gap_ms"}
+    r.update(extra)
+    return r
+
+
 def measure_peaks(torch):
     """Achievable peaks of this GPU, measured for context beside the published
     ones.  HBM: the best of two plain streams over 1 GiB fp32 (torch's
@@ -178,6 +257,8 @@ def bench_prefill(args, torch, lla, workloads, profiling):
         step(i)
     wall, gpu = _timed(torch, step, args.steps)
     wall_w, gpu_w = _timed(torch, lambda i: sets[0](zero_state=True), args.steps)
+    cold_spread = spread(_step_events(torch, step, args.steps))
+    warm_spread = spread(_step_events(torch, lambda i: sets[0](zero_state=True), args.steps))
 
     # Per-phase durations: the same work with HIP events between the three
     # phases (what lla_prefill enqueues; the state is zeroed by lla_state_init
@@ -214,10 +295,10 @@ def bench_prefill(args, torch, lla, workloads, profiling):
     e1.record(stream)
     torch.cuda.synchronize()
     walk_launch_ms = e0.elapsed_time(e1) / n_walk
+    gap_ms = args.gap_ms
     flops, nbytes = prefill_work(B, H, T, C, d)
     ms_step = wall * 1e3 / args.steps
     walk_ms = sum(phase[2]) / len(phase[2])
-    achieved = nbytes / (walk_launch_ms * 1e-3) / 1e9
     res = {
         "config": {"workload": cfg.name, "B": B, "H": H, "T": T, "C": C, "dk": d, "dv": d,
                    "inputs": "bf16 N(0,1)/sqrt(128), K rows L2-normalised; fp32 state and output",
@@ -227,6 +308,7 @@ def bench_prefill(args, torch, lla, workloads, profiling):
         "value": B * T / (ms_step * 1e-3),
         "ms_per_step": ms_step,
         "gpu_ms_per_step": gpu * 1e3 / args.steps,
+        "step_spread": cold_spread,
         "phase_ms": {"segment_states": sum(phase[0]) / len(phase[0]),
                      "state_scan": sum(phase[1]) / len(phase[1]),
                      "chunk_walk": walk_ms},
@@ -240,17 +322,15 @@ def bench_prefill(args, torch, lla, workloads, profiling):
                                / (ms_step * 1e-3),
                        "bound": "hbm" if nbytes / (PEAK_HBM_GBS * 1e9) > flops / (PEAK_BF16_TFLOPS * 1e12)
                                 else "mfma"},
-        "roofline": {"kernel": "k_chunk_walk_wide<64> (bf16, d=128)", "bound": "hbm",
-                     "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS,
-                     "traffic": profiling.stored_traffic("chunk_walk"),
-                     "algorithmic_bytes": nbytes,
-                     "algorithmic_flops": flops,
-                     "kernel_ms": walk_launch_ms,
-                     "timing": "HIP events around %d back-to-back walk launches" % n_walk},
+        "roofline": hbm_roofline("k_chunk_walk_wide<64> (bf16, d=128)", nbytes, walk_launch_ms, gap_ms,
+                                 profiling.stored_traffic("chunk_walk"),
+                                 "HIP events around %d back-to-back walk launches" % n_walk,
+                                 algorithmic_flops=flops),
         "warm": {"ms_per_step": wall_w * 1e3 / args.steps,
                  "tokens_per_s": B * T / (wall_w / args.steps),
-                 "mfma_frac": flops / (wall_w / args.steps) / (PEAK_BF16_TFLOPS * 1e12)},
+                 "mfma_frac": flops / (wall_w / args.steps) / (PEAK_BF16_TFLOPS * 1e12),
+                 "step_spread": warm_spread,
+                 "cache": "warm: one input/output set repeated (Infinity-Cache resident)"},
     }
     if not args.no_cpu_baseline:
         import oracle
@@ -259,7 +339,7 @@ def bench_prefill(args, torch, lla, workloads, profiling):
         reps, secs = repeat_for(lambda: oracle.recurrence(qc, kc, vc, nthreads=threads),
                                 args.cpu_seconds)
         res["cpu_baseline"] = {"value": reps * B * T / secs, "unit": "tokens/s", "cores": threads,
-                               "kind": "oracle", "seconds": secs,
+                               "host": args.host, "kind": "oracle", "seconds": secs,
                                "sample": "the whole workload (%d heads x %d tokens) %d times over, "
                                          "float64 token-by-token recurrence, one head per thread"
                                          % (B * H, T, reps)}
@@ -303,17 +383,18 @@ def bench_decode(args, torch, lla, workloads, profiling):
     kern_ms = gpu * 1e3 / n
     ms_step = wall * 1e3 / n
     nbytes = decode_bytes(B, H, d)
+    # per-step spread over a second pass (the steps continue from the state)
+    n_sp = min(n, 100)
+    dec_spread = spread(_step_events(torch, lambda i: calls[i](), n_sp))
     res = {
         "workload": cfg.name, "B": B, "H": H, "dk": d, "dv": d, "steps": n,
         "value": n / wall, "unit": "steps/s", "ms_per_step": ms_step,
         "gpu_ms_per_step": gpu * 1e3 / n,
         "tokens_per_s": B * n / wall,
+        "step_spread": dec_spread,
         "hbm_frac": nbytes / (ms_step * 1e-3) / (PEAK_HBM_GBS * 1e9),
-        "roofline": {"kernel": "k_decode_step_sq<bf16,128,512>", "bound": "hbm",
-                     "achieved": nbytes / (kern_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": nbytes / (kern_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                     "traffic": profiling.stored_traffic("decode_step"), "algorithmic_bytes": nbytes,
-                     "kernel_ms": kern_ms, "timing": "HIP events around the timed steps"},
+        "roofline": hbm_roofline("k_decode_step_sq<bf16,128,512>", nbytes, kern_ms, args.gap_ms,
+                                 profiling.stored_traffic("decode_step"), "HIP events around the timed steps"),
     }
     # Short continuations from the same states: T tokens per call through
     # lla_prefill (the fused path for T <= 16).
@@ -346,14 +427,14 @@ def bench_decode(args, torch, lla, workloads, profiling):
                                 args.cpu_seconds)
         head_steps_per_s = reps * nb * H * ns / secs
         res["cpu_baseline"] = {"value": head_steps_per_s / (B * H), "unit": "steps/s",
-                               "cores": threads, "kind": "oracle", "seconds": secs,
+                               "cores": threads, "host": args.host, "kind": "oracle", "seconds": secs,
                                "sample": "%d sequences x %d heads x %d decode steps (float64), "
                                          "%d times over, scaled to the %d states of one step"
                                          % (nb, H, ns, reps, B * H)}
     return res
 
 
-def bench_other_prefills(args, torch, lla, workloads):
+def bench_other_prefills(args, torch, lla, workloads, profiling):
     """The small (B=4, H=8, T=1024, d=64) and the very long (B=1, H=32,
     T=131072, C=128) prefill workloads: cold fresh-prompt steps over rotating
     input sets, back-to-back walks for the walk kernel's roofline, and the
@@ -361,7 +442,10 @@ def bench_other_prefills(args, torch, lla, workloads):
     import oracle
     dev = torch.device("cuda:0")
     out = []
-    for name, rotate, steps in (("prefill_B4_T1024", 16, args.steps), ("prefill_T131072", 2, 3)):
+    walks = {"prefill_B4_T1024": ("k_chunk_walk<bf16,64,64,64> (four waves, d=64, C=64)", "chunk_walk_T1024"),
+             "prefill_T131072": ("k_chunk_walk<bf16,128,128,128> (eight waves, d=128, C=128)",
+                                 "chunk_walk_T131072")}
+    for name, rotate, steps in (("prefill_B4_T1024", 16, args.steps), ("prefill_T131072", 2, 6)):
         cfg = workloads.CONFIGS[name]
         B, H, T, C, d = cfg.B, cfg.H, cfg.T, cfg.C, cfg.dk
         q0, k0, v0 = workloads.config_inputs(cfg, device=dev)
@@ -372,6 +456,9 @@ def bench_other_prefills(args, torch, lla, workloads):
         for i in range(max(2, args.warmup if name == "prefill_B4_T1024" else 1)):
             sets[i % rotate](zero_state=True)
         wall, gpu = _timed(torch, lambda i: sets[i % rotate](zero_state=True), steps)
+        cold_spread = spread(_step_events(torch, lambda i: sets[i % rotate](zero_state=True), steps))
+        wall_w, _ = _timed(torch, lambda i: sets[0](zero_state=True), steps)
+        warm_spread = spread(_step_events(torch, lambda i: sets[0](zero_state=True), steps))
         n_walk = max(steps, 2 * rotate)
         _, walk_s = _timed(torch, lambda i: sets[i % rotate].chunks(), n_walk)
         walk_ms = walk_s * 1e3 / n_walk
@@ -380,14 +467,16 @@ def bench_other_prefills(args, torch, lla, workloads):
         line = {"workload": cfg.name, "B": B, "H": H, "T": T, "C": C, "dk": d, "dv": d,
                 "value": B * T / (wall / steps), "unit": "tokens/s", "steps": steps,
                 "ms_per_step": wall * 1e3 / steps, "gpu_ms_per_step": step_s * 1e3,
+                "step_spread": cold_spread,
+                "warm": {"ms_per_step": wall_w * 1e3 / steps, "tokens_per_s": B * T / (wall_w / steps),
+                         "step_spread": warm_spread,
+                         "cache": "warm: one input/output set repeated"},
                 "mfma_frac": flops / step_s / (PEAK_BF16_TFLOPS * 1e12),
                 "hbm_frac": nbytes / step_s / (PEAK_HBM_GBS * 1e9),
                 "cache": "cold: %d rotating input/output sets of %.0f MB" % (rotate, nbytes / 1e6),
-                "roofline": {"kernel": "k_chunk_walk (four-wave, d=%d, C=%d)" % (d, C), "bound": "hbm",
-                             "achieved": nbytes / (walk_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
-                             "unit": "GB/s", "frac": nbytes / (walk_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                             "algorithmic_bytes": nbytes, "kernel_ms": walk_ms,
-                             "timing": "HIP events around %d back-to-back walk launches" % n_walk}}
+                "roofline": hbm_roofline(walks[name][0], nbytes, walk_ms, args.gap_ms,
+                                         profiling.stored_traffic(walks[name][1]),
+                                         "HIP events around %d back-to-back walk launches" % n_walk)}
         del sets
         torch.cuda.empty_cache()
         if not args.no_cpu_baseline:
@@ -396,7 +485,7 @@ def bench_other_prefills(args, torch, lla, workloads):
             oracle.recurrence(qc, kc, vc, nthreads=args.cpu_threads)
             secs = time.perf_counter() - t0
             line["cpu_baseline"] = {"value": B * T / secs, "unit": "tokens/s", "cores": args.cpu_threads,
-                                    "kind": "oracle", "seconds": secs,
+                                    "host": args.host, "kind": "oracle", "seconds": secs,
                                     "sample": "the whole workload once (%d heads x %d tokens), float64 "
                                               "token-by-token recurrence" % (B * H, T)}
             del qc, kc, vc
@@ -452,12 +541,9 @@ def bench_grouped(args, torch, lla, workloads, profiling):
     dec = {"workload": cfg.name, "B": B, "Hq": H, "Hkv": Hkv, "dk": d, "dv": d, "steps": n,
            "value": n / wall, "unit": "steps/s", "ms_per_step": wall * 1e3 / n,
            "gpu_ms_per_step": kern_ms, "tokens_per_s": B * n / wall,
-           "roofline": {"kernel": "k_decode_group<bf16,128,512>", "bound": "hbm",
-                        "achieved": nbytes / (kern_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
-                        "unit": "GB/s", "frac": nbytes / (kern_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                        "traffic": profiling.stored_traffic("decode_group"),
-                        "algorithmic_bytes": nbytes, "kernel_ms": kern_ms,
-                        "timing": "HIP events around the timed steps, cycling over 3 state sets"}}
+           "roofline": hbm_roofline("k_decode_group<bf16,128,512>", nbytes, kern_ms, args.gap_ms,
+                                    profiling.stored_traffic("decode_group"),
+                                    "HIP events around the timed steps, cycling over 3 state sets")}
     # Short continuations with shared-state heads: T tokens per call through
     # lla_prefill_gqa (fused grouped decode steps while T * G <= 64), from
     # the cycled state sets.
@@ -508,11 +594,9 @@ def bench_fp8(args, torch, lla, workloads, profiling):
            "ms_per_step": wall * 1e3 / args.steps, "gpu_ms_per_step": step_s * 1e3,
            "mfma_frac": flops / step_s / (PEAK_BF16_TFLOPS * 1e12),
            "hbm_frac": nbytes / step_s / (PEAK_HBM_GBS * 1e9),
-           "roofline": {"kernel": "k_chunk_walk_wide<64, fp8e4m3>", "bound": "hbm",
-                        "achieved": nbytes / (walk_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
-                        "unit": "GB/s", "frac": nbytes / (walk_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                        "traffic": None, "algorithmic_bytes": nbytes, "kernel_ms": walk_ms,
-                        "timing": "HIP events around %d back-to-back walk launches" % n_walk},
+           "roofline": hbm_roofline("k_chunk_walk_wide<64, fp8e4m3>", nbytes, walk_ms, args.gap_ms,
+                                    profiling.stored_traffic("chunk_walk_fp8"),
+                                    "HIP events around %d back-to-back walk launches" % n_walk),
            "timing": "HIP events around the timed steps (fresh-prompt lla_prefill_ex), "
                      "%d rotating input sets" % len(sets)}
     del sets, q0, k0, v0
@@ -533,11 +617,8 @@ def bench_fp8(args, torch, lla, workloads, profiling):
     dec = {"workload": cfg.name, "B": B, "H": H, "dk": d, "dv": d, "steps": n,
            "value": n / wall, "unit": "steps/s", "ms_per_step": wall * 1e3 / n,
            "gpu_ms_per_step": kern_ms, "tokens_per_s": B * n / wall,
-           "roofline": {"kernel": "k_decode_step_sq<fp8e4m3,128,512>", "bound": "hbm",
-                        "achieved": nbytes / (kern_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
-                        "unit": "GB/s", "frac": nbytes / (kern_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                        "traffic": None, "algorithmic_bytes": nbytes, "kernel_ms": kern_ms,
-                        "timing": "HIP events around the timed steps"}}
+           "roofline": hbm_roofline("k_decode_step_sq<fp8e4m3,128,512>", nbytes, kern_ms, args.gap_ms,
+                                    None, "HIP events around the timed steps")}
     del calls, qd, kd, vd, S
     torch.cuda.empty_cache()
     return {"prefill": pre, "decode": dec}
@@ -551,7 +632,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=512)
     ap.add_argument("--rotate", type=int, default=4, help="input/output sets cycled (cold cache)")
     ap.add_argument("--prefill-config", default="prefill_T8192")
-    ap.add_argument("--cpu-threads", type=int, default=min(16, os.cpu_count() or 1))
+    ap.add_argument("--cpu-threads", type=int, default=None,
+                    help="oracle threads (default: every core this process may use, see host_cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum oracle time of each CPU baseline (the sample is repeated)")
@@ -560,6 +642,9 @@ def main():
     ap.add_argument("--skip-other", action="store_true", help="skip the B=4 T=1024 and T=131072 prefills")
     ap.add_argument("--skip-fp8", action="store_true")
     args = ap.parse_args()
+    threads, args.host = host_cores()
+    if args.cpu_threads is None:
+        args.cpu_threads = threads
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -577,6 +662,7 @@ def main():
         sys.exit(1)
     lla.library()
     torch.cuda.set_device(0)
+    args.gap_ms = launch_gap_ms(torch, lla)
 
     pre = bench_prefill(args, torch, lla, workloads, profiling)
     line = {
@@ -584,19 +670,23 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": pre["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic", "config": pre["config"], "head_tokens_per_s": pre["head_tokens_per_s"],
-        "tflops": pre["tflops"], "mfma_frac": pre["mfma_frac"],
+        "tflops": pre["tflops"], "mfma_frac": pre["mfma_frac"], "launch_gap_ms": args.gap_ms,
         "hbm_gbs": pre["hbm_gbs"], "attainable": pre["attainable"],
         "gpu_ms_per_step": pre["gpu_ms_per_step"],
         "phase_ms": pre["phase_ms"], "roofline": pre["roofline"], "warm": pre["warm"],
+        "step_spread": pre["step_spread"],
         "timing": "value and ms_per_step: wall clock over the timed steps (synchronised on both "
-                  "sides); gpu_ms_per_step: HIP events around them; phase_ms: HIP events "
-                  "between the phases in a second pass of the same steps (launch gaps "
-                  "included); roofline kernel_ms: HIP events around back-to-back launches",
+                  "sides); gpu_ms_per_step: HIP events around them; step_spread: a HIP event "
+                  "between consecutive steps in a pass of its own (median, p10/p90, min/max); "
+                  "phase_ms: HIP events between the phases in a second pass of the same steps "
+                  "(launch gaps included); roofline kernel_ms: HIP events around back-to-back "
+                  "launches, less the launch gap (back-to-back near-empty launches replayed from "
+                  "a HIP graph), which every back-to-back launch also waits out",
     }
     if "cpu_baseline" in pre:
         line["cpu_baseline"] = pre["cpu_baseline"]
     if not args.skip_other:
-        line["other_prefills"] = bench_other_prefills(args, torch, lla, workloads)
+        line["other_prefills"] = bench_other_prefills(args, torch, lla, workloads, profiling)
     if not args.skip_decode:
         line["decode"] = bench_decode(args, torch, lla, workloads, profiling)
     if not args.skip_grouped:

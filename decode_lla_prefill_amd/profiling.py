@@ -1,13 +1,12 @@
-"""Kernel runs for hardware-counter passes, and summaries of rocprofv3 output.
+"""Kernel runs for rocprofv3 passes, and summaries of rocprofv3 output.
 
-    python -m decode_lla_prefill_amd.profiling run [--launches N]
-        On cuda:0: N prefill steps of the T=8192 workload (B=1, H=16, C=64,
-        d=128; state init and the three phases, over rotating input sets),
-        N decode steps of the 256 x 32 x 128 x 128 state, N grouped decode
-        steps (256 sequences, 32 query heads on 8 key/value heads, three
-        rotating state sets), and N device-to-device copies of 1 GiB, the
-        reference of known size for the HBM byte counters.  Meant to run
-        under ``rocprofv3 --pmc``.
+    python -m decode_lla_prefill_amd.profiling run [--launches N] [--workloads W,W,...]
+        On cuda:0, for each workload W (default: every key of WORKLOADS) N
+        steps over rotating input sets: fresh-prompt prefills (the
+        per-segment K^T V, the segment scan and the chunk walk, as the
+        benchmark times them) or decode steps.  Then N device-to-device copies
+        of 1 GiB, the reference of known size for the HBM byte counters.
+        Meant to run under ``rocprofv3 --pmc`` or ``--kernel-trace``.
 
     python -m decode_lla_prefill_amd.profiling stats OUT_DIR
         Per-kernel launch durations from a ``rocprofv3 --kernel-trace --stats
@@ -15,12 +14,19 @@
         the trace split by grid size (one kernel can run on several shapes).
 
     python -m decode_lla_prefill_amd.profiling traffic KERNEL FETCH_DIR WRITE_DIR
-        HBM bytes per launch of KERNEL (a key of KERNELS) from a
-        FETCH_SIZE pass and a WRITE_SIZE pass of ``run``: each counter is
-        scaled by what it reads for the 1 GiB copy, whose true traffic is
-        1 GiB read and 1 GiB written.  Prints ``key = value`` lines; bench.py
-        reads ``hbm_bytes_per_launch`` while ``kernel_source_sha`` still
-        matches the kernel's sources.
+        HBM bytes per launch of KERNEL (a key of KERNELS) from a FETCH_SIZE
+        pass and a WRITE_SIZE pass of ``run``: each counter is scaled by what
+        it reads for the 1 GiB copy, whose true traffic is 1 GiB read and
+        1 GiB written.  Prints ``key = value`` lines; bench.py reads
+        ``hbm_bytes_per_launch`` while ``kernel_source_sha`` still matches the
+        kernel's sources.
+
+    python -m decode_lla_prefill_amd.profiling counters KERNEL DIR [DIR ...] [--duration-us T]
+        Per-dispatch means of every counter the ``--pmc`` directories hold for
+        KERNEL, and what follows from them: MFMA utilisation (rocprofiler's
+        MfmaUtil), the executed bf16 matrix-core flops (MfmaFlopsBF16) and,
+        given the kernel's duration, their rate against the bf16 peak; the
+        LDS and issue counters as shares of the wave cycles.
 """
 from __future__ import annotations
 
@@ -40,16 +46,44 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 COPY_BYTES = 1 << 30
 
-# measured kernel -> (name fragment in the trace, launch grid in threads of
-# the bench workload, counter summary file, sources that define the kernel)
+# The workloads ``run`` can drive (keys of workloads.CONFIGS).
+WORKLOADS = ("prefill_T8192", "prefill_T8192_fp8", "prefill_B4_T1024", "prefill_T131072",
+             "decode_B256", "decode_B256_gqa")
+
+# measured kernel -> (name fragments as the trace shows them (mangled or
+# demangled), launch grid in threads of its workload, counter summary file,
+# sources that define the kernel, workload).  Grids follow from the plan
+# (tests/test_profiling_host.py recomputes them).
 KERNELS = {
-    "chunk_walk": ("k_chunk_walk", 16 * 16 * 2 * 256, "chunk_walk_T8192_traffic.txt",
-                   ("lla_prefill.hip", "lla_device.h")),
-    "decode_step": ("k_decode_step", 256 * 32 * 512, "decode_step_B256_H32_traffic.txt",
-                    ("lla_decode.hip", "lla_device.h")),
-    "decode_group": ("k_decode_group", 256 * 8 * 512, "decode_group_B256_Hq32_Hkv8_traffic.txt",
-                     ("lla_decode.hip", "lla_device.h")),
+    "chunk_walk": (("k_chunk_walk_wideILi64EDF16b", "k_chunk_walk_wide<64, __bf16>"), 16 * 16 * 512,
+                   "chunk_walk_T8192_traffic.txt", ("lla_prefill.hip", "lla_device.h"), "prefill_T8192"),
+    "segment_states": (("k_segment_states_wideILi64EDF16b", "k_segment_states_wide<64, __bf16>"),
+                       16 * 15 * 512, "segment_states_T8192_traffic.txt",
+                       ("lla_prefill.hip", "lla_device.h"), "prefill_T8192"),
+    "state_scan": (("k_state_scan",), 16 * 16 * 256, "state_scan_T8192_traffic.txt",
+                   ("lla_prefill.hip", "lla_device.h"), "prefill_T8192"),
+    "chunk_walk_fp8": (("k_chunk_walk_wideILi64ENS_7fp8e4m3", "k_chunk_walk_wide<64, lla::fp8e4m3>"),
+                       16 * 16 * 512, "chunk_walk_T8192_fp8_traffic.txt",
+                       ("lla_prefill.hip", "lla_device.h"), "prefill_T8192_fp8"),
+    "chunk_walk_T1024": (("k_chunk_walkIDF16bLi64ELi64ELi64ELb1ELi4E", "k_chunk_walk<__bf16, 64, 64, 64, true, 4>"),
+                         32 * 16 * 256, "chunk_walk_B4_T1024_traffic.txt",
+                         ("lla_prefill.hip", "lla_device.h"), "prefill_B4_T1024"),
+    "chunk_walk_T131072": (("k_chunk_walkIDF16bLi128ELi128ELi128ELb1ELi8E",
+                            "k_chunk_walk<__bf16, 128, 128, 128, true, 8>"),
+                           32 * 8 * 512, "chunk_walk_T131072_traffic.txt",
+                           ("lla_prefill.hip", "lla_device.h"), "prefill_T131072"),
+    "decode_step": (("k_decode_step_sq",), 256 * 32 * 512, "decode_step_B256_H32_traffic.txt",
+                    ("lla_decode.hip", "lla_device.h"), "decode_B256"),
+    "decode_group": (("k_decode_group",), 256 * 8 * 512, "decode_group_B256_Hq32_Hkv8_traffic.txt",
+                     ("lla_decode.hip", "lla_device.h"), "decode_B256_gqa"),
 }
+
+SIMD_NUM = 256 * 4  # MI355X: 256 compute units of 4 SIMDs (the SIMD_NUM of MfmaUtil)
+PEAK_BF16_TFLOPS = 2516.6
+
+
+def matches(name: str, kernel: str) -> bool:
+    return any(f in name for f in KERNELS[kernel][0])
 
 
 def code_only(text: str) -> str:
@@ -112,7 +146,7 @@ def stored_traffic(kernel: str):
 
 # ---- the counter workload -------------------------------------------------------
 
-def run(launches: int) -> None:
+def run(launches: int, which=WORKLOADS) -> None:
     import torch
     sys.path.insert(0, ROOT)
     import workloads
@@ -121,47 +155,42 @@ def run(launches: int) -> None:
     library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    cfg = workloads.CONFIGS["prefill_T8192"]
-    q0, k0, v0 = workloads.config_inputs(cfg, device=dev)
-    sets, keep = [], []
-    for r in range(4):
-        q, k, v = (x.clone() for x in (q0, k0, v0)) if r else (q0, k0, v0)
-        S = state_init(cfg.B, cfg.H, cfg.dk, cfg.dv, device=dev)
-        sets.append(PreparedPrefill(q, k, v, S, cfg.C))
-        keep.append((q, k, v))
-    for i in range(launches):
-        st = sets[i % len(sets)]
-        st.zero_state()
-        st.segment_states()
-        st.state_scan()
-        st.chunks()
-    torch.cuda.synchronize()
-    print("prefill: %d steps" % launches, flush=True)
-    del sets, keep
-    torch.cuda.empty_cache()
-
-    dc = workloads.CONFIGS["decode_B256"]
-    S = state_init(dc.B, dc.H, dc.dk, dc.dv, device=dev)
-    qd, kd, vd = workloads.decode_inputs(dc, launches, device=dev)
-    calls = [PreparedDecode(qd[i], kd[i], vd[i], S) for i in range(launches)]
-    for c in calls:
-        c()
-    torch.cuda.synchronize()
-    print("decode: %d steps" % launches, flush=True)
-    del calls, S
-    torch.cuda.empty_cache()
-
-    gc = workloads.CONFIGS["decode_B256_gqa"]
-    S0 = workloads.random_state(gc, device=dev)
-    states = [S0] + [S0.clone() for _ in range(2)]
-    qd, kd, vd = workloads.decode_inputs(gc, launches, device=dev)
-    calls = [PreparedDecode(qd[i], kd[i], vd[i], states[i % 3]) for i in range(launches)]
-    for c in calls:
-        c()
-    torch.cuda.synchronize()
-    print("grouped decode: %d steps" % launches, flush=True)
-    del calls, states, S0
-    torch.cuda.empty_cache()
+    for name in which:
+        cfg = workloads.CONFIGS[name]
+        if name.startswith("prefill"):
+            rotate = 2 if cfg.T >= 65536 else 4
+            q0, k0, v0 = workloads.config_inputs(cfg, device=dev)
+            sets = []
+            for r in range(rotate):
+                q, k, v = (x.clone() for x in (q0, k0, v0)) if r else (q0, k0, v0)
+                S = torch.empty((cfg.B, cfg.kv_heads, cfg.dk, cfg.dv), device=dev)
+                sets.append(PreparedPrefill(q, k, v, S, cfg.C))
+            for i in range(launches):
+                sets[i % rotate](zero_state=True)  # a fresh prompt: K^T V, scan, walk
+            torch.cuda.synchronize()
+            del sets, q0, k0, v0
+        elif name == "decode_B256":
+            S = state_init(cfg.B, cfg.H, cfg.dk, cfg.dv, device=dev)
+            qd, kd, vd = workloads.decode_inputs(cfg, launches, device=dev)
+            calls = [PreparedDecode(qd[i], kd[i], vd[i], S) for i in range(launches)]
+            for c in calls:
+                c()
+            torch.cuda.synchronize()
+            del calls, S, qd, kd, vd
+        elif name == "decode_B256_gqa":
+            # three state sets, so that each step reads its states from HBM
+            S0 = workloads.random_state(cfg, device=dev)
+            states = [S0] + [S0.clone() for _ in range(2)]
+            qd, kd, vd = workloads.decode_inputs(cfg, launches, device=dev)
+            calls = [PreparedDecode(qd[i], kd[i], vd[i], states[i % 3]) for i in range(launches)]
+            for c in calls:
+                c()
+            torch.cuda.synchronize()
+            del calls, states, S0, qd, kd, vd
+        else:
+            raise SystemExit("unknown workload %s" % name)
+        torch.cuda.empty_cache()
+        print("%s: %d steps" % (name, launches), flush=True)
 
     src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
     dst = torch.empty_like(src)
@@ -244,20 +273,20 @@ def _copy_mean(directory: str, counter: str) -> float:
     return sum(big) / len(big)
 
 
-def _pick(means: dict, fragment: str, grid: int | None):
-    hits = [(k, v) for k, v in means.items() if fragment in k[0] and (grid is None or k[1] == grid)]
+def _pick(means: dict, kernel: str, grid: int | None):
+    hits = [(k, v) for k, v in means.items() if matches(k[0], kernel) and (grid is None or k[1] == grid)]
     if len(hits) != 1:
         raise SystemExit("expected one (kernel, grid) matching %r grid %s, found %d"
-                         % (fragment, grid, len(hits)))
+                         % (KERNELS[kernel][0], grid, len(hits)))
     return hits[0]
 
 
 def traffic(kernel: str, fetch_dir: str, write_dir: str) -> None:
-    frag, grid, _, _ = KERNELS[kernel]
+    grid = KERNELS[kernel][1]
     fetch = _counter_means(fetch_dir, "FETCH_SIZE")
     write = _counter_means(write_dir, "WRITE_SIZE")
-    (kname, _), (f_kib, f_n) = _pick(fetch, frag, grid)
-    _, (w_kib, w_n) = _pick(write, frag, grid)
+    (kname, _), (f_kib, f_n) = _pick(fetch, kernel, grid)
+    _, (w_kib, w_n) = _pick(write, kernel, grid)
     cf_kib = _copy_mean(fetch_dir, "FETCH_SIZE")
     cw_kib = _copy_mean(write_dir, "WRITE_SIZE")
     f_scale = cf_kib * 1024.0 / COPY_BYTES   # counter bytes per true byte
@@ -280,24 +309,76 @@ def traffic(kernel: str, fetch_dir: str, write_dir: str) -> None:
     print("hbm_bytes_per_launch = %.0f" % (read_b + write_b))
 
 
+def _all_counter_means(directories, kernel: str):
+    """{counter: (mean per dispatch, dispatches)} of KERNEL (at its workload's
+    grid) over every counter_collection.csv under the directories."""
+    grid = KERNELS[kernel][1]
+    acc = collections.defaultdict(list)
+    name = None
+    for d in directories:
+        for f in _find(d, "counter_collection.csv"):
+            for r in csv.DictReader(open(f)):
+                if matches(r["Kernel_Name"], kernel) and _grid(r) == grid:
+                    acc[r["Counter_Name"]].append(float(r["Counter_Value"]))
+                    name = r["Kernel_Name"]
+    if not acc:
+        raise SystemExit("no dispatches of %s (grid %d) under %s" % (kernel, grid, directories))
+    return name, {c: (sum(v) / len(v), len(v)) for c, v in acc.items()}
+
+
+def counters(kernel: str, directories, duration_us=None) -> None:
+    kname, means = _all_counter_means(directories, kernel)
+    print("kernel = %s" % _short(kname))
+    print("grid_threads = %d" % KERNELS[kernel][1])
+    print("kernel_source_sha = %s" % kernel_source_sha(kernel))
+    for c in sorted(means):
+        print("%s = %.6g    # mean of %d dispatches" % (c, means[c][0], means[c][1]))
+    m = {c: v for c, (v, _) in means.items()}
+    if "MfmaUtil" in m:
+        print("mfma_util_percent = %.2f    # rocprofiler's MfmaUtil: sum of SQ_VALU_MFMA_BUSY_CYCLES "
+              "/ (max GRBM_GUI_ACTIVE x %d SIMDs)" % (m["MfmaUtil"], SIMD_NUM))
+    if "MfmaFlopsBF16" in m:
+        print("mfma_flops_bf16_per_launch = %.6g    # executed: SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512"
+              % m["MfmaFlopsBF16"])
+        if duration_us:
+            tf = m["MfmaFlopsBF16"] / (duration_us * 1e-6) / 1e12
+            print("kernel_duration_us = %.3f" % duration_us)
+            print("mfma_tflops_bf16 = %.2f" % tf)
+            print("mfma_frac_of_bf16_peak = %.4f    # of %.1f TFLOP/s" % (tf / PEAK_BF16_TFLOPS, PEAK_BF16_TFLOPS))
+    wave = m.get("SQ_WAVE_CYCLES")
+    if wave:
+        for c in ("SQ_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY",
+                  "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_VALU", "SQ_INST_CYCLES_VMEM"):
+            if c in m and c != "SQ_BUSY_CYCLES":
+                print("%s_share_of_wave_cycles = %.4f" % (c.lower(), m[c] / wave))
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(prog="python -m decode_lla_prefill_amd.profiling")
     sub = ap.add_subparsers(dest="cmd", required=True)
     r = sub.add_parser("run")
     r.add_argument("--launches", type=int, default=8)
+    r.add_argument("--workloads", default=",".join(WORKLOADS))
     s = sub.add_parser("stats")
     s.add_argument("directory")
     t = sub.add_parser("traffic")
     t.add_argument("kernel", choices=sorted(KERNELS))
     t.add_argument("fetch_dir")
     t.add_argument("write_dir")
+    c = sub.add_parser("counters")
+    c.add_argument("kernel", choices=sorted(KERNELS))
+    c.add_argument("directories", nargs="+")
+    c.add_argument("--duration-us", type=float, default=None,
+                   help="the kernel's average duration (kernel trace), for the MFMA rate")
     a = ap.parse_args(argv)
     if a.cmd == "run":
-        run(a.launches)
+        run(a.launches, [w for w in a.workloads.split(",") if w])
     elif a.cmd == "stats":
         stats(a.directory)
-    else:
+    elif a.cmd == "traffic":
         traffic(a.kernel, a.fetch_dir, a.write_dir)
+    else:
+        counters(a.kernel, a.directories, a.duration_us)
 
 
 if __name__ == "__main__":

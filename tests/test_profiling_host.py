@@ -18,6 +18,41 @@ def test_digest_changes_with_code_not_with_comments():
 
 
 def test_every_measured_kernel_names_its_sources():
-    for name, (fragment, grid, summary, sources) in profiling.KERNELS.items():
-        assert fragment.startswith("k_") and grid > 0 and summary.endswith("_traffic.txt")
+    for name, (fragments, grid, summary, sources, workload) in profiling.KERNELS.items():
+        assert all("k_" in f for f in fragments) and grid > 0 and summary.endswith("_traffic.txt")
         assert len(profiling.kernel_source_sha(name)) == 16
+        assert workload in profiling.WORKLOADS
+
+
+def test_kernel_grids_follow_the_plan():
+    """The launch grid each summary keys on, recomputed from the library's
+    plan (lla_prefill_segment_chunks) and the kernels' workgroup shapes."""
+    import math
+    import decode_lla_prefill_amd as lla
+    import workloads
+
+    def segments(name):
+        c = workloads.CONFIGS[name]
+        G = lla.prefill_segment_chunks(c.B, c.H, c.T, c.dk, c.dv, c.C)
+        return c, math.ceil(math.ceil(c.T / c.C) / G)
+
+    c, n = segments("prefill_T8192")
+    assert profiling.KERNELS["chunk_walk"][1] == c.B * c.H * n * 512       # one 8-wave group per segment
+    assert profiling.KERNELS["chunk_walk_fp8"][1] == c.B * c.H * n * 512
+    assert profiling.KERNELS["segment_states"][1] == c.B * c.H * (n - 1) * 512
+    assert profiling.KERNELS["state_scan"][1] == c.B * c.H * math.ceil(c.dk * c.dv / 1024) * 256
+    c, n = segments("prefill_B4_T1024")
+    assert profiling.KERNELS["chunk_walk_T1024"][1] == c.B * c.H * n * 256  # four waves, d = 64: one value block
+    c, n = segments("prefill_T131072")
+    assert profiling.KERNELS["chunk_walk_T131072"][1] == c.B * c.H * n * 512
+    c = workloads.CONFIGS["decode_B256"]
+    assert profiling.KERNELS["decode_step"][1] == c.B * c.H * 512
+    c = workloads.CONFIGS["decode_B256_gqa"]
+    assert profiling.KERNELS["decode_group"][1] == c.B * c.kv_heads * 512
+
+
+def test_kernel_names_match_in_both_trace_forms():
+    assert profiling.matches("_ZN3lla17k_chunk_walk_wideILi64EDF16bEEvPKT0_S3_S3_PfS4_PKfliiillii", "chunk_walk")
+    assert profiling.matches("void lla::k_chunk_walk_wide<64, lla::fp8e4m3>(...)", "chunk_walk_fp8")
+    assert not profiling.matches("void lla::k_chunk_walk_wide<64, lla::fp8e4m3>(...)", "chunk_walk")
+    assert profiling.matches("lla::k_state_scan(float const*, float*, long, long, long, int)", "state_scan")
