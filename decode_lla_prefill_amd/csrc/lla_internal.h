@@ -10,11 +10,16 @@
 
 namespace lla {
 
-// Workgroups the chunk walk aims to launch: two per compute unit of a
-// 256-CU MI355X.  A constant (not a device query) so that the segmentation,
-// and therefore the rounding order, depends on the shape alone.
+// (sequence, head, segment) lines the chunk walk aims for: one per compute
+// unit of a 256-CU MI355X.  A line is one eight-wave workgroup (d = 128,
+// bf16 or FP8), or one four-wave workgroup per block of value columns.
+// Measured: at T = 8192 (d = 128) fewer, longer lines lose parallelism; at
+// T = 1024 (d = 64) one line per CU (two chunks each) beats two (one chunk
+// each: the segment pass, the scan and the walk are then all fixed cost).
+// A constant (not a device query) so that the segmentation, and therefore
+// the rounding order, depends on the shape alone.
 #ifndef LLA_TARGET_WALKERS
-#define LLA_TARGET_WALKERS 512
+#define LLA_TARGET_WALKERS 256
 #endif
 constexpr int64_t kTargetWalkers = LLA_TARGET_WALKERS;
 

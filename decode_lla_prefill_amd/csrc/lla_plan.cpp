@@ -27,7 +27,7 @@ void plan_prefill(PrefillPlan& p) {
     p.BV = p.D > 64 ? 64 : p.D;
     p.n_vb = p.D / p.BV;
     p.n_c = p.T > 0 ? (p.T + p.C - 1) / p.C : 0;
-    const int64_t want = p.n_c * p.BHq * p.n_vb;
+    const int64_t want = p.n_c * p.BHq;  // lines if every segment were one chunk
     p.G = want > kTargetWalkers ? (want + kTargetWalkers - 1) / kTargetWalkers : 1;
     if (p.G > p.n_c) p.G = p.n_c > 0 ? p.n_c : 1;
     p.n_seg = p.n_c > 0 ? (p.n_c + p.G - 1) / p.G : 0;

@@ -50,28 +50,32 @@ COPY_BYTES = 1 << 30
 WORKLOADS = ("prefill_T8192", "prefill_T8192_fp8", "prefill_B4_T1024", "prefill_T131072",
              "decode_B256", "decode_B256_gqa")
 
+# what decides a prefill kernel's work: its code and the plan that cuts the
+# shape into segments
+PREFILL_SOURCES = ("lla_prefill.hip", "lla_device.h", "lla_plan.cpp", "lla_internal.h")
+
 # measured kernel -> (name fragments as the trace shows them (mangled or
 # demangled), launch grid in threads of its workload, counter summary file,
 # sources that define the kernel, workload).  Grids follow from the plan
 # (tests/test_profiling_host.py recomputes them).
 KERNELS = {
     "chunk_walk": (("k_chunk_walk_wideILi64EDF16b", "k_chunk_walk_wide<64, __bf16>"), 16 * 16 * 512,
-                   "chunk_walk_T8192_traffic.txt", ("lla_prefill.hip", "lla_device.h"), "prefill_T8192"),
+                   "chunk_walk_T8192_traffic.txt", PREFILL_SOURCES, "prefill_T8192"),
     "segment_states": (("k_segment_states_wideILi64EDF16b", "k_segment_states_wide<64, __bf16>"),
                        16 * 15 * 512, "segment_states_T8192_traffic.txt",
-                       ("lla_prefill.hip", "lla_device.h"), "prefill_T8192"),
+                       PREFILL_SOURCES, "prefill_T8192"),
     "state_scan": (("k_state_scan",), 16 * 16 * 256, "state_scan_T8192_traffic.txt",
-                   ("lla_prefill.hip", "lla_device.h"), "prefill_T8192"),
+                   PREFILL_SOURCES, "prefill_T8192"),
     "chunk_walk_fp8": (("k_chunk_walk_wideILi64ENS_7fp8e4m3", "k_chunk_walk_wide<64, lla::fp8e4m3>"),
                        16 * 16 * 512, "chunk_walk_T8192_fp8_traffic.txt",
-                       ("lla_prefill.hip", "lla_device.h"), "prefill_T8192_fp8"),
+                       PREFILL_SOURCES, "prefill_T8192_fp8"),
     "chunk_walk_T1024": (("k_chunk_walkIDF16bLi64ELi64ELi64ELb1ELi4E", "k_chunk_walk<__bf16, 64, 64, 64, true, 4>"),
-                         32 * 16 * 256, "chunk_walk_B4_T1024_traffic.txt",
-                         ("lla_prefill.hip", "lla_device.h"), "prefill_B4_T1024"),
+                         32 * 8 * 256, "chunk_walk_B4_T1024_traffic.txt",
+                         PREFILL_SOURCES, "prefill_B4_T1024"),
     "chunk_walk_T131072": (("k_chunk_walkIDF16bLi128ELi128ELi128ELb1ELi8E",
                             "k_chunk_walk<__bf16, 128, 128, 128, true, 8>"),
                            32 * 8 * 512, "chunk_walk_T131072_traffic.txt",
-                           ("lla_prefill.hip", "lla_device.h"), "prefill_T131072"),
+                           PREFILL_SOURCES, "prefill_T131072"),
     "decode_step": (("k_decode_step_sq",), 256 * 32 * 512, "decode_step_B256_H32_traffic.txt",
                     ("lla_decode.hip", "lla_device.h"), "decode_B256"),
     "decode_group": (("k_decode_group",), 256 * 8 * 512, "decode_group_B256_Hq32_Hkv8_traffic.txt",

@@ -178,12 +178,16 @@ def test_segments_cover_the_sequence(lib, B, H, T, d, C):
     n_seg = math.ceil(n_c / G)
     # one fp32 d x d state per segment per (b,h), or nothing for one segment
     assert ws == (B * H * n_seg * d * d * 4 if n_seg > 1 else 0)
-    # enough workgroups to fill the chip without one per chunk
-    assert n_seg * B * H * (2 if d > 64 else 1) >= min(n_c * B * H, 256)
+    # about one (sequence, head, segment) line per compute unit, without one per
+    # chunk: G is the smallest whole number of chunks that keeps the lines at
+    # most 256, so there are more than half that many (or one per chunk)
+    lines = n_seg * B * H
+    assert lines >= min(n_c * B * H, 129)
+    assert G == 1 or math.ceil(n_c / (G - 1)) * B * H > 256
 
 
 def test_segment_plan_for_the_t8192_workload(lib):
-    # 128 chunks x 16 heads x 2 value blocks = 4096 chunk-walks, 512 workgroups of 8
+    # 128 chunks x 16 heads = 2048 chunk lines: 256 eight-wave walk workgroups of 8 chunks
     assert lib.lla_prefill_segment_chunks(1, 16, 8192, 128, 128, 64) == 8
     assert lib.lla_prefill_workspace_size(1, 16, 8192, 128, 128, 64) == 16 * 16 * 128 * 128 * 4
 
