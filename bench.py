@@ -416,6 +416,42 @@ def bench_decode(args, torch, lla, workloads, profiling):
             "roofline": tokens_roofline("k_decode_tokens<bf16,128,512>", cbytes, fmas, ms_c)})
         del call, qc, kc, vc
 
+    # Speculative decoding at k = 4 draft tokens: the verify pass
+    # (lla_prefill_ex with LLA_PREFILL_KEEP_STATE: S read, not written) and
+    # the commit of each sequence's accepted prefix (lla_state_commit; the
+    # accepted counts m_b, uniform in 0..4 from a fixed seed, stay on the
+    # device).  Together they equal m_b decode steps bit for bit.
+    kd_ = 4
+    qs, ks, vs = (x.permute(1, 2, 0, 3).contiguous() for x in workloads.decode_inputs(cfg, kd_, device=dev))
+    acc = torch.randint(0, kd_ + 1, (B,), generator=torch.Generator(device=dev).manual_seed(cfg.seed_base + 7),
+                        device=dev, dtype=torch.int32)
+    n_acc = int(acc.sum())
+    S_spec = S.clone()
+    verify = lla.PreparedPrefill(qs, ks, vs, S_spec, C)
+    for _ in range(3):
+        verify(keep_state=True)
+        lla.state_commit(ks, vs, S_spec, acc)
+    ns = 50
+    _, v_s = _timed(torch, lambda i: verify(keep_state=True), ns)
+    _, c_s = _timed(torch, lambda i: lla.state_commit(ks, vs, S_spec, acc), ns)
+    wall_p, gpu_p = _timed(torch, lambda i: (verify(keep_state=True), lla.state_commit(ks, vs, S_spec, acc)), ns)
+    v_ms, c_ms = v_s * 1e3 / ns, c_s * 1e3 / ns
+    n_commit = int((acc > 0).sum())
+    v_bytes = B * H * (4 * d * d + kd_ * 10 * d)  # S read; q, k, v bf16 and fp32 o per token
+    c_bytes = n_commit * H * 8 * d * d + n_acc * H * 4 * d  # S read + written where m_b > 0; k, v of accepted tokens
+    res["speculative"] = {
+        "draft_tokens": kd_, "accepted_tokens_per_call": n_acc, "sequences_committing": n_commit,
+        "accepted": "m_b uniform in 0..%d per sequence (seed %d), on the device" % (kd_, cfg.seed_base + 7),
+        "value": n_acc * ns / wall_p, "unit": "accepted tokens/s",
+        "draft_tokens_per_s": B * kd_ * ns / wall_p, "ms_per_call_pair": wall_p * 1e3 / ns,
+        "gpu_ms_per_call_pair": gpu_p * 1e3 / ns,
+        "verify": hbm_roofline("k_decode_tokens<bf16,128,512> (keep state)", v_bytes, v_ms, args.gap_ms, None,
+                               "HIP events around %d back-to-back verify calls" % ns),
+        "commit": hbm_roofline("k_state_commit<bf16,4>", c_bytes, c_ms, args.gap_ms, None,
+                               "HIP events around %d back-to-back commits" % ns),
+    }
+    del verify, qs, ks, vs, S_spec
+
     if not args.no_cpu_baseline:
         # n decode steps of one (b,h) are n iterations of the recurrence from
         # its state: time the oracle on 8 sequences x all heads x 128 steps.

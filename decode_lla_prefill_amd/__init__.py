@@ -23,7 +23,8 @@ __all__ = [
     "LlaError", "library", "library_path", "state_init", "prefill", "decode_step",
     "prefill_workspace_size", "prefill_gqa_workspace_size", "prefill_segment_chunks",
     "prefill_segment_states",
-    "prefill_state_scan", "prefill_chunks", "prefill_noalloc", "PreparedPrefill", "PreparedDecode",
+    "prefill_state_scan", "prefill_chunks", "prefill_noalloc", "state_commit", "PreparedPrefill",
+    "PreparedDecode",
     "EXPORTS",
 ]
 
@@ -37,8 +38,9 @@ EXPORTS = ("lla_status_string", "lla_last_device_error", "lla_state_init",
            "lla_prefill_segment_chunks", "lla_prefill_workspace_size", "lla_prefill",
            "lla_prefill_segment_states", "lla_prefill_state_scan", "lla_prefill_chunks",
            "lla_decode_step", "lla_prefill_gqa_workspace_size", "lla_prefill_gqa",
-           "lla_decode_step_gqa", "lla_prefill_ex", "lla_prefill_noalloc")
+           "lla_decode_step_gqa", "lla_prefill_ex", "lla_prefill_noalloc", "lla_state_commit")
 PREFILL_ZERO_STATE = 1  # lla_prefill_ex: start from S_0 = 0 without reading S
+PREFILL_KEEP_STATE = 2  # lla_prefill_ex: read S, do not write it (verify pass of draft tokens)
 
 _BF16, _F32, _FP8 = 0, 1, 2
 _lib = None
@@ -98,6 +100,8 @@ def library():
         lib.lla_prefill_noalloc.argtypes = [vp, vp, vp, ci, i64, i64, i64, i64, i64, i64, i64,
                                             ctypes.c_uint, vp, vp, vp]
         lib.lla_prefill_noalloc.restype = st
+        lib.lla_state_commit.argtypes = [vp, vp, ci, i64, i64, i64, i64, i64, vp, vp, vp]
+        lib.lla_state_commit.restype = st
         _lib = lib
     return _lib
 
@@ -216,20 +220,24 @@ def _out(out, shape, device):
     return out
 
 
-def prefill(q, k, v, state, chunk: int, out=None, workspace=None, zero_state: bool = False):
+def prefill(q, k, v, state, chunk: int, out=None, workspace=None, zero_state: bool = False,
+            keep_state: bool = False):
     """Chunkwise prefill: returns o [B,Hq,T,dv] fp32; ``state`` [B,Hkv,dk,dv] goes
     S_0 -> S_T in place.  k, v with fewer heads than q (Hq a multiple of Hkv)
     select shared-state heads (lla_prefill_gqa).  ``zero_state``: a fresh
-    prompt -- start from S_0 = 0 without reading ``state`` (lla_prefill_ex)."""
+    prompt -- start from S_0 = 0 without reading ``state`` (lla_prefill_ex).
+    ``keep_state``: a verify pass over draft tokens -- ``state`` is read but
+    keeps S_0 (lla_prefill_ex; then :func:`state_commit`)."""
     lib = library()
     B, Hq, Hkv, T, dk, dv = _qkv_shape(q, k, v)
     _state_check(state, B, Hkv, dk, dv)
     out = _out(out, (B, Hq, T, dv), q.device)
     ws, ws_bytes = _workspace(B, Hq, T, dk, dv, chunk, q.device, workspace, Hkv)
     _same_device(q.device, state=state, out=out, workspace=ws)
-    if zero_state:
+    if zero_state or keep_state:
+        flags = (PREFILL_ZERO_STATE if zero_state else 0) | (PREFILL_KEEP_STATE if keep_state else 0)
         _check(lib.lla_prefill_ex(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, Hq, Hkv, T, dk, dv,
-                                  chunk, PREFILL_ZERO_STATE, _ptr(state), _ptr(out), _ptr(ws),
+                                  chunk, flags, _ptr(state), _ptr(out), _ptr(ws),
                                   ws_bytes, _stream(q)), "lla_prefill_ex")
     elif Hq == Hkv:
         _check(lib.lla_prefill(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, Hq, T, dk, dv, chunk,
@@ -255,6 +263,29 @@ def prefill_noalloc(q, k, v, state, chunk: int, out=None, zero_state: bool = Fal
                                    PREFILL_ZERO_STATE if zero_state else 0, _ptr(state), _ptr(out),
                                    _stream(q)), "lla_prefill_noalloc")
     return out
+
+
+def state_commit(k, v, state, accepted=None):
+    """After a verify pass (``prefill(..., keep_state=True)``): ``state`` +=
+    sum over the first m_b tokens of k_t v_t^T for every sequence b, m_b =
+    ``accepted[b]`` (a device int32 tensor [B]; None: all T), with the decode
+    step's arithmetic (lla_state_commit).  k, v: [B, Hkv, T, d]."""
+    lib = library()
+    _need(k, "k", ndim=4)
+    _need(v, "v", dtype=k.dtype, ndim=4)
+    B, H, T, dk = k.shape
+    dv = v.shape[3]
+    if tuple(v.shape[:3]) != (B, H, T):
+        raise ValueError("shape mismatch: k %s v %s" % (tuple(k.shape), tuple(v.shape)))
+    _state_check(state, B, H, dk, dv)
+    if accepted is not None:
+        _need(accepted, "accepted", dtype=torch.int32, ndim=1)
+        if accepted.shape[0] != B:
+            raise ValueError("accepted has %d entries, expected %d" % (accepted.shape[0], B))
+    _same_device(k.device, v=v, state=state, accepted=accepted)
+    _check(lib.lla_state_commit(_ptr(k), _ptr(v), _dtype_code(k), B, H, T, dk, dv, _ptr(accepted),
+                                _ptr(state), _stream(k)), "lla_state_commit")
+    return state
 
 
 def prefill_segment_states(k, v, chunk: int, workspace):
@@ -369,8 +400,8 @@ class PreparedPrefill:
             self._fn = lib.lla_prefill
             self._args = (_ptr(q), _ptr(k), _ptr(v), dt, B, H, T, dk, dv, chunk,
                           _ptr(state), _ptr(self.out), ws, ws_bytes)
-        self._fresh_args = (_ptr(q), _ptr(k), _ptr(v), dt, B, H, Hkv, T, dk, dv, chunk,
-                            PREFILL_ZERO_STATE, _ptr(state), _ptr(self.out), ws, ws_bytes)
+        self._ex_head = (_ptr(q), _ptr(k), _ptr(v), dt, B, H, Hkv, T, dk, dv, chunk)
+        self._ex_tail = (_ptr(state), _ptr(self.out), ws, ws_bytes)
         self._init_args = (_ptr(state), B, Hkv, dk, dv)
         # every tensor whose address is stored above stays alive with this
         # object (the library reads and writes them on each call)
@@ -382,12 +413,13 @@ class PreparedPrefill:
     def _stream(self):
         return torch.cuda.current_stream(self._device).cuda_stream
 
-    def __call__(self, zero_state: bool = False):
+    def __call__(self, zero_state: bool = False, keep_state: bool = False):
         """One prefill; ``zero_state``: a fresh prompt (S_0 = 0, the state is
-        not read)."""
+        not read); ``keep_state``: a verify pass (the state is not written)."""
         st = self._stream()
-        if zero_state:
-            _check(self._lib.lla_prefill_ex(*self._fresh_args, st), "lla_prefill_ex")
+        if zero_state or keep_state:
+            flags = (PREFILL_ZERO_STATE if zero_state else 0) | (PREFILL_KEEP_STATE if keep_state else 0)
+            _check(self._lib.lla_prefill_ex(*self._ex_head, flags, *self._ex_tail, st), "lla_prefill_ex")
         else:
             _check(self._fn(*self._args, st), self._fn.__name__)
         return self.out

@@ -44,6 +44,7 @@ int raw_enum(const E& e) {
 
 int64_t elem_size(lla_dtype dt) { return dt == LLA_FP8_E4M3 ? 1 : (dt == LLA_BF16 ? 2 : 4); }
 bool known_dtype(int dt) { return dt == LLA_BF16 || dt == LLA_F32 || dt == LLA_FP8_E4M3; }
+constexpr unsigned kKnownFlags = LLA_PREFILL_ZERO_STATE | LLA_PREFILL_KEEP_STATE;
 
 // Sizes shared by every call.  `C` < 0 means "no chunk size" (decode, init).
 lla_status check_sizes(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int64_t C) {
@@ -168,7 +169,8 @@ const char* lla_status_string(lla_status s) {
         case LLA_ERR_DTYPE: return "unknown dtype";
         case LLA_ERR_UNSUPPORTED:
             return "unsupported request (fp32 inputs with C > 64, a grouped decode shape other than "
-                   "dk = dv in {64, 128} with at most 16 query heads per group, or unknown option bits)";
+                   "dk = dv in {64, 128} with at most 16 query heads per group, unknown option bits, "
+                   "or a keep-state prefill off the fused short-prompt route)";
         case LLA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
         case LLA_ERR_ALIAS: return "an output overlaps another buffer";
         case LLA_ERR_WORKSPACE: return "workspace missing or too small";
@@ -246,20 +248,23 @@ namespace {
 lla_status prefill_impl(const void* Q, const void* K, const void* V, int dt_raw, int64_t B,
                         Heads h, int64_t T, int64_t dk, int64_t dv, int64_t C, unsigned flags,
                         float* S, float* O, void* workspace, size_t workspace_bytes, void* stream) {
-    if (flags & ~(unsigned)LLA_PREFILL_ZERO_STATE) return LLA_ERR_UNSUPPORTED;
+    if (flags & ~kKnownFlags) return LLA_ERR_UNSUPPORTED;
     const bool zero = (flags & LLA_PREFILL_ZERO_STATE) != 0;
+    const bool keep = (flags & LLA_PREFILL_KEEP_STATE) != 0;
     lla::PrefillPlan p;
     PrefillBufs b{Q, K, V, nullptr, S, O, workspace, workspace_bytes};
     lla_status st = check_prefill(b, true, true, true, true, true, dt_raw, B, h, T, dk, dv, C, p);
     if (st != LLA_OK) return st;
     const lla_dtype dtype = (lla_dtype)dt_raw;  // checked
     hipStream_t s = (hipStream_t)stream;
-    if (T == 0)  // S_T = S_0: untouched, or zero for a fresh prompt
-        return zero ? device_status(lla::launch_fill_zero(S, p.BH * dk * dv, s)) : LLA_OK;
+    const bool fused = lla::decode_tokens_fit(T, (int)dk, (int)dv, p.group);
+    if (keep && T > 0 && !fused) return LLA_ERR_UNSUPPORTED;  // the verify pass runs on the fused route only
+    if (T == 0)  // S_T = S_0: untouched, or zero for a fresh prompt (never written with KEEP_STATE)
+        return zero && !keep ? device_status(lla::launch_fill_zero(S, p.BH * dk * dv, s)) : LLA_OK;
     p.zero_start = zero;
-    if (lla::decode_tokens_fit(T, (int)dk, (int)dv, p.group))  // a short prompt: fused decode steps
+    if (fused)  // a short prompt: fused decode steps
         return device_status(lla::launch_decode_tokens(dtype, Q, K, V, p.BH, (int)T, p.group, (int)dk, S, O,
-                                                       zero, s));
+                                                       zero, keep, s));
     float* ws = (float*)workspace;
     st = device_status(lla::launch_segment_states(p, K, V, ws, s));
     if (st != LLA_OK) return st;
@@ -324,12 +329,14 @@ lla_status lla_prefill_noalloc(const void* Q, const void* K, const void* V, lla_
                                unsigned flags, float* S, float* O, void* stream) {
     // Everything but the workspace is checked first (no HIP call), then the
     // workspace the plan needs against the static array's size.
-    if (flags & ~(unsigned)LLA_PREFILL_ZERO_STATE) return LLA_ERR_UNSUPPORTED;
+    if (flags & ~kKnownFlags) return LLA_ERR_UNSUPPORTED;
     lla::PrefillPlan p;
     PrefillBufs b{Q, K, V, nullptr, S, O, nullptr, 0};
     lla_status st = check_prefill(b, true, true, true, true, false, raw_enum(dtype), B, Heads{Hq, Hkv}, T, dk,
                                   dv, C, p);
     if (st != LLA_OK) return st;
+    if ((flags & LLA_PREFILL_KEEP_STATE) && T > 0 && !lla::decode_tokens_fit(T, (int)dk, (int)dv, p.group))
+        return LLA_ERR_UNSUPPORTED;
     const size_t need = ws_bytes_for(p);
     if (need > lla::kNoAllocScratchBytes) return LLA_ERR_SCRATCH;
     float* ws = nullptr;
@@ -339,6 +346,25 @@ lla_status lla_prefill_noalloc(const void* Q, const void* K, const void* V, lla_
     }
     return prefill_impl(Q, K, V, raw_enum(dtype), B, Heads{Hq, Hkv}, T, dk, dv, C, flags, S, O, ws,
                         ws ? lla::kNoAllocScratchBytes : 0, stream);
+}
+
+lla_status lla_state_commit(const void* K, const void* V, lla_dtype dtype, int64_t B, int64_t H,
+                            int64_t T, int64_t dk, int64_t dv, const int32_t* accepted, float* S,
+                            void* stream) {
+    lla_status st = check_sizes(B, H, T, dk, dv, -1);
+    if (st != LLA_OK) return st;
+    const int dt_raw = raw_enum(dtype);
+    if (!known_dtype(dt_raw)) return LLA_ERR_DTYPE;
+    if (!S || (T > 0 && (!K || !V))) return LLA_ERR_NULL;
+    if (!aligned16(S) || (T > 0 && (!aligned16(K) || !aligned16(V))) || (accepted && !aligned16(accepted)))
+        return LLA_ERR_ALIGN;
+    if (T == 0) return LLA_OK;
+    const int64_t es = elem_size((lla_dtype)dt_raw);
+    const Span ss = span(S, B * H * dk * dv * 4), sk = span(K, B * H * T * dk * es),
+               sv = span(V, B * H * T * dv * es), sa = span(accepted, accepted ? B * 4 : 0);
+    if (overlap(ss, sk) || overlap(ss, sv) || overlap(ss, sa)) return LLA_ERR_ALIAS;
+    return device_status(lla::launch_state_commit((lla_dtype)dt_raw, K, V, accepted, B * H, (int)H, (int)T,
+                                                  (int)dk, (int)dv, S, (hipStream_t)stream));
 }
 
 lla_status lla_decode_step(const void* q, const void* k, const void* v, lla_dtype dtype,

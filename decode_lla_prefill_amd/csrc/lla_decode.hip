@@ -170,7 +170,10 @@ __global__ __launch_bounds__(NT) void k_decode_tokens(const Tin* __restrict__ q,
                                                       const Tin* __restrict__ v,
                                                       float* __restrict__ S,
                                                       float* __restrict__ o, int T, int G,
-                                                      int zero_start) {
+                                                      int mode) {
+    // mode bit 0: S_0 = 0 (S is not read); bit 1: S is not written (a verify
+    // pass over draft tokens, lla_prefill_ex with LLA_PREFILL_KEEP_STATE)
+    const bool zero_start = (mode & 1) != 0, keep_state = (mode & 2) != 0;
     constexpr int CG = D / 4, RG = NT / CG, RPT = D / RG;
     static_assert(NT % CG == 0 && D % RG == 0, "thread layout must tile the state");
     constexpr int QROWS = GQ > 0 ? 2 * GQ : QMAX;             // staged query rows
@@ -257,6 +260,7 @@ __global__ __launch_bounds__(NT) void k_decode_tokens(const Tin* __restrict__ q,
             __syncthreads();  // red is rewritten by the next batch or token
         }
     }
+    if (keep_state) return;
 #pragma unroll
     for (int m = 0; m < RPT; ++m)
         __builtin_nontemporal_store(x[m], reinterpret_cast<f32x4*>(Sb + (rg + m * RG) * D + 4 * cg));
@@ -319,6 +323,85 @@ __global__ __launch_bounds__(NT) void k_decode_group(const Tin* __restrict__ q,
         }
         __syncthreads();  // red is rewritten by the next query head
     }
+}
+
+// The commit after a verify pass over T draft tokens (speculative decoding):
+// S += sum over the first m accepted tokens t of k_t v_t^T, per state element
+// in token order with one fmaf each -- exactly the update of m decode steps
+// (lla_decode_step), so the state after the commit equals the state after m
+// decode steps bit for bit.  m = accepted[sequence], clamped to [0, T], or T
+// when accepted is null; m = 0 leaves the state unread and unwritten.
+// One workgroup per key/value head bh (sequence bh / Hkv); k, v rows
+// bh * T + t.  A thread owns VEC consecutive elements of a row (VEC = 4 when
+// dv is a multiple of 4, else 1) at a stride of kThreads * VEC elements.
+template <typename Tin, int VEC>
+__global__ __launch_bounds__(kThreads) void k_state_commit(const Tin* __restrict__ k,
+                                                          const Tin* __restrict__ v,
+                                                          const int32_t* __restrict__ accepted,
+                                                          float* __restrict__ S, int T, int Hkv,
+                                                          int dk, int dv) {
+    constexpr int TB = 16;          // tokens staged per pass
+    constexpr int NE = 128 * 128 / (kThreads * VEC);  // element groups per thread at most
+    __shared__ float ks[TB][128], vs[TB][128];
+    typedef float vecf __attribute__((ext_vector_type(VEC)));
+    const int tid = threadIdx.x;
+    const int64_t bh = blockIdx.x;
+    int m = accepted ? accepted[bh / Hkv] : T;
+    m = m < 0 ? 0 : (m > T ? T : m);
+    if (m == 0) return;  // uniform over the workgroup
+    float* Sb = S + bh * (int64_t)dk * dv;
+    const int ngrp = dk * dv / VEC;  // VEC divides dv, so a group stays in one row
+    vecf x[NE];
+#pragma unroll
+    for (int n = 0; n < NE; ++n) {
+        const int e = tid + n * kThreads;
+        if (e < ngrp) x[n] = *reinterpret_cast<const vecf*>(Sb + (int64_t)e * VEC);
+    }
+    for (int t0 = 0; t0 < m; t0 += TB) {
+        const int nt = m - t0 < TB ? m - t0 : TB;
+        __syncthreads();  // the previous pass is done with ks, vs
+        for (int e = tid; e < nt * dk; e += kThreads)
+            ks[e / dk][e % dk] = to_f32(k[(bh * T + t0 + e / dk) * (int64_t)dk + e % dk]);
+        for (int e = tid; e < nt * dv; e += kThreads)
+            vs[e / dv][e % dv] = to_f32(v[(bh * T + t0 + e / dv) * (int64_t)dv + e % dv]);
+        __syncthreads();
+        for (int t = 0; t < nt; ++t) {
+#pragma unroll
+            for (int n = 0; n < NE; ++n) {
+                const int e = tid + n * kThreads;
+                if (e < ngrp) {
+                    const int i = e * VEC / dv, j = e * VEC % dv;
+                    const float ki = ks[t][i];
+#pragma unroll
+                    for (int u = 0; u < VEC; ++u) x[n][u] = fmaf(ki, vs[t][j + u], x[n][u]);  // rank-1 update
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int n = 0; n < NE; ++n) {
+        const int e = tid + n * kThreads;
+        if (e < ngrp) *reinterpret_cast<vecf*>(Sb + (int64_t)e * VEC) = x[n];
+    }
+}
+
+template <typename Tin>
+static hipError_t commit_t(const void* k, const void* v, const int32_t* accepted, int64_t BHkv, int Hkv,
+                           int T, int dk, int dv, float* S, hipStream_t st) {
+    if ((dv & 3) == 0)
+        hipLaunchKernelGGL((k_state_commit<Tin, 4>), dim3((unsigned)BHkv), dim3(kThreads), 0, st,
+                           (const Tin*)k, (const Tin*)v, accepted, S, T, Hkv, dk, dv);
+    else
+        hipLaunchKernelGGL((k_state_commit<Tin, 1>), dim3((unsigned)BHkv), dim3(kThreads), 0, st,
+                           (const Tin*)k, (const Tin*)v, accepted, S, T, Hkv, dk, dv);
+    return hipGetLastError();
+}
+
+hipError_t launch_state_commit(lla_dtype dtype, const void* k, const void* v, const int32_t* accepted,
+                               int64_t BHkv, int Hkv, int T, int dk, int dv, float* S, hipStream_t st) {
+    if (dtype == LLA_FP8_E4M3) return commit_t<fp8e4m3>(k, v, accepted, BHkv, Hkv, T, dk, dv, S, st);
+    if (dtype == LLA_BF16) return commit_t<bf16>(k, v, accepted, BHkv, Hkv, T, dk, dv, S, st);
+    return commit_t<float>(k, v, accepted, BHkv, Hkv, T, dk, dv, S, st);
 }
 
 __global__ __launch_bounds__(kThreads) void k_fill_zero(float* __restrict__ p, int64_t n) {
@@ -391,8 +474,8 @@ static hipError_t tokens_g(const void* q, const void* k, const void* v, int64_t 
 
 hipError_t launch_decode_tokens(lla_dtype dtype, const void* q, const void* k, const void* v,
                                 int64_t BHkv, int T, int group, int d, float* S, float* o,
-                                bool zero_start, hipStream_t st) {
-    const int z = zero_start ? 1 : 0;
+                                bool zero_start, bool keep_state, hipStream_t st) {
+    const int z = (zero_start ? 1 : 0) | (keep_state ? 2 : 0);
     if (dtype == LLA_FP8_E4M3) return tokens_g<fp8e4m3>(q, k, v, BHkv, T, group, d, S, o, z, st);
     if (dtype == LLA_BF16) return tokens_g<bf16>(q, k, v, BHkv, T, group, d, S, o, z, st);
     return tokens_g<float>(q, k, v, BHkv, T, group, d, S, o, z, st);

@@ -71,7 +71,12 @@ constexpr int kDecodeTokensQueries = 64;
 bool decode_tokens_fit(int64_t T, int dk, int dv, int64_t group);
 hipError_t launch_decode_tokens(lla_dtype dtype, const void* q, const void* k, const void* v,
                                 int64_t BHkv, int T, int group, int d, float* S, float* o,
-                                bool zero_start, hipStream_t st);
+                                bool zero_start, bool keep_state, hipStream_t st);
+// S += sum_{t < m} k_t v_t^T per key/value head (m = accepted[head / Hkv]
+// clamped to [0, T], or T for a null accepted), with the decode step's
+// per-element arithmetic; k, v: [BHkv][T][d].
+hipError_t launch_state_commit(lla_dtype dtype, const void* k, const void* v, const int32_t* accepted,
+                               int64_t BHkv, int Hkv, int T, int dk, int dv, float* S, hipStream_t st);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 
 // Shared-state heads: `group` query heads read each key/value state (dk = dv

@@ -84,7 +84,8 @@ typedef enum {
     LLA_ERR_DTYPE = 3,       /* unknown dtype */
     LLA_ERR_UNSUPPORTED = 4, /* valid request the library does not handle: fp32 with C > 64,
                                 a grouped decode shape other than dk = dv in {64, 128} with
-                                at most 16 query heads per group, unknown option bits */
+                                at most 16 query heads per group, unknown option bits,
+                                LLA_PREFILL_KEEP_STATE off the fused short-prompt route */
     LLA_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned */
     LLA_ERR_ALIAS = 6,       /* an output overlaps an input, another output or the workspace */
     LLA_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than lla_prefill_workspace_size() */
@@ -238,6 +239,18 @@ lla_status lla_prefill_gqa(const void *Q, const void *K, const void *V, lla_dtyp
  *     lla_state_init call and the read of S_0.
  */
 #define LLA_PREFILL_ZERO_STATE 1u
+/*
+ *   LLA_PREFILL_KEEP_STATE: S is read but not written -- the verify pass of
+ *     speculative decoding (blog "A 128 000 tokens, l'attention avale 85 % du
+ *     calcul", on speculative decoding adding tokens per decode iteration):
+ *     the T draft tokens' outputs o_1..o_T are computed from S_0 and S keeps
+ *     S_0, so that lla_state_commit can then advance it by the accepted
+ *     prefix only.  Runs on the fused short-prompt route (1 <= T <= 16,
+ *     dk = dv in {64, 128}, T * G <= 64 with shared-state heads), where o_t
+ *     equals what t decode steps give, bit for bit; other shapes return
+ *     LLA_ERR_UNSUPPORTED.  With T = 0 nothing is written.
+ */
+#define LLA_PREFILL_KEEP_STATE 2u
 
 /*
  * lla_prefill_gqa with options (a bitwise OR of LLA_PREFILL_* values, 0 for
@@ -250,6 +263,25 @@ lla_status lla_prefill_ex(const void *Q, const void *K, const void *V, lla_dtype
                           int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t dk,
                           int64_t dv, int64_t C, unsigned flags, float *S, float *O,
                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The commit after a verify pass (LLA_PREFILL_KEEP_STATE): for every
+ * sequence b and key/value head h,
+ *     S[b][h] += sum over t < m_b of k_t v_t^T,
+ * where m_b = accepted[b] is the number of draft tokens sequence b accepted
+ * (clamped to [0, T]; NULL means all T).  Each state element receives one
+ * fmaf per token in token order -- the update lla_decode_step applies -- so
+ * after the commit S equals the state m_b decode steps would leave, bit for
+ * bit; a sequence with m_b = 0 is neither read nor written.  K, V: the draft
+ * tokens as given to the verify pass, [B][H][T][dk] and [B][H][T][dv]
+ * (dtype), H = key/value heads; accepted: device array of B int32 (read on
+ * the device: the acceptance decision never has to reach the host); S:
+ * [B][H][dk][dv] fp32, in place.  Limits and errors as lla_prefill (no chunk
+ * size); T = 0 is a no-op.
+ */
+lla_status lla_state_commit(const void *K, const void *V, lla_dtype dtype, int64_t B, int64_t H,
+                            int64_t T, int64_t dk, int64_t dv, const int32_t *accepted, float *S,
+                            void *stream);
 
 /*
  * lla_prefill_ex without a workspace argument, for callers that cannot

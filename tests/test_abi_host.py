@@ -58,6 +58,8 @@ def lib():
     L.lla_decode_step_gqa.argtypes = [vp, vp, vp, ctypes.c_int] + [i64] * 5 + [vp, vp, vp]
     L.lla_prefill_noalloc.restype = ctypes.c_int
     L.lla_prefill_noalloc.argtypes = [vp, vp, vp, ctypes.c_int] + [i64] * 7 + [ctypes.c_uint, vp, vp, vp]
+    L.lla_state_commit.restype = ctypes.c_int
+    L.lla_state_commit.argtypes = [vp, vp, ctypes.c_int] + [i64] * 5 + [vp, vp, vp]
     L.lla_prefill_ex.restype = ctypes.c_int
     L.lla_prefill_ex.argtypes = ([vp, vp, vp, ctypes.c_int] + [i64] * 7 + [ctypes.c_uint] +
                                  [vp, vp, vp, sz, vp])
@@ -306,9 +308,32 @@ def _ex_args(b, Hq, Hkv, flags):
             b.ws_bytes, None)
 
 
-@pytest.mark.parametrize("flags", [2, 4, 0x80000000, 3])
+@pytest.mark.parametrize("flags", [4, 8, 0x80000000, 5])
 def test_prefill_ex_rejects_unknown_flags(lib, flags):
     assert lib.lla_prefill_ex(*_ex_args(Bufs(), 2, 2, flags)) == E_UNSUP
+
+
+KEEP_STATE = 2
+
+
+@pytest.mark.parametrize("change", [dict(T=17), dict(dk=96, dv=96), dict(dk=64, dv=128), dict(T=16, H=8)])
+@pytest.mark.parametrize("flags", [KEEP_STATE, KEEP_STATE | ZERO_STATE])
+def test_keep_state_runs_on_the_fused_route_only(lib, change, flags):
+    # a verify pass needs 1 <= T <= 16, dk = dv in {64, 128} and T * G <= 64;
+    # refused before any HIP call otherwise
+    b = Bufs(T=4, dk=128, dv=128)
+    Hq, Hkv = (32, 4) if "H" in change else (2, 2)  # T * G = 16 * 8 = 128 > 64
+    for key, val in change.items():
+        if key != "H":
+            setattr(b, key, val)
+    assert lib.lla_prefill_ex(*_ex_args(b, Hq, Hkv, flags)) == E_UNSUP
+    assert lib.lla_prefill_noalloc(*_noalloc_args(b, Hq, Hkv, flags)) == E_UNSUP
+
+
+def test_keep_state_with_an_empty_prompt_is_a_noop(lib):
+    b = Bufs(T=0)
+    b.q = b.k = b.v = b.O = None
+    assert lib.lla_prefill_ex(*_ex_args(b, 2, 2, KEEP_STATE | ZERO_STATE)) == OK
 
 
 @pytest.mark.parametrize("change,expect", [
@@ -354,7 +379,7 @@ def test_prefill_noalloc_checks_like_prefill_ex(lib, change, expect, flags):
 
 
 def test_prefill_noalloc_rejects_unknown_flags(lib):
-    assert lib.lla_prefill_noalloc(*_noalloc_args(Bufs(), 2, 2, 2)) == E_UNSUP
+    assert lib.lla_prefill_noalloc(*_noalloc_args(Bufs(), 2, 2, 4)) == E_UNSUP
 
 
 def test_prefill_noalloc_rejects_a_workspace_beyond_the_static_array(lib):
@@ -378,3 +403,18 @@ def test_every_multi_head_shape_fits_the_static_array(lib):
                 for C in (32, 64, 128):
                     worst = max(worst, lib.lla_prefill_workspace_size(1, BH, T, d, d, C))
     assert 0 < worst <= _scratch_bytes()
+
+
+# lla_state_commit: the commit after a verify pass
+@pytest.mark.parametrize("change,expect", [
+    (dict(S=None), E_NULL), (dict(k=None), E_NULL), (dict(v=None), E_NULL),
+    (dict(B=0), E_SHAPE), (dict(H=0), E_SHAPE), (dict(T=-1), E_SHAPE), (dict(dk=129), E_SHAPE),
+    (dict(dtype=9), E_DTYPE), (dict(S=4 * A + 4), E_ALIGN), (dict(acc=6 * A + 4), E_ALIGN),
+    (dict(S=A + 64), E_ALIAS), (dict(acc=4 * A + 64), E_ALIAS),
+    (dict(T=0, k=None, v=None), OK),
+])
+def test_state_commit_rejects(lib, change, expect):
+    d = dict(k=A, v=2 * A, dtype=BF16, B=2, H=4, T=4, dk=128, dv=128, acc=6 * A, S=4 * A)
+    d.update(change)
+    assert lib.lla_state_commit(d["k"], d["v"], d["dtype"], d["B"], d["H"], d["T"], d["dk"], d["dv"],
+                                d["acc"], d["S"], None) == expect

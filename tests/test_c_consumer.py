@@ -23,8 +23,9 @@ int main(void) {
     lla_status null_q = lla_prefill(NULL, NULL, NULL, LLA_BF16, 1, 1, 8, 2, 2, 4,
                                     NULL, NULL, NULL, 0, NULL);
     lla_status bad_flags = lla_prefill_ex((void *)16, (void *)32, (void *)48, LLA_BF16, 1, 1, 1, 8,
-                                          2, 2, 4, 2u, (float *)64, (float *)80, NULL, 0, NULL);
-    printf("%zu %zu %lld %d %d %d|%s\n", ws, ws_gqa, G, (int)null_q, (int)bad_flags,
+                                          2, 2, 4, 4u, (float *)64, (float *)80, NULL, 0, NULL);
+    lla_status null_s = lla_state_commit((void *)16, (void *)32, LLA_BF16, 1, 1, 4, 64, 64, NULL, NULL, NULL);
+    printf("%zu %zu %lld %d %d %d %d|%s\n", ws, ws_gqa, G, (int)null_q, (int)bad_flags, (int)null_s,
            lla_last_device_error(), lla_status_string(LLA_ERR_SHAPE));
     return 0;
 }
@@ -42,10 +43,10 @@ def test_plain_c_program_uses_the_library(tmp_path):
                     "-Wl,-rpath," + libdir, "-o", str(exe)], check=True)
     out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.strip()
     nums, text = out.split("|")
-    ws, ws_gqa, G, null_q, bad_flags, dev_err = (int(x) for x in nums.split())
+    ws, ws_gqa, G, null_q, bad_flags, null_s, dev_err = (int(x) for x in nums.split())
     assert ws == 16 * 16 * 128 * 128 * 4   # 16 heads x 16 segments x one fp32 state
     assert ws_gqa == 4 * 16 * 128 * 128 * 4  # the segment states belong to the 4 key/value heads
     assert G == 8
-    assert null_q == 1 and bad_flags == 4   # LLA_ERR_NULL, LLA_ERR_UNSUPPORTED
+    assert null_q == 1 and bad_flags == 4 and null_s == 1  # LLA_ERR_NULL, LLA_ERR_UNSUPPORTED
     assert dev_err == 0
     assert text == lla.library().lla_status_string(2).decode()
