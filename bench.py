@@ -447,7 +447,7 @@ def bench_decode(args, torch, lla, workloads, profiling):
         "gpu_ms_per_call_pair": gpu_p * 1e3 / ns,
         "verify": hbm_roofline("k_decode_tokens<bf16,128,512> (keep state)", v_bytes, v_ms, args.gap_ms, None,
                                "HIP events around %d back-to-back verify calls" % ns),
-        "commit": hbm_roofline("k_state_commit<bf16,4>", c_bytes, c_ms, args.gap_ms, None,
+        "commit": hbm_roofline("k_state_commit_sq<bf16,128,512>", c_bytes, c_ms, args.gap_ms, None,
                                "HIP events around %d back-to-back commits" % ns),
     }
     del verify, qs, ks, vs, S_spec

@@ -385,10 +385,64 @@ __global__ __launch_bounds__(kThreads) void k_state_commit(const Tin* __restrict
     }
 }
 
+// The same commit for square heads of 64 and 128 in the decode step's
+// layout (k_decode_step_sq): NT threads = (D/4) column groups x RG row
+// groups, each thread RPT rows of one 16-byte column group, all of its state
+// loads issued before the first use, streaming loads and stores.  Per
+// element the arithmetic is that of k_state_commit (one fmaf per token in
+// token order), so the two give identical bits.
+template <typename Tin, int D, int NT>
+__global__ __launch_bounds__(NT) void k_state_commit_sq(const Tin* __restrict__ k,
+                                                       const Tin* __restrict__ v,
+                                                       const int32_t* __restrict__ accepted,
+                                                       float* __restrict__ S, int T, int Hkv) {
+    constexpr int CG = D / 4, RG = NT / CG, RPT = D / RG;
+    static_assert(NT % CG == 0 && D % RG == 0, "thread layout must tile the state");
+    constexpr int TB = 16;  // tokens staged per pass
+    __shared__ float ks[TB][D], vs[TB][D];
+    const int tid = threadIdx.x, cg = tid % CG, rg = tid / CG;
+    const int64_t bh = blockIdx.x;
+    int m = accepted ? accepted[bh / Hkv] : T;
+    m = m < 0 ? 0 : (m > T ? T : m);
+    if (m == 0) return;  // uniform over the workgroup
+    float* Sb = S + bh * (int64_t)D * D;
+    f32x4 x[RPT];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r)
+        x[r] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sb + (rg + r * RG) * D + 4 * cg));
+    for (int t0 = 0; t0 < m; t0 += TB) {
+        const int nt = m - t0 < TB ? m - t0 : TB;
+        __syncthreads();  // the previous pass is done with ks, vs
+        for (int e = tid; e < nt * D; e += NT) {
+            ks[e / D][e % D] = to_f32(k[(bh * T + t0) * D + e]);
+            vs[e / D][e % D] = to_f32(v[(bh * T + t0) * D + e]);
+        }
+        __syncthreads();
+        for (int t = 0; t < nt; ++t) {
+            const f32x4 vj = {vs[t][4 * cg], vs[t][4 * cg + 1], vs[t][4 * cg + 2], vs[t][4 * cg + 3]};
+#pragma unroll
+            for (int r = 0; r < RPT; ++r) {
+                const float ki = ks[t][rg + r * RG];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) x[r][u] = fmaf(ki, vj[u], x[r][u]);  // rank-1 update
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < RPT; ++r)
+        __builtin_nontemporal_store(x[r], reinterpret_cast<f32x4*>(Sb + (rg + r * RG) * D + 4 * cg));
+}
+
 template <typename Tin>
 static hipError_t commit_t(const void* k, const void* v, const int32_t* accepted, int64_t BHkv, int Hkv,
                            int T, int dk, int dv, float* S, hipStream_t st) {
-    if ((dv & 3) == 0)
+    if (dk == 128 && dv == 128)
+        hipLaunchKernelGGL((k_state_commit_sq<Tin, 128, 512>), dim3((unsigned)BHkv), dim3(512), 0, st,
+                           (const Tin*)k, (const Tin*)v, accepted, S, T, Hkv);
+    else if (dk == 64 && dv == 64)
+        hipLaunchKernelGGL((k_state_commit_sq<Tin, 64, 256>), dim3((unsigned)BHkv), dim3(256), 0, st,
+                           (const Tin*)k, (const Tin*)v, accepted, S, T, Hkv);
+    else if ((dv & 3) == 0)
         hipLaunchKernelGGL((k_state_commit<Tin, 4>), dim3((unsigned)BHkv), dim3(kThreads), 0, st,
                            (const Tin*)k, (const Tin*)v, accepted, S, T, Hkv, dk, dv);
     else
