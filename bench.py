@@ -581,8 +581,9 @@ def bench_grouped(args, torch, lla, workloads, profiling):
                                     profiling.stored_traffic("decode_group"),
                                     "HIP events around the timed steps, cycling over 3 state sets")}
     # Short continuations with shared-state heads: T tokens per call through
-    # lla_prefill_gqa (fused grouped decode steps while T * G <= 64), from
-    # the cycled state sets.
+    # lla_prefill_gqa (T * G <= 64: fused grouped decode steps below 8
+    # tokens, one chunk on the matrix cores from 8 on), from the cycled
+    # state sets.
     dec["continuation"] = []
     for tc in (4, 16):
         qc, kc, vc = (x.permute(1, 2, 0, 3).contiguous()
@@ -594,11 +595,21 @@ def bench_grouped(args, torch, lla, workloads, profiling):
         wall_c, gpu_c = _timed(torch, lambda i: cont[i % 3](), nc)
         ms_c = gpu_c * 1e3 / nc
         cbytes = B * Hkv * (8 * d * d + tc * 4 * d) + B * H * tc * 6 * d
-        fmas = B * (Hkv + H) * tc * d * d  # per token: one update per state, one read per query head
+        # the method's flops per call: per state K^T V (2 d^2 T); per query
+        # head and token the state read (2 d^2) and the kept scores times V
+        # (about 2 d t for token t)
+        flops = B * Hkv * 2 * d * d * tc + B * H * (2 * d * d * tc + 2 * d * tc * (tc + 1) // 2 * 2)
+        matrix = tc >= 8
+        kname = "k_tokens_grouped<bf16,128,64,4> (matrix cores)" if matrix else \
+            "k_decode_tokens<bf16> (fused decode steps)"
+        r = hbm_roofline(kname, cbytes, ms_c, args.gap_ms, None,
+                         "HIP events around %d back-to-back calls cycling over 3 state sets" % nc)
+        r["algorithmic_flops"] = flops
+        if matrix:
+            r["mfma_frac"] = flops / (r["kernel_ms"] * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)
         dec["continuation"].append({
             "tokens_per_call": tc, "value": B * tc * nc / wall_c, "unit": "tokens/s",
-            "gpu_ms_per_call": ms_c,
-            "roofline": tokens_roofline("k_decode_tokens<bf16,128,512> (grouped)", cbytes, fmas, ms_c)})
+            "gpu_ms_per_call": ms_c, "roofline": r})
         del cont, qc, kc, vc
     del calls, qd, kd, vd, S, S0
     torch.cuda.empty_cache()

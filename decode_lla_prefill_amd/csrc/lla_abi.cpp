@@ -262,9 +262,16 @@ lla_status prefill_impl(const void* Q, const void* K, const void* V, int dt_raw,
     if (T == 0)  // S_T = S_0: untouched, or zero for a fresh prompt (never written with KEEP_STATE)
         return zero && !keep ? device_status(lla::launch_fill_zero(S, p.BH * dk * dv, s)) : LLA_OK;
     p.zero_start = zero;
-    if (fused)  // a short prompt: fused decode steps
+    if (fused) {  // a short prompt
+        // Several query heads per state (bf16 or FP8) and at least 8 tokens:
+        // one chunk on the matrix cores; otherwise, and for a verify pass,
+        // fused decode steps (the bits of T decode steps).
+        if (p.group > 1 && T >= lla::kGroupedMatrixMinTokens && !keep && dtype != LLA_F32)
+            return device_status(lla::launch_tokens_grouped(dtype, Q, K, V, p.BH, (int)T, p.group, (int)dk, S,
+                                                            O, zero, s));
         return device_status(lla::launch_decode_tokens(dtype, Q, K, V, p.BH, (int)T, p.group, (int)dk, S, O,
                                                        zero, keep, s));
+    }
     float* ws = (float*)workspace;
     st = device_status(lla::launch_segment_states(p, K, V, ws, s));
     if (st != LLA_OK) return st;

@@ -72,6 +72,14 @@ bool decode_tokens_fit(int64_t T, int dk, int dv, int64_t group);
 hipError_t launch_decode_tokens(lla_dtype dtype, const void* q, const void* k, const void* v,
                                 int64_t BHkv, int T, int group, int d, float* S, float* o,
                                 bool zero_start, bool keep_state, hipStream_t st);
+// Short continuations with shared-state heads on the matrix cores (bf16 or
+// FP8 inputs, d in {64, 128}, T * group <= 64): one chunk of the walk per
+// key/value head (k_tokens_grouped).  Not the bits of T decode steps.  Used
+// from kGroupedMatrixMinTokens tokens on: below that the fused decode steps
+// are faster (their cost grows with T, this kernel's hardly does).
+constexpr int kGroupedMatrixMinTokens = 8;
+hipError_t launch_tokens_grouped(lla_dtype dtype, const void* q, const void* k, const void* v, int64_t BHkv,
+                                 int T, int group, int d, float* S, float* o, bool zero_start, hipStream_t st);
 // S += sum_{t < m} k_t v_t^T per key/value head (m = accepted[head / Hkv]
 // clamped to [0, T], or T for a null accepted), with the decode step's
 // per-element arithmetic; k, v: [BHkv][T][d].

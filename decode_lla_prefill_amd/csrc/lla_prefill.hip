@@ -379,9 +379,12 @@ struct ScoreTiles {
 
 // `hook(ds)` runs after the matrix-core ops of depth step ds: a caller can
 // place other work (global stores, loads) between the steps.
+// `group` > 0: query row i is token i / group of a group of query heads
+// (see k_tokens_grouped), so key j is kept while j <= i / group.
 template <typename Cf, typename T, typename Hook = NoHook>
 __device__ __forceinline__ void chunk_scores(const ScoreTiles<Cf>& st, const T* Qs, const T* Ks, T* Ps,
-                                             int w, int g, int c16, const Hook& hook = Hook()) {
+                                             int w, int g, int c16, const Hook& hook = Hook(),
+                                             int group = 0) {
     // Scores of the kept triangle, computed transposed: tile (jt, it) holds
     // A^T = K_c Q_c^T, i.e. lane (g, c16) has A[i][j] for query
     // i = 16 it + c16 and keys j = 16 jt + 4g + r.  Entries with j > i are
@@ -408,9 +411,10 @@ __device__ __forceinline__ void chunk_scores(const ScoreTiles<Cf>& st, const T* 
         for (int m = 0; m < PW; ++m) {
             if (!st.own[m]) continue;
             const int i = 16 * tit[m] + c16;
+            const int last = group > 0 ? i / group : i;  // the last key row i reads
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                if (16 * tjt[m] + 4 * g + r > i) sacc[m][r] = 0.0f;
+                if (16 * tjt[m] + 4 * g + r > last) sacc[m][r] = 0.0f;
             // the lane's part of the address, recomputed per chunk rather
             // than one live register per tile
             const int at = opaque(c16 * Cf::PLD + Cf::PG * g) + Cf::p_at(tit[m], 0, 16 * tjt[m]);
@@ -865,6 +869,112 @@ __global__ __launch_bounds__(NW * kWave) void k_chunk_walk(
 }
 
 // ---------------------------------------------------------------------------
+// Short continuations with shared-state heads, on the matrix cores.  For a
+// key/value head with state S_0, T <= 16 new tokens and G query heads
+// (T G <= 64), every output is
+//     o_t^(g) = S_0^T q_t^(g) + sum_{s <= t} (q_t^(g) . k_s) v_s,
+// which is one chunk of the walk: the T G query rows, ordered token-major
+// (row r = t G + g), against the T key and value rows (rows past T are
+// zero), with key s kept for row r while s <= r / G -- every kept entry lies
+// in the walk's lower-triangle tiles.  So the chunk's helpers run unchanged:
+// scores and mask (chunk_scores with the group's mask), O = P V + Q S_0
+// (chunk_output), then S_T = S_0 + K^T V (state_hop).  One workgroup per
+// key/value head and block of BV value columns, one value tile per wave, so
+// that two or more workgroups share a compute unit and one's state loads
+// overlap another's arithmetic (the scores, from all D key columns, are
+// computed by each block).
+// S enters Q S and P enters P V as bf16 high + low pairs, as in the walk, so
+// integers are exact under the walk's bounds and floats carry the walk's
+// error; the outputs are not the bits of T decode steps (the verify pass of
+// speculative decoding keeps k_decode_tokens for that).
+// q, o: [key/value head][g][T][D] (the group's query heads are consecutive);
+// k, v: [key/value head][T][D]; S: [key/value head][D][D].
+// ---------------------------------------------------------------------------
+
+// Rows of a tile staged from global memory: row r < nrows comes from
+// src(r) (D elements, 16-byte aligned), later rows are zero.  FP8 inputs are
+// decoded to bf16 on the way.
+template <typename In, int D, int LD, int ROWS, int NTH, typename Src>
+__device__ __forceinline__ void stage_rows(bf16* lds, int nrows, const Src& src, int tid) {
+    constexpr int VE = Vec<In>::n;  // input elements per 16-byte load
+    constexpr int VPR = D / VE;
+    for (int e = tid; e < ROWS * VPR; e += NTH) {
+        const int row = e / VPR, cv = e % VPR;
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (row < nrows) x = *reinterpret_cast<const u32x4*>(src(row) + cv * VE);
+        bf16* dst = lds + row * LD + cv * VE;
+        if constexpr (sizeof(In) == 2) {
+            *reinterpret_cast<u32x4*>(dst) = x;
+        } else {  // 16 FP8 values -> two 8-element bf16 vectors
+            uint32_t y[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) fp8x4_to_bf16(x[i], y[2 * i], y[2 * i + 1]);
+            *reinterpret_cast<u32x4*>(dst) = u32x4{y[0], y[1], y[2], y[3]};
+            *reinterpret_cast<u32x4*>(dst + 8) = u32x4{y[4], y[5], y[6], y[7]};
+        }
+    }
+}
+
+template <typename In, int D, int BV, int NW>
+__global__ __launch_bounds__(NW * kWave) void k_tokens_grouped(
+    const In* __restrict__ Q, const In* __restrict__ K, const In* __restrict__ V, float* __restrict__ S,
+    float* __restrict__ O, int T, int G, int zero_start) {
+    using Cf = WalkCfg<bf16, 64, D, BV, NW>;
+    using Fr = typename Cf::Fr;
+    constexpr int NTH = Cf::NTH;
+    static_assert(Cf::ALL_WAVES, "every wave owns value tiles");
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Cf::WALK_BYTES];
+    bf16* const Qs = reinterpret_cast<bf16*>(smem);
+    bf16* const Ks = Qs + Cf::K_OFF;
+    bf16* const Vs = Qs + Cf::V_OFF;
+    bf16* const Ps = Qs + Cf::P_OFF;
+
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    constexpr int NB = D / BV;  // value blocks per state
+    const int64_t bh = blockIdx.x / NB;
+    const int v0 = BV * (int)(blockIdx.x % NB);
+    const int R = T * G;  // query rows
+    const In* Qb = Q + bh * (int64_t)G * T * D;
+    const In* Kb = K + bh * (int64_t)T * D;
+    const In* Vb = V + bh * (int64_t)T * D;
+    float* Ob = O + bh * (int64_t)G * T * D + v0;
+    float* Sb = S + bh * (int64_t)D * D + v0;
+
+    // S_0 straight into the accumulator layout (no column read when S_0 = 0)
+    f32x4 Sacc[Cf::NVW][Cf::NDT];
+    state_gmem_to_regs<Cf>(Sacc, Sb, D, D, zero_start ? 0 : BV, w, g, c16);
+    // row r = t G + g of Q is token t of query head g
+    stage_rows<In, D, Cf::LQ, 64, NTH>(Qs, R, [&](int r) { return Qb + ((int64_t)(r % G) * T + r / G) * D; }, tid);
+    stage_rows<In, D, Cf::LK, 64, NTH>(Ks, T, [&](int r) { return Kb + (int64_t)r * D; }, tid);
+    stage_rows<In, BV, Cf::LV, 64, NTH>(Vs, T, [&](int r) { return Vb + (int64_t)r * D + v0; }, tid);
+    __syncthreads();
+
+    const ScoreTiles<Cf> stiles(w);
+    chunk_scores<Cf>(stiles, Qs, Ks, Ps, w, g, c16, NoHook(), G);
+    __syncthreads();  // P complete
+
+    Fr Vf[Cf::NVW][Cf::NTS];
+    load_vfrags<Cf>(Vf, Vs, w, g, lane);
+    f32x4 Oacc[Cf::NT][Cf::NVW];
+    chunk_output<Cf>(Oacc, Sacc, Vf, Qs, Ps, w, g, c16);
+    state_hop<Cf>(Sacc, Vf, Ks, w, g, lane);
+
+    // Oacc[it][vw] holds O[row 16 it + c16][value columns 16 (w + NW vw) + 4g .. + 3]
+#pragma unroll
+    for (int it = 0; it < Cf::NT; ++it) {
+        const int r = 16 * it + c16;
+        if (r < R) {
+            float* orow = Ob + ((int64_t)(r % G) * T + r / G) * D;
+#pragma unroll
+            for (int vw = 0; vw < Cf::NVW; ++vw)
+                *reinterpret_cast<f32x4*>(orow + 16 * (w + NW * vw) + 4 * g) = Oacc[it][vw];
+        }
+    }
+    state_regs_to_gmem<Cf>(Sb, Sacc, D, D, w, g, c16);
+}
+
+// ---------------------------------------------------------------------------
 // Phase 3, wide form for d = 128 bf16 (or FP8, staged as bf16) inputs and
 // chunks of up to 64 tokens:
 // one workgroup of eight waves per (b,h) and segment covers all 128 value
@@ -1229,6 +1339,29 @@ static hipError_t launch_seg_t(const PrefillPlan& p, const void* K, const void* 
             }                                                                              \
         }                                                                                  \
     } while (0)
+
+constexpr int kGroupedBV = 64;  // value columns per workgroup of k_tokens_grouped
+
+template <typename In>
+static hipError_t tokens_grouped_t(const void* q, const void* k, const void* v, int64_t BHkv, int T, int G,
+                                   int d, float* S, float* o, int zero, hipStream_t st) {
+    if (d == 128) {
+        constexpr int BV = kGroupedBV;
+        hipLaunchKernelGGL((k_tokens_grouped<In, 128, BV, BV / 16>), dim3((unsigned)(BHkv * (128 / BV))),
+                           dim3(BV / 16 * kWave), 0, st, (const In*)q, (const In*)k, (const In*)v, S, o, T, G, zero);
+    } else {
+        hipLaunchKernelGGL((k_tokens_grouped<In, 64, 64, 4>), dim3((unsigned)BHkv), dim3(4 * kWave), 0, st,
+                           (const In*)q, (const In*)k, (const In*)v, S, o, T, G, zero);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_tokens_grouped(lla_dtype dtype, const void* q, const void* k, const void* v, int64_t BHkv,
+                                 int T, int group, int d, float* S, float* o, bool zero_start, hipStream_t st) {
+    const int z = zero_start ? 1 : 0;
+    if (dtype == LLA_FP8_E4M3) return tokens_grouped_t<fp8e4m3>(q, k, v, BHkv, T, group, d, S, o, z, st);
+    return tokens_grouped_t<bf16>(q, k, v, BHkv, T, group, d, S, o, z, st);
+}
 
 hipError_t launch_chunk_walk(const PrefillPlan& p, const void* Q, const void* K, const void* V,
                              float* S, float* O, float* ws, hipStream_t st) {

@@ -153,11 +153,16 @@ size_t lla_prefill_workspace_size(int64_t B, int64_t H, int64_t T, int64_t dk,
  * Short prompts -- a few tokens continuing an existing state, where prefill
  * behaves like decode (deck: "Prefill and decode") -- take another route:
  * for 1 <= T <= 16 with dk = dv in {64, 128} (and, with shared-state heads,
- * T * G <= 64) the call runs T fused decode steps in one kernel (the state
- * read and written once, held in registers between the steps) with the
- * arithmetic of lla_decode_step (lla_decode_step_gqa), so its results equal T
- * successive decode-step calls bit for bit.  The workspace is not
- * touched on this route (it is still validated).
+ * T * G <= 64) the state is read and written once for all T tokens.  With
+ * one query head per state, or fp32 inputs, the call runs T fused decode
+ * steps (the state held in registers between the steps) with the arithmetic
+ * of lla_decode_step (lla_decode_step_gqa), so its results equal T
+ * successive decode-step calls bit for bit.  With several query heads per
+ * state, bf16 or FP8 inputs and T >= 8 it runs the T tokens' G query heads
+ * as one chunk on the matrix cores (the numerics of the chunked prefill
+ * above: integers exact within its bounds, floats within its error, not the
+ * bits of decode steps); with T < 8 the fused decode steps are used there
+ * too.  The workspace is not touched on this route (it is still validated).
  */
 lla_status lla_prefill(const void *Q, const void *K, const void *V, lla_dtype dtype,
                        int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int64_t C,
@@ -221,7 +226,7 @@ lla_status lla_decode_step(const void *q, const void *k, const void *v, lla_dtyp
  * segment scan run once per key/value head; each query head's walk reads
  * them.  When G > 1 the walks always start from the workspace (which then
  * holds at least one state per key/value head).  Short prompts with
- * T * G <= 64 take the fused decode-step route described at lla_prefill.
+ * T * G <= 64 take the short-prompt route described at lla_prefill.
  */
 size_t lla_prefill_gqa_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t T,
                                       int64_t dk, int64_t dv, int64_t C);

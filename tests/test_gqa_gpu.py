@@ -4,7 +4,10 @@ Query head h reads key/value head h // G, G = Hq / Hkv.  The prefill and the
 decode step are checked against the oracle (exact on integer inputs, within
 the bf16 tolerance on gaussian ones), against the plain call on key/value
 heads repeated over their group (the same arithmetic: identical bits), and at
-the full benchmark sizes on sampled heads."""
+the full benchmark sizes on sampled heads.  Short prompts with groups run on
+the matrix cores (bf16, FP8, at least 8 tokens) or as fused grouped decode
+steps (fewer tokens, fp32 inputs, verify passes), and are checked
+accordingly."""
 import numpy as np
 import pytest
 import torch
@@ -22,9 +25,10 @@ def dev():
     return need_gpu()
 
 
-def _run_prefill(q, k, v, S0, C, dev):
+def _run_prefill(q, k, v, S0, C, dev, zero_state=False):
     S = S0.to(dev, torch.float32).contiguous().clone()
-    o = lla.prefill(q.to(dev).contiguous(), k.to(dev).contiguous(), v.to(dev).contiguous(), S, chunk=C)
+    o = lla.prefill(q.to(dev).contiguous(), k.to(dev).contiguous(), v.to(dev).contiguous(), S, chunk=C,
+                    zero_state=zero_state)
     torch.cuda.synchronize()
     return o, S
 
@@ -179,26 +183,49 @@ def test_gqa_decode_full_size_sampled(dev):
 
 # ---- short continuations with shared-state heads ---------------------------------
 
-@pytest.mark.parametrize("B,Hq,Hkv,T,d,dtype", [
-    (2, 8, 2, 5, 128, torch.bfloat16), (1, 16, 1, 4, 128, torch.bfloat16),
-    (3, 4, 2, 16, 64, torch.float32), (2, 6, 3, 7, 64, torch.float8_e4m3fn),
-    (1, 8, 1, 8, 128, torch.bfloat16),
+@pytest.mark.parametrize("B,Hq,Hkv,T,d,dtype,keep", [
+    (2, 8, 2, 5, 128, torch.bfloat16, False), (2, 8, 2, 5, 128, torch.bfloat16, True),
+    (1, 16, 1, 4, 128, torch.bfloat16, False), (3, 4, 2, 16, 64, torch.float32, False),
+    (3, 4, 2, 16, 64, torch.float32, True), (2, 6, 3, 7, 64, torch.float8_e4m3fn, False),
+    (1, 8, 1, 8, 128, torch.bfloat16, True), (2, 4, 1, 1, 128, torch.bfloat16, False),
 ])
-def test_gqa_short_prompt_equals_grouped_decode_steps(dev, B, Hq, Hkv, T, d, dtype):
-    """T <= 16 tokens with T * G <= 64 run as fused grouped decode steps: the
-    same bits as T lla_decode_step_gqa calls."""
-    print("gqa short prompt", B, Hq, Hkv, T, d, dtype, flush=True)
+def test_gqa_short_prompt_decode_steps_route_equals_grouped_decode_steps(dev, B, Hq, Hkv, T, d, dtype, keep):
+    """T <= 16 tokens with T * G <= 64 that run as fused grouped decode steps
+    -- fewer than 8 tokens, fp32 inputs, and every verify pass (the state
+    kept) -- give the same bits as T lla_decode_step_gqa calls."""
+    print("gqa short prompt, decode-step route", B, Hq, Hkv, T, d, dtype, keep, flush=True)
     q, k, v = workloads.gaussian(B, Hq, T, d, d, seed_base=T * 3 + Hq, scale=d ** -0.5, dtype=dtype,
                                  device=dev, Hkv=Hkv)
     S0 = torch.randn((B, Hkv, d, d), generator=torch.Generator(device=dev).manual_seed(T), device=dev)
     S_a = S0.clone()
-    o_a = lla.prefill(q, k, v, S_a, chunk=64)
+    o_a = lla.prefill(q, k, v, S_a, chunk=64, keep_state=keep)
     S_b = S0.clone()
     o_b = torch.stack([lla.decode_step(q[:, :, t].contiguous(), k[:, :, t].contiguous(),
                                        v[:, :, t].contiguous(), S_b) for t in range(T)], dim=2)
     torch.cuda.synchronize()
     assert torch.equal(o_a, o_b)
-    assert torch.equal(S_a, S_b)
+    assert torch.equal(S_a, S0 if keep else S_b)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,d,dtype", [
+    (4, 32, 8, 16, 128, torch.bfloat16), (1, 8, 1, 8, 128, torch.bfloat16), (3, 4, 2, 16, 64, torch.bfloat16),
+    (2, 6, 2, 9, 128, torch.bfloat16), (2, 8, 2, 10, 64, torch.float8_e4m3fn),
+    (1, 6, 1, 8, 128, torch.float8_e4m3fn), (2, 8, 2, 5, 128, torch.bfloat16),
+])
+def test_gqa_short_prompt_on_matrix_cores_within_the_bar(dev, B, Hq, Hkv, T, d, dtype):
+    """With several query heads per state, bf16 and FP8 short prompts of 8 to
+    16 tokens run as one chunk on the matrix cores (T G query rows, ragged
+    when not a multiple of 16): within the floating-point bar of the oracle,
+    from a gaussian state, fresh or continued.  (Shorter ones, last case,
+    take the decode-step route, also within the bar.)"""
+    print("gqa short prompt, matrix cores", B, Hq, Hkv, T, d, dtype, flush=True)
+    scale = 1.0 if dtype == torch.float8_e4m3fn else d ** -0.5
+    q, k, v = workloads.gaussian(B, Hq, T, d, d, seed_base=T * 5 + Hq, scale=scale, dtype=dtype, Hkv=Hkv)
+    S0 = torch.randn((B, Hkv, d, d), generator=torch.Generator().manual_seed(T + 1))
+    for fresh in (False, True):
+        o, S = _run_prefill(q, k, v, torch.zeros_like(S0) if fresh else S0, 64, dev, zero_state=fresh)
+        O_ref, S_ref = oracle.grouped_recurrence(q, k, v, None if fresh else S0, nthreads=8)
+        assert rel_err(np64(o), O_ref) <= TOL and rel_err(np64(S), S_ref) <= TOL, fresh
 
 
 @pytest.mark.parametrize("Hq,Hkv,T", [(8, 1, 8), (8, 1, 9), (4, 1, 16), (4, 1, 17), (2, 1, 1)])
