@@ -602,7 +602,8 @@ def bench_grouped(args, torch, lla, workloads, profiling):
         matrix = tc >= 8
         kname = "k_tokens_grouped<bf16,128,64,4> (matrix cores)" if matrix else \
             "k_decode_tokens<bf16> (fused decode steps)"
-        r = hbm_roofline(kname, cbytes, ms_c, args.gap_ms, None,
+        r = hbm_roofline(kname, cbytes, ms_c, args.gap_ms,
+                         profiling.stored_traffic("tokens_grouped") if tc == 16 else None,
                          "HIP events around %d back-to-back calls cycling over 3 state sets" % nc)
         r["algorithmic_flops"] = flops
         if matrix:

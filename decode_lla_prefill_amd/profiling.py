@@ -48,7 +48,7 @@ COPY_BYTES = 1 << 30
 
 # The workloads ``run`` can drive (keys of workloads.CONFIGS).
 WORKLOADS = ("prefill_T8192", "prefill_T8192_fp8", "prefill_B4_T1024", "prefill_T131072",
-             "decode_B256", "decode_B256_gqa")
+             "decode_B256", "decode_B256_gqa", "decode_B256_gqa_T16")
 
 # what decides a prefill kernel's work: its code and the plan that cuts the
 # shape into segments
@@ -80,6 +80,11 @@ KERNELS = {
                     ("lla_decode.hip", "lla_device.h"), "decode_B256"),
     "decode_group": (("k_decode_group",), 256 * 8 * 512, "decode_group_B256_Hq32_Hkv8_traffic.txt",
                      ("lla_decode.hip", "lla_device.h"), "decode_B256_gqa"),
+    # 16-token continuations of the grouped states: one 4-wave workgroup per
+    # key/value head and 64 value columns
+    "tokens_grouped": (("k_tokens_groupedIDF16bLi128ELi64ELi4E", "k_tokens_grouped<__bf16, 128, 64, 4>"),
+                       256 * 8 * 2 * 256, "tokens_grouped_B256_Hq32_Hkv8_T16_traffic.txt",
+                       PREFILL_SOURCES, "decode_B256_gqa_T16"),
 }
 
 SIMD_NUM = 256 * 4  # MI355X: 256 compute units of 4 SIMDs (the SIMD_NUM of MfmaUtil)
@@ -160,7 +165,7 @@ def run(launches: int, which=WORKLOADS) -> None:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     for name in which:
-        cfg = workloads.CONFIGS[name]
+        cfg = workloads.CONFIGS.get(name)
         if name.startswith("prefill"):
             rotate = 2 if cfg.T >= 65536 else 4
             q0, k0, v0 = workloads.config_inputs(cfg, device=dev)
@@ -181,6 +186,19 @@ def run(launches: int, which=WORKLOADS) -> None:
                 c()
             torch.cuda.synchronize()
             del calls, S, qd, kd, vd
+        elif name == "decode_B256_gqa_T16":
+            # 16-token continuations of the grouped states, cycling over
+            # three state sets (lla_prefill_gqa, short-prompt route)
+            cfg = workloads.CONFIGS["decode_B256_gqa"]
+            S0 = workloads.random_state(cfg, device=dev)
+            states = [S0] + [S0.clone() for _ in range(2)]
+            qc, kc, vc = (x.permute(1, 2, 0, 3).contiguous()
+                          for x in workloads.decode_inputs(cfg, 16, device=dev))
+            calls = [PreparedPrefill(qc, kc, vc, states[i], cfg.C) for i in range(3)]
+            for i in range(launches):
+                calls[i % 3]()
+            torch.cuda.synchronize()
+            del calls, states, S0, qc, kc, vc
         elif name == "decode_B256_gqa":
             # three state sets, so that each step reads its states from HBM
             S0 = workloads.random_state(cfg, device=dev)

@@ -49,6 +49,8 @@ def test_kernel_grids_follow_the_plan():
     assert profiling.KERNELS["decode_step"][1] == c.B * c.H * 512
     c = workloads.CONFIGS["decode_B256_gqa"]
     assert profiling.KERNELS["decode_group"][1] == c.B * c.kv_heads * 512
+    # two 64-column blocks per 128 x 128 state, four waves each
+    assert profiling.KERNELS["tokens_grouped"][1] == c.B * c.kv_heads * 2 * 256
 
 
 def test_kernel_names_match_in_both_trace_forms():
