@@ -53,8 +53,9 @@
  * |q_t . k_s| and every state entry is at most 2^16 in magnitude and every
  * other partial sum (of P V, Q S, K^T V and O) stays below 2^24; one bf16
  * value alone would hold integers exactly only up to 256.  The decode
- * kernels (and the short-prompt route) run fp32 FMAs: exact while partial
- * sums stay below 2^24.  fp32 inputs use fp32 matrix-core instructions
+ * kernels (and the short-prompt route's fused decode steps) run fp32 FMAs:
+ * exact while partial sums stay below 2^24; the short-prompt route's chunk
+ * on the matrix cores (grouped heads, T >= 8) has the bounds above.  fp32 inputs use fp32 matrix-core instructions
  * throughout, exact under the same 2^24 condition.  FP8 inputs (the 8-bit format
  * that the blog "A 128 000 tokens, l'attention avale 85 % du calcul" says the
  * attention measurements it reports use, for the arithmetic and the cache
