@@ -31,6 +31,11 @@ fewer rows; decode applies the rank-1 update, then reads the state.
 heads (several query heads reading one key/value head's state) by repeating
 each key/value head over its group and calling the two functions above.
 
+:func:`gated_recurrence` and :func:`gated_decode_step` give the gated
+(decayed) state under the reading ``S_t = g_t S_{t-1} + k_t v_t^T`` with one
+scalar gate per stream and token (the pages cite the gated chunkwise form but
+state no gate); with ``g = 1`` they are the two functions above.
+
 :func:`decode_e4m3` gives the values of FP8 (E4M3) inputs from the format's
 definition, so FP8 tensors enter the oracle exactly as they do the GPU.
 
@@ -97,6 +102,11 @@ def _load():
             lib.lla_oracle_recurrence.restype = ctypes.c_int
             lib.lla_oracle_decode_step.argtypes = [dp, dp, dp, dp, dp, i64, i64, i64]
             lib.lla_oracle_decode_step.restype = ctypes.c_int
+            lib.lla_oracle_gated_recurrence.argtypes = [dp, dp, dp, dp, dp, dp, i64, i64, i64, i64,
+                                                        ctypes.c_int]
+            lib.lla_oracle_gated_recurrence.restype = ctypes.c_int
+            lib.lla_oracle_gated_decode_step.argtypes = [dp, dp, dp, dp, dp, dp, i64, i64, i64]
+            lib.lla_oracle_gated_decode_step.restype = ctypes.c_int
             _lib = lib
     return _lib
 
@@ -180,6 +190,59 @@ def decode_step(q, k, v, S):
                                         BH, dk, dv)
     if rc != 0:
         raise RuntimeError("oracle decode step rejected its arguments")
+    return o, S
+
+
+# --- gated (decayed) state, float64 ------------------------------------------
+#
+# Slide deck "Chunking, causality, and parallel prefill", section "Boundary,
+# evidence, and sources": it cites the chunkwise form of gated linear
+# attention but states no gate.  Reading taken (a reading, not the pages'
+# formula): one scalar gate g_t per (batch, head) stream and token, applied
+# to the previous state before the token's update,
+#     S_t = g_t S_{t-1} + k_t v_t^T,   o_t = S_t^T q_t.
+# With g = 1 it is the recurrence above.
+
+
+def gated_recurrence(q, k, v, gate, S0=None, nthreads: int = 1):
+    """Token-by-token gated recurrence in float64.
+
+    q, k: [..., T, dk]; v: [..., T, dv]; gate: [..., T]; S0: [..., dk, dv] or
+    None (zeros).  Returns ``(O, S_T)``."""
+    q, k, v, gate = _f64(q), _f64(k), _f64(v), _f64(gate)
+    lead = q.shape[:-2]
+    T, dk = q.shape[-2], q.shape[-1]
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:-1] != q.shape[:-1] or gate.shape != q.shape[:-1]:
+        raise ValueError("shape mismatch: q %s k %s v %s gate %s" % (q.shape, k.shape, v.shape, gate.shape))
+    BH = int(np.prod(lead)) if lead else 1
+    S = np.zeros(lead + (dk, dv)) if S0 is None else _f64(S0).copy()
+    if S.shape != lead + (dk, dv):
+        raise ValueError("S0 shape %s, expected %s" % (S.shape, lead + (dk, dv)))
+    O = np.zeros(lead + (T, dv))
+    rc = _load().lla_oracle_gated_recurrence(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(S), _ptr(O),
+                                             BH, T, dk, dv, int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle gated recurrence rejected its arguments")
+    return O, S
+
+
+def gated_decode_step(q, k, v, gate, S):
+    """One gated decode step in float64: ``S = g S + k v^T``, then
+    ``o = S^T q``.  q, k: [..., dk]; v: [..., dv]; gate: [...]; S: [..., dk,
+    dv].  Returns ``(o, S_new)`` without modifying the caller's S."""
+    q, k, v, gate = _f64(q), _f64(k), _f64(v), _f64(gate)
+    S = _f64(S).copy()
+    lead = q.shape[:-1]
+    dk, dv = q.shape[-1], v.shape[-1]
+    if gate.shape != lead:
+        raise ValueError("gate shape %s, expected %s" % (gate.shape, lead))
+    BH = int(np.prod(lead)) if lead else 1
+    o = np.zeros(lead + (dv,))
+    rc = _load().lla_oracle_gated_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(S), _ptr(o),
+                                              BH, dk, dv)
+    if rc != 0:
+        raise RuntimeError("oracle gated decode step rejected its arguments")
     return o, S
 
 

@@ -29,8 +29,20 @@
  * streams round-robin.  No blocking, fusion or reordering beyond the
  * recurrence itself: the update is applied, then the state is read.
  *
+ * Gated (decayed) state -- a reading, not a formula of the pages: the deck's
+ * "Boundary, evidence, and sources" cites the chunkwise form of gated linear
+ * attention without stating a gate.  Read as one scalar gate g_t per stream
+ * and token, applied to the previous state before the token's update:
+ *
+ *       S_t = g_t S_{t-1} + k_t v_t^T,     o_t = S_t^T q_t
+ *
+ * With g_t = 1 this is the recurrence above, operation for operation
+ * (1.0 * x == x).  gate : [BH][T].
+ *
  * Parity: pinned by the tests against the deck's printed trace values, the
- * closed forms O = tril(Q K^T) V + Q S_0 and S_T = S_0 + K^T V, and brute force.
+ * closed forms O = tril(Q K^T) V + Q S_0 and S_T = S_0 + K^T V, and brute force;
+ * the gated form against its own closed form (tril(Q K^T) weighted by the
+ * products of the gates in between), g = 1 (the trace) and g = 0.
  *
  * Build: gcc -O2 -ffp-contract=off -fPIC -shared -pthread (no FMA contraction,
  * so each product and each sum is rounded as written).
@@ -42,6 +54,7 @@
 
 typedef struct {
     const double *q, *k, *v;
+    const double *gate;   /* [BH][T] or NULL (no gate) */
     double *S, *O;
     int64_t BH, T, dk, dv;
     int64_t ckpt_every;   /* > 0: copy S after every ckpt_every tokens */
@@ -69,6 +82,15 @@ static void recurrence_token(const double *qt, const double *kt, const double *v
     }
 }
 
+/* One token of the gated recurrence: S = g S, then S += k v^T, then o = S^T q. */
+static void gated_token(const double *qt, const double *kt, const double *vt, double g,
+                        double *S, double *ot, int64_t dk, int64_t dv)
+{
+    for (int64_t i = 0; i < dk * dv; ++i)
+        S[i] = g * S[i];
+    recurrence_token(qt, kt, vt, S, ot, dk, dv);
+}
+
 static void *worker(void *arg)
 {
     job_t *jb = (job_t *)arg;
@@ -78,8 +100,12 @@ static void *worker(void *arg)
         double *S = jb->S + bh * dk * dv;
         for (int64_t t = 0; t < T; ++t) {
             const int64_t row = bh * T + t;
-            recurrence_token(jb->q + row * dk, jb->k + row * dk, jb->v + row * dv,
-                             S, jb->O + row * dv, dk, dv);
+            if (jb->gate)
+                gated_token(jb->q + row * dk, jb->k + row * dk, jb->v + row * dv, jb->gate[row],
+                            S, jb->O + row * dv, dk, dv);
+            else
+                recurrence_token(jb->q + row * dk, jb->k + row * dk, jb->v + row * dv,
+                                 S, jb->O + row * dv, dk, dv);
             if (jb->ckpt && jb->ckpt_every > 0 && (t + 1) % jb->ckpt_every == 0) {
                 const int64_t c = (t + 1) / jb->ckpt_every - 1;
                 memcpy(jb->ckpt + (bh * n_ckpt + c) * dk * dv, S,
@@ -97,10 +123,9 @@ static void *worker(void *arg)
  * copied to ckpt[bh][c] (floor(T / ckpt_every) checkpoints per stream).
  * Returns 0, or -1 on a bad argument.
  */
-int lla_oracle_recurrence(const double *q, const double *k, const double *v,
-                          double *S, double *O,
-                          int64_t BH, int64_t T, int64_t dk, int64_t dv,
-                          int64_t ckpt_every, double *ckpt, int nthreads)
+static int run_jobs(const double *q, const double *k, const double *v, const double *gate,
+                    double *S, double *O, int64_t BH, int64_t T, int64_t dk, int64_t dv,
+                    int64_t ckpt_every, double *ckpt, int nthreads)
 {
     if (BH < 0 || T < 0 || dk < 1 || dv < 1 || !S || (T > 0 && (!q || !k || !v || !O)))
         return -1;
@@ -116,7 +141,7 @@ int lla_oracle_recurrence(const double *q, const double *k, const double *v,
         return -1;
     }
     for (int i = 0; i < nthreads; ++i) {
-        job_t j = {q, k, v, S, O, BH, T, dk, dv, ckpt_every, ckpt, i, nthreads};
+        job_t j = {q, k, v, gate, S, O, BH, T, dk, dv, ckpt_every, ckpt, i, nthreads};
         jobs[i] = j;
     }
     /* Each job owns a disjoint set of streams; a job whose thread cannot be
@@ -138,6 +163,28 @@ int lla_oracle_recurrence(const double *q, const double *k, const double *v,
     return 0;
 }
 
+int lla_oracle_recurrence(const double *q, const double *k, const double *v,
+                          double *S, double *O,
+                          int64_t BH, int64_t T, int64_t dk, int64_t dv,
+                          int64_t ckpt_every, double *ckpt, int nthreads)
+{
+    return run_jobs(q, k, v, NULL, S, O, BH, T, dk, dv, ckpt_every, ckpt, nthreads);
+}
+
+/*
+ * The gated recurrence (see the header): gate [BH][T], one g_t per stream and
+ * token.  S holds S_0 on entry and S_T on return.  Returns 0, or -1 on a bad
+ * argument.
+ */
+int lla_oracle_gated_recurrence(const double *q, const double *k, const double *v,
+                                const double *gate, double *S, double *O,
+                                int64_t BH, int64_t T, int64_t dk, int64_t dv, int nthreads)
+{
+    if (T > 0 && !gate)
+        return -1;
+    return run_jobs(q, k, v, gate, S, O, BH, T, dk, dv, 0, NULL, nthreads);
+}
+
 /*
  * One decode step for BH independent streams: the 1x1-triangle case of the
  * deck's "Mechanism map" -- S += k v^T, then o = S^T q.
@@ -151,5 +198,18 @@ int lla_oracle_decode_step(const double *q, const double *k, const double *v,
     for (int64_t bh = 0; bh < BH; ++bh)
         recurrence_token(q + bh * dk, k + bh * dk, v + bh * dv, S + bh * dk * dv,
                          o + bh * dv, dk, dv);
+    return 0;
+}
+
+/* One gated decode step per stream: S = g S, S += k v^T, o = S^T q; gate [BH]. */
+int lla_oracle_gated_decode_step(const double *q, const double *k, const double *v,
+                                 const double *gate, double *S, double *o,
+                                 int64_t BH, int64_t dk, int64_t dv)
+{
+    if (BH < 0 || dk < 1 || dv < 1 || (BH > 0 && (!q || !k || !v || !gate || !S || !o)))
+        return -1;
+    for (int64_t bh = 0; bh < BH; ++bh)
+        gated_token(q + bh * dk, k + bh * dk, v + bh * dv, gate[bh], S + bh * dk * dv,
+                    o + bh * dv, dk, dv);
     return 0;
 }
