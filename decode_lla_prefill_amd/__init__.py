@@ -38,7 +38,8 @@ EXPORTS = ("lla_status_string", "lla_last_device_error", "lla_state_init",
            "lla_prefill_segment_chunks", "lla_prefill_workspace_size", "lla_prefill",
            "lla_prefill_segment_states", "lla_prefill_state_scan", "lla_prefill_chunks",
            "lla_decode_step", "lla_prefill_gqa_workspace_size", "lla_prefill_gqa",
-           "lla_decode_step_gqa", "lla_prefill_ex", "lla_prefill_noalloc", "lla_state_commit")
+           "lla_decode_step_gqa", "lla_prefill_ex", "lla_prefill_noalloc", "lla_state_commit",
+           "lla_prefill_gated_workspace_size", "lla_prefill_gated", "lla_decode_step_gated")
 PREFILL_ZERO_STATE = 1  # lla_prefill_ex: start from S_0 = 0 without reading S
 PREFILL_KEEP_STATE = 2  # lla_prefill_ex: read S, do not write it (verify pass of draft tokens)
 
@@ -102,6 +103,13 @@ def library():
         lib.lla_prefill_noalloc.restype = st
         lib.lla_state_commit.argtypes = [vp, vp, ci, i64, i64, i64, i64, i64, vp, vp, vp]
         lib.lla_state_commit.restype = st
+        lib.lla_prefill_gated_workspace_size.argtypes = [i64] * 6
+        lib.lla_prefill_gated_workspace_size.restype = sz
+        lib.lla_prefill_gated.argtypes = [vp, vp, vp, vp, ci, i64, i64, i64, i64, i64, i64, ctypes.c_uint,
+                                          vp, vp, vp, sz, vp]
+        lib.lla_prefill_gated.restype = st
+        lib.lla_decode_step_gated.argtypes = [vp, vp, vp, vp, ci, i64, i64, i64, i64, vp, vp, vp]
+        lib.lla_decode_step_gated.restype = st
         _lib = lib
     return _lib
 
@@ -249,6 +257,37 @@ def prefill(q, k, v, state, chunk: int, out=None, workspace=None, zero_state: bo
     return out
 
 
+def prefill_gated_workspace_size(B, H, T, dk, dv, chunk) -> int:
+    return int(library().lla_prefill_gated_workspace_size(B, H, T, dk, dv, chunk))
+
+
+def prefill_gated(q, k, v, gate, state, chunk: int, out=None, workspace=None, zero_state: bool = False):
+    """Prefill with a decayed state (lla_prefill_gated): ``S_t = g_t S_{t-1}
+    + k_t v_t^T``, ``o_t = S_t^T q_t``, one gate per (b,h) and token.
+    ``gate``: fp32 [B,H,T]; q, k, v: [B,H,T,*] (one query head per state).
+    Returns o [B,H,T,dv] fp32; ``state`` goes S_0 -> S_T in place."""
+    lib = library()
+    B, Hq, Hkv, T, dk, dv = _qkv_shape(q, k, v)
+    if Hq != Hkv:
+        raise ValueError("the gated prefill takes one query head per state")
+    _need(gate, "gate", dtype=torch.float32, ndim=3)
+    if tuple(gate.shape) != (B, Hq, T):
+        raise ValueError("gate shape %s, expected %s" % (tuple(gate.shape), (B, Hq, T)))
+    _state_check(state, B, Hq, dk, dv)
+    out = _out(out, (B, Hq, T, dv), q.device)
+    need = prefill_gated_workspace_size(B, Hq, T, dk, dv, chunk)
+    if workspace is None and need:
+        workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
+    if workspace is not None:
+        _need(workspace, "workspace")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _same_device(q.device, gate=gate, state=state, out=out, workspace=workspace)
+    _check(lib.lla_prefill_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _dtype_code(q), B, Hq, T, dk, dv, chunk,
+                                 PREFILL_ZERO_STATE if zero_state else 0, _ptr(state), _ptr(out), _ptr(workspace),
+                                 ws_bytes, _stream(q)), "lla_prefill_gated")
+    return out
+
+
 def prefill_noalloc(q, k, v, state, chunk: int, out=None, zero_state: bool = False):
     """:func:`prefill` through lla_prefill_noalloc: the library takes the
     workspace from its static per-device array instead of the caller, so the
@@ -366,6 +405,24 @@ def decode_step(q, k, v, state, out=None):
     _same_device(q.device, state=state, out=out)
     fn, args = _step_call(lib, q, k, v, state, out, B, Hq, Hkv, dk, dv)
     _check(fn(*args, _stream(q)), fn.__name__)
+    return out
+
+
+def decode_step_gated(q, k, v, gate, state, out=None):
+    """One gated decode step (lla_decode_step_gated): ``state = g state + k
+    v^T`` in place, then o = state^T q.  q, k, v: [B,H,d*]; gate: fp32 [B,H]."""
+    lib = library()
+    B, Hq, Hkv, dk, dv = _step_shape(q, k, v)
+    if Hq != Hkv:
+        raise ValueError("the gated decode step takes one query head per state")
+    _need(gate, "gate", dtype=torch.float32, ndim=2)
+    if tuple(gate.shape) != (B, Hq):
+        raise ValueError("gate shape %s, expected %s" % (tuple(gate.shape), (B, Hq)))
+    _state_check(state, B, Hq, dk, dv)
+    out = _out(out, (B, Hq, dv), q.device)
+    _same_device(q.device, gate=gate, state=state, out=out)
+    _check(lib.lla_decode_step_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _dtype_code(q), B, Hq, dk, dv,
+                                     _ptr(state), _ptr(out), _stream(q)), "lla_decode_step_gated")
     return out
 
 

@@ -101,6 +101,15 @@ size_t ws_bytes_for(const lla::PrefillPlan& p) {
     return (size_t)(p.BH * p.n_seg * (int64_t)p.dk * p.dv) * sizeof(float);
 }
 
+// The gated prefill's workspace: the segment states, then one decay (float)
+// per (b,h) and segment; none with a single segment.
+size_t gated_ws_bytes_for(const lla::PrefillPlan& p) {
+    if (p.n_seg <= 1) return 0;
+    return (size_t)(p.BH * p.n_seg * ((int64_t)p.dk * p.dv + 1)) * sizeof(float);
+}
+
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
 // Which buffers a prefill phase touches; null entries are not used.
 struct PrefillBufs {
     const void *Q, *K, *V;
@@ -280,8 +289,10 @@ lla_status prefill_impl(const void* Q, const void* K, const void* V, int dt_raw,
     return device_status(lla::launch_chunk_walk(p, Q, K, V, S, O, ws, s));
 }
 
+// gate: null, or one gate per (b,h) (gated step, one query head per state).
 lla_status decode_impl(const void* q, const void* k, const void* v, int dt_raw, int64_t B,
-                       Heads h, int64_t dk, int64_t dv, float* S, float* o, void* stream) {
+                       Heads h, int64_t dk, int64_t dv, float* S, float* o, void* stream,
+                       const float* gate = nullptr, bool gated = false) {
     lla_status st = check_heads(h);
     if (st != LLA_OK) return st;
     st = check_sizes(B, h.q, 1, dk, dv, -1);
@@ -290,8 +301,9 @@ lla_status decode_impl(const void* q, const void* k, const void* v, int dt_raw, 
     const lla_dtype dtype = (lla_dtype)dt_raw;
     const int64_t group = h.q / h.kv;
     if (group > 1 && !lla::decode_group_fit(group, (int)dk, (int)dv)) return LLA_ERR_UNSUPPORTED;
-    if (!q || !k || !v || !S || !o) return LLA_ERR_NULL;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(S) || !aligned16(o))
+    if (!q || !k || !v || !S || !o || (gated && !gate)) return LLA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(S) || !aligned16(o) ||
+        (gated && !aligned4(gate)))
         return LLA_ERR_ALIGN;
     const int64_t BHq = B * h.q, BHkv = B * h.kv, es = elem_size(dtype);
     const Span sq = span(q, BHq * dk * es), sk = span(k, BHkv * dk * es), sv = span(v, BHkv * dv * es);
@@ -299,7 +311,13 @@ lla_status decode_impl(const void* q, const void* k, const void* v, int dt_raw, 
     if (overlap(ss, sq) || overlap(ss, sk) || overlap(ss, sv) || overlap(ss, so) || overlap(so, sq) ||
         overlap(so, sk) || overlap(so, sv))
         return LLA_ERR_ALIAS;
+    if (gated) {
+        const Span sg = span(gate, BHq * 4);
+        if (overlap(ss, sg) || overlap(so, sg)) return LLA_ERR_ALIAS;
+    }
     hipStream_t s = (hipStream_t)stream;
+    if (gated)
+        return device_status(lla::launch_decode_step_gated(dtype, q, k, v, gate, BHkv, (int)dk, (int)dv, S, o, s));
     if (group > 1)
         return device_status(lla::launch_decode_group(dtype, q, k, v, BHkv, (int)group, (int)dk, S, o, s));
     return device_status(lla::launch_decode_step(dtype, q, k, v, BHkv, (int)dk, (int)dv, S, o, s));
@@ -384,6 +402,47 @@ lla_status lla_decode_step_gqa(const void* q, const void* k, const void* v, lla_
                                int64_t B, int64_t Hq, int64_t Hkv, int64_t dk, int64_t dv, float* S,
                                float* o, void* stream) {
     return decode_impl(q, k, v, raw_enum(dtype), B, Heads{Hq, Hkv}, dk, dv, S, o, stream);
+}
+
+size_t lla_prefill_gated_workspace_size(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int64_t C) {
+    if (check_sizes(B, H, T, dk, dv, C) != LLA_OK) return 0;
+    return gated_ws_bytes_for(make_plan(LLA_BF16, B, Heads{H, H}, T, dk, dv, C));
+}
+
+lla_status lla_prefill_gated(const void* Q, const void* K, const void* V, const float* gate, lla_dtype dtype,
+                             int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int64_t C, unsigned flags,
+                             float* S, float* O, void* workspace, size_t workspace_bytes, void* stream) {
+    if (flags & ~(unsigned)LLA_PREFILL_ZERO_STATE) return LLA_ERR_UNSUPPORTED;
+    const bool zero = (flags & LLA_PREFILL_ZERO_STATE) != 0;
+    lla::PrefillPlan p;
+    PrefillBufs b{Q, K, V, nullptr, S, O, nullptr, 0};
+    lla_status st = check_prefill(b, true, true, true, true, false, raw_enum(dtype), B, Heads{H, H}, T, dk, dv,
+                                  C, p);
+    if (st != LLA_OK) return st;
+    const size_t need = gated_ws_bytes_for(p);
+    if (T > 0 && !gate) return LLA_ERR_NULL;
+    if (need > 0 && (!workspace || workspace_bytes < need)) return LLA_ERR_WORKSPACE;
+    if ((T > 0 && !aligned4(gate)) || (need > 0 && !aligned16(workspace))) return LLA_ERR_ALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    if (T == 0) return zero ? device_status(lla::launch_fill_zero(S, B * H * dk * dv, s)) : LLA_OK;
+    // The gate is read only; the workspace is written: neither may overlap an
+    // output, and the workspace nothing at all.
+    const int64_t BH = B * H, es = elem_size((lla_dtype)raw_enum(dtype));
+    const Span sq = span(Q, BH * T * dk * es), sk = span(K, BH * T * dk * es), sv = span(V, BH * T * dv * es);
+    const Span so = span(O, BH * T * dv * 4), ss = span(S, BH * dk * dv * 4), sg = span(gate, BH * T * 4);
+    const Span sw = span(need > 0 ? workspace : nullptr, (int64_t)need);
+    if (overlap(so, sg) || overlap(ss, sg)) return LLA_ERR_ALIAS;
+    for (Span x : {sq, sk, sv, so, ss, sg})
+        if (overlap(sw, x)) return LLA_ERR_ALIAS;
+    p.zero_start = zero;
+    p.use_ws = need > 0;
+    return device_status(lla::launch_gated_prefill(p, Q, K, V, gate, S, O, (float*)workspace, s));
+}
+
+lla_status lla_decode_step_gated(const void* q, const void* k, const void* v, const float* gate,
+                                 lla_dtype dtype, int64_t B, int64_t H, int64_t dk, int64_t dv, float* S,
+                                 float* o, void* stream) {
+    return decode_impl(q, k, v, raw_enum(dtype), B, Heads{H, H}, dk, dv, S, o, stream, gate, true);
 }
 
 }  // extern "C"

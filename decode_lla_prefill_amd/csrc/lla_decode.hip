@@ -21,12 +21,15 @@
 
 namespace lla {
 
-template <typename Tin, int VW, int RPT>
+// GATED: S = g S + k v^T with one gate per (b,h) (see the gated prefill in
+// lla_prefill.hip), g = gate[bh] taken in [2^-126, 1] like there.
+template <typename Tin, int VW, int RPT, bool GATED = false>
 __global__ __launch_bounds__(kThreads) void k_decode_step(const Tin* __restrict__ q,
                                                           const Tin* __restrict__ k,
                                                           const Tin* __restrict__ v,
                                                           float* __restrict__ S,
-                                                          float* __restrict__ o, int dk, int dv) {
+                                                          float* __restrict__ o, int dk, int dv,
+                                                          const float* __restrict__ gate) {
     typedef float vecf __attribute__((ext_vector_type(VW)));
     __shared__ float qs[128], ks[128], vs[128];
     __shared__ float red[kThreads * VW];
@@ -46,6 +49,8 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(const Tin* __restrict_
     const bool active = rg < rg_n;
     const int j0 = cg * VW;
     float* Sb = S + bh * (int64_t)dk * dv;
+    float gm = 1.0f;
+    if constexpr (GATED) gm = decay_gate(gate[bh]);
 
     vecf vj;
 #pragma unroll
@@ -72,6 +77,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(const Tin* __restrict_
                     const float ki = ks[i], qi = qs[i];
 #pragma unroll
                     for (int u = 0; u < VW; ++u) {
+                        if constexpr (GATED) s[m][u] = gm * s[m][u];  // decay
                         s[m][u] = fmaf(ki, vj[u], s[m][u]);  // rank-1 update
                         acc[u] = fmaf(qi, s[m][u], acc[u]);  // state read
                     }
@@ -98,12 +104,13 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(const Tin* __restrict_
 // Compile-time shape for the common case dk = dv = D (D a multiple of 4):
 // NT threads = (D/4) column groups x RG row groups, RPT = D/RG rows each.
 // All RPT 16-byte state loads of a thread are issued before the first use.
-template <typename Tin, int D, int NT>
+template <typename Tin, int D, int NT, bool GATED = false>
 __global__ __launch_bounds__(NT) void k_decode_step_sq(const Tin* __restrict__ q,
                                                       const Tin* __restrict__ k,
                                                       const Tin* __restrict__ v,
                                                       float* __restrict__ S,
-                                                      float* __restrict__ o) {
+                                                      float* __restrict__ o,
+                                                      const float* __restrict__ gate) {
     constexpr int CG = D / 4, RG = NT / CG, RPT = D / RG;
     static_assert(NT % CG == 0 && D % RG == 0, "thread layout must tile the state");
     __shared__ float qs[D], ks[D], vs[D];
@@ -126,12 +133,15 @@ __global__ __launch_bounds__(NT) void k_decode_step_sq(const Tin* __restrict__ q
         x[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sb + (rg + m * RG) * D + 4 * cg));
     const f32x4 vj = {vs[4 * cg], vs[4 * cg + 1], vs[4 * cg + 2], vs[4 * cg + 3]};
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float gm = 1.0f;
+    if constexpr (GATED) gm = decay_gate(gate[bh]);
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
         const int i = rg + m * RG;
         const float ki = ks[i], qi = qs[i];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
+            if constexpr (GATED) x[m][u] = gm * x[m][u];  // decay
             x[m][u] = fmaf(ki, vj[u], x[m][u]);  // rank-1 update
             acc[u] = fmaf(qi, x[m][u], acc[u]);  // state read
         }
@@ -469,32 +479,40 @@ __global__ __launch_bounds__(kThreads) void k_fill_zero(float* __restrict__ p, i
     }
 }
 
-template <typename Tin>
+template <typename Tin, bool GATED>
 static hipError_t decode_t(const void* q, const void* k, const void* v, int64_t BH, int dk,
-                           int dv, float* S, float* o, hipStream_t st) {
+                           int dv, float* S, float* o, const float* gate, hipStream_t st) {
     if (dk == 128 && dv == 128) {
-        hipLaunchKernelGGL((k_decode_step_sq<Tin, 128, 512>), dim3((unsigned)BH), dim3(512), 0, st,
-                           (const Tin*)q, (const Tin*)k, (const Tin*)v, S, o);
+        hipLaunchKernelGGL((k_decode_step_sq<Tin, 128, 512, GATED>), dim3((unsigned)BH), dim3(512), 0, st,
+                           (const Tin*)q, (const Tin*)k, (const Tin*)v, S, o, gate);
     } else if (dk == 64 && dv == 64) {
-        hipLaunchKernelGGL((k_decode_step_sq<Tin, 64, 256>), dim3((unsigned)BH), dim3(256), 0, st,
-                           (const Tin*)q, (const Tin*)k, (const Tin*)v, S, o);
+        hipLaunchKernelGGL((k_decode_step_sq<Tin, 64, 256, GATED>), dim3((unsigned)BH), dim3(256), 0, st,
+                           (const Tin*)q, (const Tin*)k, (const Tin*)v, S, o, gate);
     } else if ((dv & 3) == 0) {
         // 256 threads = (dv/4) column groups x rg row groups; RPT rows each
         // cover dk <= 128 in one batch when dv = 128 (8 row groups x 16).
-        hipLaunchKernelGGL((k_decode_step<Tin, 4, 16>), dim3((unsigned)BH), dim3(kThreads), 0, st,
-                           (const Tin*)q, (const Tin*)k, (const Tin*)v, S, o, dk, dv);
+        hipLaunchKernelGGL((k_decode_step<Tin, 4, 16, GATED>), dim3((unsigned)BH), dim3(kThreads), 0, st,
+                           (const Tin*)q, (const Tin*)k, (const Tin*)v, S, o, dk, dv, gate);
     } else {
-        hipLaunchKernelGGL((k_decode_step<Tin, 1, 4>), dim3((unsigned)BH), dim3(kThreads), 0, st,
-                           (const Tin*)q, (const Tin*)k, (const Tin*)v, S, o, dk, dv);
+        hipLaunchKernelGGL((k_decode_step<Tin, 1, 4, GATED>), dim3((unsigned)BH), dim3(kThreads), 0, st,
+                           (const Tin*)q, (const Tin*)k, (const Tin*)v, S, o, dk, dv, gate);
     }
     return hipGetLastError();
 }
 
 hipError_t launch_decode_step(lla_dtype dtype, const void* q, const void* k, const void* v,
                               int64_t BH, int dk, int dv, float* S, float* o, hipStream_t st) {
-    if (dtype == LLA_FP8_E4M3) return decode_t<fp8e4m3>(q, k, v, BH, dk, dv, S, o, st);
-    if (dtype == LLA_BF16) return decode_t<bf16>(q, k, v, BH, dk, dv, S, o, st);
-    return decode_t<float>(q, k, v, BH, dk, dv, S, o, st);
+    if (dtype == LLA_FP8_E4M3) return decode_t<fp8e4m3, false>(q, k, v, BH, dk, dv, S, o, nullptr, st);
+    if (dtype == LLA_BF16) return decode_t<bf16, false>(q, k, v, BH, dk, dv, S, o, nullptr, st);
+    return decode_t<float, false>(q, k, v, BH, dk, dv, S, o, nullptr, st);
+}
+
+hipError_t launch_decode_step_gated(lla_dtype dtype, const void* q, const void* k, const void* v,
+                                    const float* gate, int64_t BH, int dk, int dv, float* S, float* o,
+                                    hipStream_t st) {
+    if (dtype == LLA_FP8_E4M3) return decode_t<fp8e4m3, true>(q, k, v, BH, dk, dv, S, o, gate, st);
+    if (dtype == LLA_BF16) return decode_t<bf16, true>(q, k, v, BH, dk, dv, S, o, gate, st);
+    return decode_t<float, true>(q, k, v, BH, dk, dv, S, o, gate, st);
 }
 
 bool decode_tokens_fit(int64_t T, int dk, int dv, int64_t group) {

@@ -73,6 +73,11 @@ __device__ __forceinline__ void fp8x4_to_bf16(uint32_t w, uint32_t& lo, uint32_t
 template <typename In> struct Compute { typedef In type; };
 template <> struct Compute<fp8e4m3> { typedef bf16 type; };
 
+// A decay gate as the kernels take it: g in [2^-126, 1] (g <= 0 and NaN act
+// as 2^-126, g > 1 as 1).  The gated prefill works with log2 of it, clamped
+// to the same range.
+__device__ __forceinline__ float decay_gate(float g) { return fminf(fmaxf(g, 0x1p-126f), 1.0f); }
+
 __device__ __forceinline__ bf16 to_bf16(float x) { return (bf16)x; }  // round to nearest even
 __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
 __device__ __forceinline__ float to_f32(float x) { return x; }

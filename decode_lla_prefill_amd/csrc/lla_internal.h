@@ -62,6 +62,15 @@ hipError_t launch_chunk_walk(const PrefillPlan& p, const void* Q, const void* K,
 hipError_t launch_decode_step(lla_dtype dtype, const void* q, const void* k, const void* v,
                               int64_t BH, int dk, int dv, float* S, float* o, hipStream_t st);
 
+// Gated (decayed) state, one gate per (b,h) and token (one query head per
+// state): the prefill's segment pass, scan and walk (workspace: the segment
+// states, then BH * n_seg floats of segment decays), and the decode step.
+hipError_t launch_gated_prefill(const PrefillPlan& p, const void* Q, const void* K, const void* V,
+                                const float* gate, float* S, float* O, float* ws, hipStream_t st);
+hipError_t launch_decode_step_gated(lla_dtype dtype, const void* q, const void* k, const void* v,
+                                    const float* gate, int64_t BH, int dk, int dv, float* S, float* o,
+                                    hipStream_t st);
+
 // Short prompts (T <= kDecodeTokensMax tokens, dk = dv in {64, 128}; with
 // shared-state heads, T * group <= kDecodeTokensQueries) run as T fused decode
 // steps with the state in registers; lla_prefill takes this route when

@@ -353,6 +353,9 @@ __device__ __forceinline__ void state_hop(f32x4 (&Sacc)[Cf::NVW][Cf::NDT],
 struct NoHook {
     __device__ __forceinline__ void operator()(int) const {}
 };
+// No gate: chunk_scores keeps the masked scores as they are, chunk_output
+// adds Q S unscaled (see DecayGate and DecayRows for the gated walk).
+struct NoGate {};
 
 // The score tiles wave w owns: triangle tiles e = w, w + NW, ... as (query
 // tile it, key tile jt) pairs.  A wave short of tiles repeats the last one
@@ -381,10 +384,12 @@ struct ScoreTiles {
 // place other work (global stores, loads) between the steps.
 // `group` > 0: query row i is token i / group of a group of query heads
 // (see k_tokens_grouped), so key j is kept while j <= i / group.
-template <typename Cf, typename T, typename Hook = NoHook>
+// `gate(x, i, j0)` (gated walk) scales the masked scores x[r] of query i and
+// keys j0 + r before they are stored.
+template <typename Cf, typename T, typename Hook = NoHook, typename Gate = NoGate>
 __device__ __forceinline__ void chunk_scores(const ScoreTiles<Cf>& st, const T* Qs, const T* Ks, T* Ps,
                                              int w, int g, int c16, const Hook& hook = Hook(),
-                                             int group = 0) {
+                                             int group = 0, const Gate& gate = Gate()) {
     // Scores of the kept triangle, computed transposed: tile (jt, it) holds
     // A^T = K_c Q_c^T, i.e. lane (g, c16) has A[i][j] for query
     // i = 16 it + c16 and keys j = 16 jt + 4g + r.  Entries with j > i are
@@ -415,6 +420,7 @@ __device__ __forceinline__ void chunk_scores(const ScoreTiles<Cf>& st, const T* 
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 if (16 * tjt[m] + 4 * g + r > last) sacc[m][r] = 0.0f;
+            if constexpr (!std::is_same<Gate, NoGate>::value) gate(sacc[m], i, 16 * tjt[m] + 4 * g);
             // the lane's part of the address, recomputed per chunk rather
             // than one live register per tile
             const int at = opaque(c16 * Cf::PLD + Cf::PG * g) + Cf::p_at(tit[m], 0, 16 * tjt[m]);
@@ -483,13 +489,21 @@ __device__ __forceinline__ void state_operand(typename Cf::Fr& hi, typename Cf::
 // Sacc.  Oacc is overwritten.  The Q S part is software pipelined: the Q
 // slices and the state operand of depth step ds + 1 are read and formed
 // while the matrix-core ops of step ds run; `hook(ds)` runs after step ds.
-template <typename Cf, typename T, typename Hook = NoHook>
+// `rows(it)` (gated walk): the factor of query row 16 it + c16's Q S part,
+// which is then accumulated apart and added, scaled, after P V.
+template <typename Cf, typename T, typename Hook = NoHook, typename RowScale = NoGate>
 __device__ __forceinline__ void chunk_output(f32x4 (&Oacc)[Cf::NT][Cf::NVW],
                                              const f32x4 (&Sacc)[Cf::NVW][Cf::NDT],
                                              const typename Cf::Fr (&Vf)[Cf::NVW][Cf::NTS],
                                              const T* Qs, const T* Ps, int w, int g, int c16,
-                                             const Hook& hook = Hook()) {
+                                             const Hook& hook = Hook(), const RowScale& rows = RowScale()) {
     using Fr = typename Cf::Fr;
+    constexpr bool SCALED = !std::is_same<RowScale, NoGate>::value;
+    f32x4 Oqs[SCALED ? Cf::NT : 1][Cf::NVW];  // Q S apart (gated walk only)
+    auto qs_acc = [&](int it, int vw) -> f32x4& {
+        if constexpr (SCALED) return Oqs[it][vw];
+        else return Oacc[it][vw];
+    };
     auto q_slices = [&](Fr (&qb)[Cf::NT], int ds) {  // depth slots as in state_operand
 #pragma unroll
         for (int it = 0; it < Cf::NT; ++it) {
@@ -545,6 +559,12 @@ __device__ __forceinline__ void chunk_output(f32x4 (&Oacc)[Cf::NT][Cf::NVW],
         }
     }
     // incoming state read: Q_c S_c
+    if constexpr (SCALED) {
+#pragma unroll
+        for (int it = 0; it < Cf::NT; ++it)
+#pragma unroll
+            for (int vw = 0; vw < Cf::NVW; ++vw) qs_acc(it, vw) = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     if constexpr (!EARLY_QS) {
         q_slices(qb[0], 0);
 #pragma unroll
@@ -563,13 +583,23 @@ __device__ __forceinline__ void chunk_output(f32x4 (&Oacc)[Cf::NT][Cf::NVW],
         for (int vw = 0; vw < Cf::NVW; ++vw) {
             if (!owns(vw)) continue;
 #pragma unroll
-            for (int it = 0; it < Cf::NT; ++it) Oacc[it][vw] = mma(Shi[cur][vw], qb[cur][it], Oacc[it][vw]);
+            for (int it = 0; it < Cf::NT; ++it) qs_acc(it, vw) = mma(Shi[cur][vw], qb[cur][it], qs_acc(it, vw));
             if constexpr (Cf::BF) {
 #pragma unroll
-                for (int it = 0; it < Cf::NT; ++it) Oacc[it][vw] = mma(Slo[cur][vw], qb[cur][it], Oacc[it][vw]);
+                for (int it = 0; it < Cf::NT; ++it) qs_acc(it, vw) = mma(Slo[cur][vw], qb[cur][it], qs_acc(it, vw));
             }
         }
         hook(ds);
+    }
+    if constexpr (SCALED) {
+#pragma unroll
+        for (int it = 0; it < Cf::NT; ++it) {
+            const float f = rows(it);
+#pragma unroll
+            for (int vw = 0; vw < Cf::NVW; ++vw)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Oacc[it][vw][r] = fmaf(f, Oqs[it][vw][r], Oacc[it][vw][r]);
+        }
     }
 }
 
@@ -1222,6 +1252,343 @@ __global__ __launch_bounds__(512) void k_segment_states_wide(const In* __restric
 }
 
 // ---------------------------------------------------------------------------
+// Gated (decayed) state: S_t = g_t S_{t-1} + k_t v_t^T, o_t = S_t^T q_t, one
+// gate g_t per (b,h) and token.  The slide deck cites the chunkwise form of
+// gated linear attention ("Boundary, evidence, and sources") but gives no
+// gate; this is the plainest decay, a scalar applied to the previous state
+// before the token's update (g = 1: the walk above).  Gates are taken in
+// [2^-126, 1]: g <= 0 (and NaN) acts as 2^-126, g > 1 as 1.
+// Per chunk, with b_t = sum_{l <= t} log2 g_l over the chunk's rows (rows past
+// the last count 0) and B = b_{CT-1}, the chunk form is
+//     O_i     = sum_{j <= i} 2^{b_i - b_j} (q_i . k_j) v_j + 2^{b_i} q_i S_c
+//     S_{c+1} = 2^B S_c + sum_j 2^{B - b_j} k_j v_j^T
+// and every factor is at most 1.  The masked scores are scaled in fp32 before
+// their bf16 high + low split; Q S is accumulated apart and added scaled in
+// fp32; the hop takes V scaled by 2^{B - b_j} as a high + low pair.  So the
+// numerics are the ungated walk's.  A segment's total decay (the sum of its
+// chunks' B) goes to the workspace after the states, and the scan is
+// P_{s+1} = 2^{L_s} P_s + increment_s.
+// ---------------------------------------------------------------------------
+
+// Wave 0: the chunk's prefix b_t into Bs[0 .. CT-1], from the gates of rows
+// `lane` (g0) and 64 + `lane` (g1), 1 past the chunk's rows.
+template <int CT>
+__device__ __forceinline__ void chunk_decay(float* Bs, float g0, float g1, int lane) {
+    auto log2g = [](float x) { return fminf(fmaxf(log2f(x), -126.0f), 0.0f); };
+    auto scan = [&](float a) {
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const float y = __shfl_up(a, d, kWave);
+            if (lane >= d) a += y;
+        }
+        return a;
+    };
+    const float a = scan(log2g(g0));
+    if (lane < CT) Bs[lane] = a;
+    if constexpr (CT > kWave) Bs[kWave + lane] = scan(log2g(g1)) + __shfl(a, kWave - 1, kWave);
+}
+
+// Masked score (query i, keys j0 .. j0 + 3) times 2^{b_i - b_j} (masked
+// entries are zero and stay zero: the factor is clamped to at most 1).
+struct DecayGate {
+    const float* Bs;
+    __device__ __forceinline__ void operator()(f32x4& x, int i, int j0) const {
+        const float bi = Bs[i];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[r] = x[r] * exp2f(fminf(bi - Bs[j0 + r], 0.0f));
+    }
+};
+// The factor 2^{b_i} of query row i = 16 it + c16's incoming-state term.
+struct DecayRows {
+    const float* Bs;
+    int c16;
+    __device__ __forceinline__ float operator()(int it) const { return exp2f(Bs[16 * it + c16]); }
+};
+
+// Gated state hop: S = 2^B S + K^T (2^{B - b} V), V's time slots as in
+// load_vfrags (slot s of lane group g: time 32 ts + 4g + s, then 32 ts + 16 +
+// 4g + s - 4).
+template <typename Cf, typename T>
+__device__ __forceinline__ void state_hop_gated(f32x4 (&Sacc)[Cf::NVW][Cf::NDT],
+                                                const typename Cf::Fr (&Vf)[Cf::NVW][Cf::NTS],
+                                                const T* Ks, const float* Bs, int w, int g, int lane) {
+    using Fr = typename Cf::Fr;
+    const float B = Bs[Cf::CT - 1];
+    const float dS = exp2f(B);
+#pragma unroll
+    for (int vw = 0; vw < Cf::NVW; ++vw)
+#pragma unroll
+        for (int dt = 0; dt < Cf::NDT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Sacc[vw][dt][r] = Sacc[vw][dt][r] * dS;
+    Fr Vh[Cf::NVW][Cf::NTS], Vl[Cf::NVW][Cf::NTS];
+#pragma unroll
+    for (int ts = 0; ts < Cf::NTS; ++ts) {
+        float h[8];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            h[s] = exp2f(B - Bs[32 * ts + 4 * g + s]);
+            h[4 + s] = exp2f(B - Bs[32 * ts + 16 + 4 * g + s]);
+        }
+#pragma unroll
+        for (int vw = 0; vw < Cf::NVW; ++vw)
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const float x = to_f32(Vf[vw][ts][s]) * h[s];
+                if constexpr (Cf::BF) {
+                    const bf16 hi = to_bf16(x);
+                    Vh[vw][ts][s] = hi;
+                    Vl[vw][ts][s] = to_bf16(x - to_f32(hi));
+                } else {
+                    Vh[vw][ts][s] = x;
+                }
+            }
+    }
+#pragma unroll
+    for (int dt = 0; dt < Cf::NDT; ++dt) {
+#pragma unroll
+        for (int ts = 0; ts < Cf::NTS; ++ts) {
+            const Fr kt = lds_col(Ks, Cf::LK, 32 * ts, 16 * dt, lane);
+#pragma unroll
+            for (int vw = 0; vw < Cf::NVW; ++vw) {
+                if (!(Cf::ALL_WAVES || w + Cf::NW * vw < Cf::NVT)) continue;
+                Sacc[vw][dt] = mma(kt, Vh[vw][ts], Sacc[vw][dt]);
+                if constexpr (Cf::BF) Sacc[vw][dt] = mma(kt, Vl[vw][ts], Sacc[vw][dt]);
+            }
+        }
+    }
+}
+
+// Gated phase 1: each segment's increment sum_t 2^{L_seg - b_t} k_t v_t^T
+// (decays measured to the segment's end) into slot seg + 1, and its total
+// decay L_seg (log2) into dec[bh * n_seg + seg].  One workgroup per (b,h),
+// segment but the last, and value block.
+template <typename In, int CT, int D, int BV, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_gated_segment_states(
+    const In* __restrict__ K, const In* __restrict__ V, const float* __restrict__ gate,
+    float* __restrict__ ws, float* __restrict__ dec, int64_t T_len, int dk, int dv, int C, int64_t G,
+    int64_t n_seg, int n_vb) {
+    using T = typename Compute<In>::type;
+    using Cf = WalkCfg<T, CT, D, BV, kWaves>;
+    using Fr = typename Cf::Fr;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Cf::SEG_BYTES];
+    __shared__ __attribute__((aligned(16))) float Bs[CT];
+    T* Ks = reinterpret_cast<T*>(smem);
+    T* Vs = Ks + CT * Cf::LK;
+    float* Sst = reinterpret_cast<float*>(smem);
+
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t nsm1 = n_seg - 1;
+    int64_t line;
+    int vb;
+    split_id(blockIdx.x, (int64_t)(gridDim.x / n_vb), n_vb, line, vb);
+    const int64_t bh = line / nsm1, seg = line - bh * nsm1;
+    const int v0 = vb * BV;
+    const int nv = min(BV, dv - v0);
+    const int64_t n_c = (T_len + C - 1) / C;
+    const int64_t c0 = seg * G, c1 = min(n_c, c0 + G);
+    const In* Kb = K + bh * T_len * dk;
+    const In* Vb = V + bh * T_len * dv + v0;
+    const float* gb = gate + bh * T_len;
+
+    f32x4 Sacc[Cf::NVW][Cf::NDT];
+#pragma unroll
+    for (int vw = 0; vw < Cf::NVW; ++vw)
+#pragma unroll
+        for (int dt = 0; dt < Cf::NDT; ++dt) Sacc[vw][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto rows_of = [&](int64_t c) { return (int)min((int64_t)C, T_len - c * C); };
+    auto gate_of = [&](int64_t c, int r) { return r < rows_of(c) ? gb[c * C + r] : 1.0f; };
+    float L = 0.0f;  // the segment's decay so far (log2)
+
+    using TK = Tile<T, CT, D, typename Cf::LKL, Cf::NTH, In>;
+    using TV = Tile<T, CT, BV, typename Cf::LVL, Cf::NTH, In>;
+    TK tk;
+    TV tv;
+    if constexpr (VEC) {
+        tk.init(dk, dk, tid);
+        tv.init(dv, nv, tid);
+        tk.gather(Kb + c0 * C * dk, dk, rows_of(c0));
+        tv.gather(Vb + c0 * C * dv, dv, rows_of(c0));
+    }
+    float g0 = 1.0f, g1 = 1.0f;
+    if (w == 0) {
+        g0 = gate_of(c0, lane);
+        if constexpr (CT > kWave) g1 = gate_of(c0, kWave + lane);
+    }
+    for (int64_t c = c0; c < c1; ++c) {
+        if constexpr (VEC) {
+            tk.scatter(Ks, tid);
+            tv.scatter(Vs, tid);
+        } else {
+            TK::load_scalar(Kb + c * C * dk, dk, rows_of(c), dk, Ks, tid);
+            TV::load_scalar(Vb + c * C * dv, dv, rows_of(c), nv, Vs, tid);
+        }
+        if (w == 0) chunk_decay<CT>(Bs, g0, g1, lane);
+        __syncthreads();
+        if (c + 1 < c1) {  // the next chunk's loads fly during this chunk's math
+            if constexpr (VEC) {
+                tk.gather(Kb + (c + 1) * C * dk, dk, rows_of(c + 1));
+                tv.gather(Vb + (c + 1) * C * dv, dv, rows_of(c + 1));
+            }
+            if (w == 0) {
+                g0 = gate_of(c + 1, lane);
+                if constexpr (CT > kWave) g1 = gate_of(c + 1, kWave + lane);
+            }
+        }
+        Fr Vf[Cf::NVW][Cf::NTS];
+        load_vfrags<Cf>(Vf, Vs, w, g, lane);
+        state_hop_gated<Cf>(Sacc, Vf, Ks, Bs, w, g, lane);
+        L += Bs[CT - 1];
+        __syncthreads();
+    }
+    // (the loop ended with a barrier: the tiles are free)
+    state_regs_to_lds<Cf>(Sst, Sacc, w, g, c16);
+    __syncthreads();
+    state_lds_to_gmem<Cf>(ws + (bh * n_seg + seg + 1) * (int64_t)dk * dv + v0, Sst, dk, dv, nv, tid);
+    if (vb == 0 && tid == 0) dec[bh * n_seg + seg] = L;
+}
+
+// Gated phase 2: slot 0 = S_0, slot s = 2^{L_{s-1}} slot (s-1) + increment
+// (s - 1).  One thread per state element of one (b,h).
+__global__ __launch_bounds__(kThreads) void k_gated_state_scan(const float* __restrict__ S,
+                                                               float* __restrict__ ws,
+                                                               const float* __restrict__ dec,
+                                                               int64_t n_seg, int64_t dkdv,
+                                                               int64_t blocks_per_bh, int zero_start) {
+    const int64_t bh = blockIdx.x / blocks_per_bh;
+    const int64_t e = (blockIdx.x % blocks_per_bh) * kThreads + threadIdx.x;
+    if (e >= dkdv) return;
+    float* slot = ws + bh * n_seg * dkdv + e;
+    const float* L = dec + bh * n_seg;
+    float acc = zero_start ? 0.0f : S[bh * dkdv + e];
+    slot[0] = acc;
+    for (int64_t s = 1; s < n_seg; ++s) {
+        acc = fmaf(exp2f(L[s - 1]), acc, slot[s * dkdv]);
+        slot[s * dkdv] = acc;
+    }
+}
+
+// Gated phase 3: the chunk walk of k_chunk_walk with the decays (one query
+// head per state).
+template <typename In, int CT, int D, int BV, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_gated_walk(
+    const In* __restrict__ Q, const In* __restrict__ K, const In* __restrict__ V,
+    const float* __restrict__ gate, float* __restrict__ S, float* __restrict__ O,
+    const float* __restrict__ ws, int64_t T_len, int dk, int dv, int C, int64_t G, int64_t n_seg,
+    int n_vb, int zero_start) {
+    using T = typename Compute<In>::type;
+    using Cf = WalkCfg<T, CT, D, BV, kWaves>;
+    using Fr = typename Cf::Fr;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Cf::WALK_BYTES];
+    __shared__ __attribute__((aligned(16))) float Bs[CT];
+    T* Qs = reinterpret_cast<T*>(smem);
+    T* Ks = Qs + Cf::K_OFF;
+    T* Vs = Qs + Cf::V_OFF;
+    T* Ps = Qs + Cf::P_OFF;
+    float* Sst = reinterpret_cast<float*>(smem);
+
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int64_t line;
+    int vb;
+    split_id(blockIdx.x, (int64_t)(gridDim.x / n_vb), n_vb, line, vb);
+    const int64_t bh = line / n_seg, seg = line - bh * n_seg;
+    const ScoreTiles<Cf> stiles(w);
+    const int v0 = vb * BV;
+    const int nv = min(BV, dv - v0);
+    const int64_t n_c = (T_len + C - 1) / C;
+    const int64_t c0 = seg * G, c1 = min(n_c, c0 + G);
+    const bool last_seg = seg == n_seg - 1;
+    const int64_t dkdv = (int64_t)dk * dv;
+    const In* Qb = Q + bh * T_len * dk;
+    const In* Kb = K + bh * T_len * dk;
+    const In* Vb = V + bh * T_len * dv + v0;
+    const float* gb = gate + bh * T_len;
+    float* Ob = O + bh * T_len * dv + v0;
+
+    // Incoming state of this segment, columns [v0, v0 + nv) (zero_start
+    // without a workspace: S_0 = 0, S is not read)
+    const float* Sin = (ws == nullptr ? S + bh * dkdv : ws + (bh * n_seg + seg) * dkdv) + v0;
+    f32x4 Sacc[Cf::NVW][Cf::NDT];
+    state_gmem_to_lds<Cf>(Sst, Sin, dk, dv, (ws == nullptr && zero_start) ? 0 : nv, tid);
+    __syncthreads();
+    state_lds_to_regs<Cf>(Sacc, Sst, w, g, c16);
+    __syncthreads();  // the state area is reused by the tiles
+
+    using TQ = Tile<T, CT, D, typename Cf::LQL, Cf::NTH, In>;
+    using TK = Tile<T, CT, D, typename Cf::LKL, Cf::NTH, In>;
+    using TV = Tile<T, CT, BV, typename Cf::LVL, Cf::NTH, In>;
+    TQ tq;
+    TK tk;
+    TV tv;
+    auto rows_of = [&](int64_t c) { return (int)min((int64_t)C, T_len - c * C); };
+    auto gate_of = [&](int64_t c, int r) { return r < rows_of(c) ? gb[c * C + r] : 1.0f; };
+    if constexpr (VEC) {
+        tq.init(dk, dk, tid);
+        tk.init(dk, dk, tid);
+        tv.init(dv, nv, tid);
+        tq.gather(Qb + c0 * C * dk, dk, rows_of(c0));
+        tk.gather(Kb + c0 * C * dk, dk, rows_of(c0));
+        tv.gather(Vb + c0 * C * dv, dv, rows_of(c0));
+    }
+    float g0 = 1.0f, g1 = 1.0f;
+    if (w == 0) {
+        g0 = gate_of(c0, lane);
+        if constexpr (CT > kWave) g1 = gate_of(c0, kWave + lane);
+    }
+
+    f32x4 Oacc[Cf::NT][Cf::NVW];
+    int64_t t_prev = 0;
+    int n_prev = 0;
+    for (int64_t c = c0; c < c1; ++c) {
+        const int nrows = rows_of(c);
+        const int64_t t0 = c * C;
+        if constexpr (VEC) {
+            tq.scatter(Qs, tid);
+            tk.scatter(Ks, tid);
+            tv.scatter(Vs, tid);
+        } else {
+            TQ::load_scalar(Qb + t0 * dk, dk, nrows, dk, Qs, tid);
+            TK::load_scalar(Kb + t0 * dk, dk, nrows, dk, Ks, tid);
+            TV::load_scalar(Vb + t0 * dv, dv, nrows, nv, Vs, tid);
+        }
+        if (w == 0) chunk_decay<CT>(Bs, g0, g1, lane);
+        __syncthreads();
+        if (c > c0) store_out<Cf, VEC>(Ob, Oacc, t_prev, n_prev, nv, dv, w, g, c16);
+        if (c + 1 < c1) {  // the next chunk's loads fly during this chunk's math
+            if constexpr (VEC) {
+                const int nr = rows_of(c + 1);
+                tq.gather(Qb + (t0 + C) * dk, dk, nr);
+                tk.gather(Kb + (t0 + C) * dk, dk, nr);
+                tv.gather(Vb + (t0 + C) * dv, dv, nr);
+            }
+            if (w == 0) {
+                g0 = gate_of(c + 1, lane);
+                if constexpr (CT > kWave) g1 = gate_of(c + 1, kWave + lane);
+            }
+        }
+
+        chunk_scores<Cf>(stiles, Qs, Ks, Ps, w, g, c16, NoHook(), 0, DecayGate{Bs});
+        __syncthreads();
+        Fr Vf[Cf::NVW][Cf::NTS];
+        load_vfrags<Cf>(Vf, Vs, w, g, lane);
+        chunk_output<Cf>(Oacc, Sacc, Vf, Qs, Ps, w, g, c16, NoHook(), DecayRows{Bs, c16});
+        t_prev = t0;
+        n_prev = nrows;
+        if (c + 1 < c1 || last_seg) state_hop_gated<Cf>(Sacc, Vf, Ks, Bs, w, g, lane);
+        __syncthreads();
+    }
+    if (c1 > c0) store_out<Cf, VEC>(Ob, Oacc, t_prev, n_prev, nv, dv, w, g, c16);
+
+    if (last_seg) {  // (the loop ended with a barrier)
+        state_regs_to_lds<Cf>(Sst, Sacc, w, g, c16);
+        __syncthreads();
+        state_lds_to_gmem<Cf>(S + bh * dkdv + v0, Sst, dk, dv, nv, tid);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Host side: dispatch over (input type, chunk tile, head dim); the plan
 // itself is made in lla_plan.cpp.
 // ---------------------------------------------------------------------------
@@ -1373,6 +1740,58 @@ hipError_t launch_segment_states(const PrefillPlan& p, const void* K, const void
                                  hipStream_t st) {
     if (p.n_seg <= 1) return hipSuccess;
     LLA_DISPATCH(launch_seg_t, p, K, V, ws, st);
+}
+
+// ---- the gated walk: the four-wave kernels for every shape ---------------------
+
+template <typename In, int CT, int D>
+static hipError_t launch_gated_seg_t(const PrefillPlan& p, const void* K, const void* V, const float* gate,
+                                     float* ws, float* dec, hipStream_t st) {
+    constexpr int BV = D > 64 ? 64 : D;
+    const int64_t grid = p.BH * (p.n_seg - 1) * p.n_vb;
+    if (p.vec)
+        hipLaunchKernelGGL((k_gated_segment_states<In, CT, D, BV, true>), dim3((unsigned)grid), dim3(kThreads),
+                           0, st, (const In*)K, (const In*)V, gate, ws, dec, p.T, p.dk, p.dv, p.C, p.G, p.n_seg,
+                           p.n_vb);
+    else
+        hipLaunchKernelGGL((k_gated_segment_states<In, CT, D, BV, false>), dim3((unsigned)grid), dim3(kThreads),
+                           0, st, (const In*)K, (const In*)V, gate, ws, dec, p.T, p.dk, p.dv, p.C, p.G, p.n_seg,
+                           p.n_vb);
+    return hipGetLastError();
+}
+
+template <typename In, int CT, int D>
+static hipError_t launch_gated_walk_t(const PrefillPlan& p, const void* Q, const void* K, const void* V,
+                                      const float* gate, float* S, float* O, float* ws, hipStream_t st) {
+    constexpr int BV = D > 64 ? 64 : D;
+    const int64_t grid = p.BH * p.n_seg * p.n_vb;
+    const float* wsr = p.use_ws ? ws : nullptr;
+    if (p.vec)
+        hipLaunchKernelGGL((k_gated_walk<In, CT, D, BV, true>), dim3((unsigned)grid), dim3(kThreads), 0, st,
+                           (const In*)Q, (const In*)K, (const In*)V, gate, S, O, wsr, p.T, p.dk, p.dv, p.C, p.G,
+                           p.n_seg, p.n_vb, (int)p.zero_start);
+    else
+        hipLaunchKernelGGL((k_gated_walk<In, CT, D, BV, false>), dim3((unsigned)grid), dim3(kThreads), 0, st,
+                           (const In*)Q, (const In*)K, (const In*)V, gate, S, O, wsr, p.T, p.dk, p.dv, p.C, p.G,
+                           p.n_seg, p.n_vb, (int)p.zero_start);
+    return hipGetLastError();
+}
+
+hipError_t launch_gated_prefill(const PrefillPlan& p, const void* Q, const void* K, const void* V,
+                                const float* gate, float* S, float* O, float* ws, hipStream_t st) {
+    if (p.n_c == 0) return hipSuccess;
+    if (p.use_ws) {
+        const int64_t dkdv = (int64_t)p.dk * p.dv;
+        float* dec = ws + p.BH * p.n_seg * dkdv;  // after the states
+        hipError_t e = [&]() -> hipError_t { LLA_DISPATCH(launch_gated_seg_t, p, K, V, gate, ws, dec, st); }();
+        if (e != hipSuccess) return e;
+        const int64_t blocks_per_bh = (dkdv + kThreads - 1) / kThreads;
+        hipLaunchKernelGGL(k_gated_state_scan, dim3((unsigned)(p.BH * blocks_per_bh)), dim3(kThreads), 0, st, S,
+                           ws, dec, p.n_seg, dkdv, blocks_per_bh, (int)p.zero_start);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    LLA_DISPATCH(launch_gated_walk_t, p, Q, K, V, gate, S, O, ws, st);
 }
 
 hipError_t launch_state_scan(const PrefillPlan& p, const float* S, float* ws, hipStream_t st) {

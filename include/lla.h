@@ -331,6 +331,46 @@ lla_status lla_decode_step_gqa(const void *q, const void *k, const void *v, lla_
                                int64_t B, int64_t Hq, int64_t Hkv, int64_t dk, int64_t dv,
                                float *S, float *o, void *stream);
 
+/*
+ * Gated (decayed) state.  The slide deck "Chunking, causality, and parallel
+ * prefill" ("Boundary, evidence, and sources") cites the chunkwise form of
+ * gated linear attention but gives no gate; these calls take the plainest
+ * decay, one scalar gate g_t per (b,h) and token applied to the previous
+ * state before the token's update:
+ *     S_t = g_t S_{t-1} + k_t v_t^T,    o_t = S_t^T q_t.
+ * With g = 1 this is lla_prefill's recurrence.  gate: fp32, [B][H][T] for
+ * the prefill, [B][H] for the decode step, 4-byte aligned, read only.  Gates
+ * are taken in [2^-126, 1]: g <= 0 (and NaN) act as 2^-126, g > 1 as 1.
+ * One query head per state (no shared-state heads).  Sizes, dtypes, chunk
+ * sizes, S, O and the errors are those of lla_prefill; options: only
+ * LLA_PREFILL_ZERO_STATE (others: LLA_ERR_UNSUPPORTED).  Every prompt length
+ * takes the chunked path (segment pass, scan, walk), with the chunked
+ * prefill's numerics: the decays scale the masked scores before their bf16
+ * high + low split, Q_c S_c is added scaled in fp32, and the state hop takes
+ * V scaled as a high + low pair, so results are within the same error of the
+ * exact recurrence (integers exact under the same bounds when every gate is 1).
+ * The workspace (lla_prefill_gated_workspace_size bytes, 16-byte aligned;
+ * 0 with a single segment, then it may be NULL) holds the segment states and
+ * one decay per segment; it must not overlap any other buffer.
+ */
+size_t lla_prefill_gated_workspace_size(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
+                                        int64_t C);
+
+lla_status lla_prefill_gated(const void *Q, const void *K, const void *V, const float *gate,
+                             lla_dtype dtype, int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
+                             int64_t C, unsigned flags, float *S, float *O, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/*
+ * One gated decode step: S = g S + k v^T, then o = S^T q, for B*H states
+ * (gate [B][H]).  Arguments and errors as lla_decode_step.  The arithmetic is
+ * lla_decode_step's after the state is scaled by g, so g = 1 gives identical
+ * bits.
+ */
+lla_status lla_decode_step_gated(const void *q, const void *k, const void *v, const float *gate,
+                                 lla_dtype dtype, int64_t B, int64_t H, int64_t dk, int64_t dv,
+                                 float *S, float *o, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

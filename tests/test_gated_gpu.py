@@ -1,0 +1,199 @@
+"""The gated (decayed) state on the GPU, through the C ABI, against the oracle.
+
+Reading (the slide deck "Chunking, causality, and parallel prefill" cites the
+chunkwise form of gated linear attention, section "Boundary, evidence, and
+sources", without a gate): S_t = g_t S_{t-1} + k_t v_t^T, o_t = S_t^T q_t,
+one gate per (b,h) and token.  The oracle (oracle.gated_recurrence) is pinned
+in tests/test_oracle_gated.py.  Checked here: the chunked prefill within the
+floating-point bar on every kernel shape (one and several segments, chunk
+tiles of 32, 64 and 128, ragged T and head dims, bf16, fp32 and FP8 inputs);
+gates of one on integer inputs exact; the zero-state option; continuation
+(prefill, prefill) and (prefill, decode steps); the decode step exact on
+integer inputs with dyadic gates and bit-equal to lla_decode_step at g = 1;
+gates at the ends of their range; the full T=8192 and decode workloads on
+sampled heads."""
+import numpy as np
+import pytest
+import torch
+
+import decode_lla_prefill_amd as lla
+import oracle
+import workloads
+from gpu_util import TOL, need_gpu, np64, rel_err
+
+pytestmark = pytest.mark.gpu
+FP8 = torch.float8_e4m3fn
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return need_gpu()
+
+
+def _bar(dtype):
+    return 1e-5 if dtype == torch.float32 else TOL
+
+
+CASES = [
+    # B, H, T, dk, dv, C, dtype, gate range
+    (2, 3, 1000, 64, 64, 64, torch.bfloat16, (0.5, 1.0)),      # several segments
+    (1, 2, 2000, 128, 128, 64, torch.bfloat16, (0.9, 1.0)),    # d = 128, two value blocks
+    (1, 2, 900, 128, 128, 128, torch.bfloat16, (0.8, 1.0)),    # chunk tile 128
+    (2, 2, 333, 32, 32, 32, torch.bfloat16, (0.0, 1.0)),       # chunk tile 32, gates down to 0
+    (1, 3, 700, 48, 40, 40, torch.float32, (0.7, 1.0)),        # fp32, ragged dims and chunks
+    (2, 2, 600, 128, 128, 64, FP8, (0.9, 1.0)),                # FP8 inputs
+    (1, 2, 500, 40, 24, 48, torch.bfloat16, (0.6, 1.0)),       # dims not multiples of 16
+    (3, 1, 17, 64, 64, 64, torch.bfloat16, (0.5, 1.0)),        # one chunk, ragged
+    (1, 1, 5000, 20, 22, 64, torch.bfloat16, (0.95, 1.0)),     # element path, many chunks
+]
+
+
+@pytest.mark.parametrize("B,H,T,dk,dv,C,dtype,grange", CASES)
+def test_gated_prefill_within_the_bar(dev, B, H, T, dk, dv, C, dtype, grange):
+    print("gated prefill", B, H, T, dk, dv, C, dtype, grange, flush=True)
+    scale = 1.0 if dtype == FP8 else dk ** -0.5
+    q, k, v = workloads.gaussian(B, H, T, dk, dv, seed_base=T + dk + C, scale=scale, dtype=dtype)
+    g = workloads.gates(B, H, T, seed=T + 7, lo=grange[0], hi=grange[1])
+    S0 = torch.randn((B, H, dk, dv), generator=torch.Generator().manual_seed(T))
+    O_ref, S_ref = oracle.gated_recurrence(q, k, v, g, S0, nthreads=8)
+    S = S0.to(dev).contiguous()
+    o = lla.prefill_gated(q.to(dev), k.to(dev), v.to(dev), g.to(dev), S, C)
+    torch.cuda.synchronize()
+    bar = _bar(dtype)
+    assert rel_err(np64(o), O_ref) <= bar and rel_err(np64(S), S_ref) <= bar
+
+
+@pytest.mark.parametrize("B,H,T,d,C", [(1, 2, 1500, 64, 64), (2, 1, 700, 128, 128), (1, 2, 400, 32, 32)])
+def test_gates_of_one_on_integers_exact(dev, B, H, T, d, C):
+    """g = 1 is the ungated method: integer inputs give exact outputs and S_T."""
+    q, k, v = workloads.integers(B, H, T, d, d, seed=T + C)
+    S0 = torch.randint(-4, 5, (B, H, d, d), generator=torch.Generator().manual_seed(3)).float()
+    O_ref, S_ref = oracle.recurrence(q, k, v, S0, nthreads=8)
+    S = S0.to(dev)
+    o = lla.prefill_gated(q.to(dev), k.to(dev), v.to(dev), torch.ones(B, H, T, device=dev), S, C)
+    torch.cuda.synchronize()
+    assert np.array_equal(np64(o), O_ref) and np.array_equal(np64(S), S_ref)
+
+
+def test_zero_state_option_equals_a_zero_state(dev):
+    B, H, T, d, C = 1, 2, 1200, 64, 64
+    q, k, v = workloads.gaussian(B, H, T, d, d, seed_base=5, scale=d ** -0.5, device=dev)
+    g = workloads.gates(B, H, T, seed=5, device=dev)
+    S_a = torch.zeros((B, H, d, d), device=dev)
+    o_a = lla.prefill_gated(q, k, v, g, S_a, C)
+    S_b = torch.full((B, H, d, d), float("nan"), device=dev)
+    o_b = lla.prefill_gated(q, k, v, g, S_b, C, zero_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, o_b) and torch.equal(S_a, S_b)
+
+
+def test_empty_prompt(dev):
+    z = torch.zeros((1, 2, 0, 64), dtype=torch.bfloat16, device=dev)
+    S = torch.full((1, 2, 64, 64), 3.0, device=dev)
+    lla.prefill_gated(z, z, z, torch.zeros((1, 2, 0), device=dev), S, 64)
+    torch.cuda.synchronize()
+    assert torch.all(S == 3.0)
+    lla.prefill_gated(z, z, z, torch.zeros((1, 2, 0), device=dev), S, 64, zero_state=True)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(S) == 0
+
+
+def test_prefill_then_prefill_and_then_decode_steps(dev):
+    """The decayed state is still the one object handed between calls."""
+    B, H, T1, T2, n, d, C = 2, 2, 700, 500, 6, 128, 64
+    T = T1 + T2 + n
+    q, k, v = workloads.gaussian(B, H, T, d, d, seed_base=11, scale=d ** -0.5)
+    g = workloads.gates(B, H, T, seed=11, lo=0.8)
+    O_ref, S_ref = oracle.gated_recurrence(q, k, v, g, None, nthreads=8)
+    qd, kd, vd, gd = (x.to(dev) for x in (q, k, v, g))
+    S = torch.zeros((B, H, d, d), device=dev)
+    o1 = lla.prefill_gated(qd[:, :, :T1].contiguous(), kd[:, :, :T1].contiguous(), vd[:, :, :T1].contiguous(),
+                           gd[:, :, :T1].contiguous(), S, C)
+    o2 = lla.prefill_gated(qd[:, :, T1:T1 + T2].contiguous(), kd[:, :, T1:T1 + T2].contiguous(),
+                           vd[:, :, T1:T1 + T2].contiguous(), gd[:, :, T1:T1 + T2].contiguous(), S, C)
+    steps = [lla.decode_step_gated(qd[:, :, t].contiguous(), kd[:, :, t].contiguous(), vd[:, :, t].contiguous(),
+                                   gd[:, :, t].contiguous(), S) for t in range(T1 + T2, T)]
+    torch.cuda.synchronize()
+    o = torch.cat([o1, o2, torch.stack(steps, dim=2)], dim=2)
+    assert rel_err(np64(o), O_ref) <= TOL and rel_err(np64(S), S_ref) <= TOL
+
+
+@pytest.mark.parametrize("B,H,dk,dv,dtype", [(4, 8, 128, 128, torch.bfloat16), (3, 5, 64, 64, torch.float32),
+                                             (2, 3, 40, 72, torch.bfloat16), (2, 2, 7, 9, FP8)])
+def test_decode_step_dyadic_gates_integers_exact(dev, B, H, dk, dv, dtype):
+    """Gates 1, 1/2, 1/4 and small integers: every product and sum is exact
+    in fp32, so the decode step equals the oracle bit for bit."""
+    q, k, v = workloads.integers(B, H, 3, dk, dv, seed=dk + dv, dtype=dtype)
+    g = torch.tensor([1.0, 0.5, 0.25])[torch.randint(0, 3, (B, H, 3), generator=torch.Generator().manual_seed(1))]
+    S = torch.randint(-8, 9, (B, H, dk, dv), generator=torch.Generator().manual_seed(2)).float()
+    Sd = S.to(dev)
+    Sr = S.double().numpy()
+    for t in range(3):
+        o = lla.decode_step_gated(q[:, :, t].contiguous().to(dev), k[:, :, t].contiguous().to(dev),
+                                  v[:, :, t].contiguous().to(dev), g[:, :, t].contiguous().to(dev), Sd)
+        torch.cuda.synchronize()
+        o_ref, Sr = oracle.gated_decode_step(q[:, :, t], k[:, :, t], v[:, :, t], g[:, :, t], Sr)
+        assert np.array_equal(np64(o), o_ref), t
+    assert np.array_equal(np64(Sd), Sr)
+
+
+@pytest.mark.parametrize("d", [128, 64, 40])
+def test_decode_step_gate_one_is_the_decode_step_bit_for_bit(dev, d):
+    B, H = 8, 4
+    q, k, v = workloads.gaussian(B, H, 1, d, d, seed_base=d, scale=d ** -0.5, device=dev)
+    S0 = torch.randn((B, H, d, d), generator=torch.Generator(device=dev).manual_seed(d), device=dev)
+    S_a, S_b = S0.clone(), S0.clone()
+    o_a = lla.decode_step_gated(q[:, :, 0].contiguous(), k[:, :, 0].contiguous(), v[:, :, 0].contiguous(),
+                                torch.ones(B, H, device=dev), S_a)
+    o_b = lla.decode_step(q[:, :, 0].contiguous(), k[:, :, 0].contiguous(), v[:, :, 0].contiguous(), S_b)
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, o_b) and torch.equal(S_a, S_b)
+
+
+def test_gates_outside_the_range_are_clamped(dev):
+    """g > 1 acts as 1, g <= 0 as 2^-126 (about nothing kept): the results
+    match the oracle run on the clamped gates."""
+    B, H, T, d, C = 1, 2, 400, 64, 64
+    q, k, v = workloads.gaussian(B, H, T, d, d, seed_base=13, scale=d ** -0.5)
+    g = workloads.gates(B, H, T, seed=13, lo=-0.5, hi=1.5)
+    g_used = g.clamp(2.0 ** -126, 1.0)
+    S0 = torch.randn((B, H, d, d), generator=torch.Generator().manual_seed(13))
+    O_ref, S_ref = oracle.gated_recurrence(q, k, v, g_used, S0, nthreads=8)
+    S = S0.to(dev)
+    o = lla.prefill_gated(q.to(dev), k.to(dev), v.to(dev), g.to(dev), S, C)
+    torch.cuda.synchronize()
+    assert rel_err(np64(o), O_ref) <= TOL and rel_err(np64(S), S_ref) <= TOL
+
+
+def test_gated_prefill_full_size_sampled_heads(dev):
+    """The T=8192 workload's shape (B=1, H=16, d=128, C=64) with gates in
+    [0.9, 1]: the whole call on the GPU, four heads against the oracle."""
+    cfg = workloads.CONFIGS["prefill_T8192"]
+    B, H, T, C, d = cfg.B, cfg.H, cfg.T, cfg.C, cfg.dk
+    q, k, v = workloads.config_inputs(cfg, device=dev)
+    g = workloads.gates(B, H, T, seed=cfg.seed_base + 9, device=dev)
+    S = torch.zeros((B, H, d, d), device=dev)
+    o = lla.prefill_gated(q, k, v, g, S, C, zero_state=True)
+    torch.cuda.synchronize()
+    heads = [0, 5, 10, 15]
+    O_ref, S_ref = oracle.gated_recurrence(q[:, heads].cpu(), k[:, heads].cpu(), v[:, heads].cpu(),
+                                           g[:, heads].cpu(), None, nthreads=4)
+    assert rel_err(np64(o[:, heads]), O_ref) <= TOL and rel_err(np64(S[:, heads]), S_ref) <= TOL
+
+
+def test_gated_decode_full_size_sampled(dev):
+    """The decode workload's shape (B=256, H=32, d=128): one gated step, 64
+    sampled states against the oracle."""
+    cfg = workloads.CONFIGS["decode_B256"]
+    B, H, d = cfg.B, cfg.H, cfg.dk
+    S0 = workloads.random_state(cfg, device=dev)
+    qd, kd, vd = workloads.decode_inputs(cfg, 1, device=dev)
+    g = workloads.gates(B, H, 1, seed=4, device=dev)[:, :, 0].contiguous()
+    S = S0.clone()
+    o = lla.decode_step_gated(qd[0], kd[0], vd[0], g, S)
+    torch.cuda.synchronize()
+    idx = torch.arange(0, B * H, (B * H) // 64)
+    bs, hs = idx // H, idx % H
+    o_ref, S_ref = oracle.gated_decode_step(qd[0][bs, hs].cpu(), kd[0][bs, hs].cpu(), vd[0][bs, hs].cpu(),
+                                            g[bs, hs].cpu(), S0[bs, hs].cpu())
+    assert rel_err(np64(o[bs, hs]), o_ref) <= 1e-5 and rel_err(np64(S[bs, hs]), S_ref) <= 1e-6

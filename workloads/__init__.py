@@ -164,6 +164,14 @@ def decode_inputs(cfg: Config, steps: int, device="cpu", B=None):
     return tuple(out)
 
 
+def gates(B, H, T, seed, lo=0.9, hi=1.0, device="cpu"):
+    """Decay gates [B,H,T] fp32, uniform in [lo, hi] (seeded).  The default
+    range is that of forget gates close to one, which keep a long memory;
+    lo = 0 reaches gates that forget everything."""
+    g = _gen(device, seed)
+    return torch.rand((B, H, T), generator=g, dtype=torch.float32, device=device) * (hi - lo) + lo
+
+
 def random_state(cfg: Config, device="cpu", B=None):
     """A state S [B,Hkv,dk,dv] fp32 drawn N(0,1) with seed seed_base + 6."""
     g = _gen(device, cfg.seed_base + 6)
