@@ -7,8 +7,9 @@ second) on the T=8192 workload (B=1, H=16, C=64, d_k=d_v=128, bf16 Q/K/V,
 fp32 state and output); the decode workload (256 sequences x 32 heads,
 d=128, state from a seeded T=4096 prefill) is reported under ``decode`` in
 steps/s.  The same two workloads with query heads grouped four to a
-key/value head (shared states) are reported under ``grouped_heads``, and with
-FP8 (E4M3) inputs under ``fp8_inputs``.
+key/value head (shared states) are reported under ``grouped_heads``, with
+FP8 (E4M3) inputs under ``fp8_inputs``, and with a decayed state (one gate
+per head and token, S_t = g_t S_{t-1} + k_t v_t^T) under ``gated_state``.
 
 Prefill is timed cold: the timed steps rotate over several input/output
 sets whose total exceeds the 256 MB Infinity Cache, so each step's inputs
@@ -672,6 +673,61 @@ def bench_fp8(args, torch, lla, workloads, profiling):
     return {"prefill": pre, "decode": dec}
 
 
+def bench_gated(args, torch, lla, workloads, profiling):
+    """Gated (decayed) state, S_t = g_t S_{t-1} + k_t v_t^T with gates in
+    [0.9, 1]: the T=8192 prefill and the 256 x 32 decode batch."""
+    dev = torch.device("cuda:0")
+    cfg = workloads.CONFIGS["prefill_T8192"]
+    B, H, T, C, d = cfg.B, cfg.H, cfg.T, cfg.C, cfg.dk
+    q0, k0, v0 = workloads.config_inputs(cfg, device=dev)
+    g0 = workloads.gates(B, H, T, seed=cfg.seed_base + 9, device=dev)
+    sets = []
+    for r in range(args.rotate):
+        q, k, v, g = (x.clone() for x in (q0, k0, v0, g0)) if r else (q0, k0, v0, g0)
+        sets.append(lla.PreparedGatedPrefill(q, k, v, g, torch.empty((B, H, d, d), device=dev), C))
+    for i in range(args.warmup):
+        sets[i % len(sets)](zero_state=True)
+    wall, gpu = _timed(torch, lambda i: sets[i % len(sets)](zero_state=True), args.steps)
+    flops, nbytes = prefill_work(B, H, T, C, d)
+    nbytes += B * H * T * 4  # the gates
+    step_ms = gpu * 1e3 / args.steps
+    pre = {"workload": cfg.name + "_gated", "B": B, "H": H, "T": T, "C": C, "dk": d, "dv": d,
+           "gates": "uniform in [0.9, 1], one per (b,h) and token",
+           "value": B * T / (wall / args.steps), "unit": "tokens/s",
+           "ms_per_step": wall * 1e3 / args.steps, "gpu_ms_per_step": step_ms,
+           "mfma_frac": flops / (step_ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+           # the whole step (segment pass, scan, walk) against the step's algorithmic bytes
+           "roofline": hbm_roofline("fresh-prompt lla_prefill_gated step (k_gated_segment_states, "
+                                    "k_gated_state_scan, k_gated_walk<bf16,64,128,64>)", nbytes, step_ms,
+                                    0.0, None, "HIP events around %d back-to-back steps, %d rotating input sets"
+                                    % (args.steps, len(sets))),
+           "timing": "HIP events around the timed steps"}
+    del sets, q0, k0, v0, g0
+    torch.cuda.empty_cache()
+
+    cfg = workloads.CONFIGS["decode_B256"]
+    B, H, d = cfg.B, cfg.H, cfg.dk
+    S = workloads.random_state(cfg, device=dev)
+    n = args.decode_steps
+    qd, kd, vd = workloads.decode_inputs(cfg, n + args.warmup, device=dev)
+    gd = workloads.gates(n + args.warmup, B, H, seed=cfg.seed_base + 9, device=dev)
+    o = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    calls = [lla.PreparedGatedDecode(qd[i], kd[i], vd[i], gd[i], S, out=o) for i in range(n + args.warmup)]
+    for i in range(args.warmup):
+        calls[n + i]()
+    wall, gpu = _timed(torch, lambda i: calls[i](), n)
+    kern_ms = gpu * 1e3 / n
+    nbytes = decode_bytes(B, H, d) + B * H * 4
+    dec = {"workload": cfg.name + "_gated", "B": B, "H": H, "dk": d, "dv": d, "steps": n,
+           "value": n / wall, "unit": "steps/s", "ms_per_step": wall * 1e3 / n,
+           "gpu_ms_per_step": kern_ms, "tokens_per_s": B * n / wall,
+           "roofline": hbm_roofline("k_decode_step_sq<bf16,128,512,gated>", nbytes, kern_ms, args.gap_ms,
+                                    None, "HIP events around the timed steps")}
+    del calls, qd, kd, vd, gd, S
+    torch.cuda.empty_cache()
+    return {"prefill": pre, "decode": dec}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -689,6 +745,7 @@ def main():
     ap.add_argument("--skip-grouped", action="store_true")
     ap.add_argument("--skip-other", action="store_true", help="skip the B=4 T=1024 and T=131072 prefills")
     ap.add_argument("--skip-fp8", action="store_true")
+    ap.add_argument("--skip-gated", action="store_true")
     args = ap.parse_args()
     threads, args.host = host_cores()
     if args.cpu_threads is None:
@@ -741,6 +798,8 @@ def main():
         line["grouped_heads"] = bench_grouped(args, torch, lla, workloads, profiling)
     if not args.skip_fp8:
         line["fp8_inputs"] = bench_fp8(args, torch, lla, workloads, profiling)
+    if not args.skip_gated:
+        line["gated_state"] = bench_gated(args, torch, lla, workloads, profiling)
     peaks = measure_peaks(torch)
     line["measured_peaks"] = peaks
     # the same figures against what this GPU measurably sustains

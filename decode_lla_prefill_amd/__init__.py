@@ -506,6 +506,69 @@ class PreparedPrefill:
         return self.out
 
 
+class PreparedGatedPrefill:
+    """A gated prefill (lla_prefill_gated) over fixed buffers, checked and
+    marshalled once (see PreparedPrefill): calling it runs one prefill on the
+    current stream, a fresh prompt with ``zero_state``."""
+
+    def __init__(self, q, k, v, gate, state, chunk, out=None, workspace=None):
+        lib = library()
+        B, Hq, Hkv, T, dk, dv = _qkv_shape(q, k, v)
+        if Hq != Hkv:
+            raise ValueError("the gated prefill takes one query head per state")
+        _need(gate, "gate", dtype=torch.float32, ndim=3)
+        if tuple(gate.shape) != (B, Hq, T):
+            raise ValueError("gate shape %s, expected %s" % (tuple(gate.shape), (B, Hq, T)))
+        _state_check(state, B, Hq, dk, dv)
+        self.out = _out(out, (B, Hq, T, dv), q.device)
+        need = prefill_gated_workspace_size(B, Hq, T, dk, dv, chunk)
+        if workspace is None and need:
+            workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
+        if workspace is not None:
+            _need(workspace, "workspace")
+        self.workspace = workspace
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        _same_device(q.device, gate=gate, state=state, out=self.out, workspace=workspace)
+        self._fn = lib.lla_prefill_gated
+        self._head = (_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _dtype_code(q), B, Hq, T, dk, dv, chunk)
+        self._tail = (_ptr(state), _ptr(self.out), _ptr(workspace), ws_bytes)
+        self._keep = (q, k, v, gate, state, self.out, workspace)  # the buffers behind the addresses
+        self._device = q.device
+
+    def __call__(self, zero_state: bool = False):
+        st = torch.cuda.current_stream(self._device).cuda_stream
+        _check(self._fn(*self._head, PREFILL_ZERO_STATE if zero_state else 0, *self._tail, st),
+               "lla_prefill_gated")
+        return self.out
+
+
+class PreparedGatedDecode:
+    """A gated decode step (lla_decode_step_gated) over fixed buffers,
+    marshalled once."""
+
+    def __init__(self, q, k, v, gate, state, out=None):
+        lib = library()
+        B, Hq, Hkv, dk, dv = _step_shape(q, k, v)
+        if Hq != Hkv:
+            raise ValueError("the gated decode step takes one query head per state")
+        _need(gate, "gate", dtype=torch.float32, ndim=2)
+        if tuple(gate.shape) != (B, Hq):
+            raise ValueError("gate shape %s, expected %s" % (tuple(gate.shape), (B, Hq)))
+        _state_check(state, B, Hq, dk, dv)
+        self.out = _out(out, (B, Hq, dv), q.device)
+        _same_device(q.device, gate=gate, state=state, out=self.out)
+        self._fn = lib.lla_decode_step_gated
+        self._args = (_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _dtype_code(q), B, Hq, dk, dv, _ptr(state),
+                      _ptr(self.out))
+        self._keep = (q, k, v, gate, state, self.out)
+        self._device = q.device
+
+    def __call__(self):
+        _check(self._fn(*self._args, torch.cuda.current_stream(self._device).cuda_stream),
+               "lla_decode_step_gated")
+        return self.out
+
+
 class PreparedDecode:
     """A decode step over fixed buffers, marshalled once (see PreparedPrefill)."""
 

@@ -604,6 +604,114 @@ __device__ __forceinline__ void chunk_output(f32x4 (&Oacc)[Cf::NT][Cf::NVW],
 }
 
 // ---------------------------------------------------------------------------
+// Gated (decayed) state: S_t = g_t S_{t-1} + k_t v_t^T, o_t = S_t^T q_t, one
+// gate g_t per (b,h) and token.  The slide deck cites the chunkwise form of
+// gated linear attention ("Boundary, evidence, and sources") but gives no
+// gate; this is the plainest decay, a scalar applied to the previous state
+// before the token's update (g = 1: the walk above).  Gates are taken in
+// [2^-126, 1]: g <= 0 (and NaN) acts as 2^-126, g > 1 as 1.
+// Per chunk, with b_t = sum_{l <= t} log2 g_l over the chunk's rows (rows past
+// the last count 0) and B = b_{CT-1}, the chunk form is
+//     O_i     = sum_{j <= i} 2^{b_i - b_j} (q_i . k_j) v_j + 2^{b_i} q_i S_c
+//     S_{c+1} = 2^B S_c + sum_j 2^{B - b_j} k_j v_j^T
+// and every factor is at most 1.  The masked scores are scaled in fp32 before
+// their bf16 high + low split; Q S is accumulated apart and added scaled in
+// fp32; the hop takes V scaled by 2^{B - b_j} as a high + low pair.  So the
+// numerics are the ungated walk's.  A segment's total decay (the sum of its
+// chunks' B) goes to the workspace after the states, and the scan is
+// P_{s+1} = 2^{L_s} P_s + increment_s.
+// ---------------------------------------------------------------------------
+
+// Wave 0: the chunk's prefix b_t into Bs[0 .. CT-1], from the gates of rows
+// `lane` (g0) and 64 + `lane` (g1), 1 past the chunk's rows.
+template <int CT>
+__device__ __forceinline__ void chunk_decay(float* Bs, float g0, float g1, int lane) {
+    auto log2g = [](float x) { return fminf(fmaxf(log2f(x), -126.0f), 0.0f); };
+    auto scan = [&](float a) {
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const float y = __shfl_up(a, d, kWave);
+            if (lane >= d) a += y;
+        }
+        return a;
+    };
+    const float a = scan(log2g(g0));
+    if (lane < CT) Bs[lane] = a;
+    if constexpr (CT > kWave) Bs[kWave + lane] = scan(log2g(g1)) + __shfl(a, kWave - 1, kWave);
+}
+
+// Masked score (query i, keys j0 .. j0 + 3) times 2^{b_i - b_j} (masked
+// entries are zero and stay zero: the factor is clamped to at most 1).
+struct DecayGate {
+    const float* Bs;
+    __device__ __forceinline__ void operator()(f32x4& x, int i, int j0) const {
+        const float bi = Bs[i];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[r] = x[r] * exp2f(fminf(bi - Bs[j0 + r], 0.0f));
+    }
+};
+// The factor 2^{b_i} of query row i = 16 it + c16's incoming-state term.
+struct DecayRows {
+    const float* Bs;
+    int c16;
+    __device__ __forceinline__ float operator()(int it) const { return exp2f(Bs[16 * it + c16]); }
+};
+
+// Gated state hop: S = 2^B S + K^T (2^{B - b} V), V's time slots as in
+// load_vfrags (slot s of lane group g: time 32 ts + 4g + s, then 32 ts + 16 +
+// 4g + s - 4).
+template <typename Cf, typename T>
+__device__ __forceinline__ void state_hop_gated(f32x4 (&Sacc)[Cf::NVW][Cf::NDT],
+                                                const typename Cf::Fr (&Vf)[Cf::NVW][Cf::NTS],
+                                                const T* Ks, const float* Bs, int w, int g, int lane) {
+    using Fr = typename Cf::Fr;
+    const float B = Bs[Cf::CT - 1];
+    const float dS = exp2f(B);
+#pragma unroll
+    for (int vw = 0; vw < Cf::NVW; ++vw)
+#pragma unroll
+        for (int dt = 0; dt < Cf::NDT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Sacc[vw][dt][r] = Sacc[vw][dt][r] * dS;
+    Fr Vh[Cf::NVW][Cf::NTS], Vl[Cf::NVW][Cf::NTS];
+#pragma unroll
+    for (int ts = 0; ts < Cf::NTS; ++ts) {
+        float h[8];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            h[s] = exp2f(B - Bs[32 * ts + 4 * g + s]);
+            h[4 + s] = exp2f(B - Bs[32 * ts + 16 + 4 * g + s]);
+        }
+#pragma unroll
+        for (int vw = 0; vw < Cf::NVW; ++vw)
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const float x = to_f32(Vf[vw][ts][s]) * h[s];
+                if constexpr (Cf::BF) {
+                    const bf16 hi = to_bf16(x);
+                    Vh[vw][ts][s] = hi;
+                    Vl[vw][ts][s] = to_bf16(x - to_f32(hi));
+                } else {
+                    Vh[vw][ts][s] = x;
+                }
+            }
+    }
+#pragma unroll
+    for (int dt = 0; dt < Cf::NDT; ++dt) {
+#pragma unroll
+        for (int ts = 0; ts < Cf::NTS; ++ts) {
+            const Fr kt = lds_col(Ks, Cf::LK, 32 * ts, 16 * dt, lane);
+#pragma unroll
+            for (int vw = 0; vw < Cf::NVW; ++vw) {
+                if (!(Cf::ALL_WAVES || w + Cf::NW * vw < Cf::NVT)) continue;
+                Sacc[vw][dt] = mma(kt, Vh[vw][ts], Sacc[vw][dt]);
+                if constexpr (Cf::BF) Sacc[vw][dt] = mma(kt, Vl[vw][ts], Sacc[vw][dt]);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Phase 1: per-segment state increments K_seg^T V_seg -> ws slot seg + 1,
 // one workgroup per (b,h), segment (all but the last) and value block.
 // ---------------------------------------------------------------------------
@@ -1028,15 +1136,20 @@ struct WideCfg : WalkCfg<bf16, CT, 128, 128, kWideWaves> {
     static constexpr int BYTES = (2 * BUF + Base::NP * Base::P_ELEMS) * 2;
 };
 
-template <int CT, typename In>
+// GATED: the gated walk (see k_gated_walk) with one query head per state;
+// the chunk's decay prefix is double buffered (Bs2), written for chunk c + 1
+// by wave 0 while chunk c is computed.
+template <int CT, typename In, bool GATED = false>
 __global__ __launch_bounds__(kWideWaves * kWave) void k_chunk_walk_wide(
     const In* __restrict__ Q, const In* __restrict__ K, const In* __restrict__ V,
     float* __restrict__ S, float* __restrict__ O, const float* __restrict__ ws, int64_t T_len,
-    int dk, int dv, int C, int64_t G, int64_t n_seg, int group, int zero_start) {
+    int dk, int dv, int C, int64_t G, int64_t n_seg, int group, int zero_start,
+    const float* __restrict__ gate) {
     using Cf = WideCfg<CT>;
     using Fr = typename Cf::Fr;
     constexpr int NTH = Cf::NTH;
     __shared__ __attribute__((aligned(16))) unsigned char smem[Cf::BYTES];
+    __shared__ __attribute__((aligned(16))) float Bs2[GATED ? 2 : 1][GATED ? CT : 4];
     bf16* const buf = reinterpret_cast<bf16*>(smem);
     bf16* const Ps = buf + 2 * Cf::BUF;
 
@@ -1055,6 +1168,17 @@ __global__ __launch_bounds__(kWideWaves * kWave) void k_chunk_walk_wide(
     const In* Vb = V + bh * T_len * dv;
     float* Ob = O + bq * T_len * dv;
     auto rows_of = [&](int64_t c) { return c < c1 ? (int)min((int64_t)C, T_len - c * C) : 0; };
+    // gates of row r of chunk c (1 past the chunk's rows); wave 0 holds the
+    // next chunk's in g0, g1
+    auto gate_of = [&](int64_t c, int r) { return r < rows_of(c) ? gate[bh * T_len + c * C + r] : 1.0f; };
+    float g0 = 1.0f, g1 = 1.0f;
+    if constexpr (GATED) {
+        if (w == 0) {
+            chunk_decay<CT>(Bs2[0], gate_of(c0, lane), CT > kWave ? gate_of(c0, kWave + lane) : 1.0f, lane);
+            g0 = gate_of(c0 + 1, lane);
+            if constexpr (CT > kWave) g1 = gate_of(c0 + 1, kWave + lane);
+        }
+    }
 
     // The first chunk's tile loads, then the incoming state straight into
     // the accumulator registers: the first chunk's scores need only the
@@ -1102,7 +1226,8 @@ __global__ __launch_bounds__(kWideWaves * kWave) void k_chunk_walk_wide(
         // the scores, the loads of chunk c + 2 go between the depth steps of
         // the output.
         const rsrc_t rso = make_rsrc(Ob + t_prev * dv, (uint32_t)(n_prev * dv * 4));
-        chunk_scores<Cf>(stiles, Qs, Ks, Ps, w, g, c16, [&](int ds) {
+        const float* Bs = Bs2[GATED ? b : 0];
+        auto out_hook = [&](int ds) {
             if (ds < Cf::NT) {
 #pragma unroll
                 for (int vw = 0; vw < Cf::NVW; ++vw) {
@@ -1111,15 +1236,27 @@ __global__ __launch_bounds__(kWideWaves * kWave) void k_chunk_walk_wide(
                     buf_store16(rso, opaque(off) + (uint32_t)(16 * ds * dv * 4), Oacc[ds][vw]);
                 }
             }
-        });
+        };
+        if constexpr (GATED)
+            chunk_scores<Cf>(stiles, Qs, Ks, Ps, w, g, c16, out_hook, 0, DecayGate{Bs});
+        else
+            chunk_scores<Cf>(stiles, Qs, Ks, Ps, w, g, c16, out_hook);
         // The next chunk into the free buffer (its last readers finished
         // before the previous barrier).
         if (c + 1 < c1) {
             tq.scatter(nxt, tid);
             tk.scatter(nxt + Cf::K_OFF, tid);
             tv.scatter(nxt + Cf::V_OFF, tid);
+            if constexpr (GATED)
+                if (w == 0) chunk_decay<CT>(Bs2[1 - b], g0, g1, lane);
         }
         __syncthreads();  // P complete
+        if constexpr (GATED) {
+            if (w == 0) {
+                g0 = gate_of(c + 2, lane);
+                if constexpr (CT > kWave) g1 = gate_of(c + 2, kWave + lane);
+            }
+        }
 
         const int64_t t2 = (c + 2) * C;
         const int n2 = rows_of(c + 2);
@@ -1127,17 +1264,26 @@ __global__ __launch_bounds__(kWideWaves * kWave) void k_chunk_walk_wide(
                      rv = tv.source(Vb + t2 * dv, dv, n2);
         Fr Vf[Cf::NVW][Cf::NTS];
         load_vfrags<Cf>(Vf, Vs, w, g, lane);
-        chunk_output<Cf>(Oacc, Sacc, Vf, Qs, Ps, w, g, c16, [&](int ds) {
+        auto load_hook = [&](int ds) {
 #pragma unroll
             for (int n = 0; n < decltype(tq)::NPT; ++n) {
                 if (ds == 0) tq.load(rq, n);
                 if (ds == 1) tk.load(rk, n);
                 if (ds == 2) tv.load(rv, n);
             }
-        });
+        };
+        if constexpr (GATED)
+            chunk_output<Cf>(Oacc, Sacc, Vf, Qs, Ps, w, g, c16, load_hook, DecayRows{Bs, c16});
+        else
+            chunk_output<Cf>(Oacc, Sacc, Vf, Qs, Ps, w, g, c16, load_hook);
         t_prev = c * C;
         n_prev = rows_of(c);
-        if (c + 1 < c1 || last_seg) state_hop<Cf>(Sacc, Vf, Ks, w, g, lane);
+        if (c + 1 < c1 || last_seg) {
+            if constexpr (GATED)
+                state_hop_gated<Cf>(Sacc, Vf, Ks, Bs, w, g, lane);
+            else
+                state_hop<Cf>(Sacc, Vf, Ks, w, g, lane);
+        }
         __syncthreads();  // this buffer and P free; the next buffer visible
     }
     store_out<Cf, true>(Ob, Oacc, t_prev, n_prev, dv, dv, w, g, c16);
@@ -1163,16 +1309,21 @@ struct SegWideCfg : WalkCfg<bf16, CT, 128, 128, 8> {
     static constexpr int BYTES = TILE_BYTES > Base::STATE_BYTES ? TILE_BYTES : Base::STATE_BYTES;
 };
 
-template <int CT, typename In>
+// GATED: the gated segment pass (see k_gated_segment_states): the chunk's
+// decay prefix double buffered like the tiles, the segment's total decay to
+// dec[bh * n_seg + seg].
+template <int CT, typename In, bool GATED = false>
 __global__ __launch_bounds__(512) void k_segment_states_wide(const In* __restrict__ K,
                                                              const In* __restrict__ V,
                                                              float* __restrict__ ws, int64_t T_len,
                                                              int dk, int dv, int C, int64_t G,
-                                                             int64_t n_seg) {
+                                                             int64_t n_seg, const float* __restrict__ gate,
+                                                             float* __restrict__ dec) {
     using Cf = SegWideCfg<CT>;
     using Fr = typename Cf::Fr;
     constexpr int NTH = Cf::NTH;
     __shared__ __attribute__((aligned(16))) unsigned char smem[Cf::BYTES];
+    __shared__ __attribute__((aligned(16))) float Bs2[GATED ? 2 : 1][GATED ? CT : 4];
     bf16* const buf = reinterpret_cast<bf16*>(smem);
     float* const Sst = reinterpret_cast<float*>(smem);
 
@@ -1207,6 +1358,15 @@ __global__ __launch_bounds__(512) void k_segment_states_wide(const In* __restric
     }
     tk[0].scatter(buf, tid);
     tv[0].scatter(buf + Cf::V_AT, tid);
+    auto gate_of = [&](int64_t c, int r) { return r < rows_of(c) ? gate[bh * T_len + c * C + r] : 1.0f; };
+    float g0 = 1.0f, g1 = 1.0f, L = 0.0f;
+    if constexpr (GATED) {
+        if (w == 0) {
+            chunk_decay<CT>(Bs2[0], gate_of(c0, lane), CT > kWave ? gate_of(c0, kWave + lane) : 1.0f, lane);
+            g0 = gate_of(c0 + 1, lane);
+            if constexpr (CT > kWave) g1 = gate_of(c0 + 1, kWave + lane);
+        }
+    }
     __syncthreads();
 
     for (int64_t cb = c0; cb < c1; cb += PF) {
@@ -1222,6 +1382,8 @@ __global__ __launch_bounds__(512) void k_segment_states_wide(const In* __restric
             if (c + 1 < c1) {  // the free buffer's last readers passed the previous barrier
                 tk[un].scatter(nxt, tid);
                 tv[un].scatter(nxt + Cf::V_AT, tid);
+                if constexpr (GATED)
+                    if (w == 0) chunk_decay<CT>(Bs2[1 - b], g0, g1, lane);
             }
             // set u held chunk c, written to LDS one chunk ago: reload it
             const int64_t tn = (c + PF) * C;
@@ -1230,15 +1392,29 @@ __global__ __launch_bounds__(512) void k_segment_states_wide(const In* __restric
 
             Fr Vf[Cf::NVW][Cf::NTS];
             load_vfrags<Cf>(Vf, Vs, w, g, lane);
-#pragma unroll
-            for (int dt = 0; dt < Cf::NDT; ++dt) {
-#pragma unroll
-                for (int ts = 0; ts < Cf::NTS; ++ts)
-                    Sacc[0][dt] = mma(lds_col(Ks, Cf::LK, 32 * ts, 16 * dt, lane), Vf[0][ts], Sacc[0][dt]);
+            if constexpr (GATED) {
 #pragma unroll
                 for (int n = 0; n < TK::NPT; ++n) {
-                    if (dt == 1) tk[u].load(rk, n);
-                    if (dt == 3) tv[u].load(rv, n);
+                    tk[u].load(rk, n);
+                    tv[u].load(rv, n);
+                }
+                if (w == 0) {
+                    g0 = gate_of(c + 2, lane);
+                    if constexpr (CT > kWave) g1 = gate_of(c + 2, kWave + lane);
+                }
+                state_hop_gated<Cf>(Sacc, Vf, Ks, Bs2[b], w, g, lane);
+                L += Bs2[b][CT - 1];
+            } else {
+#pragma unroll
+                for (int dt = 0; dt < Cf::NDT; ++dt) {
+#pragma unroll
+                    for (int ts = 0; ts < Cf::NTS; ++ts)
+                        Sacc[0][dt] = mma(lds_col(Ks, Cf::LK, 32 * ts, 16 * dt, lane), Vf[0][ts], Sacc[0][dt]);
+#pragma unroll
+                    for (int n = 0; n < TK::NPT; ++n) {
+                        if (dt == 1) tk[u].load(rk, n);
+                        if (dt == 3) tv[u].load(rv, n);
+                    }
                 }
             }
             __syncthreads();  // this buffer free; the next one visible
@@ -1249,114 +1425,8 @@ __global__ __launch_bounds__(512) void k_segment_states_wide(const In* __restric
     state_regs_to_lds<Cf>(Sst, Sacc, w, g, c16);
     __syncthreads();
     state_lds_to_gmem<Cf>(ws + (bh * n_seg + seg + 1) * (int64_t)dk * dv, Sst, dk, dv, dv, tid);
-}
-
-// ---------------------------------------------------------------------------
-// Gated (decayed) state: S_t = g_t S_{t-1} + k_t v_t^T, o_t = S_t^T q_t, one
-// gate g_t per (b,h) and token.  The slide deck cites the chunkwise form of
-// gated linear attention ("Boundary, evidence, and sources") but gives no
-// gate; this is the plainest decay, a scalar applied to the previous state
-// before the token's update (g = 1: the walk above).  Gates are taken in
-// [2^-126, 1]: g <= 0 (and NaN) acts as 2^-126, g > 1 as 1.
-// Per chunk, with b_t = sum_{l <= t} log2 g_l over the chunk's rows (rows past
-// the last count 0) and B = b_{CT-1}, the chunk form is
-//     O_i     = sum_{j <= i} 2^{b_i - b_j} (q_i . k_j) v_j + 2^{b_i} q_i S_c
-//     S_{c+1} = 2^B S_c + sum_j 2^{B - b_j} k_j v_j^T
-// and every factor is at most 1.  The masked scores are scaled in fp32 before
-// their bf16 high + low split; Q S is accumulated apart and added scaled in
-// fp32; the hop takes V scaled by 2^{B - b_j} as a high + low pair.  So the
-// numerics are the ungated walk's.  A segment's total decay (the sum of its
-// chunks' B) goes to the workspace after the states, and the scan is
-// P_{s+1} = 2^{L_s} P_s + increment_s.
-// ---------------------------------------------------------------------------
-
-// Wave 0: the chunk's prefix b_t into Bs[0 .. CT-1], from the gates of rows
-// `lane` (g0) and 64 + `lane` (g1), 1 past the chunk's rows.
-template <int CT>
-__device__ __forceinline__ void chunk_decay(float* Bs, float g0, float g1, int lane) {
-    auto log2g = [](float x) { return fminf(fmaxf(log2f(x), -126.0f), 0.0f); };
-    auto scan = [&](float a) {
-#pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) {
-            const float y = __shfl_up(a, d, kWave);
-            if (lane >= d) a += y;
-        }
-        return a;
-    };
-    const float a = scan(log2g(g0));
-    if (lane < CT) Bs[lane] = a;
-    if constexpr (CT > kWave) Bs[kWave + lane] = scan(log2g(g1)) + __shfl(a, kWave - 1, kWave);
-}
-
-// Masked score (query i, keys j0 .. j0 + 3) times 2^{b_i - b_j} (masked
-// entries are zero and stay zero: the factor is clamped to at most 1).
-struct DecayGate {
-    const float* Bs;
-    __device__ __forceinline__ void operator()(f32x4& x, int i, int j0) const {
-        const float bi = Bs[i];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) x[r] = x[r] * exp2f(fminf(bi - Bs[j0 + r], 0.0f));
-    }
-};
-// The factor 2^{b_i} of query row i = 16 it + c16's incoming-state term.
-struct DecayRows {
-    const float* Bs;
-    int c16;
-    __device__ __forceinline__ float operator()(int it) const { return exp2f(Bs[16 * it + c16]); }
-};
-
-// Gated state hop: S = 2^B S + K^T (2^{B - b} V), V's time slots as in
-// load_vfrags (slot s of lane group g: time 32 ts + 4g + s, then 32 ts + 16 +
-// 4g + s - 4).
-template <typename Cf, typename T>
-__device__ __forceinline__ void state_hop_gated(f32x4 (&Sacc)[Cf::NVW][Cf::NDT],
-                                                const typename Cf::Fr (&Vf)[Cf::NVW][Cf::NTS],
-                                                const T* Ks, const float* Bs, int w, int g, int lane) {
-    using Fr = typename Cf::Fr;
-    const float B = Bs[Cf::CT - 1];
-    const float dS = exp2f(B);
-#pragma unroll
-    for (int vw = 0; vw < Cf::NVW; ++vw)
-#pragma unroll
-        for (int dt = 0; dt < Cf::NDT; ++dt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Sacc[vw][dt][r] = Sacc[vw][dt][r] * dS;
-    Fr Vh[Cf::NVW][Cf::NTS], Vl[Cf::NVW][Cf::NTS];
-#pragma unroll
-    for (int ts = 0; ts < Cf::NTS; ++ts) {
-        float h[8];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            h[s] = exp2f(B - Bs[32 * ts + 4 * g + s]);
-            h[4 + s] = exp2f(B - Bs[32 * ts + 16 + 4 * g + s]);
-        }
-#pragma unroll
-        for (int vw = 0; vw < Cf::NVW; ++vw)
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const float x = to_f32(Vf[vw][ts][s]) * h[s];
-                if constexpr (Cf::BF) {
-                    const bf16 hi = to_bf16(x);
-                    Vh[vw][ts][s] = hi;
-                    Vl[vw][ts][s] = to_bf16(x - to_f32(hi));
-                } else {
-                    Vh[vw][ts][s] = x;
-                }
-            }
-    }
-#pragma unroll
-    for (int dt = 0; dt < Cf::NDT; ++dt) {
-#pragma unroll
-        for (int ts = 0; ts < Cf::NTS; ++ts) {
-            const Fr kt = lds_col(Ks, Cf::LK, 32 * ts, 16 * dt, lane);
-#pragma unroll
-            for (int vw = 0; vw < Cf::NVW; ++vw) {
-                if (!(Cf::ALL_WAVES || w + Cf::NW * vw < Cf::NVT)) continue;
-                Sacc[vw][dt] = mma(kt, Vh[vw][ts], Sacc[vw][dt]);
-                if constexpr (Cf::BF) Sacc[vw][dt] = mma(kt, Vl[vw][ts], Sacc[vw][dt]);
-            }
-        }
-    }
+    if constexpr (GATED)
+        if (tid == 0) dec[bh * n_seg + seg] = L;
 }
 
 // Gated phase 1: each segment's increment sum_t 2^{L_seg - b_t} k_t v_t^T
@@ -1603,7 +1673,7 @@ static hipError_t launch_walk_t(const PrefillPlan& p, const void* Q, const void*
             hipLaunchKernelGGL((k_chunk_walk_wide<CT, In>), dim3((unsigned)(p.BHq * p.n_seg)), dim3(kWideWaves * kWave), 0, st,
                                (const In*)Q, (const In*)K, (const In*)V, S, O,
                                (const float*)(p.use_ws ? ws : nullptr), p.T, p.dk, p.dv, p.C, p.G,
-                               p.n_seg, p.group, (int)p.zero_start);
+                               p.n_seg, p.group, (int)p.zero_start, (const float*)nullptr);
             return hipGetLastError();
         }
     }
@@ -1638,7 +1708,7 @@ static hipError_t launch_seg_t(const PrefillPlan& p, const void* K, const void* 
         if (p.vec) {  // one eight-wave workgroup per (b,h) and segment
             hipLaunchKernelGGL((k_segment_states_wide<CT, In>), dim3((unsigned)(p.BH * (p.n_seg - 1))),
                                dim3(512), 0, st, (const In*)K, (const In*)V, ws, p.T, p.dk, p.dv,
-                               p.C, p.G, p.n_seg);
+                               p.C, p.G, p.n_seg, (const float*)nullptr, (float*)nullptr);
             return hipGetLastError();
         }
     }
@@ -1747,6 +1817,15 @@ hipError_t launch_segment_states(const PrefillPlan& p, const void* K, const void
 template <typename In, int CT, int D>
 static hipError_t launch_gated_seg_t(const PrefillPlan& p, const void* K, const void* V, const float* gate,
                                      float* ws, float* dec, hipStream_t st) {
+    using T = typename Compute<In>::type;
+    if constexpr (std::is_same<T, bf16>::value && D == 128 && CT <= 64) {
+        if (p.vec) {  // one eight-wave workgroup per (b,h) and segment
+            hipLaunchKernelGGL((k_segment_states_wide<CT, In, true>), dim3((unsigned)(p.BH * (p.n_seg - 1))),
+                               dim3(512), 0, st, (const In*)K, (const In*)V, ws, p.T, p.dk, p.dv, p.C, p.G,
+                               p.n_seg, gate, dec);
+            return hipGetLastError();
+        }
+    }
     constexpr int BV = D > 64 ? 64 : D;
     const int64_t grid = p.BH * (p.n_seg - 1) * p.n_vb;
     if (p.vec)
@@ -1763,6 +1842,16 @@ static hipError_t launch_gated_seg_t(const PrefillPlan& p, const void* K, const 
 template <typename In, int CT, int D>
 static hipError_t launch_gated_walk_t(const PrefillPlan& p, const void* Q, const void* K, const void* V,
                                       const float* gate, float* S, float* O, float* ws, hipStream_t st) {
+    using T = typename Compute<In>::type;
+    if constexpr (std::is_same<T, bf16>::value && D == 128 && CT <= 64) {
+        if (p.vec) {  // one eight-wave workgroup per (b,h) and segment
+            hipLaunchKernelGGL((k_chunk_walk_wide<CT, In, true>), dim3((unsigned)(p.BHq * p.n_seg)),
+                               dim3(kWideWaves * kWave), 0, st, (const In*)Q, (const In*)K, (const In*)V, S, O,
+                               (const float*)(p.use_ws ? ws : nullptr), p.T, p.dk, p.dv, p.C, p.G, p.n_seg, 1,
+                               (int)p.zero_start, gate);
+            return hipGetLastError();
+        }
+    }
     constexpr int BV = D > 64 ? 64 : D;
     const int64_t grid = p.BH * p.n_seg * p.n_vb;
     const float* wsr = p.use_ws ? ws : nullptr;

@@ -59,14 +59,14 @@ PREFILL_SOURCES = ("lla_prefill.hip", "lla_device.h", "lla_plan.cpp", "lla_inter
 # sources that define the kernel, workload).  Grids follow from the plan
 # (tests/test_profiling_host.py recomputes them).
 KERNELS = {
-    "chunk_walk": (("k_chunk_walk_wideILi64EDF16b", "k_chunk_walk_wide<64, __bf16>"), 16 * 16 * 512,
+    "chunk_walk": (("k_chunk_walk_wideILi64EDF16bLb0E", "k_chunk_walk_wide<64, __bf16, false>"), 16 * 16 * 512,
                    "chunk_walk_T8192_traffic.txt", PREFILL_SOURCES, "prefill_T8192"),
-    "segment_states": (("k_segment_states_wideILi64EDF16b", "k_segment_states_wide<64, __bf16>"),
+    "segment_states": (("k_segment_states_wideILi64EDF16bLb0E", "k_segment_states_wide<64, __bf16, false>"),
                        16 * 15 * 512, "segment_states_T8192_traffic.txt",
                        PREFILL_SOURCES, "prefill_T8192"),
     "state_scan": (("k_state_scan",), 16 * 16 * 256, "state_scan_T8192_traffic.txt",
                    PREFILL_SOURCES, "prefill_T8192"),
-    "chunk_walk_fp8": (("k_chunk_walk_wideILi64ENS_7fp8e4m3", "k_chunk_walk_wide<64, lla::fp8e4m3>"),
+    "chunk_walk_fp8": (("k_chunk_walk_wideILi64ENS_7fp8e4m3ELb0E", "k_chunk_walk_wide<64, lla::fp8e4m3, false>"),
                        16 * 16 * 512, "chunk_walk_T8192_fp8_traffic.txt",
                        PREFILL_SOURCES, "prefill_T8192_fp8"),
     "chunk_walk_T1024": (("k_chunk_walkIDF16bLi64ELi64ELi64ELb1ELi4E", "k_chunk_walk<__bf16, 64, 64, 64, true, 4>"),

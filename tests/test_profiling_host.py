@@ -54,7 +54,10 @@ def test_kernel_grids_follow_the_plan():
 
 
 def test_kernel_names_match_in_both_trace_forms():
-    assert profiling.matches("_ZN3lla17k_chunk_walk_wideILi64EDF16bEEvPKT0_S3_S3_PfS4_PKfliiillii", "chunk_walk")
-    assert profiling.matches("void lla::k_chunk_walk_wide<64, lla::fp8e4m3>(...)", "chunk_walk_fp8")
-    assert not profiling.matches("void lla::k_chunk_walk_wide<64, lla::fp8e4m3>(...)", "chunk_walk")
+    assert profiling.matches("_ZN3lla17k_chunk_walk_wideILi64EDF16bLb0EEEvPKT0_S3_S3_PfS4_PKfliiilliiS6_", "chunk_walk")
+    assert profiling.matches("void lla::k_chunk_walk_wide<64, lla::fp8e4m3, false>(...)", "chunk_walk_fp8")
+    assert not profiling.matches("void lla::k_chunk_walk_wide<64, lla::fp8e4m3, false>(...)", "chunk_walk")
+    # the gated walk has the plain walk's grid: it must not be taken for it
+    assert not profiling.matches("_ZN3lla17k_chunk_walk_wideILi64EDF16bLb1EEEvPKT0_S3_S3_PfS4_PKfliiilliiS6_",
+                                 "chunk_walk")
     assert profiling.matches("lla::k_state_scan(float const*, float*, long, long, long, int)", "state_scan")
