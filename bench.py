@@ -722,7 +722,7 @@ def bench_gated(args, torch, lla, workloads, profiling):
            "value": n / wall, "unit": "steps/s", "ms_per_step": wall * 1e3 / n,
            "gpu_ms_per_step": kern_ms, "tokens_per_s": B * n / wall,
            "roofline": hbm_roofline("k_decode_step_sq<bf16,128,512,gated>", nbytes, kern_ms, args.gap_ms,
-                                    None, "HIP events around the timed steps")}
+                                    profiling.stored_traffic("gated_decode"), "HIP events around the timed steps")}
     del calls, qd, kd, vd, gd, S
     torch.cuda.empty_cache()
     return {"prefill": pre, "decode": dec}

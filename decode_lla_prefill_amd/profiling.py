@@ -48,7 +48,8 @@ COPY_BYTES = 1 << 30
 
 # The workloads ``run`` can drive (keys of workloads.CONFIGS).
 WORKLOADS = ("prefill_T8192", "prefill_T8192_fp8", "prefill_B4_T1024", "prefill_T131072",
-             "decode_B256", "decode_B256_gqa", "decode_B256_gqa_T16")
+             "decode_B256", "decode_B256_gqa", "decode_B256_gqa_T16", "prefill_T8192_gated",
+             "decode_B256_gated")
 
 # what decides a prefill kernel's work: its code and the plan that cuts the
 # shape into segments
@@ -76,7 +77,8 @@ KERNELS = {
                             "k_chunk_walk<__bf16, 128, 128, 128, true, 8>"),
                            32 * 8 * 512, "chunk_walk_T131072_traffic.txt",
                            PREFILL_SOURCES, "prefill_T131072"),
-    "decode_step": (("k_decode_step_sq",), 256 * 32 * 512, "decode_step_B256_H32_traffic.txt",
+    "decode_step": (("k_decode_step_sqIDF16bLi128ELi512ELb0E", "k_decode_step_sq<__bf16, 128, 512, false>"),
+                    256 * 32 * 512, "decode_step_B256_H32_traffic.txt",
                     ("lla_decode.hip", "lla_device.h"), "decode_B256"),
     "decode_group": (("k_decode_group",), 256 * 8 * 512, "decode_group_B256_Hq32_Hkv8_traffic.txt",
                      ("lla_decode.hip", "lla_device.h"), "decode_B256_gqa"),
@@ -85,6 +87,16 @@ KERNELS = {
     "tokens_grouped": (("k_tokens_groupedIDF16bLi128ELi64ELi4E", "k_tokens_grouped<__bf16, 128, 64, 4>"),
                        256 * 8 * 2 * 256, "tokens_grouped_B256_Hq32_Hkv8_T16_traffic.txt",
                        PREFILL_SOURCES, "decode_B256_gqa_T16"),
+    # the gated (decayed) state: the T=8192 prefill's walk and segment pass
+    # (the plain kernels with the GATED flag), and the decode step
+    "gated_walk": (("k_chunk_walk_wideILi64EDF16bLb1E", "k_chunk_walk_wide<64, __bf16, true>"), 16 * 16 * 512,
+                   "gated_walk_T8192_traffic.txt", PREFILL_SOURCES, "prefill_T8192_gated"),
+    "gated_segment_states": (("k_segment_states_wideILi64EDF16bLb1E", "k_segment_states_wide<64, __bf16, true>"),
+                             16 * 15 * 512, "gated_segment_states_T8192_traffic.txt", PREFILL_SOURCES,
+                             "prefill_T8192_gated"),
+    "gated_decode": (("k_decode_step_sqIDF16bLi128ELi512ELb1E", "k_decode_step_sq<__bf16, 128, 512, true>"),
+                     256 * 32 * 512, "gated_decode_B256_H32_traffic.txt", ("lla_decode.hip", "lla_device.h"),
+                     "decode_B256_gated"),
 }
 
 SIMD_NUM = 256 * 4  # MI355X: 256 compute units of 4 SIMDs (the SIMD_NUM of MfmaUtil)
@@ -159,7 +171,8 @@ def run(launches: int, which=WORKLOADS) -> None:
     import torch
     sys.path.insert(0, ROOT)
     import workloads
-    from . import PreparedDecode, PreparedPrefill, library, state_init
+    from . import (PreparedDecode, PreparedGatedDecode, PreparedGatedPrefill, PreparedPrefill, library,
+                   state_init)
 
     library()
     dev = torch.device("cuda:0")
@@ -186,6 +199,30 @@ def run(launches: int, which=WORKLOADS) -> None:
                 c()
             torch.cuda.synchronize()
             del calls, S, qd, kd, vd
+        elif name == "prefill_T8192_gated":
+            # the T=8192 prefill with a decayed state, gates in [0.9, 1]
+            cfg = workloads.CONFIGS["prefill_T8192"]
+            q0, k0, v0 = workloads.config_inputs(cfg, device=dev)
+            g0 = workloads.gates(cfg.B, cfg.H, cfg.T, seed=cfg.seed_base + 9, device=dev)
+            sets = []
+            for r in range(4):
+                q, k, v, g = (x.clone() for x in (q0, k0, v0, g0)) if r else (q0, k0, v0, g0)
+                S = torch.empty((cfg.B, cfg.H, cfg.dk, cfg.dv), device=dev)
+                sets.append(PreparedGatedPrefill(q, k, v, g, S, cfg.C))
+            for i in range(launches):
+                sets[i % 4](zero_state=True)
+            torch.cuda.synchronize()
+            del sets, q0, k0, v0, g0
+        elif name == "decode_B256_gated":
+            cfg = workloads.CONFIGS["decode_B256"]
+            S = state_init(cfg.B, cfg.H, cfg.dk, cfg.dv, device=dev)
+            qd, kd, vd = workloads.decode_inputs(cfg, launches, device=dev)
+            gd = workloads.gates(launches, cfg.B, cfg.H, seed=cfg.seed_base + 9, device=dev)
+            calls = [PreparedGatedDecode(qd[i], kd[i], vd[i], gd[i], S) for i in range(launches)]
+            for c in calls:
+                c()
+            torch.cuda.synchronize()
+            del calls, S, qd, kd, vd, gd
         elif name == "decode_B256_gqa_T16":
             # 16-token continuations of the grouped states, cycling over
             # three state sets (lla_prefill_gqa, short-prompt route)

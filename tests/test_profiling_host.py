@@ -51,6 +51,10 @@ def test_kernel_grids_follow_the_plan():
     assert profiling.KERNELS["decode_group"][1] == c.B * c.kv_heads * 512
     # two 64-column blocks per 128 x 128 state, four waves each
     assert profiling.KERNELS["tokens_grouped"][1] == c.B * c.kv_heads * 2 * 256
+    # the gated kernels: the plain wide ones' grids (the same plan)
+    assert profiling.KERNELS["gated_walk"][1] == profiling.KERNELS["chunk_walk"][1]
+    assert profiling.KERNELS["gated_segment_states"][1] == profiling.KERNELS["segment_states"][1]
+    assert profiling.KERNELS["gated_decode"][1] == profiling.KERNELS["decode_step"][1]
 
 
 def test_kernel_names_match_in_both_trace_forms():
@@ -61,3 +65,7 @@ def test_kernel_names_match_in_both_trace_forms():
     assert not profiling.matches("_ZN3lla17k_chunk_walk_wideILi64EDF16bLb1EEEvPKT0_S3_S3_PfS4_PKfliiilliiS6_",
                                  "chunk_walk")
     assert profiling.matches("lla::k_state_scan(float const*, float*, long, long, long, int)", "state_scan")
+    assert not profiling.matches("_ZN3lla16k_decode_step_sqIDF16bLi128ELi512ELb1EEEvPKT_S3_S3_PfS4_PKf",
+                                 "decode_step")
+    assert profiling.matches("_ZN3lla16k_decode_step_sqIDF16bLi128ELi512ELb1EEEvPKT_S3_S3_PfS4_PKf",
+                             "gated_decode")
