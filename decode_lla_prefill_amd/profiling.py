@@ -179,7 +179,7 @@ def run(launches: int, which=WORKLOADS) -> None:
     torch.cuda.set_device(dev)
     for name in which:
         cfg = workloads.CONFIGS.get(name)
-        if name.startswith("prefill"):
+        if name.startswith("prefill") and not name.endswith("_gated"):
             rotate = 2 if cfg.T >= 65536 else 4
             q0, k0, v0 = workloads.config_inputs(cfg, device=dev)
             sets = []
