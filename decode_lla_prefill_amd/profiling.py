@@ -88,10 +88,13 @@ KERNELS = {
                        256 * 8 * 2 * 256, "tokens_grouped_B256_Hq32_Hkv8_T16_traffic.txt",
                        PREFILL_SOURCES, "decode_B256_gqa_T16"),
     # the gated (decayed) state: the T=8192 prefill's walk and segment pass
-    # (the plain kernels with the GATED flag), and the decode step
-    "gated_walk": (("k_chunk_walk_wideILi64EDF16bLb1E", "k_chunk_walk_wide<64, __bf16, true>"), 16 * 16 * 512,
+    # (the plain kernels with the GATED flag), and the decode step.  The
+    # trace demangles the bf16-with-flag names as "<64, bool _Accum, bool, E>".
+    "gated_walk": (("k_chunk_walk_wideILi64EDF16bLb1E", "k_chunk_walk_wide<64, __bf16, true>",
+                    "k_chunk_walk_wide<64, bool _Accum, bool, E>"), 16 * 16 * 512,
                    "gated_walk_T8192_traffic.txt", PREFILL_SOURCES, "prefill_T8192_gated"),
-    "gated_segment_states": (("k_segment_states_wideILi64EDF16bLb1E", "k_segment_states_wide<64, __bf16, true>"),
+    "gated_segment_states": (("k_segment_states_wideILi64EDF16bLb1E", "k_segment_states_wide<64, __bf16, true>",
+                              "k_segment_states_wide<64, bool _Accum, bool, E>"),
                              16 * 15 * 512, "gated_segment_states_T8192_traffic.txt", PREFILL_SOURCES,
                              "prefill_T8192_gated"),
     "gated_decode": (("k_decode_step_sqIDF16bLi128ELi512ELb1E", "k_decode_step_sq<__bf16, 128, 512, true>"),
