@@ -4,8 +4,9 @@
 The oracle (lla_oracle.c) and the library's host code (argument checking,
 status strings, the plan) are rebuilt with -fsanitize=address,undefined and
 no recovery, so the first finding aborts.  A child process with the
-sanitizer runtime preloaded then runs the oracle's pins (test_oracle.py) and
-the C ABI's host checks (test_abi_host.py) against those builds.  A planted
+sanitizer runtime preloaded then runs the oracle's pins (test_oracle.py,
+test_oracle_gated.py) and the C ABI's host checks (test_abi_host.py,
+test_gated_host.py) against those builds.  A planted
 out-of-bounds read in a throwaway C function, built and loaded the same way,
 must abort, which shows the sanitizers are live in that setting."""
 import os
@@ -63,6 +64,7 @@ def test_a_planted_out_of_bounds_read_aborts(sanitized, tmp_path):
 def test_oracle_pins_and_abi_host_checks_under_sanitizers(sanitized):
     _, _, env = sanitized
     r = _child(env, "-m", "pytest", "-q", "-m", "not gpu", "-p", "no:cacheprovider",
-               "tests/test_oracle.py", "tests/test_abi_host.py")
+               "tests/test_oracle.py", "tests/test_abi_host.py", "tests/test_oracle_gated.py",
+               "tests/test_gated_host.py")
     assert r.returncode == 0, (r.stdout[-3000:], r.stderr[-3000:])
     assert " passed" in r.stdout and "error" not in r.stdout.splitlines()[-1]
