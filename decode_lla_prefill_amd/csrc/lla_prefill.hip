@@ -622,11 +622,18 @@ __device__ __forceinline__ void chunk_output(f32x4 (&Oacc)[Cf::NT][Cf::NVW],
 // P_{s+1} = 2^{L_s} P_s + increment_s.
 // ---------------------------------------------------------------------------
 
-// Wave 0: the chunk's prefix b_t into Bs[0 .. CT-1], from the gates of rows
+// A chunk's decay table, 3 CT floats: D[t] = b_t, D[CT + t] = 2^{B - b_t}
+// (the hop's factor of row t), D[2 CT + t] = 2^{b_t} (the incoming-state
+// factor of query row t).  exp2 and log2 are the hardware instructions
+// (about 1 ulp): arguments are at most 0, and results below 2^-126 only
+// scale away terms that are already negligible.
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Wave 0: a chunk's decay table from the gates of rows
 // `lane` (g0) and 64 + `lane` (g1), 1 past the chunk's rows.
 template <int CT>
-__device__ __forceinline__ void chunk_decay(float* Bs, float g0, float g1, int lane) {
-    auto log2g = [](float x) { return fminf(fmaxf(log2f(x), -126.0f), 0.0f); };
+__device__ __forceinline__ void chunk_decay(float* D, float g0, float g1, int lane) {
+    auto log2g = [](float x) { return fminf(fmaxf(__builtin_amdgcn_logf(x), -126.0f), 0.0f); };
     auto scan = [&](float a) {
 #pragma unroll
         for (int d = 1; d < kWave; d <<= 1) {
@@ -636,25 +643,42 @@ __device__ __forceinline__ void chunk_decay(float* Bs, float g0, float g1, int l
         return a;
     };
     const float a = scan(log2g(g0));
-    if (lane < CT) Bs[lane] = a;
-    if constexpr (CT > kWave) Bs[kWave + lane] = scan(log2g(g1)) + __shfl(a, kWave - 1, kWave);
+    if constexpr (CT > kWave) {
+        const float a1 = scan(log2g(g1)) + __shfl(a, kWave - 1, kWave);
+        const float B = __shfl(a1, kWave - 1, kWave);
+        D[lane] = a;
+        D[CT + lane] = hw_exp2(B - a);
+        D[2 * CT + lane] = hw_exp2(a);
+        D[kWave + lane] = a1;
+        D[CT + kWave + lane] = hw_exp2(B - a1);
+        D[2 * CT + kWave + lane] = hw_exp2(a1);
+    } else {
+        const float B = __shfl(a, CT - 1, kWave);
+        if (lane < CT) {
+            D[lane] = a;
+            D[CT + lane] = hw_exp2(B - a);
+            D[2 * CT + lane] = hw_exp2(a);
+        }
+    }
 }
 
 // Masked score (query i, keys j0 .. j0 + 3) times 2^{b_i - b_j} (masked
 // entries are zero and stay zero: the factor is clamped to at most 1).
 struct DecayGate {
-    const float* Bs;
+    const float* Bs;  // the decay table
     __device__ __forceinline__ void operator()(f32x4& x, int i, int j0) const {
         const float bi = Bs[i];
+        const f32x4 bj = *reinterpret_cast<const f32x4*>(Bs + j0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) x[r] = x[r] * exp2f(fminf(bi - Bs[j0 + r], 0.0f));
+        for (int r = 0; r < 4; ++r) x[r] = x[r] * hw_exp2(fminf(bi - bj[r], 0.0f));
     }
 };
 // The factor 2^{b_i} of query row i = 16 it + c16's incoming-state term.
+template <int CT>
 struct DecayRows {
-    const float* Bs;
+    const float* Bs;  // the decay table
     int c16;
-    __device__ __forceinline__ float operator()(int it) const { return exp2f(Bs[16 * it + c16]); }
+    __device__ __forceinline__ float operator()(int it) const { return Bs[2 * CT + 16 * it + c16]; }
 };
 
 // Gated state hop: S = 2^B S + K^T (2^{B - b} V), V's time slots as in
@@ -665,8 +689,7 @@ __device__ __forceinline__ void state_hop_gated(f32x4 (&Sacc)[Cf::NVW][Cf::NDT],
                                                 const typename Cf::Fr (&Vf)[Cf::NVW][Cf::NTS],
                                                 const T* Ks, const float* Bs, int w, int g, int lane) {
     using Fr = typename Cf::Fr;
-    const float B = Bs[Cf::CT - 1];
-    const float dS = exp2f(B);
+    const float dS = Bs[3 * Cf::CT - 1];  // 2^B
 #pragma unroll
     for (int vw = 0; vw < Cf::NVW; ++vw)
 #pragma unroll
@@ -676,12 +699,9 @@ __device__ __forceinline__ void state_hop_gated(f32x4 (&Sacc)[Cf::NVW][Cf::NDT],
     Fr Vh[Cf::NVW][Cf::NTS], Vl[Cf::NVW][Cf::NTS];
 #pragma unroll
     for (int ts = 0; ts < Cf::NTS; ++ts) {
-        float h[8];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            h[s] = exp2f(B - Bs[32 * ts + 4 * g + s]);
-            h[4 + s] = exp2f(B - Bs[32 * ts + 16 + 4 * g + s]);
-        }
+        const f32x4 h0 = *reinterpret_cast<const f32x4*>(Bs + Cf::CT + 32 * ts + 4 * g);
+        const f32x4 h1 = *reinterpret_cast<const f32x4*>(Bs + Cf::CT + 32 * ts + 16 + 4 * g);
+        const float h[8] = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
 #pragma unroll
         for (int vw = 0; vw < Cf::NVW; ++vw)
 #pragma unroll
@@ -1149,7 +1169,7 @@ __global__ __launch_bounds__(kWideWaves * kWave) void k_chunk_walk_wide(
     using Fr = typename Cf::Fr;
     constexpr int NTH = Cf::NTH;
     __shared__ __attribute__((aligned(16))) unsigned char smem[Cf::BYTES];
-    __shared__ __attribute__((aligned(16))) float Bs2[GATED ? 2 : 1][GATED ? CT : 4];
+    __shared__ __attribute__((aligned(16))) float Bs2[GATED ? 2 : 1][GATED ? 3 * CT : 4];
     bf16* const buf = reinterpret_cast<bf16*>(smem);
     bf16* const Ps = buf + 2 * Cf::BUF;
 
@@ -1273,7 +1293,7 @@ __global__ __launch_bounds__(kWideWaves * kWave) void k_chunk_walk_wide(
             }
         };
         if constexpr (GATED)
-            chunk_output<Cf>(Oacc, Sacc, Vf, Qs, Ps, w, g, c16, load_hook, DecayRows{Bs, c16});
+            chunk_output<Cf>(Oacc, Sacc, Vf, Qs, Ps, w, g, c16, load_hook, DecayRows<CT>{Bs, c16});
         else
             chunk_output<Cf>(Oacc, Sacc, Vf, Qs, Ps, w, g, c16, load_hook);
         t_prev = c * C;
@@ -1323,7 +1343,7 @@ __global__ __launch_bounds__(512) void k_segment_states_wide(const In* __restric
     using Fr = typename Cf::Fr;
     constexpr int NTH = Cf::NTH;
     __shared__ __attribute__((aligned(16))) unsigned char smem[Cf::BYTES];
-    __shared__ __attribute__((aligned(16))) float Bs2[GATED ? 2 : 1][GATED ? CT : 4];
+    __shared__ __attribute__((aligned(16))) float Bs2[GATED ? 2 : 1][GATED ? 3 * CT : 4];
     bf16* const buf = reinterpret_cast<bf16*>(smem);
     float* const Sst = reinterpret_cast<float*>(smem);
 
@@ -1442,7 +1462,7 @@ __global__ __launch_bounds__(kThreads) void k_gated_segment_states(
     using Cf = WalkCfg<T, CT, D, BV, kWaves>;
     using Fr = typename Cf::Fr;
     __shared__ __attribute__((aligned(16))) unsigned char smem[Cf::SEG_BYTES];
-    __shared__ __attribute__((aligned(16))) float Bs[CT];
+    __shared__ __attribute__((aligned(16))) float Bs[3 * CT];
     T* Ks = reinterpret_cast<T*>(smem);
     T* Vs = Ks + CT * Cf::LK;
     float* Sst = reinterpret_cast<float*>(smem);
@@ -1551,7 +1571,7 @@ __global__ __launch_bounds__(kThreads) void k_gated_walk(
     using Cf = WalkCfg<T, CT, D, BV, kWaves>;
     using Fr = typename Cf::Fr;
     __shared__ __attribute__((aligned(16))) unsigned char smem[Cf::WALK_BYTES];
-    __shared__ __attribute__((aligned(16))) float Bs[CT];
+    __shared__ __attribute__((aligned(16))) float Bs[3 * CT];
     T* Qs = reinterpret_cast<T*>(smem);
     T* Ks = Qs + Cf::K_OFF;
     T* Vs = Qs + Cf::V_OFF;
@@ -1643,7 +1663,7 @@ __global__ __launch_bounds__(kThreads) void k_gated_walk(
         __syncthreads();
         Fr Vf[Cf::NVW][Cf::NTS];
         load_vfrags<Cf>(Vf, Vs, w, g, lane);
-        chunk_output<Cf>(Oacc, Sacc, Vf, Qs, Ps, w, g, c16, NoHook(), DecayRows{Bs, c16});
+        chunk_output<Cf>(Oacc, Sacc, Vf, Qs, Ps, w, g, c16, NoHook(), DecayRows<CT>{Bs, c16});
         t_prev = t0;
         n_prev = nrows;
         if (c + 1 < c1 || last_seg) state_hop_gated<Cf>(Sacc, Vf, Ks, Bs, w, g, lane);
