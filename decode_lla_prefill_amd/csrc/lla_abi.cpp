@@ -179,7 +179,8 @@ const char* lla_status_string(lla_status s) {
         case LLA_ERR_UNSUPPORTED:
             return "unsupported request (fp32 inputs with C > 64, a grouped decode shape other than "
                    "dk = dv in {64, 128} with at most 16 query heads per group, unknown option bits, "
-                   "or a keep-state prefill off the fused short-prompt route)";
+                   "a keep-state prefill off the fused short-prompt route, or a gated prefill option "
+                   "other than the zero state)";
         case LLA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
         case LLA_ERR_ALIAS: return "an output overlaps another buffer";
         case LLA_ERR_WORKSPACE: return "workspace missing or too small";

@@ -86,8 +86,9 @@ typedef enum {
     LLA_ERR_UNSUPPORTED = 4, /* valid request the library does not handle: fp32 with C > 64,
                                 a grouped decode shape other than dk = dv in {64, 128} with
                                 at most 16 query heads per group, unknown option bits,
-                                LLA_PREFILL_KEEP_STATE off the fused short-prompt route */
-    LLA_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned */
+                                LLA_PREFILL_KEEP_STATE off the fused short-prompt route or
+                                on a gated prefill */
+    LLA_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned (a gate: 4-byte) */
     LLA_ERR_ALIAS = 6,       /* an output overlaps an input, another output or the workspace */
     LLA_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than lla_prefill_workspace_size() */
     LLA_ERR_DEVICE = 8,      /* a HIP call failed (see lla_last_device_error) */

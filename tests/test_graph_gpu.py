@@ -6,7 +6,8 @@
 * A fresh-prompt prefill and a decode step captured into a HIP graph (their
   kernels only: no allocation and no memset node is recorded) and replayed
   several times, with new inputs written eagerly and the stream synchronised
-  between replays, give the bits of the same calls made eagerly.
+  between replays, give the bits of the same calls made eagerly -- plain,
+  grouped, FP8 and gated.
 """
 import gc
 
@@ -122,6 +123,53 @@ def test_graph_replays_equal_eager_calls_grouped_and_fp8(Hq, Hkv, dtype):
         S_ref = torch.empty_like(S)
         o_ref = lla.prefill(q.clone(), k.clone(), v.clone(), S_ref, chunk=C, zero_state=True)
         od_ref = lla.decode_step(qd.clone(), kd.clone(), vd.clone(), S_ref)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(pre.out, o_ref), r
+        assert torch.equal(dec.out, od_ref), r
+        assert torch.equal(S, S_ref), r
+
+
+@pytest.mark.parametrize("T,d,C", [(700, 128, 64), (500, 64, 32)])
+def test_graph_replays_equal_eager_calls_gated(T, d, C):
+    """The gated prefill (segment pass, scan with the segment decays, walk)
+    and the gated decode step captured and replayed with new inputs and
+    gates: the bits of the eager calls."""
+    dev = need_gpu()
+    B, H = 2, 3
+    q, k, v = (torch.empty((B, H, T, d), dtype=torch.bfloat16, device=dev) for _ in range(3))
+    qd, kd, vd = (torch.empty((B, H, d), dtype=torch.bfloat16, device=dev) for _ in range(3))
+    g, gd = torch.empty((B, H, T), device=dev), torch.empty((B, H), device=dev)
+    S = lla.state_init(B, H, d, d, device=dev)
+    pre = lla.PreparedGatedPrefill(q, k, v, g, S, C)
+    dec = lla.PreparedGatedDecode(qd, kd, vd, gd, S)
+
+    def fill(seed):
+        _fill((q, k, v, qd, kd, vd), seed)
+        gen = torch.Generator(device=dev).manual_seed(seed + 100)
+        g.copy_(torch.rand(g.shape, generator=gen, device=dev) * 0.5 + 0.5)
+        gd.copy_(torch.rand(gd.shape, generator=gen, device=dev) * 0.5 + 0.5)
+
+    fill(0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        pre(zero_state=True)
+        dec()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        pre(zero_state=True)
+        dec()
+    torch.cuda.synchronize()
+    for r in range(1, 5):
+        print("gated graph replay", T, d, C, r, flush=True)
+        fill(r)
+        S_ref = torch.empty_like(S)
+        o_ref = lla.prefill_gated(q.clone(), k.clone(), v.clone(), g.clone(), S_ref, C, zero_state=True)
+        od_ref = lla.decode_step_gated(qd.clone(), kd.clone(), vd.clone(), gd.clone(), S_ref)
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
