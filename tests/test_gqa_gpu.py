@@ -181,6 +181,24 @@ def test_gqa_decode_full_size_sampled(dev):
         assert rel_err(np64(S[b:b + 1]), S_ref) <= 1e-6, b
 
 
+def test_gqa_continuation_on_matrix_cores_full_size_sampled(dev):
+    """The benchmark's 16-token continuation of the grouped decode states
+    (256 sequences, 32 query heads on 8 key/value heads, d=128), launched as
+    the benchmark launches it (PreparedPrefill: the matrix-core route);
+    sampled sequences against the oracle within the bar."""
+    cfg = workloads.CONFIGS["decode_B256_gqa"]
+    S0 = workloads.random_state(cfg, device=dev)
+    qc, kc, vc = (x.permute(1, 2, 0, 3).contiguous() for x in workloads.decode_inputs(cfg, 16, device=dev))
+    S = S0.clone()
+    o = lla.PreparedPrefill(qc, kc, vc, S, cfg.C)()
+    torch.cuda.synchronize()
+    for b in (0, 131, 255):
+        O_ref, S_ref = oracle.grouped_recurrence(qc[b:b + 1].cpu(), kc[b:b + 1].cpu(), vc[b:b + 1].cpu(),
+                                                 S0[b:b + 1].cpu(), nthreads=8)
+        assert rel_err(np64(o[b:b + 1]), O_ref) <= TOL, b
+        assert rel_err(np64(S[b:b + 1]), S_ref) <= TOL, b
+
+
 # ---- short continuations with shared-state heads ---------------------------------
 
 @pytest.mark.parametrize("B,Hq,Hkv,T,d,dtype,keep", [
