@@ -59,9 +59,16 @@ lla_status check_sizes(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, 
 }
 
 lla_status check_dtype(int dt, int64_t C) {
+    (void)C;
     if (!known_dtype(dt)) return LLA_ERR_DTYPE;
-    if (dt == LLA_F32 && C > kMaxChunkF32) return LLA_ERR_UNSUPPORTED;
     return LLA_OK;
+}
+
+// The phase calls share one plan, and lla_prefill_state_scan has no dtype:
+// fp32 inputs with C > 64 (planned as sub-chunks) stay with the one-call
+// entry points.
+lla_status check_phase_dtype(int dt, int64_t C) {
+    return dt == LLA_F32 && C > kMaxChunkF32 ? LLA_ERR_UNSUPPORTED : LLA_OK;
 }
 
 lla_status device_status(hipError_t e) {
@@ -177,7 +184,7 @@ const char* lla_status_string(lla_status s) {
         case LLA_ERR_SHAPE: return "a size is out of range";
         case LLA_ERR_DTYPE: return "unknown dtype";
         case LLA_ERR_UNSUPPORTED:
-            return "unsupported request (fp32 inputs with C > 64, a grouped decode shape other than "
+            return "unsupported request (fp32 inputs with C > 64 in the phase calls, a grouped decode shape other than "
                    "dk = dv in {64, 128} with at most 16 query heads per group, unknown option bits, "
                    "a keep-state prefill off the fused short-prompt route, or a gated prefill option "
                    "other than the zero state)";
@@ -224,6 +231,7 @@ lla_status lla_prefill_segment_states(const void* K, const void* V, lla_dtype dt
     PrefillBufs b{nullptr, K, V, nullptr, nullptr, nullptr, workspace, workspace_bytes};
     lla_status st = check_prefill(b, false, true, false, false, true, raw_enum(dtype), B, Heads{H, H}, T, dk,
                                   dv, C, p);
+    if (st == LLA_OK) st = check_phase_dtype(raw_enum(dtype), C);
     if (st != LLA_OK || T == 0) return st;
     return device_status(lla::launch_segment_states(p, K, V, (float*)workspace, (hipStream_t)stream));
 }
@@ -247,6 +255,7 @@ lla_status lla_prefill_chunks(const void* Q, const void* K, const void* V, lla_d
     PrefillBufs b{Q, K, V, nullptr, S, O, workspace, workspace_bytes};
     lla_status st = check_prefill(b, true, true, true, true, true, raw_enum(dtype), B, Heads{H, H}, T, dk,
                                   dv, C, p);
+    if (st == LLA_OK) st = check_phase_dtype(raw_enum(dtype), C);
     if (st != LLA_OK || T == 0) return st;
     return device_status(lla::launch_chunk_walk(p, Q, K, V, S, O, (float*)workspace, (hipStream_t)stream));
 }

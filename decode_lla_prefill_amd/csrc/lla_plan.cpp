@@ -31,6 +31,18 @@ void plan_prefill(PrefillPlan& p) {
     p.G = want > kTargetWalkers ? (want + kTargetWalkers - 1) / kTargetWalkers : 1;
     if (p.G > p.n_c) p.G = p.n_c > 0 ? p.n_c : 1;
     p.n_seg = p.n_c > 0 ? (p.n_c + p.G - 1) / p.G : 0;
+    // fp32 tiles of more than 64 rows do not fit the walks' LDS: such chunks
+    // run as sub-chunks of ceil(C/2) tokens, twice as many per segment (the
+    // chunk form gives the same result for any chunk size, up to rounding).
+    // That never makes more segments than the plan for C itself, so the
+    // workspace sizes, which do not depend on the dtype, still cover it.
+    if (p.dtype == LLA_F32 && p.C > 64 && p.n_c > 0) {
+        p.C = (p.C + 1) / 2;
+        p.CT = pad_dim(p.C);
+        p.n_c = (p.T + p.C - 1) / p.C;
+        p.G = 2 * p.G < p.n_c ? 2 * p.G : p.n_c;
+        p.n_seg = (p.n_c + p.G - 1) / p.G;
+    }
     // a walk reads its starting state from the workspace when there are
     // several segments, or several query heads per state (the group's walks
     // must not read S while one of them writes S_T)

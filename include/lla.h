@@ -36,8 +36,9 @@
  * enqueues work on that stream and returns without synchronising; results
  * are valid once the stream has been synchronised.
  * Limits: B, H >= 1; T >= 0 (T = 0 is a no-op that leaves S untouched);
- * 1 <= dk, dv <= 128; 1 <= C <= 128 for bf16 and FP8 inputs, 1 <= C <= 64 for
- * fp32 inputs; B*H <= 2^20 (H counts query heads in the grouped calls) and
+ * 1 <= dk, dv <= 128; 1 <= C <= 128 (fp32 inputs with C > 64 run as chunks of
+ * ceil(C/2) tokens, which gives the same result up to rounding; the three
+ * phase calls refuse them); B*H <= 2^20 (H counts query heads in the grouped calls) and
  * B*H*T*max(dk,dv) <= 2^58, else LLA_ERR_SHAPE.  C need not divide T: the last
  * chunk of a sequence is shorter.
  * Errors: arguments are checked on the host before anything is enqueued; on
@@ -83,7 +84,8 @@ typedef enum {
     LLA_ERR_NULL = 1,        /* a required pointer is NULL */
     LLA_ERR_SHAPE = 2,       /* a size is out of range */
     LLA_ERR_DTYPE = 3,       /* unknown dtype */
-    LLA_ERR_UNSUPPORTED = 4, /* valid request the library does not handle: fp32 with C > 64,
+    LLA_ERR_UNSUPPORTED = 4, /* valid request the library does not handle: fp32 with C > 64
+                                in the phase calls,
                                 a grouped decode shape other than dk = dv in {64, 128} with
                                 at most 16 query heads per group, unknown option bits,
                                 LLA_PREFILL_KEEP_STATE off the fused short-prompt route or

@@ -116,7 +116,7 @@ class Bufs:
     (dict(B=0), E_SHAPE), (dict(H=0), E_SHAPE), (dict(T=-1), E_SHAPE),
     (dict(dk=0), E_SHAPE), (dict(dk=129), E_SHAPE), (dict(dv=129), E_SHAPE),
     (dict(C=0), E_SHAPE), (dict(C=129), E_SHAPE),
-    (dict(dtype=7), E_DTYPE), (dict(dtype=F32, C=128), E_UNSUP),
+    (dict(dtype=7), E_DTYPE),
     (dict(q=A + 8), E_ALIGN), (dict(O=5 * A + 4), E_ALIGN), (dict(S=4 * A + 2), E_ALIGN),
     (dict(O=A + 64), E_ALIAS), (dict(S=3 * A), E_ALIAS), (dict(O=4 * A + 16), E_ALIAS),
     (dict(T=8192, ws_bytes=16), E_WS), (dict(T=8192, ws=None), E_WS),
@@ -126,6 +126,34 @@ def test_prefill_rejects(lib, fn, change, expect):
     for key, val in change.items():
         setattr(b, key, val)
     assert getattr(lib, fn)(*b.args()) == expect
+
+
+def test_fp32_chunks_over_64_only_in_the_one_call_entry_points(lib):
+    # lla_prefill plans fp32 chunks of C > 64 as sub-chunks: the dtype passes,
+    # and the next check (here a NULL q) decides.  The phase calls share one
+    # plan with the dtype-less scan and refuse it.
+    b = Bufs(dtype=F32, C=128)
+    assert lib.lla_prefill_chunks(*b.args()) == E_UNSUP
+    assert lib.lla_prefill_segment_states(b.k, b.v, F32, 1, 2, 100, 64, 64, 128, b.ws, b.ws_bytes,
+                                          None) == E_UNSUP
+    b.q = None
+    assert lib.lla_prefill(*b.args()) == E_NULL
+    b.q = A
+    b.O = A + 64
+    assert lib.lla_prefill(*b.args()) == E_ALIAS
+
+
+@pytest.mark.parametrize("B,H,d", [(1, 16, 128), (4, 8, 64), (1, 1, 32), (64, 32, 128), (2, 3, 100)])
+def test_fp32_sub_chunk_plan_fits_the_dtype_less_workspace(lib, B, H, d):
+    # With exactly lla_prefill_workspace_size bytes, the fp32 plan for C > 64
+    # passes the workspace check and stops at the next one (O aliases q).
+    for C in (65, 66, 77, 100, 127, 128):
+        for T in (1, 17, 64, 65, 129, 200, 1000, 4097, 8192, 65536):
+            ws = lib.lla_prefill_workspace_size(B, H, T, d, d, C)
+            b = Bufs(B=B, H=H, T=T, dk=d, dv=d, C=C, dtype=F32)
+            b.ws, b.ws_bytes = (6 * A, ws) if ws > 0 else (None, 0)
+            b.O = A + 64
+            assert lib.lla_prefill(*b.args()) == E_ALIAS, (C, T)
 
 
 def test_prefill_empty_prompt_is_a_noop(lib):
@@ -367,7 +395,7 @@ def _scratch_bytes():
 
 @pytest.mark.parametrize("change,expect", [
     (dict(q=None), E_NULL), (dict(S=None), E_NULL), (dict(B=0), E_SHAPE), (dict(dtype=7), E_DTYPE),
-    (dict(O=5 * A + 4), E_ALIGN), (dict(O=A + 64), E_ALIAS), (dict(dtype=F32, C=128), E_UNSUP),
+    (dict(O=5 * A + 4), E_ALIGN), (dict(O=A + 64), E_ALIAS), (dict(dtype=F32, C=128, q=None), E_NULL),
 ])
 @pytest.mark.parametrize("flags", [0, ZERO_STATE])
 def test_prefill_noalloc_checks_like_prefill_ex(lib, change, expect, flags):

@@ -41,6 +41,8 @@ CASES = [
     (1, 2, 900, 128, 128, 128, torch.bfloat16, (0.8, 1.0)),    # chunk tile 128
     (2, 2, 333, 32, 32, 32, torch.bfloat16, (0.0, 1.0)),       # chunk tile 32, gates down to 0
     (1, 3, 700, 48, 40, 40, torch.float32, (0.7, 1.0)),        # fp32, ragged dims and chunks
+    (1, 2, 1500, 128, 128, 128, torch.float32, (0.9, 1.0)),    # fp32, C > 64: sub-chunks of 64
+    (2, 1, 400, 64, 64, 100, torch.float32, (0.5, 1.0)),       # fp32, sub-chunks of 50
     (2, 2, 600, 128, 128, 64, FP8, (0.9, 1.0)),                # FP8 inputs
     (1, 2, 500, 40, 24, 48, torch.bfloat16, (0.6, 1.0)),       # dims not multiples of 16
     (3, 1, 17, 64, 64, 64, torch.bfloat16, (0.5, 1.0)),        # one chunk, ragged

@@ -44,7 +44,7 @@ def _prefill(lib, **change):
     (dict(gate=None), E_NULL), (dict(q=None), E_NULL), (dict(S=None), E_NULL), (dict(O=None), E_NULL),
     (dict(flags=2), E_UNSUP), (dict(flags=4), E_UNSUP),
     (dict(B=0), E_SHAPE), (dict(dk=129), E_SHAPE), (dict(C=0), E_SHAPE), (dict(C=129), E_SHAPE),
-    (dict(dtype=7), E_DTYPE), (dict(dtype=F32, C=128), E_UNSUP),
+    (dict(dtype=7), E_DTYPE), (dict(dtype=F32, C=128, q=None), E_NULL),
     (dict(gate=7 * A + 2), E_ALIGN), (dict(q=A + 8), E_ALIGN),
     (dict(gate=5 * A + 64), E_ALIAS), (dict(gate=4 * A), E_ALIAS), (dict(O=A + 64), E_ALIAS),
     (dict(T=8192, ws_bytes=16), E_WS), (dict(T=8192, ws=None), E_WS),

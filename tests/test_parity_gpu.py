@@ -53,6 +53,9 @@ INT_CASES = [
     (1, 2, 2000, 64, 32, 32, torch.float32),
     (2, 1, 333, 128, 128, 64, torch.float32),
     (1, 1, 50, 3, 2, 7, torch.float32),
+    (1, 2, 2000, 64, 64, 128, torch.float32),   # fp32 with C > 64: sub-chunks of 64
+    (2, 1, 333, 128, 128, 100, torch.float32),  # sub-chunks of 50
+    (1, 3, 70, 40, 24, 65, torch.float32),      # sub-chunks of 33, one segment
     (1, 2, 37, 16, 16, 1, torch.bfloat16),      # C = 1: the recurrence itself
     (2, 1, 300, 24, 40, 128, torch.bfloat16),   # C = 128 with odd head dims
     (1, 3, 500, 128, 128, 32, torch.bfloat16),  # C = 32 at d = 128
@@ -149,8 +152,27 @@ def test_gaussian_with_random_incoming_state(dev):
     assert rel_err(np64(o), O_ref) <= TOL and rel_err(np64(S), S_ref) <= TOL
 
 
-def test_fp32_gaussian_is_fp32_accurate(dev):
+@pytest.mark.parametrize("C", [64, 100, 128])
+def test_fp32_gaussian_is_fp32_accurate(dev, C):
     q, k, v = workloads.gaussian(2, 2, 500, 64, 64, seed_base=80, scale=0.125, dtype=torch.float32)
-    o, S = gpu_prefill(q, k, v, C=64)
+    o, S = gpu_prefill(q, k, v, C=C)
     O_ref, S_ref = oracle.recurrence(q, k, v, nthreads=4)
     assert rel_err(np64(o), O_ref) <= 1e-5 and rel_err(np64(S), S_ref) <= 1e-5
+
+
+def test_fp32_chunks_over_64_with_state_and_workspace(dev):
+    # several segments at d = 128: the sub-chunk plan runs in the workspace
+    # the dtype-less size function gives
+    q, k, v = workloads.gaussian(1, 4, 3000, 128, 128, seed_base=90, scale=128 ** -0.5, dtype=torch.float32)
+    S0 = torch.randn((1, 4, 128, 128), generator=torch.Generator().manual_seed(91))
+    assert lla.prefill_workspace_size(1, 4, 3000, 128, 128, 128) > 0
+    o, S = gpu_prefill(q, k, v, C=128, S0=S0)
+    O_ref, S_ref = oracle.recurrence(q, k, v, S0, nthreads=4)
+    assert rel_err(np64(o), O_ref) <= 1e-5 and rel_err(np64(S), S_ref) <= 1e-5
+
+
+def test_fp32_chunks_over_64_refused_by_the_phase_calls(dev):
+    k = torch.zeros((1, 2, 300, 64), device=dev)
+    ws = torch.empty(lla.prefill_workspace_size(1, 2, 300, 64, 64, 128) // 4 + 4, device=dev)
+    with pytest.raises(lla.LlaError):
+        lla.prefill_segment_states(k, k, 128, ws)

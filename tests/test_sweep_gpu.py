@@ -30,8 +30,6 @@ def _draw_prefill_cases(n, seed):
         dk = int(rng.choice([128, 128, 64, 32, 16, 40, 72, 96, 120, 8, 1, 3]))
         dv = dk if rng.rand() < 0.7 else int(rng.choice([128, 64, 48, 8, 5]))
         C = int(rng.choice([64, 64, 128, 32, 16, 1, 7, 48, 100]))
-        if dtype == torch.float32 and C > 64:
-            C = 64
         Hkv = int(rng.choice([1, 2, 3, 4]))
         G = int(rng.choice([1, 1, 2, 4]))
         B = int(rng.choice([1, 2, 3]))
@@ -110,8 +108,6 @@ def _draw_float_cases(n, seed):
         dk = int(rng.choice([128, 128, 64, 32, 40, 96, 8]))
         dv = dk if rng.rand() < 0.7 else int(rng.choice([128, 64, 24]))
         C = int(rng.choice([64, 64, 128, 32, 16, 48]))
-        if dtype == torch.float32 and C > 64:
-            C = 64
         Hkv = int(rng.choice([1, 2, 3]))
         G = int(rng.choice([1, 1, 2, 4]))
         B = int(rng.choice([1, 2]))
