@@ -184,8 +184,7 @@ const char* lla_status_string(lla_status s) {
         case LLA_ERR_SHAPE: return "a size is out of range";
         case LLA_ERR_DTYPE: return "unknown dtype";
         case LLA_ERR_UNSUPPORTED:
-            return "unsupported request (fp32 inputs with C > 64 in the phase calls, a grouped decode shape other than "
-                   "dk = dv in {64, 128} with at most 16 query heads per group, unknown option bits, "
+            return "unsupported request (fp32 inputs with C > 64 in the phase calls, unknown option bits, "
                    "a keep-state prefill off the fused short-prompt route, or a gated prefill option "
                    "other than the zero state)";
         case LLA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
@@ -310,7 +309,6 @@ lla_status decode_impl(const void* q, const void* k, const void* v, int dt_raw, 
     if (!known_dtype(dt_raw)) return LLA_ERR_DTYPE;
     const lla_dtype dtype = (lla_dtype)dt_raw;
     const int64_t group = h.q / h.kv;
-    if (group > 1 && !lla::decode_group_fit(group, (int)dk, (int)dv)) return LLA_ERR_UNSUPPORTED;
     if (!q || !k || !v || !S || !o || (gated && !gate)) return LLA_ERR_NULL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(S) || !aligned16(o) ||
         (gated && !aligned4(gate)))
@@ -329,7 +327,8 @@ lla_status decode_impl(const void* q, const void* k, const void* v, int dt_raw, 
     if (gated)
         return device_status(lla::launch_decode_step_gated(dtype, q, k, v, gate, BHkv, (int)dk, (int)dv, S, o, s));
     if (group > 1)
-        return device_status(lla::launch_decode_group(dtype, q, k, v, BHkv, (int)group, (int)dk, S, o, s));
+        return device_status(lla::launch_decode_group(dtype, q, k, v, BHkv, (int)group, (int)dk, (int)dv, S, o,
+                                                                s));
     return device_status(lla::launch_decode_step(dtype, q, k, v, BHkv, (int)dk, (int)dv, S, o, s));
 }
 

@@ -282,7 +282,8 @@ __global__ __launch_bounds__(NT) void k_decode_tokens(const Tin* __restrict__ q,
 // of the group's G query heads.  Query head g of state bh is row bh * G + g
 // of q and o.  For every query head the arithmetic (update, then the state
 // read in row order, then the row-group reduction) is that of
-// k_decode_step_sq, so a group of one gives identical bits.
+// k_decode_step_sq, so a group of one gives identical bits.  The query rows
+// are staged in LDS GMAX at a time.
 template <typename Tin, int D, int NT, int GMAX>
 __global__ __launch_bounds__(NT) void k_decode_group(const Tin* __restrict__ q,
                                                      const Tin* __restrict__ k,
@@ -296,7 +297,8 @@ __global__ __launch_bounds__(NT) void k_decode_group(const Tin* __restrict__ q,
     const int tid = threadIdx.x, cg = tid % CG, rg = tid / CG;
     const int64_t bh = blockIdx.x;
     float* Sb = S + bh * (int64_t)D * D;
-    for (int e = tid; e < G * D; e += NT) qs[e / D][e % D] = to_f32(q[bh * G * D + e]);
+    const int nb0 = G < GMAX ? G : GMAX;
+    for (int e = tid; e < nb0 * D; e += NT) qs[e / D][e % D] = to_f32(q[bh * G * D + e]);
     for (int i = tid; i < D; i += NT) {
         ks[i] = to_f32(k[bh * D + i]);
         vs[i] = to_f32(v[bh * D + i]);
@@ -315,23 +317,116 @@ __global__ __launch_bounds__(NT) void k_decode_group(const Tin* __restrict__ q,
         for (int u = 0; u < 4; ++u) x[m][u] = fmaf(ki, vj[u], x[m][u]);  // rank-1 update
         __builtin_nontemporal_store(x[m], reinterpret_cast<f32x4*>(Sb + i * D + 4 * cg));
     }
-    for (int g = 0; g < G; ++g) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int g0 = 0; g0 < G; g0 += GMAX) {
+        const int nb = G - g0 < GMAX ? G - g0 : GMAX;
+        if (g0 > 0) {  // the previous batch's last barrier ended every read of qs
+            for (int e = tid; e < nb * D; e += NT) qs[e / D][e % D] = to_f32(q[(bh * G + g0) * D + e]);
+            __syncthreads();
+        }
+        for (int g = 0; g < nb; ++g) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < RPT; ++m) {
+                const float qi = qs[g][rg + m * RG];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) acc[u] = fmaf(qi, x[m][u], acc[u]);  // state read
+            }
+            red[rg][cg] = acc;
+            __syncthreads();
+            for (int j = tid; j < D; j += NT) {  // o[j] = sum over row groups, in order
+                float sum = 0.0f;
+#pragma unroll
+                for (int r = 0; r < RG; ++r) sum += red[r][j / 4][j % 4];
+                o[(bh * G + g0 + g) * D + j] = sum;
+            }
+            __syncthreads();  // red (and, after the last head, qs) is rewritten next
+        }
+    }
+}
+
+// Shared-state heads for the other head dims (dk, dv <= 128): the thread
+// layout and arithmetic of k_decode_step (VW value columns per thread,
+// row groups of rg_n, rows rg + m * rg_n), with all of a thread's rows in
+// registers at once (RPT * rg_n >= dk, checked by the launcher), so every
+// query head's o has the bits of a plain decode step on the updated state.
+// The query rows are staged in LDS GB at a time.
+template <typename Tin, int VW, int RPT, int GB>
+__global__ __launch_bounds__(kThreads) void k_decode_group_any(const Tin* __restrict__ q,
+                                                               const Tin* __restrict__ k,
+                                                               const Tin* __restrict__ v,
+                                                               float* __restrict__ S,
+                                                               float* __restrict__ o, int dk, int dv, int G) {
+    typedef float vecf __attribute__((ext_vector_type(VW)));
+    __shared__ float qs[GB][128], ks[128], vs[128];
+    __shared__ float red[kThreads * VW];
+    const int tid = threadIdx.x;
+    const int64_t bh = blockIdx.x;
+    for (int i = tid; i < dk; i += kThreads) ks[i] = to_f32(k[bh * dk + i]);
+    for (int j = tid; j < dv; j += kThreads) vs[j] = to_f32(v[bh * dv + j]);
+    __syncthreads();
+    const int ncg = (dv + VW - 1) / VW;  // column groups
+    const int rg_n = kThreads / ncg;     // row groups
+    const int cg = tid % ncg, rg = tid / ncg;
+    const bool active = rg < rg_n;
+    const int j0 = cg * VW;
+    float* Sb = S + bh * (int64_t)dk * dv;
+    vecf vj;
+#pragma unroll
+    for (int u = 0; u < VW; ++u) vj[u] = (j0 + u < dv) ? vs[j0 + u] : 0.0f;
+    vecf s[RPT];
+    if (active) {
 #pragma unroll
         for (int m = 0; m < RPT; ++m) {
-            const float qi = qs[g][rg + m * RG];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) acc[u] = fmaf(qi, x[m][u], acc[u]);  // state read
+            const int i = rg + m * rg_n;
+            if (i < dk) {
+                if constexpr (VW == 4)
+                    s[m] = __builtin_nontemporal_load(reinterpret_cast<const vecf*>(Sb + (int64_t)i * dv + j0));
+                else
+                    s[m] = Sb[(int64_t)i * dv + j0];
+            }
         }
-        red[rg][cg] = acc;
-        __syncthreads();
-        for (int j = tid; j < D; j += NT) {  // o[j] = sum over row groups, in order
-            float sum = 0.0f;
 #pragma unroll
-            for (int r = 0; r < RG; ++r) sum += red[r][j / 4][j % 4];
-            o[(bh * G + g) * D + j] = sum;
+        for (int m = 0; m < RPT; ++m) {
+            const int i = rg + m * rg_n;
+            if (i < dk) {
+                const float ki = ks[i];
+#pragma unroll
+                for (int u = 0; u < VW; ++u) s[m][u] = fmaf(ki, vj[u], s[m][u]);  // rank-1 update
+                if constexpr (VW == 4)
+                    __builtin_nontemporal_store(s[m], reinterpret_cast<vecf*>(Sb + (int64_t)i * dv + j0));
+                else
+                    Sb[(int64_t)i * dv + j0] = s[m][0];
+            }
         }
-        __syncthreads();  // red is rewritten by the next query head
+    }
+    for (int g0 = 0; g0 < G; g0 += GB) {
+        const int nb = G - g0 < GB ? G - g0 : GB;
+        for (int e = tid; e < nb * dk; e += kThreads) qs[e / dk][e % dk] = to_f32(q[(bh * G + g0) * dk + e]);
+        __syncthreads();  // the previous batch's last barrier ended every read of qs
+        for (int g = 0; g < nb; ++g) {
+            vecf acc = {};
+            if (active) {
+#pragma unroll
+                for (int m = 0; m < RPT; ++m) {
+                    const int i = rg + m * rg_n;
+                    if (i < dk) {
+                        const float qi = qs[g][i];
+#pragma unroll
+                        for (int u = 0; u < VW; ++u) acc[u] = fmaf(qi, s[m][u], acc[u]);  // state read
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < VW; ++u) red[tid * VW + u] = acc[u];
+            __syncthreads();
+            for (int j = tid; j < dv; j += kThreads) {  // o[j] = sum over row groups, in order
+                const int c = j / VW, u = j % VW;
+                float sum = 0.0f;
+                for (int r = 0; r < rg_n; ++r) sum += red[(r * ncg + c) * VW + u];
+                o[(bh * G + g0 + g) * dv + j] = sum;
+            }
+            __syncthreads();  // red (and, after the last head, qs) is rewritten next
+        }
     }
 }
 
@@ -553,27 +648,43 @@ hipError_t launch_decode_tokens(lla_dtype dtype, const void* q, const void* k, c
     return tokens_g<float>(q, k, v, BHkv, T, group, d, S, o, z, st);
 }
 
-bool decode_group_fit(int64_t group, int dk, int dv) {
-    return group >= 1 && group <= kDecodeGroupMax && dk == dv && (dk == 64 || dk == 128);
+// Rows per thread that k_decode_group_any needs to hold a whole dk x dv
+// state in one pass with VW columns per thread.
+static int group_any_rows(int dk, int dv, int VW) {
+    const int ncg = (dv + VW - 1) / VW, rg_n = kThreads / ncg;
+    return (dk + rg_n - 1) / rg_n;
 }
 
 template <typename Tin>
-static hipError_t group_t(const void* q, const void* k, const void* v, int64_t BHkv, int G, int d,
+static hipError_t group_t(const void* q, const void* k, const void* v, int64_t BHkv, int G, int dk, int dv,
                           float* S, float* o, hipStream_t st) {
-    if (d == 128)
-        hipLaunchKernelGGL((k_decode_group<Tin, 128, 512, kDecodeGroupMax>), dim3((unsigned)BHkv), dim3(512),
-                           0, st, (const Tin*)q, (const Tin*)k, (const Tin*)v, S, o, G);
-    else
-        hipLaunchKernelGGL((k_decode_group<Tin, 64, 256, kDecodeGroupMax>), dim3((unsigned)BHkv), dim3(256),
-                           0, st, (const Tin*)q, (const Tin*)k, (const Tin*)v, S, o, G);
+    const Tin *qq = (const Tin*)q, *kk = (const Tin*)k, *vv = (const Tin*)v;
+    const dim3 grid((unsigned)BHkv);
+    if (dk == 128 && dv == 128)
+        hipLaunchKernelGGL((k_decode_group<Tin, 128, 512, kDecodeGroupBatch>), grid, dim3(512), 0, st, qq, kk, vv,
+                           S, o, G);
+    else if (dk == 64 && dv == 64)
+        hipLaunchKernelGGL((k_decode_group<Tin, 64, 256, kDecodeGroupBatch>), grid, dim3(256), 0, st, qq, kk, vv,
+                           S, o, G);
+    else if ((dv & 3) == 0) {
+        // dv / 4 <= 32 column groups leave >= 8 row groups: 16 rows each cover dk <= 128
+        if (group_any_rows(dk, dv, 4) > 16) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((k_decode_group_any<Tin, 4, 16, kDecodeGroupBatch>), grid, dim3(kThreads), 0, st, qq,
+                           kk, vv, S, o, dk, dv, G);
+    } else {
+        // dv <= 128 columns leave >= 2 row groups: 64 rows each cover dk <= 128
+        if (group_any_rows(dk, dv, 1) > 64) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((k_decode_group_any<Tin, 1, 64, kDecodeGroupBatch>), grid, dim3(kThreads), 0, st, qq,
+                           kk, vv, S, o, dk, dv, G);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_decode_group(lla_dtype dtype, const void* q, const void* k, const void* v,
-                               int64_t BHkv, int group, int d, float* S, float* o, hipStream_t st) {
-    if (dtype == LLA_FP8_E4M3) return group_t<fp8e4m3>(q, k, v, BHkv, group, d, S, o, st);
-    if (dtype == LLA_BF16) return group_t<bf16>(q, k, v, BHkv, group, d, S, o, st);
-    return group_t<float>(q, k, v, BHkv, group, d, S, o, st);
+                               int64_t BHkv, int group, int dk, int dv, float* S, float* o, hipStream_t st) {
+    if (dtype == LLA_FP8_E4M3) return group_t<fp8e4m3>(q, k, v, BHkv, group, dk, dv, S, o, st);
+    if (dtype == LLA_BF16) return group_t<bf16>(q, k, v, BHkv, group, dk, dv, S, o, st);
+    return group_t<float>(q, k, v, BHkv, group, dk, dv, S, o, st);
 }
 
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st) {

@@ -96,12 +96,13 @@ hipError_t launch_state_commit(lla_dtype dtype, const void* k, const void* v, co
                                int64_t BHkv, int Hkv, int T, int dk, int dv, float* S, hipStream_t st);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 
-// Shared-state heads: `group` query heads read each key/value state (dk = dv
-// in {64, 128}, group <= kDecodeGroupMax).  q, o: [BHkv * group][d].
-constexpr int kDecodeGroupMax = 16;
-bool decode_group_fit(int64_t group, int dk, int dv);
+// Shared-state heads: `group` query heads read each key/value state (any
+// group >= 1, dk, dv <= 128).  q: [BHkv * group][dk], o: [BHkv * group][dv].
+// The query rows are staged kDecodeGroupBatch at a time.
+constexpr int kDecodeGroupMax = 16;  // largest group of the fused short continuations
+constexpr int kDecodeGroupBatch = 16;
 hipError_t launch_decode_group(lla_dtype dtype, const void* q, const void* k, const void* v,
-                               int64_t BHkv, int group, int d, float* S, float* o, hipStream_t st);
+                               int64_t BHkv, int group, int dk, int dv, float* S, float* o, hipStream_t st);
 
 // lla_prefill_noalloc: the prefill workspace in a static device array of
 // this many bytes per device (lla_noalloc.hip); *out = its address on the

@@ -80,7 +80,7 @@ KERNELS = {
     "decode_step": (("k_decode_step_sqIDF16bLi128ELi512ELb0E", "k_decode_step_sq<__bf16, 128, 512, false>"),
                     256 * 32 * 512, "decode_step_B256_H32_traffic.txt",
                     ("lla_decode.hip", "lla_device.h"), "decode_B256"),
-    "decode_group": (("k_decode_group",), 256 * 8 * 512, "decode_group_B256_Hq32_Hkv8_traffic.txt",
+    "decode_group": (("k_decode_groupIDF16bLi128E", "k_decode_group<__bf16, 128,"), 256 * 8 * 512, "decode_group_B256_Hq32_Hkv8_traffic.txt",
                      ("lla_decode.hip", "lla_device.h"), "decode_B256_gqa"),
     # 16-token continuations of the grouped states: one 4-wave workgroup per
     # key/value head and 64 value columns

@@ -85,9 +85,7 @@ typedef enum {
     LLA_ERR_SHAPE = 2,       /* a size is out of range */
     LLA_ERR_DTYPE = 3,       /* unknown dtype */
     LLA_ERR_UNSUPPORTED = 4, /* valid request the library does not handle: fp32 with C > 64
-                                in the phase calls,
-                                a grouped decode shape other than dk = dv in {64, 128} with
-                                at most 16 query heads per group, unknown option bits,
+                                in the phase calls, unknown option bits,
                                 LLA_PREFILL_KEEP_STATE off the fused short-prompt route or
                                 on a gated prefill */
     LLA_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned (a gate: 4-byte) */
@@ -326,8 +324,7 @@ lla_status lla_prefill_noalloc(const void *Q, const void *K, const void *V, lla_
  * One decode step with shared-state heads: q: [B][Hq][dk], k: [B][Hkv][dk],
  * v: [B][Hkv][dv] (dtype); S: [B][Hkv][dk][dv] fp32 updated once in place;
  * o: [B][Hq][dv] fp32.  Each state is read from memory once for the G query
- * heads of its group.  For G > 1 the library needs dk = dv in {64, 128} and
- * G <= 16 (else LLA_ERR_UNSUPPORTED); G = 1 is lla_decode_step.  Per query
+ * heads of its group (any G = Hq / Hkv; G = 1 is lla_decode_step).  Per query
  * head the arithmetic is that of lla_decode_step (identical bits).
  */
 lla_status lla_decode_step_gqa(const void *q, const void *k, const void *v, lla_dtype dtype,

@@ -305,8 +305,8 @@ def test_prefill_gqa_workspace(lib):
 
 @pytest.mark.parametrize("change,expect", [
     (dict(Hkv=0), E_SHAPE), (dict(Hq=6, Hkv=4), E_SHAPE), (dict(Hq=2, Hkv=4), E_SHAPE),
-    (dict(Hq=17, Hkv=1), E_UNSUP), (dict(dk=96, dv=96), E_UNSUP), (dict(dk=64, dv=128), E_UNSUP),
-    (dict(q=None), E_NULL), (dict(dtype=5), E_DTYPE), (dict(o=2 * A + 256), E_ALIAS),
+    (dict(Hq=17, Hkv=1, q=None), E_NULL), (dict(dk=96, dv=96, q=None), E_NULL),
+    (dict(dk=64, dv=7, q=None), E_NULL), (dict(q=None), E_NULL), (dict(dtype=5), E_DTYPE), (dict(o=2 * A + 256), E_ALIAS),
 ])
 def test_decode_gqa_rejects(lib, change, expect):
     d = dict(q=A, k=2 * A, v=3 * A, dtype=BF16, B=2, Hq=8, Hkv=2, dk=128, dv=128, S=4 * A, o=5 * A)

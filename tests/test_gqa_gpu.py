@@ -130,6 +130,55 @@ def test_gqa_decode_integers_exact(dev, B, Hq, Hkv, d, dtype):
     assert np.array_equal(np64(S), S_ref)
 
 
+# Groups beyond one LDS batch of 16 query rows, and head dims other than
+# 64 and 128 (the general kernel: 4 value columns per thread when dv is a
+# multiple of 4, else 1)
+ANY_SHAPES = [
+    # B, Hq, Hkv, dk, dv, dtype
+    (2, 40, 2, 128, 128, torch.bfloat16),        # G = 20: two batches
+    (1, 64, 1, 64, 64, torch.float32),           # G = 64: four batches
+    (3, 8, 2, 96, 80, torch.bfloat16),
+    (2, 6, 1, 128, 5, torch.float32),
+    (1, 34, 2, 40, 127, torch.float8_e4m3fn),    # G = 17, 64 rows per thread
+    (2, 48, 3, 1, 1, torch.bfloat16),
+    (1, 36, 2, 33, 128, torch.bfloat16),         # G = 18 on the general kernel
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,dk,dv,dtype", ANY_SHAPES)
+def test_gqa_decode_any_shape_integers_exact(dev, B, Hq, Hkv, dk, dv, dtype):
+    print("gqa decode any", B, Hq, Hkv, dk, dv, dtype, flush=True)
+    gen = torch.Generator().manual_seed(Hq * 7 + dk + dv)
+    q = torch.randint(-2, 3, (B, Hq, dk), generator=gen).to(dtype)
+    k = torch.randint(-2, 3, (B, Hkv, dk), generator=gen).to(dtype)
+    v = torch.randint(-2, 3, (B, Hkv, dv), generator=gen).to(dtype)
+    S0 = torch.randint(-300, 301, (B, Hkv, dk, dv), generator=gen).float()
+    S = S0.to(dev).contiguous()
+    o = lla.decode_step(q.to(dev).contiguous(), k.to(dev).contiguous(), v.to(dev).contiguous(), S)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.grouped_decode_step(q, k, v, S0)
+    assert np.array_equal(np64(o), o_ref)
+    assert np.array_equal(np64(S), S_ref)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,dk,dv,dtype", ANY_SHAPES)
+def test_gqa_decode_any_shape_equals_repeated_heads(dev, B, Hq, Hkv, dk, dv, dtype):
+    G = Hq // Hkv
+    gen = torch.Generator(device=dev).manual_seed(Hq + dk * dv)
+    q = torch.randn((B, Hq, dk), generator=gen, device=dev).to(dtype)
+    k = torch.randn((B, Hkv, dk), generator=gen, device=dev).to(dtype)
+    v = torch.randn((B, Hkv, dv), generator=gen, device=dev).to(dtype)
+    S0 = torch.randn((B, Hkv, dk, dv), generator=gen, device=dev)
+    S_g = S0.clone()
+    o_g = lla.decode_step(q, k, v, S_g)
+    S_r = S0.repeat_interleave(G, dim=1).contiguous()
+    o_r = lla.decode_step(q, k.repeat_interleave(G, dim=1).contiguous(),
+                          v.repeat_interleave(G, dim=1).contiguous(), S_r)
+    torch.cuda.synchronize()
+    assert torch.equal(o_g, o_r)
+    assert torch.equal(S_g, S_r[:, ::G])
+
+
 @pytest.mark.parametrize("Hq,Hkv,d", [(32, 8, 128), (16, 1, 128), (8, 8, 64), (12, 3, 64)])
 def test_gqa_decode_equals_repeated_heads(dev, Hq, Hkv, d):
     B, G = 5, Hq // Hkv

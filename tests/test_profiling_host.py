@@ -69,3 +69,7 @@ def test_kernel_names_match_in_both_trace_forms():
                                  "decode_step")
     assert profiling.matches("_ZN3lla16k_decode_step_sqIDF16bLi128ELi512ELb1EEEvPKT_S3_S3_PfS4_PKf",
                              "gated_decode")
+    assert profiling.matches("_ZN3lla14k_decode_groupIDF16bLi128ELi512ELi16EEEvPKT_S3_S3_PfS4_i", "decode_group")
+    assert profiling.matches("void lla::k_decode_group<__bf16, 128, 512, 16>(...)", "decode_group")
+    # the general grouped kernel is another kernel
+    assert not profiling.matches("void lla::k_decode_group_any<__bf16, 4, 16, 16>(...)", "decode_group")
