@@ -236,6 +236,15 @@ def measure_peaks(torch):
     }
 
 
+# the walk kernel of each prefill workload: (label, key of its counter summary)
+WALK_OF_CONFIG = {
+    "prefill_T8192": ("k_chunk_walk_wide<64> (bf16, d=128)", "chunk_walk"),
+    "prefill_B4_T1024": ("k_chunk_walk<bf16,64,64,64> (four waves, d=64, C=64)", "chunk_walk_T1024"),
+    "prefill_T131072": ("k_chunk_walk_wide<64> (bf16, d=128; C=128 run as two 64-token chunks)",
+                        "chunk_walk_T131072"),
+}
+
+
 def bench_prefill(args, torch, lla, workloads, profiling):
     cfg = workloads.CONFIGS[args.prefill_config]
     dev = torch.device("cuda:0")
@@ -323,8 +332,10 @@ def bench_prefill(args, torch, lla, workloads, profiling):
                                / (ms_step * 1e-3),
                        "bound": "hbm" if nbytes / (PEAK_HBM_GBS * 1e9) > flops / (PEAK_BF16_TFLOPS * 1e12)
                                 else "mfma"},
-        "roofline": hbm_roofline("k_chunk_walk_wide<64> (bf16, d=128)", nbytes, walk_launch_ms, gap_ms,
-                                 profiling.stored_traffic("chunk_walk"),
+        "roofline": hbm_roofline(WALK_OF_CONFIG.get(args.prefill_config, ("chunk walk", None))[0], nbytes,
+                                 walk_launch_ms, gap_ms,
+                                 profiling.stored_traffic(WALK_OF_CONFIG[args.prefill_config][1])
+                                 if args.prefill_config in WALK_OF_CONFIG else None,
                                  "HIP events around %d back-to-back walk launches" % n_walk,
                                  algorithmic_flops=flops),
         "warm": {"ms_per_step": wall_w * 1e3 / args.steps,
@@ -479,9 +490,7 @@ def bench_other_prefills(args, torch, lla, workloads, profiling):
     import oracle
     dev = torch.device("cuda:0")
     out = []
-    walks = {"prefill_B4_T1024": ("k_chunk_walk<bf16,64,64,64> (four waves, d=64, C=64)", "chunk_walk_T1024"),
-             "prefill_T131072": ("k_chunk_walk<bf16,128,128,128> (eight waves, d=128, C=128)",
-                                 "chunk_walk_T131072")}
+    walks = WALK_OF_CONFIG
     for name, rotate, steps in (("prefill_B4_T1024", 16, args.steps), ("prefill_T131072", 2, 6)):
         cfg = workloads.CONFIGS[name]
         B, H, T, C, d = cfg.B, cfg.H, cfg.T, cfg.C, cfg.dk

@@ -14,8 +14,7 @@ namespace {
 thread_local int g_last_device_error = 0;
 
 constexpr int64_t kMaxHeadDim = 128;
-constexpr int64_t kMaxChunkBf16 = 128;
-constexpr int64_t kMaxChunkF32 = 64;
+constexpr int64_t kMaxChunk = 128;
 // B*H bound: every launch grid stays far below 2^32 work-items.
 constexpr int64_t kMaxStreams = (int64_t)1 << 20;
 
@@ -51,25 +50,14 @@ lla_status check_sizes(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, 
     if (B < 1 || H < 1 || T < 0) return LLA_ERR_SHAPE;
     if (dk < 1 || dk > kMaxHeadDim || dv < 1 || dv > kMaxHeadDim) return LLA_ERR_SHAPE;
     if (B > kMaxStreams || H > kMaxStreams || B * H > kMaxStreams) return LLA_ERR_SHAPE;
-    if (C >= 0 && (C < 1 || C > kMaxChunkBf16)) return LLA_ERR_SHAPE;
+    if (C >= 0 && (C < 1 || C > kMaxChunk)) return LLA_ERR_SHAPE;
     // B*H*T*max(dk,dv)*4 bytes must be representable.
     const int64_t dmax = dk > dv ? dk : dv;
     if (T > 0 && B * H > (((int64_t)1 << 60) / T) / (dmax * 4)) return LLA_ERR_SHAPE;
     return LLA_OK;
 }
 
-lla_status check_dtype(int dt, int64_t C) {
-    (void)C;
-    if (!known_dtype(dt)) return LLA_ERR_DTYPE;
-    return LLA_OK;
-}
-
-// The phase calls share one plan, and lla_prefill_state_scan has no dtype:
-// fp32 inputs with C > 64 (planned as sub-chunks) stay with the one-call
-// entry points.
-lla_status check_phase_dtype(int dt, int64_t C) {
-    return dt == LLA_F32 && C > kMaxChunkF32 ? LLA_ERR_UNSUPPORTED : LLA_OK;
-}
+lla_status check_dtype(int dt) { return known_dtype(dt) ? LLA_OK : LLA_ERR_DTYPE; }
 
 lla_status device_status(hipError_t e) {
     if (e == hipSuccess) return LLA_OK;
@@ -134,7 +122,7 @@ lla_status check_prefill(const PrefillBufs& b, bool needs_q, bool needs_kv, bool
     if (st != LLA_OK) return st;
     st = check_sizes(B, h.q, T, dk, dv, C);
     if (st != LLA_OK) return st;
-    st = check_dtype(dt_raw, C);
+    st = check_dtype(dt_raw);
     if (st != LLA_OK) return st;
     const lla_dtype dt = (lla_dtype)dt_raw;
     plan = make_plan(dt, B, h, T, dk, dv, C);
@@ -184,7 +172,7 @@ const char* lla_status_string(lla_status s) {
         case LLA_ERR_SHAPE: return "a size is out of range";
         case LLA_ERR_DTYPE: return "unknown dtype";
         case LLA_ERR_UNSUPPORTED:
-            return "unsupported request (fp32 inputs with C > 64 in the phase calls, unknown option bits, "
+            return "unsupported request (unknown option bits, "
                    "a keep-state prefill off the fused short-prompt route, or a gated prefill option "
                    "other than the zero state)";
         case LLA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
@@ -230,7 +218,6 @@ lla_status lla_prefill_segment_states(const void* K, const void* V, lla_dtype dt
     PrefillBufs b{nullptr, K, V, nullptr, nullptr, nullptr, workspace, workspace_bytes};
     lla_status st = check_prefill(b, false, true, false, false, true, raw_enum(dtype), B, Heads{H, H}, T, dk,
                                   dv, C, p);
-    if (st == LLA_OK) st = check_phase_dtype(raw_enum(dtype), C);
     if (st != LLA_OK || T == 0) return st;
     return device_status(lla::launch_segment_states(p, K, V, (float*)workspace, (hipStream_t)stream));
 }
@@ -254,7 +241,6 @@ lla_status lla_prefill_chunks(const void* Q, const void* K, const void* V, lla_d
     PrefillBufs b{Q, K, V, nullptr, S, O, workspace, workspace_bytes};
     lla_status st = check_prefill(b, true, true, true, true, true, raw_enum(dtype), B, Heads{H, H}, T, dk,
                                   dv, C, p);
-    if (st == LLA_OK) st = check_phase_dtype(raw_enum(dtype), C);
     if (st != LLA_OK || T == 0) return st;
     return device_status(lla::launch_chunk_walk(p, Q, K, V, S, O, (float*)workspace, (hipStream_t)stream));
 }

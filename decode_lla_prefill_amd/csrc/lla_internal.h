@@ -23,8 +23,8 @@ namespace lla {
 #endif
 constexpr int64_t kTargetWalkers = LLA_TARGET_WALKERS;
 
-// Chunks of up to 64 tokens carry the masked scores P into P V as a bf16
-// high + low pair (1), not as one bf16 value (0).
+// The masked scores P enter P V as a bf16 high + low pair (1), not as one
+// bf16 value (0).
 #ifndef LLA_SPLIT_P
 #define LLA_SPLIT_P 1
 #endif
@@ -37,9 +37,9 @@ struct PrefillPlan {
     int group;            // query heads per key/value head = H / Hkv
     int64_t BHq;          // B * H
     bool use_ws;          // the walk starts every segment from the workspace
-    int dk, dv, C;
+    int dk, dv, C;  // C: the chunk run (the caller's, or half of one over 64 tokens)
     int D;        // padded head dim (32, 64 or 128) used for both dk and dv
-    int CT;       // padded chunk tile (32, 64 or 128 rows)
+    int CT;       // padded chunk tile (32 or 64 rows; C > 64 runs as two sub-chunks)
     int BV;       // value columns per workgroup (D, or 64 when D = 128)
     int n_vb;     // value-column blocks = D / BV
     int64_t n_c;  // chunks per sequence = ceil(T / C)

@@ -1,7 +1,7 @@
 // lla_plan.cpp -- the prefill plan: how a shape is cut into work for the
 // kernels.  Host code only (no kernels): the chunk tile and head-dim tile a
 // shape compiles to, the number of chunks one workgroup walks (a segment) and
-// whether the walks start from the workspace.
+// whether the walks start from the workspace.  Chunk tiles are 32 or 64 rows.
 //
 // The chunk form of the slide deck "Chunking, causality, and parallel
 // prefill" ("Split into chunks", "Incoming and outgoing state") serialises
@@ -31,12 +31,14 @@ void plan_prefill(PrefillPlan& p) {
     p.G = want > kTargetWalkers ? (want + kTargetWalkers - 1) / kTargetWalkers : 1;
     if (p.G > p.n_c) p.G = p.n_c > 0 ? p.n_c : 1;
     p.n_seg = p.n_c > 0 ? (p.n_c + p.G - 1) / p.G : 0;
-    // fp32 tiles of more than 64 rows do not fit the walks' LDS: such chunks
-    // run as sub-chunks of ceil(C/2) tokens, twice as many per segment (the
-    // chunk form gives the same result for any chunk size, up to rounding).
-    // That never makes more segments than the plan for C itself, so the
-    // workspace sizes, which do not depend on the dtype, still cover it.
-    if (p.dtype == LLA_F32 && p.C > 64 && p.n_c > 0) {
+    // Chunks of more than 64 tokens run as two sub-chunks of ceil(C/2)
+    // tokens each, twice as many per segment: the chunk form gives the same
+    // result for any chunk size, up to rounding, and the 64-row tiles of the
+    // double-buffered walks were measured faster than 128-row ones (fp32
+    // tiles of 128 rows would not fit the LDS at all).  For an even C the
+    // segments then start at the same tokens as in the plan for C; for an
+    // odd C there are never more of them.
+    if (p.C > 64 && p.n_c > 0) {
         p.C = (p.C + 1) / 2;
         p.CT = pad_dim(p.C);
         p.n_c = (p.T + p.C - 1) / p.C;

@@ -4,7 +4,8 @@
 // Method (slide deck "Chunking, causality, and parallel prefill"): per chunk c
 // of C tokens, O_c = tril(Q_c K_c^T) V_c + Q_c S_c and S_{c+1} = S_c + K_c^T V_c
 // ("Split into chunks", "Causal triangle", "Incoming and outgoing state");
-// only the chunk-to-chunk state hop is serial.
+// only the chunk-to-chunk state hop is serial.  Chunks of more than 64
+// tokens run as two sub-chunks (see lla_plan.cpp), so tiles are 32 or 64 rows.
 //
 // Three kernels:
 //   k_segment_states : per (b,h), segment of G chunks and block of value
@@ -38,10 +39,10 @@ struct WalkCfg {
     static constexpr int CT = CT_, D = D_, BV = BV_;
     static constexpr int NW = NW_, NTH = NW * kWave;  // waves, threads per workgroup
     static constexpr bool BF = std::is_same<T, bf16>::value;
+    static_assert(CT_ == 32 || CT_ == 64, "chunk tiles are 32 or 64 rows (longer chunks run as two sub-chunks)");
     // The state operand of Q S in natural depth order, so that Q is read in
-    // 16-byte rows (see state_operand).  Chunks of 128 keep the interleaved
-    // order: their walks have no registers to spare for the regrouping.
-    static constexpr bool NATQ = BF && CT <= 64;
+    // 16-byte rows (see state_operand).
+    static constexpr bool NATQ = BF;
     // The masked scores P as a bf16 high + low pair (second tile right after
     // P), so that P V carries P to about 16 bits instead of bf16's 8: an
     // output dominated by one large score term then keeps fp32-like accuracy.
@@ -64,10 +65,8 @@ struct WalkCfg {
     // 32 (it / 2 + 1) of them.  Tiles it and NT - 1 - it need 32 (NT / 2 + 1)
     // columns together, so each such pair shares 16 rows of one stride:
     // tile it < NT / 2 from column 0, its partner right after it.  At
-    // C = 128 a P tile is 10,752 elements instead of the 17,408 of the
-    // padded square, which makes room for the low part in the
-    // single-buffered walk; one row stride keeps every tile's lane offset
-    // the same.
+    // C = 64 a P tile is 3,584 elements instead of the 5,120 of the padded
+    // square; one row stride keeps every tile's lane offset the same.
     static constexpr int PPAD = BF ? 16 : 4;
     static constexpr int PLD = 32 * (CT / 32 + 1) + PPAD;  // elements per row
     __device__ __host__ static constexpr int p_row0(int it) { return 16 * (it < CT / 32 ? it : CT / 16 - 1 - it); }
@@ -516,16 +515,11 @@ __device__ __forceinline__ void chunk_output(f32x4 (&Oacc)[Cf::NT][Cf::NVW],
     };
     auto owns = [&](int vw) { return Cf::ALL_WAVES || w + Cf::NW * vw < Cf::NVT; };
 
-    // The first depth step's Q slices and state operand are read ahead of
-    // P V, except in chunks of 128 tokens, whose walks have no registers to
-    // hold them through it.
-    constexpr bool EARLY_QS = Cf::CT <= 64;
+    // The first depth step's Q slices and state operand are read ahead of P V.
     Fr qb[2][Cf::NT], Shi[2][Cf::NVW], Slo[2][Cf::NVW];
-    if constexpr (EARLY_QS) {
-        q_slices(qb[0], 0);
+    q_slices(qb[0], 0);
 #pragma unroll
-        for (int vw = 0; vw < Cf::NVW; ++vw) state_operand<Cf>(Shi[0][vw], Slo[0][vw], Sacc[vw], 0);
-    }
+    for (int vw = 0; vw < Cf::NVW; ++vw) state_operand<Cf>(Shi[0][vw], Slo[0][vw], Sacc[vw], 0);
 
     // All query tiles of the chunk are accumulated side by side (depth
     // outer, tile inner), so consecutive matrix-core ops are independent.
@@ -564,11 +558,6 @@ __device__ __forceinline__ void chunk_output(f32x4 (&Oacc)[Cf::NT][Cf::NVW],
         for (int it = 0; it < Cf::NT; ++it)
 #pragma unroll
             for (int vw = 0; vw < Cf::NVW; ++vw) qs_acc(it, vw) = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    if constexpr (!EARLY_QS) {
-        q_slices(qb[0], 0);
-#pragma unroll
-        for (int vw = 0; vw < Cf::NVW; ++vw) state_operand<Cf>(Shi[0][vw], Slo[0][vw], Sacc[vw], 0);
     }
 #pragma unroll
     for (int ds = 0; ds < Cf::NDS; ++ds) {
@@ -629,10 +618,10 @@ __device__ __forceinline__ void chunk_output(f32x4 (&Oacc)[Cf::NT][Cf::NVW],
 // scale away terms that are already negligible.
 __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Wave 0: a chunk's decay table from the gates of rows
-// `lane` (g0) and 64 + `lane` (g1), 1 past the chunk's rows.
+// Wave 0: a chunk's decay table from the gate g of row `lane` (1 past the
+// chunk's rows).
 template <int CT>
-__device__ __forceinline__ void chunk_decay(float* D, float g0, float g1, int lane) {
+__device__ __forceinline__ void chunk_decay(float* D, float g, int lane) {
     auto log2g = [](float x) { return fminf(fmaxf(__builtin_amdgcn_logf(x), -126.0f), 0.0f); };
     auto scan = [&](float a) {
 #pragma unroll
@@ -642,23 +631,13 @@ __device__ __forceinline__ void chunk_decay(float* D, float g0, float g1, int la
         }
         return a;
     };
-    const float a = scan(log2g(g0));
-    if constexpr (CT > kWave) {
-        const float a1 = scan(log2g(g1)) + __shfl(a, kWave - 1, kWave);
-        const float B = __shfl(a1, kWave - 1, kWave);
+    static_assert(CT <= kWave, "one gate per lane");
+    const float a = scan(log2g(g));
+    const float B = __shfl(a, CT - 1, kWave);
+    if (lane < CT) {
         D[lane] = a;
         D[CT + lane] = hw_exp2(B - a);
         D[2 * CT + lane] = hw_exp2(a);
-        D[kWave + lane] = a1;
-        D[CT + kWave + lane] = hw_exp2(B - a1);
-        D[2 * CT + kWave + lane] = hw_exp2(a1);
-    } else {
-        const float B = __shfl(a, CT - 1, kWave);
-        if (lane < CT) {
-            D[lane] = a;
-            D[CT + lane] = hw_exp2(B - a);
-            D[2 * CT + lane] = hw_exp2(a);
-        }
     }
 }
 
@@ -1133,8 +1112,7 @@ __global__ __launch_bounds__(NW * kWave) void k_tokens_grouped(
 }
 
 // ---------------------------------------------------------------------------
-// Phase 3, wide form for d = 128 bf16 (or FP8, staged as bf16) inputs and
-// chunks of up to 64 tokens:
+// Phase 3, wide form for d = 128 bf16 (or FP8, staged as bf16) inputs:
 // one workgroup of eight waves per (b,h) and segment covers all 128 value
 // columns (wave w owns value tile w), so the score triangle is computed and
 // the Q, K tiles are loaded once per chunk.  Q, K, V are double buffered in
@@ -1189,14 +1167,13 @@ __global__ __launch_bounds__(kWideWaves * kWave) void k_chunk_walk_wide(
     float* Ob = O + bq * T_len * dv;
     auto rows_of = [&](int64_t c) { return c < c1 ? (int)min((int64_t)C, T_len - c * C) : 0; };
     // gates of row r of chunk c (1 past the chunk's rows); wave 0 holds the
-    // next chunk's in g0, g1
+    // next chunk's in g0
     auto gate_of = [&](int64_t c, int r) { return r < rows_of(c) ? gate[bh * T_len + c * C + r] : 1.0f; };
-    float g0 = 1.0f, g1 = 1.0f;
+    float g0 = 1.0f;
     if constexpr (GATED) {
         if (w == 0) {
-            chunk_decay<CT>(Bs2[0], gate_of(c0, lane), CT > kWave ? gate_of(c0, kWave + lane) : 1.0f, lane);
+            chunk_decay<CT>(Bs2[0], gate_of(c0, lane), lane);
             g0 = gate_of(c0 + 1, lane);
-            if constexpr (CT > kWave) g1 = gate_of(c0 + 1, kWave + lane);
         }
     }
 
@@ -1268,13 +1245,12 @@ __global__ __launch_bounds__(kWideWaves * kWave) void k_chunk_walk_wide(
             tk.scatter(nxt + Cf::K_OFF, tid);
             tv.scatter(nxt + Cf::V_OFF, tid);
             if constexpr (GATED)
-                if (w == 0) chunk_decay<CT>(Bs2[1 - b], g0, g1, lane);
+                if (w == 0) chunk_decay<CT>(Bs2[1 - b], g0, lane);
         }
         __syncthreads();  // P complete
         if constexpr (GATED) {
             if (w == 0) {
                 g0 = gate_of(c + 2, lane);
-                if constexpr (CT > kWave) g1 = gate_of(c + 2, kWave + lane);
             }
         }
 
@@ -1313,7 +1289,7 @@ __global__ __launch_bounds__(kWideWaves * kWave) void k_chunk_walk_wide(
 }
 
 // ---------------------------------------------------------------------------
-// Phase 1, wide form for d = 128 bf16 (or FP8) inputs and chunks of up to 64 tokens:
+// Phase 1, wide form for d = 128 bf16 (or FP8) inputs:
 // one workgroup of eight waves per (b,h) and segment (all but the last)
 // covers all 128 value columns, so K is loaded once.  The K, V tiles are
 // double buffered: chunk c + 1 is written into the free buffer while chunk
@@ -1379,12 +1355,11 @@ __global__ __launch_bounds__(512) void k_segment_states_wide(const In* __restric
     tk[0].scatter(buf, tid);
     tv[0].scatter(buf + Cf::V_AT, tid);
     auto gate_of = [&](int64_t c, int r) { return r < rows_of(c) ? gate[bh * T_len + c * C + r] : 1.0f; };
-    float g0 = 1.0f, g1 = 1.0f, L = 0.0f;
+    float g0 = 1.0f, L = 0.0f;
     if constexpr (GATED) {
         if (w == 0) {
-            chunk_decay<CT>(Bs2[0], gate_of(c0, lane), CT > kWave ? gate_of(c0, kWave + lane) : 1.0f, lane);
+            chunk_decay<CT>(Bs2[0], gate_of(c0, lane), lane);
             g0 = gate_of(c0 + 1, lane);
-            if constexpr (CT > kWave) g1 = gate_of(c0 + 1, kWave + lane);
         }
     }
     __syncthreads();
@@ -1403,7 +1378,7 @@ __global__ __launch_bounds__(512) void k_segment_states_wide(const In* __restric
                 tk[un].scatter(nxt, tid);
                 tv[un].scatter(nxt + Cf::V_AT, tid);
                 if constexpr (GATED)
-                    if (w == 0) chunk_decay<CT>(Bs2[1 - b], g0, g1, lane);
+                    if (w == 0) chunk_decay<CT>(Bs2[1 - b], g0, lane);
             }
             // set u held chunk c, written to LDS one chunk ago: reload it
             const int64_t tn = (c + PF) * C;
@@ -1420,7 +1395,6 @@ __global__ __launch_bounds__(512) void k_segment_states_wide(const In* __restric
                 }
                 if (w == 0) {
                     g0 = gate_of(c + 2, lane);
-                    if constexpr (CT > kWave) g1 = gate_of(c + 2, kWave + lane);
                 }
                 state_hop_gated<Cf>(Sacc, Vf, Ks, Bs2[b], w, g, lane);
                 L += Bs2[b][CT - 1];
@@ -1501,11 +1475,8 @@ __global__ __launch_bounds__(kThreads) void k_gated_segment_states(
         tk.gather(Kb + c0 * C * dk, dk, rows_of(c0));
         tv.gather(Vb + c0 * C * dv, dv, rows_of(c0));
     }
-    float g0 = 1.0f, g1 = 1.0f;
-    if (w == 0) {
-        g0 = gate_of(c0, lane);
-        if constexpr (CT > kWave) g1 = gate_of(c0, kWave + lane);
-    }
+    float g0 = 1.0f;
+    if (w == 0) g0 = gate_of(c0, lane);
     for (int64_t c = c0; c < c1; ++c) {
         if constexpr (VEC) {
             tk.scatter(Ks, tid);
@@ -1514,7 +1485,7 @@ __global__ __launch_bounds__(kThreads) void k_gated_segment_states(
             TK::load_scalar(Kb + c * C * dk, dk, rows_of(c), dk, Ks, tid);
             TV::load_scalar(Vb + c * C * dv, dv, rows_of(c), nv, Vs, tid);
         }
-        if (w == 0) chunk_decay<CT>(Bs, g0, g1, lane);
+        if (w == 0) chunk_decay<CT>(Bs, g0, lane);
         __syncthreads();
         if (c + 1 < c1) {  // the next chunk's loads fly during this chunk's math
             if constexpr (VEC) {
@@ -1523,7 +1494,6 @@ __global__ __launch_bounds__(kThreads) void k_gated_segment_states(
             }
             if (w == 0) {
                 g0 = gate_of(c + 1, lane);
-                if constexpr (CT > kWave) g1 = gate_of(c + 1, kWave + lane);
             }
         }
         Fr Vf[Cf::NVW][Cf::NTS];
@@ -1622,11 +1592,8 @@ __global__ __launch_bounds__(kThreads) void k_gated_walk(
         tk.gather(Kb + c0 * C * dk, dk, rows_of(c0));
         tv.gather(Vb + c0 * C * dv, dv, rows_of(c0));
     }
-    float g0 = 1.0f, g1 = 1.0f;
-    if (w == 0) {
-        g0 = gate_of(c0, lane);
-        if constexpr (CT > kWave) g1 = gate_of(c0, kWave + lane);
-    }
+    float g0 = 1.0f;
+    if (w == 0) g0 = gate_of(c0, lane);
 
     f32x4 Oacc[Cf::NT][Cf::NVW];
     int64_t t_prev = 0;
@@ -1643,7 +1610,7 @@ __global__ __launch_bounds__(kThreads) void k_gated_walk(
             TK::load_scalar(Kb + t0 * dk, dk, nrows, dk, Ks, tid);
             TV::load_scalar(Vb + t0 * dv, dv, nrows, nv, Vs, tid);
         }
-        if (w == 0) chunk_decay<CT>(Bs, g0, g1, lane);
+        if (w == 0) chunk_decay<CT>(Bs, g0, lane);
         __syncthreads();
         if (c > c0) store_out<Cf, VEC>(Ob, Oacc, t_prev, n_prev, nv, dv, w, g, c16);
         if (c + 1 < c1) {  // the next chunk's loads fly during this chunk's math
@@ -1655,7 +1622,6 @@ __global__ __launch_bounds__(kThreads) void k_gated_walk(
             }
             if (w == 0) {
                 g0 = gate_of(c + 1, lane);
-                if constexpr (CT > kWave) g1 = gate_of(c + 1, kWave + lane);
             }
         }
 
@@ -1688,21 +1654,12 @@ template <typename In, int CT, int D>
 static hipError_t launch_walk_t(const PrefillPlan& p, const void* Q, const void* K, const void* V,
                                 float* S, float* O, float* ws, hipStream_t st) {
     using T = typename Compute<In>::type;
-    if constexpr (std::is_same<T, bf16>::value && D == 128 && CT <= 64) {
+    if constexpr (std::is_same<T, bf16>::value && D == 128) {
         if (p.vec) {  // one eight-wave workgroup per (b,h) and segment
             hipLaunchKernelGGL((k_chunk_walk_wide<CT, In>), dim3((unsigned)(p.BHq * p.n_seg)), dim3(kWideWaves * kWave), 0, st,
                                (const In*)Q, (const In*)K, (const In*)V, S, O,
                                (const float*)(p.use_ws ? ws : nullptr), p.T, p.dk, p.dv, p.C, p.G,
                                p.n_seg, p.group, (int)p.zero_start, (const float*)nullptr);
-            return hipGetLastError();
-        }
-    }
-    if constexpr (std::is_same<T, bf16>::value && D == 128 && CT == 128) {
-        if (p.vec) {  // chunks of 128: one single-buffered eight-wave workgroup per (b,h) and segment
-            hipLaunchKernelGGL((k_chunk_walk<In, 128, 128, 128, true, 8>), dim3((unsigned)(p.BHq * p.n_seg)),
-                               dim3(8 * kWave), 0, st, (const In*)Q, (const In*)K, (const In*)V, S, O,
-                               (const float*)(p.use_ws ? ws : nullptr), p.T, p.dk, p.dv, p.C, p.G,
-                               p.n_seg, 1, p.group, (int)p.zero_start);
             return hipGetLastError();
         }
     }
@@ -1724,19 +1681,11 @@ template <typename In, int CT, int D>
 static hipError_t launch_seg_t(const PrefillPlan& p, const void* K, const void* V, float* ws,
                                hipStream_t st) {
     using T = typename Compute<In>::type;
-    if constexpr (std::is_same<T, bf16>::value && D == 128 && CT <= 64) {
+    if constexpr (std::is_same<T, bf16>::value && D == 128) {
         if (p.vec) {  // one eight-wave workgroup per (b,h) and segment
             hipLaunchKernelGGL((k_segment_states_wide<CT, In>), dim3((unsigned)(p.BH * (p.n_seg - 1))),
                                dim3(512), 0, st, (const In*)K, (const In*)V, ws, p.T, p.dk, p.dv,
                                p.C, p.G, p.n_seg, (const float*)nullptr, (float*)nullptr);
-            return hipGetLastError();
-        }
-    }
-    if constexpr (std::is_same<T, bf16>::value && D == 128 && CT == 128) {
-        if (p.vec) {  // chunks of 128: one eight-wave workgroup per (b,h) and segment
-            hipLaunchKernelGGL((k_segment_states<In, 128, 128, 128, true, 8>),
-                               dim3((unsigned)(p.BH * (p.n_seg - 1))), dim3(8 * kWave), 0, st,
-                               (const In*)K, (const In*)V, ws, p.T, p.dk, p.dv, p.C, p.G, p.n_seg, 1);
             return hipGetLastError();
         }
     }
@@ -1761,28 +1710,20 @@ static hipError_t launch_seg_t(const PrefillPlan& p, const void* K, const void* 
                 if (p.D == 32) return FN<fp8e4m3, 32, 32>(__VA_ARGS__);                    \
                 if (p.D == 64) return FN<fp8e4m3, 32, 64>(__VA_ARGS__);                    \
                 return FN<fp8e4m3, 32, 128>(__VA_ARGS__);                                  \
-            } else if (p.CT == 64) {                                                       \
+            } else {                                                                       \
                 if (p.D == 32) return FN<fp8e4m3, 64, 32>(__VA_ARGS__);                    \
                 if (p.D == 64) return FN<fp8e4m3, 64, 64>(__VA_ARGS__);                    \
                 return FN<fp8e4m3, 64, 128>(__VA_ARGS__);                                  \
-            } else {                                                                       \
-                if (p.D == 32) return FN<fp8e4m3, 128, 32>(__VA_ARGS__);                   \
-                if (p.D == 64) return FN<fp8e4m3, 128, 64>(__VA_ARGS__);                   \
-                return FN<fp8e4m3, 128, 128>(__VA_ARGS__);                                 \
             }                                                                              \
         } else if (p.dtype == LLA_BF16) {                                                  \
             if (p.CT == 32) {                                                              \
                 if (p.D == 32) return FN<bf16, 32, 32>(__VA_ARGS__);                       \
                 if (p.D == 64) return FN<bf16, 32, 64>(__VA_ARGS__);                       \
                 return FN<bf16, 32, 128>(__VA_ARGS__);                                     \
-            } else if (p.CT == 64) {                                                       \
+            } else {                                                                       \
                 if (p.D == 32) return FN<bf16, 64, 32>(__VA_ARGS__);                       \
                 if (p.D == 64) return FN<bf16, 64, 64>(__VA_ARGS__);                       \
                 return FN<bf16, 64, 128>(__VA_ARGS__);                                     \
-            } else {                                                                       \
-                if (p.D == 32) return FN<bf16, 128, 32>(__VA_ARGS__);                      \
-                if (p.D == 64) return FN<bf16, 128, 64>(__VA_ARGS__);                      \
-                return FN<bf16, 128, 128>(__VA_ARGS__);                                    \
             }                                                                              \
         } else {                                                                           \
             if (p.CT == 32) {                                                              \
@@ -1838,7 +1779,7 @@ template <typename In, int CT, int D>
 static hipError_t launch_gated_seg_t(const PrefillPlan& p, const void* K, const void* V, const float* gate,
                                      float* ws, float* dec, hipStream_t st) {
     using T = typename Compute<In>::type;
-    if constexpr (std::is_same<T, bf16>::value && D == 128 && CT <= 64) {
+    if constexpr (std::is_same<T, bf16>::value && D == 128) {
         if (p.vec) {  // one eight-wave workgroup per (b,h) and segment
             hipLaunchKernelGGL((k_segment_states_wide<CT, In, true>), dim3((unsigned)(p.BH * (p.n_seg - 1))),
                                dim3(512), 0, st, (const In*)K, (const In*)V, ws, p.T, p.dk, p.dv, p.C, p.G,
@@ -1863,7 +1804,7 @@ template <typename In, int CT, int D>
 static hipError_t launch_gated_walk_t(const PrefillPlan& p, const void* Q, const void* K, const void* V,
                                       const float* gate, float* S, float* O, float* ws, hipStream_t st) {
     using T = typename Compute<In>::type;
-    if constexpr (std::is_same<T, bf16>::value && D == 128 && CT <= 64) {
+    if constexpr (std::is_same<T, bf16>::value && D == 128) {
         if (p.vec) {  // one eight-wave workgroup per (b,h) and segment
             hipLaunchKernelGGL((k_chunk_walk_wide<CT, In, true>), dim3((unsigned)(p.BHq * p.n_seg)),
                                dim3(kWideWaves * kWave), 0, st, (const In*)Q, (const In*)K, (const In*)V, S, O,

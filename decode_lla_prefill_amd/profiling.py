@@ -50,6 +50,11 @@ COPY_BYTES = 1 << 30
 WORKLOADS = ("prefill_T8192", "prefill_T8192_fp8", "prefill_B4_T1024", "prefill_T131072",
              "decode_B256", "decode_B256_gqa", "decode_B256_gqa_T16", "prefill_T8192_gated",
              "decode_B256_gated")
+# Workloads whose measured kernel has the name and the grid of another's
+# (the T=131072 walk is the T=8192 walk's kernel on 256 workgroups too):
+# their counters come from a run of their own, never from the default run.
+RUN_ALONE = ("prefill_T131072",)
+DEFAULT_RUN = tuple(w for w in WORKLOADS if w not in RUN_ALONE)
 
 # what decides a prefill kernel's work: its code and the plan that cuts the
 # shape into segments
@@ -73,8 +78,9 @@ KERNELS = {
     "chunk_walk_T1024": (("k_chunk_walkIDF16bLi64ELi64ELi64ELb1ELi4E", "k_chunk_walk<__bf16, 64, 64, 64, true, 4>"),
                          32 * 8 * 256, "chunk_walk_B4_T1024_traffic.txt",
                          PREFILL_SOURCES, "prefill_B4_T1024"),
-    "chunk_walk_T131072": (("k_chunk_walkIDF16bLi128ELi128ELi128ELb1ELi8E",
-                            "k_chunk_walk<__bf16, 128, 128, 128, true, 8>"),
+    # chunks of 128 run as two of 64 on the wide walk (counters from a run of
+    # this workload alone: the kernel and grid are chunk_walk's)
+    "chunk_walk_T131072": (("k_chunk_walk_wideILi64EDF16bLb0E", "k_chunk_walk_wide<64, __bf16, false>"),
                            32 * 8 * 512, "chunk_walk_T131072_traffic.txt",
                            PREFILL_SOURCES, "prefill_T131072"),
     "decode_step": (("k_decode_step_sqIDF16bLi128ELi512ELb0E", "k_decode_step_sq<__bf16, 128, 512, false>"),
@@ -170,7 +176,7 @@ def stored_traffic(kernel: str):
 
 # ---- the counter workload -------------------------------------------------------
 
-def run(launches: int, which=WORKLOADS) -> None:
+def run(launches: int, which=DEFAULT_RUN) -> None:
     import torch
     sys.path.insert(0, ROOT)
     import workloads
@@ -420,7 +426,8 @@ def main(argv=None):
     sub = ap.add_subparsers(dest="cmd", required=True)
     r = sub.add_parser("run")
     r.add_argument("--launches", type=int, default=8)
-    r.add_argument("--workloads", default=",".join(WORKLOADS))
+    r.add_argument("--workloads", default=",".join(DEFAULT_RUN),
+                   help="comma-separated, of %s" % ",".join(WORKLOADS))
     s = sub.add_parser("stats")
     s.add_argument("directory")
     t = sub.add_parser("traffic")

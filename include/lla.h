@@ -36,11 +36,11 @@
  * enqueues work on that stream and returns without synchronising; results
  * are valid once the stream has been synchronised.
  * Limits: B, H >= 1; T >= 0 (T = 0 is a no-op that leaves S untouched);
- * 1 <= dk, dv <= 128; 1 <= C <= 128 (fp32 inputs with C > 64 run as chunks of
- * ceil(C/2) tokens, which gives the same result up to rounding; the three
- * phase calls refuse them); B*H <= 2^20 (H counts query heads in the grouped calls) and
+ * 1 <= dk, dv <= 128; 1 <= C <= 128; B*H <= 2^20 (H counts query heads in the grouped calls) and
  * B*H*T*max(dk,dv) <= 2^58, else LLA_ERR_SHAPE.  C need not divide T: the last
- * chunk of a sequence is shorter.
+ * chunk of a sequence is shorter.  The library runs chunks of C > 64 tokens as
+ * two chunks of c = ceil(C/2) tokens each (c = C for C <= 64): the chunk form
+ * gives the same result for any chunk size, up to rounding.
  * Errors: arguments are checked on the host before anything is enqueued; on
  * any error no buffer is touched and a status other than LLA_OK is returned.
  * LLA_ERR_DEVICE means the HIP launch itself failed (lla_last_device_error()
@@ -84,8 +84,7 @@ typedef enum {
     LLA_ERR_NULL = 1,        /* a required pointer is NULL */
     LLA_ERR_SHAPE = 2,       /* a size is out of range */
     LLA_ERR_DTYPE = 3,       /* unknown dtype */
-    LLA_ERR_UNSUPPORTED = 4, /* valid request the library does not handle: fp32 with C > 64
-                                in the phase calls, unknown option bits,
+    LLA_ERR_UNSUPPORTED = 4, /* valid request the library does not handle: unknown option bits,
                                 LLA_PREFILL_KEEP_STATE off the fused short-prompt route or
                                 on a gated prefill */
     LLA_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned (a gate: 4-byte) */
@@ -117,8 +116,9 @@ lla_status lla_state_init(float *S, int64_t B, int64_t H, int64_t dk, int64_t dv
                           void *stream);
 
 /*
- * Number of consecutive chunks one workgroup walks in lla_prefill (a
- * "segment"); a sequence has ceil(ceil(T/C) / G) segments.  The choice
+ * Number G of consecutive chunks of c tokens (c = C, or ceil(C/2) for
+ * C > 64) one workgroup walks in lla_prefill (a "segment"); a sequence has
+ * ceil(ceil(T/c) / G) segments.  The choice
  * depends on the shape only (not on the device), so results are
  * reproducible across devices.  Returns 0 for invalid sizes.
  */
@@ -144,7 +144,8 @@ size_t lla_prefill_workspace_size(int64_t B, int64_t H, int64_t T, int64_t dk,
  * workspace: device buffer of at least lla_prefill_workspace_size() bytes
  *    (may be NULL when that size is 0).  Its content on return is the state
  *    at the start of every segment: state s of (b, h) -- [B][H][n_seg][dk][dv]
- *    fp32 -- holds S after s*G*C tokens (G = lla_prefill_segment_chunks).
+ *    fp32 -- holds S after s*G*c tokens (G = lla_prefill_segment_chunks, c as
+ *    above; for an even C, G*c is a whole number of chunks of C).
  *
  * Enqueues up to three kernels on `stream`: per-segment K^T V, a scan over
  * segments, then the chunk walk (one workgroup per segment: per chunk the

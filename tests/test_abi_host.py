@@ -128,16 +128,16 @@ def test_prefill_rejects(lib, fn, change, expect):
     assert getattr(lib, fn)(*b.args()) == expect
 
 
-def test_fp32_chunks_over_64_only_in_the_one_call_entry_points(lib):
-    # lla_prefill plans fp32 chunks of C > 64 as sub-chunks: the dtype passes,
-    # and the next check (here a NULL q) decides.  The phase calls share one
-    # plan with the dtype-less scan and refuse it.
+def test_fp32_chunks_over_64_pass_the_dtype_check_everywhere(lib):
+    # chunks of C > 64 run as two sub-chunks for every dtype, so the plan
+    # does not depend on it: the one-call and the phase calls take fp32 at
+    # C = 128, and the next check (a NULL pointer) decides
     b = Bufs(dtype=F32, C=128)
-    assert lib.lla_prefill_chunks(*b.args()) == E_UNSUP
-    assert lib.lla_prefill_segment_states(b.k, b.v, F32, 1, 2, 100, 64, 64, 128, b.ws, b.ws_bytes,
-                                          None) == E_UNSUP
     b.q = None
     assert lib.lla_prefill(*b.args()) == E_NULL
+    assert lib.lla_prefill_chunks(*b.args()) == E_NULL
+    assert lib.lla_prefill_segment_states(None, b.v, F32, 1, 2, 100, 64, 64, 128, b.ws, b.ws_bytes,
+                                          None) == E_NULL
     b.q = A
     b.O = A + 64
     assert lib.lla_prefill(*b.args()) == E_ALIAS
@@ -196,28 +196,48 @@ def test_state_init_rejects(lib):
 
 # ---- planning: segments and workspace ------------------------------------------------
 
+def _lines_rule_G(B, H, T, C):
+    """Chunks of C per segment by the line rule: the smallest whole number
+    that keeps the (sequence, head, segment) lines at most 256."""
+    n_c = math.ceil(T / C)
+    return min(math.ceil(n_c * B * H / 256), n_c)
+
+
 @pytest.mark.parametrize("B,H,T,d,C", [
     (1, 1, 8, 2, 4), (1, 1, 7, 2, 4), (4, 8, 1024, 64, 64), (1, 16, 8192, 128, 64),
     (1, 32, 131072, 128, 128), (256, 32, 4096, 128, 64), (3, 5, 1000, 33, 17), (1, 1, 1, 1, 1),
+    (2, 3, 1000, 64, 101), (1, 16, 8192, 128, 100), (1, 2, 70, 16, 65), (4, 8, 1024, 64, 128),
 ])
 def test_segments_cover_the_sequence(lib, B, H, T, d, C):
     G = lib.lla_prefill_segment_chunks(B, H, T, d, d, C)
     ws = lib.lla_prefill_workspace_size(B, H, T, d, d, C)
-    n_c = math.ceil(T / C)
+    c = C if C <= 64 else (C + 1) // 2  # the chunk the library runs
+    n_c = math.ceil(T / c)
     assert 1 <= G <= n_c
     n_seg = math.ceil(n_c / G)
     # one fp32 d x d state per segment per (b,h), or nothing for one segment
     assert ws == (B * H * n_seg * d * d * 4 if n_seg > 1 else 0)
-    # about one (sequence, head, segment) line per compute unit, without one per
-    # chunk: G is the smallest whole number of chunks that keeps the lines at
-    # most 256, so there are more than half that many (or one per chunk)
-    lines = n_seg * B * H
-    assert lines >= min(n_c * B * H, 129)
-    assert G == 1 or math.ceil(n_c / (G - 1)) * B * H > 256
+    G_C = _lines_rule_G(B, H, T, C)
+    n_seg_C = math.ceil(math.ceil(T / C) / G_C)
+    if C <= 64:
+        assert G == G_C
+    else:
+        # two sub-chunks per chunk of C, twice as many per segment: never more
+        # segments than the plan for C, and for an even C the same tokens
+        assert G == min(2 * G_C, n_c)
+        assert n_seg <= n_seg_C
+        if C % 2 == 0:
+            assert n_seg == n_seg_C and (n_seg == 1 or G * c == G_C * C)
+    # about one line per compute unit, without one per chunk: more than half
+    # of 256 lines (or one per chunk)
+    lines = n_seg_C * B * H
+    assert lines >= min(math.ceil(T / C) * B * H, 129)
 
 
 def test_segment_plan_for_the_t8192_workload(lib):
-    # 128 chunks x 16 heads = 2048 chunk lines: 256 eight-wave walk workgroups of 8 chunks
+    # 128 chunks x 16 heads = 2048 chunk lines: 256 eight-wave walk workgroups of 8 chunks;
+    # chunks of 128 run as two of 64: the same 16 segments, of 8 chunks of 64
+    assert lib.lla_prefill_segment_chunks(1, 16, 8192, 128, 128, 128) == 8
     assert lib.lla_prefill_segment_chunks(1, 16, 8192, 128, 128, 64) == 8
     assert lib.lla_prefill_workspace_size(1, 16, 8192, 128, 128, 64) == 16 * 16 * 128 * 128 * 4
 

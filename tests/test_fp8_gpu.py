@@ -31,7 +31,7 @@ def _prefill(q, k, v, S0, C, dev):
 
 
 # B, Hq, Hkv, T, dk, dv, C: the eight-wave d=128 walk (ragged tail, several
-# segments), C = 128 and d = 64 four-wave walks, a ragged head dim (element
+# segments), C = 128 (two 64-token sub-chunks), d = 64 four-wave walks, a ragged head dim (element
 # path), a short prompt (fused decode steps), grouped heads
 FP8_INT = [
     (2, 3, 3, 300, 128, 128, 64),

@@ -38,7 +38,7 @@ CASES = [
     # B, H, T, dk, dv, C, dtype, gate range
     (2, 3, 1000, 64, 64, 64, torch.bfloat16, (0.5, 1.0)),      # several segments
     (1, 2, 2000, 128, 128, 64, torch.bfloat16, (0.9, 1.0)),    # d = 128, two value blocks
-    (1, 2, 900, 128, 128, 128, torch.bfloat16, (0.8, 1.0)),    # chunk tile 128
+    (1, 2, 900, 128, 128, 128, torch.bfloat16, (0.8, 1.0)),    # chunks of 128 (two of 64)
     (2, 2, 333, 32, 32, 32, torch.bfloat16, (0.0, 1.0)),       # chunk tile 32, gates down to 0
     (1, 3, 700, 48, 40, 40, torch.float32, (0.7, 1.0)),        # fp32, ragged dims and chunks
     (1, 2, 1500, 128, 128, 128, torch.float32, (0.9, 1.0)),    # fp32, C > 64: sub-chunks of 64

@@ -58,6 +58,7 @@ INT_CASES = [
     (1, 3, 70, 40, 24, 65, torch.float32),      # sub-chunks of 33, one segment
     (1, 2, 37, 16, 16, 1, torch.bfloat16),      # C = 1: the recurrence itself
     (2, 1, 300, 24, 40, 128, torch.bfloat16),   # C = 128 with odd head dims
+    (1, 2, 1000, 64, 64, 101, torch.bfloat16),  # odd C > 64: two sub-chunks of 51
     (1, 3, 500, 128, 128, 32, torch.bfloat16),  # C = 32 at d = 128
     (2, 2, 260, 104, 120, 20, torch.bfloat16),  # ragged chunks, partial columns
 ]
@@ -79,7 +80,7 @@ def test_integer_inputs_exact(dev, B, H, T, dk, dv, C, dtype):
 # the results are exact integers, the same at every chunk size.
 LARGE_SCORE_CASES = [
     # B, Hq, Hkv, T, dk, dv, C, dtype
-    (1, 2, 2, 1000, 128, 128, 128, torch.bfloat16),      # eight-wave walk, chunks of 128
+    (1, 2, 2, 1000, 128, 128, 128, torch.bfloat16),      # chunks of 128 (run as two of 64)
     (1, 2, 2, 1000, 128, 128, 64, torch.bfloat16),       # double-buffered eight-wave walk
     (1, 2, 2, 500, 128, 128, 32, torch.bfloat16),
     (2, 2, 2, 700, 128, 128, 128, torch.float8_e4m3fn),  # E4M3 holds {-8..8} exactly
@@ -171,8 +172,25 @@ def test_fp32_chunks_over_64_with_state_and_workspace(dev):
     assert rel_err(np64(o), O_ref) <= 1e-5 and rel_err(np64(S), S_ref) <= 1e-5
 
 
-def test_fp32_chunks_over_64_refused_by_the_phase_calls(dev):
-    k = torch.zeros((1, 2, 300, 64), device=dev)
-    ws = torch.empty(lla.prefill_workspace_size(1, 2, 300, 64, 64, 128) // 4 + 4, device=dev)
-    with pytest.raises(lla.LlaError):
-        lla.prefill_segment_states(k, k, 128, ws)
+@pytest.mark.parametrize("C,dtype", [(128, torch.float32), (101, torch.float32), (101, torch.bfloat16)])
+def test_phases_at_chunks_over_64_equal_the_one_call(dev, C, dtype):
+    # chunks over 64 tokens run as two sub-chunks of c = ceil(C/2) in every
+    # call; segment s starts after s G c tokens (G = prefill_segment_chunks)
+    B, H, T, d = 1, 3, 6000, 64
+    q, k, v = (x.to(dev) for x in workloads.integers(B, H, T, d, d, seed=C, dtype=dtype))
+    G = lla.prefill_segment_chunks(B, H, T, d, d, C)
+    c = (C + 1) // 2
+    n_seg = -(-(-(-T // c)) // G)
+    assert n_seg > 1
+    S_a = lla.state_init(B, H, d, d, device=dev)
+    o_a = lla.prefill(q, k, v, S_a, chunk=C)
+    S_b = lla.state_init(B, H, d, d, device=dev)
+    ws = lla.prefill_segment_states(k, v, C, None)
+    lla.prefill_state_scan(S_b, T, C, ws)
+    o_b = lla.prefill_chunks(q, k, v, S_b, C, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, o_b) and torch.equal(S_a, S_b)
+    O_ref, S_ref, ck = oracle.recurrence(q.cpu(), k.cpu(), v.cpu(), ckpt_every=G * c, nthreads=3)
+    assert np.array_equal(np64(o_a), O_ref) and np.array_equal(np64(S_a), S_ref)
+    slots = np64(ws.view(B, H, n_seg, d, d))
+    assert np.array_equal(slots[:, :, 1:], ck[:, :, :n_seg - 1])

@@ -34,7 +34,8 @@ def test_kernel_grids_follow_the_plan():
     def segments(name):
         c = workloads.CONFIGS[name]
         G = lla.prefill_segment_chunks(c.B, c.H, c.T, c.dk, c.dv, c.C)
-        return c, math.ceil(math.ceil(c.T / c.C) / G)
+        run_chunk = c.C if c.C <= 64 else (c.C + 1) // 2  # chunks over 64 tokens run as two
+        return c, math.ceil(math.ceil(c.T / run_chunk) / G)
 
     c, n = segments("prefill_T8192")
     assert profiling.KERNELS["chunk_walk"][1] == c.B * c.H * n * 512       # one 8-wave group per segment
@@ -73,3 +74,20 @@ def test_kernel_names_match_in_both_trace_forms():
     assert profiling.matches("void lla::k_decode_group<__bf16, 128, 512, 16>(...)", "decode_group")
     # the general grouped kernel is another kernel
     assert not profiling.matches("void lla::k_decode_group_any<__bf16, 4, 16, 16>(...)", "decode_group")
+
+
+def test_kernels_sharing_a_name_and_grid_are_measured_in_separate_runs():
+    # the counters of a kernel are averaged over every dispatch of its name
+    # at its grid, so two measured kernels that match each other's names at
+    # the same grid must come from different runs
+    keys = sorted(profiling.KERNELS)
+    for i, a in enumerate(keys):
+        for b in keys[i + 1:]:
+            fa, ga, _, _, wa = profiling.KERNELS[a]
+            fb, gb, _, _, wb = profiling.KERNELS[b]
+            if ga != gb or wa == wb:
+                continue
+            clash = any(profiling.matches(f, b) for f in fa) or any(profiling.matches(f, a) for f in fb)
+            if clash:
+                assert (wa in profiling.DEFAULT_RUN) != (wb in profiling.DEFAULT_RUN), (a, b)
+    assert set(profiling.DEFAULT_RUN) | set(profiling.RUN_ALONE) == set(profiling.WORKLOADS)

@@ -3,8 +3,8 @@ key/value heads, sequence length, head dims, chunk size, input type, fresh
 prompt or not) drawn once from a fixed seed, each run through the C ABI on
 integer inputs and compared with the oracle bit for bit.  Every kernel
 variant the plan can pick is reached: the eight-wave double-buffered walk
-(d = 128, C <= 64), the eight-wave single-buffered walk (d = 128, C = 128),
-the four-wave walks (vector and element paths), one or several segments,
+(d = 128), the four-wave walks (vector and element paths), chunks of more
+than 64 tokens (run as two sub-chunks), one or several segments,
 grouped heads, the fused short-prompt route, bf16, fp32 and FP8 inputs.
 A second draw runs gaussian inputs from a gaussian state and holds every
 path to the floating-point bar on these shapes."""
