@@ -610,7 +610,7 @@ def bench_grouped(args, torch, lla, workloads, profiling):
         # (about 2 d t for token t)
         flops = B * Hkv * 2 * d * d * tc + B * H * (2 * d * d * tc + 2 * d * tc * (tc + 1) // 2 * 2)
         matrix = tc >= 8
-        kname = "k_tokens_grouped<bf16,128,64,4> (matrix cores)" if matrix else \
+        kname = "k_tokens_grouped_pipe<bf16> (matrix cores)" if matrix else \
             "k_decode_tokens<bf16> (fused decode steps)"
         r = hbm_roofline(kname, cbytes, ms_c, args.gap_ms,
                          profiling.stored_traffic("tokens_grouped") if tc == 16 else None,

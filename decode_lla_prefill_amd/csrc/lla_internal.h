@@ -83,8 +83,9 @@ hipError_t launch_decode_tokens(lla_dtype dtype, const void* q, const void* k, c
                                 bool zero_start, bool keep_state, hipStream_t st);
 // Short continuations with shared-state heads on the matrix cores (bf16 or
 // FP8 inputs, d in {64, 128}, T * group <= 64): one chunk of the walk per
-// key/value head (k_tokens_grouped).  Not the bits of T decode steps.  Used
-// from kGroupedMatrixMinTokens tokens on: below that the fused decode steps
+// key/value head (k_tokens_grouped; k_tokens_grouped_pipe at d = 128).  Not
+// the bits of T decode steps.  Used from kGroupedMatrixMinTokens tokens on:
+// below that the fused decode steps
 // are faster (their cost grows with T, this kernel's hardly does).
 constexpr int kGroupedMatrixMinTokens = 8;
 hipError_t launch_tokens_grouped(lla_dtype dtype, const void* q, const void* k, const void* v, int64_t BHkv,

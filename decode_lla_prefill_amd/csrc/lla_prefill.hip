@@ -1015,11 +1015,11 @@ __global__ __launch_bounds__(NW * kWave) void k_chunk_walk(
 // zero), with key s kept for row r while s <= r / G -- every kept entry lies
 // in the walk's lower-triangle tiles.  So the chunk's helpers run unchanged:
 // scores and mask (chunk_scores with the group's mask), O = P V + Q S_0
-// (chunk_output), then S_T = S_0 + K^T V (state_hop).  One workgroup per
-// key/value head and block of BV value columns, one value tile per wave, so
-// that two or more workgroups share a compute unit and one's state loads
-// overlap another's arithmetic (the scores, from all D key columns, are
-// computed by each block).
+// (chunk_output), then S_T = S_0 + K^T V (state_hop).  For d = 64 (this
+// kernel) one workgroup per key/value head, one value tile per wave, so that
+// several workgroups share a compute unit and one's state loads overlap
+// another's arithmetic; d = 128 takes the persistent k_tokens_grouped_pipe
+// below.
 // S enters Q S and P enters P V as bf16 high + low pairs, as in the walk, so
 // integers are exact under the walk's bounds and floats carry the walk's
 // error; the outputs are not the bits of T decode steps (the verify pass of
@@ -1109,6 +1109,132 @@ __global__ __launch_bounds__(NW * kWave) void k_tokens_grouped(
         }
     }
     state_regs_to_gmem<Cf>(Sb, Sacc, D, D, w, g, c16);
+}
+
+// The same continuation for d = 128, persistent and pipelined: one
+// eight-wave workgroup (all 128 value columns, wave w owns value tile w)
+// walks the key/value heads bh = blockIdx.x, blockIdx.x + gridDim.x, ...
+// While head bh is computed, the loads of the next head -- its state rows and
+// its Q, K and V rows, into registers -- are in flight.  The state moves
+// between global memory and LDS as 16-byte row pieces (coalesced, like the
+// decode step's), and between LDS and the accumulator layout inside the
+// workgroup.  One workgroup per state reads its Q and K rows once.  The
+// arithmetic per head is k_tokens_grouped's (the walk's chunk helpers), so
+// the bits are the same.
+constexpr int kGroupedPipeWGs = 256;  // workgroups of k_tokens_grouped_pipe (one per compute unit)
+
+template <typename In>
+__global__ __launch_bounds__(8 * kWave) void k_tokens_grouped_pipe(
+    const In* __restrict__ Q, const In* __restrict__ K, const In* __restrict__ V, float* __restrict__ S,
+    float* __restrict__ O, int64_t BHkv, int T, int G, int zero_start) {
+    constexpr int D = 128, NW = 8;
+    using Cf = WalkCfg<bf16, 64, D, D, NW>;
+    using Fr = typename Cf::Fr;
+    constexpr int NTH = Cf::NTH;
+    static_assert(Cf::NVW == 1 && Cf::ALL_WAVES, "one value tile per wave");
+    constexpr int KROWS = kDecodeTokensMax;     // key and value rows staged (T <= this)
+    constexpr int SV = D * D / 4 / NTH;          // 16-byte state pieces per thread
+    static_assert(SV * 4 * NTH == D * D, "the state splits evenly over the threads");
+    // Q, K, V and P tiles, then the fp32 state (D rows of stride SLD)
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Cf::WALK_BYTES + Cf::STATE_BYTES];
+    bf16* const Qs = reinterpret_cast<bf16*>(smem);
+    bf16* const Ks = Qs + Cf::K_OFF;
+    bf16* const Vs = Qs + Cf::V_OFF;
+    bf16* const Ps = Qs + Cf::P_OFF;
+    float* const Sst = reinterpret_cast<float*>(smem + Cf::WALK_BYTES);
+
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int R = T * G;  // query rows, row r = t G + j is token t of query head j
+    const int64_t q_elems = (int64_t)G * T * D;  // per key/value head
+    const int64_t stride = gridDim.x;
+
+    // Key and value rows past T stay zero for every head: rows KROWS.. are
+    // cleared here, rows T..KROWS-1 are written as zeros by every scatter.
+    for (int e = tid; e < (64 - KROWS) * D / 8; e += NTH) {
+        const int row = KROWS + e / (D / 8), c8 = 8 * (e % (D / 8));
+        *reinterpret_cast<u32x4*>(Ks + row * Cf::LK + c8) = u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(Vs + row * Cf::LV + c8) = u32x4{0u, 0u, 0u, 0u};
+    }
+
+    using TQ = Tile<bf16, 64, D, typename Cf::LQL, NTH, In>;
+    using TK = Tile<bf16, KROWS, D, typename Cf::LKL, NTH, In>;
+    using TV = Tile<bf16, KROWS, D, typename Cf::LVL, NTH, In>;
+    TQ tq;
+    TK tk;
+    TV tv;
+    tk.init(D, D, tid);
+    tv.init(D, D, tid);
+    u32x4 sp[SV];  // state piece n of this thread: row (tid + NTH n) / 32, columns 4 ((tid + NTH n) % 32) ..
+    // The next head's rows into registers.  Q vector n of this thread: tile
+    // row e / VPR, i.e. query row r, read from row (r % G) T + r / G of the
+    // head's [G][T][D] block.
+    auto gather = [&](int64_t bh) {
+        const rsrc_t rq = make_rsrc(Q + bh * q_elems, (uint32_t)(q_elems * sizeof(In)));
+#pragma unroll
+        for (int n = 0; n < TQ::NPT; ++n) {
+            const int e = tid + n * NTH, r = e / TQ::VPR, cv = e % TQ::VPR;
+            const uint32_t off = r < R ? (uint32_t)((((r % G) * T + r / G) * D + cv * TQ::VE) * sizeof(In)) : kOutside;
+            tq.r[n] = buf_load16(rq, off);
+        }
+        tk.gather(K + bh * (int64_t)T * D, D, T);
+        tv.gather(V + bh * (int64_t)T * D, D, T);
+        const rsrc_t rs = make_rsrc(S + bh * (int64_t)D * D, zero_start ? 0u : (uint32_t)(D * D * 4));
+#pragma unroll
+        for (int n = 0; n < SV; ++n) sp[n] = buf_load16(rs, (uint32_t)((tid + NTH * n) * 16));
+    };
+
+    const ScoreTiles<Cf> stiles(w);
+    auto head = [&](int64_t bh) {
+        const int64_t nx = bh + stride;
+        __syncthreads();  // the previous head's readers of the tiles, P and the state area are done
+        tq.scatter(Qs, tid);
+        tk.scatter(Ks, tid);
+        tv.scatter(Vs, tid);
+#pragma unroll
+        for (int n = 0; n < SV; ++n) {
+            const int e = tid + NTH * n;
+            *reinterpret_cast<u32x4*>(Sst + (e / (D / 4)) * Cf::SLD + 4 * (e % (D / 4))) = sp[n];
+        }
+        if (nx < BHkv) gather(nx);  // in flight during this head
+        __syncthreads();
+
+        f32x4 Sacc[1][Cf::NDT];
+        state_lds_to_regs<Cf>(Sacc, Sst, w, g, c16);
+        chunk_scores<Cf>(stiles, Qs, Ks, Ps, w, g, c16, NoHook(), G);
+        __syncthreads();  // P complete; every wave has its state slice
+        Fr Vf[1][Cf::NTS];
+        load_vfrags<Cf>(Vf, Vs, w, g, lane);
+        f32x4 Oacc[Cf::NT][1];
+        chunk_output<Cf>(Oacc, Sacc, Vf, Qs, Ps, w, g, c16);
+        state_hop<Cf>(Sacc, Vf, Ks, w, g, lane);
+
+        // Oacc[it][0] holds O[row 16 it + c16][value columns 16 w + 4g .. + 3]
+        const rsrc_t ro = make_rsrc(O + bh * q_elems, (uint32_t)(q_elems * 4));
+#pragma unroll
+        for (int it = 0; it < Cf::NT; ++it) {
+            const int r = 16 * it + c16;
+            const uint32_t off = r < R ? (uint32_t)((((r % G) * T + r / G) * D + 16 * w + 4 * g) * 4) : kOutside;
+            buf_store16(ro, off, Oacc[it][0]);
+        }
+        state_regs_to_lds<Cf>(Sst, Sacc, w, g, c16);
+        __syncthreads();
+        const rsrc_t rs = make_rsrc(S + bh * (int64_t)D * D, (uint32_t)(D * D * 4));
+#pragma unroll
+        for (int n = 0; n < SV; ++n) {
+            const int e = tid + NTH * n;
+            buf_store16(rs, (uint32_t)(e * 16),
+                        *reinterpret_cast<const f32x4*>(Sst + (e / (D / 4)) * Cf::SLD + 4 * (e % (D / 4))));
+        }
+    };
+    // The first head outside the loop, so that the compiler's wait counts
+    // for the prefetched registers need not merge the two ways they are
+    // loaded (before the loop, and by the previous head).
+    int64_t bh = blockIdx.x;
+    if (bh >= BHkv) return;
+    gather(bh);
+    head(bh);
+    for (bh += stride; bh < BHkv; bh += stride) head(bh);
 }
 
 // ---------------------------------------------------------------------------
@@ -1738,15 +1864,14 @@ static hipError_t launch_seg_t(const PrefillPlan& p, const void* K, const void* 
         }                                                                                  \
     } while (0)
 
-constexpr int kGroupedBV = 64;  // value columns per workgroup of k_tokens_grouped
 
 template <typename In>
 static hipError_t tokens_grouped_t(const void* q, const void* k, const void* v, int64_t BHkv, int T, int G,
                                    int d, float* S, float* o, int zero, hipStream_t st) {
     if (d == 128) {
-        constexpr int BV = kGroupedBV;
-        hipLaunchKernelGGL((k_tokens_grouped<In, 128, BV, BV / 16>), dim3((unsigned)(BHkv * (128 / BV))),
-                           dim3(BV / 16 * kWave), 0, st, (const In*)q, (const In*)k, (const In*)v, S, o, T, G, zero);
+        const int64_t wgs = BHkv < kGroupedPipeWGs ? BHkv : kGroupedPipeWGs;
+        hipLaunchKernelGGL((k_tokens_grouped_pipe<In>), dim3((unsigned)wgs), dim3(8 * kWave), 0, st, (const In*)q,
+                           (const In*)k, (const In*)v, S, o, BHkv, T, G, zero);
     } else {
         hipLaunchKernelGGL((k_tokens_grouped<In, 64, 64, 4>), dim3((unsigned)BHkv), dim3(4 * kWave), 0, st,
                            (const In*)q, (const In*)k, (const In*)v, S, o, T, G, zero);

@@ -88,10 +88,10 @@ KERNELS = {
                     ("lla_decode.hip", "lla_device.h"), "decode_B256"),
     "decode_group": (("k_decode_groupIDF16bLi128E", "k_decode_group<__bf16, 128,"), 256 * 8 * 512, "decode_group_B256_Hq32_Hkv8_traffic.txt",
                      ("lla_decode.hip", "lla_device.h"), "decode_B256_gqa"),
-    # 16-token continuations of the grouped states: one 4-wave workgroup per
-    # key/value head and 64 value columns
-    "tokens_grouped": (("k_tokens_groupedIDF16bLi128ELi64ELi4E", "k_tokens_grouped<__bf16, 128, 64, 4>"),
-                       256 * 8 * 2 * 256, "tokens_grouped_B256_Hq32_Hkv8_T16_traffic.txt",
+    # 16-token continuations of the grouped states: one persistent 8-wave
+    # workgroup per compute unit, walking the key/value heads
+    "tokens_grouped": (("k_tokens_grouped_pipeIDF16bE", "k_tokens_grouped_pipe<__bf16>"),
+                       256 * 512, "tokens_grouped_B256_Hq32_Hkv8_T16_traffic.txt",
                        PREFILL_SOURCES, "decode_B256_gqa_T16"),
     # the gated (decayed) state: the T=8192 prefill's walk and segment pass
     # (the plain kernels with the GATED flag), and the decode step.  The

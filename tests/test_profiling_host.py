@@ -50,8 +50,8 @@ def test_kernel_grids_follow_the_plan():
     assert profiling.KERNELS["decode_step"][1] == c.B * c.H * 512
     c = workloads.CONFIGS["decode_B256_gqa"]
     assert profiling.KERNELS["decode_group"][1] == c.B * c.kv_heads * 512
-    # two 64-column blocks per 128 x 128 state, four waves each
-    assert profiling.KERNELS["tokens_grouped"][1] == c.B * c.kv_heads * 2 * 256
+    # one persistent 8-wave workgroup per compute unit (2,048 states > 256)
+    assert profiling.KERNELS["tokens_grouped"][1] == min(c.B * c.kv_heads, 256) * 512
     # the gated kernels: the plain wide ones' grids (the same plan)
     assert profiling.KERNELS["gated_walk"][1] == profiling.KERNELS["chunk_walk"][1]
     assert profiling.KERNELS["gated_segment_states"][1] == profiling.KERNELS["segment_states"][1]
