@@ -104,11 +104,6 @@ struct PadLayout {
     __device__ __forceinline__ static int off(int row, int col) { return row * LD + col; }
 };
 
-// s_waitcnt immediate (gfx9 family) that waits until at most n vector memory
-// operations are outstanding and leaves the other counters alone: vmcnt in
-// bits 3:0 and 15:14, expcnt (7) in 6:4, lgkmcnt (15) in 11:8.
-constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-
 // ---- buffer (descriptor-based) global access ----------------------------------
 //
 // A buffer descriptor covers [base, base + bytes); a load whose offset falls
