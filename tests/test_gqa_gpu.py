@@ -312,3 +312,28 @@ def test_gqa_short_prompt_integers_exact_at_the_route_boundary(dev, Hq, Hkv, T):
     O_z, S_zr = oracle.grouped_recurrence(q, k, v, nthreads=8)
     assert np.array_equal(np64(o_z), O_z)
     assert np.array_equal(np64(S_z), S_zr)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,dtype", [(75, 16, 4, 12, torch.bfloat16), (130, 8, 4, 16, torch.float8_e4m3fn),
+                                              (3, 16, 2, 8, torch.bfloat16)])
+def test_gqa_matrix_core_continuation_walks_several_heads_per_workgroup(dev, B, Hq, Hkv, T, dtype):
+    """At d = 128 the matrix-core continuation runs 256 persistent workgroups
+    that walk the key/value heads (300 and 520 heads here: two or three per
+    workgroup, the next head's loads in flight during the current one; 6
+    heads: one each): integers exact against the oracle, from a given state
+    and fresh (the state never read)."""
+    print("gqa matrix-core continuation, several heads per workgroup", B, Hq, Hkv, T, dtype, flush=True)
+    d = 128
+    q, k, v = workloads.integers(B, Hq, T, d, d, seed=B + T, Hkv=Hkv, dtype=dtype)
+    S0 = torch.randint(-300, 301, (B, Hkv, d, d), generator=torch.Generator().manual_seed(B)).float()
+    o, S = _run_prefill(q, k, v, S0, 64, dev)
+    O_ref, S_ref = oracle.grouped_recurrence(q, k, v, S0, nthreads=8)
+    assert np.array_equal(np64(o), O_ref)
+    assert np.array_equal(np64(S), S_ref)
+    S_z = torch.full((B, Hkv, d, d), float("nan"), device=dev)  # fresh prompt: S never read
+    o_z = lla.prefill(q.to(dev).contiguous(), k.to(dev).contiguous(), v.to(dev).contiguous(), S_z,
+                      chunk=64, zero_state=True)
+    torch.cuda.synchronize()
+    O_z, S_zr = oracle.grouped_recurrence(q, k, v, nthreads=8)
+    assert np.array_equal(np64(o_z), O_z)
+    assert np.array_equal(np64(S_z), S_zr)
