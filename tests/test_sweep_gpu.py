@@ -79,7 +79,25 @@ def _draw_decode_cases(n, seed):
 DECODE_CASES = _draw_decode_cases(24, 424242)
 
 
-@pytest.mark.parametrize("B,Hq,dk,dv,G,dtype", DECODE_CASES)
+def _draw_grouped_any_cases(n, seed):
+    """Shared-state heads at any group size and head dims: the square
+    kernels past one LDS batch of 16 query rows, and the general grouped
+    kernel (4 or 1 value columns per thread)."""
+    rng = np.random.RandomState(seed)
+    cases = []
+    for _ in range(n):
+        dtype = DTYPES[rng.randint(3)]
+        G = int(rng.choice([2, 3, 5, 8, 17, 24, 40]))
+        dk = int(rng.choice([128, 64, 1, 7, 40, 96, 128]))
+        dv = dk if rng.rand() < 0.4 else int(rng.choice([128, 100, 64, 12, 3, 1]))
+        cases.append((int(rng.choice([1, 2, 5])), G * int(rng.choice([1, 2])), dk, dv, G, dtype))
+    return cases
+
+
+DECODE_CASES_ANY = _draw_grouped_any_cases(16, 77077)
+
+
+@pytest.mark.parametrize("B,Hq,dk,dv,G,dtype", DECODE_CASES + DECODE_CASES_ANY)
 def test_sweep_decode_steps_integers_exact(B, Hq, dk, dv, G, dtype):
     """Four decode steps in a row from an integer state, exact against the oracle."""
     dev = need_gpu()
