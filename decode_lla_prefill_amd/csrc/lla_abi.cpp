@@ -172,9 +172,8 @@ const char* lla_status_string(lla_status s) {
         case LLA_ERR_SHAPE: return "a size is out of range";
         case LLA_ERR_DTYPE: return "unknown dtype";
         case LLA_ERR_UNSUPPORTED:
-            return "unsupported request (unknown option bits, "
-                   "a keep-state prefill off the fused short-prompt route, or a gated prefill option "
-                   "other than the zero state)";
+            return "unsupported request (unknown option bits, or a gated prefill option other than "
+                   "the zero state)";
         case LLA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
         case LLA_ERR_ALIAS: return "an output overlaps another buffer";
         case LLA_ERR_WORKSPACE: return "workspace missing or too small";
@@ -262,10 +261,10 @@ lla_status prefill_impl(const void* Q, const void* K, const void* V, int dt_raw,
     const lla_dtype dtype = (lla_dtype)dt_raw;  // checked
     hipStream_t s = (hipStream_t)stream;
     const bool fused = lla::decode_tokens_fit(T, (int)dk, (int)dv, p.group);
-    if (keep && T > 0 && !fused) return LLA_ERR_UNSUPPORTED;  // the verify pass runs on the fused route only
     if (T == 0)  // S_T = S_0: untouched, or zero for a fresh prompt (never written with KEEP_STATE)
         return zero && !keep ? device_status(lla::launch_fill_zero(S, p.BH * dk * dv, s)) : LLA_OK;
     p.zero_start = zero;
+    p.keep = keep;
     if (fused) {  // a short prompt
         // Several query heads per state (bf16 or FP8) and at least 8 tokens:
         // one chunk on the matrix cores; otherwise, and for a verify pass,
@@ -355,8 +354,6 @@ lla_status lla_prefill_noalloc(const void* Q, const void* K, const void* V, lla_
     lla_status st = check_prefill(b, true, true, true, true, false, raw_enum(dtype), B, Heads{Hq, Hkv}, T, dk,
                                   dv, C, p);
     if (st != LLA_OK) return st;
-    if ((flags & LLA_PREFILL_KEEP_STATE) && T > 0 && !lla::decode_tokens_fit(T, (int)dk, (int)dv, p.group))
-        return LLA_ERR_UNSUPPORTED;
     const size_t need = ws_bytes_for(p);
     if (need > lla::kNoAllocScratchBytes) return LLA_ERR_SCRATCH;
     float* ws = nullptr;

@@ -47,6 +47,7 @@ struct PrefillPlan {
     int64_t n_seg;  // segments per sequence = ceil(n_c / G)
     bool vec;     // 16-byte vector loads possible (dk, dv multiples of one vector)
     bool zero_start;  // S_0 = 0: S is written (S_T) but not read
+    bool keep;        // the verify pass: S is read (unless zero_start) but never written
     lla_dtype dtype;
 };
 

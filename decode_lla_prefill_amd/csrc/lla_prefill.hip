@@ -893,7 +893,7 @@ template <typename In, int CT, int D, int BV, bool VEC, int NW = kWaves>
 __global__ __launch_bounds__(NW * kWave) void k_chunk_walk(
     const In* __restrict__ Q, const In* __restrict__ K, const In* __restrict__ V,
     float* __restrict__ S, float* __restrict__ O, const float* __restrict__ ws, int64_t T_len,
-    int dk, int dv, int C, int64_t G, int64_t n_seg, int n_vb, int group, int zero_start) {
+    int dk, int dv, int C, int64_t G, int64_t n_seg, int n_vb, int group, int zero_start, int keep) {
     using T = typename Compute<In>::type;
     using Cf = WalkCfg<T, CT, D, BV, NW>;
     using Fr = typename Cf::Fr;
@@ -992,13 +992,16 @@ __global__ __launch_bounds__(NW * kWave) void k_chunk_walk(
         n_prev = nrows;
 
         // State hop S_{c+1} = S_c + K_c^T V_c (not needed after the last
-        // chunk of a segment whose successor starts from the scanned state).
-        if (c + 1 < c1 || last_seg) state_hop<Cf>(Sacc, Vf, Ks, w, g, lane);
+        // chunk of a segment whose successor starts from the scanned state,
+        // nor after the last one when S_T is not kept).
+        if (c + 1 < c1 || (last_seg && !keep)) state_hop<Cf>(Sacc, Vf, Ks, w, g, lane);
         __syncthreads();
     }
     if (c1 > c0) store_out<Cf, VEC>(Ob, Oacc, t_prev, n_prev, nv, dv, w, g, c16);
 
-    if (last_seg && bq % group == 0) {  // one writer per group (the loop ended with a barrier)
+    // S_T: one writer per group (the loop ended with a barrier); none for a
+    // verify pass, which leaves S as it was
+    if (last_seg && bq % group == 0 && !keep) {
         state_regs_to_lds<Cf>(Sst, Sacc, w, g, c16);
         __syncthreads();
         state_lds_to_gmem<Cf>(S + bh * dkdv + v0, Sst, dk, dv, nv, tid);
@@ -1267,7 +1270,7 @@ template <int CT, typename In, bool GATED = false>
 __global__ __launch_bounds__(kWideWaves * kWave) void k_chunk_walk_wide(
     const In* __restrict__ Q, const In* __restrict__ K, const In* __restrict__ V,
     float* __restrict__ S, float* __restrict__ O, const float* __restrict__ ws, int64_t T_len,
-    int dk, int dv, int C, int64_t G, int64_t n_seg, int group, int zero_start,
+    int dk, int dv, int C, int64_t G, int64_t n_seg, int group, int zero_start, int keep,
     const float* __restrict__ gate) {
     using Cf = WideCfg<CT>;
     using Fr = typename Cf::Fr;
@@ -1400,7 +1403,7 @@ __global__ __launch_bounds__(kWideWaves * kWave) void k_chunk_walk_wide(
             chunk_output<Cf>(Oacc, Sacc, Vf, Qs, Ps, w, g, c16, load_hook);
         t_prev = c * C;
         n_prev = rows_of(c);
-        if (c + 1 < c1 || last_seg) {
+        if (c + 1 < c1 || (last_seg && !keep)) {
             if constexpr (GATED)
                 state_hop_gated<Cf>(Sacc, Vf, Ks, Bs, w, g, lane);
             else
@@ -1410,7 +1413,7 @@ __global__ __launch_bounds__(kWideWaves * kWave) void k_chunk_walk_wide(
     }
     store_out<Cf, true>(Ob, Oacc, t_prev, n_prev, dv, dv, w, g, c16);
 
-    if (last_seg && bq % group == 0)  // one writer per group
+    if (last_seg && bq % group == 0 && !keep)  // one writer per group; none for a verify pass
         state_regs_to_gmem<Cf>(S + bh * dkdv, Sacc, dk, dv, w, g, c16);
 }
 
@@ -1785,7 +1788,7 @@ static hipError_t launch_walk_t(const PrefillPlan& p, const void* Q, const void*
             hipLaunchKernelGGL((k_chunk_walk_wide<CT, In>), dim3((unsigned)(p.BHq * p.n_seg)), dim3(kWideWaves * kWave), 0, st,
                                (const In*)Q, (const In*)K, (const In*)V, S, O,
                                (const float*)(p.use_ws ? ws : nullptr), p.T, p.dk, p.dv, p.C, p.G,
-                               p.n_seg, p.group, (int)p.zero_start, (const float*)nullptr);
+                               p.n_seg, p.group, (int)p.zero_start, (int)p.keep, (const float*)nullptr);
             return hipGetLastError();
         }
     }
@@ -1795,11 +1798,11 @@ static hipError_t launch_walk_t(const PrefillPlan& p, const void* Q, const void*
     if (p.vec)
         hipLaunchKernelGGL((k_chunk_walk<In, CT, D, BV, true>), dim3((unsigned)grid), dim3(kThreads), 0,
                            st, (const In*)Q, (const In*)K, (const In*)V, S, O, wsr, p.T,
-                           p.dk, p.dv, p.C, p.G, p.n_seg, p.n_vb, p.group, (int)p.zero_start);
+                           p.dk, p.dv, p.C, p.G, p.n_seg, p.n_vb, p.group, (int)p.zero_start, (int)p.keep);
     else
         hipLaunchKernelGGL((k_chunk_walk<In, CT, D, BV, false>), dim3((unsigned)grid), dim3(kThreads), 0,
                            st, (const In*)Q, (const In*)K, (const In*)V, S, O, wsr, p.T,
-                           p.dk, p.dv, p.C, p.G, p.n_seg, p.n_vb, p.group, (int)p.zero_start);
+                           p.dk, p.dv, p.C, p.G, p.n_seg, p.n_vb, p.group, (int)p.zero_start, (int)p.keep);
     return hipGetLastError();
 }
 
@@ -1934,7 +1937,7 @@ static hipError_t launch_gated_walk_t(const PrefillPlan& p, const void* Q, const
             hipLaunchKernelGGL((k_chunk_walk_wide<CT, In, true>), dim3((unsigned)(p.BHq * p.n_seg)),
                                dim3(kWideWaves * kWave), 0, st, (const In*)Q, (const In*)K, (const In*)V, S, O,
                                (const float*)(p.use_ws ? ws : nullptr), p.T, p.dk, p.dv, p.C, p.G, p.n_seg, 1,
-                               (int)p.zero_start, gate);
+                               (int)p.zero_start, 0, gate);
             return hipGetLastError();
         }
     }

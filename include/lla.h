@@ -85,8 +85,7 @@ typedef enum {
     LLA_ERR_SHAPE = 2,       /* a size is out of range */
     LLA_ERR_DTYPE = 3,       /* unknown dtype */
     LLA_ERR_UNSUPPORTED = 4, /* valid request the library does not handle: unknown option bits,
-                                LLA_PREFILL_KEEP_STATE off the fused short-prompt route or
-                                on a gated prefill */
+                                LLA_PREFILL_KEEP_STATE on a gated prefill */
     LLA_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned (a gate: 4-byte) */
     LLA_ERR_ALIAS = 6,       /* an output overlaps an input, another output or the workspace */
     LLA_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than lla_prefill_workspace_size() */
@@ -253,10 +252,12 @@ lla_status lla_prefill_gqa(const void *Q, const void *K, const void *V, lla_dtyp
  *     calcul", on speculative decoding adding tokens per decode iteration):
  *     the T draft tokens' outputs o_1..o_T are computed from S_0 and S keeps
  *     S_0, so that lla_state_commit can then advance it by the accepted
- *     prefix only.  Runs on the fused short-prompt route (1 <= T <= 16,
- *     dk = dv in {64, 128}, T * G <= 64 with shared-state heads), where o_t
- *     equals what t decode steps give, bit for bit; other shapes return
- *     LLA_ERR_UNSUPPORTED.  With T = 0 nothing is written.
+ *     prefix only.  On the fused short-prompt route (1 <= T <= 16,
+ *     dk = dv in {64, 128}, T * G <= 64 with shared-state heads) o_t equals
+ *     what t decode steps give, bit for bit; other shapes take the chunked
+ *     path, whose outputs are those of the same call without the option
+ *     (the prefill's numerics).  With LLA_PREFILL_ZERO_STATE too, S is neither
+ *     read nor written; with T = 0 nothing is written.
  */
 #define LLA_PREFILL_KEEP_STATE 2u
 

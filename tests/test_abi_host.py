@@ -366,16 +366,18 @@ KEEP_STATE = 2
 
 @pytest.mark.parametrize("change", [dict(T=17), dict(dk=96, dv=96), dict(dk=64, dv=128), dict(T=16, H=8)])
 @pytest.mark.parametrize("flags", [KEEP_STATE, KEEP_STATE | ZERO_STATE])
-def test_keep_state_runs_on_the_fused_route_only(lib, change, flags):
-    # a verify pass needs 1 <= T <= 16, dk = dv in {64, 128} and T * G <= 64;
-    # refused before any HIP call otherwise
+def test_keep_state_is_checked_like_any_prefill_off_the_fused_route(lib, change, flags):
+    # a verify pass off the fused short-prompt route (T > 16, other head
+    # dims, T * G > 64) takes the chunked path: the usual checks decide
+    # (here a NULL q), nothing refuses the option
     b = Bufs(T=4, dk=128, dv=128)
     Hq, Hkv = (32, 4) if "H" in change else (2, 2)  # T * G = 16 * 8 = 128 > 64
     for key, val in change.items():
         if key != "H":
             setattr(b, key, val)
-    assert lib.lla_prefill_ex(*_ex_args(b, Hq, Hkv, flags)) == E_UNSUP
-    assert lib.lla_prefill_noalloc(*_noalloc_args(b, Hq, Hkv, flags)) == E_UNSUP
+    b.q = None
+    assert lib.lla_prefill_ex(*_ex_args(b, Hq, Hkv, flags)) == E_NULL
+    assert lib.lla_prefill_noalloc(*_noalloc_args(b, Hq, Hkv, flags)) == E_NULL
 
 
 def test_keep_state_with_an_empty_prompt_is_a_noop(lib):

@@ -2,9 +2,11 @@
 k draft tokens with LLA_PREFILL_KEEP_STATE gives every draft token's output
 and leaves the state as it was; lla_state_commit then advances each
 sequence's state by its accepted prefix m (0..k, read on the device).
-Together they equal m decode steps bit for bit -- outputs of all k tokens,
-state after the commit -- and, on integer inputs, the oracle's recurrence
-exactly."""
+On the fused short-prompt route they equal m decode steps bit for bit --
+outputs of all k tokens, state after the commit -- and, on integer inputs,
+the oracle's recurrence exactly.  Longer drafts and other shapes run the
+chunked prefill without its state write: the prefill's outputs, the same
+commit."""
 import numpy as np
 import pytest
 import torch
@@ -121,3 +123,57 @@ def test_commit_of_longer_drafts_and_odd_head_dims():
     for b, m in enumerate([40, 17, 0]):
         _, S_ref = oracle.recurrence(q[b:b + 1, :, :m], kk[b:b + 1, :, :m], v[b:b + 1, :, :m], S0[b:b + 1])
         assert np.array_equal(np64(S[b:b + 1]), S_ref), b
+
+
+# Verify passes off the fused short-prompt route run the chunked prefill
+# without its final state write: longer drafts, other head dims, T * G > 64.
+CHUNKED_CASES = [
+    # B, Hq, Hkv, k (draft tokens), dk, dv, C, dtype
+    (3, 2, 2, 40, 64, 64, 64, torch.bfloat16),      # one segment: the walk reads S itself
+    (2, 4, 2, 24, 128, 128, 64, torch.bfloat16),    # shared-state heads, T * G = 48 > 16 tokens
+    (1, 32, 4, 16, 128, 128, 64, torch.bfloat16),   # T * G = 128 > 64
+    (2, 3, 3, 30, 40, 24, 16, torch.float32),       # other head dims, several chunks
+    (1, 2, 2, 3000, 128, 128, 128, FP8),            # several segments (workspace), C = 128
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,k,dk,dv,C,dtype", CHUNKED_CASES)
+def test_chunked_verify_pass_leaves_the_state_and_commits_exactly(B, Hq, Hkv, k, dk, dv, C, dtype):
+    """The outputs equal those of the same prefill without the option (bit
+    for bit) and the oracle's (integers, exact); S is not written; the commit
+    of each sequence's accepted prefix is exact against the oracle."""
+    dev = need_gpu()
+    print("speculative chunked verify", B, Hq, Hkv, k, dk, dv, C, dtype, flush=True)
+    q, kk, v = workloads.integers(B, Hq, k, dk, dv, seed=1000 + k, lo=-1, hi=1, dtype=dtype, Hkv=Hkv)
+    S0 = torch.randint(-20, 21, (B, Hkv, dk, dv), generator=torch.Generator().manual_seed(k)).float()
+    qd, kd, vd = (x.to(dev) for x in (q, kk, v))
+    S = S0.to(dev).clone()
+    o = lla.prefill(qd, kd, vd, S, chunk=C, keep_state=True)
+    S_plain = S0.to(dev).clone()
+    o_plain = lla.prefill(qd, kd, vd, S_plain, chunk=C)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_plain)
+    assert np.array_equal(np64(S), S0.double().numpy())  # the verify pass wrote nothing
+    O_ref, _ = oracle.grouped_recurrence(q, kk, v, S0, nthreads=8)
+    assert np.array_equal(np64(o), O_ref)
+    accepted = [(5 * b + 3) % (k + 1) for b in range(B)]
+    lla.state_commit(kd, vd, S, torch.tensor(accepted, dtype=torch.int32, device=dev))
+    torch.cuda.synchronize()
+    for b, m in enumerate(accepted):
+        _, S_ref = oracle.grouped_recurrence(q[b:b + 1, :, :m], kk[b:b + 1, :, :m], v[b:b + 1, :, :m],
+                                             S0[b:b + 1], nthreads=4)
+        assert np.array_equal(np64(S[b:b + 1]), S_ref), b
+
+
+def test_chunked_verify_pass_of_a_fresh_prompt_reads_and_writes_nothing():
+    """KEEP_STATE with ZERO_STATE off the fused route: outputs of the fresh
+    prompt, S (NaN here) neither read nor written."""
+    dev = need_gpu()
+    B, H, k, d = 1, 4, 700, 64
+    q, kk, v = (x.to(dev) for x in workloads.integers(B, H, k, d, d, seed=77))
+    S = torch.full((B, H, d, d), float("nan"), device=dev)
+    o = lla.prefill(q, kk, v, S, chunk=64, zero_state=True, keep_state=True)
+    torch.cuda.synchronize()
+    O_ref, _ = oracle.recurrence(q.cpu(), kk.cpu(), v.cpu(), nthreads=4)
+    assert np.array_equal(np64(o), O_ref)
+    assert torch.isnan(S).all()
