@@ -176,3 +176,45 @@ def test_graph_replays_equal_eager_calls_gated(T, d, C):
         assert torch.equal(pre.out, o_ref), r
         assert torch.equal(dec.out, od_ref), r
         assert torch.equal(S, S_ref), r
+
+
+def test_graph_replays_equal_eager_calls_grouped_continuation():
+    """A captured 16-token continuation of grouped states on the matrix
+    cores (the persistent kernel: 320 key/value heads, so workgroups walk
+    more than one), replayed from a reset state, equals the eager call."""
+    dev = need_gpu()
+    B, Hq, Hkv, T, d = 80, 16, 4, 16, 128
+    q = torch.empty((B, Hq, T, d), dtype=torch.bfloat16, device=dev)
+    k, v = (torch.empty((B, Hkv, T, d), dtype=torch.bfloat16, device=dev) for _ in range(2))
+    S0 = torch.empty((B, Hkv, d, d), device=dev)
+    S = torch.empty_like(S0)
+    cont = lla.PreparedPrefill(q, k, v, S, 64)
+
+    def fill(seed):
+        g = torch.Generator(device=dev).manual_seed(seed)
+        for t in (q, k, v):
+            t.copy_(torch.randn(t.shape, generator=g, device=dev).mul_(d ** -0.5).to(torch.bfloat16))
+        S0.copy_(torch.randn(S0.shape, generator=g, device=dev))
+        S.copy_(S0)
+
+    fill(0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        cont()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cont()
+    torch.cuda.synchronize()
+    for r in range(1, 5):
+        print("graph replay, grouped continuation", r, flush=True)
+        fill(r)
+        S_ref = S0.clone()
+        o_ref = lla.prefill(q.clone(), k.clone(), v.clone(), S_ref, chunk=64)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(cont.out, o_ref), r
+        assert torch.equal(S, S_ref), r
