@@ -24,7 +24,8 @@ __all__ = [
     "prefill_workspace_size", "prefill_gqa_workspace_size", "prefill_segment_chunks",
     "prefill_segment_states",
     "prefill_state_scan", "prefill_chunks", "prefill_noalloc", "state_commit", "PreparedPrefill",
-    "PreparedDecode",
+    "PreparedDecode", "prefill_gated_workspace_size", "prefill_gated", "decode_step_gated",
+    "state_commit_gated", "PreparedGatedPrefill", "PreparedGatedDecode",
     "EXPORTS",
 ]
 
@@ -39,7 +40,8 @@ EXPORTS = ("lla_status_string", "lla_last_device_error", "lla_state_init",
            "lla_prefill_segment_states", "lla_prefill_state_scan", "lla_prefill_chunks",
            "lla_decode_step", "lla_prefill_gqa_workspace_size", "lla_prefill_gqa",
            "lla_decode_step_gqa", "lla_prefill_ex", "lla_prefill_noalloc", "lla_state_commit",
-           "lla_prefill_gated_workspace_size", "lla_prefill_gated", "lla_decode_step_gated")
+           "lla_prefill_gated_workspace_size", "lla_prefill_gated", "lla_decode_step_gated",
+           "lla_state_commit_gated")
 PREFILL_ZERO_STATE = 1  # lla_prefill_ex: start from S_0 = 0 without reading S
 PREFILL_KEEP_STATE = 2  # lla_prefill_ex: read S, do not write it (verify pass of draft tokens)
 
@@ -110,6 +112,8 @@ def library():
         lib.lla_prefill_gated.restype = st
         lib.lla_decode_step_gated.argtypes = [vp, vp, vp, vp, ci, i64, i64, i64, i64, vp, vp, vp]
         lib.lla_decode_step_gated.restype = st
+        lib.lla_state_commit_gated.argtypes = [vp, vp, vp, ci, i64, i64, i64, i64, i64, vp, vp, vp]
+        lib.lla_state_commit_gated.restype = st
         _lib = lib
     return _lib
 
@@ -261,11 +265,14 @@ def prefill_gated_workspace_size(B, H, T, dk, dv, chunk) -> int:
     return int(library().lla_prefill_gated_workspace_size(B, H, T, dk, dv, chunk))
 
 
-def prefill_gated(q, k, v, gate, state, chunk: int, out=None, workspace=None, zero_state: bool = False):
+def prefill_gated(q, k, v, gate, state, chunk: int, out=None, workspace=None, zero_state: bool = False,
+                  keep_state: bool = False):
     """Prefill with a decayed state (lla_prefill_gated): ``S_t = g_t S_{t-1}
     + k_t v_t^T``, ``o_t = S_t^T q_t``, one gate per (b,h) and token.
     ``gate``: fp32 [B,H,T]; q, k, v: [B,H,T,*] (one query head per state).
-    Returns o [B,H,T,dv] fp32; ``state`` goes S_0 -> S_T in place."""
+    Returns o [B,H,T,dv] fp32; ``state`` goes S_0 -> S_T in place
+    (``keep_state``: a verify pass, ``state`` not written; then
+    :func:`state_commit_gated`)."""
     lib = library()
     B, Hq, Hkv, T, dk, dv = _qkv_shape(q, k, v)
     if Hq != Hkv:
@@ -282,9 +289,10 @@ def prefill_gated(q, k, v, gate, state, chunk: int, out=None, workspace=None, ze
         _need(workspace, "workspace")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _same_device(q.device, gate=gate, state=state, out=out, workspace=workspace)
+    flags = (PREFILL_ZERO_STATE if zero_state else 0) | (PREFILL_KEEP_STATE if keep_state else 0)
     _check(lib.lla_prefill_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _dtype_code(q), B, Hq, T, dk, dv, chunk,
-                                 PREFILL_ZERO_STATE if zero_state else 0, _ptr(state), _ptr(out), _ptr(workspace),
-                                 ws_bytes, _stream(q)), "lla_prefill_gated")
+                                 flags, _ptr(state), _ptr(out), _ptr(workspace), ws_bytes, _stream(q)),
+           "lla_prefill_gated")
     return out
 
 
@@ -304,12 +312,8 @@ def prefill_noalloc(q, k, v, state, chunk: int, out=None, zero_state: bool = Fal
     return out
 
 
-def state_commit(k, v, state, accepted=None):
-    """After a verify pass (``prefill(..., keep_state=True)``): ``state`` +=
-    sum over the first m_b tokens of k_t v_t^T for every sequence b, m_b =
-    ``accepted[b]`` (a device int32 tensor [B]; None: all T), with the decode
-    step's arithmetic (lla_state_commit).  k, v: [B, Hkv, T, d]."""
-    lib = library()
+def _commit_args(k, v, state, accepted):
+    """Checks the buffers of a commit; returns (B, H, T, dk, dv)."""
     _need(k, "k", ndim=4)
     _need(v, "v", dtype=k.dtype, ndim=4)
     B, H, T, dk = k.shape
@@ -322,8 +326,34 @@ def state_commit(k, v, state, accepted=None):
         if accepted.shape[0] != B:
             raise ValueError("accepted has %d entries, expected %d" % (accepted.shape[0], B))
     _same_device(k.device, v=v, state=state, accepted=accepted)
+    return B, H, T, dk, dv
+
+
+def state_commit(k, v, state, accepted=None):
+    """After a verify pass (``prefill(..., keep_state=True)``): ``state`` +=
+    sum over the first m_b tokens of k_t v_t^T for every sequence b, m_b =
+    ``accepted[b]`` (a device int32 tensor [B]; None: all T), with the decode
+    step's arithmetic (lla_state_commit).  k, v: [B, Hkv, T, d]."""
+    lib = library()
+    B, H, T, dk, dv = _commit_args(k, v, state, accepted)
     _check(lib.lla_state_commit(_ptr(k), _ptr(v), _dtype_code(k), B, H, T, dk, dv, _ptr(accepted),
                                 _ptr(state), _stream(k)), "lla_state_commit")
+    return state
+
+
+def state_commit_gated(k, v, gate, state, accepted=None):
+    """After a gated verify pass (``prefill_gated(..., keep_state=True)``):
+    for every sequence b and its first m_b tokens in order, ``state = g_t
+    state + k_t v_t^T`` with the gated decode step's arithmetic
+    (lla_state_commit_gated).  k, v: [B, H, T, d]; gate: fp32 [B, H, T]."""
+    lib = library()
+    B, H, T, dk, dv = _commit_args(k, v, state, accepted)
+    _need(gate, "gate", dtype=torch.float32, ndim=3)
+    if tuple(gate.shape) != (B, H, T):
+        raise ValueError("gate shape %s, expected %s" % (tuple(gate.shape), (B, H, T)))
+    _same_device(k.device, gate=gate)
+    _check(lib.lla_state_commit_gated(_ptr(k), _ptr(v), _ptr(gate), _dtype_code(k), B, H, T, dk, dv,
+                                      _ptr(accepted), _ptr(state), _stream(k)), "lla_state_commit_gated")
     return state
 
 
@@ -535,10 +565,10 @@ class PreparedGatedPrefill:
         self._keep = (q, k, v, gate, state, self.out, workspace)  # the buffers behind the addresses
         self._device = q.device
 
-    def __call__(self, zero_state: bool = False):
+    def __call__(self, zero_state: bool = False, keep_state: bool = False):
         st = torch.cuda.current_stream(self._device).cuda_stream
-        _check(self._fn(*self._head, PREFILL_ZERO_STATE if zero_state else 0, *self._tail, st),
-               "lla_prefill_gated")
+        flags = (PREFILL_ZERO_STATE if zero_state else 0) | (PREFILL_KEEP_STATE if keep_state else 0)
+        _check(self._fn(*self._head, flags, *self._tail, st), "lla_prefill_gated")
         return self.out
 
 

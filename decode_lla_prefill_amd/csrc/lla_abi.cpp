@@ -172,8 +172,7 @@ const char* lla_status_string(lla_status s) {
         case LLA_ERR_SHAPE: return "a size is out of range";
         case LLA_ERR_DTYPE: return "unknown dtype";
         case LLA_ERR_UNSUPPORTED:
-            return "unsupported request (unknown option bits, or a gated prefill option other than "
-                   "the zero state)";
+            return "unsupported request (unknown option bits)";
         case LLA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
         case LLA_ERR_ALIAS: return "an output overlaps another buffer";
         case LLA_ERR_WORKSPACE: return "workspace missing or too small";
@@ -317,6 +316,31 @@ lla_status decode_impl(const void* q, const void* k, const void* v, int dt_raw, 
     return device_status(lla::launch_decode_step(dtype, q, k, v, BHkv, (int)dk, (int)dv, S, o, s));
 }
 
+// lla_state_commit and lla_state_commit_gated (gate non-null only for the latter).
+lla_status commit_impl(const void* K, const void* V, const float* gate, bool gated, int dt_raw, int64_t B,
+                       int64_t H, int64_t T, int64_t dk, int64_t dv, const int32_t* accepted, float* S,
+                       void* stream) {
+    lla_status st = check_sizes(B, H, T, dk, dv, -1);
+    if (st != LLA_OK) return st;
+    if (!known_dtype(dt_raw)) return LLA_ERR_DTYPE;
+    if (!S || (T > 0 && (!K || !V || (gated && !gate)))) return LLA_ERR_NULL;
+    if (!aligned16(S) || (T > 0 && (!aligned16(K) || !aligned16(V))) || (accepted && !aligned16(accepted)) ||
+        (gated && T > 0 && !aligned4(gate)))
+        return LLA_ERR_ALIGN;
+    if (T == 0) return LLA_OK;
+    const int64_t es = elem_size((lla_dtype)dt_raw);
+    const Span ss = span(S, B * H * dk * dv * 4), sk = span(K, B * H * T * dk * es),
+               sv = span(V, B * H * T * dv * es), sa = span(accepted, accepted ? B * 4 : 0),
+               sg = span(gated ? gate : nullptr, gated ? B * H * T * 4 : 0);
+    if (overlap(ss, sk) || overlap(ss, sv) || overlap(ss, sa) || overlap(ss, sg)) return LLA_ERR_ALIAS;
+    hipStream_t s = (hipStream_t)stream;
+    if (gated)
+        return device_status(lla::launch_state_commit_gated((lla_dtype)dt_raw, K, V, gate, accepted, B * H, (int)H,
+                                                            (int)T, (int)dk, (int)dv, S, s));
+    return device_status(lla::launch_state_commit((lla_dtype)dt_raw, K, V, accepted, B * H, (int)H, (int)T,
+                                                  (int)dk, (int)dv, S, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -368,20 +392,13 @@ lla_status lla_prefill_noalloc(const void* Q, const void* K, const void* V, lla_
 lla_status lla_state_commit(const void* K, const void* V, lla_dtype dtype, int64_t B, int64_t H,
                             int64_t T, int64_t dk, int64_t dv, const int32_t* accepted, float* S,
                             void* stream) {
-    lla_status st = check_sizes(B, H, T, dk, dv, -1);
-    if (st != LLA_OK) return st;
-    const int dt_raw = raw_enum(dtype);
-    if (!known_dtype(dt_raw)) return LLA_ERR_DTYPE;
-    if (!S || (T > 0 && (!K || !V))) return LLA_ERR_NULL;
-    if (!aligned16(S) || (T > 0 && (!aligned16(K) || !aligned16(V))) || (accepted && !aligned16(accepted)))
-        return LLA_ERR_ALIGN;
-    if (T == 0) return LLA_OK;
-    const int64_t es = elem_size((lla_dtype)dt_raw);
-    const Span ss = span(S, B * H * dk * dv * 4), sk = span(K, B * H * T * dk * es),
-               sv = span(V, B * H * T * dv * es), sa = span(accepted, accepted ? B * 4 : 0);
-    if (overlap(ss, sk) || overlap(ss, sv) || overlap(ss, sa)) return LLA_ERR_ALIAS;
-    return device_status(lla::launch_state_commit((lla_dtype)dt_raw, K, V, accepted, B * H, (int)H, (int)T,
-                                                  (int)dk, (int)dv, S, (hipStream_t)stream));
+    return commit_impl(K, V, nullptr, false, raw_enum(dtype), B, H, T, dk, dv, accepted, S, stream);
+}
+
+lla_status lla_state_commit_gated(const void* K, const void* V, const float* gate, lla_dtype dtype, int64_t B,
+                                  int64_t H, int64_t T, int64_t dk, int64_t dv, const int32_t* accepted,
+                                  float* S, void* stream) {
+    return commit_impl(K, V, gate, true, raw_enum(dtype), B, H, T, dk, dv, accepted, S, stream);
 }
 
 lla_status lla_decode_step(const void* q, const void* k, const void* v, lla_dtype dtype,
@@ -404,8 +421,9 @@ size_t lla_prefill_gated_workspace_size(int64_t B, int64_t H, int64_t T, int64_t
 lla_status lla_prefill_gated(const void* Q, const void* K, const void* V, const float* gate, lla_dtype dtype,
                              int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int64_t C, unsigned flags,
                              float* S, float* O, void* workspace, size_t workspace_bytes, void* stream) {
-    if (flags & ~(unsigned)LLA_PREFILL_ZERO_STATE) return LLA_ERR_UNSUPPORTED;
+    if (flags & ~kKnownFlags) return LLA_ERR_UNSUPPORTED;
     const bool zero = (flags & LLA_PREFILL_ZERO_STATE) != 0;
+    const bool keep = (flags & LLA_PREFILL_KEEP_STATE) != 0;
     lla::PrefillPlan p;
     PrefillBufs b{Q, K, V, nullptr, S, O, nullptr, 0};
     lla_status st = check_prefill(b, true, true, true, true, false, raw_enum(dtype), B, Heads{H, H}, T, dk, dv,
@@ -416,7 +434,7 @@ lla_status lla_prefill_gated(const void* Q, const void* K, const void* V, const 
     if (need > 0 && (!workspace || workspace_bytes < need)) return LLA_ERR_WORKSPACE;
     if ((T > 0 && !aligned4(gate)) || (need > 0 && !aligned16(workspace))) return LLA_ERR_ALIGN;
     hipStream_t s = (hipStream_t)stream;
-    if (T == 0) return zero ? device_status(lla::launch_fill_zero(S, B * H * dk * dv, s)) : LLA_OK;
+    if (T == 0) return zero && !keep ? device_status(lla::launch_fill_zero(S, B * H * dk * dv, s)) : LLA_OK;
     // The gate is read only; the workspace is written: neither may overlap an
     // output, and the workspace nothing at all.
     const int64_t BH = B * H, es = elem_size((lla_dtype)raw_enum(dtype));
@@ -427,6 +445,7 @@ lla_status lla_prefill_gated(const void* Q, const void* K, const void* V, const 
     for (Span x : {sq, sk, sv, so, ss, sg})
         if (overlap(sw, x)) return LLA_ERR_ALIAS;
     p.zero_start = zero;
+    p.keep = keep;
     p.use_ws = need > 0;
     return device_status(lla::launch_gated_prefill(p, Q, K, V, gate, S, O, (float*)workspace, s));
 }

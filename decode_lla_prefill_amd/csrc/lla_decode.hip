@@ -439,15 +439,18 @@ __global__ __launch_bounds__(kThreads) void k_decode_group_any(const Tin* __rest
 // One workgroup per key/value head bh (sequence bh / Hkv); k, v rows
 // bh * T + t.  A thread owns VEC consecutive elements of a row (VEC = 4 when
 // dv is a multiple of 4, else 1) at a stride of kThreads * VEC elements.
-template <typename Tin, int VEC>
+// GATED: the gated commit, S <- g_t S + k_t v_t^T per accepted token with
+// g_t = gate[bh * T + t] (taken in [2^-126, 1]), the arithmetic of the gated
+// decode step, so the state equals m gated decode steps' bit for bit.
+template <typename Tin, int VEC, bool GATED = false>
 __global__ __launch_bounds__(kThreads) void k_state_commit(const Tin* __restrict__ k,
                                                           const Tin* __restrict__ v,
                                                           const int32_t* __restrict__ accepted,
                                                           float* __restrict__ S, int T, int Hkv,
-                                                          int dk, int dv) {
+                                                          int dk, int dv, const float* __restrict__ gate) {
     constexpr int TB = 16;          // tokens staged per pass
     constexpr int NE = 128 * 128 / (kThreads * VEC);  // element groups per thread at most
-    __shared__ float ks[TB][128], vs[TB][128];
+    __shared__ float ks[TB][128], vs[TB][128], gs[TB];
     typedef float vecf __attribute__((ext_vector_type(VEC)));
     const int tid = threadIdx.x;
     const int64_t bh = blockIdx.x;
@@ -469,8 +472,12 @@ __global__ __launch_bounds__(kThreads) void k_state_commit(const Tin* __restrict
             ks[e / dk][e % dk] = to_f32(k[(bh * T + t0 + e / dk) * (int64_t)dk + e % dk]);
         for (int e = tid; e < nt * dv; e += kThreads)
             vs[e / dv][e % dv] = to_f32(v[(bh * T + t0 + e / dv) * (int64_t)dv + e % dv]);
+        if constexpr (GATED)
+            if (tid < nt) gs[tid] = decay_gate(gate[bh * T + t0 + tid]);
         __syncthreads();
         for (int t = 0; t < nt; ++t) {
+            float gm = 1.0f;
+            if constexpr (GATED) gm = gs[t];
 #pragma unroll
             for (int n = 0; n < NE; ++n) {
                 const int e = tid + n * kThreads;
@@ -478,7 +485,10 @@ __global__ __launch_bounds__(kThreads) void k_state_commit(const Tin* __restrict
                     const int i = e * VEC / dv, j = e * VEC % dv;
                     const float ki = ks[t][i];
 #pragma unroll
-                    for (int u = 0; u < VEC; ++u) x[n][u] = fmaf(ki, vs[t][j + u], x[n][u]);  // rank-1 update
+                    for (int u = 0; u < VEC; ++u) {
+                        if constexpr (GATED) x[n][u] = gm * x[n][u];  // decay
+                        x[n][u] = fmaf(ki, vs[t][j + u], x[n][u]);    // rank-1 update
+                    }
                 }
             }
         }
@@ -495,16 +505,18 @@ __global__ __launch_bounds__(kThreads) void k_state_commit(const Tin* __restrict
 // groups, each thread RPT rows of one 16-byte column group, all of its state
 // loads issued before the first use, streaming loads and stores.  Per
 // element the arithmetic is that of k_state_commit (one fmaf per token in
-// token order), so the two give identical bits.
-template <typename Tin, int D, int NT>
+// token order), so the two give identical bits (GATED: with the decay
+// first, as there).
+template <typename Tin, int D, int NT, bool GATED = false>
 __global__ __launch_bounds__(NT) void k_state_commit_sq(const Tin* __restrict__ k,
                                                        const Tin* __restrict__ v,
                                                        const int32_t* __restrict__ accepted,
-                                                       float* __restrict__ S, int T, int Hkv) {
+                                                       float* __restrict__ S, int T, int Hkv,
+                                                       const float* __restrict__ gate) {
     constexpr int CG = D / 4, RG = NT / CG, RPT = D / RG;
     static_assert(NT % CG == 0 && D % RG == 0, "thread layout must tile the state");
     constexpr int TB = 16;  // tokens staged per pass
-    __shared__ float ks[TB][D], vs[TB][D];
+    __shared__ float ks[TB][D], vs[TB][D], gs[TB];
     const int tid = threadIdx.x, cg = tid % CG, rg = tid / CG;
     const int64_t bh = blockIdx.x;
     int m = accepted ? accepted[bh / Hkv] : T;
@@ -522,14 +534,21 @@ __global__ __launch_bounds__(NT) void k_state_commit_sq(const Tin* __restrict__ 
             ks[e / D][e % D] = to_f32(k[(bh * T + t0) * D + e]);
             vs[e / D][e % D] = to_f32(v[(bh * T + t0) * D + e]);
         }
+        if constexpr (GATED)
+            if (tid < nt) gs[tid] = decay_gate(gate[bh * T + t0 + tid]);
         __syncthreads();
         for (int t = 0; t < nt; ++t) {
             const f32x4 vj = {vs[t][4 * cg], vs[t][4 * cg + 1], vs[t][4 * cg + 2], vs[t][4 * cg + 3]};
+            float gm = 1.0f;
+            if constexpr (GATED) gm = gs[t];
 #pragma unroll
             for (int r = 0; r < RPT; ++r) {
                 const float ki = ks[t][rg + r * RG];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) x[r][u] = fmaf(ki, vj[u], x[r][u]);  // rank-1 update
+                for (int u = 0; u < 4; ++u) {
+                    if constexpr (GATED) x[r][u] = gm * x[r][u];  // decay
+                    x[r][u] = fmaf(ki, vj[u], x[r][u]);          // rank-1 update
+                }
             }
         }
     }
@@ -538,29 +557,42 @@ __global__ __launch_bounds__(NT) void k_state_commit_sq(const Tin* __restrict__ 
         __builtin_nontemporal_store(x[r], reinterpret_cast<f32x4*>(Sb + (rg + r * RG) * D + 4 * cg));
 }
 
-template <typename Tin>
+template <typename Tin, bool GATED>
 static hipError_t commit_t(const void* k, const void* v, const int32_t* accepted, int64_t BHkv, int Hkv,
-                           int T, int dk, int dv, float* S, hipStream_t st) {
+                           int T, int dk, int dv, float* S, const float* gate, hipStream_t st) {
     if (dk == 128 && dv == 128)
-        hipLaunchKernelGGL((k_state_commit_sq<Tin, 128, 512>), dim3((unsigned)BHkv), dim3(512), 0, st,
-                           (const Tin*)k, (const Tin*)v, accepted, S, T, Hkv);
+        hipLaunchKernelGGL((k_state_commit_sq<Tin, 128, 512, GATED>), dim3((unsigned)BHkv), dim3(512), 0, st,
+                           (const Tin*)k, (const Tin*)v, accepted, S, T, Hkv, gate);
     else if (dk == 64 && dv == 64)
-        hipLaunchKernelGGL((k_state_commit_sq<Tin, 64, 256>), dim3((unsigned)BHkv), dim3(256), 0, st,
-                           (const Tin*)k, (const Tin*)v, accepted, S, T, Hkv);
+        hipLaunchKernelGGL((k_state_commit_sq<Tin, 64, 256, GATED>), dim3((unsigned)BHkv), dim3(256), 0, st,
+                           (const Tin*)k, (const Tin*)v, accepted, S, T, Hkv, gate);
     else if ((dv & 3) == 0)
-        hipLaunchKernelGGL((k_state_commit<Tin, 4>), dim3((unsigned)BHkv), dim3(kThreads), 0, st,
-                           (const Tin*)k, (const Tin*)v, accepted, S, T, Hkv, dk, dv);
+        hipLaunchKernelGGL((k_state_commit<Tin, 4, GATED>), dim3((unsigned)BHkv), dim3(kThreads), 0, st,
+                           (const Tin*)k, (const Tin*)v, accepted, S, T, Hkv, dk, dv, gate);
     else
-        hipLaunchKernelGGL((k_state_commit<Tin, 1>), dim3((unsigned)BHkv), dim3(kThreads), 0, st,
-                           (const Tin*)k, (const Tin*)v, accepted, S, T, Hkv, dk, dv);
+        hipLaunchKernelGGL((k_state_commit<Tin, 1, GATED>), dim3((unsigned)BHkv), dim3(kThreads), 0, st,
+                           (const Tin*)k, (const Tin*)v, accepted, S, T, Hkv, dk, dv, gate);
     return hipGetLastError();
+}
+
+template <bool GATED>
+static hipError_t commit_dt(lla_dtype dtype, const void* k, const void* v, const int32_t* accepted,
+                            int64_t BHkv, int Hkv, int T, int dk, int dv, float* S, const float* gate,
+                            hipStream_t st) {
+    if (dtype == LLA_FP8_E4M3) return commit_t<fp8e4m3, GATED>(k, v, accepted, BHkv, Hkv, T, dk, dv, S, gate, st);
+    if (dtype == LLA_BF16) return commit_t<bf16, GATED>(k, v, accepted, BHkv, Hkv, T, dk, dv, S, gate, st);
+    return commit_t<float, GATED>(k, v, accepted, BHkv, Hkv, T, dk, dv, S, gate, st);
 }
 
 hipError_t launch_state_commit(lla_dtype dtype, const void* k, const void* v, const int32_t* accepted,
                                int64_t BHkv, int Hkv, int T, int dk, int dv, float* S, hipStream_t st) {
-    if (dtype == LLA_FP8_E4M3) return commit_t<fp8e4m3>(k, v, accepted, BHkv, Hkv, T, dk, dv, S, st);
-    if (dtype == LLA_BF16) return commit_t<bf16>(k, v, accepted, BHkv, Hkv, T, dk, dv, S, st);
-    return commit_t<float>(k, v, accepted, BHkv, Hkv, T, dk, dv, S, st);
+    return commit_dt<false>(dtype, k, v, accepted, BHkv, Hkv, T, dk, dv, S, nullptr, st);
+}
+
+hipError_t launch_state_commit_gated(lla_dtype dtype, const void* k, const void* v, const float* gate,
+                                     const int32_t* accepted, int64_t BH, int H, int T, int dk, int dv,
+                                     float* S, hipStream_t st) {
+    return commit_dt<true>(dtype, k, v, accepted, BH, H, T, dk, dv, S, gate, st);
 }
 
 __global__ __launch_bounds__(kThreads) void k_fill_zero(float* __restrict__ p, int64_t n) {

@@ -96,6 +96,11 @@ hipError_t launch_tokens_grouped(lla_dtype dtype, const void* q, const void* k, 
 // per-element arithmetic; k, v: [BHkv][T][d].
 hipError_t launch_state_commit(lla_dtype dtype, const void* k, const void* v, const int32_t* accepted,
                                int64_t BHkv, int Hkv, int T, int dk, int dv, float* S, hipStream_t st);
+// The gated commit: S <- g_t S + k_t v_t^T for t < m (the gated decode
+// step's arithmetic), gate: [BH][T]; H heads per sequence.
+hipError_t launch_state_commit_gated(lla_dtype dtype, const void* k, const void* v, const float* gate,
+                                     const int32_t* accepted, int64_t BH, int H, int T, int dk, int dv,
+                                     float* S, hipStream_t st);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 
 // Shared-state heads: `group` query heads read each key/value state (any

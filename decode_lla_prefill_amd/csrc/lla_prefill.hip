@@ -1665,7 +1665,7 @@ __global__ __launch_bounds__(kThreads) void k_gated_walk(
     const In* __restrict__ Q, const In* __restrict__ K, const In* __restrict__ V,
     const float* __restrict__ gate, float* __restrict__ S, float* __restrict__ O,
     const float* __restrict__ ws, int64_t T_len, int dk, int dv, int C, int64_t G, int64_t n_seg,
-    int n_vb, int zero_start) {
+    int n_vb, int zero_start, int keep) {
     using T = typename Compute<In>::type;
     using Cf = WalkCfg<T, CT, D, BV, kWaves>;
     using Fr = typename Cf::Fr;
@@ -1761,12 +1761,12 @@ __global__ __launch_bounds__(kThreads) void k_gated_walk(
         chunk_output<Cf>(Oacc, Sacc, Vf, Qs, Ps, w, g, c16, NoHook(), DecayRows<CT>{Bs, c16});
         t_prev = t0;
         n_prev = nrows;
-        if (c + 1 < c1 || last_seg) state_hop_gated<Cf>(Sacc, Vf, Ks, Bs, w, g, lane);
+        if (c + 1 < c1 || (last_seg && !keep)) state_hop_gated<Cf>(Sacc, Vf, Ks, Bs, w, g, lane);
         __syncthreads();
     }
     if (c1 > c0) store_out<Cf, VEC>(Ob, Oacc, t_prev, n_prev, nv, dv, w, g, c16);
 
-    if (last_seg) {  // (the loop ended with a barrier)
+    if (last_seg && !keep) {  // (the loop ended with a barrier); a verify pass leaves S as it was
         state_regs_to_lds<Cf>(Sst, Sacc, w, g, c16);
         __syncthreads();
         state_lds_to_gmem<Cf>(S + bh * dkdv + v0, Sst, dk, dv, nv, tid);
@@ -1937,7 +1937,7 @@ static hipError_t launch_gated_walk_t(const PrefillPlan& p, const void* Q, const
             hipLaunchKernelGGL((k_chunk_walk_wide<CT, In, true>), dim3((unsigned)(p.BHq * p.n_seg)),
                                dim3(kWideWaves * kWave), 0, st, (const In*)Q, (const In*)K, (const In*)V, S, O,
                                (const float*)(p.use_ws ? ws : nullptr), p.T, p.dk, p.dv, p.C, p.G, p.n_seg, 1,
-                               (int)p.zero_start, 0, gate);
+                               (int)p.zero_start, (int)p.keep, gate);
             return hipGetLastError();
         }
     }
@@ -1947,11 +1947,11 @@ static hipError_t launch_gated_walk_t(const PrefillPlan& p, const void* Q, const
     if (p.vec)
         hipLaunchKernelGGL((k_gated_walk<In, CT, D, BV, true>), dim3((unsigned)grid), dim3(kThreads), 0, st,
                            (const In*)Q, (const In*)K, (const In*)V, gate, S, O, wsr, p.T, p.dk, p.dv, p.C, p.G,
-                           p.n_seg, p.n_vb, (int)p.zero_start);
+                           p.n_seg, p.n_vb, (int)p.zero_start, (int)p.keep);
     else
         hipLaunchKernelGGL((k_gated_walk<In, CT, D, BV, false>), dim3((unsigned)grid), dim3(kThreads), 0, st,
                            (const In*)Q, (const In*)K, (const In*)V, gate, S, O, wsr, p.T, p.dk, p.dv, p.C, p.G,
-                           p.n_seg, p.n_vb, (int)p.zero_start);
+                           p.n_seg, p.n_vb, (int)p.zero_start, (int)p.keep);
     return hipGetLastError();
 }
 

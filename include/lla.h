@@ -84,8 +84,7 @@ typedef enum {
     LLA_ERR_NULL = 1,        /* a required pointer is NULL */
     LLA_ERR_SHAPE = 2,       /* a size is out of range */
     LLA_ERR_DTYPE = 3,       /* unknown dtype */
-    LLA_ERR_UNSUPPORTED = 4, /* valid request the library does not handle: unknown option bits,
-                                LLA_PREFILL_KEEP_STATE on a gated prefill */
+    LLA_ERR_UNSUPPORTED = 4, /* unknown option bits */
     LLA_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned (a gate: 4-byte) */
     LLA_ERR_ALIAS = 6,       /* an output overlaps an input, another output or the workspace */
     LLA_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than lla_prefill_workspace_size() */
@@ -344,8 +343,10 @@ lla_status lla_decode_step_gqa(const void *q, const void *k, const void *v, lla_
  * the prefill, [B][H] for the decode step, 4-byte aligned, read only.  Gates
  * are taken in [2^-126, 1]: g <= 0 (and NaN) act as 2^-126, g > 1 as 1.
  * One query head per state (no shared-state heads).  Sizes, dtypes, chunk
- * sizes, S, O and the errors are those of lla_prefill; options: only
- * LLA_PREFILL_ZERO_STATE (others: LLA_ERR_UNSUPPORTED).  Every prompt length
+ * sizes, S, O and the errors are those of lla_prefill; options as
+ * lla_prefill_ex: LLA_PREFILL_ZERO_STATE, and LLA_PREFILL_KEEP_STATE for the
+ * verify pass of speculative decoding (S not written; then
+ * lla_state_commit_gated).  Every prompt length
  * takes the chunked path (segment pass, scan, walk), with the chunked
  * prefill's numerics: the decays scale the masked scores before their bf16
  * high + low split, Q_c S_c is added scaled in fp32, and the state hop takes
@@ -372,6 +373,23 @@ lla_status lla_prefill_gated(const void *Q, const void *K, const void *V, const 
 lla_status lla_decode_step_gated(const void *q, const void *k, const void *v, const float *gate,
                                  lla_dtype dtype, int64_t B, int64_t H, int64_t dk, int64_t dv,
                                  float *S, float *o, void *stream);
+
+/*
+ * The commit after a gated verify pass (lla_prefill_gated with
+ * LLA_PREFILL_KEEP_STATE): for every sequence b and head h, for the first
+ * m_b draft tokens t in order,
+ *     S[b][h] <- g_t S[b][h] + k_t v_t^T,
+ * with the gated decode step's per-element arithmetic (the decay, then one
+ * fmaf), so S equals the state of m_b gated decode steps bit for bit.  gate:
+ * the verify pass's [B][H][T] gates (4-byte aligned, read only); the other
+ * arguments, limits and errors as lla_state_commit (H heads per sequence,
+ * one query head per state).  For callers with a decayed state that
+ * speculate (blog "A 128 000 tokens, l'attention avale 85 % du calcul", on
+ * speculative decoding adding tokens per decode iteration).
+ */
+lla_status lla_state_commit_gated(const void *K, const void *V, const float *gate, lla_dtype dtype,
+                                  int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
+                                  const int32_t *accepted, float *S, void *stream);
 
 #ifdef __cplusplus
 }

@@ -199,3 +199,56 @@ def test_gated_decode_full_size_sampled(dev):
     o_ref, S_ref = oracle.gated_decode_step(qd[0][bs, hs].cpu(), kd[0][bs, hs].cpu(), vd[0][bs, hs].cpu(),
                                             g[bs, hs].cpu(), S0[bs, hs].cpu())
     assert rel_err(np64(o[bs, hs]), o_ref) <= 1e-5 and rel_err(np64(S[bs, hs]), S_ref) <= 1e-6
+
+
+# ---- speculative decoding with a decayed state ------------------------------------
+
+@pytest.mark.parametrize("B,H,k,d,C,dtype", [(6, 4, 5, 128, 64, torch.bfloat16), (5, 3, 40, 64, 64, torch.float32),
+                                             (4, 2, 300, 128, 128, FP8), (3, 2, 9, 40, 16, torch.bfloat16)])
+def test_gated_verify_and_commit_equal_gated_decode_steps(dev, B, H, k, d, C, dtype):
+    """A gated verify pass (KEEP_STATE) gives the outputs of the plain gated
+    prefill and leaves S as it was; lla_state_commit_gated then advances each
+    sequence by its accepted prefix m_b, bit-equal to m_b gated decode steps."""
+    print("gated verify + commit", B, H, k, d, C, dtype, flush=True)
+    scale = 1.0 if dtype == FP8 else d ** -0.5
+    q, kk, v = workloads.gaussian(B, H, k, d, d, seed_base=k + d, scale=scale, dtype=dtype, device=dev)
+    g = workloads.gates(B, H, k, seed=k, lo=0.5, hi=1.0, device=dev)
+    S0 = torch.randn((B, H, d, d), generator=torch.Generator(device=dev).manual_seed(k), device=dev)
+    S = S0.clone()
+    o = lla.prefill_gated(q, kk, v, g, S, C, keep_state=True)
+    S_plain = S0.clone()
+    o_plain = lla.prefill_gated(q, kk, v, g, S_plain, C)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_plain)
+    assert torch.equal(S, S0)  # the verify pass wrote nothing
+    accepted = [(3 * b + 1) % (k + 1) for b in range(B)]
+    lla.state_commit_gated(kk, v, g, S, torch.tensor(accepted, dtype=torch.int32, device=dev))
+    Sd = S0.clone()
+    want = S0.clone()
+    for t in range(max(accepted)):
+        lla.decode_step_gated(q[:, :, t].contiguous(), kk[:, :, t].contiguous(), v[:, :, t].contiguous(),
+                              g[:, :, t].contiguous(), Sd)
+        for b in range(B):
+            if accepted[b] == t + 1:
+                want[b] = Sd[b]
+    torch.cuda.synchronize()
+    assert torch.equal(S, want)
+
+
+def test_gated_commit_with_dyadic_gates_exact_against_the_oracle(dev):
+    """Gates 1, 1/2, 1/4 on small integers keep every step exact in fp32: the
+    commit of m_b tokens equals the oracle's m_b gated decode steps."""
+    B, H, k, dk, dv = 4, 3, 7, 24, 7
+    q, kk, v = workloads.integers(B, H, k, dk, dv, seed=41, lo=-2, hi=2)
+    g = torch.tensor([1.0, 0.5, 0.25])[torch.randint(0, 3, (B, H, k), generator=torch.Generator().manual_seed(3))]
+    S0 = torch.randint(-8, 9, (B, H, dk, dv), generator=torch.Generator().manual_seed(4)).float()
+    S = S0.to(dev)
+    accepted = [7, 0, 3, 100]  # 100 clamps to 7
+    lla.state_commit_gated(kk.to(dev), v.to(dev), g.to(dev), S, torch.tensor(accepted, dtype=torch.int32, device=dev))
+    torch.cuda.synchronize()
+    for b, m in enumerate(accepted):
+        Sr = S0[b:b + 1].double().numpy()
+        for t in range(min(m, k)):
+            _, Sr = oracle.gated_decode_step(q[b:b + 1, :, t], kk[b:b + 1, :, t], v[b:b + 1, :, t], g[b:b + 1, :, t],
+                                             Sr)
+        assert np.array_equal(np64(S[b:b + 1]), Sr), b

@@ -29,6 +29,8 @@ def lib():
     L.lla_prefill_segment_chunks.argtypes = [i64] * 6
     L.lla_decode_step_gated.restype = ctypes.c_int
     L.lla_decode_step_gated.argtypes = [vp, vp, vp, vp, ctypes.c_int] + [i64] * 4 + [vp, vp, vp]
+    L.lla_state_commit_gated.restype = ctypes.c_int
+    L.lla_state_commit_gated.argtypes = [vp, vp, vp, ctypes.c_int] + [i64] * 5 + [vp, vp, vp]
     return L
 
 
@@ -42,7 +44,8 @@ def _prefill(lib, **change):
 
 @pytest.mark.parametrize("change,expect", [
     (dict(gate=None), E_NULL), (dict(q=None), E_NULL), (dict(S=None), E_NULL), (dict(O=None), E_NULL),
-    (dict(flags=2), E_UNSUP), (dict(flags=4), E_UNSUP),
+    (dict(flags=4), E_UNSUP), (dict(flags=7), E_UNSUP), (dict(flags=2, q=None), E_NULL),
+    (dict(flags=3, q=None), E_NULL),
     (dict(B=0), E_SHAPE), (dict(dk=129), E_SHAPE), (dict(C=0), E_SHAPE), (dict(C=129), E_SHAPE),
     (dict(dtype=7), E_DTYPE), (dict(dtype=F32, C=128, q=None), E_NULL),
     (dict(gate=7 * A + 2), E_ALIGN), (dict(q=A + 8), E_ALIGN),
@@ -99,3 +102,24 @@ def test_python_binding_checks_gate_shapes_without_the_gpu():
         lla.prefill_gated(q, q, q, torch.ones(1, 2, 8), S, 8)  # host tensors
     with pytest.raises((ValueError, TypeError)):
         lla.decode_step_gated(q[:, :, 0], q[:, :, 0], q[:, :, 0], torch.ones(1, 2), S)
+
+
+def _commit(lib, **change):
+    d = dict(k=A, v=2 * A, gate=3 * A, dtype=BF16, B=2, H=4, T=6, dk=128, dv=128, acc=5 * A, S=4 * A)
+    d.update(change)
+    return lib.lla_state_commit_gated(d["k"], d["v"], d["gate"], d["dtype"], d["B"], d["H"], d["T"], d["dk"],
+                                      d["dv"], d["acc"], d["S"], None)
+
+
+@pytest.mark.parametrize("change,expect", [
+    (dict(gate=None), E_NULL), (dict(k=None), E_NULL), (dict(S=None), E_NULL), (dict(B=0), E_SHAPE),
+    (dict(dk=129), E_SHAPE), (dict(dtype=9), E_DTYPE), (dict(gate=3 * A + 2), E_ALIGN),
+    (dict(acc=5 * A + 4), E_ALIGN), (dict(S=4 * A + 8), E_ALIGN),
+    (dict(gate=4 * A + 64), E_ALIAS), (dict(S=A + 16), E_ALIAS), (dict(acc=4 * A + 4096), E_ALIAS),
+])
+def test_state_commit_gated_rejects(lib, change, expect):
+    assert _commit(lib, **change) == expect
+
+
+def test_state_commit_gated_of_no_tokens_is_a_noop(lib):
+    assert _commit(lib, T=0, k=None, v=None, gate=None) == OK
