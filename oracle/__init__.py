@@ -296,6 +296,38 @@ def grouped_decode_step(q, k, v, S):
     return o, np.ascontiguousarray(S_new[:, ::G])
 
 
+def gated_grouped_recurrence(q, k, v, gate, S0=None, nthreads: int = 1):
+    """Gated recurrence with shared-state heads, float64: each key/value
+    head's state S_t = g_t S_{t-1} + k_t v_t^T (gate [B, Hkv, T], one per
+    state and token) is read by the G query heads of its group, o_t = S_t^T
+    q_t.  Every key/value head, its gates and its state are repeated for the
+    group, then :func:`gated_recurrence` runs on Hq independent heads.
+    Returns ``(O [B,Hq,T,dv], S_T [B,Hkv,dk,dv])`` (the copies are equal; the
+    first is returned)."""
+    q, k, v, gate = _f64(q), _f64(k), _f64(v), _f64(gate)
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4 or gate.ndim != 3:
+        raise ValueError("q, k, v must be [B, H, T, d] and gate [B, Hkv, T]")
+    G = _group(q.shape[1], k.shape[1])
+    S0e = None if S0 is None else np.repeat(_f64(S0), G, axis=1)
+    O, S = gated_recurrence(q, np.repeat(k, G, axis=1), np.repeat(v, G, axis=1), np.repeat(gate, G, axis=1),
+                            S0e, nthreads=nthreads)
+    return O, np.ascontiguousarray(S[:, ::G])
+
+
+def gated_grouped_decode_step(q, k, v, gate, S):
+    """One gated decode step with shared-state heads, float64: q [B,Hq,dk],
+    k [B,Hkv,dk], v [B,Hkv,dv], gate [B,Hkv], S [B,Hkv,dk,dv].  ``S = g S +
+    k v^T`` once per key/value head, then every query head h reads ``o_h =
+    S_{h//G}^T q_h``.  Returns ``(o [B,Hq,dv], S_new)``."""
+    q, k, v, gate = _f64(q), _f64(k), _f64(v), _f64(gate)
+    if q.ndim != 3 or k.ndim != 3 or v.ndim != 3 or gate.ndim != 2:
+        raise ValueError("q, k, v must be [B, H, d] and gate [B, Hkv]")
+    G = _group(q.shape[1], k.shape[1])
+    o, S_new = gated_decode_step(q, np.repeat(k, G, axis=1), np.repeat(v, G, axis=1), np.repeat(gate, G, axis=1),
+                                 np.repeat(_f64(S), G, axis=1))
+    return o, np.ascontiguousarray(S_new[:, ::G])
+
+
 # --- the deck's chunk form, step by step (numpy, float64, small inputs) -----
 
 def causal_mask(A: np.ndarray) -> np.ndarray:

@@ -16,6 +16,10 @@ than themselves:
 * brute force on tiny inputs (explicit sums over every s <= t);
 * a planted mistake -- the gate applied after the update, S_t = g_t (S_{t-1}
   + k_t v_t^T) -- fails the closed form.
+With shared-state heads (each key/value head's state and gates read by the
+G query heads of its group): brute force with the explicit head mapping,
+g = 1 equal to the ungated grouped oracle bit for bit, the decode step as one
+token of the recurrence, and a planted h % Hkv mapping that fails.
 """
 import json
 import os
@@ -149,3 +153,90 @@ def test_prefill_then_prefill_equals_one_prefill():
     Oa, Sa = oracle.gated_recurrence(q[:, :13], k[:, :13], v[:, :13], g[:, :13], S0)
     Ob, Sb = oracle.gated_recurrence(q[:, 13:], k[:, 13:], v[:, 13:], g[:, 13:], Sa)
     assert np.array_equal(np.concatenate([Oa, Ob], 1), O) and np.array_equal(Sb, S)
+
+
+# ---- shared-state heads with the decayed state ------------------------------------
+
+def _gated_grouped_brute_force(q, k, v, g, S0):
+    """Explicit sums: query head h of a group of G reads key/value head h // G,
+    whose state decays by that head's gates."""
+    B, Hq, T, dk = q.shape
+    Hkv, dv = k.shape[1], v.shape[3]
+    G = Hq // Hkv
+    O = np.zeros((B, Hq, T, dv))
+    S = np.zeros((B, Hkv, dk, dv))
+    for b in range(B):
+        for hk in range(Hkv):
+            for t in range(T):
+                c = 1.0
+                for l in range(t + 1):
+                    c *= g[b, hk, l]
+                St = c * S0[b, hk]
+                for s in range(t + 1):
+                    w = 1.0
+                    for l in range(s + 1, t + 1):
+                        w *= g[b, hk, l]
+                    St = St + w * np.outer(k[b, hk, s], v[b, hk, s])
+                for j in range(G):
+                    O[b, hk * G + j, t] = St.T @ q[b, hk * G + j, t]
+                if t == T - 1:
+                    S[b, hk] = St
+    return O, S
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 2), (6, 1), (3, 3)])
+def test_gated_grouped_recurrence_vs_brute_force(Hq, Hkv):
+    rng = np.random.default_rng(Hq * 10 + Hkv)
+    B, T, dk, dv = 2, 6, 3, 4
+    q = rng.standard_normal((B, Hq, T, dk))
+    k = rng.standard_normal((B, Hkv, T, dk))
+    v = rng.standard_normal((B, Hkv, T, dv))
+    g = rng.uniform(0.2, 1.0, (B, Hkv, T))
+    S0 = rng.standard_normal((B, Hkv, dk, dv))
+    O, S = oracle.gated_grouped_recurrence(q, k, v, g, S0)
+    O_ref, S_ref = _gated_grouped_brute_force(q, k, v, g, S0)
+    assert np.allclose(O, O_ref, rtol=1e-12, atol=1e-12)
+    assert np.allclose(S, S_ref, rtol=1e-12, atol=1e-12)
+
+
+def test_gated_grouped_gate_one_is_the_grouped_recurrence_bit_for_bit():
+    rng = np.random.default_rng(21)
+    q = rng.standard_normal((2, 6, 20, 5))
+    k = rng.standard_normal((2, 2, 20, 5))
+    v = rng.standard_normal((2, 2, 20, 3))
+    S0 = rng.standard_normal((2, 2, 5, 3))
+    O1, S1 = oracle.gated_grouped_recurrence(q, k, v, np.ones((2, 2, 20)), S0)
+    O0, S0_ = oracle.grouped_recurrence(q, k, v, S0)
+    assert np.array_equal(O1, O0) and np.array_equal(S1, S0_)
+
+
+def test_gated_grouped_decode_step_is_one_token_of_the_recurrence():
+    rng = np.random.default_rng(23)
+    q = rng.standard_normal((3, 8, 4, 6))
+    k = rng.standard_normal((3, 2, 4, 6))
+    v = rng.standard_normal((3, 2, 4, 5))
+    g = rng.uniform(0.3, 1.0, (3, 2, 4))
+    S0 = rng.standard_normal((3, 2, 6, 5))
+    O, S = oracle.gated_grouped_recurrence(q, k, v, g, S0)
+    Sd = S0.copy()
+    for t in range(4):
+        o, Sd = oracle.gated_grouped_decode_step(q[:, :, t], k[:, :, t], v[:, :, t], g[:, :, t], Sd)
+        assert np.array_equal(o, O[:, :, t])
+    assert np.array_equal(Sd, S)
+
+
+def test_gated_grouped_mapping_mistake_is_caught():
+    """A planted mistake -- query head h reading key/value head h % Hkv
+    instead of h // G -- disagrees with the brute force."""
+    rng = np.random.default_rng(25)
+    B, Hq, Hkv, T, d = 1, 4, 2, 5, 3
+    q = rng.standard_normal((B, Hq, T, d))
+    k = rng.standard_normal((B, Hkv, T, d))
+    v = rng.standard_normal((B, Hkv, T, d))
+    g = rng.uniform(0.3, 1.0, (B, Hkv, T))
+    O_ref, _ = _gated_grouped_brute_force(q, k, v, g, np.zeros((B, Hkv, d, d)))
+    idx = np.arange(Hq) % Hkv
+    O_bad, _ = oracle.gated_recurrence(q, k[:, idx], v[:, idx], g[:, idx])
+    O, _ = oracle.gated_grouped_recurrence(q, k, v, g)
+    assert np.allclose(O, O_ref, rtol=1e-12, atol=1e-12)
+    assert not np.allclose(O_bad, O_ref, rtol=1e-3, atol=1e-3)
