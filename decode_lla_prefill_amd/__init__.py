@@ -41,7 +41,8 @@ EXPORTS = ("lla_status_string", "lla_last_device_error", "lla_state_init",
            "lla_decode_step", "lla_prefill_gqa_workspace_size", "lla_prefill_gqa",
            "lla_decode_step_gqa", "lla_prefill_ex", "lla_prefill_noalloc", "lla_state_commit",
            "lla_prefill_gated_workspace_size", "lla_prefill_gated", "lla_decode_step_gated",
-           "lla_state_commit_gated")
+           "lla_state_commit_gated", "lla_prefill_gated_gqa_workspace_size", "lla_prefill_gated_gqa",
+           "lla_decode_step_gated_gqa")
 PREFILL_ZERO_STATE = 1  # lla_prefill_ex: start from S_0 = 0 without reading S
 PREFILL_KEEP_STATE = 2  # lla_prefill_ex: read S, do not write it (verify pass of draft tokens)
 
@@ -114,6 +115,13 @@ def library():
         lib.lla_decode_step_gated.restype = st
         lib.lla_state_commit_gated.argtypes = [vp, vp, vp, ci, i64, i64, i64, i64, i64, vp, vp, vp]
         lib.lla_state_commit_gated.restype = st
+        lib.lla_prefill_gated_gqa_workspace_size.argtypes = [i64] * 7
+        lib.lla_prefill_gated_gqa_workspace_size.restype = sz
+        lib.lla_prefill_gated_gqa.argtypes = [vp, vp, vp, vp, ci, i64, i64, i64, i64, i64, i64, i64,
+                                              ctypes.c_uint, vp, vp, vp, sz, vp]
+        lib.lla_prefill_gated_gqa.restype = st
+        lib.lla_decode_step_gated_gqa.argtypes = [vp, vp, vp, vp, ci, i64, i64, i64, i64, i64, vp, vp, vp]
+        lib.lla_decode_step_gated_gqa.restype = st
         _lib = lib
     return _lib
 
@@ -261,38 +269,46 @@ def prefill(q, k, v, state, chunk: int, out=None, workspace=None, zero_state: bo
     return out
 
 
-def prefill_gated_workspace_size(B, H, T, dk, dv, chunk) -> int:
-    return int(library().lla_prefill_gated_workspace_size(B, H, T, dk, dv, chunk))
+def prefill_gated_workspace_size(B, H, T, dk, dv, chunk, Hkv=None) -> int:
+    """Workspace bytes of a gated prefill (H query heads on Hkv states;
+    Hkv defaults to H)."""
+    return int(library().lla_prefill_gated_gqa_workspace_size(B, H, Hkv or H, T, dk, dv, chunk))
 
 
-def prefill_gated(q, k, v, gate, state, chunk: int, out=None, workspace=None, zero_state: bool = False,
-                  keep_state: bool = False):
-    """Prefill with a decayed state (lla_prefill_gated): ``S_t = g_t S_{t-1}
-    + k_t v_t^T``, ``o_t = S_t^T q_t``, one gate per (b,h) and token.
-    ``gate``: fp32 [B,H,T]; q, k, v: [B,H,T,*] (one query head per state).
-    Returns o [B,H,T,dv] fp32; ``state`` goes S_0 -> S_T in place
-    (``keep_state``: a verify pass, ``state`` not written; then
-    :func:`state_commit_gated`)."""
-    lib = library()
+def _gated_prefill_args(q, k, v, gate, state, chunk, out, workspace):
+    """Checks a gated prefill's buffers; returns the head of its argument
+    list, its tail and the output."""
     B, Hq, Hkv, T, dk, dv = _qkv_shape(q, k, v)
-    if Hq != Hkv:
-        raise ValueError("the gated prefill takes one query head per state")
     _need(gate, "gate", dtype=torch.float32, ndim=3)
-    if tuple(gate.shape) != (B, Hq, T):
-        raise ValueError("gate shape %s, expected %s" % (tuple(gate.shape), (B, Hq, T)))
-    _state_check(state, B, Hq, dk, dv)
+    if tuple(gate.shape) != (B, Hkv, T):
+        raise ValueError("gate shape %s, expected %s (one gate per state and token)" % (tuple(gate.shape),
+                                                                                       (B, Hkv, T)))
+    _state_check(state, B, Hkv, dk, dv)
     out = _out(out, (B, Hq, T, dv), q.device)
-    need = prefill_gated_workspace_size(B, Hq, T, dk, dv, chunk)
+    need = prefill_gated_workspace_size(B, Hq, T, dk, dv, chunk, Hkv)
     if workspace is None and need:
         workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
     if workspace is not None:
         _need(workspace, "workspace")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _same_device(q.device, gate=gate, state=state, out=out, workspace=workspace)
+    head = (_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _dtype_code(q), B, Hq, Hkv, T, dk, dv, chunk)
+    tail = (_ptr(state), _ptr(out), _ptr(workspace), ws_bytes)
+    return head, tail, out, workspace
+
+
+def prefill_gated(q, k, v, gate, state, chunk: int, out=None, workspace=None, zero_state: bool = False,
+                  keep_state: bool = False):
+    """Prefill with a decayed state (lla_prefill_gated_gqa): ``S_t = g_t
+    S_{t-1} + k_t v_t^T``, ``o_t = S_t^T q_t``, one gate per state and token.
+    q: [B,Hq,T,dk]; k, v: [B,Hkv,T,*] (Hq a multiple of Hkv: shared-state
+    heads); ``gate``: fp32 [B,Hkv,T].  Returns o [B,Hq,T,dv] fp32; ``state``
+    [B,Hkv,dk,dv] goes S_0 -> S_T in place (``keep_state``: a verify pass,
+    ``state`` not written; then :func:`state_commit_gated`)."""
+    lib = library()
+    head, tail, out, _ = _gated_prefill_args(q, k, v, gate, state, chunk, out, workspace)
     flags = (PREFILL_ZERO_STATE if zero_state else 0) | (PREFILL_KEEP_STATE if keep_state else 0)
-    _check(lib.lla_prefill_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _dtype_code(q), B, Hq, T, dk, dv, chunk,
-                                 flags, _ptr(state), _ptr(out), _ptr(workspace), ws_bytes, _stream(q)),
-           "lla_prefill_gated")
+    _check(lib.lla_prefill_gated_gqa(*head, flags, *tail, _stream(q)), "lla_prefill_gated_gqa")
     return out
 
 
@@ -438,21 +454,25 @@ def decode_step(q, k, v, state, out=None):
     return out
 
 
-def decode_step_gated(q, k, v, gate, state, out=None):
-    """One gated decode step (lla_decode_step_gated): ``state = g state + k
-    v^T`` in place, then o = state^T q.  q, k, v: [B,H,d*]; gate: fp32 [B,H]."""
-    lib = library()
+def _gated_step_args(q, k, v, gate, state, out):
     B, Hq, Hkv, dk, dv = _step_shape(q, k, v)
-    if Hq != Hkv:
-        raise ValueError("the gated decode step takes one query head per state")
     _need(gate, "gate", dtype=torch.float32, ndim=2)
-    if tuple(gate.shape) != (B, Hq):
-        raise ValueError("gate shape %s, expected %s" % (tuple(gate.shape), (B, Hq)))
-    _state_check(state, B, Hq, dk, dv)
+    if tuple(gate.shape) != (B, Hkv):
+        raise ValueError("gate shape %s, expected %s (one gate per state)" % (tuple(gate.shape), (B, Hkv)))
+    _state_check(state, B, Hkv, dk, dv)
     out = _out(out, (B, Hq, dv), q.device)
     _same_device(q.device, gate=gate, state=state, out=out)
-    _check(lib.lla_decode_step_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _dtype_code(q), B, Hq, dk, dv,
-                                     _ptr(state), _ptr(out), _stream(q)), "lla_decode_step_gated")
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _dtype_code(q), B, Hq, Hkv, dk, dv, _ptr(state), _ptr(out))
+    return args, out
+
+
+def decode_step_gated(q, k, v, gate, state, out=None):
+    """One gated decode step (lla_decode_step_gated_gqa): ``state = g state +
+    k v^T`` in place, then o = state^T q for every query head.  q: [B,Hq,dk];
+    k, v: [B,Hkv,d*]; gate: fp32 [B,Hkv]."""
+    lib = library()
+    args, out = _gated_step_args(q, k, v, gate, state, out)
+    _check(lib.lla_decode_step_gated_gqa(*args, _stream(q)), "lla_decode_step_gated_gqa")
     return out
 
 
@@ -537,65 +557,40 @@ class PreparedPrefill:
 
 
 class PreparedGatedPrefill:
-    """A gated prefill (lla_prefill_gated) over fixed buffers, checked and
+    """A gated prefill (lla_prefill_gated_gqa) over fixed buffers, checked and
     marshalled once (see PreparedPrefill): calling it runs one prefill on the
-    current stream, a fresh prompt with ``zero_state``."""
+    current stream, a fresh prompt with ``zero_state``, a verify pass with
+    ``keep_state``."""
 
     def __init__(self, q, k, v, gate, state, chunk, out=None, workspace=None):
         lib = library()
-        B, Hq, Hkv, T, dk, dv = _qkv_shape(q, k, v)
-        if Hq != Hkv:
-            raise ValueError("the gated prefill takes one query head per state")
-        _need(gate, "gate", dtype=torch.float32, ndim=3)
-        if tuple(gate.shape) != (B, Hq, T):
-            raise ValueError("gate shape %s, expected %s" % (tuple(gate.shape), (B, Hq, T)))
-        _state_check(state, B, Hq, dk, dv)
-        self.out = _out(out, (B, Hq, T, dv), q.device)
-        need = prefill_gated_workspace_size(B, Hq, T, dk, dv, chunk)
-        if workspace is None and need:
-            workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
-        if workspace is not None:
-            _need(workspace, "workspace")
-        self.workspace = workspace
-        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-        _same_device(q.device, gate=gate, state=state, out=self.out, workspace=workspace)
-        self._fn = lib.lla_prefill_gated
-        self._head = (_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _dtype_code(q), B, Hq, T, dk, dv, chunk)
-        self._tail = (_ptr(state), _ptr(self.out), _ptr(workspace), ws_bytes)
-        self._keep = (q, k, v, gate, state, self.out, workspace)  # the buffers behind the addresses
+        self._head, self._tail, self.out, self.workspace = _gated_prefill_args(q, k, v, gate, state, chunk, out,
+                                                                               workspace)
+        self._fn = lib.lla_prefill_gated_gqa
+        self._keep = (q, k, v, gate, state, self.out, self.workspace)  # the buffers behind the addresses
         self._device = q.device
 
     def __call__(self, zero_state: bool = False, keep_state: bool = False):
         st = torch.cuda.current_stream(self._device).cuda_stream
         flags = (PREFILL_ZERO_STATE if zero_state else 0) | (PREFILL_KEEP_STATE if keep_state else 0)
-        _check(self._fn(*self._head, flags, *self._tail, st), "lla_prefill_gated")
+        _check(self._fn(*self._head, flags, *self._tail, st), "lla_prefill_gated_gqa")
         return self.out
 
 
 class PreparedGatedDecode:
-    """A gated decode step (lla_decode_step_gated) over fixed buffers,
+    """A gated decode step (lla_decode_step_gated_gqa) over fixed buffers,
     marshalled once."""
 
     def __init__(self, q, k, v, gate, state, out=None):
         lib = library()
-        B, Hq, Hkv, dk, dv = _step_shape(q, k, v)
-        if Hq != Hkv:
-            raise ValueError("the gated decode step takes one query head per state")
-        _need(gate, "gate", dtype=torch.float32, ndim=2)
-        if tuple(gate.shape) != (B, Hq):
-            raise ValueError("gate shape %s, expected %s" % (tuple(gate.shape), (B, Hq)))
-        _state_check(state, B, Hq, dk, dv)
-        self.out = _out(out, (B, Hq, dv), q.device)
-        _same_device(q.device, gate=gate, state=state, out=self.out)
-        self._fn = lib.lla_decode_step_gated
-        self._args = (_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _dtype_code(q), B, Hq, dk, dv, _ptr(state),
-                      _ptr(self.out))
+        self._args, self.out = _gated_step_args(q, k, v, gate, state, out)
+        self._fn = lib.lla_decode_step_gated_gqa
         self._keep = (q, k, v, gate, state, self.out)
         self._device = q.device
 
     def __call__(self):
         _check(self._fn(*self._args, torch.cuda.current_stream(self._device).cuda_stream),
-               "lla_decode_step_gated")
+               "lla_decode_step_gated_gqa")
         return self.out
 
 

@@ -99,7 +99,8 @@ size_t ws_bytes_for(const lla::PrefillPlan& p) {
 // The gated prefill's workspace: the segment states, then one decay (float)
 // per (b,h) and segment; none with a single segment.
 size_t gated_ws_bytes_for(const lla::PrefillPlan& p) {
-    if (p.n_seg <= 1) return 0;
+    // grouped heads stage their start states even for a single segment
+    if (p.n_seg <= 1 && p.group <= 1) return 0;
     return (size_t)(p.BH * p.n_seg * ((int64_t)p.dk * p.dv + 1)) * sizeof(float);
 }
 
@@ -303,11 +304,14 @@ lla_status decode_impl(const void* q, const void* k, const void* v, int dt_raw, 
     if (overlap(ss, sq) || overlap(ss, sk) || overlap(ss, sv) || overlap(ss, so) || overlap(so, sq) ||
         overlap(so, sk) || overlap(so, sv))
         return LLA_ERR_ALIAS;
-    if (gated) {
-        const Span sg = span(gate, BHq * 4);
+    if (gated) {  // one gate per state
+        const Span sg = span(gate, BHkv * 4);
         if (overlap(ss, sg) || overlap(so, sg)) return LLA_ERR_ALIAS;
     }
     hipStream_t s = (hipStream_t)stream;
+    if (gated && group > 1)
+        return device_status(lla::launch_decode_group_gated(dtype, q, k, v, gate, BHkv, (int)group, (int)dk,
+                                                            (int)dv, S, o, s));
     if (gated)
         return device_status(lla::launch_decode_step_gated(dtype, q, k, v, gate, BHkv, (int)dk, (int)dv, S, o, s));
     if (group > 1)
@@ -340,6 +344,42 @@ lla_status commit_impl(const void* K, const void* V, const float* gate, bool gat
     return device_status(lla::launch_state_commit((lla_dtype)dt_raw, K, V, accepted, B * H, (int)H, (int)T,
                                                   (int)dk, (int)dv, S, s));
 }
+
+// lla_prefill_gated(_gqa); the dtype as its raw integer (a C caller may pass
+// any int, which the C++ enum need not hold).
+lla_status gated_prefill_impl(const void* Q, const void* K, const void* V, const float* gate, int dt_raw,
+                              int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t dk, int64_t dv, int64_t C,
+                              unsigned flags, float* S, float* O, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+    if (flags & ~kKnownFlags) return LLA_ERR_UNSUPPORTED;
+    const bool zero = (flags & LLA_PREFILL_ZERO_STATE) != 0;
+    const bool keep = (flags & LLA_PREFILL_KEEP_STATE) != 0;
+    lla::PrefillPlan p;
+    PrefillBufs b{Q, K, V, nullptr, S, O, nullptr, 0};
+    lla_status st = check_prefill(b, true, true, true, true, false, dt_raw, B, Heads{Hq, Hkv}, T, dk, dv,
+                                  C, p);
+    if (st != LLA_OK) return st;
+    const size_t need = gated_ws_bytes_for(p);
+    if (T > 0 && !gate) return LLA_ERR_NULL;
+    if (need > 0 && (!workspace || workspace_bytes < need)) return LLA_ERR_WORKSPACE;
+    if ((T > 0 && !aligned4(gate)) || (need > 0 && !aligned16(workspace))) return LLA_ERR_ALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    if (T == 0) return zero && !keep ? device_status(lla::launch_fill_zero(S, B * Hkv * dk * dv, s)) : LLA_OK;
+    // The gate is read only; the workspace is written: neither may overlap an
+    // output, and the workspace nothing at all.
+    const int64_t BHq = B * Hq, BHkv = B * Hkv, es = elem_size((lla_dtype)dt_raw);
+    const Span sq = span(Q, BHq * T * dk * es), sk = span(K, BHkv * T * dk * es), sv = span(V, BHkv * T * dv * es);
+    const Span so = span(O, BHq * T * dv * 4), ss = span(S, BHkv * dk * dv * 4), sg = span(gate, BHkv * T * 4);
+    const Span sw = span(need > 0 ? workspace : nullptr, (int64_t)need);
+    if (overlap(so, sg) || overlap(ss, sg)) return LLA_ERR_ALIAS;
+    for (Span x : {sq, sk, sv, so, ss, sg})
+        if (overlap(sw, x)) return LLA_ERR_ALIAS;
+    p.zero_start = zero;
+    p.keep = keep;
+    p.use_ws = need > 0;
+    return device_status(lla::launch_gated_prefill(p, Q, K, V, gate, S, O, (float*)workspace, s));
+}
+
 
 }  // namespace
 
@@ -414,46 +454,40 @@ lla_status lla_decode_step_gqa(const void* q, const void* k, const void* v, lla_
 }
 
 size_t lla_prefill_gated_workspace_size(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int64_t C) {
-    if (check_sizes(B, H, T, dk, dv, C) != LLA_OK) return 0;
-    return gated_ws_bytes_for(make_plan(LLA_BF16, B, Heads{H, H}, T, dk, dv, C));
+    return lla_prefill_gated_gqa_workspace_size(B, H, H, T, dk, dv, C);
+}
+
+size_t lla_prefill_gated_gqa_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t dk, int64_t dv,
+                                            int64_t C) {
+    if (check_heads(Heads{Hq, Hkv}) != LLA_OK || check_sizes(B, Hq, T, dk, dv, C) != LLA_OK) return 0;
+    return gated_ws_bytes_for(make_plan(LLA_BF16, B, Heads{Hq, Hkv}, T, dk, dv, C));
 }
 
 lla_status lla_prefill_gated(const void* Q, const void* K, const void* V, const float* gate, lla_dtype dtype,
                              int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int64_t C, unsigned flags,
                              float* S, float* O, void* workspace, size_t workspace_bytes, void* stream) {
-    if (flags & ~kKnownFlags) return LLA_ERR_UNSUPPORTED;
-    const bool zero = (flags & LLA_PREFILL_ZERO_STATE) != 0;
-    const bool keep = (flags & LLA_PREFILL_KEEP_STATE) != 0;
-    lla::PrefillPlan p;
-    PrefillBufs b{Q, K, V, nullptr, S, O, nullptr, 0};
-    lla_status st = check_prefill(b, true, true, true, true, false, raw_enum(dtype), B, Heads{H, H}, T, dk, dv,
-                                  C, p);
-    if (st != LLA_OK) return st;
-    const size_t need = gated_ws_bytes_for(p);
-    if (T > 0 && !gate) return LLA_ERR_NULL;
-    if (need > 0 && (!workspace || workspace_bytes < need)) return LLA_ERR_WORKSPACE;
-    if ((T > 0 && !aligned4(gate)) || (need > 0 && !aligned16(workspace))) return LLA_ERR_ALIGN;
-    hipStream_t s = (hipStream_t)stream;
-    if (T == 0) return zero && !keep ? device_status(lla::launch_fill_zero(S, B * H * dk * dv, s)) : LLA_OK;
-    // The gate is read only; the workspace is written: neither may overlap an
-    // output, and the workspace nothing at all.
-    const int64_t BH = B * H, es = elem_size((lla_dtype)raw_enum(dtype));
-    const Span sq = span(Q, BH * T * dk * es), sk = span(K, BH * T * dk * es), sv = span(V, BH * T * dv * es);
-    const Span so = span(O, BH * T * dv * 4), ss = span(S, BH * dk * dv * 4), sg = span(gate, BH * T * 4);
-    const Span sw = span(need > 0 ? workspace : nullptr, (int64_t)need);
-    if (overlap(so, sg) || overlap(ss, sg)) return LLA_ERR_ALIAS;
-    for (Span x : {sq, sk, sv, so, ss, sg})
-        if (overlap(sw, x)) return LLA_ERR_ALIAS;
-    p.zero_start = zero;
-    p.keep = keep;
-    p.use_ws = need > 0;
-    return device_status(lla::launch_gated_prefill(p, Q, K, V, gate, S, O, (float*)workspace, s));
+    return gated_prefill_impl(Q, K, V, gate, raw_enum(dtype), B, H, H, T, dk, dv, C, flags, S, O, workspace,
+                              workspace_bytes, stream);
+}
+
+lla_status lla_prefill_gated_gqa(const void* Q, const void* K, const void* V, const float* gate, lla_dtype dtype,
+                                 int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t dk, int64_t dv, int64_t C,
+                                 unsigned flags, float* S, float* O, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+    return gated_prefill_impl(Q, K, V, gate, raw_enum(dtype), B, Hq, Hkv, T, dk, dv, C, flags, S, O, workspace,
+                              workspace_bytes, stream);
 }
 
 lla_status lla_decode_step_gated(const void* q, const void* k, const void* v, const float* gate,
                                  lla_dtype dtype, int64_t B, int64_t H, int64_t dk, int64_t dv, float* S,
                                  float* o, void* stream) {
     return decode_impl(q, k, v, raw_enum(dtype), B, Heads{H, H}, dk, dv, S, o, stream, gate, true);
+}
+
+lla_status lla_decode_step_gated_gqa(const void* q, const void* k, const void* v, const float* gate,
+                                     lla_dtype dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t dk, int64_t dv,
+                                     float* S, float* o, void* stream) {
+    return decode_impl(q, k, v, raw_enum(dtype), B, Heads{Hq, Hkv}, dk, dv, S, o, stream, gate, true);
 }
 
 }  // extern "C"

@@ -283,13 +283,15 @@ __global__ __launch_bounds__(NT) void k_decode_tokens(const Tin* __restrict__ q,
 // of q and o.  For every query head the arithmetic (update, then the state
 // read in row order, then the row-group reduction) is that of
 // k_decode_step_sq, so a group of one gives identical bits.  The query rows
-// are staged in LDS GMAX at a time.
-template <typename Tin, int D, int NT, int GMAX>
+// are staged in LDS GMAX at a time.  GATED: S = g S + k v^T with one gate per
+// key/value head (gate[bh]), as in the gated step.
+template <typename Tin, int D, int NT, int GMAX, bool GATED = false>
 __global__ __launch_bounds__(NT) void k_decode_group(const Tin* __restrict__ q,
                                                      const Tin* __restrict__ k,
                                                      const Tin* __restrict__ v,
                                                      float* __restrict__ S,
-                                                     float* __restrict__ o, int G) {
+                                                     float* __restrict__ o, int G,
+                                                     const float* __restrict__ gate) {
     constexpr int CG = D / 4, RG = NT / CG, RPT = D / RG;
     static_assert(NT % CG == 0 && D % RG == 0, "thread layout must tile the state");
     __shared__ float qs[GMAX][D], ks[D], vs[D];
@@ -309,12 +311,17 @@ __global__ __launch_bounds__(NT) void k_decode_group(const Tin* __restrict__ q,
     for (int m = 0; m < RPT; ++m)
         x[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sb + (rg + m * RG) * D + 4 * cg));
     const f32x4 vj = {vs[4 * cg], vs[4 * cg + 1], vs[4 * cg + 2], vs[4 * cg + 3]};
+    float gm = 1.0f;
+    if constexpr (GATED) gm = decay_gate(gate[bh]);
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
         const int i = rg + m * RG;
         const float ki = ks[i];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) x[m][u] = fmaf(ki, vj[u], x[m][u]);  // rank-1 update
+        for (int u = 0; u < 4; ++u) {
+            if constexpr (GATED) x[m][u] = gm * x[m][u];  // decay
+            x[m][u] = fmaf(ki, vj[u], x[m][u]);          // rank-1 update
+        }
         __builtin_nontemporal_store(x[m], reinterpret_cast<f32x4*>(Sb + i * D + 4 * cg));
     }
     for (int g0 = 0; g0 < G; g0 += GMAX) {
@@ -349,13 +356,14 @@ __global__ __launch_bounds__(NT) void k_decode_group(const Tin* __restrict__ q,
 // row groups of rg_n, rows rg + m * rg_n), with all of a thread's rows in
 // registers at once (RPT * rg_n >= dk, checked by the launcher), so every
 // query head's o has the bits of a plain decode step on the updated state.
-// The query rows are staged in LDS GB at a time.
-template <typename Tin, int VW, int RPT, int GB>
+// The query rows are staged in LDS GB at a time.  GATED as k_decode_group.
+template <typename Tin, int VW, int RPT, int GB, bool GATED = false>
 __global__ __launch_bounds__(kThreads) void k_decode_group_any(const Tin* __restrict__ q,
                                                                const Tin* __restrict__ k,
                                                                const Tin* __restrict__ v,
                                                                float* __restrict__ S,
-                                                               float* __restrict__ o, int dk, int dv, int G) {
+                                                               float* __restrict__ o, int dk, int dv, int G,
+                                                               const float* __restrict__ gate) {
     typedef float vecf __attribute__((ext_vector_type(VW)));
     __shared__ float qs[GB][128], ks[128], vs[128];
     __shared__ float red[kThreads * VW];
@@ -385,13 +393,18 @@ __global__ __launch_bounds__(kThreads) void k_decode_group_any(const Tin* __rest
                     s[m] = Sb[(int64_t)i * dv + j0];
             }
         }
+        float gm = 1.0f;
+        if constexpr (GATED) gm = decay_gate(gate[bh]);
 #pragma unroll
         for (int m = 0; m < RPT; ++m) {
             const int i = rg + m * rg_n;
             if (i < dk) {
                 const float ki = ks[i];
 #pragma unroll
-                for (int u = 0; u < VW; ++u) s[m][u] = fmaf(ki, vj[u], s[m][u]);  // rank-1 update
+                for (int u = 0; u < VW; ++u) {
+                    if constexpr (GATED) s[m][u] = gm * s[m][u];  // decay
+                    s[m][u] = fmaf(ki, vj[u], s[m][u]);          // rank-1 update
+                }
                 if constexpr (VW == 4)
                     __builtin_nontemporal_store(s[m], reinterpret_cast<vecf*>(Sb + (int64_t)i * dv + j0));
                 else
@@ -687,36 +700,48 @@ static int group_any_rows(int dk, int dv, int VW) {
     return (dk + rg_n - 1) / rg_n;
 }
 
-template <typename Tin>
+template <typename Tin, bool GATED>
 static hipError_t group_t(const void* q, const void* k, const void* v, int64_t BHkv, int G, int dk, int dv,
-                          float* S, float* o, hipStream_t st) {
+                          float* S, float* o, const float* gate, hipStream_t st) {
     const Tin *qq = (const Tin*)q, *kk = (const Tin*)k, *vv = (const Tin*)v;
     const dim3 grid((unsigned)BHkv);
     if (dk == 128 && dv == 128)
-        hipLaunchKernelGGL((k_decode_group<Tin, 128, 512, kDecodeGroupBatch>), grid, dim3(512), 0, st, qq, kk, vv,
-                           S, o, G);
+        hipLaunchKernelGGL((k_decode_group<Tin, 128, 512, kDecodeGroupBatch, GATED>), grid, dim3(512), 0, st, qq, kk,
+                           vv, S, o, G, gate);
     else if (dk == 64 && dv == 64)
-        hipLaunchKernelGGL((k_decode_group<Tin, 64, 256, kDecodeGroupBatch>), grid, dim3(256), 0, st, qq, kk, vv,
-                           S, o, G);
+        hipLaunchKernelGGL((k_decode_group<Tin, 64, 256, kDecodeGroupBatch, GATED>), grid, dim3(256), 0, st, qq, kk,
+                           vv, S, o, G, gate);
     else if ((dv & 3) == 0) {
         // dv / 4 <= 32 column groups leave >= 8 row groups: 16 rows each cover dk <= 128
         if (group_any_rows(dk, dv, 4) > 16) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((k_decode_group_any<Tin, 4, 16, kDecodeGroupBatch>), grid, dim3(kThreads), 0, st, qq,
-                           kk, vv, S, o, dk, dv, G);
+        hipLaunchKernelGGL((k_decode_group_any<Tin, 4, 16, kDecodeGroupBatch, GATED>), grid, dim3(kThreads), 0, st,
+                           qq, kk, vv, S, o, dk, dv, G, gate);
     } else {
         // dv <= 128 columns leave >= 2 row groups: 64 rows each cover dk <= 128
         if (group_any_rows(dk, dv, 1) > 64) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((k_decode_group_any<Tin, 1, 64, kDecodeGroupBatch>), grid, dim3(kThreads), 0, st, qq,
-                           kk, vv, S, o, dk, dv, G);
+        hipLaunchKernelGGL((k_decode_group_any<Tin, 1, 64, kDecodeGroupBatch, GATED>), grid, dim3(kThreads), 0, st,
+                           qq, kk, vv, S, o, dk, dv, G, gate);
     }
     return hipGetLastError();
 }
 
+template <bool GATED>
+static hipError_t group_dt(lla_dtype dtype, const void* q, const void* k, const void* v, int64_t BHkv, int group,
+                           int dk, int dv, float* S, float* o, const float* gate, hipStream_t st) {
+    if (dtype == LLA_FP8_E4M3) return group_t<fp8e4m3, GATED>(q, k, v, BHkv, group, dk, dv, S, o, gate, st);
+    if (dtype == LLA_BF16) return group_t<bf16, GATED>(q, k, v, BHkv, group, dk, dv, S, o, gate, st);
+    return group_t<float, GATED>(q, k, v, BHkv, group, dk, dv, S, o, gate, st);
+}
+
 hipError_t launch_decode_group(lla_dtype dtype, const void* q, const void* k, const void* v,
                                int64_t BHkv, int group, int dk, int dv, float* S, float* o, hipStream_t st) {
-    if (dtype == LLA_FP8_E4M3) return group_t<fp8e4m3>(q, k, v, BHkv, group, dk, dv, S, o, st);
-    if (dtype == LLA_BF16) return group_t<bf16>(q, k, v, BHkv, group, dk, dv, S, o, st);
-    return group_t<float>(q, k, v, BHkv, group, dk, dv, S, o, st);
+    return group_dt<false>(dtype, q, k, v, BHkv, group, dk, dv, S, o, nullptr, st);
+}
+
+hipError_t launch_decode_group_gated(lla_dtype dtype, const void* q, const void* k, const void* v,
+                                     const float* gate, int64_t BHkv, int group, int dk, int dv, float* S,
+                                     float* o, hipStream_t st) {
+    return group_dt<true>(dtype, q, k, v, BHkv, group, dk, dv, S, o, gate, st);
 }
 
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st) {

@@ -110,6 +110,10 @@ constexpr int kDecodeGroupMax = 16;  // largest group of the fused short continu
 constexpr int kDecodeGroupBatch = 16;
 hipError_t launch_decode_group(lla_dtype dtype, const void* q, const void* k, const void* v,
                                int64_t BHkv, int group, int dk, int dv, float* S, float* o, hipStream_t st);
+// The same with a decayed state: S = g S + k v^T, one gate per key/value head.
+hipError_t launch_decode_group_gated(lla_dtype dtype, const void* q, const void* k, const void* v,
+                                     const float* gate, int64_t BHkv, int group, int dk, int dv, float* S,
+                                     float* o, hipStream_t st);
 
 // lla_prefill_noalloc: the prefill workspace in a static device array of
 // this many bytes per device (lla_noalloc.hip); *out = its address on the

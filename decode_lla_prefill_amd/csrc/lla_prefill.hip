@@ -1665,7 +1665,7 @@ __global__ __launch_bounds__(kThreads) void k_gated_walk(
     const In* __restrict__ Q, const In* __restrict__ K, const In* __restrict__ V,
     const float* __restrict__ gate, float* __restrict__ S, float* __restrict__ O,
     const float* __restrict__ ws, int64_t T_len, int dk, int dv, int C, int64_t G, int64_t n_seg,
-    int n_vb, int zero_start, int keep) {
+    int n_vb, int group, int zero_start, int keep) {
     using T = typename Compute<In>::type;
     using Cf = WalkCfg<T, CT, D, BV, kWaves>;
     using Fr = typename Cf::Fr;
@@ -1682,7 +1682,9 @@ __global__ __launch_bounds__(kThreads) void k_gated_walk(
     int64_t line;
     int vb;
     split_id(blockIdx.x, (int64_t)(gridDim.x / n_vb), n_vb, line, vb);
-    const int64_t bh = line / n_seg, seg = line - bh * n_seg;
+    // line = (query head, segment); the query heads of a group share the
+    // key/value head bh = bq / group: its K, V, gates and states
+    const int64_t bq = line / n_seg, seg = line - bq * n_seg, bh = bq / group;
     const ScoreTiles<Cf> stiles(w);
     const int v0 = vb * BV;
     const int nv = min(BV, dv - v0);
@@ -1690,11 +1692,11 @@ __global__ __launch_bounds__(kThreads) void k_gated_walk(
     const int64_t c0 = seg * G, c1 = min(n_c, c0 + G);
     const bool last_seg = seg == n_seg - 1;
     const int64_t dkdv = (int64_t)dk * dv;
-    const In* Qb = Q + bh * T_len * dk;
+    const In* Qb = Q + bq * T_len * dk;
     const In* Kb = K + bh * T_len * dk;
     const In* Vb = V + bh * T_len * dv + v0;
     const float* gb = gate + bh * T_len;
-    float* Ob = O + bh * T_len * dv + v0;
+    float* Ob = O + bq * T_len * dv + v0;
 
     // Incoming state of this segment, columns [v0, v0 + nv) (zero_start
     // without a workspace: S_0 = 0, S is not read)
@@ -1766,7 +1768,9 @@ __global__ __launch_bounds__(kThreads) void k_gated_walk(
     }
     if (c1 > c0) store_out<Cf, VEC>(Ob, Oacc, t_prev, n_prev, nv, dv, w, g, c16);
 
-    if (last_seg && !keep) {  // (the loop ended with a barrier); a verify pass leaves S as it was
+    // S_T: one writer per group (the loop ended with a barrier); none for a
+    // verify pass, which leaves S as it was
+    if (last_seg && !keep && bq % group == 0) {
         state_regs_to_lds<Cf>(Sst, Sacc, w, g, c16);
         __syncthreads();
         state_lds_to_gmem<Cf>(S + bh * dkdv + v0, Sst, dk, dv, nv, tid);
@@ -1936,32 +1940,33 @@ static hipError_t launch_gated_walk_t(const PrefillPlan& p, const void* Q, const
         if (p.vec) {  // one eight-wave workgroup per (b,h) and segment
             hipLaunchKernelGGL((k_chunk_walk_wide<CT, In, true>), dim3((unsigned)(p.BHq * p.n_seg)),
                                dim3(kWideWaves * kWave), 0, st, (const In*)Q, (const In*)K, (const In*)V, S, O,
-                               (const float*)(p.use_ws ? ws : nullptr), p.T, p.dk, p.dv, p.C, p.G, p.n_seg, 1,
-                               (int)p.zero_start, (int)p.keep, gate);
+                               (const float*)(p.use_ws ? ws : nullptr), p.T, p.dk, p.dv, p.C, p.G, p.n_seg,
+                               p.group, (int)p.zero_start, (int)p.keep, gate);
             return hipGetLastError();
         }
     }
     constexpr int BV = D > 64 ? 64 : D;
-    const int64_t grid = p.BH * p.n_seg * p.n_vb;
+    const int64_t grid = p.BHq * p.n_seg * p.n_vb;
     const float* wsr = p.use_ws ? ws : nullptr;
     if (p.vec)
         hipLaunchKernelGGL((k_gated_walk<In, CT, D, BV, true>), dim3((unsigned)grid), dim3(kThreads), 0, st,
                            (const In*)Q, (const In*)K, (const In*)V, gate, S, O, wsr, p.T, p.dk, p.dv, p.C, p.G,
-                           p.n_seg, p.n_vb, (int)p.zero_start, (int)p.keep);
+                           p.n_seg, p.n_vb, p.group, (int)p.zero_start, (int)p.keep);
     else
         hipLaunchKernelGGL((k_gated_walk<In, CT, D, BV, false>), dim3((unsigned)grid), dim3(kThreads), 0, st,
                            (const In*)Q, (const In*)K, (const In*)V, gate, S, O, wsr, p.T, p.dk, p.dv, p.C, p.G,
-                           p.n_seg, p.n_vb, (int)p.zero_start, (int)p.keep);
+                           p.n_seg, p.n_vb, p.group, (int)p.zero_start, (int)p.keep);
     return hipGetLastError();
 }
 
 hipError_t launch_gated_prefill(const PrefillPlan& p, const void* Q, const void* K, const void* V,
                                 const float* gate, float* S, float* O, float* ws, hipStream_t st) {
     if (p.n_c == 0) return hipSuccess;
-    if (p.use_ws) {
+    if (p.use_ws) {  // several segments, or several query heads per state (slot 0 = S_0)
         const int64_t dkdv = (int64_t)p.dk * p.dv;
         float* dec = ws + p.BH * p.n_seg * dkdv;  // after the states
-        hipError_t e = [&]() -> hipError_t { LLA_DISPATCH(launch_gated_seg_t, p, K, V, gate, ws, dec, st); }();
+        hipError_t e = hipSuccess;
+        if (p.n_seg > 1) e = [&]() -> hipError_t { LLA_DISPATCH(launch_gated_seg_t, p, K, V, gate, ws, dec, st); }();
         if (e != hipSuccess) return e;
         const int64_t blocks_per_bh = (dkdv + kThreads - 1) / kThreads;
         hipLaunchKernelGGL(k_gated_state_scan, dim3((unsigned)(p.BH * blocks_per_bh)), dim3(kThreads), 0, st, S,

@@ -342,7 +342,8 @@ lla_status lla_decode_step_gqa(const void *q, const void *k, const void *v, lla_
  * With g = 1 this is lla_prefill's recurrence.  gate: fp32, [B][H][T] for
  * the prefill, [B][H] for the decode step, 4-byte aligned, read only.  Gates
  * are taken in [2^-126, 1]: g <= 0 (and NaN) act as 2^-126, g > 1 as 1.
- * One query head per state (no shared-state heads).  Sizes, dtypes, chunk
+ * One query head per state here; the _gqa forms below take shared-state
+ * heads.  Sizes, dtypes, chunk
  * sizes, S, O and the errors are those of lla_prefill; options as
  * lla_prefill_ex: LLA_PREFILL_ZERO_STATE, and LLA_PREFILL_KEEP_STATE for the
  * verify pass of speculative decoding (S not written; then
@@ -373,6 +374,28 @@ lla_status lla_prefill_gated(const void *Q, const void *K, const void *V, const 
 lla_status lla_decode_step_gated(const void *q, const void *k, const void *v, const float *gate,
                                  lla_dtype dtype, int64_t B, int64_t H, int64_t dk, int64_t dv,
                                  float *S, float *o, void *stream);
+
+/*
+ * The gated calls with shared-state heads (as lla_prefill_gqa and
+ * lla_decode_step_gqa): Hq query heads read Hkv decayed states, query head h
+ * the state h / (Hq / Hkv).  The gates belong to the states: gate
+ * [B][Hkv][T] for the prefill, [B][Hkv] for the decode step.  Q, O: Hq
+ * heads; K, V, S: Hkv heads.  The workspace is that of
+ * lla_prefill_gated_gqa_workspace_size (with several query heads per state it
+ * holds the start states even for one segment).  With Hq = Hkv these are the
+ * calls above.  lla_state_commit_gated takes the Hkv states and their gates.
+ */
+size_t lla_prefill_gated_gqa_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t dk,
+                                            int64_t dv, int64_t C);
+
+lla_status lla_prefill_gated_gqa(const void *Q, const void *K, const void *V, const float *gate,
+                                 lla_dtype dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t dk,
+                                 int64_t dv, int64_t C, unsigned flags, float *S, float *O, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+
+lla_status lla_decode_step_gated_gqa(const void *q, const void *k, const void *v, const float *gate,
+                                     lla_dtype dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t dk,
+                                     int64_t dv, float *S, float *o, void *stream);
 
 /*
  * The commit after a gated verify pass (lla_prefill_gated with

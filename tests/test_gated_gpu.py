@@ -252,3 +252,111 @@ def test_gated_commit_with_dyadic_gates_exact_against_the_oracle(dev):
             _, Sr = oracle.gated_decode_step(q[b:b + 1, :, t], kk[b:b + 1, :, t], v[b:b + 1, :, t], g[b:b + 1, :, t],
                                              Sr)
         assert np.array_equal(np64(S[b:b + 1]), Sr), b
+
+
+# ---- shared-state heads with the decayed state -------------------------------------
+
+GQA_CASES = [
+    # B, Hq, Hkv, T, dk, dv, C, dtype
+    (2, 8, 2, 700, 128, 128, 64, torch.bfloat16),    # eight-wave walk, several segments
+    (2, 4, 1, 17, 64, 64, 64, torch.bfloat16),       # one segment: start states staged in the workspace
+    (1, 16, 4, 2000, 128, 128, 128, FP8),            # chunks of 128 as two of 64
+    (1, 6, 2, 300, 64, 64, 32, torch.float32),       # four-wave walk
+    (2, 6, 3, 500, 40, 48, 48, torch.bfloat16),      # dims not multiples of 16
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,dk,dv,C,dtype", GQA_CASES)
+def test_gated_grouped_prefill_within_the_bar(dev, B, Hq, Hkv, T, dk, dv, C, dtype):
+    print("gated grouped prefill", B, Hq, Hkv, T, dk, dv, C, dtype, flush=True)
+    scale = 1.0 if dtype == FP8 else dk ** -0.5
+    q, k, v = workloads.gaussian(B, Hq, T, dk, dv, seed_base=T + Hq, scale=scale, dtype=dtype, Hkv=Hkv)
+    g = workloads.gates(B, Hkv, T, seed=T + 3, lo=0.8, hi=1.0)
+    S0 = torch.randn((B, Hkv, dk, dv), generator=torch.Generator().manual_seed(T))
+    O_ref, S_ref = oracle.gated_grouped_recurrence(q, k, v, g, S0, nthreads=8)
+    for fresh in (False, True):
+        S = torch.zeros_like(S0).to(dev) if fresh else S0.to(dev).contiguous()
+        o = lla.prefill_gated(q.to(dev), k.to(dev), v.to(dev), g.to(dev), S, C, zero_state=fresh)
+        torch.cuda.synchronize()
+        if fresh:
+            O_ref, S_ref = oracle.gated_grouped_recurrence(q, k, v, g, None, nthreads=8)
+        bar = _bar(dtype)
+        assert rel_err(np64(o), O_ref) <= bar and rel_err(np64(S), S_ref) <= bar, fresh
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,d,C", [(1, 8, 2, 1500, 128, 64), (2, 6, 2, 400, 64, 64)])
+def test_gated_grouped_gates_of_one_on_integers_exact(dev, B, Hq, Hkv, T, d, C):
+    q, k, v = workloads.integers(B, Hq, T, d, d, seed=T + d, Hkv=Hkv)
+    g = torch.ones((B, Hkv, T))
+    S0 = torch.randint(-50, 51, (B, Hkv, d, d), generator=torch.Generator().manual_seed(T)).float()
+    S = S0.to(dev)
+    o = lla.prefill_gated(q.to(dev), k.to(dev), v.to(dev), g.to(dev), S, C)
+    torch.cuda.synchronize()
+    O_ref, S_ref = oracle.gated_grouped_recurrence(q, k, v, g, S0, nthreads=8)
+    assert np.array_equal(np64(o), O_ref) and np.array_equal(np64(S), S_ref)
+
+
+@pytest.mark.parametrize("Hq,Hkv,dk,dv,dtype", [(32, 8, 128, 128, torch.bfloat16), (12, 3, 64, 64, torch.float32),
+                                                (40, 2, 128, 128, FP8), (6, 2, 40, 7, torch.bfloat16)])
+def test_gated_grouped_decode_equals_gated_steps_on_repeated_heads(dev, Hq, Hkv, dk, dv, dtype):
+    """Per query head the arithmetic of the gated step (the decay, the
+    update, the state read in row order): bit-equal to gated steps on the
+    key/value heads, states and gates repeated over each group."""
+    B, G = 5, Hq // Hkv
+    gen = torch.Generator(device=dev).manual_seed(Hq + dk)
+    q = torch.randn((B, Hq, dk), generator=gen, device=dev).to(dtype)
+    k = torch.randn((B, Hkv, dk), generator=gen, device=dev).to(dtype)
+    v = torch.randn((B, Hkv, dv), generator=gen, device=dev).to(dtype)
+    gt = torch.rand((B, Hkv), generator=gen, device=dev) * 0.5 + 0.5
+    S0 = torch.randn((B, Hkv, dk, dv), generator=gen, device=dev)
+    S_g = S0.clone()
+    o_g = lla.decode_step_gated(q, k, v, gt, S_g)
+    S_r = S0.repeat_interleave(G, dim=1).contiguous()
+    o_r = lla.decode_step_gated(q, k.repeat_interleave(G, dim=1).contiguous(), v.repeat_interleave(G, dim=1).contiguous(),
+                                gt.repeat_interleave(G, dim=1).contiguous(), S_r)
+    torch.cuda.synchronize()
+    assert torch.equal(o_g, o_r)
+    assert torch.equal(S_g, S_r[:, ::G])
+
+
+def test_gated_grouped_decode_dyadic_gates_integers_exact(dev):
+    B, Hq, Hkv, dk, dv = 3, 8, 2, 64, 24
+    q, k, v = workloads.integers(B, Hq, 3, dk, dv, seed=5, Hkv=Hkv)
+    g = torch.tensor([1.0, 0.5, 0.25])[torch.randint(0, 3, (B, Hkv, 3), generator=torch.Generator().manual_seed(6))]
+    S = torch.randint(-8, 9, (B, Hkv, dk, dv), generator=torch.Generator().manual_seed(7)).float()
+    Sd = S.to(dev)
+    Sr = S.double().numpy()
+    for t in range(3):
+        o = lla.decode_step_gated(q[:, :, t].contiguous().to(dev), k[:, :, t].contiguous().to(dev),
+                                  v[:, :, t].contiguous().to(dev), g[:, :, t].contiguous().to(dev), Sd)
+        torch.cuda.synchronize()
+        o_ref, Sr = oracle.gated_grouped_decode_step(q[:, :, t], k[:, :, t], v[:, :, t], g[:, :, t], Sr)
+        assert np.array_equal(np64(o), o_ref), t
+    assert np.array_equal(np64(Sd), Sr)
+
+
+def test_gated_grouped_verify_pass_and_commit(dev):
+    """Shared-state heads with a decayed state: the verify pass equals the
+    plain gated prefill and leaves S; the commit (on the key/value states)
+    equals m_b gated decode steps."""
+    B, Hq, Hkv, k, d, C = 4, 8, 2, 12, 128, 64
+    q, kk, v = workloads.gaussian(B, Hq, k, d, d, seed_base=31, scale=d ** -0.5, device=dev, Hkv=Hkv)
+    g = workloads.gates(B, Hkv, k, seed=32, lo=0.5, hi=1.0, device=dev)
+    S0 = torch.randn((B, Hkv, d, d), generator=torch.Generator(device=dev).manual_seed(33), device=dev)
+    S = S0.clone()
+    o = lla.prefill_gated(q, kk, v, g, S, C, keep_state=True)
+    S_plain = S0.clone()
+    o_plain = lla.prefill_gated(q, kk, v, g, S_plain, C)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_plain) and torch.equal(S, S0)
+    accepted = [0, 5, 12, 7]
+    lla.state_commit_gated(kk, v, g, S, torch.tensor(accepted, dtype=torch.int32, device=dev))
+    Sd, want = S0.clone(), S0.clone()
+    for t in range(max(accepted)):
+        lla.decode_step_gated(q[:, :, t].contiguous(), kk[:, :, t].contiguous(), v[:, :, t].contiguous(),
+                              g[:, :, t].contiguous(), Sd)
+        for b in range(B):
+            if accepted[b] == t + 1:
+                want[b] = Sd[b]
+    torch.cuda.synchronize()
+    assert torch.equal(S, want)

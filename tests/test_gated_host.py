@@ -29,6 +29,13 @@ def lib():
     L.lla_prefill_segment_chunks.argtypes = [i64] * 6
     L.lla_decode_step_gated.restype = ctypes.c_int
     L.lla_decode_step_gated.argtypes = [vp, vp, vp, vp, ctypes.c_int] + [i64] * 4 + [vp, vp, vp]
+    L.lla_prefill_gated_gqa.restype = ctypes.c_int
+    L.lla_prefill_gated_gqa.argtypes = ([vp, vp, vp, vp, ctypes.c_int] + [i64] * 7 + [ctypes.c_uint] +
+                                        [vp, vp, vp, sz, vp])
+    L.lla_prefill_gated_gqa_workspace_size.restype = sz
+    L.lla_prefill_gated_gqa_workspace_size.argtypes = [i64] * 7
+    L.lla_decode_step_gated_gqa.restype = ctypes.c_int
+    L.lla_decode_step_gated_gqa.argtypes = [vp, vp, vp, vp, ctypes.c_int] + [i64] * 5 + [vp, vp, vp]
     L.lla_state_commit_gated.restype = ctypes.c_int
     L.lla_state_commit_gated.argtypes = [vp, vp, vp, ctypes.c_int] + [i64] * 5 + [vp, vp, vp]
     return L
@@ -123,3 +130,49 @@ def test_state_commit_gated_rejects(lib, change, expect):
 
 def test_state_commit_gated_of_no_tokens_is_a_noop(lib):
     assert _commit(lib, T=0, k=None, v=None, gate=None) == OK
+
+
+def _prefill_gqa(lib, **change):
+    d = dict(q=A, k=2 * A, v=3 * A, gate=7 * A, dtype=BF16, B=1, Hq=8, Hkv=2, T=100, dk=64, dv=64, C=64, flags=0,
+             S=4 * A, O=5 * A, ws=6 * A, ws_bytes=1 << 30)
+    d.update(change)
+    return lib.lla_prefill_gated_gqa(d["q"], d["k"], d["v"], d["gate"], d["dtype"], d["B"], d["Hq"], d["Hkv"],
+                                     d["T"], d["dk"], d["dv"], d["C"], d["flags"], d["S"], d["O"], d["ws"],
+                                     d["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("change,expect", [
+    (dict(Hkv=3), E_SHAPE), (dict(Hq=1), E_SHAPE), (dict(Hkv=0), E_SHAPE), (dict(gate=None), E_NULL),
+    (dict(dtype=9), E_DTYPE), (dict(flags=4), E_UNSUP),
+    # one segment, but grouped heads stage their start states: a workspace is needed
+    (dict(ws=None), E_WS), (dict(ws_bytes=16), E_WS),
+    # the gate holds one value per state and token: B * Hkv * T = 200 floats
+    (dict(gate=4 * A + 64), E_ALIAS), (dict(O=7 * A + 784), E_ALIAS),
+])
+def test_prefill_gated_gqa_rejects(lib, change, expect):
+    assert _prefill_gqa(lib, **change) == expect
+
+
+def test_gated_gqa_workspace_stages_the_start_states_of_grouped_heads(lib):
+    # 50 tokens, one chunk, 2 states: one segment, yet a slot and a decay per state
+    assert lib.lla_prefill_gated_gqa_workspace_size(1, 8, 2, 50, 64, 64, 64) == 2 * 1 * (64 * 64 + 1) * 4
+    assert lib.lla_prefill_gated_gqa_workspace_size(1, 2, 2, 50, 64, 64, 64) == 0
+    # 100 tokens: two chunks, one segment each
+    assert lib.lla_prefill_gated_gqa_workspace_size(1, 8, 2, 100, 64, 64, 64) == 2 * 2 * (64 * 64 + 1) * 4
+    for args in [(1, 16, 8192, 128, 128, 64), (2, 3, 100, 32, 32, 32)]:
+        B, H = args[0], args[1]
+        assert lib.lla_prefill_gated_gqa_workspace_size(B, H, H, *args[2:]) == \
+            lib.lla_prefill_gated_workspace_size(*args)
+
+
+def test_decode_step_gated_gqa_rejects(lib):
+    args = dict(q=A, k=2 * A, v=3 * A, gate=7 * A, dtype=BF16, B=2, Hq=8, Hkv=2, dk=128, dv=128, S=4 * A, o=5 * A)
+
+    def call(**change):
+        d = dict(args, **change)
+        return lib.lla_decode_step_gated_gqa(d["q"], d["k"], d["v"], d["gate"], d["dtype"], d["B"], d["Hq"],
+                                             d["Hkv"], d["dk"], d["dv"], d["S"], d["o"], None)
+    assert call(Hkv=3) == E_SHAPE
+    assert call(gate=None) == E_NULL
+    assert call(gate=7 * A + 2) == E_ALIGN
+    assert call(gate=4 * A + 64) == E_ALIAS  # inside S
