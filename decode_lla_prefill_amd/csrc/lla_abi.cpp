@@ -283,7 +283,7 @@ lla_status prefill_impl(const void* Q, const void* K, const void* V, int dt_raw,
     return device_status(lla::launch_chunk_walk(p, Q, K, V, S, O, ws, s));
 }
 
-// gate: null, or one gate per (b,h) (gated step, one query head per state).
+// gate: null, or one gate per state (the gated step), [B][Hkv].
 lla_status decode_impl(const void* q, const void* k, const void* v, int dt_raw, int64_t B,
                        Heads h, int64_t dk, int64_t dv, float* S, float* o, void* stream,
                        const float* gate = nullptr, bool gated = false) {

@@ -1263,9 +1263,9 @@ struct WideCfg : WalkCfg<bf16, CT, 128, 128, kWideWaves> {
     static constexpr int BYTES = (2 * BUF + Base::NP * Base::P_ELEMS) * 2;
 };
 
-// GATED: the gated walk (see k_gated_walk) with one query head per state;
-// the chunk's decay prefix is double buffered (Bs2), written for chunk c + 1
-// by wave 0 while chunk c is computed.
+// GATED: the gated walk (see k_gated_walk), the gates those of the key/value
+// head; the chunk's decay prefix is double buffered (Bs2), written for chunk
+// c + 1 by wave 0 while chunk c is computed.
 template <int CT, typename In, bool GATED = false>
 __global__ __launch_bounds__(kWideWaves * kWave) void k_chunk_walk_wide(
     const In* __restrict__ Q, const In* __restrict__ K, const In* __restrict__ V,

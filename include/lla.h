@@ -405,8 +405,9 @@ lla_status lla_decode_step_gated_gqa(const void *q, const void *k, const void *v
  * with the gated decode step's per-element arithmetic (the decay, then one
  * fmaf), so S equals the state of m_b gated decode steps bit for bit.  gate:
  * the verify pass's [B][H][T] gates (4-byte aligned, read only); the other
- * arguments, limits and errors as lla_state_commit (H heads per sequence,
- * one query head per state).  For callers with a decayed state that
+ * arguments, limits and errors as lla_state_commit (H states per sequence:
+ * with shared-state heads, the Hkv states and their gates).  For callers with
+ * a decayed state that
  * speculate (blog "A 128 000 tokens, l'attention avale 85 % du calcul", on
  * speculative decoding adding tokens per decode iteration).
  */
