@@ -1639,22 +1639,50 @@ __global__ __launch_bounds__(kThreads) void k_gated_segment_states(
 }
 
 // Gated phase 2: slot 0 = S_0, slot s = 2^{L_{s-1}} slot (s-1) + increment
-// (s - 1).  One thread per state element of one (b,h).
+// (s - 1).  Four consecutive state elements of one (b,h) per thread.
 __global__ __launch_bounds__(kThreads) void k_gated_state_scan(const float* __restrict__ S,
                                                                float* __restrict__ ws,
                                                                const float* __restrict__ dec,
                                                                int64_t n_seg, int64_t dkdv,
                                                                int64_t blocks_per_bh, int zero_start) {
     const int64_t bh = blockIdx.x / blocks_per_bh;
-    const int64_t e = (blockIdx.x % blocks_per_bh) * kThreads + threadIdx.x;
+    const int64_t e = ((blockIdx.x % blocks_per_bh) * kThreads + threadIdx.x) * 4;
     if (e >= dkdv) return;
     float* slot = ws + bh * n_seg * dkdv + e;
     const float* L = dec + bh * n_seg;
-    float acc = zero_start ? 0.0f : S[bh * dkdv + e];
-    slot[0] = acc;
-    for (int64_t s = 1; s < n_seg; ++s) {
-        acc = fmaf(exp2f(L[s - 1]), acc, slot[s * dkdv]);
-        slot[s * dkdv] = acc;
+    const float* s0 = S + bh * dkdv + e;
+    if (e + 4 <= dkdv && (dkdv & 3) == 0) {
+        // as k_state_scan: slot 0 and the first U increments loaded together,
+        // then folded in segment order (slot 0 is written even for a single
+        // segment: grouped heads read their start state there)
+        constexpr int U = 16;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (!zero_start) acc = *reinterpret_cast<const f32x4*>(s0);
+        for (int64_t s = 1; s < n_seg || s == 1; s += U) {
+            f32x4 x[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (s + u < n_seg) x[u] = *reinterpret_cast<const f32x4*>(slot + (s + u) * dkdv);
+            if (s == 1) *reinterpret_cast<f32x4*>(slot) = acc;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (s + u < n_seg) {
+                    const float f = exp2f(L[s + u - 1]);  // the previous segment's total decay
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[r] = fmaf(f, acc[r], x[u][r]);
+                    *reinterpret_cast<f32x4*>(slot + (s + u) * dkdv) = acc;
+                }
+        }
+    } else {
+        const int m = (int)min((int64_t)4, dkdv - e);
+        for (int j = 0; j < m; ++j) {
+            float acc = zero_start ? 0.0f : s0[j];
+            slot[j] = acc;
+            for (int64_t s = 1; s < n_seg; ++s) {
+                acc = fmaf(exp2f(L[s - 1]), acc, slot[s * dkdv + j]);
+                slot[s * dkdv + j] = acc;
+            }
+        }
     }
 }
 
@@ -1968,7 +1996,8 @@ hipError_t launch_gated_prefill(const PrefillPlan& p, const void* Q, const void*
         hipError_t e = hipSuccess;
         if (p.n_seg > 1) e = [&]() -> hipError_t { LLA_DISPATCH(launch_gated_seg_t, p, K, V, gate, ws, dec, st); }();
         if (e != hipSuccess) return e;
-        const int64_t blocks_per_bh = (dkdv + kThreads - 1) / kThreads;
+        const int64_t per_block = (int64_t)kThreads * 4;  // four elements per thread
+        const int64_t blocks_per_bh = (dkdv + per_block - 1) / per_block;
         hipLaunchKernelGGL(k_gated_state_scan, dim3((unsigned)(p.BH * blocks_per_bh)), dim3(kThreads), 0, st, S,
                            ws, dec, p.n_seg, dkdv, blocks_per_bh, (int)p.zero_start);
         e = hipGetLastError();
