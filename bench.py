@@ -236,12 +236,15 @@ def measure_peaks(torch):
     }
 
 
-# the walk kernel of each prefill workload: (label, key of its counter summary)
+# the walk kernel of each prefill workload: (label, key of its counter summary,
+# whether a fresh-prompt step is that one kernel alone -- the one-launch walk,
+# whose workgroups sum the earlier segments themselves)
 WALK_OF_CONFIG = {
-    "prefill_T8192": ("k_chunk_walk_wide<64> (bf16, d=128)", "chunk_walk"),
-    "prefill_B4_T1024": ("k_chunk_walk<bf16,64,64,64> (four waves, d=64, C=64)", "chunk_walk_T1024"),
+    "prefill_T8192": ("k_chunk_walk_wide<64> (bf16, d=128)", "chunk_walk", False),
+    "prefill_B4_T1024": ("k_chunk_walk<bf16,64,64,64,...,one launch> (four waves, d=64, C=64; the whole "
+                         "fresh-prompt step)", "chunk_walk_T1024", True),
     "prefill_T131072": ("k_chunk_walk_wide<64> (bf16, d=128; C=128 run as two 64-token chunks)",
-                        "chunk_walk_T131072"),
+                        "chunk_walk_T131072", False),
 }
 
 
@@ -296,12 +299,18 @@ def bench_prefill(args, torch, lla, workloads, profiling):
     # sets between two events.  Every set's workspace holds its segment
     # states from the pass above, and a walk reads only those, q, k and v, so
     # the repeated walks are the same work as the one inside a step.
+    # A workload whose fresh-prompt step is the one-launch walk times the
+    # steps themselves.
+    one_launch = WALK_OF_CONFIG.get(args.prefill_config, (None, None, False))[2]
     n_walk = max(args.steps, 4 * n_sets)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
     for i in range(n_walk):
-        sets[i % n_sets].chunks()
+        if one_launch:
+            sets[i % n_sets](zero_state=True)
+        else:
+            sets[i % n_sets].chunks()
     e1.record(stream)
     torch.cuda.synchronize()
     walk_launch_ms = e0.elapsed_time(e1) / n_walk
@@ -313,8 +322,9 @@ def bench_prefill(args, torch, lla, workloads, profiling):
         "config": {"workload": cfg.name, "B": B, "H": H, "T": T, "C": C, "dk": d, "dv": d,
                    "inputs": "bf16 N(0,1)/sqrt(128), K rows L2-normalised; fp32 state and output",
                    "cache": "cold: %d rotating input/output sets of %.0f MB" % (n_sets, nbytes / 1e6),
-                   "step": "one fresh-prompt lla_prefill_ex (S_0 = 0): per-segment K^T V, "
-                           "segment scan, chunk walk"},
+                   "step": "one fresh-prompt lla_prefill_ex (S_0 = 0): " + (
+                       "one launch, each segment's walk summing the earlier segments' K^T V" if one_launch
+                       else "per-segment K^T V, segment scan, chunk walk")},
         "value": B * T / (ms_step * 1e-3),
         "ms_per_step": ms_step,
         "gpu_ms_per_step": gpu * 1e3 / args.steps,
@@ -506,7 +516,10 @@ def bench_other_prefills(args, torch, lla, workloads, profiling):
         wall_w, _ = _timed(torch, lambda i: sets[0](zero_state=True), steps)
         warm_spread = spread(_step_events(torch, lambda i: sets[0](zero_state=True), steps))
         n_walk = max(steps, 2 * rotate)
-        _, walk_s = _timed(torch, lambda i: sets[i % rotate].chunks(), n_walk)
+        if walks[name][2]:  # the step is the walk
+            _, walk_s = _timed(torch, lambda i: sets[i % rotate](zero_state=True), n_walk)
+        else:
+            _, walk_s = _timed(torch, lambda i: sets[i % rotate].chunks(), n_walk)
         walk_ms = walk_s * 1e3 / n_walk
         flops, nbytes = prefill_work(B, H, T, C, d)
         step_s = gpu / steps
@@ -522,7 +535,9 @@ def bench_other_prefills(args, torch, lla, workloads, profiling):
                 "cache": "cold: %d rotating input/output sets of %.0f MB" % (rotate, nbytes / 1e6),
                 "roofline": hbm_roofline(walks[name][0], nbytes, walk_ms, args.gap_ms,
                                          profiling.stored_traffic(walks[name][1]),
-                                         "HIP events around %d back-to-back walk launches" % n_walk)}
+                                         "HIP events around %d back-to-back %s" % (
+                                             n_walk, "fresh-prompt steps (one launch each)" if walks[name][2]
+                                             else "walk launches"))}
         del sets
         torch.cuda.empty_cache()
         if not args.no_cpu_baseline:

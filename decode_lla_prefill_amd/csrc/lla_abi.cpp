@@ -276,10 +276,13 @@ lla_status prefill_impl(const void* Q, const void* K, const void* V, int dt_raw,
                                                        zero, keep, s));
     }
     float* ws = (float*)workspace;
-    st = device_status(lla::launch_segment_states(p, K, V, ws, s));
-    if (st != LLA_OK) return st;
-    st = device_status(lla::launch_state_scan(p, S, ws, s));
-    if (st != LLA_OK) return st;
+    p.prefix = lla::prefix_walk_fits(p);
+    if (!p.prefix) {
+        st = device_status(lla::launch_segment_states(p, K, V, ws, s));
+        if (st != LLA_OK) return st;
+        st = device_status(lla::launch_state_scan(p, S, ws, s));
+        if (st != LLA_OK) return st;
+    }
     return device_status(lla::launch_chunk_walk(p, Q, K, V, S, O, ws, s));
 }
 

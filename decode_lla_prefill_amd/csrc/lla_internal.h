@@ -48,11 +48,27 @@ struct PrefillPlan {
     bool vec;     // 16-byte vector loads possible (dk, dv multiples of one vector)
     bool zero_start;  // S_0 = 0: S is written (S_T) but not read
     bool keep;        // the verify pass: S is read (unless zero_start) but never written
+    bool prefix;      // one launch: every walk sums the segments before its own (prefix_walk_fits)
     lla_dtype dtype;
 };
 
 // Fills the derived fields from B, H, T, dk, dv, C, dtype (already validated).
 void plan_prefill(PrefillPlan& p);
+
+// Whether lla_prefill runs as one walk whose workgroups sum the earlier
+// segments' K^T V themselves (same bits as the three phases): bf16 or FP8
+// inputs on the four-wave walk, several segments, S not both read and
+// written (a fresh prompt or a verify pass), and at most kPrefixMaxChunks
+// chunks before the last segment.  Measured: at 12-15 chunks before the
+// last segment the one launch is 0-16 % faster than the three phases (2-4 µs
+// saved on 10-25 µs steps), at 28-60 chunks 20-90 % slower; fp32 inputs,
+// whose state hop costs more, were slower at 14.  Needs zero_start and
+// keep set.
+#ifndef LLA_PREFIX_MAX_CHUNKS
+#define LLA_PREFIX_MAX_CHUNKS 16
+#endif
+constexpr int64_t kPrefixMaxChunks = LLA_PREFIX_MAX_CHUNKS;
+bool prefix_walk_fits(const PrefillPlan& p);
 
 hipError_t launch_segment_states(const PrefillPlan& p, const void* K, const void* V,
                                  float* ws, hipStream_t st);

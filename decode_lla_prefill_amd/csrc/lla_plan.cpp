@@ -51,6 +51,13 @@ void plan_prefill(PrefillPlan& p) {
     p.use_ws = p.n_seg > 1 || p.group > 1;
     const int ve = p.dtype == LLA_FP8_E4M3 ? 16 : (p.dtype == LLA_BF16 ? 8 : 4);  // per 16 bytes
     p.vec = (p.dk % ve == 0) && (p.dv % ve == 0);
+    p.prefix = false;
+}
+
+bool prefix_walk_fits(const PrefillPlan& p) {
+    // bf16 or FP8 on the four-wave walk (d = 128 in whole vectors takes the eight-wave walk)
+    if (p.dtype == LLA_F32 || (p.D == 128 && p.vec)) return false;
+    return p.n_seg > 1 && (p.zero_start || p.keep) && (p.n_seg - 1) * p.G <= kPrefixMaxChunks;
 }
 
 }  // namespace lla

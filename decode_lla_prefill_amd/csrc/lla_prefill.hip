@@ -199,6 +199,14 @@ __device__ __forceinline__ void split_id(int64_t id, int64_t n_lines, int n_vb, 
     line = 8 * grp + off % r;
 }
 
+// Workgroup id -> work unit such that units u, u + 1, ... share an XCD:
+// ids go round-robin over the 8 XCDs, so XCD x takes the ids congruent to x
+// mod 8 and receives a contiguous range of units (a bijection on [0, n)).
+__device__ __forceinline__ int64_t xcd_major(int64_t id, int64_t n) {
+    const int64_t x = id & 7, k = id >> 3, q = n >> 3, r = n & 7;
+    return x * q + min(x, r) + k;
+}
+
 // The value-column operand slices of a wave: V[32 ts + (time slot)][16 vt + c16].
 template <typename Cf, typename T>
 __device__ __forceinline__ void load_vfrags(typename Cf::Fr (&Vf)[Cf::NVW][Cf::NTS], const T* Vs,
@@ -889,7 +897,15 @@ __device__ __forceinline__ void store_out(float* Ob, const f32x4 (&Oacc)[Cf::NT]
     }
 }
 
-template <typename In, int CT, int D, int BV, bool VEC, int NW = kWaves>
+// PREFIX: the walk of a fresh prompt or a verify pass (S is not both read
+// and written) with few chunks before its last segment.  Instead of reading
+// its start state from the workspace, each workgroup sums the earlier
+// segments' K^T V itself: every segment's sum from zero over its chunks
+// (the segment pass's products, in its order), each added to S_0 in segment
+// order (the scan's additions) -- so the bits of the three phases, in one
+// launch.  The lines of a query head are given workgroup ids that share an
+// XCD, so the K and V rows they all read come from one L2.
+template <typename In, int CT, int D, int BV, bool VEC, int NW = kWaves, bool PREFIX = false>
 __global__ __launch_bounds__(NW * kWave) void k_chunk_walk(
     const In* __restrict__ Q, const In* __restrict__ K, const In* __restrict__ V,
     float* __restrict__ S, float* __restrict__ O, const float* __restrict__ ws, int64_t T_len,
@@ -908,7 +924,13 @@ __global__ __launch_bounds__(NW * kWave) void k_chunk_walk(
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     int64_t line;
     int vb;
-    split_id(blockIdx.x, (int64_t)(gridDim.x / n_vb), n_vb, line, vb);
+    if constexpr (PREFIX) {
+        const int64_t u = xcd_major(blockIdx.x, gridDim.x);  // (line, value block), line-major
+        line = u / n_vb;
+        vb = (int)(u - line * n_vb);
+    } else {
+        split_id(blockIdx.x, (int64_t)(gridDim.x / n_vb), n_vb, line, vb);
+    }
     // line = (query head, segment); the query heads of a group share the
     // key/value head bh = bq / group: its K, V and states
     const int64_t bq = line / n_seg, seg = line - bq * n_seg, bh = bq / group;
@@ -937,6 +959,68 @@ __global__ __launch_bounds__(NW * kWave) void k_chunk_walk(
     using TQ = Tile<T, CT, D, typename Cf::LQL, Cf::NTH, In>;
     using TK = Tile<T, CT, D, typename Cf::LKL, Cf::NTH, In>;
     using TV = Tile<T, CT, BV, typename Cf::LVL, Cf::NTH, In>;
+    if constexpr (PREFIX) {
+        // Chunks [0, c0): segment by segment, each summed from zero over its
+        // G chunks and then added to S.  All full (only a sequence's last
+        // chunk is short, and it lies in the last segment).
+        f32x4 Inc[Cf::NVW][Cf::NDT];
+#pragma unroll
+        for (int vw = 0; vw < Cf::NVW; ++vw)
+#pragma unroll
+            for (int dt = 0; dt < Cf::NDT; ++dt) Inc[vw][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        auto hop = [&](int64_t c) {  // chunk c staged in Ks, Vs
+            Fr Vf[Cf::NVW][Cf::NTS];
+            load_vfrags<Cf>(Vf, Vs, w, g, lane);
+            state_hop<Cf>(Inc, Vf, Ks, w, g, lane);
+            if (c % G == G - 1) {  // a segment's sum is complete
+#pragma unroll
+                for (int vw = 0; vw < Cf::NVW; ++vw)
+#pragma unroll
+                    for (int dt = 0; dt < Cf::NDT; ++dt) {
+                        Sacc[vw][dt] += Inc[vw][dt];
+                        Inc[vw][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    }
+            }
+        };
+        if constexpr (VEC) {
+            constexpr int PF = 2;  // chunks of loads in flight (register sets used round robin)
+            TK pk[PF];
+            TV pv[PF];
+#pragma unroll
+            for (int u = 0; u < PF; ++u) {
+                pk[u].init(dk, dk, tid);
+                pv[u].init(dv, nv, tid);
+                if (u < c0) {
+                    pk[u].gather(Kb + u * C * dk, dk, C);
+                    pv[u].gather(Vb + u * C * dv, dv, C);
+                }
+            }
+            for (int64_t c = 0; c < c0; c += PF) {
+#pragma unroll
+                for (int u = 0; u < PF; ++u) {
+                    const int64_t cc = c + u;
+                    if (cc >= c0) break;
+                    pk[u].scatter(Ks, tid);
+                    pv[u].scatter(Vs, tid);
+                    __syncthreads();
+                    if (cc + PF < c0) {
+                        pk[u].gather(Kb + (cc + PF) * C * dk, dk, C);
+                        pv[u].gather(Vb + (cc + PF) * C * dv, dv, C);
+                    }
+                    hop(cc);
+                    __syncthreads();
+                }
+            }
+        } else {
+            for (int64_t c = 0; c < c0; ++c) {
+                TK::load_scalar(Kb + c * C * dk, dk, C, dk, Ks, tid);
+                TV::load_scalar(Vb + c * C * dv, dv, C, nv, Vs, tid);
+                __syncthreads();
+                hop(c);
+                __syncthreads();
+            }
+        }
+    }
     TQ tq;
     TK tk;
     TV tv;
@@ -1827,6 +1911,21 @@ static hipError_t launch_walk_t(const PrefillPlan& p, const void* Q, const void*
     constexpr int BV = D > 64 ? 64 : D;
     const int64_t grid = p.BHq * p.n_seg * p.n_vb;
     const float* wsr = p.use_ws ? ws : nullptr;
+    if constexpr (!std::is_same<In, float>::value) {  // (fp32 inputs keep the three phases)
+        if (p.prefix) {  // no workspace: each walk sums the segments before its own
+            if (p.vec)
+                hipLaunchKernelGGL((k_chunk_walk<In, CT, D, BV, true, kWaves, true>), dim3((unsigned)grid),
+                                   dim3(kThreads), 0, st, (const In*)Q, (const In*)K, (const In*)V, S, O,
+                                   (const float*)nullptr, p.T, p.dk, p.dv, p.C, p.G, p.n_seg, p.n_vb, p.group,
+                                   (int)p.zero_start, (int)p.keep);
+            else
+                hipLaunchKernelGGL((k_chunk_walk<In, CT, D, BV, false, kWaves, true>), dim3((unsigned)grid),
+                                   dim3(kThreads), 0, st, (const In*)Q, (const In*)K, (const In*)V, S, O,
+                                   (const float*)nullptr, p.T, p.dk, p.dv, p.C, p.G, p.n_seg, p.n_vb, p.group,
+                                   (int)p.zero_start, (int)p.keep);
+            return hipGetLastError();
+        }
+    }
     if (p.vec)
         hipLaunchKernelGGL((k_chunk_walk<In, CT, D, BV, true>), dim3((unsigned)grid), dim3(kThreads), 0,
                            st, (const In*)Q, (const In*)K, (const In*)V, S, O, wsr, p.T,

@@ -75,7 +75,10 @@ KERNELS = {
     "chunk_walk_fp8": (("k_chunk_walk_wideILi64ENS_7fp8e4m3ELb0E", "k_chunk_walk_wide<64, lla::fp8e4m3, false>"),
                        16 * 16 * 512, "chunk_walk_T8192_fp8_traffic.txt",
                        PREFILL_SOURCES, "prefill_T8192_fp8"),
-    "chunk_walk_T1024": (("k_chunk_walkIDF16bLi64ELi64ELi64ELb1ELi4E", "k_chunk_walk<__bf16, 64, 64, 64, true, 4>"),
+    # a fresh T=1024 prompt is one launch: the four-wave walk whose
+    # workgroups sum the earlier segments themselves (the last template flag)
+    "chunk_walk_T1024": (("k_chunk_walkIDF16bLi64ELi64ELi64ELb1ELi4ELb1E",
+                          "k_chunk_walk<__bf16, 64, 64, 64, true, 4, true>"),
                          32 * 8 * 256, "chunk_walk_B4_T1024_traffic.txt",
                          PREFILL_SOURCES, "prefill_B4_T1024"),
     # chunks of 128 run as two of 64 on the wide walk (counters from a run of
@@ -197,7 +200,7 @@ def run(launches: int, which=DEFAULT_RUN) -> None:
                 S = torch.empty((cfg.B, cfg.kv_heads, cfg.dk, cfg.dv), device=dev)
                 sets.append(PreparedPrefill(q, k, v, S, cfg.C))
             for i in range(launches):
-                sets[i % rotate](zero_state=True)  # a fresh prompt: K^T V, scan, walk
+                sets[i % rotate](zero_state=True)  # a fresh prompt: K^T V, scan, walk (or the one-launch walk)
             torch.cuda.synchronize()
             del sets, q0, k0, v0
         elif name == "decode_B256":

@@ -266,6 +266,14 @@ lla_status lla_prefill_gqa(const void *Q, const void *K, const void *V, lla_dtyp
  * this is lla_prefill; the workspace is that of lla_prefill_gqa_workspace_size.
  * Results with LLA_PREFILL_ZERO_STATE equal those of lla_state_init followed
  * by the call without it, bit for bit.
+ *
+ * With either option S is not both read and written, and a shape with
+ * several segments but at most 16 chunks (of c tokens) before its last
+ * segment -- bf16 or FP8 inputs, head dims up to 64 (or rows that are not
+ * whole 16-byte vectors) -- runs as one kernel: every segment's walk sums the
+ * earlier segments' K^T V itself, in the order of the segment pass and the
+ * scan, so the results are the bits of the three phases.  The workspace is
+ * not written on that route (its content on return is unspecified).
  */
 lla_status lla_prefill_ex(const void *Q, const void *K, const void *V, lla_dtype dtype,
                           int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t dk,

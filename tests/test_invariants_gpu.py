@@ -193,3 +193,67 @@ def test_prepared_fresh_prompt_repeats(dev):
     assert torch.equal(o1, o2) and torch.equal(S1, S)
     O_ref, S_ref = oracle.recurrence(q.cpu(), k.cpu(), v.cpu(), nthreads=8)
     assert rel_err(np64(o2), O_ref) <= TOL and rel_err(np64(S), S_ref) <= TOL
+
+
+# B, Hq, Hkv, T, dk, dv, C, dtype: shapes whose fresh prompts lla_prefill runs
+# as one launch (the walks sum the earlier segments themselves): the T=1024
+# workload (8 segments of 2 chunks), 32-row tiles with a short last chunk,
+# two value blocks (fp32, D = 128), the element path (dk, dv not whole
+# vectors), FP8 with chunks of 100 run as two of 50 (16 chunks before the
+# last segment, the most this route takes), shared-state heads
+ONE_LAUNCH_CASES = [
+    (4, 8, 8, 1024, 64, 64, 64, torch.bfloat16),
+    (2, 4, 4, 500, 64, 64, 32, torch.bfloat16),
+    (1, 2, 2, 77, 40, 72, 16, torch.float32),
+    (1, 3, 3, 500, 7, 5, 48, torch.float32),
+    (2, 4, 4, 900, 64, 64, 100, torch.float8_e4m3fn),
+    (1, 8, 2, 600, 64, 64, 64, torch.bfloat16),
+]
+
+
+def _three_phases(q, k, v, S, C):
+    """lla_prefill's three phases called one by one (shared-state heads as
+    repeated heads: the same sums per head)."""
+    Hq, Hkv = q.shape[1], k.shape[1]
+    if Hq != Hkv:
+        k, v = (x.repeat_interleave(Hq // Hkv, dim=1).contiguous() for x in (k, v))
+        S = S.repeat_interleave(Hq // Hkv, dim=1).contiguous()
+    ws = lla.prefill_segment_states(k, v, C, None)
+    lla.prefill_state_scan(S, q.shape[2], C, ws)
+    o = lla.prefill_chunks(q, k, v, S, C, workspace=ws)
+    return o, S[:, ::Hq // Hkv]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,dk,dv,C,dtype", ONE_LAUNCH_CASES)
+def test_one_launch_fresh_prompt_equals_three_phases(dev, B, Hq, Hkv, T, dk, dv, C, dtype):
+    """Gaussian inputs, so that any change in the order of the sums shows:
+    the one-launch walk gives the bits of the segment pass, the scan and the
+    walk, and agrees with the oracle."""
+    print("one launch", B, Hq, Hkv, T, dk, dv, C, dtype, flush=True)
+    scale = 1.0 if dtype == torch.float8_e4m3fn else dk ** -0.5
+    q, k, v = workloads.gaussian(B, Hq, T, dk, dv, seed_base=T + dk, scale=scale, dtype=dtype, device=dev,
+                                 Hkv=Hkv)
+    G = lla.prefill_segment_chunks(B, Hq, T, dk, dv, C)
+    c = (C + 1) // 2 if C > 64 else C
+    assert 1 < -(-T // (G * c)) and (-(-T // (G * c)) - 1) * G <= 16  # the one-launch route
+    S_a = torch.full((B, Hkv, dk, dv), float("nan"), device=dev)
+    o_a = lla.prefill(q, k, v, S_a, chunk=C, zero_state=True)
+    o_b, S_b = _three_phases(q, k, v, lla.state_init(B, Hkv, dk, dv, device=dev), C)
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, o_b) and torch.equal(S_a, S_b)
+    O_ref, S_ref = oracle.grouped_recurrence(q.cpu(), k.cpu(), v.cpu(), nthreads=8)
+    bar = 1e-5 if dtype == torch.float32 else TOL
+    assert rel_err(np64(o_a), O_ref) <= bar and rel_err(np64(S_a), S_ref) <= bar
+
+
+def test_one_launch_verify_pass_equals_three_phases(dev):
+    """A verify pass (S read, left as it was) from a gaussian state on the
+    one-launch route: the outputs of the three phases, S untouched."""
+    B, H, T, d, C = 2, 4, 300, 64, 64
+    q, k, v = workloads.gaussian(B, H, T, d, d, seed_base=31, scale=d ** -0.5, device=dev)
+    S0 = torch.randn((B, H, d, d), generator=torch.Generator().manual_seed(5)).to(dev)
+    S_a = S0.clone()
+    o_a = lla.prefill(q, k, v, S_a, chunk=C, keep_state=True)
+    o_b, _ = _three_phases(q, k, v, S0.clone(), C)
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, o_b) and torch.equal(S_a, S0)
