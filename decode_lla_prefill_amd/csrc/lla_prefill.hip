@@ -968,11 +968,13 @@ __global__ __launch_bounds__(NW * kWave) void k_chunk_walk(
         for (int vw = 0; vw < Cf::NVW; ++vw)
 #pragma unroll
             for (int dt = 0; dt < Cf::NDT; ++dt) Inc[vw][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        auto hop = [&](int64_t c) {  // chunk c staged in Ks, Vs
+        int64_t left = G;  // chunks of the current segment still to sum
+        auto hop = [&]() {  // the next chunk in order, staged in Ks, Vs
             Fr Vf[Cf::NVW][Cf::NTS];
             load_vfrags<Cf>(Vf, Vs, w, g, lane);
             state_hop<Cf>(Inc, Vf, Ks, w, g, lane);
-            if (c % G == G - 1) {  // a segment's sum is complete
+            if (--left == 0) {  // a segment's sum is complete
+                left = G;
 #pragma unroll
                 for (int vw = 0; vw < Cf::NVW; ++vw)
 #pragma unroll
@@ -1007,7 +1009,7 @@ __global__ __launch_bounds__(NW * kWave) void k_chunk_walk(
                         pk[u].gather(Kb + (cc + PF) * C * dk, dk, C);
                         pv[u].gather(Vb + (cc + PF) * C * dv, dv, C);
                     }
-                    hop(cc);
+                    hop();
                     __syncthreads();
                 }
             }
@@ -1016,7 +1018,7 @@ __global__ __launch_bounds__(NW * kWave) void k_chunk_walk(
                 TK::load_scalar(Kb + c * C * dk, dk, C, dk, Ks, tid);
                 TV::load_scalar(Vb + c * C * dv, dv, C, nv, Vs, tid);
                 __syncthreads();
-                hop(c);
+                hop();
                 __syncthreads();
             }
         }

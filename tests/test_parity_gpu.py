@@ -107,6 +107,23 @@ def test_integer_inputs_with_large_scores_exact(dev, B, Hq, Hkv, T, dk, dv, C, d
     assert np.array_equal(np64(o), O_ref)
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,T,dk,dv,C,dtype", [
+    (1, 3, 3, 900, 64, 64, 128, torch.bfloat16),     # 14 chunks of 64 before the last segment
+    (2, 4, 2, 700, 64, 64, 64, torch.float8_e4m3fn),  # shared-state heads, FP8
+])
+def test_integer_fresh_prompt_with_large_scores_one_launch_exact(dev, B, Hq, Hkv, T, dk, dv, C, dtype):
+    """A fresh prompt on the one-launch walk (the walks sum the earlier
+    segments themselves) with scores past one bf16 value: exact."""
+    q, k, v = workloads.integers(B, Hq, T, dk, dv, seed=5 * T + C, lo=-8, hi=8, dtype=dtype, Hkv=Hkv,
+                                 v_range=(-1, 1))
+    S = torch.full((B, Hkv, dk, dv), float("nan"), device=dev)
+    o = lla.prefill(q.to(dev), k.to(dev), v.to(dev), S, chunk=C, zero_state=True)
+    torch.cuda.synchronize()
+    O_ref, S_ref = oracle.grouped_recurrence(q, k, v, np.zeros((B, Hkv, dk, dv)), nthreads=8)
+    assert np.array_equal(np64(S), S_ref)
+    assert np.array_equal(np64(o), O_ref)
+
+
 def test_integer_inputs_with_incoming_state_exact(dev):
     q, k, v = workloads.integers(2, 3, 700, 64, 64, seed=5)
     g = torch.Generator().manual_seed(6)
