@@ -468,3 +468,23 @@ def test_state_commit_rejects(lib, change, expect):
     d.update(change)
     assert lib.lla_state_commit(d["k"], d["v"], d["dtype"], d["B"], d["H"], d["T"], d["dk"], d["dv"],
                                 d["acc"], d["S"], None) == expect
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """No fallback: without the HIP library every entry point raises instead
+    of computing anything elsewhere."""
+    import subprocess
+    import sys
+    code = ("import decode_lla_prefill_amd as lla\n"
+            "try:\n"
+            "    lla.library()\n"
+            "except ImportError as e:\n"
+            "    print('raised', e)\n"
+            "else:\n"
+            "    print('loaded')\n")
+    env = dict(os.environ, LLA_LIBRARY=str(tmp_path / "absent" / "liblla.so"))
+    repo = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = subprocess.run([sys.executable, "-c", code], cwd=repo, env=env, capture_output=True, text=True,
+                         timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.startswith("raised") and "not built" in out.stdout
