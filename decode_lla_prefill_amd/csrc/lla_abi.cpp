@@ -6,6 +6,11 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+#include <atomic>
+#include <chrono>
+#include <random>
+
 #include "lla.h"
 #include "lla_internal.h"
 
@@ -91,9 +96,45 @@ lla::PrefillPlan make_plan(lla_dtype dt, int64_t B, Heads h, int64_t T, int64_t 
     return p;
 }
 
+// The workspace a prefill requires (what the arguments are checked against).
 size_t ws_bytes_for(const lla::PrefillPlan& p) {
     if (!p.use_ws) return 0;
     return (size_t)(p.BH * p.n_seg * (int64_t)p.dk * p.dv) * sizeof(float);
+}
+
+// The workspace size the library reports: the required one, and for shapes
+// that can run as one launch also room for its published segment sums (with
+// less, that route sums every earlier segment itself).
+size_t ws_bytes_reported(const lla::PrefillPlan& p) {
+    const size_t need = ws_bytes_for(p);
+    if (need == 0 || !lla::prefix_capable(p)) return need;
+    const size_t pub = lla::prefix_publish_bytes(p);
+    return need > pub ? need : pub;
+}
+
+// A flag value for one call's published segment sums: a Weyl sequence (odd
+// step, so 2^64 calls before a repeat) from a seed drawn once per process,
+// never 0.  A flag left in the workspace by an earlier call never equals a
+// later call's token, so no clearing is needed between calls.
+unsigned long long next_token() {
+    static std::atomic<unsigned long long> state{[] {
+        std::random_device rd;
+        return ((unsigned long long)rd() << 32) ^ (unsigned long long)rd() ^
+               (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count();
+    }()};
+    unsigned long long t;
+    do {
+        t = state.fetch_add(0x9E3779B97F4A7C15ull, std::memory_order_relaxed) + 0x9E3779B97F4A7C15ull;
+    } while (t == 0);
+    return t;
+}
+
+// Published sums need a fresh token per execution, which a captured launch
+// (replayed with the arguments of its capture) does not get: on a stream
+// that is capturing, the one-launch walk sums every earlier segment itself.
+bool capturing(hipStream_t s) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    return hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone;
 }
 
 // The gated prefill's workspace: the segment states, then one decay (float)
@@ -150,7 +191,11 @@ lla_status check_prefill(const PrefillBufs& b, bool needs_q, bool needs_kv, bool
     const Span o = span(needs_o ? b.O : nullptr, needs_o ? BHq * T * dv * 4 : 0);
     const void* s_ptr = b.S_out ? (const void*)b.S_out : (const void*)b.S_in;
     const Span s = span(needs_s ? s_ptr : nullptr, needs_s ? BHkv * dk * dv * 4 : 0);
-    const Span w = span((needs_ws && need_ws > 0) ? b.ws : nullptr, (int64_t)need_ws);
+    // (a one-launch walk given room for its published sums writes them too)
+    size_t used_ws = need_ws;
+    if (need_ws > 0 && lla::prefix_capable(plan) && b.ws_bytes >= lla::prefix_publish_bytes(plan))
+        used_ws = std::max(used_ws, lla::prefix_publish_bytes(plan));
+    const Span w = span((needs_ws && need_ws > 0) ? b.ws : nullptr, (int64_t)used_ws);
     // Outputs (O, S when written, the workspace) must not overlap anything else.
     const Span all[] = {q, k, v, o, s, w};
     const int outs[] = {3, b.S_out ? 4 : -1, 5};
@@ -207,7 +252,7 @@ size_t lla_prefill_workspace_size(int64_t B, int64_t H, int64_t T, int64_t dk, i
 size_t lla_prefill_gqa_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t dk,
                                       int64_t dv, int64_t C) {
     if (check_heads(Heads{Hq, Hkv}) != LLA_OK || check_sizes(B, Hq, T, dk, dv, C) != LLA_OK) return 0;
-    return ws_bytes_for(make_plan(LLA_BF16, B, Heads{Hq, Hkv}, T, dk, dv, C));
+    return ws_bytes_reported(make_plan(LLA_BF16, B, Heads{Hq, Hkv}, T, dk, dv, C));
 }
 
 lla_status lla_prefill_segment_states(const void* K, const void* V, lla_dtype dtype, int64_t B,
@@ -277,6 +322,10 @@ lla_status prefill_impl(const void* Q, const void* K, const void* V, int dt_raw,
     }
     float* ws = (float*)workspace;
     p.prefix = lla::prefix_walk_fits(p);
+    if (p.prefix && ws && workspace_bytes >= lla::prefix_publish_bytes(p) && !capturing(s)) {
+        p.publish = true;
+        p.token = next_token();
+    }
     if (!p.prefix) {
         st = device_status(lla::launch_segment_states(p, K, V, ws, s));
         if (st != LLA_OK) return st;

@@ -49,6 +49,8 @@ struct PrefillPlan {
     bool zero_start;  // S_0 = 0: S is written (S_T) but not read
     bool keep;        // the verify pass: S is read (unless zero_start) but never written
     bool prefix;      // one launch: every walk sums the segments before its own (prefix_walk_fits)
+    bool publish;     // ... and reads the earlier segments' sums from the workspace where published
+    unsigned long long token;  // this call's flag value for the published sums (never 0)
     lla_dtype dtype;
 };
 
@@ -69,6 +71,15 @@ void plan_prefill(PrefillPlan& p);
 #endif
 constexpr int64_t kPrefixMaxChunks = LLA_PREFIX_MAX_CHUNKS;
 bool prefix_walk_fits(const PrefillPlan& p);
+
+// The one-launch walk's published segment sums (the kernel's layout): one
+// slot of 64 * D floats per (key/value head, segment, value block) -- four
+// waves, one value tile each, D / 16 key tiles of 16 x 16 -- then one 8-byte
+// flag per slot.  prefix_capable: the shape could take the one-launch walk
+// for some dtype and options, so the workspace size covers the slots.
+bool prefix_capable(const PrefillPlan& p);
+int64_t prefix_slot_floats(const PrefillPlan& p);
+size_t prefix_publish_bytes(const PrefillPlan& p);
 
 hipError_t launch_segment_states(const PrefillPlan& p, const void* K, const void* V,
                                  float* ws, hipStream_t st);

@@ -52,12 +52,22 @@ void plan_prefill(PrefillPlan& p) {
     const int ve = p.dtype == LLA_FP8_E4M3 ? 16 : (p.dtype == LLA_BF16 ? 8 : 4);  // per 16 bytes
     p.vec = (p.dk % ve == 0) && (p.dv % ve == 0);
     p.prefix = false;
+    p.publish = false;
+    p.token = 0;
 }
+
+bool prefix_capable(const PrefillPlan& p) { return p.n_seg > 1 && (p.n_seg - 1) * p.G <= kPrefixMaxChunks; }
 
 bool prefix_walk_fits(const PrefillPlan& p) {
     // bf16 or FP8 on the four-wave walk (d = 128 in whole vectors takes the eight-wave walk)
     if (p.dtype == LLA_F32 || (p.D == 128 && p.vec)) return false;
-    return p.n_seg > 1 && (p.zero_start || p.keep) && (p.n_seg - 1) * p.G <= kPrefixMaxChunks;
+    return prefix_capable(p) && (p.zero_start || p.keep);
+}
+
+int64_t prefix_slot_floats(const PrefillPlan& p) { return p.BH * p.n_seg * p.n_vb * 64 * (int64_t)p.D; }
+
+size_t prefix_publish_bytes(const PrefillPlan& p) {
+    return (size_t)prefix_slot_floats(p) * sizeof(float) + (size_t)(p.BH * p.n_seg * p.n_vb) * 8u;
 }
 
 }  // namespace lla

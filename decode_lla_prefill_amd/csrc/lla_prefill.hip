@@ -202,6 +202,9 @@ __device__ __forceinline__ void split_id(int64_t id, int64_t n_lines, int n_vb, 
 // Workgroup id -> work unit such that units u, u + 1, ... share an XCD:
 // ids go round-robin over the 8 XCDs, so XCD x takes the ids congruent to x
 // mod 8 and receives a contiguous range of units (a bijection on [0, n)).
+// The XCD (XCC) the calling wave runs on: hardware register XCC_ID, bits 0-3.
+__device__ __forceinline__ unsigned xcc_id() { return __builtin_amdgcn_s_getreg((3 << 11) | 20) & 15u; }
+
 __device__ __forceinline__ int64_t xcd_major(int64_t id, int64_t n) {
     const int64_t x = id & 7, k = id >> 3, q = n >> 3, r = n & 7;
     return x * q + min(x, r) + k;
@@ -905,11 +908,16 @@ __device__ __forceinline__ void store_out(float* Ob, const f32x4 (&Oacc)[Cf::NT]
 // order (the scan's additions) -- so the bits of the three phases, in one
 // launch.  The lines of a query head are given workgroup ids that share an
 // XCD, so the K and V rows they all read come from one L2.
+// How long a walk waits for an earlier segment's published sum before it
+// sums that segment itself: 2,000 ticks of the 100 MHz real-time counter.
+constexpr uint64_t kPublishWaitTicks = 2000;
+
 template <typename In, int CT, int D, int BV, bool VEC, int NW = kWaves, bool PREFIX = false>
 __global__ __launch_bounds__(NW * kWave) void k_chunk_walk(
     const In* __restrict__ Q, const In* __restrict__ K, const In* __restrict__ V,
     float* __restrict__ S, float* __restrict__ O, const float* __restrict__ ws, int64_t T_len,
-    int dk, int dv, int C, int64_t G, int64_t n_seg, int n_vb, int group, int zero_start, int keep) {
+    int dk, int dv, int C, int64_t G, int64_t n_seg, int n_vb, int group, int zero_start, int keep,
+    float* __restrict__ pub, unsigned long long* __restrict__ flags, unsigned long long token) {
     using T = typename Compute<In>::type;
     using Cf = WalkCfg<T, CT, D, BV, NW>;
     using Fr = typename Cf::Fr;
@@ -959,70 +967,8 @@ __global__ __launch_bounds__(NW * kWave) void k_chunk_walk(
     using TQ = Tile<T, CT, D, typename Cf::LQL, Cf::NTH, In>;
     using TK = Tile<T, CT, D, typename Cf::LKL, Cf::NTH, In>;
     using TV = Tile<T, CT, BV, typename Cf::LVL, Cf::NTH, In>;
-    if constexpr (PREFIX) {
-        // Chunks [0, c0): segment by segment, each summed from zero over its
-        // G chunks and then added to S.  All full (only a sequence's last
-        // chunk is short, and it lies in the last segment).
-        f32x4 Inc[Cf::NVW][Cf::NDT];
-#pragma unroll
-        for (int vw = 0; vw < Cf::NVW; ++vw)
-#pragma unroll
-            for (int dt = 0; dt < Cf::NDT; ++dt) Inc[vw][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        int64_t left = G;  // chunks of the current segment still to sum
-        auto hop = [&]() {  // the next chunk in order, staged in Ks, Vs
-            Fr Vf[Cf::NVW][Cf::NTS];
-            load_vfrags<Cf>(Vf, Vs, w, g, lane);
-            state_hop<Cf>(Inc, Vf, Ks, w, g, lane);
-            if (--left == 0) {  // a segment's sum is complete
-                left = G;
-#pragma unroll
-                for (int vw = 0; vw < Cf::NVW; ++vw)
-#pragma unroll
-                    for (int dt = 0; dt < Cf::NDT; ++dt) {
-                        Sacc[vw][dt] += Inc[vw][dt];
-                        Inc[vw][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    }
-            }
-        };
-        if constexpr (VEC) {
-            constexpr int PF = 2;  // chunks of loads in flight (register sets used round robin)
-            TK pk[PF];
-            TV pv[PF];
-#pragma unroll
-            for (int u = 0; u < PF; ++u) {
-                pk[u].init(dk, dk, tid);
-                pv[u].init(dv, nv, tid);
-                if (u < c0) {
-                    pk[u].gather(Kb + u * C * dk, dk, C);
-                    pv[u].gather(Vb + u * C * dv, dv, C);
-                }
-            }
-            for (int64_t c = 0; c < c0; c += PF) {
-#pragma unroll
-                for (int u = 0; u < PF; ++u) {
-                    const int64_t cc = c + u;
-                    if (cc >= c0) break;
-                    pk[u].scatter(Ks, tid);
-                    pv[u].scatter(Vs, tid);
-                    __syncthreads();
-                    if (cc + PF < c0) {
-                        pk[u].gather(Kb + (cc + PF) * C * dk, dk, C);
-                        pv[u].gather(Vb + (cc + PF) * C * dv, dv, C);
-                    }
-                    hop();
-                    __syncthreads();
-                }
-            }
-        } else {
-            for (int64_t c = 0; c < c0; ++c) {
-                TK::load_scalar(Kb + c * C * dk, dk, C, dk, Ks, tid);
-                TV::load_scalar(Vb + c * C * dv, dv, C, nv, Vs, tid);
-                __syncthreads();
-                hop();
-                __syncthreads();
-            }
-        }
-    }
+    // The first chunk's tiles: loaded into registers now (with PREFIX, their
+    // round trip overlaps the earlier segments' sums), staged at the walk.
     TQ tq;
     TK tk;
     TV tv;
@@ -1034,6 +980,177 @@ __global__ __launch_bounds__(NW * kWave) void k_chunk_walk(
         tq.gather(Qb + c0 * C * dk, dk, rows_of(c0));
         tk.gather(Kb + c0 * C * dk, dk, rows_of(c0));
         tv.gather(Vb + c0 * C * dv, dv, rows_of(c0));
+    }
+    if constexpr (PREFIX) {
+        // The segments before this one, each summed from zero over its G
+        // chunks (all full: only a sequence's last chunk is short, and it
+        // lies in the last segment) and then added to S in segment order.
+        f32x4 Inc[Cf::NVW][Cf::NDT];
+        // Segments [ja, jb) summed in order: each one's Inc = sum over its
+        // chunks of K_c^T V_c, from zero, in chunk order (the segment pass's
+        // products); then, if `add`, S += Inc at the segment's end (the
+        // scan's additions).  One ring of loads runs across the whole range.
+        auto sum_segments = [&](int64_t ja, int64_t jb, bool add) {
+#pragma unroll
+            for (int vw = 0; vw < Cf::NVW; ++vw)
+#pragma unroll
+                for (int dt = 0; dt < Cf::NDT; ++dt) Inc[vw][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const int64_t a = ja * G, b = jb * G;
+            int64_t left = G;  // chunks of the current segment still to sum
+            auto hop = [&]() {  // the next chunk in order, staged in Ks, Vs
+                Fr Vf[Cf::NVW][Cf::NTS];
+                load_vfrags<Cf>(Vf, Vs, w, g, lane);
+                state_hop<Cf>(Inc, Vf, Ks, w, g, lane);
+                if (--left == 0 && add) {  // a segment's sum is complete
+                    left = G;
+#pragma unroll
+                    for (int vw = 0; vw < Cf::NVW; ++vw)
+#pragma unroll
+                        for (int dt = 0; dt < Cf::NDT; ++dt) {
+                            Sacc[vw][dt] += Inc[vw][dt];
+                            Inc[vw][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        }
+                }
+            };
+            if constexpr (VEC) {
+                constexpr int PF = 2;  // chunks of loads in flight (register sets used round robin)
+                TK pk[PF];
+                TV pv[PF];
+#pragma unroll
+                for (int u = 0; u < PF; ++u) {
+                    pk[u].init(dk, dk, tid);
+                    pv[u].init(dv, nv, tid);
+                    if (a + u < b) {
+                        pk[u].gather(Kb + (a + u) * C * dk, dk, C);
+                        pv[u].gather(Vb + (a + u) * C * dv, dv, C);
+                    }
+                }
+                for (int64_t c = a; c < b; c += PF) {
+#pragma unroll
+                    for (int u = 0; u < PF; ++u) {
+                        const int64_t cc = c + u;
+                        if (cc >= b) break;
+                        pk[u].scatter(Ks, tid);
+                        pv[u].scatter(Vs, tid);
+                        __syncthreads();
+                        if (cc + PF < b) {
+                            pk[u].gather(Kb + (cc + PF) * C * dk, dk, C);
+                            pv[u].gather(Vb + (cc + PF) * C * dv, dv, C);
+                        }
+                        hop();
+                        __syncthreads();
+                    }
+                }
+            } else {
+                for (int64_t c = a; c < b; ++c) {
+                    TK::load_scalar(Kb + c * C * dk, dk, C, dk, Ks, tid);
+                    TV::load_scalar(Vb + c * C * dv, dv, C, nv, Vs, tid);
+                    __syncthreads();
+                    hop();
+                    __syncthreads();
+                }
+            }
+        };
+        // Published sums (pub != null): every segment but the last sums its
+        // own chunks first and stores the sum where the later segments of its
+        // key/value head read it (one writer per group), so that a walk
+        // reads an earlier segment's sum instead of summing it again.  A slot
+        // holds one workgroup's Inc in register order ((w, vw, dt), then lane,
+        // then the 4 rows): 16-byte accesses, no LDS stage.
+        // The hand-over goes through the L2 of one XCD, which all its compute
+        // units share (their vector caches write through to it, and a kernel
+        // starts with them invalidated): the writer's stores are complete
+        // in L2 before its flag is set, and a reader uses a slot only if its
+        // flag names the reader's own XCD -- this call's token xor the
+        // writer's XCD id.  Flags are device-scope atomics (one coherent value
+        // for all XCDs), so no cache of another XCD is ever trusted and no
+        // L2 is written back or invalidated.  A slot written on another XCD,
+        // or not flagged by the deadline, is summed by the reader itself:
+        // the same products in the same order, so the bits do not depend on
+        // which happens, and no wait outlasts the deadline.
+        constexpr int SLOT = Cf::NW * Cf::NVW * Cf::NDT * 256;  // floats per (segment, value block)
+        auto slot_at = [&](int64_t j, int vw, int dt) {
+            return pub + ((bh * n_seg + j) * n_vb + vb) * SLOT + (((w * Cf::NVW + vw) * Cf::NDT + dt) * 64 + lane) * 4;
+        };
+        auto flag_at = [&](int64_t j) { return flags + (bh * n_seg + j) * n_vb + vb; };
+        const unsigned long long mine = token ^ (unsigned long long)xcc_id();
+        if (pub != nullptr && !last_seg && bq % group == 0) {
+            sum_segments(seg, seg + 1, false);  // (the sum stays in Inc)
+#pragma unroll
+            for (int vw = 0; vw < Cf::NVW; ++vw)
+#pragma unroll
+                for (int dt = 0; dt < Cf::NDT; ++dt)
+                    if (Cf::ALL_WAVES || w + Cf::NW * vw < Cf::NVT)
+                        *reinterpret_cast<f32x4*>(slot_at(seg, vw, dt)) = Inc[vw][dt];
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            __builtin_amdgcn_s_waitcnt(0);  // this wave's stores acknowledged by L2
+            __syncthreads();
+            if (tid == 0) __hip_atomic_store(flag_at(seg), mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        // Wave 0 decides, for the whole workgroup (the sums use barriers),
+        // which earlier segments to read: lane j polls segment j's flag until
+        // it names this XCD, names another one, or the deadline passes.
+        __shared__ uint64_t use_sh;
+        if (w == 0) {
+            uint64_t use = 0;
+            if (pub != nullptr && seg > 0) {
+                const uint64_t deadline = __builtin_amdgcn_s_memrealtime() + kPublishWaitTicks;
+                const bool mine_lane = lane < seg;
+                bool here = false, settled = !mine_lane;
+                for (;;) {
+                    if (!settled) {
+                        const unsigned long long f =
+                            __hip_atomic_load(flag_at(lane), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        here = f == mine;
+                        settled = here || (f ^ token) < 16;  // flagged on this XCD or another one
+                    }
+                    if (__ballot(!settled) == 0 || __builtin_amdgcn_s_memrealtime() > deadline) break;
+                    __builtin_amdgcn_s_sleep(2);
+                }
+                use = __ballot(here);
+            }
+            if (lane == 0) use_sh = use;
+        }
+        __syncthreads();
+        const uint64_t use = use_sh;  // (the same value in every lane)
+        // Segments in order: a run of published ones is loaded up to eight
+        // at a time (one memory round trip), a run of the others is summed
+        // here with one ring of loads; each segment's sum is added to S in
+        // segment order either way.
+        auto published = [&](int64_t j) { return j < 64 && ((use >> j) & 1u); };
+        constexpr int GRP = 8;
+        for (int64_t j = 0; j < seg;) {
+            if (!published(j)) {
+                int64_t r = j + 1;
+                while (r < seg && !published(r)) ++r;
+                sum_segments(j, r, true);
+                j = r;
+                continue;
+            }
+            f32x4 Ld[GRP][Cf::NVW][Cf::NDT];
+            int n = 0;
+#pragma unroll
+            for (int u = 0; u < GRP; ++u) {
+                const bool from_slot = j + u < seg && published(j + u) && n == u;
+                if (from_slot) ++n;
+#pragma unroll
+                for (int vw = 0; vw < Cf::NVW; ++vw)
+#pragma unroll
+                    for (int dt = 0; dt < Cf::NDT; ++dt)
+                        Ld[u][vw][dt] = (from_slot && (Cf::ALL_WAVES || w + Cf::NW * vw < Cf::NVT))
+                                            ? *reinterpret_cast<const f32x4*>(slot_at(j + u, vw, dt))
+                                            : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int u = 0; u < GRP; ++u) {
+                if (u >= n) break;
+#pragma unroll
+                for (int vw = 0; vw < Cf::NVW; ++vw)
+#pragma unroll
+                    for (int dt = 0; dt < Cf::NDT; ++dt) Sacc[vw][dt] += Ld[u][vw][dt];
+            }
+            j += n;
+        }
     }
 
     // A chunk's outputs stay in registers until the next chunk has started:
@@ -1914,28 +2031,33 @@ static hipError_t launch_walk_t(const PrefillPlan& p, const void* Q, const void*
     const int64_t grid = p.BHq * p.n_seg * p.n_vb;
     const float* wsr = p.use_ws ? ws : nullptr;
     if constexpr (!std::is_same<In, float>::value) {  // (fp32 inputs keep the three phases)
-        if (p.prefix) {  // no workspace: each walk sums the segments before its own
+        if (p.prefix) {  // each walk sums the segments before its own, or reads their published sums
+            float* pub = p.publish ? ws : nullptr;
+            unsigned long long* fl =
+                p.publish ? reinterpret_cast<unsigned long long*>(ws + prefix_slot_floats(p)) : nullptr;
             if (p.vec)
                 hipLaunchKernelGGL((k_chunk_walk<In, CT, D, BV, true, kWaves, true>), dim3((unsigned)grid),
                                    dim3(kThreads), 0, st, (const In*)Q, (const In*)K, (const In*)V, S, O,
                                    (const float*)nullptr, p.T, p.dk, p.dv, p.C, p.G, p.n_seg, p.n_vb, p.group,
-                                   (int)p.zero_start, (int)p.keep);
+                                   (int)p.zero_start, (int)p.keep, pub, fl, p.token);
             else
                 hipLaunchKernelGGL((k_chunk_walk<In, CT, D, BV, false, kWaves, true>), dim3((unsigned)grid),
                                    dim3(kThreads), 0, st, (const In*)Q, (const In*)K, (const In*)V, S, O,
                                    (const float*)nullptr, p.T, p.dk, p.dv, p.C, p.G, p.n_seg, p.n_vb, p.group,
-                                   (int)p.zero_start, (int)p.keep);
+                                   (int)p.zero_start, (int)p.keep, pub, fl, p.token);
             return hipGetLastError();
         }
     }
     if (p.vec)
         hipLaunchKernelGGL((k_chunk_walk<In, CT, D, BV, true>), dim3((unsigned)grid), dim3(kThreads), 0,
                            st, (const In*)Q, (const In*)K, (const In*)V, S, O, wsr, p.T,
-                           p.dk, p.dv, p.C, p.G, p.n_seg, p.n_vb, p.group, (int)p.zero_start, (int)p.keep);
+                           p.dk, p.dv, p.C, p.G, p.n_seg, p.n_vb, p.group, (int)p.zero_start, (int)p.keep,
+                           (float*)nullptr, (unsigned long long*)nullptr, 0ull);
     else
         hipLaunchKernelGGL((k_chunk_walk<In, CT, D, BV, false>), dim3((unsigned)grid), dim3(kThreads), 0,
                            st, (const In*)Q, (const In*)K, (const In*)V, S, O, wsr, p.T,
-                           p.dk, p.dv, p.C, p.G, p.n_seg, p.n_vb, p.group, (int)p.zero_start, (int)p.keep);
+                           p.dk, p.dv, p.C, p.G, p.n_seg, p.n_vb, p.group, (int)p.zero_start, (int)p.keep,
+                           (float*)nullptr, (unsigned long long*)nullptr, 0ull);
     return hipGetLastError();
 }
 

@@ -124,9 +124,12 @@ int64_t lla_prefill_segment_chunks(int64_t B, int64_t H, int64_t T, int64_t dk,
                                    int64_t dv, int64_t C);
 
 /*
- * Bytes of device workspace lla_prefill needs for this shape: one fp32
- * dk x dv state per segment per (b, h) when a sequence has more than one
- * segment, else 0.  Returns 0 for invalid sizes as well.
+ * Bytes of device workspace for this shape: one fp32 dk x dv state per
+ * segment per (b, h) when a sequence has more than one segment, else 0 --
+ * what lla_prefill requires -- or more for a shape that can run as one launch
+ * (see lla_prefill_ex): room for that route's published segment sums.  A call
+ * given only the states' size still runs that route, with the same results,
+ * without publishing.  Returns 0 for invalid sizes as well.
  */
 size_t lla_prefill_workspace_size(int64_t B, int64_t H, int64_t T, int64_t dk,
                                   int64_t dv, int64_t C);
@@ -272,8 +275,16 @@ lla_status lla_prefill_gqa(const void *Q, const void *K, const void *V, lla_dtyp
  * segment -- bf16 or FP8 inputs, head dims up to 64 (or rows that are not
  * whole 16-byte vectors) -- runs as one kernel: every segment's walk sums the
  * earlier segments' K^T V itself, in the order of the segment pass and the
- * scan, so the results are the bits of the three phases.  The workspace is
- * not written on that route (its content on return is unspecified).
+ * scan, so the results are the bits of the three phases.  Given the
+ * workspace lla_prefill_gqa_workspace_size reports, every segment but the
+ * last first sums its own chunks and publishes the sum there, and a later
+ * segment's walk reads a published sum instead of summing that segment
+ * again (when both workgroups run on one XCD and the sum arrives within a
+ * short bounded wait; otherwise it sums it itself -- the same bits either
+ * way).  A call enqueued while its stream is capturing a HIP graph does not
+ * publish: a flag value unique to each call tells this call's sums from an
+ * earlier call's, and a graph would replay one value.  The workspace's
+ * content on return is unspecified on this route.
  */
 lla_status lla_prefill_ex(const void *Q, const void *K, const void *V, lla_dtype dtype,
                           int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t dk,

@@ -196,6 +196,27 @@ def test_state_init_rejects(lib):
 
 # ---- planning: segments and workspace ------------------------------------------------
 
+def _pad(x):
+    return 32 if x <= 32 else (64 if x <= 64 else 128)
+
+
+def _expected_workspace(B, H, n_seg, G, d):
+    """One fp32 d x d state per segment per (b,h), nothing for one segment;
+    for a shape that can run as one launch (several segments, at most 16
+    chunks before the last) at least the room for that walk's published
+    segment sums: a slot of 64 x D floats per (b,h), segment and value block
+    (D = the padded head dim, blocks of 64 columns), and an 8-byte flag per
+    slot."""
+    if n_seg <= 1:
+        return 0
+    states = B * H * n_seg * d * d * 4
+    if (n_seg - 1) * G > 16:
+        return states
+    D = _pad(d)
+    slots = B * H * n_seg * (D // min(D, 64))
+    return max(states, slots * 64 * D * 4 + slots * 8)
+
+
 def _lines_rule_G(B, H, T, C):
     """Chunks of C per segment by the line rule: the smallest whole number
     that keeps the (sequence, head, segment) lines at most 256."""
@@ -215,8 +236,7 @@ def test_segments_cover_the_sequence(lib, B, H, T, d, C):
     n_c = math.ceil(T / c)
     assert 1 <= G <= n_c
     n_seg = math.ceil(n_c / G)
-    # one fp32 d x d state per segment per (b,h), or nothing for one segment
-    assert ws == (B * H * n_seg * d * d * 4 if n_seg > 1 else 0)
+    assert ws == _expected_workspace(B, H, n_seg, G, d)
     G_C = _lines_rule_G(B, H, T, C)
     n_seg_C = math.ceil(math.ceil(T / C) / G_C)
     if C <= 64:

@@ -83,7 +83,9 @@ def test_gated_workspace_is_the_states_and_one_decay_per_segment(lib, B, H, T, d
         assert need == 0
     else:
         assert need == B * H * n_seg * (d * d + 1) * 4
-        assert need == lib.lla_prefill_workspace_size(B, H, T, d, d, C) + B * H * n_seg * 4
+        # (at least the plain prefill's states; that size also covers the
+        # one-launch walk's published sums where a shape can take it)
+        assert need - B * H * n_seg * 4 <= lib.lla_prefill_workspace_size(B, H, T, d, d, C)
 
 
 def _decode(lib, **change):

@@ -83,6 +83,42 @@ def test_graph_replays_equal_eager_calls():
         assert torch.equal(S, S_ref), r
 
 
+def test_graph_replays_equal_eager_calls_one_launch():
+    """A fresh prompt on the one-launch walk (d = 64, eleven segments): eager
+    calls read the earlier segments' published sums, a captured call (whose
+    replays could not tell one execution's flags from another's) sums them
+    itself; the bits are the same."""
+    dev = need_gpu()
+    B, H, T, d, C = 1, 4, 700, 64, 64
+    q, k, v = (torch.empty((B, H, T, d), dtype=torch.bfloat16, device=dev) for _ in range(3))
+    S = lla.state_init(B, H, d, d, device=dev)
+    pre = lla.PreparedPrefill(q, k, v, S, C)
+    _fill((q, k, v), 0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        pre(zero_state=True)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        pre(zero_state=True)
+    torch.cuda.synchronize()
+    for r in range(1, 5):
+        print("one-launch graph replay", r, flush=True)
+        _fill((q, k, v), r)
+        S_ref = torch.empty_like(S)
+        o_ref = lla.prefill(q.clone(), k.clone(), v.clone(), S_ref, chunk=C, zero_state=True)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(pre.out, o_ref), r
+        assert torch.equal(S, S_ref), r
+        pre(zero_state=True)  # an eager call between the replays, on the same workspace
+        torch.cuda.synchronize()
+        assert torch.equal(pre.out, o_ref), r
+
+
 @pytest.mark.parametrize("Hq,Hkv,dtype", [(8, 2, torch.bfloat16), (4, 4, torch.float8_e4m3fn),
                                            (8, 4, torch.float8_e4m3fn)])
 def test_graph_replays_equal_eager_calls_grouped_and_fp8(Hq, Hkv, dtype):

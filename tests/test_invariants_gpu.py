@@ -246,6 +246,69 @@ def test_one_launch_fresh_prompt_equals_three_phases(dev, B, Hq, Hkv, T, dk, dv,
     assert rel_err(np64(o_a), O_ref) <= bar and rel_err(np64(S_a), S_ref) <= bar
 
 
+def _published_layout(B, Hkv, T, dk, dv, C):
+    """Segments, value blocks and the floats of slots before the flags of the
+    one-launch walk's published sums in the workspace: a slot of 64 x D
+    floats per (b, key/value head, segment, value block), D the padded head
+    dim, blocks of 64 value columns; then one 8-byte flag per slot."""
+    G = lla.prefill_segment_chunks(B, Hkv, T, dk, dv, C)
+    c = (C + 1) // 2 if C > 64 else C
+    n_seg = -(-(-(-T // c)) // G)
+    m = max(dk, dv)
+    D = 32 if m <= 32 else (64 if m <= 64 else 128)
+    n_vb = D // min(D, 64)
+    return n_seg, n_vb, B * Hkv * n_seg * n_vb * 64 * D
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,dk,dv,C,dtype", [
+    (4, 8, 8, 1024, 64, 64, 64, torch.bfloat16),
+    (2, 4, 4, 900, 64, 64, 100, torch.float8_e4m3fn),
+    (1, 8, 2, 600, 64, 64, 64, torch.bfloat16),
+    (1, 4, 4, 700, 40, 56, 64, torch.bfloat16),
+])
+def test_one_launch_published_sums_equal_summing_in_place(dev, B, Hq, Hkv, T, dk, dv, C, dtype):
+    """With room for the published sums, every segment but the last publishes
+    its K^T V and the later walks read it; with only the required workspace
+    every walk sums the earlier segments itself.  Same bits either way.  The
+    flags of the published slots all hold the call's token afterwards (xor
+    the id, 0-15, of the XCD that wrote the slot)."""
+    print("published sums", B, Hq, Hkv, T, dk, dv, C, dtype, flush=True)
+    scale = 1.0 if dtype == torch.float8_e4m3fn else dk ** -0.5
+    q, k, v = workloads.gaussian(B, Hq, T, dk, dv, seed_base=3 * T + dv, scale=scale, dtype=dtype, device=dev,
+                                 Hkv=Hkv)
+    n_seg, n_vb, slot_floats = _published_layout(B, Hkv, T, dk, dv, C)
+    required = B * Hkv * n_seg * dk * dv  # floats: one state per segment
+    full = lla.prefill_gqa_workspace_size(B, Hq, Hkv, T, dk, dv, C) // 4
+    assert full >= slot_floats + 2 * B * Hkv * n_seg * n_vb > required  # (this shape publishes)
+    ws_small = torch.empty(required, dtype=torch.float32, device=dev)
+    ws_full = torch.full((full,), float("nan"), dtype=torch.float32, device=dev)
+    S_a = torch.full((B, Hkv, dk, dv), float("nan"), device=dev)
+    S_b = torch.full((B, Hkv, dk, dv), float("nan"), device=dev)
+    o_a = lla.prefill(q, k, v, S_a, chunk=C, zero_state=True, workspace=ws_small)
+    o_b = lla.prefill(q, k, v, S_b, chunk=C, zero_state=True, workspace=ws_full)
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, o_b) and torch.equal(S_a, S_b)
+    flags = ws_full[slot_floats:slot_floats + 2 * B * Hkv * n_seg * n_vb].view(torch.int64)
+    published = flags.view(B * Hkv, n_seg, n_vb)[:, :-1].cpu()
+    assert (published != 0).all() and ((published >> 4) == (published.flatten()[0] >> 4)).all()
+
+
+def test_one_launch_workspace_reused_across_calls(dev):
+    """Calls that reuse one workspace, each with new inputs: what an earlier
+    call published (slots and flags) never enters a later call's result."""
+    B, H, T, d, C = 4, 8, 1024, 64, 64
+    ws = torch.empty(lla.prefill_workspace_size(B, H, T, d, d, C) // 4, dtype=torch.float32, device=dev)
+    for r in range(4):
+        print("reuse", r, flush=True)
+        q, k, v = workloads.gaussian(B, H, T, d, d, seed_base=100 + r, scale=d ** -0.5, device=dev)
+        S_a = torch.empty((B, H, d, d), device=dev)
+        S_b = torch.empty((B, H, d, d), device=dev)
+        o_a = lla.prefill(q, k, v, S_a, chunk=C, zero_state=True, workspace=ws)
+        o_b, S_ref = _three_phases(q, k, v, lla.state_init(B, H, d, d, device=dev), C)
+        torch.cuda.synchronize()
+        assert torch.equal(o_a, o_b) and torch.equal(S_a, S_ref), r
+
+
 def test_one_launch_verify_pass_equals_three_phases(dev):
     """A verify pass (S read, left as it was) from a gaussian state on the
     one-launch route: the outputs of the three phases, S untouched."""
