@@ -321,8 +321,9 @@ lla_status prefill_impl(const void* Q, const void* K, const void* V, int dt_raw,
                                                        zero, keep, s));
     }
     float* ws = (float*)workspace;
-    p.prefix = lla::prefix_walk_fits(p);
-    if (p.prefix && ws && workspace_bytes >= lla::prefix_publish_bytes(p) && !capturing(s)) {
+    const bool can_publish = ws && workspace_bytes >= lla::prefix_publish_bytes(p) && !capturing(s);
+    p.prefix = lla::prefix_walk_fits(p, can_publish);
+    if (p.prefix && can_publish) {
         p.publish = true;
         p.token = next_token();
     }

@@ -70,7 +70,19 @@ void plan_prefill(PrefillPlan& p);
 #define LLA_PREFIX_MAX_CHUNKS 16
 #endif
 constexpr int64_t kPrefixMaxChunks = LLA_PREFIX_MAX_CHUNKS;
-bool prefix_walk_fits(const PrefillPlan& p);
+// With the earlier segments' sums published (see below): at most 16 segments,
+// 8 chunks per segment (a writer's own sum stays well inside the readers'
+// bounded wait) and 64 chunks before the last one.  Measured (fresh prompts,
+// d = 64 and 32, T = 2048-4096, G = 2-8): up to 15 % faster than the three
+// phases with cold inputs at 8-16 segments, 17 % slower at 32; without
+// publication such shapes keep the three phases (summing 28-60 chunks again
+// measured 20-90 % slower).
+constexpr int64_t kPublishMaxSegments = 16;
+constexpr int64_t kPublishMaxChunks = 64;
+constexpr int64_t kPublishMaxG = 8;
+// `published`: the call can publish (workspace large enough, stream not
+// capturing), which admits the larger shapes above.
+bool prefix_walk_fits(const PrefillPlan& p, bool published);
 
 // The one-launch walk's published segment sums (the kernel's layout): one
 // slot of 64 * D floats per (key/value head, segment, value block) -- four

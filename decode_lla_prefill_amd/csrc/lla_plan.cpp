@@ -56,12 +56,27 @@ void plan_prefill(PrefillPlan& p) {
     p.token = 0;
 }
 
-bool prefix_capable(const PrefillPlan& p) { return p.n_seg > 1 && (p.n_seg - 1) * p.G <= kPrefixMaxChunks; }
+// Whether the shape runs as one launch: few chunks before the last segment
+// (each walk can sum them itself), or -- when the earlier segments' sums are
+// published -- a few more segments with every XCD's range of workgroup ids
+// (xcd_major) holding whole key/value heads, so that every reader finds its
+// writers on its own XCD.
+static bool prefix_shape(const PrefillPlan& p, bool published) {
+    if (p.n_seg <= 1) return false;
+    const int64_t before = (p.n_seg - 1) * p.G;
+    if (before <= kPrefixMaxChunks) return true;
+    if (!published || p.n_seg > kPublishMaxSegments || before > kPublishMaxChunks || p.G > kPublishMaxG)
+        return false;
+    const int64_t units = p.BHq * p.n_seg * p.n_vb, per_head = (int64_t)p.group * p.n_seg * p.n_vb;
+    return units % 8 == 0 && (units / 8) % per_head == 0;
+}
 
-bool prefix_walk_fits(const PrefillPlan& p) {
+bool prefix_capable(const PrefillPlan& p) { return prefix_shape(p, true); }
+
+bool prefix_walk_fits(const PrefillPlan& p, bool published) {
     // bf16 or FP8 on the four-wave walk (d = 128 in whole vectors takes the eight-wave walk)
     if (p.dtype == LLA_F32 || (p.D == 128 && p.vec)) return false;
-    return prefix_capable(p) && (p.zero_start || p.keep);
+    return (p.zero_start || p.keep) && prefix_shape(p, published);
 }
 
 int64_t prefix_slot_floats(const PrefillPlan& p) { return p.BH * p.n_seg * p.n_vb * 64 * (int64_t)p.D; }

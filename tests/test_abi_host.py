@@ -202,18 +202,24 @@ def _pad(x):
 
 def _expected_workspace(B, H, n_seg, G, d):
     """One fp32 d x d state per segment per (b,h), nothing for one segment;
-    for a shape that can run as one launch (several segments, at most 16
-    chunks before the last) at least the room for that walk's published
-    segment sums: a slot of 64 x D floats per (b,h), segment and value block
-    (D = the padded head dim, blocks of 64 columns), and an 8-byte flag per
-    slot."""
+    for a shape that can run as one launch -- several segments and at most 16
+    chunks before the last, or, with published sums, at most 16 segments of
+    at most 8 chunks, 64 chunks before the last and whole heads in each of
+    the 8 XCDs' ranges of workgroups -- at least the room for that walk's
+    published segment sums: a slot of 64 x D floats per (b,h), segment and
+    value block (D = the padded head dim, blocks of 64 columns), and an
+    8-byte flag per slot."""
     if n_seg <= 1:
         return 0
     states = B * H * n_seg * d * d * 4
-    if (n_seg - 1) * G > 16:
-        return states
     D = _pad(d)
-    slots = B * H * n_seg * (D // min(D, 64))
+    n_vb = D // min(D, 64)
+    before = (n_seg - 1) * G
+    units = B * H * n_seg * n_vb
+    wide = n_seg <= 16 and G <= 8 and before <= 64 and units % 8 == 0 and (units // 8) % (n_seg * n_vb) == 0
+    if before > 16 and not wide:
+        return states
+    slots = B * H * n_seg * n_vb
     return max(states, slots * 64 * D * 4 + slots * 8)
 
 
@@ -228,6 +234,7 @@ def _lines_rule_G(B, H, T, C):
     (1, 1, 8, 2, 4), (1, 1, 7, 2, 4), (4, 8, 1024, 64, 64), (1, 16, 8192, 128, 64),
     (1, 32, 131072, 128, 128), (256, 32, 4096, 128, 64), (3, 5, 1000, 33, 17), (1, 1, 1, 1, 1),
     (2, 3, 1000, 64, 101), (1, 16, 8192, 128, 100), (1, 2, 70, 16, 65), (4, 8, 1024, 64, 128),
+    (1, 16, 2048, 64, 64), (1, 16, 4096, 64, 64), (1, 8, 4096, 64, 64), (1, 12, 2048, 64, 64),
 ])
 def test_segments_cover_the_sequence(lib, B, H, T, d, C):
     G = lib.lla_prefill_segment_chunks(B, H, T, d, d, C)

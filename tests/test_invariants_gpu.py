@@ -265,6 +265,11 @@ def _published_layout(B, Hkv, T, dk, dv, C):
     (2, 4, 4, 900, 64, 64, 100, torch.float8_e4m3fn),
     (1, 8, 2, 600, 64, 64, 64, torch.bfloat16),
     (1, 4, 4, 700, 40, 56, 64, torch.bfloat16),
+    # one launch only with published sums (more than 16 chunks before the last
+    # segment); with the required workspace alone these run the three phases
+    (1, 16, 16, 2048, 64, 64, 64, torch.bfloat16),
+    (1, 32, 32, 2048, 32, 32, 32, torch.bfloat16),
+    (2, 16, 16, 2048, 64, 64, 64, torch.float8_e4m3fn),
 ])
 def test_one_launch_published_sums_equal_summing_in_place(dev, B, Hq, Hkv, T, dk, dv, C, dtype):
     """With room for the published sums, every segment but the last publishes
