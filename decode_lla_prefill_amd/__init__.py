@@ -26,7 +26,7 @@ __all__ = [
     "prefill_state_scan", "prefill_chunks", "prefill_noalloc", "state_commit", "PreparedPrefill",
     "PreparedDecode", "prefill_gated_workspace_size", "prefill_gated", "decode_step_gated",
     "state_commit_gated", "PreparedGatedPrefill", "PreparedGatedDecode",
-    "EXPORTS",
+    "set_publish_wait_ticks", "EXPORTS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -42,7 +42,7 @@ EXPORTS = ("lla_status_string", "lla_last_device_error", "lla_state_init",
            "lla_decode_step_gqa", "lla_prefill_ex", "lla_prefill_noalloc", "lla_state_commit",
            "lla_prefill_gated_workspace_size", "lla_prefill_gated", "lla_decode_step_gated",
            "lla_state_commit_gated", "lla_prefill_gated_gqa_workspace_size", "lla_prefill_gated_gqa",
-           "lla_decode_step_gated_gqa")
+           "lla_decode_step_gated_gqa", "lla_set_publish_wait_ticks")
 PREFILL_ZERO_STATE = 1  # lla_prefill_ex: start from S_0 = 0 without reading S
 PREFILL_KEEP_STATE = 2  # lla_prefill_ex: read S, do not write it (verify pass of draft tokens)
 
@@ -101,6 +101,8 @@ def library():
         lib.lla_prefill_ex.argtypes = [vp, vp, vp, ci, i64, i64, i64, i64, i64, i64, i64,
                                        ctypes.c_uint, vp, vp, vp, sz, vp]
         lib.lla_prefill_ex.restype = st
+        lib.lla_set_publish_wait_ticks.argtypes = [i64]
+        lib.lla_set_publish_wait_ticks.restype = st
         lib.lla_prefill_noalloc.argtypes = [vp, vp, vp, ci, i64, i64, i64, i64, i64, i64, i64,
                                             ctypes.c_uint, vp, vp, vp]
         lib.lla_prefill_noalloc.restype = st
@@ -205,6 +207,13 @@ def state_init(B: int, H: int, dk: int, dv: int, device=None, out: torch.Tensor 
 def prefill_segment_chunks(B, H, T, dk, dv, chunk) -> int:
     """Chunks one workgroup walks (G); segment s covers tokens [s*G*C, (s+1)*G*C)."""
     return int(library().lla_prefill_segment_chunks(B, H, T, dk, dv, chunk))
+
+
+def set_publish_wait_ticks(ticks: int) -> None:
+    """How long (100 MHz GPU real-time ticks) a one-launch walk waits for an
+    earlier segment's published sum before summing it itself, for later
+    calls (lla_set_publish_wait_ticks; results do not depend on it)."""
+    _check(library().lla_set_publish_wait_ticks(int(ticks)), "lla_set_publish_wait_ticks")
 
 
 def prefill_workspace_size(B, H, T, dk, dv, chunk) -> int:

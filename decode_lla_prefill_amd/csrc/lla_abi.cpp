@@ -129,6 +129,8 @@ unsigned long long next_token() {
     return t;
 }
 
+std::atomic<uint64_t> g_publish_wait{lla::kPublishWaitTicks};
+
 // Published sums need a fresh token per execution, which a captured launch
 // (replayed with the arguments of its capture) does not get: on a stream
 // that is capturing, the one-launch walk sums every earlier segment itself.
@@ -244,6 +246,12 @@ int64_t lla_prefill_segment_chunks(int64_t B, int64_t H, int64_t T, int64_t dk, 
     return make_plan(LLA_BF16, B, Heads{H, H}, T, dk, dv, C).G;
 }
 
+lla_status lla_set_publish_wait_ticks(int64_t ticks) {
+    if (ticks < 0) return LLA_ERR_SHAPE;
+    g_publish_wait.store((uint64_t)ticks, std::memory_order_relaxed);
+    return LLA_OK;
+}
+
 size_t lla_prefill_workspace_size(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
                                   int64_t C) {
     return lla_prefill_gqa_workspace_size(B, H, H, T, dk, dv, C);
@@ -326,6 +334,7 @@ lla_status prefill_impl(const void* Q, const void* K, const void* V, int dt_raw,
     if (p.prefix && can_publish) {
         p.publish = true;
         p.token = next_token();
+        p.wait_ticks = g_publish_wait.load(std::memory_order_relaxed);
     }
     if (!p.prefix) {
         st = device_status(lla::launch_segment_states(p, K, V, ws, s));

@@ -51,6 +51,7 @@ struct PrefillPlan {
     bool prefix;      // one launch: every walk sums the segments before its own (prefix_walk_fits)
     bool publish;     // ... and reads the earlier segments' sums from the workspace where published
     unsigned long long token;  // this call's flag value for the published sums (never 0)
+    uint64_t wait_ticks;       // a reader's wait for them (100 MHz ticks; lla_set_publish_wait_ticks)
     lla_dtype dtype;
 };
 
@@ -80,6 +81,10 @@ constexpr int64_t kPrefixMaxChunks = LLA_PREFIX_MAX_CHUNKS;
 constexpr int64_t kPublishMaxSegments = 16;
 constexpr int64_t kPublishMaxChunks = 64;
 constexpr int64_t kPublishMaxG = 8;
+// How long a walk waits for an earlier segment's published sum before it sums
+// that segment itself, by default: 2,000 ticks of the 100 MHz real-time
+// counter (20 us; a writer's own sum takes a few).
+constexpr uint64_t kPublishWaitTicks = 2000;
 // `published`: the call can publish (workspace large enough, stream not
 // capturing), which admits the larger shapes above.
 bool prefix_walk_fits(const PrefillPlan& p, bool published);

@@ -54,6 +54,7 @@ void plan_prefill(PrefillPlan& p) {
     p.prefix = false;
     p.publish = false;
     p.token = 0;
+    p.wait_ticks = 0;
 }
 
 // Whether the shape runs as one launch: few chunks before the last segment

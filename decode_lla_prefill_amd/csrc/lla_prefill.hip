@@ -908,16 +908,13 @@ __device__ __forceinline__ void store_out(float* Ob, const f32x4 (&Oacc)[Cf::NT]
 // order (the scan's additions) -- so the bits of the three phases, in one
 // launch.  The lines of a query head are given workgroup ids that share an
 // XCD, so the K and V rows they all read come from one L2.
-// How long a walk waits for an earlier segment's published sum before it
-// sums that segment itself: 2,000 ticks of the 100 MHz real-time counter.
-constexpr uint64_t kPublishWaitTicks = 2000;
-
 template <typename In, int CT, int D, int BV, bool VEC, int NW = kWaves, bool PREFIX = false>
 __global__ __launch_bounds__(NW * kWave) void k_chunk_walk(
     const In* __restrict__ Q, const In* __restrict__ K, const In* __restrict__ V,
     float* __restrict__ S, float* __restrict__ O, const float* __restrict__ ws, int64_t T_len,
     int dk, int dv, int C, int64_t G, int64_t n_seg, int n_vb, int group, int zero_start, int keep,
-    float* __restrict__ pub, unsigned long long* __restrict__ flags, unsigned long long token) {
+    float* __restrict__ pub, unsigned long long* __restrict__ flags, unsigned long long token,
+    uint64_t wait_ticks) {
     using T = typename Compute<In>::type;
     using Cf = WalkCfg<T, CT, D, BV, NW>;
     using Fr = typename Cf::Fr;
@@ -1065,7 +1062,8 @@ __global__ __launch_bounds__(NW * kWave) void k_chunk_walk(
         // writer's XCD id.  Flags are device-scope atomics (one coherent value
         // for all XCDs), so no cache of another XCD is ever trusted and no
         // L2 is written back or invalidated.  A slot written on another XCD,
-        // or not flagged by the deadline, is summed by the reader itself:
+        // or not flagged by the deadline (wait_ticks of the 100 MHz real-time
+        // counter after the first poll), is summed by the reader itself:
         // the same products in the same order, so the bits do not depend on
         // which happens, and no wait outlasts the deadline.
         constexpr int SLOT = Cf::NW * Cf::NVW * Cf::NDT * 256;  // floats per (segment, value block)
@@ -1094,7 +1092,7 @@ __global__ __launch_bounds__(NW * kWave) void k_chunk_walk(
         if (w == 0) {
             uint64_t use = 0;
             if (pub != nullptr && seg > 0) {
-                const uint64_t deadline = __builtin_amdgcn_s_memrealtime() + kPublishWaitTicks;
+                const uint64_t deadline = __builtin_amdgcn_s_memrealtime() + wait_ticks;
                 const bool mine_lane = lane < seg;
                 bool here = false, settled = !mine_lane;
                 for (;;) {
@@ -2039,12 +2037,12 @@ static hipError_t launch_walk_t(const PrefillPlan& p, const void* Q, const void*
                 hipLaunchKernelGGL((k_chunk_walk<In, CT, D, BV, true, kWaves, true>), dim3((unsigned)grid),
                                    dim3(kThreads), 0, st, (const In*)Q, (const In*)K, (const In*)V, S, O,
                                    (const float*)nullptr, p.T, p.dk, p.dv, p.C, p.G, p.n_seg, p.n_vb, p.group,
-                                   (int)p.zero_start, (int)p.keep, pub, fl, p.token);
+                                   (int)p.zero_start, (int)p.keep, pub, fl, p.token, p.wait_ticks);
             else
                 hipLaunchKernelGGL((k_chunk_walk<In, CT, D, BV, false, kWaves, true>), dim3((unsigned)grid),
                                    dim3(kThreads), 0, st, (const In*)Q, (const In*)K, (const In*)V, S, O,
                                    (const float*)nullptr, p.T, p.dk, p.dv, p.C, p.G, p.n_seg, p.n_vb, p.group,
-                                   (int)p.zero_start, (int)p.keep, pub, fl, p.token);
+                                   (int)p.zero_start, (int)p.keep, pub, fl, p.token, p.wait_ticks);
             return hipGetLastError();
         }
     }
@@ -2052,12 +2050,12 @@ static hipError_t launch_walk_t(const PrefillPlan& p, const void* Q, const void*
         hipLaunchKernelGGL((k_chunk_walk<In, CT, D, BV, true>), dim3((unsigned)grid), dim3(kThreads), 0,
                            st, (const In*)Q, (const In*)K, (const In*)V, S, O, wsr, p.T,
                            p.dk, p.dv, p.C, p.G, p.n_seg, p.n_vb, p.group, (int)p.zero_start, (int)p.keep,
-                           (float*)nullptr, (unsigned long long*)nullptr, 0ull);
+                           (float*)nullptr, (unsigned long long*)nullptr, 0ull, (uint64_t)0);
     else
         hipLaunchKernelGGL((k_chunk_walk<In, CT, D, BV, false>), dim3((unsigned)grid), dim3(kThreads), 0,
                            st, (const In*)Q, (const In*)K, (const In*)V, S, O, wsr, p.T,
                            p.dk, p.dv, p.C, p.G, p.n_seg, p.n_vb, p.group, (int)p.zero_start, (int)p.keep,
-                           (float*)nullptr, (unsigned long long*)nullptr, 0ull);
+                           (float*)nullptr, (unsigned long long*)nullptr, 0ull, (uint64_t)0);
     return hipGetLastError();
 }
 

@@ -286,6 +286,17 @@ lla_status lla_prefill_gqa(const void *Q, const void *K, const void *V, lla_dtyp
  * earlier call's, and a graph would replay one value.  The workspace's
  * content on return is unspecified on this route.
  */
+/*
+ * How long, in ticks of the GPU's 100 MHz real-time counter, a walk on the
+ * one-launch route waits for an earlier segment's published sum before it
+ * sums that segment itself (default 2000, 20 us), for the calls enqueued
+ * after this one in the process.  Results never depend on it: any segment
+ * not yet published when the wait ends is summed with the same products in
+ * the same order.  0 polls each flag once.  For tests of that fallback and
+ * for tuning; LLA_ERR_SHAPE for a negative value.
+ */
+lla_status lla_set_publish_wait_ticks(int64_t ticks);
+
 lla_status lla_prefill_ex(const void *Q, const void *K, const void *V, lla_dtype dtype,
                           int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t dk,
                           int64_t dv, int64_t C, unsigned flags, float *S, float *O,

@@ -298,6 +298,26 @@ def test_one_launch_published_sums_equal_summing_in_place(dev, B, Hq, Hkv, T, dk
     assert (published != 0).all() and ((published >> 4) == (published.flatten()[0] >> 4)).all()
 
 
+@pytest.mark.parametrize("ticks", [0, 1, 50])
+def test_one_launch_short_publish_wait_same_bits(dev, ticks):
+    """With the readers' wait for published sums cut to almost nothing, most
+    earlier segments are not yet published when a walk looks, so it sums them
+    itself, interleaved with the ones it reads: the bits of the three phases
+    regardless (the wait is set from the host; every wait still ends)."""
+    print("publish wait", ticks, flush=True)
+    try:
+        lla.set_publish_wait_ticks(ticks)
+        for B, H, T, d, C in ((4, 8, 1024, 64, 64), (1, 16, 2048, 64, 64)):
+            q, k, v = workloads.gaussian(B, H, T, d, d, seed_base=200 + T, scale=d ** -0.5, device=dev)
+            S_a = torch.empty((B, H, d, d), device=dev)
+            o_a = lla.prefill(q, k, v, S_a, chunk=C, zero_state=True)
+            o_b, S_b = _three_phases(q, k, v, lla.state_init(B, H, d, d, device=dev), C)
+            torch.cuda.synchronize()
+            assert torch.equal(o_a, o_b) and torch.equal(S_a, S_b), (ticks, B, H, T)
+    finally:
+        lla.set_publish_wait_ticks(2000)
+
+
 def test_one_launch_workspace_reused_across_calls(dev):
     """Calls that reuse one workspace, each with new inputs: what an earlier
     call published (slots and flags) never enters a later call's result."""
