@@ -58,3 +58,16 @@ def test_noalloc_grouped_heads_and_short_prompts():
     q, k, v = (x[:, :, :0] for x in (q, k, v))
     a, b = _both(q, k, v, torch.ones((1, 4, 128, 128)), 64, True, dev)
     assert np.array_equal(a[1], b[1]) and (a[1] == 0).all()
+
+
+def test_noalloc_one_launch_published_sums_on_calls_in_a_row():
+    """Fresh prompts on the one-launch route, whose segments publish their
+    sums in the static array: three calls in a row with new inputs and other
+    layouts (the array keeps the earlier calls' sums and flags), each bit for
+    bit the call with a caller workspace."""
+    dev = need_gpu()
+    for r, (B, H, T, d, C) in enumerate(((4, 8, 1024, 64, 64), (2, 8, 1024, 64, 64), (4, 8, 1024, 64, 64))):
+        print("noalloc one launch", r, B, H, T, d, C, flush=True)
+        q, k, v = workloads.gaussian(B, H, T, d, d, seed_base=520 + r, scale=d ** -0.5)
+        a, b = _both(q, k, v, torch.full((B, H, d, d), float("nan")), C, True, dev)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]), r
